@@ -1,0 +1,202 @@
+"""ctypes/numpy front end of the CPU oracle.
+
+TEST INFRASTRUCTURE. Only the test suite, the smoke check and the benchmark's
+CPU-baseline leg may import this package. The GPU library never calls it and
+has no fallback to it.
+
+Inputs are numpy arrays on the host: bf16 data as ``uint16`` bit patterns,
+fp32 as ``float32``. Every function returns freshly allocated numpy arrays and
+raises ``OracleError`` on a nonzero status.
+"""
+import ctypes
+import os
+
+import numpy as np
+
+from . import build as _build
+
+FMT_E4M3 = 1
+FMT_E2M1 = 2
+_FMT_NAMES = {"e4m3": FMT_E4M3, "e2m1": FMT_E2M1}
+
+_lib = None
+
+
+class OracleError(RuntimeError):
+    pass
+
+
+def fmt_id(fmt):
+    if isinstance(fmt, str):
+        return _FMT_NAMES[fmt.lower()]
+    return int(fmt)
+
+
+def _load():
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not _build.is_current():
+        _build.build()
+    lib = ctypes.CDLL(_build.LIB)
+    i64, i32, f32 = ctypes.c_int64, ctypes.c_int, ctypes.c_float
+    vp = ctypes.c_void_p
+    sig = {
+        "oracle_version": ([], i32),
+        "oracle_decode": ([i32, ctypes.c_uint8], f32),
+        "oracle_encode": ([i32, f32], ctypes.c_uint8),
+        "oracle_encode_array": ([i32, vp, i64, vp], None),
+        "oracle_decode_array": ([i32, vp, i64, vp], None),
+        "oracle_format_max": ([i32], f32),
+        "oracle_default_floor": ([i32], f32),
+        "oracle_scale": ([i32, f32, f32, vp, vp], i32),
+        "oracle_per_token": ([vp, i64, i64, i32, i32, f32, vp, vp], i32),
+        "oracle_per_token_f32": ([vp, i64, i64, i32, i32, f32, vp, vp], i32),
+        "oracle_swiglu_per_token": ([vp, i64, i64, vp, i32, i32, f32, vp, vp], i32),
+        "oracle_swiglu_values": ([vp, i64, i64, vp, vp], i32),
+        "oracle_per_block": ([vp, i64, i64, i32, i32, f32, vp, vp], i32),
+        "oracle_per_channel_T": ([vp, i64, i64, i32, i32, f32, vp, vp], i32),
+        "oracle_dequant_per_token": ([vp, vp, i64, i64, i32, i32, vp], i32),
+    }
+    for name, (args, res) in sig.items():
+        fn = getattr(lib, name)
+        fn.argtypes = args
+        fn.restype = res
+    _lib = lib
+    return lib
+
+
+def _ptr(a):
+    return None if a is None else a.ctypes.data_as(ctypes.c_void_p)
+
+
+def _check(rc, what):
+    if rc != 0:
+        raise OracleError(f"{what}: oracle status {rc}")
+
+
+def _u16(x):
+    x = np.ascontiguousarray(x)
+    if x.dtype != np.uint16:
+        raise TypeError("bf16 input must be given as uint16 bit patterns")
+    return x
+
+
+def _f32(x):
+    return np.ascontiguousarray(x, dtype=np.float32)
+
+
+def _code_shape(fmt, rows, cols):
+    return (rows, cols) if fmt == FMT_E4M3 else (rows, cols // 2)
+
+
+def format_max(fmt):
+    return _load().oracle_format_max(fmt_id(fmt))
+
+
+def default_floor(fmt):
+    return _load().oracle_default_floor(fmt_id(fmt))
+
+
+def encode(fmt, y):
+    y = _f32(y)
+    out = np.empty(y.shape, np.uint8)
+    _load().oracle_encode_array(fmt_id(fmt), _ptr(y), y.size, _ptr(out))
+    return out
+
+
+def decode(fmt, codes):
+    codes = np.ascontiguousarray(codes, dtype=np.uint8)
+    out = np.empty(codes.shape, np.float32)
+    _load().oracle_decode_array(fmt_id(fmt), _ptr(codes), codes.size, _ptr(out))
+    return out
+
+
+def scale(fmt, amax, clamp_min=0.0):
+    sf = np.zeros(1, np.float32)
+    inv = np.zeros(1, np.float32)
+    _check(_load().oracle_scale(fmt_id(fmt), float(amax), float(clamp_min), _ptr(sf), _ptr(inv)),
+           "scale")
+    return sf[0], inv[0]
+
+
+def per_token(x, fmt="e4m3", group=128, clamp_min=0.0):
+    f = fmt_id(fmt)
+    x = _u16(x)
+    rows, cols = x.shape
+    q = np.zeros(_code_shape(f, rows, cols), np.uint8)
+    sf = np.zeros((rows, cols // group if group > 0 else 0), np.float32)
+    _check(_load().oracle_per_token(_ptr(x), rows, cols, f, group, clamp_min, _ptr(q), _ptr(sf)),
+           "per_token")
+    return q, sf
+
+
+def per_token_f32(x, fmt="e4m3", group=128, clamp_min=0.0):
+    f = fmt_id(fmt)
+    x = _f32(x)
+    rows, cols = x.shape
+    q = np.zeros(_code_shape(f, rows, cols), np.uint8)
+    sf = np.zeros((rows, cols // group if group > 0 else 0), np.float32)
+    _check(_load().oracle_per_token_f32(_ptr(x), rows, cols, f, group, clamp_min, _ptr(q),
+                                        _ptr(sf)), "per_token_f32")
+    return q, sf
+
+
+def e2m1(x, group=32, clamp_min=0.0):
+    return per_token(x, FMT_E2M1, group, clamp_min)
+
+
+def swiglu_values(h, w=None):
+    h = _u16(h)
+    rows, two_n = h.shape
+    cols = two_n // 2
+    w = None if w is None else _f32(w)
+    v = np.zeros((rows, cols), np.float32)
+    _check(_load().oracle_swiglu_values(_ptr(h), rows, cols, _ptr(w), _ptr(v)), "swiglu_values")
+    return v
+
+
+def swiglu_per_token(h, w=None, fmt="e4m3", group=128, clamp_min=0.0):
+    f = fmt_id(fmt)
+    h = _u16(h)
+    rows, two_n = h.shape
+    cols = two_n // 2
+    w = None if w is None else _f32(w)
+    q = np.zeros(_code_shape(f, rows, cols), np.uint8)
+    sf = np.zeros((rows, cols // group if group > 0 else 0), np.float32)
+    _check(_load().oracle_swiglu_per_token(_ptr(h), rows, cols, _ptr(w), f, group, clamp_min,
+                                           _ptr(q), _ptr(sf)), "swiglu_per_token")
+    return q, sf
+
+
+def per_block(x, fmt="e4m3", block=128, clamp_min=0.0):
+    f = fmt_id(fmt)
+    x = _u16(x)
+    rows, cols = x.shape
+    q = np.zeros(_code_shape(f, rows, cols), np.uint8)
+    sf = np.zeros((rows // block, cols // block), np.float32)
+    _check(_load().oracle_per_block(_ptr(x), rows, cols, f, block, clamp_min, _ptr(q), _ptr(sf)),
+           "per_block")
+    return q, sf
+
+
+def per_channel_T(x, fmt="e4m3", group=128, clamp_min=0.0):
+    f = fmt_id(fmt)
+    x = _u16(x)
+    rows, cols = x.shape
+    qT = np.zeros(_code_shape(f, cols, rows), np.uint8)
+    sf = np.zeros((cols, rows // group), np.float32)
+    _check(_load().oracle_per_channel_T(_ptr(x), rows, cols, f, group, clamp_min, _ptr(qT),
+                                        _ptr(sf)), "per_channel_T")
+    return qT, sf
+
+
+def dequant_per_token(q, sf, cols, fmt="e4m3", group=128):
+    f = fmt_id(fmt)
+    q = np.ascontiguousarray(q, dtype=np.uint8)
+    sf = _f32(sf)
+    rows = q.shape[0]
+    out = np.zeros((rows, cols), np.float32)
+    _check(_load().oracle_dequant_per_token(_ptr(q), _ptr(sf), rows, cols, f, group, _ptr(out)),
+           "dequant_per_token")
+    return out

@@ -1,0 +1,441 @@
+/*
+ * qcast_oracle.cpp -- CPU oracle for the TileKernels-style quantization casts.
+ *
+ * TEST INFRASTRUCTURE, NOT PRODUCT CODE. Only the test suite, the smoke check
+ * and the benchmark's CPU-baseline leg may load this library. It shares no
+ * source with the GPU library (no headers, tables or helpers); the two meet
+ * only on byte buffers produced by the seeded input generators.
+ *
+ * Sources (web pages; cited by title and section):
+ *  [WALK]  "DeepSeek开源TileKernels：用Python写的GPU算子逼近硬件性能上限"
+ *          (itsolotime.com), §3.1 quantization config, §3.2 per-token cast
+ *          kernel, §3.3 SwiGLU fused with the cast.
+ *  [SPLIT] "TileKernels 与 DeepGEMM 的分界线：DeepSeek 开源内核栈的分工"
+ *          (chatdocs.ruinique.com), §二 operator table (per_token_cast,
+ *          per_block_cast, per_channel_cast (+transpose),
+ *          swiglu_forward_and_per_token_cast), §四 A (formats E4M3/E2M1).
+ *  [NEWS]  "刚刚！DeepSeek开源高性能GPU算子库TileKernels", item 2 (quant/:
+ *          per-token, per-block and per-channel granularities).
+ * The number formats are the ones [WALK] §3.1 names, float8_e4m3fn and
+ * float4_e2m1fn; their bit layouts follow the OCP 8-bit floating point
+ * specification (E4M3, "fn": no infinities, one NaN pattern per sign) and the
+ * OCP Microscaling specification (E2M1: no infinities, no NaN).
+ *
+ * Readings where the pages are silent (each is listed in the design notes):
+ *  - rounding is to nearest, ties to the code with an even mantissa;
+ *  - a magnitude at or beyond the format maximum saturates to it;
+ *  - the sign of zero is kept (-0 and tiny negatives give the negative zero);
+ *  - the floor is applied to the group abs-max before the division;
+ *  - sf_inv is the fp32 reciprocal of sf, and the codes come from x * sf_inv
+ *    ([WALK] §3.2 multiplies by the inverse scale);
+ *  - SwiGLU values stay fp32 and are never rounded to bf16;
+ *  - NaN inputs are not defined by the pages; this oracle maps them to the
+ *    E4M3 NaN code and, for E2M1, to the saturated maximum (not graded).
+ *
+ * Arithmetic discipline: plain C++ on one thread, fp32 where the method is
+ * fp32 (the scale, the inverse, the scaled value, SwiGLU) with no
+ * contraction, no fast-math, and denormals kept (checked at every entry).
+ * The encoder is deliberately unlike a bit-trick: it searches a sorted table
+ * of every representable magnitude and compares against exact midpoints.
+ */
+#include "qcast_oracle.h"
+
+#include <cmath>
+#include <cstring>
+#include <vector>
+#include <xmmintrin.h>
+
+namespace {
+
+float f32_from_bits(uint32_t u) {
+  float f;
+  std::memcpy(&f, &u, sizeof f);
+  return f;
+}
+
+/* A bf16 is the upper 16 bits of an fp32, so widening is exact. */
+float bf16_value(uint16_t h) { return f32_from_bits(static_cast<uint32_t>(h) << 16); }
+
+/* ------------------------------------------------------------------------ */
+/* Formats                                                                   */
+/* ------------------------------------------------------------------------ */
+
+/* The non-negative finite values of a format, in code order. For both formats
+ * the codes 0..n-1 are ordered by magnitude, so index == code. */
+struct FormatTable {
+  int n = 0;                 /* number of non-negative finite codes */
+  double value[128] = {};    /* value[code] */
+  uint8_t sign_bit = 0;      /* bit that makes a code negative */
+  uint8_t nan_code = 0;      /* positive NaN code, or the max code if none */
+  float max = 0.0f;          /* largest finite magnitude */
+  float default_floor = 0.0f;
+};
+
+/* E4M3 "fn" (OCP FP8): s eeee mmm, exponent bias 7. Exponent field 0 holds
+ * the subnormals m * 2^-9; fields 1..15 hold (1 + m/8) * 2^(e-7), except that
+ * 0x7F / 0xFF are NaN. There is no infinity. */
+double e4m3_magnitude(int code7) {
+  const int e = (code7 >> 3) & 0xF;
+  const int m = code7 & 0x7;
+  if (e == 0) return std::ldexp(static_cast<double>(m), -9);
+  return std::ldexp(1.0 + m / 8.0, e - 7);
+}
+
+/* E2M1 (OCP MX FP4): s ee m, exponent bias 1. Exponent field 0 holds the
+ * subnormal m * 0.5; fields 1..3 hold (1 + m/2) * 2^(e-1). No NaN, no inf. */
+double e2m1_magnitude(int code3) {
+  const int e = (code3 >> 1) & 0x3;
+  const int m = code3 & 0x1;
+  if (e == 0) return 0.5 * m;
+  return std::ldexp(1.0 + m / 2.0, e - 1);
+}
+
+FormatTable make_e4m3() {
+  FormatTable t;
+  t.n = 127; /* 0x00 .. 0x7E; 0x7F is NaN */
+  for (int c = 0; c < t.n; ++c) t.value[c] = e4m3_magnitude(c);
+  t.sign_bit = 0x80;
+  t.nan_code = 0x7F;
+  t.max = static_cast<float>(t.value[t.n - 1]); /* 448 */
+  /* [WALK] §3.1: clamp_min_value is 1e-4 for float8_e4m3fn; as an fp32 that is
+   * the float nearest to 1e-4. */
+  t.default_floor = 1e-4f;
+  return t;
+}
+
+FormatTable make_e2m1() {
+  FormatTable t;
+  t.n = 8;
+  for (int c = 0; c < t.n; ++c) t.value[c] = e2m1_magnitude(c);
+  t.sign_bit = 0x08;
+  t.nan_code = 0x07;
+  t.max = static_cast<float>(t.value[t.n - 1]); /* 6 */
+  /* [WALK] §3.1: for float4_e2m1fn the floor is the format maximum times
+   * 2^-126, which puts sf = floor / max at the fp32 normal boundary. */
+  t.default_floor = static_cast<float>(std::ldexp(6.0, -126));
+  return t;
+}
+
+const FormatTable* table_for(int fmt) {
+  static const FormatTable e4m3 = make_e4m3();
+  static const FormatTable e2m1 = make_e2m1();
+  if (fmt == ORACLE_FMT_E4M3) return &e4m3;
+  if (fmt == ORACLE_FMT_E2M1) return &e2m1;
+  return nullptr;
+}
+
+/* Encode an fp32 value: nearest representable magnitude, ties to the even
+ * code, saturating at the maximum, sign attached afterwards. Comparisons are
+ * made in double, where every table value, every midpoint and every fp32 is
+ * exact. */
+uint8_t encode(const FormatTable& t, float y) {
+  if (std::isnan(y)) return t.nan_code;
+  const bool negative = std::signbit(y);
+  const double a = std::fabs(static_cast<double>(y));
+  int code;
+  if (a >= t.value[t.n - 1]) {
+    code = t.n - 1;
+  } else {
+    int lo = 0, hi = t.n - 1; /* invariant: value[lo] <= a < value[hi] */
+    while (hi - lo > 1) {
+      const int mid = (lo + hi) / 2;
+      if (t.value[mid] <= a) lo = mid; else hi = mid;
+    }
+    const double midpoint = 0.5 * (t.value[lo] + t.value[hi]);
+    if (a < midpoint) code = lo;
+    else if (a > midpoint) code = hi;
+    else code = (lo % 2 == 0) ? lo : hi;
+  }
+  return static_cast<uint8_t>(code | (negative ? t.sign_bit : 0));
+}
+
+float decode(const FormatTable& t, uint8_t code) {
+  const uint8_t magnitude_code = code & static_cast<uint8_t>(t.sign_bit - 1);
+  const bool negative = (code & t.sign_bit) != 0;
+  if (magnitude_code >= t.n) return std::nanf("");
+  const float v = static_cast<float>(t.value[magnitude_code]);
+  return negative ? -v : v;
+}
+
+/* ------------------------------------------------------------------------ */
+/* Floating-point environment                                                */
+/* ------------------------------------------------------------------------ */
+
+/* The fp32 steps must run with denormals kept and round-to-nearest. MXCSR bit
+ * 15 is flush-to-zero, bit 6 denormals-are-zero, bits 13-14 the rounding
+ * control. */
+bool fp_env_ok() {
+  const unsigned csr = _mm_getcsr();
+  return (csr & 0x8000u) == 0 && (csr & 0x0040u) == 0 && (csr & 0x6000u) == 0;
+}
+
+/* ------------------------------------------------------------------------ */
+/* Scale ([WALK] §3.1 clamp_min_value, §3.2 get_sf_and_inv)                  */
+/* ------------------------------------------------------------------------ */
+
+struct Scale {
+  float sf;
+  float sf_inv;
+};
+
+float floor_for(const FormatTable& t, float clamp_min) {
+  /* [WALK] §3.1: a custom clamp value, when given, replaces the default. */
+  return clamp_min > 0.0f ? clamp_min : t.default_floor;
+}
+
+Scale scale_from_amax(const FormatTable& t, float amax, float floor) {
+  const float a = (amax < floor) ? floor : amax;
+  Scale s;
+  s.sf = a / t.max;
+  s.sf_inv = 1.0f / s.sf;
+  return s;
+}
+
+/* ------------------------------------------------------------------------ */
+/* Code storage                                                              */
+/* ------------------------------------------------------------------------ */
+
+/* Store a code at (row, col) of an output with `cols` logical columns. E4M3
+ * takes a byte per code; E2M1 packs column 2k into the low nibble and 2k+1
+ * into the high nibble of byte k of the row. */
+void put_code(int fmt, uint8_t* q, int64_t cols, int64_t row, int64_t col, uint8_t code) {
+  if (fmt == ORACLE_FMT_E4M3) {
+    q[row * cols + col] = code;
+  } else {
+    uint8_t& b = q[row * (cols / 2) + col / 2];
+    if (col % 2 == 0) b = static_cast<uint8_t>((b & 0xF0) | (code & 0x0F));
+    else b = static_cast<uint8_t>((b & 0x0F) | ((code & 0x0F) << 4));
+  }
+}
+
+uint8_t get_code(int fmt, const uint8_t* q, int64_t cols, int64_t row, int64_t col) {
+  if (fmt == ORACLE_FMT_E4M3) return q[row * cols + col];
+  const uint8_t b = q[row * (cols / 2) + col / 2];
+  return (col % 2 == 0) ? (b & 0x0F) : (b >> 4);
+}
+
+/* Common checks for a per-token style cast. */
+int check_common(const void* a, const void* b, const void* c, int fmt, int group) {
+  if (!a || !b || !c) return ORACLE_ERR_NULL;
+  if (!table_for(fmt)) return ORACLE_ERR_FORMAT;
+  if (group <= 0) return ORACLE_ERR_GROUP;
+  if (!fp_env_ok()) return ORACLE_ERR_FPENV;
+  return ORACLE_OK;
+}
+
+/* Per-token cast of rows of fp32 values ([WALK] §3.2): for each row and each
+ * run of `group` columns, the abs-max, the scale, then every element times
+ * the inverse scale, encoded. */
+void per_token_rows(const float* x, int64_t rows, int64_t cols, int fmt, int group, float floor,
+                    uint8_t* q, float* sf) {
+  const FormatTable& t = *table_for(fmt);
+  const int64_t groups = cols / group;
+  for (int64_t r = 0; r < rows; ++r) {
+    const float* xr = x + r * cols;
+    for (int64_t k = 0; k < groups; ++k) {
+      float amax = 0.0f;
+      for (int64_t i = 0; i < group; ++i) {
+        const float m = std::fabs(xr[k * group + i]);
+        if (m > amax) amax = m;
+      }
+      const Scale s = scale_from_amax(t, amax, floor);
+      for (int64_t i = 0; i < group; ++i) {
+        const int64_t c = k * group + i;
+        const float y = xr[c] * s.sf_inv;
+        put_code(fmt, q, cols, r, c, encode(t, y));
+      }
+      sf[r * groups + k] = s.sf;
+    }
+  }
+}
+
+} /* namespace */
+
+/* ======================================================================== */
+/* Exported functions                                                        */
+/* ======================================================================== */
+
+extern "C" {
+
+int oracle_version(void) { return 1; }
+
+float oracle_decode(int fmt, uint8_t code) {
+  const FormatTable* t = table_for(fmt);
+  return t ? decode(*t, code) : std::nanf("");
+}
+
+uint8_t oracle_encode(int fmt, float y) {
+  const FormatTable* t = table_for(fmt);
+  return t ? encode(*t, y) : 0;
+}
+
+void oracle_encode_array(int fmt, const float* y, int64_t n, uint8_t* codes) {
+  const FormatTable* t = table_for(fmt);
+  if (!t) return;
+  for (int64_t i = 0; i < n; ++i) codes[i] = encode(*t, y[i]);
+}
+
+void oracle_decode_array(int fmt, const uint8_t* codes, int64_t n, float* out) {
+  const FormatTable* t = table_for(fmt);
+  if (!t) return;
+  for (int64_t i = 0; i < n; ++i) out[i] = decode(*t, codes[i]);
+}
+
+float oracle_format_max(int fmt) {
+  const FormatTable* t = table_for(fmt);
+  return t ? t->max : 0.0f;
+}
+
+float oracle_default_floor(int fmt) {
+  const FormatTable* t = table_for(fmt);
+  return t ? t->default_floor : 0.0f;
+}
+
+int oracle_scale(int fmt, float amax, float clamp_min, float* sf, float* sf_inv) {
+  const FormatTable* t = table_for(fmt);
+  if (!t) return ORACLE_ERR_FORMAT;
+  if (!sf || !sf_inv) return ORACLE_ERR_NULL;
+  if (!fp_env_ok()) return ORACLE_ERR_FPENV;
+  const Scale s = scale_from_amax(*t, amax, floor_for(*t, clamp_min));
+  *sf = s.sf;
+  *sf_inv = s.sf_inv;
+  return ORACLE_OK;
+}
+
+int oracle_per_token_f32(const float* x, int64_t rows, int64_t cols, int fmt, int group,
+                         float clamp_min, uint8_t* q, float* sf) {
+  const int rc = check_common(x, q, sf, fmt, group);
+  if (rc != ORACLE_OK) return rc;
+  if (rows < 0 || cols < 0 || cols % group != 0) return ORACLE_ERR_SHAPE;
+  if (fmt == ORACLE_FMT_E2M1 && group % 2 != 0) return ORACLE_ERR_GROUP;
+  per_token_rows(x, rows, cols, fmt, group, floor_for(*table_for(fmt), clamp_min), q, sf);
+  return ORACLE_OK;
+}
+
+int oracle_per_token(const uint16_t* x, int64_t rows, int64_t cols, int fmt, int group,
+                     float clamp_min, uint8_t* q, float* sf) {
+  const int rc = check_common(x, q, sf, fmt, group);
+  if (rc != ORACLE_OK) return rc;
+  if (rows < 0 || cols < 0 || cols % group != 0) return ORACLE_ERR_SHAPE;
+  if (fmt == ORACLE_FMT_E2M1 && group % 2 != 0) return ORACLE_ERR_GROUP;
+  const float floor = floor_for(*table_for(fmt), clamp_min);
+  std::vector<float> row(static_cast<size_t>(cols));
+  const int64_t code_bytes = (fmt == ORACLE_FMT_E4M3) ? cols : cols / 2;
+  const int64_t groups = cols / group;
+  for (int64_t r = 0; r < rows; ++r) {
+    for (int64_t c = 0; c < cols; ++c) row[c] = bf16_value(x[r * cols + c]);
+    per_token_rows(row.data(), 1, cols, fmt, group, floor, q + r * code_bytes, sf + r * groups);
+  }
+  return ORACLE_OK;
+}
+
+int oracle_swiglu_values(const uint16_t* h, int64_t rows, int64_t cols, const float* w,
+                         float* v) {
+  if (!h || !v) return ORACLE_ERR_NULL;
+  if (rows < 0 || cols < 0) return ORACLE_ERR_SHAPE;
+  if (!fp_env_ok()) return ORACLE_ERR_FPENV;
+  /* [WALK] §3.3: the left half is the SiLU input, the right half multiplies
+   * it; SiLU is written g / (1 + exp(-g)); the routing weight multiplies last.
+   * All in fp32. */
+  for (int64_t r = 0; r < rows; ++r) {
+    const uint16_t* hr = h + r * 2 * cols;
+    for (int64_t j = 0; j < cols; ++j) {
+      const float g = bf16_value(hr[j]);
+      const float u = bf16_value(hr[cols + j]);
+      const float silu = g / (1.0f + std::exp(-g));
+      float val = silu * u;
+      if (w) val = val * w[r];
+      v[r * cols + j] = val;
+    }
+  }
+  return ORACLE_OK;
+}
+
+int oracle_swiglu_per_token(const uint16_t* h, int64_t rows, int64_t cols, const float* w,
+                            int fmt, int group, float clamp_min, uint8_t* q, float* sf) {
+  const int rc = check_common(h, q, sf, fmt, group);
+  if (rc != ORACLE_OK) return rc;
+  if (rows < 0 || cols < 0 || cols % group != 0) return ORACLE_ERR_SHAPE;
+  if (fmt == ORACLE_FMT_E2M1 && group % 2 != 0) return ORACLE_ERR_GROUP;
+  const float floor = floor_for(*table_for(fmt), clamp_min);
+  std::vector<float> v(static_cast<size_t>(cols));
+  const int64_t code_bytes = (fmt == ORACLE_FMT_E4M3) ? cols : cols / 2;
+  const int64_t groups = cols / group;
+  for (int64_t r = 0; r < rows; ++r) {
+    oracle_swiglu_values(h + r * 2 * cols, 1, cols, w ? w + r : nullptr, v.data());
+    per_token_rows(v.data(), 1, cols, fmt, group, floor, q + r * code_bytes, sf + r * groups);
+  }
+  return ORACLE_OK;
+}
+
+int oracle_per_block(const uint16_t* x, int64_t rows, int64_t cols, int fmt, int block,
+                     float clamp_min, uint8_t* q, float* sf) {
+  const int rc = check_common(x, q, sf, fmt, block);
+  if (rc != ORACLE_OK) return rc;
+  if (rows < 0 || cols < 0 || rows % block != 0 || cols % block != 0) return ORACLE_ERR_SHAPE;
+  if (fmt == ORACLE_FMT_E2M1 && block % 2 != 0) return ORACLE_ERR_GROUP;
+  const FormatTable& t = *table_for(fmt);
+  const float floor = floor_for(t, clamp_min);
+  const int64_t brows = rows / block, bcols = cols / block;
+  for (int64_t bi = 0; bi < brows; ++bi) {
+    for (int64_t bj = 0; bj < bcols; ++bj) {
+      float amax = 0.0f;
+      for (int64_t r = bi * block; r < (bi + 1) * block; ++r)
+        for (int64_t c = bj * block; c < (bj + 1) * block; ++c) {
+          const float m = std::fabs(bf16_value(x[r * cols + c]));
+          if (m > amax) amax = m;
+        }
+      const Scale s = scale_from_amax(t, amax, floor);
+      for (int64_t r = bi * block; r < (bi + 1) * block; ++r)
+        for (int64_t c = bj * block; c < (bj + 1) * block; ++c) {
+          const float y = bf16_value(x[r * cols + c]) * s.sf_inv;
+          put_code(fmt, q, cols, r, c, encode(t, y));
+        }
+      sf[bi * bcols + bj] = s.sf;
+    }
+  }
+  return ORACLE_OK;
+}
+
+int oracle_per_channel_T(const uint16_t* x, int64_t rows, int64_t cols, int fmt, int group,
+                         float clamp_min, uint8_t* qT, float* sf) {
+  const int rc = check_common(x, qT, sf, fmt, group);
+  if (rc != ORACLE_OK) return rc;
+  if (rows < 0 || cols < 0 || rows % group != 0) return ORACLE_ERR_SHAPE;
+  if (fmt == ORACLE_FMT_E2M1 && group % 2 != 0) return ORACLE_ERR_GROUP;
+  const FormatTable& t = *table_for(fmt);
+  const float floor = floor_for(t, clamp_min);
+  const int64_t groups = rows / group;
+  /* Output row c of qT is channel c; its columns are the tokens. */
+  for (int64_t c = 0; c < cols; ++c) {
+    for (int64_t g = 0; g < groups; ++g) {
+      float amax = 0.0f;
+      for (int64_t tk = g * group; tk < (g + 1) * group; ++tk) {
+        const float m = std::fabs(bf16_value(x[tk * cols + c]));
+        if (m > amax) amax = m;
+      }
+      const Scale s = scale_from_amax(t, amax, floor);
+      for (int64_t tk = g * group; tk < (g + 1) * group; ++tk) {
+        const float y = bf16_value(x[tk * cols + c]) * s.sf_inv;
+        put_code(fmt, qT, rows, c, tk, encode(t, y));
+      }
+      sf[c * groups + g] = s.sf;
+    }
+  }
+  return ORACLE_OK;
+}
+
+int oracle_dequant_per_token(const uint8_t* q, const float* sf, int64_t rows, int64_t cols,
+                             int fmt, int group, float* out) {
+  const int rc = check_common(q, sf, out, fmt, group);
+  if (rc != ORACLE_OK) return rc;
+  if (rows < 0 || cols < 0 || cols % group != 0) return ORACLE_ERR_SHAPE;
+  const FormatTable& t = *table_for(fmt);
+  const int64_t groups = cols / group;
+  for (int64_t r = 0; r < rows; ++r)
+    for (int64_t c = 0; c < cols; ++c)
+      out[r * cols + c] = decode(t, get_code(fmt, q, cols, r, c)) * sf[r * groups + c / group];
+  return ORACLE_OK;
+}
+
+} /* extern "C" */

@@ -1,0 +1,91 @@
+/*
+ * qcast_oracle.h -- the CPU oracle's own interface.
+ *
+ * TEST INFRASTRUCTURE. This header and qcast_oracle.cpp are a plain, slow,
+ * single-threaded restatement of what the quantization casts compute. Only the
+ * test suite, the smoke check and the benchmark's CPU-baseline leg may load it.
+ * It shares no source with the GPU library and must never be used as a
+ * fallback for it.
+ *
+ * All pointers are HOST pointers, row-major and contiguous. Inputs are bf16
+ * bit patterns (uint16_t). Codes are bytes (E4M3) or packed nibbles (E2M1:
+ * byte k of a row holds column 2k in its low nibble, 2k+1 in its high nibble).
+ * Scales are fp32.
+ *
+ * Every cast returns ORACLE_OK or an error code; on an error nothing is
+ * written.
+ */
+#ifndef QCAST_ORACLE_H
+#define QCAST_ORACLE_H
+
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+enum {
+  ORACLE_OK = 0,
+  ORACLE_ERR_NULL = 1,
+  ORACLE_ERR_SHAPE = 2,
+  ORACLE_ERR_FORMAT = 4,
+  ORACLE_ERR_GROUP = 5,
+  ORACLE_ERR_FPENV = 7 /* FTZ/DAZ set or rounding mode not nearest */
+};
+
+enum { ORACLE_FMT_E4M3 = 1, ORACLE_FMT_E2M1 = 2 };
+
+int oracle_version(void);
+
+/* ---- format codecs (one element at a time, and array forms) ---- */
+float oracle_decode(int fmt, uint8_t code);     /* NaN for E4M3 0x7F/0xFF */
+uint8_t oracle_encode(int fmt, float y);        /* RNE, saturating, signed zero */
+void oracle_encode_array(int fmt, const float* y, int64_t n, uint8_t* codes);
+void oracle_decode_array(int fmt, const uint8_t* codes, int64_t n, float* out);
+float oracle_format_max(int fmt);
+float oracle_default_floor(int fmt);
+
+/* Scale of one group: a = max(amax, floor); sf = a / fmt_max; sf_inv = 1/sf.
+ * clamp_min <= 0 selects the format's default floor. */
+int oracle_scale(int fmt, float amax, float clamp_min, float* sf, float* sf_inv);
+
+/* ---- casts ---- */
+/* x [rows, cols] bf16 -> q [rows, cols] (E4M3) or [rows, cols/2] (E2M1),
+ * sf [rows, cols/group]. */
+int oracle_per_token(const uint16_t* x, int64_t rows, int64_t cols, int fmt, int group,
+                     float clamp_min, uint8_t* q, float* sf);
+
+/* h [rows, 2*cols] bf16 = [gate | up]; w [rows] fp32 or NULL.
+ * v = (g / (1 + exp(-g))) * u (* w[r]) in fp32, then the per-token cast of v. */
+int oracle_swiglu_per_token(const uint16_t* h, int64_t rows, int64_t cols, const float* w,
+                            int fmt, int group, float clamp_min, uint8_t* q, float* sf);
+
+/* The fp32 SwiGLU values alone: v [rows, cols]. */
+int oracle_swiglu_values(const uint16_t* h, int64_t rows, int64_t cols, const float* w,
+                         float* v);
+
+/* Per-token cast of fp32 input values (used to check the SwiGLU path and the
+ * dequantize/requantize round trip). */
+int oracle_per_token_f32(const float* x, int64_t rows, int64_t cols, int fmt, int group,
+                         float clamp_min, uint8_t* q, float* sf);
+
+/* x [rows, cols] bf16; one scale per block x block tile: sf [rows/block, cols/block];
+ * q like per_token. */
+int oracle_per_block(const uint16_t* x, int64_t rows, int64_t cols, int fmt, int block,
+                     float clamp_min, uint8_t* q, float* sf);
+
+/* x [rows (tokens), cols (channels)] bf16; the scale groups run along tokens:
+ * group g of channel c is x[g*G .. g*G+G-1][c]. Output transposed:
+ * qT [cols, rows] (E4M3) or [cols, rows/2] (E2M1), sf [cols, rows/group]. */
+int oracle_per_channel_T(const uint16_t* x, int64_t rows, int64_t cols, int fmt, int group,
+                         float clamp_min, uint8_t* qT, float* sf);
+
+/* Dequantize per-token codes: out[r][c] = decode(q[r][c]) * sf[r][c/group] (fp32). */
+int oracle_dequant_per_token(const uint8_t* q, const float* sf, int64_t rows, int64_t cols,
+                             int fmt, int group, float* out);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* QCAST_ORACLE_H */

@@ -1,0 +1,75 @@
+"""Write oracle_digests.json: SHA-256 digests of the oracle's outputs on
+small seeded workloads.
+
+This script calls only the oracle and the seeded input generators. The
+digests guard the oracle against unintended changes: a deliberate change to
+its arithmetic regenerates them, and the commit names the passage of the
+pages (or the reading of it) that justifies the change.
+
+    python tests/golden/make_golden.py
+"""
+import hashlib
+import json
+import os
+import sys
+
+import numpy as np
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+ROOT = os.path.dirname(os.path.dirname(HERE))
+sys.path.insert(0, ROOT)
+
+import oracle  # noqa: E402
+from precision_quantization_amd import workloads  # noqa: E402
+
+# Small versions of each workload recipe (same structure, fewer rows).
+CASES = {
+    "per_token_small": lambda: workloads.per_token_small(),
+    "per_token_hidden_r64": lambda: workloads.per_token_hidden(rows=64),
+    "swiglu_r32": lambda: workloads.swiglu_input(rows=32),
+    "per_block_256x512": lambda: workloads.weight_block(rows=256, cols=512),
+    "per_channel_T_256x384": lambda: workloads.activation_channel(rows=256, cols=384),
+    "e2m1_r16": lambda: workloads.student_t(rows=16),
+}
+
+
+def digest(*arrays):
+    h = hashlib.sha256()
+    for a in arrays:
+        h.update(np.ascontiguousarray(a).tobytes())
+    return h.hexdigest()
+
+
+def run_case(wl):
+    x = workloads.bf16_bits(wl.x)
+    if wl.op == "per_token":
+        q, sf = oracle.per_token(x, wl.fmt, wl.group)
+    elif wl.op == "e2m1":
+        q, sf = oracle.e2m1(x, wl.group)
+    elif wl.op == "swiglu_per_token":
+        q, sf = oracle.swiglu_per_token(x, wl.w.numpy(), wl.fmt, wl.group)
+    elif wl.op == "per_block":
+        q, sf = oracle.per_block(x, wl.fmt, wl.group)
+    elif wl.op == "per_channel_T":
+        q, sf = oracle.per_channel_T(x, wl.fmt, wl.group)
+    else:
+        raise ValueError(wl.op)
+    return q, sf
+
+
+def compute():
+    out = {}
+    for name, make in CASES.items():
+        wl = make()
+        q, sf = run_case(wl)
+        out[name] = {"input": workloads.sha256(wl.x), "codes": digest(q), "scales": digest(sf)}
+    return out
+
+
+if __name__ == "__main__":
+    path = os.path.join(HERE, "oracle_digests.json")
+    data = {"_source": "written by tests/golden/make_golden.py (oracle + seeded generators only)"}
+    data.update(compute())
+    with open(path, "w") as f:
+        json.dump(data, f, indent=1, sort_keys=True)
+    print("wrote", path)
