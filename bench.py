@@ -1,0 +1,248 @@
+"""Benchmark of the quantization-cast hot path on one MI355X.
+
+One step is one pass of every cast over its own synthetic workload, shaped
+like DeepSeek-V3 MoE tensors:
+    per_token      bf16 X[4096, 7168] -> E4M3 + fp32 scales (1 x 128 groups)
+    swiglu         bf16 H[8192, 4096] (gate | up) + fp32 w[8192] -> E4M3 [8192, 2048]
+    per_block      bf16 W[7168, 18432] -> E4M3 + one scale per 128 x 128 block
+    per_channel_T  bf16 A[16384, 7168] -> E4M3 [7168, 16384] + scales per 128 tokens
+    e2m1           bf16 X[16384, 7168] (0.5 * t3) -> packed E2M1 + scales (1 x 32)
+Inputs are resident in HBM before timing starts; the step touches about
+1.23 GB, five times the 256 MB last-level cache, so every kernel reads
+inputs that the rest of the step has evicted.
+
+value = algorithmic bytes of the whole step (inputs read once, codes and
+scales written once) / time per step, in GB/s. Per-kernel durations come from
+HIP events recorded on the launch stream around each kernel in the timed
+steps. The roofline object is for the kernel with the largest share of the
+step. The CPU baseline is the oracle (single thread) on the first half of the
+rows of every workload, on this host.
+
+    python bench.py [--gpus 1] [--steps 50] [--warmup 5]
+"""
+import argparse
+import json
+import os
+import platform
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+PEAK_HBM_GBS = 8000.0
+METRIC = "achieved HBM GB/s (bytes in+out) and % of MI355X peak, per cast kernel"
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic.json")
+
+
+def log(msg):
+    print(msg, file=sys.stderr, flush=True)
+
+
+def make_workloads():
+    from precision_quantization_amd import workloads as W
+    return [
+        ("per_token", W.per_token_hidden()),
+        ("swiglu", W.swiglu_input()),
+        ("per_block", W.weight_block()),
+        ("per_channel_T", W.activation_channel()),
+        ("e2m1", W.student_t()),
+    ]
+
+
+def kernel_calls(wls, dev):
+    """Per kernel: a closure launching it on the current stream into
+    preallocated outputs."""
+    import torch
+    import precision_quantization_amd as pq
+    calls = []
+    for name, wl in wls:
+        x = wl.x.to(dev)
+        rows, cols = wl.x.shape
+        if name == "per_token":
+            out = torch.empty(rows, cols, dtype=torch.float8_e4m3fn, device=dev)
+            sf = torch.empty(rows, cols // 128, dtype=torch.float32, device=dev)
+            fn = lambda x=x, out=out, sf=sf: pq.qcast_per_token(x, "e4m3", 128, out=out, out_sf=sf)
+        elif name == "swiglu":
+            w = wl.w.to(dev)
+            out = torch.empty(rows, cols // 2, dtype=torch.float8_e4m3fn, device=dev)
+            sf = torch.empty(rows, cols // 2 // 128, dtype=torch.float32, device=dev)
+            fn = lambda x=x, w=w, out=out, sf=sf: pq.qcast_swiglu_per_token(
+                x, w, "e4m3", 128, out=out, out_sf=sf)
+        elif name == "per_block":
+            out = torch.empty(rows, cols, dtype=torch.float8_e4m3fn, device=dev)
+            sf = torch.empty(rows // 128, cols // 128, dtype=torch.float32, device=dev)
+            fn = lambda x=x, out=out, sf=sf: pq.qcast_per_block(x, "e4m3", 128, out=out, out_sf=sf)
+        elif name == "per_channel_T":
+            out = torch.empty(cols, rows, dtype=torch.float8_e4m3fn, device=dev)
+            sf = torch.empty(cols, rows // 128, dtype=torch.float32, device=dev)
+            fn = lambda x=x, out=out, sf=sf: pq.qcast_per_channel_T(x, "e4m3", 128, out=out,
+                                                                    out_sf=sf)
+        elif name == "e2m1":
+            out = torch.empty(rows, cols // 2, dtype=torch.uint8, device=dev)
+            sf = torch.empty(rows, cols // 32, dtype=torch.float32, device=dev)
+            fn = lambda x=x, out=out, sf=sf: pq.qcast_e2m1(x, 32, out=out, out_sf=sf)
+        calls.append((name, wl, fn))
+    return calls
+
+
+def copy_ceiling(dev, nbytes):
+    """Bandwidth of a plain device copy moving nbytes in total (half read,
+    half written), cold: the empirical ceiling for a streaming kernel."""
+    import torch
+    half = nbytes // 2
+    src = torch.empty(half, dtype=torch.uint8, device=dev).fill_(1)
+    dst = torch.empty(half, dtype=torch.uint8, device=dev)
+    flush = torch.empty(1 << 30, dtype=torch.uint8, device=dev)
+    times = []
+    for _ in range(6):
+        flush.fill_(0)
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record()
+        dst.copy_(src)
+        b.record()
+        torch.cuda.synchronize()
+        times.append(a.elapsed_time(b))
+    ms = sorted(times[1:])[len(times[1:]) // 2]
+    return nbytes / (ms * 1e-3) / 1e9
+
+
+def cpu_baseline(wls, fraction=0.5):
+    """The oracle, single-threaded, on the first `fraction` of the rows of
+    every workload; GB/s over the same algorithmic bytes."""
+    import oracle
+    from precision_quantization_amd import workloads as W
+    total_bytes = 0
+    total_s = 0.0
+    for name, wl in wls:
+        n = max(128, int(wl.rows * fraction) // 128 * 128)
+        sub = W.Workload(wl.name, wl.op, wl.x[:n], wl.fmt, wl.group,
+                         w=None if wl.w is None else wl.w[:n])
+        xb = W.bf16_bits(sub.x)
+        t0 = time.perf_counter()
+        if name == "per_token":
+            oracle.per_token(xb, "e4m3", 128)
+        elif name == "swiglu":
+            oracle.swiglu_per_token(xb, sub.w.numpy(), "e4m3", 128)
+        elif name == "per_block":
+            oracle.per_block(xb, "e4m3", 128)
+        elif name == "per_channel_T":
+            oracle.per_channel_T(xb, "e4m3", 128)
+        elif name == "e2m1":
+            oracle.e2m1(xb, 32)
+        total_s += time.perf_counter() - t0
+        total_bytes += sub.algorithmic_bytes()
+    return total_bytes / total_s / 1e9, total_s
+
+
+def load_traffic(dominant):
+    """HBM bytes per launch of the dominant kernel from the committed counter
+    summary, if it was taken from the library as it is now built."""
+    try:
+        from precision_quantization_amd import build
+        with open(TRAFFIC_FILE) as f:
+            t = json.load(f)
+        if t.get("library_digest") != build.source_digest():
+            return None
+        return t["kernels"][dominant]["bytes_per_launch"]
+    except (OSError, KeyError, ValueError):
+        return None
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU; --gpus {args.gpus} is not supported: the casts shard "
+              "by rows with no exchange between GPUs, so a multi-GPU run adds nothing to "
+              "measure here.", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    dev = torch.device("cuda:0")
+    log("bench: generating workloads")
+    wls = make_workloads()
+    calls = kernel_calls(wls, dev)
+    step_bytes = sum(wl.algorithmic_bytes() for _, wl in wls)
+    torch.cuda.synchronize()
+    log("bench: warmup")
+    for _ in range(args.warmup):
+        for _, _, fn in calls:
+            fn()
+    torch.cuda.synchronize()
+
+    n = len(calls)
+    ev = [[(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+           for _ in range(n)] for _ in range(args.steps)]
+    log(f"bench: timing {args.steps} steps")
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for s in range(args.steps):
+        for i, (_, _, fn) in enumerate(calls):
+            ev[s][i][0].record()
+            fn()
+            ev[s][i][1].record()
+    torch.cuda.synchronize()
+    elapsed = time.perf_counter() - t0
+    ms_per_step = elapsed * 1e3 / args.steps
+
+    kernels = {}
+    for i, (name, wl, _) in enumerate(calls):
+        ms = sorted(ev[s][i][0].elapsed_time(ev[s][i][1]) for s in range(args.steps))
+        avg = sum(ms) / len(ms)
+        b = wl.algorithmic_bytes()
+        kernels[name] = {
+            "shape": list(wl.x.shape), "bytes": b, "avg_us": round(avg * 1e3, 2),
+            "median_us": round(ms[len(ms) // 2] * 1e3, 2),
+            "GBps": round(b / (avg * 1e-3) / 1e9, 1),
+            "frac": round(b / (avg * 1e-3) / 1e9 / PEAK_HBM_GBS, 4),
+        }
+    dominant = max(kernels, key=lambda k: kernels[k]["avg_us"])
+    d = kernels[dominant]
+    traffic = load_traffic(dominant)
+    copy_gbs = copy_ceiling(dev, d["bytes"])
+    result = {
+        "metric": METRIC,
+        "value": round(step_bytes * args.steps / elapsed / 1e9, 1),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f32",
+        "data": "synthetic",
+        "config": {
+            "workload": "one pass of the five casts on DeepSeek-V3-shaped inputs: per_token "
+                        "X[4096,7168] E4M3 g128; swiglu H[8192,4096]+w E4M3 g128; per_block "
+                        "W[7168,18432] E4M3 128x128; per_channel_T A[16384,7168] E4M3 g128 "
+                        "transposed; e2m1 X[16384,7168] packed g32",
+            "step_bytes": step_bytes,
+        },
+        "roofline": {
+            "bound": "hbm", "kernel": dominant, "achieved": d["GBps"], "peak": PEAK_HBM_GBS,
+            "unit": "GB/s", "frac": d["frac"], "traffic": traffic,
+        },
+        "kernels": kernels,
+        "copy_ceiling_GBps": round(copy_gbs, 1),
+    }
+    if not args.no_cpu_baseline:
+        log("bench: CPU baseline (oracle)")
+        gbs, secs = cpu_baseline(wls)
+        result["cpu_baseline"] = {
+            "value": round(gbs, 4), "unit": "GB/s", "cores": 1, "kind": "oracle",
+            "sample": f"first half of the rows of each of the five workloads "
+                      f"({secs:.1f} s on {platform.processor() or platform.machine()}, "
+                      f"{os.cpu_count()} cores present)",
+        }
+    print(json.dumps(result), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,155 @@
+/*
+ * qcast.h -- C ABI of the MI355X (gfx950) quantization-cast library.
+ *
+ * The operations are the memory-bound quantization casts of DeepSeek's
+ * TileKernels quant/ module as the pages describe them:
+ *   [WALK]  "DeepSeek开源TileKernels：用Python写的GPU算子逼近硬件性能上限"
+ *           (itsolotime.com): quick start (per_token_cast(x, fmt='e4m3',
+ *           num_per_channels=128) -> (out, out_sf)), §3.1 (CastInputConfig /
+ *           CastOutputConfig, clamp_min_value), §3.2 (per-token cast kernel),
+ *           §3.3 (SwiGLU fused with the per-token cast).
+ *   [SPLIT] "TileKernels 与 DeepGEMM 的分界线：DeepSeek 开源内核栈的分工"
+ *           (chatdocs.ruinique.com): §二 operator table (per_token_cast,
+ *           per_block_cast, per_channel_cast (+transpose),
+ *           swiglu_forward_and_per_token_cast), §四 A (E4M3 / E2M1 formats),
+ *           §六 (where the casts sit in a MoE layer).
+ *
+ * What every cast computes, per scale group of elements x_i:
+ *     amax   = max_i |x_i|
+ *     a      = max(amax, floor)                      fp32
+ *     sf     = a / fmt_max                           fp32, IEEE division
+ *     sf_inv = 1 / sf                                fp32, IEEE division
+ *     code_i = encode(x_i * sf_inv)                  fp32 product, then
+ *              round to nearest (ties to even mantissa), saturating, sign kept
+ * fmt_max is 448 for E4M3 and 6 for E2M1. The default floor
+ * ([WALK] §3.1) is 1e-4f for E4M3 and 6 * 2^-126 for E2M1; a clamp_min > 0
+ * replaces it.
+ *
+ * Conventions shared by every entry point:
+ *  - Every data pointer is a DEVICE pointer on the current HIP device, owned
+ *    (allocated and freed) by the caller. The library never allocates,
+ *    frees, synchronizes or keeps a pointer after returning.
+ *  - Tensors are row-major and contiguous. bf16 inputs are passed as raw
+ *    16-bit patterns. Inputs must not overlap outputs.
+ *  - Alignment: inputs and code outputs 16 bytes, scale outputs 4 bytes,
+ *    the optional row weight 4 bytes.
+ *  - Work is enqueued on `stream` (a hipStream_t passed as void*; NULL is
+ *    the default stream) and the call returns at once.
+ *  - The return value is a qcast_status. Arguments are checked before any
+ *    HIP call; on an error nothing is launched and no output is touched.
+ *    QCAST_ERR_LAUNCH reports a failed launch (hipGetLastError).
+ *  - rows == 0 (or an empty row) is valid and launches nothing.
+ *  - Calls on one stream are ordered; concurrent calls on different streams
+ *    are independent (no shared mutable device state).
+ */
+#ifndef QCAST_H
+#define QCAST_H
+
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define QCAST_ABI_VERSION 1
+
+#ifndef QCAST_API
+#define QCAST_API __attribute__((visibility("default")))
+#endif
+
+typedef enum {
+  QCAST_OK = 0,
+  QCAST_ERR_NULL = 1,   /* a required pointer is NULL */
+  QCAST_ERR_SHAPE = 2,  /* negative size, or sizes not divisible as required */
+  QCAST_ERR_ALIGN = 3,  /* a pointer is not aligned as required */
+  QCAST_ERR_FORMAT = 4, /* format not supported by this entry point */
+  QCAST_ERR_GROUP = 5,  /* group / block size not supported */
+  QCAST_ERR_LAUNCH = 6, /* the kernel launch failed */
+  QCAST_ERR_DEVICE = 7  /* no usable HIP device */
+} qcast_status;
+
+typedef enum { QCAST_FMT_E4M3 = 1, QCAST_FMT_E2M1 = 2 } qcast_fmt;
+
+/*
+ * Per-token cast ([WALK] quick start and §3.2; [SPLIT] §二 per_token_cast).
+ * One scale per run of `group` consecutive elements of a row (the page's
+ * num_per_channels).
+ *   x     [rows, cols] bf16.
+ *   q     E4M3: [rows, cols] bytes.  E2M1: [rows, cols/2] bytes, column 2k in
+ *         the low nibble of byte k and column 2k+1 in its high nibble.
+ *   sf    [rows, cols/group] fp32.
+ *   group 32, 64 or 128; cols % group == 0.
+ *   clamp_min  <= 0 selects the format's default floor.
+ */
+QCAST_API int qcast_per_token(const void* x, int64_t rows, int64_t cols, int fmt, int group,
+                    float clamp_min, void* q, float* sf, void* stream);
+
+/*
+ * Per-token cast to packed FP4 E2M1 ([SPLIT] §四 A format list; [WALK] §3.1
+ * float4_e2m1fn floor). Same as qcast_per_token with fmt = QCAST_FMT_E2M1.
+ *   q_packed [rows, cols/2] bytes; sf [rows, cols/group] fp32.
+ */
+QCAST_API int qcast_e2m1(const void* x, int64_t rows, int64_t cols, int group, float clamp_min,
+               uint8_t* q_packed, float* sf, void* stream);
+
+/*
+ * SwiGLU forward fused with the per-token cast ([WALK] §3.3; [SPLIT] §二
+ * swiglu_forward_and_per_token_cast, §六 step 6).
+ *   h          [rows, 2*cols] bf16: columns [0, cols) are the gate (the SiLU
+ *              input), columns [cols, 2*cols) the up projection.
+ *   row_weight [rows] fp32 routing weight, or NULL for none.
+ *   v[r][j] = (g / (1 + exp(-g))) * u * row_weight[r], fp32, never rounded
+ *   to bf16; then the per-token cast of v with `group`.
+ *   q [rows, cols] E4M3 bytes; sf [rows, cols/group] fp32.
+ *   fmt must be QCAST_FMT_E4M3. The exponential and the division use the
+ *   hardware's fast forms, so the codes may differ from an exact evaluation
+ *   by one step where v lies next to a rounding midpoint.
+ */
+QCAST_API int qcast_swiglu_per_token(const void* h, int64_t rows, int64_t cols, const float* row_weight,
+                           int fmt, int group, float clamp_min, void* q, float* sf,
+                           void* stream);
+
+/*
+ * Per-block cast of a weight ([SPLIT] §二 per_block_cast; [NEWS]
+ * "刚刚！DeepSeek开源高性能GPU算子库TileKernels", item 2, per-block granularity).
+ * One scale per block x block tile.
+ *   x  [rows, cols] bf16; rows % block == 0 and cols % block == 0.
+ *   q  [rows, cols] E4M3 bytes; sf [rows/block, cols/block] fp32.
+ *   block must be 128; fmt must be QCAST_FMT_E4M3.
+ */
+QCAST_API int qcast_per_block(const void* x, int64_t rows, int64_t cols, int fmt, int block,
+                    float clamp_min, void* q, float* sf, void* stream);
+
+/*
+ * Per-channel cast written transposed ([SPLIT] §二 per_channel_cast
+ * (+transpose); it feeds the weight-gradient GEMMs of §三 / §六 steps 12, 15,
+ * which contract over tokens).
+ *   x   [rows, cols] bf16, rows = tokens, cols = channels.
+ *   The scale groups run along tokens: group g of channel c is
+ *   x[g*group .. g*group + group - 1][c].
+ *   qT  [cols, rows] E4M3 bytes: qT[c][t] is the code of x[t][c].
+ *   sf  [cols, rows/group] fp32.
+ *   group must be 128; rows % group == 0; cols % 8 == 0;
+ *   fmt must be QCAST_FMT_E4M3.
+ */
+QCAST_API int qcast_per_channel_T(const void* x, int64_t rows, int64_t cols, int fmt, int group,
+                        float clamp_min, void* qT, float* sf, void* stream);
+
+/* Human-readable name of a status code (static string). */
+QCAST_API const char* qcast_status_str(int status);
+
+/* QCAST_ABI_VERSION of the built library. */
+QCAST_API int qcast_abi_version(void);
+
+/*
+ * Override the compute-unit count used to size the persistent grids
+ * (the pages' config.py get_num_sms() override, [WALK] §1.2). 0 restores the
+ * device's own count. Affects later launches only; results never depend on it.
+ */
+QCAST_API void qcast_set_num_cus(int n);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* QCAST_H */

@@ -1,0 +1,158 @@
+"""MI355X (gfx950) quantization casts: a thin Python binding of libqcast.so.
+
+Each ``qcast_*`` function has the name of the C entry point it calls and does
+argument marshalling only: it checks that tensors are on one GPU and
+contiguous, allocates outputs that were not given, and passes raw pointers
+and torch's current stream. Every step of a cast runs in the HIP kernels; a
+missing library raises ``QcastError``.
+
+Outputs: E4M3 codes as ``torch.float8_e4m3fn`` (one byte per code), E2M1
+codes as ``torch.uint8`` with two codes per byte (low nibble = even column),
+scales as ``torch.float32``.
+
+``per_token_cast(x, fmt='e4m3', num_per_channels=128) -> (out, out_sf)``
+mirrors the call shown in the quick start of the page
+"DeepSeek开源TileKernels：用Python写的GPU算子逼近硬件性能上限".
+"""
+import torch
+
+from ._lib import FMT_E2M1, FMT_E4M3, QcastError, check, fmt_id, load
+
+__all__ = ["qcast_per_token", "qcast_e2m1", "qcast_swiglu_per_token", "qcast_per_block",
+           "qcast_per_channel_T", "qcast_abi_version", "qcast_set_num_cus", "per_token_cast",
+           "QcastError", "FMT_E4M3", "FMT_E2M1"]
+
+
+def _bf16_input(x, name):
+    if not isinstance(x, torch.Tensor) or not x.is_cuda:
+        raise QcastError(1, f"{name} must be a CUDA (HIP) tensor")
+    if x.dtype != torch.bfloat16:
+        raise QcastError(2, f"{name} must be bfloat16, got {x.dtype}")
+    if x.dim() != 2 or not x.is_contiguous():
+        raise QcastError(2, f"{name} must be a contiguous 2-D tensor")
+    return x
+
+
+def _out(t, shape, dtype, device, name):
+    if t is None:
+        return torch.empty(shape, dtype=dtype, device=device)
+    if tuple(t.shape) != tuple(shape) or t.dtype != dtype or t.device != device or \
+            not t.is_contiguous():
+        raise QcastError(2, f"{name} must be a contiguous {dtype} tensor of shape {shape} "
+                            f"on {device}")
+    return t
+
+
+def _stream(device, stream):
+    if stream is not None:
+        return stream.cuda_stream if hasattr(stream, "cuda_stream") else int(stream)
+    return torch.cuda.current_stream(device).cuda_stream
+
+
+def _code_dtype(f):
+    return torch.float8_e4m3fn if f == FMT_E4M3 else torch.uint8
+
+
+def qcast_per_token(x, fmt="e4m3", group=128, clamp_min=0.0, out=None, out_sf=None,
+                    stream=None):
+    """Per-token cast of bf16 ``x [rows, cols]``; see include/qcast.h."""
+    f = fmt_id(fmt)
+    x = _bf16_input(x, "x")
+    rows, cols = x.shape
+    qshape = (rows, cols) if f == FMT_E4M3 else (rows, cols // 2)
+    out = _out(out, qshape, _code_dtype(f), x.device, "out")
+    out_sf = _out(out_sf, (rows, cols // group if group > 0 else 0), torch.float32, x.device,
+                  "out_sf")
+    with torch.cuda.device(x.device):
+        check(load().qcast_per_token(x.data_ptr(), rows, cols, f, group, clamp_min,
+                                     out.data_ptr(), out_sf.data_ptr(), _stream(x.device, stream)),
+              "qcast_per_token")
+    return out, out_sf
+
+
+def qcast_e2m1(x, group=32, clamp_min=0.0, out=None, out_sf=None, stream=None):
+    """Per-token cast to packed E2M1: ``out [rows, cols/2]`` uint8."""
+    x = _bf16_input(x, "x")
+    rows, cols = x.shape
+    out = _out(out, (rows, cols // 2), torch.uint8, x.device, "out")
+    out_sf = _out(out_sf, (rows, cols // group if group > 0 else 0), torch.float32, x.device,
+                  "out_sf")
+    with torch.cuda.device(x.device):
+        check(load().qcast_e2m1(x.data_ptr(), rows, cols, group, clamp_min, out.data_ptr(),
+                                out_sf.data_ptr(), _stream(x.device, stream)), "qcast_e2m1")
+    return out, out_sf
+
+
+def qcast_swiglu_per_token(h, row_weight=None, fmt="e4m3", group=128, clamp_min=0.0, out=None,
+                           out_sf=None, stream=None):
+    """SwiGLU of ``h [rows, 2N]`` (gate | up) times ``row_weight [rows]`` (fp32
+    or None), cast per token: ``out [rows, N]``, ``out_sf [rows, N/group]``."""
+    f = fmt_id(fmt)
+    h = _bf16_input(h, "h")
+    rows, two_n = h.shape
+    if two_n % 2:
+        raise QcastError(2, "h must have an even number of columns (gate | up)")
+    cols = two_n // 2
+    wptr = None
+    if row_weight is not None:
+        if row_weight.dtype != torch.float32 or tuple(row_weight.shape) != (rows,) or \
+                row_weight.device != h.device or not row_weight.is_contiguous():
+            raise QcastError(2, "row_weight must be a contiguous float32 [rows] tensor on h's device")
+        wptr = row_weight.data_ptr()
+    out = _out(out, (rows, cols), _code_dtype(f), h.device, "out")
+    out_sf = _out(out_sf, (rows, cols // group if group > 0 else 0), torch.float32, h.device,
+                  "out_sf")
+    with torch.cuda.device(h.device):
+        check(load().qcast_swiglu_per_token(h.data_ptr(), rows, cols, wptr, f, group, clamp_min,
+                                            out.data_ptr(), out_sf.data_ptr(),
+                                            _stream(h.device, stream)), "qcast_swiglu_per_token")
+    return out, out_sf
+
+
+def qcast_per_block(x, fmt="e4m3", block=128, clamp_min=0.0, out=None, out_sf=None,
+                    stream=None):
+    """One scale per ``block x block`` tile: ``out [rows, cols]``,
+    ``out_sf [rows/block, cols/block]``."""
+    f = fmt_id(fmt)
+    x = _bf16_input(x, "x")
+    rows, cols = x.shape
+    out = _out(out, (rows, cols), _code_dtype(f), x.device, "out")
+    out_sf = _out(out_sf, (rows // block if block > 0 else 0, cols // block if block > 0 else 0),
+                  torch.float32, x.device, "out_sf")
+    with torch.cuda.device(x.device):
+        check(load().qcast_per_block(x.data_ptr(), rows, cols, f, block, clamp_min, out.data_ptr(),
+                                     out_sf.data_ptr(), _stream(x.device, stream)),
+              "qcast_per_block")
+    return out, out_sf
+
+
+def qcast_per_channel_T(x, fmt="e4m3", group=128, clamp_min=0.0, out=None, out_sf=None,
+                        stream=None):
+    """Per-channel cast of ``x [tokens, channels]`` written transposed:
+    ``out [channels, tokens]``, ``out_sf [channels, tokens/group]``."""
+    f = fmt_id(fmt)
+    x = _bf16_input(x, "x")
+    rows, cols = x.shape
+    out = _out(out, (cols, rows), _code_dtype(f), x.device, "out")
+    out_sf = _out(out_sf, (cols, rows // group if group > 0 else 0), torch.float32, x.device,
+                  "out_sf")
+    with torch.cuda.device(x.device):
+        check(load().qcast_per_channel_T(x.data_ptr(), rows, cols, f, group, clamp_min,
+                                         out.data_ptr(), out_sf.data_ptr(),
+                                         _stream(x.device, stream)), "qcast_per_channel_T")
+    return out, out_sf
+
+
+def qcast_abi_version():
+    return load().qcast_abi_version()
+
+
+def qcast_set_num_cus(n):
+    load().qcast_set_num_cus(int(n))
+
+
+def per_token_cast(x, fmt="e4m3", num_per_channels=128):
+    """``(out, out_sf)`` as in the page's quick-start call."""
+    if fmt_id(fmt) == FMT_E2M1:
+        return qcast_e2m1(x, num_per_channels)
+    return qcast_per_token(x, fmt, num_per_channels)

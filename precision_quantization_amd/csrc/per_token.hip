@@ -1,0 +1,106 @@
+// per_token.hip -- per-token cast of bf16 rows to E4M3 or packed E2M1.
+//
+// Operation: the per-token cast of the walk-through page
+// "DeepSeek开源TileKernels：用Python写的GPU算子逼近硬件性能上限", quick start and
+// §3.2 (abs-max over each run of num_per_channels elements of a row, scale
+// and inverse, codes of x * inverse); E2M1 output per §3.1 (float4_e2m1fn).
+//
+// gfx950 design. A contiguous [rows, cols] matrix with cols % G == 0 is one
+// flat stream of groups: group k is elements [kG, kG + G) and owns scale
+// sf[k], whatever the row length. The kernel walks that stream in 16-byte
+// chunks (8 bf16 per lane, one global_load_dwordx4), so a group of G
+// elements is G/8 consecutive lanes inside one DPP row; its abs-max is a
+// 2-4 step DPP reduction in registers and no LDS is touched. Each lane then
+// forms the scale, multiplies its 8 values and converts them with the
+// hardware pack-converts: 8 E4M3 bytes (one dwordx2 store) or 8 E2M1 nibbles
+// (one dword store). The first lane of each group stores the scale.
+// A workgroup keeps kUnroll chunks per lane in flight before using any.
+#include "qcast_device.h"
+#include "qcast_kernels.h"
+
+namespace qcast {
+namespace {
+
+constexpr int kUnroll = 4;
+
+template <int kLanes, int kFmt>
+__global__ __launch_bounds__(kThreads) void per_token_kernel(
+    const u32x4* __restrict__ x, int64_t nchunks, float floor, uint8_t* __restrict__ q,
+    float* __restrict__ sf) {
+  constexpr float kMax = (kFmt == kE4M3) ? kE4M3Max : kE2M1Max;
+  const int64_t step = (int64_t)gridDim.x * kThreads * kUnroll;
+  for (int64_t base = (int64_t)blockIdx.x * kThreads * kUnroll + threadIdx.x; base < nchunks;
+       base += step) {
+    u32x4 raw[kUnroll];
+#pragma unroll
+    for (int u = 0; u < kUnroll; ++u) {
+      const int64_t c = base + (int64_t)u * kThreads;
+      if (c < nchunks) raw[u] = load_stream(x + c);
+    }
+#pragma unroll
+    for (int u = 0; u < kUnroll; ++u) {
+      const int64_t c = base + (int64_t)u * kThreads;
+      // Whole groups are in or out together: nchunks is a multiple of kLanes
+      // and c % 64 equals the lane index.
+      if (c < nchunks) {
+        float v[8];
+        unpack8(raw[u], v);
+        const float amax = lane_group_max<kLanes>(absmax8(v));
+        const Scale s = group_scale(amax, floor, kMax);
+        float y[8];
+#pragma unroll
+        for (int i = 0; i < 8; ++i) y[i] = v[i] * s.inv;
+        if (kFmt == kE4M3) {
+          u32x2 out;
+          out.x = e4m3x4(y[0], y[1], y[2], y[3]);
+          out.y = e4m3x4(y[4], y[5], y[6], y[7]);
+          store_stream(reinterpret_cast<u32x2*>(q) + c, out);
+        } else {
+          store_stream(reinterpret_cast<uint32_t*>(q) + c, e2m1x8(y));
+        }
+        if ((threadIdx.x & (kLanes - 1)) == 0) sf[c / kLanes] = s.sf;
+      }
+    }
+  }
+}
+
+template <int kLanes, int kFmt>
+hipError_t launch(const void* x, int64_t nchunks, float floor, void* q, float* sf,
+                  hipStream_t stream, const LaunchCaps& caps) {
+  const int64_t per_block_iter = (int64_t)kThreads * kUnroll;
+  const int64_t iters = (nchunks + per_block_iter - 1) / per_block_iter;
+  // Persistent grid: at most 8 workgroups per CU; the same number of
+  // iterations for every workgroup.
+  const int64_t max_blocks = (int64_t)caps.num_cus * 8;
+  const int64_t iters_per_block = (iters + max_blocks - 1) / max_blocks;
+  const int64_t blocks = (iters + iters_per_block - 1) / iters_per_block;
+  hipLaunchKernelGGL((per_token_kernel<kLanes, kFmt>), dim3((unsigned)blocks), dim3(kThreads), 0,
+                     stream, static_cast<const u32x4*>(x), nchunks, floor,
+                     static_cast<uint8_t*>(q), sf);
+  return hipGetLastError();
+}
+
+}  // namespace
+
+hipError_t launch_per_token(const void* x, int64_t rows, int64_t cols, int fmt, int group,
+                            float floor, void* q, float* sf, hipStream_t stream,
+                            const LaunchCaps& caps) {
+  const int64_t nchunks = rows * cols / 8;
+  if (nchunks == 0) return hipSuccess;
+  if (fmt == kE4M3) {
+    switch (group) {
+      case 32: return launch<4, kE4M3>(x, nchunks, floor, q, sf, stream, caps);
+      case 64: return launch<8, kE4M3>(x, nchunks, floor, q, sf, stream, caps);
+      case 128: return launch<16, kE4M3>(x, nchunks, floor, q, sf, stream, caps);
+    }
+  } else {
+    switch (group) {
+      case 32: return launch<4, kE2M1>(x, nchunks, floor, q, sf, stream, caps);
+      case 64: return launch<8, kE2M1>(x, nchunks, floor, q, sf, stream, caps);
+      case 128: return launch<16, kE2M1>(x, nchunks, floor, q, sf, stream, caps);
+    }
+  }
+  return hipErrorInvalidValue;
+}
+
+}  // namespace qcast

@@ -1,0 +1,158 @@
+// qcast_abi.hip -- the C ABI declared in include/qcast.h: argument checks,
+// the format floors, the compute-unit count, and dispatch to the launchers.
+//
+// Floors ("DeepSeek开源TileKernels：用Python写的GPU算子逼近硬件性能上限", §3.1):
+// 1e-4 for E4M3 and the E2M1 maximum times 2^-126 for E2M1, unless the caller
+// passes its own clamp_min > 0.
+#include <atomic>
+
+#include "qcast.h"
+#include "qcast_device.h"
+#include "qcast_kernels.h"
+
+namespace {
+
+constexpr int kMaxDevices = 64;
+std::atomic<int> g_cu_count[kMaxDevices];   // 0 = not queried yet
+std::atomic<int> g_cu_override{0};
+
+bool aligned(const void* p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p) & (a - 1)) == 0; }
+
+float default_floor(int fmt) {
+  if (fmt == QCAST_FMT_E4M3) return 1e-4f;
+  return 6.0f * 0x1.0p-126f;   // E2M1 maximum times 2^-126
+}
+
+float floor_for(int fmt, float clamp_min) { return clamp_min > 0.0f ? clamp_min : default_floor(fmt); }
+
+int caps_for_current_device(qcast::LaunchCaps* caps) {
+  const int override_n = g_cu_override.load(std::memory_order_relaxed);
+  if (override_n > 0) {
+    caps->num_cus = override_n;
+    return QCAST_OK;
+  }
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0) return QCAST_ERR_DEVICE;
+  if (dev < kMaxDevices) {
+    int n = g_cu_count[dev].load(std::memory_order_relaxed);
+    if (n <= 0) {
+      if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
+          n <= 0)
+        return QCAST_ERR_DEVICE;
+      g_cu_count[dev].store(n, std::memory_order_relaxed);
+    }
+    caps->num_cus = n;
+    return QCAST_OK;
+  }
+  int n = 0;
+  if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0)
+    return QCAST_ERR_DEVICE;
+  caps->num_cus = n;
+  return QCAST_OK;
+}
+
+int finish(hipError_t err) { return err == hipSuccess ? QCAST_OK : QCAST_ERR_LAUNCH; }
+
+bool per_token_group_ok(int group) { return group == 32 || group == 64 || group == 128; }
+
+// Element counts beyond 2^62 would overflow the kernels' int64 offsets.
+bool too_big(int64_t rows, int64_t cols) {
+  return cols > 0 && rows > (int64_t(1) << 62) / cols;
+}
+
+}  // namespace
+
+extern "C" {
+
+int qcast_abi_version(void) { return QCAST_ABI_VERSION; }
+
+const char* qcast_status_str(int status) {
+  switch (status) {
+    case QCAST_OK: return "ok";
+    case QCAST_ERR_NULL: return "a required pointer is NULL";
+    case QCAST_ERR_SHAPE: return "unsupported shape (negative, or not divisible as required)";
+    case QCAST_ERR_ALIGN: return "pointer not aligned as required";
+    case QCAST_ERR_FORMAT: return "format not supported by this entry point";
+    case QCAST_ERR_GROUP: return "group or block size not supported";
+    case QCAST_ERR_LAUNCH: return "kernel launch failed";
+    case QCAST_ERR_DEVICE: return "no usable HIP device";
+  }
+  return "unknown status";
+}
+
+void qcast_set_num_cus(int n) { g_cu_override.store(n > 0 ? n : 0, std::memory_order_relaxed); }
+
+int qcast_per_token(const void* x, int64_t rows, int64_t cols, int fmt, int group,
+                    float clamp_min, void* q, float* sf, void* stream) {
+  if (fmt != QCAST_FMT_E4M3 && fmt != QCAST_FMT_E2M1) return QCAST_ERR_FORMAT;
+  if (!per_token_group_ok(group)) return QCAST_ERR_GROUP;
+  if (rows < 0 || cols < 0 || cols % group != 0 || too_big(rows, cols)) return QCAST_ERR_SHAPE;
+  if (rows == 0 || cols == 0) return QCAST_OK;
+  if (!x || !q || !sf) return QCAST_ERR_NULL;
+  if (!aligned(x, 16) || !aligned(q, 16) || !aligned(sf, 4)) return QCAST_ERR_ALIGN;
+  qcast::LaunchCaps caps;
+  const int rc = caps_for_current_device(&caps);
+  if (rc != QCAST_OK) return rc;
+  return finish(qcast::launch_per_token(x, rows, cols, fmt, group, floor_for(fmt, clamp_min), q,
+                                        sf, static_cast<hipStream_t>(stream), caps));
+}
+
+int qcast_e2m1(const void* x, int64_t rows, int64_t cols, int group, float clamp_min,
+               uint8_t* q_packed, float* sf, void* stream) {
+  return qcast_per_token(x, rows, cols, QCAST_FMT_E2M1, group, clamp_min, q_packed, sf, stream);
+}
+
+int qcast_swiglu_per_token(const void* h, int64_t rows, int64_t cols, const float* row_weight,
+                           int fmt, int group, float clamp_min, void* q, float* sf,
+                           void* stream) {
+  if (fmt != QCAST_FMT_E4M3) return QCAST_ERR_FORMAT;
+  if (!per_token_group_ok(group)) return QCAST_ERR_GROUP;
+  if (rows < 0 || cols < 0 || cols % group != 0 || cols / 8 >= (int64_t(1) << 16) ||
+      too_big(rows, 2 * cols))
+    return QCAST_ERR_SHAPE;
+  if (rows == 0 || cols == 0) return QCAST_OK;
+  if (!h || !q || !sf) return QCAST_ERR_NULL;
+  if (!aligned(h, 16) || !aligned(q, 16) || !aligned(sf, 4) ||
+      (row_weight && !aligned(row_weight, 4)))
+    return QCAST_ERR_ALIGN;
+  qcast::LaunchCaps caps;
+  const int rc = caps_for_current_device(&caps);
+  if (rc != QCAST_OK) return rc;
+  return finish(qcast::launch_swiglu_per_token(h, rows, cols, row_weight, group,
+                                               floor_for(fmt, clamp_min), q, sf,
+                                               static_cast<hipStream_t>(stream), caps));
+}
+
+int qcast_per_block(const void* x, int64_t rows, int64_t cols, int fmt, int block,
+                    float clamp_min, void* q, float* sf, void* stream) {
+  if (fmt != QCAST_FMT_E4M3) return QCAST_ERR_FORMAT;
+  if (block != 128) return QCAST_ERR_GROUP;
+  if (rows < 0 || cols < 0 || rows % block != 0 || cols % block != 0 || too_big(rows, cols))
+    return QCAST_ERR_SHAPE;
+  if (rows == 0 || cols == 0) return QCAST_OK;
+  if (!x || !q || !sf) return QCAST_ERR_NULL;
+  if (!aligned(x, 16) || !aligned(q, 16) || !aligned(sf, 4)) return QCAST_ERR_ALIGN;
+  qcast::LaunchCaps caps;
+  const int rc = caps_for_current_device(&caps);
+  if (rc != QCAST_OK) return rc;
+  return finish(qcast::launch_per_block(x, rows, cols, floor_for(fmt, clamp_min), q, sf,
+                                        static_cast<hipStream_t>(stream), caps));
+}
+
+int qcast_per_channel_T(const void* x, int64_t rows, int64_t cols, int fmt, int group,
+                        float clamp_min, void* qT, float* sf, void* stream) {
+  if (fmt != QCAST_FMT_E4M3) return QCAST_ERR_FORMAT;
+  if (group != 128) return QCAST_ERR_GROUP;
+  if (rows < 0 || cols < 0 || rows % group != 0 || cols % 8 != 0 || too_big(rows, cols))
+    return QCAST_ERR_SHAPE;
+  if (rows == 0 || cols == 0) return QCAST_OK;
+  if (!x || !qT || !sf) return QCAST_ERR_NULL;
+  if (!aligned(x, 16) || !aligned(qT, 16) || !aligned(sf, 4)) return QCAST_ERR_ALIGN;
+  qcast::LaunchCaps caps;
+  const int rc = caps_for_current_device(&caps);
+  if (rc != QCAST_OK) return rc;
+  return finish(qcast::launch_per_channel_T(x, rows, cols, floor_for(fmt, clamp_min), qT, sf,
+                                            static_cast<hipStream_t>(stream), caps));
+}
+
+}  // extern "C"

@@ -1,0 +1,121 @@
+// qcast_device.h -- device helpers shared by the gfx950 cast kernels.
+//
+// The scale rule follows the per-token cast of the walk-through page
+// "DeepSeek开源TileKernels：用Python写的GPU算子逼近硬件性能上限" (§3.1 floors,
+// §3.2 abs-max -> scale and inverse -> x * inverse): a = max(amax, floor),
+// sf = a / fmt_max, sf_inv = 1 / sf, both IEEE fp32 divisions, and every code
+// is the hardware conversion of the fp32 product x * sf_inv.
+//
+// gfx950 conversions used (unit scale, round to nearest even):
+//   v_cvt_pk_fp8_f32           two fp32 -> two OCP E4M3FN bytes (src0 -> the
+//                              lower byte of the selected 16-bit half)
+//   v_cvt_scalef32_pk_fp4_f32  two fp32 / scale -> two E2M1 nibbles in the
+//                              selected byte (src0 -> low nibble); scale 1.0
+// With |x * sf_inv| <= 448 * (1 + 2^-22) (resp. 6 * (1 + 2^-22)) every value
+// that reaches a conversion rounds inside the format, so the result is the
+// nearest-even code with the sign kept.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace qcast {
+
+constexpr int kThreads = 256;          // 4 wave64s per workgroup
+constexpr float kE4M3Max = 448.0f;
+constexpr float kE2M1Max = 6.0f;
+
+enum Fmt : int { kE4M3 = 1, kE2M1 = 2 };
+
+// Native vector types (the nontemporal builtins take these, not HIP's
+// struct-wrapped uint4).
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+
+struct Scale {
+  float sf;
+  float inv;
+};
+
+// a = max(amax, floor); sf = a / fmt_max; inv = 1 / sf (IEEE divisions:
+// the library is built with correctly rounded fp32 division).
+__device__ __forceinline__ Scale group_scale(float amax, float floor, float fmt_max) {
+  const float a = amax < floor ? floor : amax;
+  Scale s;
+  s.sf = a / fmt_max;
+  s.inv = 1.0f / s.sf;
+  return s;
+}
+
+// bf16 pair in one dword -> two fp32 (exact: a bf16 is the top half of an fp32).
+__device__ __forceinline__ float bf16_lo(uint32_t w) { return __uint_as_float(w << 16); }
+__device__ __forceinline__ float bf16_hi(uint32_t w) { return __uint_as_float(w & 0xffff0000u); }
+
+__device__ __forceinline__ void unpack8(const u32x4& r, float v[8]) {
+  v[0] = bf16_lo(r.x); v[1] = bf16_hi(r.x);
+  v[2] = bf16_lo(r.y); v[3] = bf16_hi(r.y);
+  v[4] = bf16_lo(r.z); v[5] = bf16_hi(r.z);
+  v[6] = bf16_lo(r.w); v[7] = bf16_hi(r.w);
+}
+
+__device__ __forceinline__ float absmax8(const float v[8]) {
+  float m = fabsf(v[0]);
+#pragma unroll
+  for (int i = 1; i < 8; ++i) m = fmaxf(m, fabsf(v[i]));
+  return m;
+}
+
+// Cross-lane moves inside a DPP row of 16 lanes.
+template <int kCtrl>
+__device__ __forceinline__ float dpp(float v) {
+  return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), kCtrl, 0xF, 0xF, false));
+}
+constexpr int kDppXor1 = 0xB1;         // quad_perm [1,0,3,2]
+constexpr int kDppXor2 = 0x4E;         // quad_perm [2,3,0,1]
+constexpr int kDppHalfMirror = 0x141;  // lane i <-> 7-i inside each 8 lanes
+constexpr int kDppMirror = 0x140;      // lane i <-> 15-i inside each 16 lanes
+constexpr int kDppRor8 = 0x128;        // lane i <- (i+8) mod 16
+
+// Max over aligned runs of kLanes lanes (4, 8 or 16); every lane of a run
+// ends with the run's maximum. Runs never straddle a DPP row.
+template <int kLanes>
+__device__ __forceinline__ float lane_group_max(float m) {
+  static_assert(kLanes == 4 || kLanes == 8 || kLanes == 16, "4, 8 or 16 lanes");
+  m = fmaxf(m, dpp<kDppXor1>(m));
+  m = fmaxf(m, dpp<kDppXor2>(m));
+  if (kLanes >= 8) m = fmaxf(m, dpp<kDppHalfMirror>(m));
+  if (kLanes >= 16) m = fmaxf(m, dpp<kDppMirror>(m));
+  return m;
+}
+
+// Max over the whole wave64; every lane gets it.
+__device__ __forceinline__ float wave_max(float m) {
+  m = lane_group_max<16>(m);
+  m = fmaxf(m, __shfl_xor(m, 16));
+  m = fmaxf(m, __shfl_xor(m, 32));
+  return m;
+}
+
+// Four fp32 -> four E4M3 bytes (v0 in the lowest byte).
+__device__ __forceinline__ uint32_t e4m3x4(float v0, float v1, float v2, float v3) {
+  uint32_t w = __builtin_amdgcn_cvt_pk_fp8_f32(v0, v1, 0u, false);
+  return __builtin_amdgcn_cvt_pk_fp8_f32(v2, v3, w, true);
+}
+
+// Eight fp32 -> eight E2M1 nibbles (v0 in the lowest nibble).
+__device__ __forceinline__ uint32_t e2m1x8(const float y[8]) {
+  uint32_t w = 0u;
+  w = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(w, y[0], y[1], 1.0f, 0);
+  w = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(w, y[2], y[3], 1.0f, 1);
+  w = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(w, y[4], y[5], 1.0f, 2);
+  w = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(w, y[6], y[7], 1.0f, 3);
+  return w;
+}
+
+// Streaming accesses: the data is touched once.
+template <typename T>
+__device__ __forceinline__ T load_stream(const T* p) { return __builtin_nontemporal_load(p); }
+template <typename T>
+__device__ __forceinline__ void store_stream(T* p, T v) { __builtin_nontemporal_store(v, p); }
+
+}  // namespace qcast

@@ -1,0 +1,134 @@
+// swiglu.hip -- SwiGLU forward fused with the per-token E4M3 cast.
+//
+// Operation: swiglu_forward_and_per_token_cast of the walk-through page
+// "DeepSeek开源TileKernels：用Python写的GPU算子逼近硬件性能上限", §3.3: with the
+// left half of each row as the gate g and the right half as the up value u,
+// v = g / (1 + exp(-g)) * u * w[row] in fp32, then the per-token cast of v
+// (§3.2). The page's point is that the unfused form costs three launches,
+// each reading and writing the whole tensor; here v lives only in registers.
+//
+// gfx950 design. Output chunk c (8 consecutive outputs of one row) needs two
+// 16-byte loads: 8 gate values and the 8 up values cols further on. The
+// output stream is walked like the per-token cast (G/8 lanes per group, DPP
+// abs-max), so the row of chunk c comes from a multiply-shift division by
+// the chunks per row. exp(-g) is the hardware base-2 exponential of
+// -g * log2(e), and the division by 1 + exp(-g) is a multiply by the
+// hardware reciprocal: together a few ulps from the exact fp32 expression,
+// which moves a code only where v lies next to a rounding midpoint. When
+// exp(-g) overflows, the reciprocal is 0 and v is a zero of the right sign,
+// as in the exact expression.
+#include "qcast_device.h"
+#include "qcast_kernels.h"
+
+namespace qcast {
+namespace {
+
+constexpr int kUnroll = 2;
+constexpr float kLog2e = 1.4426950408889634f;
+// Chunk-to-row division: row = (c * magic) >> 40 is exact for c < 2^24 and
+// chunks-per-row d < 2^16 when magic = ceil(2^40 / d).
+constexpr int64_t kMaxChunksPerLaunch = int64_t(1) << 24;
+constexpr int64_t kMaxChunksPerRow = int64_t(1) << 16;
+
+__device__ __forceinline__ float silu_times(float g, float u) {
+  const float e = __builtin_amdgcn_exp2f(-g * kLog2e);
+  return g * __builtin_amdgcn_rcpf(1.0f + e) * u;
+}
+
+template <int kLanes, bool kWeighted>
+__global__ __launch_bounds__(kThreads) void swiglu_kernel(
+    const uint16_t* __restrict__ h, const float* __restrict__ w, int64_t nchunks,
+    uint32_t chunks_per_row, uint64_t row_magic, int64_t cols, float floor,
+    uint8_t* __restrict__ q, float* __restrict__ sf) {
+  const int64_t step = (int64_t)gridDim.x * kThreads * kUnroll;
+  for (int64_t base = (int64_t)blockIdx.x * kThreads * kUnroll + threadIdx.x; base < nchunks;
+       base += step) {
+    u32x4 graw[kUnroll], uraw[kUnroll];
+    float wr[kUnroll];
+#pragma unroll
+    for (int u = 0; u < kUnroll; ++u) {
+      const int64_t c = base + (int64_t)u * kThreads;
+      if (c < nchunks) {
+        const uint32_t row = (uint32_t)(((uint64_t)c * row_magic) >> 40);
+        const uint32_t jc = (uint32_t)c - row * chunks_per_row;
+        const u32x4* g = reinterpret_cast<const u32x4*>(h + (int64_t)row * 2 * cols) + jc;
+        graw[u] = load_stream(g);
+        uraw[u] = load_stream(g + chunks_per_row);
+        wr[u] = kWeighted ? w[row] : 1.0f;
+      }
+    }
+#pragma unroll
+    for (int u = 0; u < kUnroll; ++u) {
+      const int64_t c = base + (int64_t)u * kThreads;
+      if (c < nchunks) {
+        float gv[8], uv[8], v[8];
+        unpack8(graw[u], gv);
+        unpack8(uraw[u], uv);
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+          v[i] = silu_times(gv[i], uv[i]);
+          if (kWeighted) v[i] = v[i] * wr[u];
+        }
+        const float amax = lane_group_max<kLanes>(absmax8(v));
+        const Scale s = group_scale(amax, floor, kE4M3Max);
+        u32x2 out;
+        out.x = e4m3x4(v[0] * s.inv, v[1] * s.inv, v[2] * s.inv, v[3] * s.inv);
+        out.y = e4m3x4(v[4] * s.inv, v[5] * s.inv, v[6] * s.inv, v[7] * s.inv);
+        store_stream(reinterpret_cast<u32x2*>(q) + c, out);
+        if ((threadIdx.x & (kLanes - 1)) == 0) sf[c / kLanes] = s.sf;
+      }
+    }
+  }
+}
+
+template <int kLanes, bool kWeighted>
+hipError_t launch(const uint16_t* h, const float* w, int64_t rows, int64_t cols, float floor,
+                  uint8_t* q, float* sf, hipStream_t stream, const LaunchCaps& caps) {
+  const int64_t cpr = cols / 8;
+  const uint64_t magic = ((uint64_t(1) << 40) + (uint64_t)cpr - 1) / (uint64_t)cpr;
+  const int64_t groups_per_row = cols / (kLanes * 8);
+  // Slabs of whole rows, each under 2^24 chunks, keep the division exact.
+  const int64_t slab_rows = kMaxChunksPerLaunch / cpr;
+  for (int64_t r0 = 0; r0 < rows; r0 += slab_rows) {
+    const int64_t nr = rows - r0 < slab_rows ? rows - r0 : slab_rows;
+    const int64_t nchunks = nr * cpr;
+    const int64_t per_block_iter = (int64_t)kThreads * kUnroll;
+    const int64_t iters = (nchunks + per_block_iter - 1) / per_block_iter;
+    const int64_t max_blocks = (int64_t)caps.num_cus * 8;
+    const int64_t iters_per_block = (iters + max_blocks - 1) / max_blocks;
+    const int64_t blocks = (iters + iters_per_block - 1) / iters_per_block;
+    hipLaunchKernelGGL((swiglu_kernel<kLanes, kWeighted>), dim3((unsigned)blocks),
+                       dim3(kThreads), 0, stream, h + r0 * 2 * cols,
+                       kWeighted ? w + r0 : nullptr, nchunks, (uint32_t)cpr, magic, cols, floor,
+                       q + r0 * cols, sf + r0 * groups_per_row);
+    const hipError_t err = hipGetLastError();
+    if (err != hipSuccess) return err;
+  }
+  return hipSuccess;
+}
+
+template <int kLanes>
+hipError_t launch_w(const uint16_t* h, const float* w, int64_t rows, int64_t cols, float floor,
+                    uint8_t* q, float* sf, hipStream_t stream, const LaunchCaps& caps) {
+  return w ? launch<kLanes, true>(h, w, rows, cols, floor, q, sf, stream, caps)
+           : launch<kLanes, false>(h, w, rows, cols, floor, q, sf, stream, caps);
+}
+
+}  // namespace
+
+hipError_t launch_swiglu_per_token(const void* h, int64_t rows, int64_t cols, const float* w,
+                                   int group, float floor, void* q, float* sf,
+                                   hipStream_t stream, const LaunchCaps& caps) {
+  if (rows == 0 || cols == 0) return hipSuccess;
+  if (cols / 8 >= kMaxChunksPerRow) return hipErrorInvalidValue;
+  const uint16_t* hp = static_cast<const uint16_t*>(h);
+  uint8_t* qp = static_cast<uint8_t*>(q);
+  switch (group) {
+    case 32: return launch_w<4>(hp, w, rows, cols, floor, qp, sf, stream, caps);
+    case 64: return launch_w<8>(hp, w, rows, cols, floor, qp, sf, stream, caps);
+    case 128: return launch_w<16>(hp, w, rows, cols, floor, qp, sf, stream, caps);
+  }
+  return hipErrorInvalidValue;
+}
+
+}  // namespace qcast

@@ -1,0 +1,142 @@
+"""The C ABI without a GPU: the library loads, exports every function that
+include/qcast.h declares, and rejects bad arguments before any HIP call.
+
+No test here passes a pointer that a kernel could dereference: rejected calls
+return before launching, and the one call that would get past validation is
+made only on a host without a GPU (it must then report QCAST_ERR_DEVICE).
+"""
+import ctypes
+import os
+import re
+import subprocess
+
+import pytest
+
+from conftest import ROOT, gpu_available
+
+HEADER = os.path.join(ROOT, "include", "qcast.h")
+
+OK, ERR_NULL, ERR_SHAPE, ERR_ALIGN, ERR_FORMAT, ERR_GROUP, ERR_LAUNCH, ERR_DEVICE = range(8)
+E4M3, E2M1 = 1, 2
+A16 = 0x10000          # aligned, never dereferenced (rejected before use)
+MIS = 0x10008          # 8-byte aligned only
+
+
+@pytest.fixture(scope="module")
+def lib():
+    from precision_quantization_amd import _lib
+    return _lib.load()
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    return re.findall(r"QCAST_API\s+[\w\s\*]+?\b(qcast_\w+)\s*\(", text)
+
+
+def test_header_declares_the_five_casts():
+    names = declared_functions()
+    for n in ["qcast_per_token", "qcast_swiglu_per_token", "qcast_per_block",
+              "qcast_per_channel_T", "qcast_e2m1"]:
+        assert n in names
+
+
+def test_library_exports_every_declared_symbol_and_nothing_else():
+    from precision_quantization_amd import build
+    out = subprocess.run(["nm", "-D", "--defined-only", build.LIB], capture_output=True,
+                         text=True, check=True).stdout
+    exported = {l.split()[-1] for l in out.splitlines() if " T " in l}
+    assert exported == set(declared_functions())
+
+
+def test_binding_names_match_the_c_entry_points():
+    import precision_quantization_amd as pq
+    for n in declared_functions():
+        if n != "qcast_status_str":
+            assert callable(getattr(pq, n)), n
+
+
+def test_abi_version_and_status_strings(lib):
+    assert lib.qcast_abi_version() == 1
+    for s in range(8):
+        assert lib.qcast_status_str(s).decode()
+    assert lib.qcast_status_str(99).decode() == "unknown status"
+
+
+def pt(lib, x=A16, rows=4, cols=256, fmt=E4M3, group=128, q=A16, sf=A16):
+    return lib.qcast_per_token(x, rows, cols, fmt, group, 0.0, q, sf, None)
+
+
+def test_per_token_validation(lib):
+    assert pt(lib, fmt=3) == ERR_FORMAT
+    assert pt(lib, group=16) == ERR_GROUP
+    assert pt(lib, group=256) == ERR_GROUP
+    assert pt(lib, cols=200) == ERR_SHAPE
+    assert pt(lib, rows=-1) == ERR_SHAPE
+    assert pt(lib, rows=2 ** 60, cols=2 ** 10) == ERR_SHAPE        # element count overflow
+    assert pt(lib, x=None) == ERR_NULL
+    assert pt(lib, q=None) == ERR_NULL
+    assert pt(lib, sf=None) == ERR_NULL
+    assert pt(lib, x=MIS) == ERR_ALIGN
+    assert pt(lib, q=MIS) == ERR_ALIGN
+    assert pt(lib, sf=A16 + 2) == ERR_ALIGN
+    # empty inputs are valid and launch nothing, even with null pointers
+    assert pt(lib, rows=0, x=None, q=None, sf=None) == OK
+    assert pt(lib, cols=0, x=None, q=None, sf=None) == OK
+
+
+def test_e2m1_validation(lib):
+    assert lib.qcast_e2m1(A16, 4, 256, 16, 0.0, A16, A16, None) == ERR_GROUP
+    assert lib.qcast_e2m1(A16, 4, 48, 32, 0.0, A16, A16, None) == ERR_SHAPE
+    assert lib.qcast_e2m1(None, 4, 64, 32, 0.0, A16, A16, None) == ERR_NULL
+    assert lib.qcast_e2m1(None, 0, 64, 32, 0.0, None, None, None) == OK
+
+
+def test_swiglu_validation(lib):
+    f = lib.qcast_swiglu_per_token
+    assert f(A16, 4, 256, None, E2M1, 32, 0.0, A16, A16, None) == ERR_FORMAT
+    assert f(A16, 4, 256, None, E4M3, 100, 0.0, A16, A16, None) == ERR_GROUP
+    assert f(A16, 4, 200, None, E4M3, 128, 0.0, A16, A16, None) == ERR_SHAPE
+    assert f(A16, 4, 1 << 19, None, E4M3, 128, 0.0, A16, A16, None) == ERR_SHAPE  # row too long
+    assert f(None, 4, 256, None, E4M3, 128, 0.0, A16, A16, None) == ERR_NULL
+    assert f(A16, 4, 256, A16 + 2, E4M3, 128, 0.0, A16, A16, None) == ERR_ALIGN
+    assert f(None, 0, 256, None, E4M3, 128, 0.0, None, None, None) == OK
+
+
+def test_per_block_validation(lib):
+    f = lib.qcast_per_block
+    assert f(A16, 256, 256, E2M1, 128, 0.0, A16, A16, None) == ERR_FORMAT
+    assert f(A16, 256, 256, E4M3, 64, 0.0, A16, A16, None) == ERR_GROUP
+    assert f(A16, 200, 256, E4M3, 128, 0.0, A16, A16, None) == ERR_SHAPE
+    assert f(A16, 256, 200, E4M3, 128, 0.0, A16, A16, None) == ERR_SHAPE
+    assert f(A16, 256, 256, E4M3, 128, 0.0, None, A16, None) == ERR_NULL
+    assert f(A16, 256, 256, E4M3, 128, 0.0, MIS, A16, None) == ERR_ALIGN
+
+
+def test_per_channel_T_validation(lib):
+    f = lib.qcast_per_channel_T
+    assert f(A16, 256, 64, E2M1, 128, 0.0, A16, A16, None) == ERR_FORMAT
+    assert f(A16, 256, 64, E4M3, 64, 0.0, A16, A16, None) == ERR_GROUP
+    assert f(A16, 200, 64, E4M3, 128, 0.0, A16, A16, None) == ERR_SHAPE
+    assert f(A16, 256, 60, E4M3, 128, 0.0, A16, A16, None) == ERR_SHAPE
+    assert f(A16, 256, 64, E4M3, 128, 0.0, A16, None, None) == ERR_NULL
+    assert f(MIS, 256, 64, E4M3, 128, 0.0, A16, A16, None) == ERR_ALIGN
+
+
+@pytest.mark.skipif(gpu_available(), reason="only meaningful on a host without a GPU")
+def test_valid_call_without_a_device_reports_device_error(lib):
+    assert pt(lib) == ERR_DEVICE
+
+
+def test_binding_rejects_cpu_tensors():
+    import torch
+    import precision_quantization_amd as pq
+    with pytest.raises(pq.QcastError):
+        pq.qcast_per_token(torch.zeros(4, 128, dtype=torch.bfloat16))
+
+
+def test_missing_library_fails_loudly(monkeypatch, tmp_path):
+    from precision_quantization_amd import _lib, build
+    monkeypatch.setattr(build, "LIB", str(tmp_path / "libqcast.so"))
+    monkeypatch.setattr(_lib, "_lib", None)
+    with pytest.raises(_lib.QcastError):
+        _lib.load()

@@ -1,0 +1,353 @@
+"""GPU parity: the HIP casts against the CPU oracle on the same seeded inputs.
+
+Pure casts (per-token E4M3/E2M1, per-block, per-channel transposed) must be
+bit-exact in every code byte and every fp32 scale. The SwiGLU-fused cast uses
+the hardware exponential and reciprocal, so it is held to a tolerance: codes
+at most one step apart on at most 0.1% of the elements, scales within a
+relative 1e-6, dequantized values within 2^-3 of the group abs-max.
+
+Every call goes through the C ABI (the ctypes binding), with outputs
+poisoned beforehand so that an unwritten byte cannot pass.
+"""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import precision_quantization_amd as pq
+from precision_quantization_amd import workloads
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module")
+def dev():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    return torch.device("cuda:0")
+
+
+def codes_np(t):
+    return t.view(torch.uint8).cpu().numpy()
+
+
+def sf_bits(t):
+    return t.cpu().numpy().view(np.uint32)
+
+
+def poisoned(shape, dtype, dev, byte):
+    t = torch.empty(shape, dtype=dtype, device=dev)
+    t.view(torch.uint8).fill_(byte)
+    return t
+
+
+def gpu_cast(op, x, dev, fmt="e4m3", group=128, w=None, poison=0xAA):
+    """Run one cast on the GPU with poisoned outputs; numpy codes + scales."""
+    xd = x.to(dev)
+    rows, cols = x.shape
+    code_dt = torch.float8_e4m3fn if fmt == "e4m3" else torch.uint8
+    if op == "per_token" or op == "e2m1":
+        qs = (rows, cols) if fmt == "e4m3" else (rows, cols // 2)
+        out = poisoned(qs, code_dt, dev, poison)
+        sf = poisoned((rows, cols // group), torch.float32, dev, poison)
+        if op == "e2m1":
+            pq.qcast_e2m1(xd, group, out=out, out_sf=sf)
+        else:
+            pq.qcast_per_token(xd, fmt, group, out=out, out_sf=sf)
+    elif op == "swiglu_per_token":
+        n = cols // 2
+        out = poisoned((rows, n), code_dt, dev, poison)
+        sf = poisoned((rows, n // group), torch.float32, dev, poison)
+        pq.qcast_swiglu_per_token(xd, None if w is None else w.to(dev), fmt, group, out=out,
+                                  out_sf=sf)
+    elif op == "per_block":
+        out = poisoned((rows, cols), code_dt, dev, poison)
+        sf = poisoned((rows // group, cols // group), torch.float32, dev, poison)
+        pq.qcast_per_block(xd, fmt, group, out=out, out_sf=sf)
+    elif op == "per_channel_T":
+        out = poisoned((cols, rows), code_dt, dev, poison)
+        sf = poisoned((cols, rows // group), torch.float32, dev, poison)
+        pq.qcast_per_channel_T(xd, fmt, group, out=out, out_sf=sf)
+    else:
+        raise ValueError(op)
+    torch.cuda.synchronize()
+    return codes_np(out), sf.cpu().numpy()
+
+
+def oracle_cast(op, x, fmt="e4m3", group=128, w=None):
+    xb = workloads.bf16_bits(x)
+    if op == "per_token":
+        return oracle.per_token(xb, fmt, group)
+    if op == "e2m1":
+        return oracle.e2m1(xb, group)
+    if op == "swiglu_per_token":
+        return oracle.swiglu_per_token(xb, None if w is None else w.numpy(), fmt, group)
+    if op == "per_block":
+        return oracle.per_block(xb, fmt, group)
+    if op == "per_channel_T":
+        return oracle.per_channel_T(xb, fmt, group)
+    raise ValueError(op)
+
+
+def assert_exact(op, x, dev, fmt="e4m3", group=128, poisons=(0xAA,)):
+    q_ref, sf_ref = oracle_cast(op, x, fmt, group)
+    for p in poisons:
+        q, sf = gpu_cast(op, x, dev, fmt, group, poison=p)
+        bad = np.nonzero(q != q_ref)
+        assert bad[0].size == 0, (
+            f"{op} {fmt} g{group} {tuple(x.shape)}: {bad[0].size} code bytes differ, first at "
+            f"{tuple(int(b[0]) for b in bad)}: gpu {q[tuple(b[0] for b in bad)]:#x} "
+            f"oracle {q_ref[tuple(b[0] for b in bad)]:#x}")
+        assert np.array_equal(sf.view(np.uint32), sf_ref.view(np.uint32)), \
+            f"{op}: {(sf.view(np.uint32) != sf_ref.view(np.uint32)).sum()} scales differ"
+
+
+# ------------------------------------------------------------ full-size workloads
+
+def test_full_per_token_small(dev):
+    wl = workloads.per_token_small()
+    assert_exact("per_token", wl.x, dev, poisons=(0xAA, 0x55))
+
+
+def test_full_per_token_hidden(dev):
+    wl = workloads.per_token_hidden()
+    assert_exact("per_token", wl.x, dev)
+
+
+def test_full_e2m1(dev):
+    wl = workloads.student_t()
+    # the default E2M1 floor (6 * 2^-126) and a floor of 1e-4 give the same
+    # result here only if no group has amax below 1e-4
+    amax = wl.x.float().abs().view(wl.rows, -1, 32).amax(dim=2)
+    assert (amax >= 1e-4).all()
+    assert_exact("e2m1", wl.x, dev, "e2m1", 32)
+
+
+def test_full_per_block(dev):
+    wl = workloads.weight_block()
+    assert_exact("per_block", wl.x, dev)
+
+
+def test_full_per_channel_T(dev):
+    wl = workloads.activation_channel()
+    assert_exact("per_channel_T", wl.x, dev)
+
+
+def swiglu_tolerance_check(wl, dev, q, sf):
+    """The SwiGLU bar: codes within one step on <= 0.1% of elements, scales
+    within 1e-6 relative, dequantized values within 2^-3 of the group amax."""
+    q_ref, sf_ref = oracle_cast("swiglu_per_token", wl.x, w=wl.w)
+    rel = np.abs(sf.astype(np.float64) - sf_ref) / sf_ref
+    assert rel.max() <= 1e-6, f"scale relative error {rel.max():.3g}"
+    dq = oracle.decode("e4m3", q).astype(np.float64)
+    dq_ref = oracle.decode("e4m3", q_ref).astype(np.float64)
+    diff = q != q_ref
+    frac = diff.mean()
+    assert frac <= 1e-3, f"{frac:.3%} of codes differ"
+    # one code step: E4M3 magnitudes increase with the 7-bit code, so two
+    # codes one step apart differ by one in their signed magnitude code
+    def signed(c):
+        c = c.astype(np.int64)
+        return np.where(c & 0x80, -(c & 0x7F), c & 0x7F)
+    step = np.abs(signed(q[diff]) - signed(q_ref[diff]))
+    assert step.max(initial=0) <= 1
+    g = 128
+    rows, n = q.shape
+    deq = dq.reshape(rows, n // g, g) * sf[..., None]
+    deq_ref = dq_ref.reshape(rows, n // g, g) * sf_ref[..., None]
+    v = oracle.swiglu_values(workloads.bf16_bits(wl.x), wl.w.numpy()).reshape(rows, n // g, g)
+    amax = np.abs(v).max(axis=2, keepdims=True)
+    assert (np.abs(deq - deq_ref) <= 2.0 ** -3 * amax + 1e-30).all()
+    return frac
+
+
+def test_full_swiglu(dev):
+    wl = workloads.swiglu_input()
+    q, sf = gpu_cast("swiglu_per_token", wl.x, dev, w=wl.w)
+    frac = swiglu_tolerance_check(wl, dev, q, sf)
+    print(f"swiglu full: {frac:.5%} of codes differ from the oracle")
+
+
+# ------------------------------------------------------------ small, ragged, all groups
+
+@pytest.mark.parametrize("fmt,group", [("e4m3", 128), ("e4m3", 64), ("e4m3", 32),
+                                       ("e2m1", 32), ("e2m1", 64), ("e2m1", 128)])
+@pytest.mark.parametrize("rows,cols", [(1, 128), (3, 384), (127, 7168), (257, 1024)])
+def test_per_token_shapes(dev, fmt, group, rows, cols):
+    g = torch.Generator().manual_seed(rows * 1000 + cols)
+    x = torch.randn(rows, cols, generator=g) * torch.exp(torch.randn(rows, 1, generator=g) * 4)
+    assert_exact("per_token", x.to(torch.bfloat16), dev, fmt, group)
+
+
+@pytest.mark.parametrize("rows,cols", [(128, 128), (256, 384), (384, 1152)])
+def test_per_block_shapes(dev, rows, cols):
+    g = torch.Generator().manual_seed(rows + cols)
+    x = torch.randn(rows, cols, generator=g)
+    # a different magnitude per 128 x 128 block
+    x = x * torch.exp(torch.randn(rows // 128, 1, cols // 128, 1, generator=g) * 3).expand(
+        rows // 128, 128, cols // 128, 128).reshape(rows, cols)
+    assert_exact("per_block", x.to(torch.bfloat16), dev)
+
+
+@pytest.mark.parametrize("rows,cols", [(128, 8), (128, 64), (256, 200), (384, 136), (1024, 7168)])
+def test_per_channel_T_shapes(dev, rows, cols):
+    g = torch.Generator().manual_seed(rows * 7 + cols)
+    x = torch.randn(rows, cols, generator=g) * torch.exp(torch.randn(1, cols, generator=g) * 3)
+    assert_exact("per_channel_T", x.to(torch.bfloat16), dev)
+
+
+@pytest.mark.parametrize("group", [128, 64, 32])
+@pytest.mark.parametrize("weighted", [True, False])
+@pytest.mark.parametrize("rows,cols", [(1, 128), (5, 384), (130, 2048)])
+def test_swiglu_shapes(dev, group, weighted, rows, cols):
+    wl = workloads.swiglu_input(seed=rows + cols, rows=rows, cols=cols, with_weight=weighted)
+    q, sf = gpu_cast("swiglu_per_token", wl.x, dev, group=group, w=wl.w)
+    q_ref, sf_ref = oracle_cast("swiglu_per_token", wl.x, group=group, w=wl.w)
+    assert (q != q_ref).mean() <= 1e-3 + 1.0 / q.size
+    assert (np.abs(sf.astype(np.float64) - sf_ref) / sf_ref).max() <= 1e-6
+
+
+# ------------------------------------------------------------ edge cases
+
+def rows_of(values, cols=128):
+    """bf16 tensor whose rows are `values` (each padded/cycled to `cols`)."""
+    x = np.zeros((len(values), cols), np.float32)
+    for r, v in enumerate(values):
+        v = np.asarray(v, np.float32).ravel()
+        x[r, :len(v)] = v[:cols]
+    return torch.from_numpy(x).to(torch.bfloat16)
+
+
+def edge_rows():
+    rng = np.random.default_rng(0)
+    big = float(torch.tensor([0x7F7F], dtype=torch.int16).view(torch.bfloat16).float())
+    mids = np.array([1.0625, 1.1875, 17.0, 50.0, 3 * 2.0 ** -10, 2.0 ** -10], np.float32)
+    return [
+        np.zeros(128),                                   # zero group
+        -np.zeros(128),                                  # -0 group
+        np.linspace(-5e-5, 5e-5, 128),                   # floor-active (amax < 1e-4)
+        np.r_[3.0, np.zeros(127)],                       # single nonzero
+        np.r_[-448.0 * 4, mids * 4, -mids * 4],          # power-of-two scale: exact midpoints
+        np.r_[448.0 / 8, mids / 8, -mids / 8],
+        -np.abs(rng.standard_normal(128)) * 1e-3,        # tiny negatives
+        np.r_[big, -big / 2, 1.0, -1.0],                 # largest bf16
+        rng.standard_normal(128) * 1e30,
+        rng.standard_normal(128) * 1e-30,
+    ]
+
+
+def test_edge_cases_per_token_e4m3(dev):
+    x = rows_of(edge_rows())
+    # -0.0 survives the conversion to bf16
+    assert (x[1].view(torch.int16) == -32768).all()
+    assert_exact("per_token", x, dev, "e4m3", 128, poisons=(0xAA, 0x55))
+
+
+def test_edge_cases_per_token_e2m1(dev):
+    rows = edge_rows() + [
+        np.r_[2.0 ** -127, -(2.0 ** -127), 2.0 ** -125, np.zeros(29)],   # bf16 subnormals, floor active
+        np.r_[2.0 ** -133, 3 * 2.0 ** -133, np.zeros(30)],
+    ]
+    x = rows_of(rows, 128)
+    assert_exact("per_token", x, dev, "e2m1", 32, poisons=(0xAA, 0x55))
+    assert_exact("per_token", x, dev, "e2m1", 128)
+
+
+def test_edge_cases_other_casts(dev):
+    x = rows_of(edge_rows() * 13, 256)[:128]     # 128 token rows x 256 channels
+    assert_exact("per_block", x, dev)
+    assert_exact("per_channel_T", x, dev)
+    assert_exact("per_channel_T", x.T.contiguous()[:, :128], dev)
+
+
+def test_swiglu_extremes(dev):
+    g = np.array([[100.0, -100.0, -89.0, 0.0, 20.0, -3.0, 1.0, -200.0] * 16], np.float32)
+    u = np.array([[1.0, 5.0, -2.0, 7.0, -1.0, 4.0, 3.0, -6.0] * 16], np.float32)
+    h = torch.from_numpy(np.concatenate([g, u], axis=1)).to(torch.bfloat16)
+    for w in (None, torch.tensor([0.0]), torch.tensor([0.37])):
+        q, sf = gpu_cast("swiglu_per_token", h, dev, w=w)
+        q_ref, sf_ref = oracle_cast("swiglu_per_token", h, w=w)
+        assert np.array_equal(q, q_ref), (w, q, q_ref)
+        assert np.array_equal(sf.view(np.uint32), sf_ref.view(np.uint32)), w
+
+
+# ------------------------------------------------------------ exhaustive encoder sweeps
+
+def test_every_bf16_below_448_encodes_like_the_oracle(dev):
+    # A group whose abs-max is 448 has sf = 1 and sf_inv = 1 exactly, so the
+    # other 127 elements are encoded as they are: this sweeps the hardware
+    # conversion over every finite bf16 value of magnitude <= 448.
+    bits = np.arange(0, 0x43E1, dtype=np.uint16)               # +0 .. 448
+    vals = np.concatenate([bits, bits | 0x8000])
+    n = len(vals)
+    per_row = 127
+    nrows = (n + per_row - 1) // per_row
+    x = np.zeros((nrows, 128), np.uint16)
+    x[:, 0] = 0x43E0                                           # 448
+    flat = np.zeros(nrows * per_row, np.uint16)
+    flat[:n] = vals
+    x[:, 1:] = flat.reshape(nrows, per_row)
+    assert_exact("per_token", workloads.bits_to_bf16(x), dev, "e4m3", 128)
+
+
+def test_every_bf16_below_6_encodes_like_the_oracle_e2m1(dev):
+    bits = np.arange(0, 0x40C1, dtype=np.uint16)               # +0 .. 6
+    vals = np.concatenate([bits, bits | 0x8000])
+    n = len(vals)
+    per_row = 31
+    nrows = (n + per_row - 1) // per_row
+    x = np.zeros((nrows, 32), np.uint16)
+    x[:, 0] = 0x40C0                                           # 6.0
+    flat = np.zeros(nrows * per_row, np.uint16)
+    flat[:n] = vals
+    x[:, 1:] = flat.reshape(nrows, per_row)
+    assert_exact("per_token", workloads.bits_to_bf16(x), dev, "e2m1", 32)
+
+
+# ------------------------------------------------------------ API behaviour
+
+def test_page_api_shapes(dev):
+    # per_token_cast(x, fmt='e4m3', num_per_channels=128) on bf16 [1024, 4096]
+    x = torch.randn(1024, 4096, dtype=torch.bfloat16, device=dev)
+    out, out_sf = pq.per_token_cast(x, fmt="e4m3", num_per_channels=128)
+    assert out.shape == (1024, 4096) and out.dtype == torch.float8_e4m3fn
+    assert out_sf.shape == (1024, 32) and out_sf.dtype == torch.float32
+
+
+def test_empty_input_is_a_no_op(dev):
+    x = torch.empty(0, 256, dtype=torch.bfloat16, device=dev)
+    out, sf = pq.qcast_per_token(x)
+    assert out.shape == (0, 256) and sf.shape == (0, 2)
+
+
+def test_side_stream_and_repeat_determinism(dev):
+    wl = workloads.per_token_hidden(rows=512)
+    x = wl.x.to(dev)
+    s = torch.cuda.Stream(device=dev)
+    with torch.cuda.stream(s):
+        a, asf = pq.qcast_per_token(x)
+    s.synchronize()
+    b, bsf = pq.qcast_per_token(x)
+    torch.cuda.synchronize()
+    assert torch.equal(a.view(torch.uint8), b.view(torch.uint8)) and torch.equal(asf, bsf)
+
+
+def test_binding_errors_raise(dev):
+    x = torch.zeros(4, 200, dtype=torch.bfloat16, device=dev)
+    with pytest.raises(pq.QcastError):
+        pq.qcast_per_token(x, group=128)
+    with pytest.raises(pq.QcastError):
+        pq.qcast_per_block(torch.zeros(128, 128, dtype=torch.bfloat16, device=dev), block=64)
+
+
+def test_cu_override_does_not_change_results(dev):
+    wl = workloads.per_token_hidden(rows=256)
+    x = wl.x.to(dev)
+    a, asf = pq.qcast_per_token(x)
+    try:
+        pq.qcast_set_num_cus(3)
+        b, bsf = pq.qcast_per_token(x)
+    finally:
+        pq.qcast_set_num_cus(0)
+    torch.cuda.synchronize()
+    assert torch.equal(a.view(torch.uint8), b.view(torch.uint8)) and torch.equal(asf, bsf)
