@@ -13,7 +13,7 @@ inputs that the rest of the step has evicted.
 
 value = algorithmic bytes of the whole step (inputs read once, codes and
 scales written once) / time per step, in GB/s. Per-kernel durations come from
-HIP events recorded on the launch stream around each kernel in the timed
+HIP events recorded on the launch stream between the kernels of the timed
 steps. The roofline object is for the kernel with the largest share of the
 step. The CPU baseline is the oracle (single thread) on the first half of the
 rows of every workload, on this host.
@@ -37,6 +37,45 @@ TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic.json")
 
 def log(msg):
     print(msg, file=sys.stderr, flush=True)
+
+
+class HipEvents:
+    """HIP timing events without the system-scope fence on record
+    (hipEventDisableSystemFence). One event sits between consecutive
+    kernels of a step, so each kernel is bracketed by the events before and
+    after it on the launch stream; torch's events would add a fenced marker
+    pair per kernel, about 10 us each."""
+    DISABLE_SYSTEM_FENCE = 0x20000000
+
+    def __init__(self):
+        import ctypes
+        self.ct = ctypes
+        self.hip = ctypes.CDLL("libamdhip64.so")
+        self.hip.hipEventCreateWithFlags.argtypes = [ctypes.POINTER(ctypes.c_void_p),
+                                                     ctypes.c_uint]
+        self.hip.hipEventRecord.argtypes = [ctypes.c_void_p, ctypes.c_void_p]
+        self.hip.hipEventElapsedTime.argtypes = [ctypes.POINTER(ctypes.c_float),
+                                                 ctypes.c_void_p, ctypes.c_void_p]
+        self.hip.hipEventDestroy.argtypes = [ctypes.c_void_p]
+
+    def create(self):
+        e = self.ct.c_void_p()
+        if self.hip.hipEventCreateWithFlags(self.ct.byref(e), self.DISABLE_SYSTEM_FENCE) != 0:
+            raise RuntimeError("hipEventCreateWithFlags failed")
+        return e
+
+    def record(self, e, stream):
+        if self.hip.hipEventRecord(e, stream) != 0:
+            raise RuntimeError("hipEventRecord failed")
+
+    def elapsed_ms(self, a, b):
+        f = self.ct.c_float()
+        if self.hip.hipEventElapsedTime(self.ct.byref(f), a, b) != 0:
+            raise RuntimeError("hipEventElapsedTime failed")
+        return f.value
+
+    def destroy(self, e):
+        self.hip.hipEventDestroy(e)
 
 
 def make_workloads():
@@ -87,24 +126,30 @@ def kernel_calls(wls, dev):
 
 
 def copy_ceiling(dev, nbytes):
-    """Bandwidth of a plain device copy moving nbytes in total (half read,
-    half written), cold: the empirical ceiling for a streaming kernel."""
+    """Bandwidth of the library's streaming copy (include/qcast_bench.h)
+    moving nbytes in total (half read, half written) after a 1 GiB flush:
+    the empirical ceiling for a streaming kernel of this shape."""
     import torch
-    half = nbytes // 2
+    import precision_quantization_amd as pq
+    half = nbytes // 2 // 16 * 16
     src = torch.empty(half, dtype=torch.uint8, device=dev).fill_(1)
     dst = torch.empty(half, dtype=torch.uint8, device=dev)
     flush = torch.empty(1 << 30, dtype=torch.uint8, device=dev)
+    hev = HipEvents()
+    stream = torch.cuda.current_stream(dev).cuda_stream
+    a, b = hev.create(), hev.create()
     times = []
     for _ in range(6):
         flush.fill_(0)
-        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-        a.record()
-        dst.copy_(src)
-        b.record()
+        hev.record(a, stream)
+        pq.qcast_bench_copy(src, dst)
+        hev.record(b, stream)
         torch.cuda.synchronize()
-        times.append(a.elapsed_time(b))
+        times.append(hev.elapsed_ms(a, b))
+    hev.destroy(a)
+    hev.destroy(b)
     ms = sorted(times[1:])[len(times[1:]) // 2]
-    return nbytes / (ms * 1e-3) / 1e9
+    return 2 * half / (ms * 1e-3) / 1e9
 
 
 def cpu_baseline(wls, fraction=0.5):
@@ -176,23 +221,24 @@ def main():
     torch.cuda.synchronize()
 
     n = len(calls)
-    ev = [[(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
-           for _ in range(n)] for _ in range(args.steps)]
+    hev = HipEvents()
+    stream = torch.cuda.current_stream(dev).cuda_stream
+    ev = [[hev.create() for _ in range(n + 1)] for _ in range(args.steps)]
     log(f"bench: timing {args.steps} steps")
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     for s in range(args.steps):
+        hev.record(ev[s][0], stream)
         for i, (_, _, fn) in enumerate(calls):
-            ev[s][i][0].record()
             fn()
-            ev[s][i][1].record()
+            hev.record(ev[s][i + 1], stream)
     torch.cuda.synchronize()
     elapsed = time.perf_counter() - t0
     ms_per_step = elapsed * 1e3 / args.steps
 
     kernels = {}
     for i, (name, wl, _) in enumerate(calls):
-        ms = sorted(ev[s][i][0].elapsed_time(ev[s][i][1]) for s in range(args.steps))
+        ms = sorted(hev.elapsed_ms(ev[s][i], ev[s][i + 1]) for s in range(args.steps))
         avg = sum(ms) / len(ms)
         b = wl.algorithmic_bytes()
         kernels[name] = {
@@ -201,6 +247,9 @@ def main():
             "GBps": round(b / (avg * 1e-3) / 1e9, 1),
             "frac": round(b / (avg * 1e-3) / 1e9 / PEAK_HBM_GBS, 4),
         }
+    for row in ev:
+        for e in row:
+            hev.destroy(e)
     dominant = max(kernels, key=lambda k: kernels[k]["avg_us"])
     d = kernels[dominant]
     traffic = load_traffic(dominant)

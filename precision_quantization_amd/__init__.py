@@ -19,7 +19,9 @@ import torch
 from ._lib import FMT_E2M1, FMT_E4M3, QcastError, check, fmt_id, load
 
 __all__ = ["qcast_per_token", "qcast_e2m1", "qcast_swiglu_per_token", "qcast_per_block",
-           "qcast_per_channel_T", "qcast_abi_version", "qcast_set_num_cus", "per_token_cast",
+           "qcast_per_channel_T", "qcast_abi_version", "qcast_set_num_cus", "qcast_bench_copy",
+           "qcast_bench_check_scale",
+           "per_token_cast",
            "QcastError", "FMT_E4M3", "FMT_E2M1"]
 
 
@@ -149,6 +151,31 @@ def qcast_abi_version():
 
 def qcast_set_num_cus(n):
     load().qcast_set_num_cus(int(n))
+
+
+def qcast_bench_copy(src, dst, stream=None):
+    """Measurement helper (include/qcast_bench.h): copy src's bytes to dst."""
+    if not (src.is_cuda and dst.is_cuda and src.is_contiguous() and dst.is_contiguous()):
+        raise QcastError(2, "src and dst must be contiguous CUDA tensors")
+    n = src.numel() * src.element_size()
+    if dst.numel() * dst.element_size() != n or src.device != dst.device:
+        raise QcastError(2, "src and dst must have the same size on one device")
+    with torch.cuda.device(src.device):
+        check(load().qcast_bench_copy(src.data_ptr(), dst.data_ptr(), n, _stream(src.device, stream)),
+              "qcast_bench_copy")
+
+
+def qcast_bench_check_scale(fmt, first, last, device="cuda:0", stream=None):
+    """Self-check helper (include/qcast_bench.h): mismatches of the kernels'
+    scale routine against IEEE division over fp32 patterns [first, last];
+    returns (sf mismatches, sf_inv mismatches)."""
+    dev = torch.device(device)
+    counts = torch.empty(2 * 2048, dtype=torch.int32, device=dev)
+    with torch.cuda.device(dev):
+        check(load().qcast_bench_check_scale(fmt_id(fmt), first, last, counts.data_ptr(),
+                                             _stream(dev, stream)), "qcast_bench_check_scale")
+        c = counts.view(2048, 2).sum(dim=0, dtype=torch.int64).cpu()
+    return int(c[0]), int(c[1])
 
 
 def per_token_cast(x, fmt="e4m3", num_per_channels=128):

@@ -60,6 +60,10 @@ def load():
     lib.qcast_status_str.restype = ctypes.c_char_p
     lib.qcast_abi_version.argtypes = []
     lib.qcast_abi_version.restype = i32
+    lib.qcast_bench_copy.argtypes = [vp, vp, i64, vp]
+    lib.qcast_bench_copy.restype = i32
+    lib.qcast_bench_check_scale.argtypes = [i32, ctypes.c_uint32, ctypes.c_uint32, vp, vp]
+    lib.qcast_bench_check_scale.restype = i32
     lib.qcast_set_num_cus.argtypes = [i32]
     lib.qcast_set_num_cus.restype = None
     _lib = lib
@@ -73,4 +77,5 @@ def check(status, what):
 
 
 EXPORTS = ["qcast_per_token", "qcast_e2m1", "qcast_swiglu_per_token", "qcast_per_block",
-           "qcast_per_channel_T", "qcast_status_str", "qcast_abi_version", "qcast_set_num_cus"]
+           "qcast_per_channel_T", "qcast_status_str", "qcast_abi_version", "qcast_set_num_cus",
+           "qcast_bench_copy", "qcast_bench_check_scale"]

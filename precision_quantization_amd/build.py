@@ -45,7 +45,7 @@ def sources():
 def source_digest():
     h = hashlib.sha256()
     files = sources() + sorted(glob.glob(os.path.join(CSRC, "*.h"))) + \
-        [os.path.join(INCLUDE, "qcast.h")]
+        sorted(glob.glob(os.path.join(INCLUDE, "*.h")))
     for path in files:
         with open(path, "rb") as f:
             h.update(os.path.basename(path).encode() + b"\0" + f.read())

@@ -51,7 +51,7 @@ __global__ __launch_bounds__(kThreads) void per_block_kernel(
     if ((t & 63) == 0) wave_amax[t >> 6] = m;
     __syncthreads();
     m = fmaxf(fmaxf(wave_amax[0], wave_amax[1]), fmaxf(wave_amax[2], wave_amax[3]));
-    const Scale s = group_scale(m, floor, kE4M3Max);
+    const Scale s = group_scale<kE4M3>(m, floor);
 #pragma unroll
     for (int p = 0; p < kPasses; ++p) {
       u32x2 out;

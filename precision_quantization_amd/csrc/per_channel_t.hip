@@ -35,6 +35,14 @@ constexpr int kTokens = 128;       // tokens per tile = scale group
 constexpr int kChannels = 64;      // channels per tile
 constexpr int kXcds = 8;
 
+// Order in which workgroups walk the tiles (compile-time; default chosen by
+// measurement). Bit 0: 0 = token group fastest, 1 = channel tile fastest.
+// Bit 1: 0 = each XCD takes a contiguous range of tiles, 1 = plain order.
+#ifndef QCAST_PC_ORDER
+#define QCAST_PC_ORDER 0
+#endif
+constexpr int kOrder = QCAST_PC_ORDER;
+
 __global__ __launch_bounds__(kThreads) void per_channel_t_kernel(
     const uint16_t* __restrict__ x, int64_t rows, int64_t cols, int64_t ngroups,
     int64_t ntiles, int64_t per_xcd, float floor, uint8_t* __restrict__ qT,
@@ -44,10 +52,11 @@ __global__ __launch_bounds__(kThreads) void per_channel_t_kernel(
   __shared__ float inv_s[kChannels];
 
   const int64_t b = blockIdx.x;
-  const int64_t tau = (b % kXcds) * per_xcd + b / kXcds;
+  const int64_t tau = (kOrder & 2) ? b : (b % kXcds) * per_xcd + b / kXcds;
   if (tau >= ntiles) return;
-  const int64_t ct = tau / ngroups;
-  const int64_t g = tau - ct * ngroups;
+  const int64_t nct = ntiles / ngroups;
+  const int64_t ct = (kOrder & 1) ? tau % nct : tau / ngroups;
+  const int64_t g = (kOrder & 1) ? tau / nct : tau - ct * ngroups;
   const int64_t c0 = ct * kChannels;
   const int64_t t0 = g * kTokens;
   const int nc = (int)(cols - c0 < kChannels ? cols - c0 : kChannels);
@@ -75,11 +84,12 @@ __global__ __launch_bounds__(kThreads) void per_channel_t_kernel(
   float pm[8];
 #pragma unroll
   for (int j = 0; j < 8; ++j) {
-    float m = fmaxf(fmaxf(fabsf(v[0][j]), fabsf(v[1][j])), fmaxf(fabsf(v[2][j]), fabsf(v[3][j])));
-    m = fmaxf(m, dpp<kDppRor8>(m));
-    m = fmaxf(m, __shfl_xor(m, 16));
-    m = fmaxf(m, __shfl_xor(m, 32));
-    pm[j] = m;
+    const float m = fmaxf(fmaxf(fabsf(v[0][j]), fabsf(v[1][j])), fmaxf(fabsf(v[2][j]), fabsf(v[3][j])));
+    uint32_t b = __float_as_uint(m);
+    b = umax(b, dpp<kDppRor8>(b));
+    b = umax(b, (uint32_t)__shfl_xor((int)b, 16));
+    b = umax(b, (uint32_t)__shfl_xor((int)b, 32));
+    pm[j] = __uint_as_float(b);
   }
   const int wave = t >> 6;
   if ((t & 63) < 8) {
@@ -90,7 +100,7 @@ __global__ __launch_bounds__(kThreads) void per_channel_t_kernel(
   if (t < kChannels) {
     const float m = fmaxf(fmaxf(wave_amax[0][t], wave_amax[1][t]),
                           fmaxf(wave_amax[2][t], wave_amax[3][t]));
-    const Scale s = group_scale(m, floor, kE4M3Max);
+    const Scale s = group_scale<kE4M3>(m, floor);
     inv_s[t] = s.inv;
     if (t < nc) sf[(c0 + t) * ngroups + g] = s.sf;
   }

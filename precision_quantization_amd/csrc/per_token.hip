@@ -21,13 +21,22 @@
 namespace qcast {
 namespace {
 
-constexpr int kUnroll = 4;
+// Launch shape (compile-time; the defaults were chosen by measurement):
+// chunks in flight per lane, and the cap on resident workgroups per CU for
+// the persistent grid (0: one workgroup per kUnroll*256 chunks, no loop).
+#ifndef QCAST_PT_UNROLL
+#define QCAST_PT_UNROLL 2
+#endif
+#ifndef QCAST_PT_WG_PER_CU
+#define QCAST_PT_WG_PER_CU 0
+#endif
+constexpr int kUnroll = QCAST_PT_UNROLL;
+constexpr int kWgPerCu = QCAST_PT_WG_PER_CU;
 
 template <int kLanes, int kFmt>
 __global__ __launch_bounds__(kThreads) void per_token_kernel(
     const u32x4* __restrict__ x, int64_t nchunks, float floor, uint8_t* __restrict__ q,
     float* __restrict__ sf) {
-  constexpr float kMax = (kFmt == kE4M3) ? kE4M3Max : kE2M1Max;
   const int64_t step = (int64_t)gridDim.x * kThreads * kUnroll;
   for (int64_t base = (int64_t)blockIdx.x * kThreads * kUnroll + threadIdx.x; base < nchunks;
        base += step) {
@@ -46,7 +55,7 @@ __global__ __launch_bounds__(kThreads) void per_token_kernel(
         float v[8];
         unpack8(raw[u], v);
         const float amax = lane_group_max<kLanes>(absmax8(v));
-        const Scale s = group_scale(amax, floor, kMax);
+        const Scale s = group_scale<kFmt>(amax, floor);
         float y[8];
 #pragma unroll
         for (int i = 0; i < 8; ++i) y[i] = v[i] * s.inv;
@@ -69,9 +78,9 @@ hipError_t launch(const void* x, int64_t nchunks, float floor, void* q, float* s
                   hipStream_t stream, const LaunchCaps& caps) {
   const int64_t per_block_iter = (int64_t)kThreads * kUnroll;
   const int64_t iters = (nchunks + per_block_iter - 1) / per_block_iter;
-  // Persistent grid: at most 8 workgroups per CU; the same number of
+  // Persistent grid: at most kWgPerCu workgroups per CU, the same number of
   // iterations for every workgroup.
-  const int64_t max_blocks = (int64_t)caps.num_cus * 8;
+  const int64_t max_blocks = kWgPerCu > 0 ? (int64_t)caps.num_cus * kWgPerCu : iters;
   const int64_t iters_per_block = (iters + max_blocks - 1) / max_blocks;
   const int64_t blocks = (iters + iters_per_block - 1) / iters_per_block;
   hipLaunchKernelGGL((per_token_kernel<kLanes, kFmt>), dim3((unsigned)blocks), dim3(kThreads), 0,

@@ -37,13 +37,36 @@ struct Scale {
   float inv;
 };
 
-// a = max(amax, floor); sf = a / fmt_max; inv = 1 / sf (IEEE divisions:
-// the library is built with correctly rounded fp32 division).
-__device__ __forceinline__ Scale group_scale(float amax, float floor, float fmt_max) {
+// a = max(amax, floor); sf = RN(a / fmt_max); inv = RN(1 / sf).
+//
+// Both results are the correctly rounded fp32 quotients. In the common range
+// they come from short FMA sequences instead of the full IEEE division
+// (about 6 instead of 22 instructions):
+//   sf  = q0 + r * R, with q0 = a * R, r = fma(-q0, M, a), R = RN(1 / M)
+//   inv = y0 + e * y0, with y0 = v_rcp_f32(sf), e = fma(-sf, y0, 1)
+// An exhaustive sweep over every positive fp32 shows both sequences equal to
+// the IEEE quotients for M in {448, 6} whenever a >= 2^-120 (M = 448) or
+// a >= 2^-125 (M = 6), and sf in [2^-126, 2^125). The fast path is taken for
+// M * 2^-126 <= a < M * 2^124, inside those ranges; every other a (a custom
+// floor below the normal range, or huge inputs under E2M1) takes the IEEE
+// division. qcast_bench_check_scale re-runs the sweep through this function.
+template <int kFmt>
+__device__ __forceinline__ Scale group_scale(float amax, float floor) {
+  constexpr float kMax = (kFmt == kE4M3) ? kE4M3Max : kE2M1Max;
+  constexpr float kRecip = 1.0f / kMax;                     // RN(1 / M), folded
+  constexpr float kFastLo = kMax * 0x1.0p-126f;             // exact
+  constexpr float kFastHi = (kFmt == kE4M3) ? __builtin_huge_valf() : kMax * 0x1.0p124f;
   const float a = amax < floor ? floor : amax;
   Scale s;
-  s.sf = a / fmt_max;
-  s.inv = 1.0f / s.sf;
+  if (a >= kFastLo && a < kFastHi) {
+    const float q0 = a * kRecip;
+    s.sf = __builtin_fmaf(__builtin_fmaf(-q0, kMax, a), kRecip, q0);
+    const float y0 = __builtin_amdgcn_rcpf(s.sf);
+    s.inv = __builtin_fmaf(__builtin_fmaf(-s.sf, y0, 1.0f), y0, y0);
+  } else {
+    s.sf = a / kMax;
+    s.inv = 1.0f / s.sf;
+  }
   return s;
 }
 
@@ -65,10 +88,10 @@ __device__ __forceinline__ float absmax8(const float v[8]) {
   return m;
 }
 
-// Cross-lane moves inside a DPP row of 16 lanes.
+// Cross-lane moves inside a DPP row of 16 lanes, on raw 32-bit values.
 template <int kCtrl>
-__device__ __forceinline__ float dpp(float v) {
-  return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), kCtrl, 0xF, 0xF, false));
+__device__ __forceinline__ uint32_t dpp(uint32_t v) {
+  return (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, kCtrl, 0xF, 0xF, false);
 }
 constexpr int kDppXor1 = 0xB1;         // quad_perm [1,0,3,2]
 constexpr int kDppXor2 = 0x4E;         // quad_perm [2,3,0,1]
@@ -76,24 +99,31 @@ constexpr int kDppHalfMirror = 0x141;  // lane i <-> 7-i inside each 8 lanes
 constexpr int kDppMirror = 0x140;      // lane i <-> 15-i inside each 16 lanes
 constexpr int kDppRor8 = 0x128;        // lane i <- (i+8) mod 16
 
-// Max over aligned runs of kLanes lanes (4, 8 or 16); every lane of a run
-// ends with the run's maximum. Runs never straddle a DPP row.
+// Abs-maxima are non-negative floats, whose order is the unsigned order of
+// their bit patterns, so the cross-lane maxima are integer maxima (no
+// canonicalisation of the moved values is needed).
+__device__ __forceinline__ uint32_t umax(uint32_t a, uint32_t b) { return a > b ? a : b; }
+
+// Max over aligned runs of kLanes lanes (4, 8 or 16) of a non-negative
+// value; every lane of a run ends with the run's maximum. Runs never
+// straddle a DPP row.
 template <int kLanes>
 __device__ __forceinline__ float lane_group_max(float m) {
   static_assert(kLanes == 4 || kLanes == 8 || kLanes == 16, "4, 8 or 16 lanes");
-  m = fmaxf(m, dpp<kDppXor1>(m));
-  m = fmaxf(m, dpp<kDppXor2>(m));
-  if (kLanes >= 8) m = fmaxf(m, dpp<kDppHalfMirror>(m));
-  if (kLanes >= 16) m = fmaxf(m, dpp<kDppMirror>(m));
-  return m;
+  uint32_t b = __float_as_uint(m);
+  b = umax(b, dpp<kDppXor1>(b));
+  b = umax(b, dpp<kDppXor2>(b));
+  if (kLanes >= 8) b = umax(b, dpp<kDppHalfMirror>(b));
+  if (kLanes >= 16) b = umax(b, dpp<kDppMirror>(b));
+  return __uint_as_float(b);
 }
 
-// Max over the whole wave64; every lane gets it.
+// Max over the whole wave64 of a non-negative value; every lane gets it.
 __device__ __forceinline__ float wave_max(float m) {
-  m = lane_group_max<16>(m);
-  m = fmaxf(m, __shfl_xor(m, 16));
-  m = fmaxf(m, __shfl_xor(m, 32));
-  return m;
+  uint32_t b = __float_as_uint(lane_group_max<16>(m));
+  b = umax(b, (uint32_t)__shfl_xor((int)b, 16));
+  b = umax(b, (uint32_t)__shfl_xor((int)b, 32));
+  return __uint_as_float(b);
 }
 
 // Four fp32 -> four E4M3 bytes (v0 in the lowest byte).

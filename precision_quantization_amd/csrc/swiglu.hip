@@ -23,7 +23,16 @@
 namespace qcast {
 namespace {
 
-constexpr int kUnroll = 2;
+// Launch shape (compile-time; defaults chosen by measurement): output
+// chunks in flight per lane, and the cap on workgroups per CU (0: no cap).
+#ifndef QCAST_SW_UNROLL
+#define QCAST_SW_UNROLL 1
+#endif
+#ifndef QCAST_SW_WG_PER_CU
+#define QCAST_SW_WG_PER_CU 0
+#endif
+constexpr int kUnroll = QCAST_SW_UNROLL;
+constexpr int kWgPerCu = QCAST_SW_WG_PER_CU;
 constexpr float kLog2e = 1.4426950408889634f;
 // Chunk-to-row division: row = (c * magic) >> 40 is exact for c < 2^24 and
 // chunks-per-row d < 2^16 when magic = ceil(2^40 / d).
@@ -70,7 +79,7 @@ __global__ __launch_bounds__(kThreads) void swiglu_kernel(
           if (kWeighted) v[i] = v[i] * wr[u];
         }
         const float amax = lane_group_max<kLanes>(absmax8(v));
-        const Scale s = group_scale(amax, floor, kE4M3Max);
+        const Scale s = group_scale<kE4M3>(amax, floor);
         u32x2 out;
         out.x = e4m3x4(v[0] * s.inv, v[1] * s.inv, v[2] * s.inv, v[3] * s.inv);
         out.y = e4m3x4(v[4] * s.inv, v[5] * s.inv, v[6] * s.inv, v[7] * s.inv);
@@ -94,7 +103,7 @@ hipError_t launch(const uint16_t* h, const float* w, int64_t rows, int64_t cols,
     const int64_t nchunks = nr * cpr;
     const int64_t per_block_iter = (int64_t)kThreads * kUnroll;
     const int64_t iters = (nchunks + per_block_iter - 1) / per_block_iter;
-    const int64_t max_blocks = (int64_t)caps.num_cus * 8;
+    const int64_t max_blocks = kWgPerCu > 0 ? (int64_t)caps.num_cus * kWgPerCu : iters;
     const int64_t iters_per_block = (iters + max_blocks - 1) / max_blocks;
     const int64_t blocks = (iters + iters_per_block - 1) / iters_per_block;
     hipLaunchKernelGGL((swiglu_kernel<kLanes, kWeighted>), dim3((unsigned)blocks),

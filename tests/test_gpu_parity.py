@@ -351,3 +351,56 @@ def test_cu_override_does_not_change_results(dev):
         pq.qcast_set_num_cus(0)
     torch.cuda.synchronize()
     assert torch.equal(a.view(torch.uint8), b.view(torch.uint8)) and torch.equal(asf, bsf)
+
+
+def test_bench_copy_helper(dev):
+    src = torch.randint(0, 256, ((1 << 20) + 48,), dtype=torch.uint8, device=dev)
+    dst = torch.zeros_like(src)
+    pq.qcast_bench_copy(src, dst)
+    torch.cuda.synchronize()
+    assert torch.equal(src, dst)
+
+
+# ------------------------------------------------------------ the scale routine
+
+@pytest.mark.parametrize("fmt", ["e4m3", "e2m1"])
+def test_scale_routine_equals_ieee_division_on_every_positive_fp32(dev, fmt):
+    # The kernels' short FMA sequences (and their IEEE fallback) against the
+    # IEEE quotients a / fmt_max and 1 / sf, for all 2^31 - 2^23 - 1 positive
+    # finite fp32 abs-maxima.
+    assert pq.qcast_bench_check_scale(fmt, 1, 0x7F7FFFFF) == (0, 0)
+
+
+@pytest.mark.parametrize("fmt,group", [("e4m3", 128), ("e2m1", 32)])
+def test_every_bf16_abs_max(dev, fmt, group):
+    # One group per positive finite bf16 value v (subnormals included), with
+    # v, v/2 and -v/3 in it: every abs-max a bf16 input can produce.
+    bits = np.arange(1, 0x7F80, dtype=np.uint16)
+    v = (bits.astype(np.uint32) << 16).view(np.float32)
+    x = np.zeros((len(v), group), np.float32)
+    x[:, 0] = v
+    x[:, 1] = v / 2
+    x[:, 2] = -v / 3
+    xt = torch.from_numpy(x).to(torch.bfloat16)
+    assert (xt.float().abs().amax(dim=1).numpy() == v).all()
+    assert_exact("per_token", xt, dev, fmt, group)
+    assert_exact("per_token", -xt, dev, fmt, group)
+
+
+# Floors below fmt_max * 2^-126 take the IEEE-division fallback of the scale
+# routine (3e-36 for E4M3, 5e-38 for E2M1); they are still large enough for
+# 1 / sf to stay finite.
+@pytest.mark.parametrize("fmt,group,clamp_min", [
+    ("e4m3", 128, 0.5), ("e4m3", 128, 1e-30), ("e4m3", 128, 3e-36),
+    ("e2m1", 32, 0.5), ("e2m1", 32, 1e-30), ("e2m1", 32, 5e-38)])
+def test_custom_floor(dev, fmt, group, clamp_min):
+    g = torch.Generator().manual_seed(17)
+    x = torch.randn(64, 256, generator=g) * torch.exp(torch.randn(64, 1, generator=g) * 10)
+    x[:8] = 0.0
+    x = x.to(torch.bfloat16)
+    q_ref, sf_ref = oracle.per_token(workloads.bf16_bits(x), fmt, group, clamp_min)
+    xd = x.to(dev)
+    q, sf = pq.qcast_per_token(xd, fmt, group, clamp_min=clamp_min)
+    torch.cuda.synchronize()
+    assert np.array_equal(codes_np(q), q_ref)
+    assert np.array_equal(sf.cpu().numpy().view(np.uint32), sf_ref.view(np.uint32))
