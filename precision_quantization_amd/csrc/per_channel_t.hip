@@ -9,125 +9,278 @@
 // Scale rule and codes as in the per-token cast of "DeepSeek开源TileKernels：
 // 用Python写的GPU算子逼近硬件性能上限", §3.1-§3.2.
 //
-// gfx950 design. A workgroup owns a tile of 128 tokens x 64 channels: one
-// token group for 64 channels. Lane (k, ch) loads the 16-byte chunk ch
-// (8 channels) of tokens 4k..4k+3, so each wave load reads eight 128-byte row
-// segments. Column abs-maxima: a register max over the lane's 4 tokens, a DPP
-// and two cross-lane steps over the 8 token quads of the wave, then a
-// 4 x 64 LDS exchange; 64 lanes form the 64 scales. Each lane packs the
-// codes of its 4 tokens of one channel into a dword and writes it to an LDS
-// tile [channel][token] whose dword index is XOR-swizzled by 4 * (channel/8):
-// the eight channels groups a half-wave writes land in distinct banks, and a
-// 16-byte run of tokens stays contiguous, so the read-back is one
-// ds_read_b128 per lane, conflict-free, and the store is a full 128-byte row
-// of qT per 8 lanes. (The pages' transpose pads its shared tile and rotates
-// the column index for the same purpose; the XOR form keeps 16-byte reads
-// aligned.) Workgroups are numbered so that each of the 8 XCDs walks a
-// contiguous range of tiles with the token group fastest: neighbouring tiles
-// on one XCD fill the same scale lines in its L2.
+// gfx950 design. A workgroup owns a tile of kTG token groups (128 tokens
+// each) x 8*kCC channels. Lane (k, ch) loads the 16-byte chunk ch (8
+// channels) of tokens 4k..4k+3 in each of kPasses passes, all loads issued
+// before any is used; the data stays in registers as packed bf16.
+// Column abs-maxima per token group: packed 16-bit maxima of the magnitude
+// bits (v_pk_max_u16) over the lane's tokens, the same over the lanes that
+// hold the same channel chunk (DPP / cross-lane), then a 4-wave LDS
+// exchange; one lane per (group, channel) forms the scale. Each lane packs
+// the codes of 4 tokens of one channel into a dword and writes it to an LDS
+// tile [channel][token] whose dword index is XOR-swizzled by
+// 4 * ((channel/8) mod 8): the eight channel chunks a half-wave writes land
+// in distinct banks, and each 16-byte run of tokens stays contiguous and
+// aligned, so the read-back is one ds_read_b128 per lane and the store is a
+// full row of qT (128 * kTG bytes) per channel. (The pages' transpose pads
+// its shared tile and rotates the column index for the same purpose; the
+// XOR form keeps 16-byte reads aligned.) Workgroups are numbered so that
+// each of the 8 XCDs walks a contiguous range of tiles, token groups
+// fastest, so neighbouring tiles on one XCD fill the same scale lines in its
+// L2.
 #include "qcast_device.h"
 #include "qcast_kernels.h"
 
 namespace qcast {
 namespace {
 
-constexpr int kTokens = 128;       // tokens per tile = scale group
-constexpr int kChannels = 64;      // channels per tile
+constexpr int kGroupTokens = 128;  // tokens per scale group
 constexpr int kXcds = 8;
 
-// Order in which workgroups walk the tiles (compile-time; default chosen by
-// measurement). Bit 0: 0 = token group fastest, 1 = channel tile fastest.
-// Bit 1: 0 = each XCD takes a contiguous range of tiles, 1 = plain order.
+// Tile shape (compile-time; the default was chosen by measurement): token
+// groups per tile and 8-channel chunks per tile.
+#ifndef QCAST_PC_TG
+#define QCAST_PC_TG 1
+#endif
+#ifndef QCAST_PC_CC
+#define QCAST_PC_CC 8
+#endif
+// 1: persistent, software-pipelined workgroups (QCAST_PC_WG_PER_CU per CU);
+// 0: one workgroup per tile.
+#ifndef QCAST_PC_PIPE
+#define QCAST_PC_PIPE 0
+#endif
+#ifndef QCAST_PC_WG_PER_CU
+#define QCAST_PC_WG_PER_CU 8
+#endif
+// Tiles of a persistent workgroup: 0 = strided over its XCD's range,
+// 1 = a contiguous chunk of that range (consecutive token groups of the same
+// channels, so the workgroup fills its qT rows front to back).
+#ifndef QCAST_PC_CHUNKED
+#define QCAST_PC_CHUNKED 0
+#endif
+constexpr int kPipe = QCAST_PC_PIPE;
+constexpr int kChunked = QCAST_PC_CHUNKED;
+constexpr int kPcWgPerCu = QCAST_PC_WG_PER_CU;
+// Order in which workgroups walk the tiles. Bit 0: 0 = token groups fastest,
+// 1 = channel tiles fastest. Bit 1: 0 = each XCD takes a contiguous range,
+// 1 = plain order.
 #ifndef QCAST_PC_ORDER
 #define QCAST_PC_ORDER 0
 #endif
+constexpr int kTG = QCAST_PC_TG;
+constexpr int kCC = QCAST_PC_CC;
 constexpr int kOrder = QCAST_PC_ORDER;
+static_assert(kTG == 1 || kTG == 2, "1 or 2 token groups per tile");
+static_assert(kCC == 8 || kCC == 16, "8 or 16 channel chunks per tile");
 
-__global__ __launch_bounds__(kThreads) void per_channel_t_kernel(
-    const uint16_t* __restrict__ x, int64_t rows, int64_t cols, int64_t ngroups,
-    int64_t ntiles, int64_t per_xcd, float floor, uint8_t* __restrict__ qT,
-    float* __restrict__ sf) {
-  __shared__ __attribute__((aligned(16))) uint32_t tile[kChannels * (kTokens / 4)];  // 8 KiB
-  __shared__ __attribute__((aligned(16))) float wave_amax[4][kChannels];
-  __shared__ float inv_s[kChannels];
+constexpr int kChannels = 8 * kCC;                  // channels per tile
+constexpr int kTileTokens = kGroupTokens * kTG;     // tokens per tile
+constexpr int kQuads = kThreads / kCC;              // token quads per pass
+constexpr int kPassTokens = 4 * kQuads;             // tokens per pass
+constexpr int kPasses = kTileTokens / kPassTokens;  // load passes per lane
+constexpr int kPassesPerGroup = kPasses / kTG;
+constexpr int kRowDw = kTileTokens / 4;             // dwords per LDS channel row
+constexpr int kRowVec = kRowDw / 4;                 // 16-byte vectors per row
+constexpr int kReadPasses = kChannels * kRowVec / kThreads;
+static_assert(kPassesPerGroup >= 1 && kReadPasses >= 1, "tile shape");
 
-  const int64_t b = blockIdx.x;
-  const int64_t tau = (kOrder & 2) ? b : (b % kXcds) * per_xcd + b / kXcds;
-  if (tau >= ntiles) return;
-  const int64_t nct = ntiles / ngroups;
-  const int64_t ct = (kOrder & 1) ? tau % nct : tau / ngroups;
-  const int64_t g = (kOrder & 1) ? tau / nct : tau - ct * ngroups;
-  const int64_t c0 = ct * kChannels;
-  const int64_t t0 = g * kTokens;
-  const int nc = (int)(cols - c0 < kChannels ? cols - c0 : kChannels);
+// Dword index of token dword d of channel row c in the swizzled tile.
+__device__ __forceinline__ int tile_index(int c, int d) {
+  return c * kRowDw + (d ^ (4 * ((c >> 3) & 7)));
+}
 
+// Position of a tile: first channel, first token, valid channels and groups.
+// Tile counts and in-tile offsets fit in 32 bits (checked by the launcher).
+struct TileCoord {
+  uint32_t c0, t0, gt;
+  int nc, ng;
+};
+
+__device__ __forceinline__ TileCoord tile_coord(uint32_t tau, uint32_t ngroups, uint32_t cols,
+                                                uint32_t nct, uint32_t ntg) {
+  TileCoord tc;
+  const uint32_t ct = (kOrder & 1) ? tau % nct : tau / ntg;
+  tc.gt = (kOrder & 1) ? tau / nct : tau - ct * ntg;
+  tc.c0 = ct * kChannels;
+  tc.t0 = tc.gt * kTileTokens;
+  tc.nc = (int)(cols - tc.c0 < (uint32_t)kChannels ? cols - tc.c0 : kChannels);
+  tc.ng = (int)(ngroups - tc.gt * kTG < (uint32_t)kTG ? ngroups - tc.gt * kTG : kTG);
+  return tc;
+}
+
+// Issue the lane's loads of a tile (zeros outside the tensor).
+__device__ __forceinline__ void load_tile(const uint16_t* __restrict__ x, uint32_t cols,
+                                          const TileCoord& tc, u32x4 (&raw)[kPasses][4]) {
   const int t = threadIdx.x;
-  const int ch = t & 7;        // channel chunk: channels c0 + 8ch .. +7
-  const int k = t >> 3;        // token quad: tokens t0 + 4k .. +3
-  const bool valid = ch * 8 < nc;
-
-  u32x4 raw[4];
-  if (valid) {
-    const uint16_t* src = x + (t0 + 4 * k) * cols + c0 + ch * 8;
+  const int ch = t % kCC;
+  const int k = t / kCC;
+  const bool valid_ch = ch * 8 < tc.nc;
+  // 64-bit tile base, 32-bit offsets inside the tile
+  const uint16_t* base = x + (uint64_t)tc.t0 * cols + tc.c0;
 #pragma unroll
-    for (int i = 0; i < 4; ++i) raw[i] = load_stream(reinterpret_cast<const u32x4*>(src + i * cols));
-  } else {
+  for (int p = 0; p < kPasses; ++p) {
+    const bool valid = valid_ch && (p / kPassesPerGroup) < tc.ng;
 #pragma unroll
-    for (int i = 0; i < 4; ++i) raw[i] = u32x4{0u, 0u, 0u, 0u};
-  }
-  float v[4][8];
-#pragma unroll
-  for (int i = 0; i < 4; ++i) unpack8(raw[i], v[i]);
-
-  // Column abs-max over the wave's 32 tokens: own 4 tokens, then the lanes
-  // holding the same channel chunk (lane ^ 8, ^ 16, ^ 32).
-  float pm[8];
-#pragma unroll
-  for (int j = 0; j < 8; ++j) {
-    const float m = fmaxf(fmaxf(fabsf(v[0][j]), fabsf(v[1][j])), fmaxf(fabsf(v[2][j]), fabsf(v[3][j])));
-    uint32_t b = __float_as_uint(m);
-    b = umax(b, dpp<kDppRor8>(b));
-    b = umax(b, (uint32_t)__shfl_xor((int)b, 16));
-    b = umax(b, (uint32_t)__shfl_xor((int)b, 32));
-    pm[j] = __uint_as_float(b);
-  }
-  const int wave = t >> 6;
-  if ((t & 63) < 8) {
-#pragma unroll
-    for (int j = 0; j < 8; ++j) wave_amax[wave][ch * 8 + j] = pm[j];
-  }
-  __syncthreads();
-  if (t < kChannels) {
-    const float m = fmaxf(fmaxf(wave_amax[0][t], wave_amax[1][t]),
-                          fmaxf(wave_amax[2][t], wave_amax[3][t]));
-    const Scale s = group_scale<kE4M3>(m, floor);
-    inv_s[t] = s.inv;
-    if (t < nc) sf[(c0 + t) * ngroups + g] = s.sf;
-  }
-  __syncthreads();
-
-  // Codes of tokens 4k..4k+3 for each of the lane's 8 channels, one dword
-  // per channel, into the swizzled [channel][token dword] tile.
-#pragma unroll
-  for (int j = 0; j < 8; ++j) {
-    const float inv = inv_s[ch * 8 + j];
-    const uint32_t word = e4m3x4(v[0][j] * inv, v[1][j] * inv, v[2][j] * inv, v[3][j] * inv);
-    const int c = ch * 8 + j;
-    tile[c * (kTokens / 4) + (k ^ (4 * ch))] = word;
-  }
-  __syncthreads();
-
-  // Read back channel rows: 8 lanes x 16 bytes per 128-token row.
-#pragma unroll
-  for (int p = 0; p < 2; ++p) {
-    const int idx = t + p * kThreads;
-    const int c = idx >> 3;
-    const int m4 = (idx & 7) * 4;
-    if (c < nc) {
-      const u32x4 val =
-          *reinterpret_cast<const u32x4*>(&tile[c * (kTokens / 4) + (m4 ^ (4 * (c >> 3)))]);
-      store_stream(reinterpret_cast<u32x4*>(qT + (c0 + c) * rows + t0 + m4 * 4), val);
+    for (int i = 0; i < 4; ++i) {
+      const uint32_t off = (uint32_t)(p * kPassTokens + 4 * k + i) * cols + ch * 8;
+      raw[p][i] = valid ? load_stream(reinterpret_cast<const u32x4*>(base + off))
+                        : u32x4{0u, 0u, 0u, 0u};
     }
+  }
+}
+
+struct Smem {
+  uint32_t tile[kChannels * kRowDw];
+  float wave_amax[kTG][4][kChannels];
+  float inv_s[kTG][kChannels];
+};
+
+// Scales, codes and stores of one tile whose values are in raw. Starts and
+// ends with the workgroup converged; the LDS is free again on return.
+__device__ __forceinline__ void process_tile(const TileCoord& tc, const u32x4 (&raw)[kPasses][4],
+                                             uint32_t rows, uint32_t ngroups, float floor,
+                                             Smem& sm, uint8_t* __restrict__ qT,
+                                             float* __restrict__ sf) {
+  const int t = threadIdx.x;
+  const int ch = t % kCC;
+  const int k = t / kCC;
+  const int wave = t >> 6;
+  // Column abs-maxima per token group, as packed 16-bit magnitudes: word w
+  // of a lane holds channels 8ch + 2w (low half) and 8ch + 2w + 1.
+#pragma unroll
+  for (int gi = 0; gi < kTG; ++gi) {
+    uint32_t m[4] = {0u, 0u, 0u, 0u};
+#pragma unroll
+    for (int pp = 0; pp < kPassesPerGroup; ++pp) {
+      const int p = gi * kPassesPerGroup + pp;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        m[0] = pk_umax16(m[0], raw[p][i].x & 0x7fff7fffu);
+        m[1] = pk_umax16(m[1], raw[p][i].y & 0x7fff7fffu);
+        m[2] = pk_umax16(m[2], raw[p][i].z & 0x7fff7fffu);
+        m[3] = pk_umax16(m[3], raw[p][i].w & 0x7fff7fffu);
+      }
+    }
+#pragma unroll
+    for (int w = 0; w < 4; ++w) {
+      if (kCC == 8) m[w] = pk_umax16(m[w], dpp<kDppRor8>(m[w]));
+      m[w] = pk_umax16(m[w], (uint32_t)__shfl_xor((int)m[w], 16));
+      m[w] = pk_umax16(m[w], (uint32_t)__shfl_xor((int)m[w], 32));
+    }
+    if ((t & 63) < kCC) {
+#pragma unroll
+      for (int w = 0; w < 4; ++w) {
+        sm.wave_amax[gi][wave][ch * 8 + 2 * w] = bf16_lo(m[w]);
+        sm.wave_amax[gi][wave][ch * 8 + 2 * w + 1] = bf16_hi(m[w]);
+      }
+    }
+  }
+  __syncthreads();
+  if (t < kTG * kChannels) {
+    const int gi = t / kChannels;
+    const int c = t % kChannels;
+    const float m = fmaxf(fmaxf(sm.wave_amax[gi][0][c], sm.wave_amax[gi][1][c]),
+                          fmaxf(sm.wave_amax[gi][2][c], sm.wave_amax[gi][3][c]));
+    const Scale s = group_scale<kE4M3>(m, floor);
+    sm.inv_s[gi][c] = s.inv;
+    if (c < tc.nc && gi < tc.ng)
+      sf[(uint64_t)tc.c0 * ngroups + (uint32_t)c * ngroups + tc.gt * kTG + gi] = s.sf;
+  }
+  __syncthreads();
+
+  // Codes: for each pass and each of the lane's 8 channels, the 4 tokens
+  // 4k..4k+3 of the pass as one dword of the channel's LDS row.
+#pragma unroll
+  for (int p = 0; p < kPasses; ++p) {
+    const int gi = p / kPassesPerGroup;
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      const float inv = sm.inv_s[gi][ch * 8 + j];
+      float y[4];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const uint32_t word = raw[p][i][j >> 1];
+        y[i] = ((j & 1) ? bf16_hi(word) : bf16_lo(word)) * inv;
+      }
+      sm.tile[tile_index(ch * 8 + j, p * (kPassTokens / 4) + k)] = e4m3x4(y[0], y[1], y[2], y[3]);
+    }
+  }
+  __syncthreads();
+
+  // Read back channel rows, 16 bytes per lane, and store them to qT.
+  uint8_t* out = qT + (uint64_t)tc.c0 * rows + tc.t0;
+#pragma unroll
+  for (int r = 0; r < kReadPasses; ++r) {
+    const int idx = t + r * kThreads;
+    const int c = idx / kRowVec;
+    const int mv = idx % kRowVec;
+    if (c < tc.nc && mv * 16 < tc.ng * kGroupTokens) {
+      const u32x4 val = *reinterpret_cast<const u32x4*>(&sm.tile[tile_index(c, 4 * mv)]);
+      store_stream(reinterpret_cast<u32x4*>(out + (uint32_t)c * rows + mv * 16), val);
+    }
+  }
+  __syncthreads();  // the LDS tile is reused by the next tile
+}
+
+// One workgroup per tile.
+__global__ __launch_bounds__(kThreads) void per_channel_t_kernel(
+    const uint16_t* __restrict__ x, uint32_t rows, uint32_t cols, uint32_t ngroups,
+    uint32_t nct, uint32_t ntiles, uint32_t per_xcd, float floor, uint8_t* __restrict__ qT,
+    float* __restrict__ sf) {
+  __shared__ __attribute__((aligned(16))) Smem sm;
+  const uint32_t b = blockIdx.x;
+  const uint32_t tau = (kOrder & 2) ? b : (b % kXcds) * per_xcd + b / kXcds;
+  if (tau >= ntiles) return;
+  const TileCoord tc = tile_coord(tau, ngroups, cols, nct, ntiles / nct);
+  u32x4 raw[kPasses][4];
+  load_tile(x, cols, tc, raw);
+  process_tile(tc, raw, rows, ngroups, floor, sm, qT, sf);
+}
+
+// Persistent workgroups, software-pipelined: the loads of a workgroup's next
+// tile are issued before the current tile is reduced, encoded and stored,
+// so reads stay in flight while the writes drain. Workgroup b works on XCD
+// b mod 8 and walks that XCD's contiguous range of tiles.
+__global__ __launch_bounds__(kThreads) void per_channel_t_pipelined_kernel(
+    const uint16_t* __restrict__ x, uint32_t rows, uint32_t cols, uint32_t ngroups,
+    uint32_t nct, uint32_t ntiles, uint32_t per_xcd, float floor, uint8_t* __restrict__ qT,
+    float* __restrict__ sf) {
+  __shared__ __attribute__((aligned(16))) Smem sm;
+  const uint32_t ntg = ntiles / nct;
+  const uint32_t xcd = blockIdx.x % kXcds;
+  const uint32_t slot = blockIdx.x / kXcds;
+  const uint32_t nslots = gridDim.x / kXcds;
+  const uint32_t xcd_end = (xcd + 1) * per_xcd < ntiles ? (xcd + 1) * per_xcd : ntiles;
+  // Strided: tiles xcd*per_xcd + slot + i*nslots. Chunked: a run of
+  // ceil(per_xcd / nslots) consecutive tiles per slot.
+  const uint32_t run = (per_xcd + nslots - 1) / nslots;
+  uint32_t tau = kChunked ? xcd * per_xcd + slot * run : xcd * per_xcd + slot;
+  const uint32_t end = kChunked ? (tau + run < xcd_end ? tau + run : xcd_end) : xcd_end;
+  const uint32_t slots = kChunked ? 1 : nslots;
+  if (tau >= end) return;
+  // Two register buffers in turn: while one tile is processed, the next
+  // tile's loads are in flight in the other.
+  TileCoord ta = tile_coord(tau, ngroups, cols, nct, ntg), tb = ta;
+  u32x4 ra[kPasses][4], rb[kPasses][4];
+  load_tile(x, cols, ta, ra);
+  while (true) {
+    tau += slots;
+    const bool more_b = tau < end;
+    if (more_b) {
+      tb = tile_coord(tau, ngroups, cols, nct, ntg);
+      load_tile(x, cols, tb, rb);
+    }
+    process_tile(ta, ra, rows, ngroups, floor, sm, qT, sf);
+    if (!more_b) break;
+    tau += slots;
+    const bool more_a = tau < end;
+    if (more_a) {
+      ta = tile_coord(tau, ngroups, cols, nct, ntg);
+      load_tile(x, cols, ta, ra);
+    }
+    process_tile(tb, rb, rows, ngroups, floor, sm, qT, sf);
+    if (!more_a) break;
   }
 }
 
@@ -136,17 +289,33 @@ __global__ __launch_bounds__(kThreads) void per_channel_t_kernel(
 hipError_t launch_per_channel_T(const void* x, int64_t rows, int64_t cols, float floor,
                                 void* qT, float* sf, hipStream_t stream,
                                 const LaunchCaps& caps) {
-  (void)caps;
-  const int64_t ngroups = rows / kTokens;
-  const int64_t nctiles = (cols + kChannels - 1) / kChannels;
-  const int64_t ntiles = ngroups * nctiles;
+  const int64_t ngroups = rows / kGroupTokens;
+  const int64_t ntg = (ngroups + kTG - 1) / kTG;
+  const int64_t nct = (cols + kChannels - 1) / kChannels;
+  const int64_t ntiles = ntg * nct;
   if (ntiles == 0) return hipSuccess;
+  // The kernels index tiles, and offsets inside a tile's rows, in 32 bits.
+  const int64_t lim = int64_t(1) << 31;
+  if (ntiles + 2 * kXcds >= lim || (int64_t)kTileTokens * cols >= lim ||
+      (int64_t)kChannels * rows >= lim || rows >= lim || cols >= lim)
+    return hipErrorInvalidValue;
   const int64_t per_xcd = (ntiles + kXcds - 1) / kXcds;
-  const int64_t grid = per_xcd * kXcds;
-  if (grid >= (int64_t(1) << 31)) return hipErrorInvalidValue;
+  if (kPipe) {
+    // kXcds * slots workgroups; each XCD's slots walk its range of tiles.
+    int64_t slots = (int64_t)caps.num_cus * kPcWgPerCu / kXcds;
+    if (slots < 1) slots = 1;
+    if (slots > per_xcd) slots = per_xcd;
+    hipLaunchKernelGGL(per_channel_t_pipelined_kernel, dim3((unsigned)(slots * kXcds)),
+                       dim3(kThreads), 0, stream, static_cast<const uint16_t*>(x),
+                       (uint32_t)rows, (uint32_t)cols, (uint32_t)ngroups, (uint32_t)nct,
+                       (uint32_t)ntiles, (uint32_t)per_xcd, floor, static_cast<uint8_t*>(qT), sf);
+    return hipGetLastError();
+  }
+  const int64_t grid = (kOrder & 2) ? ntiles : per_xcd * kXcds;
   hipLaunchKernelGGL(per_channel_t_kernel, dim3((unsigned)grid), dim3(kThreads), 0, stream,
-                     static_cast<const uint16_t*>(x), rows, cols, ngroups, ntiles, per_xcd,
-                     floor, static_cast<uint8_t*>(qT), sf);
+                     static_cast<const uint16_t*>(x), (uint32_t)rows, (uint32_t)cols,
+                     (uint32_t)ngroups, (uint32_t)nct, (uint32_t)ntiles, (uint32_t)per_xcd, floor,
+                     static_cast<uint8_t*>(qT), sf);
   return hipGetLastError();
 }
 

@@ -104,6 +104,15 @@ constexpr int kDppRor8 = 0x128;        // lane i <- (i+8) mod 16
 // canonicalisation of the moved values is needed).
 __device__ __forceinline__ uint32_t umax(uint32_t a, uint32_t b) { return a > b ? a : b; }
 
+// Packed maxima of two pairs of 16-bit values (v_pk_max_u16). On the
+// magnitude bits of two bf16 values (bits & 0x7fff7fff) this is their
+// abs-max pair: for finite bf16 the magnitude order is the unsigned order.
+typedef unsigned short u16x2 __attribute__((ext_vector_type(2)));
+__device__ __forceinline__ uint32_t pk_umax16(uint32_t a, uint32_t b) {
+  return __builtin_bit_cast(uint32_t, __builtin_elementwise_max(__builtin_bit_cast(u16x2, a),
+                                                                __builtin_bit_cast(u16x2, b)));
+}
+
 // Max over aligned runs of kLanes lanes (4, 8 or 16) of a non-negative
 // value; every lane of a run ends with the run's maximum. Runs never
 // straddle a DPP row.
