@@ -25,9 +25,12 @@
 // full row of qT (128 * kTG bytes) per channel. (The pages' transpose pads
 // its shared tile and rotates the column index for the same purpose; the
 // XOR form keeps 16-byte reads aligned.) Workgroups are numbered so that
-// each of the 8 XCDs walks a contiguous range of tiles, token groups
-// fastest, so neighbouring tiles on one XCD fill the same scale lines in its
-// L2.
+// each of the 8 XCDs walks a contiguous range of tiles, in strips of two
+// channel tiles: token group outer, channel tile inner. Workgroups started
+// together then read both 128-byte halves of the same 256-byte row segments
+// and write neighbouring 128-byte pieces of the same qT rows and scale
+// lines (measured about 3% faster than walking token groups of one channel
+// tile, and much faster than walking channel tiles first).
 #include "qcast_device.h"
 #include "qcast_kernels.h"
 
@@ -45,29 +48,18 @@ constexpr int kXcds = 8;
 #ifndef QCAST_PC_CC
 #define QCAST_PC_CC 8
 #endif
-// 1: persistent, software-pipelined workgroups (QCAST_PC_WG_PER_CU per CU);
-// 0: one workgroup per tile.
-#ifndef QCAST_PC_PIPE
-#define QCAST_PC_PIPE 0
-#endif
-#ifndef QCAST_PC_WG_PER_CU
-#define QCAST_PC_WG_PER_CU 8
-#endif
-// Tiles of a persistent workgroup: 0 = strided over its XCD's range,
-// 1 = a contiguous chunk of that range (consecutive token groups of the same
-// channels, so the workgroup fills its qT rows front to back).
-#ifndef QCAST_PC_CHUNKED
-#define QCAST_PC_CHUNKED 0
-#endif
-constexpr int kPipe = QCAST_PC_PIPE;
-constexpr int kChunked = QCAST_PC_CHUNKED;
-constexpr int kPcWgPerCu = QCAST_PC_WG_PER_CU;
 // Order in which workgroups walk the tiles. Bit 0: 0 = token groups fastest,
 // 1 = channel tiles fastest. Bit 1: 0 = each XCD takes a contiguous range,
-// 1 = plain order.
+// 1 = plain order. Bit 2: strips of QCAST_PC_STRIP channel tiles, token
+// group outer and channel tile inner inside a strip (bit 0 ignored), so the
+// tiles in flight cover a compact block of both the input and the output.
 #ifndef QCAST_PC_ORDER
-#define QCAST_PC_ORDER 0
+#define QCAST_PC_ORDER 4
 #endif
+#ifndef QCAST_PC_STRIP
+#define QCAST_PC_STRIP 2
+#endif
+constexpr uint32_t kStrip = QCAST_PC_STRIP;
 constexpr int kTG = QCAST_PC_TG;
 constexpr int kCC = QCAST_PC_CC;
 constexpr int kOrder = QCAST_PC_ORDER;
@@ -100,8 +92,17 @@ struct TileCoord {
 __device__ __forceinline__ TileCoord tile_coord(uint32_t tau, uint32_t ngroups, uint32_t cols,
                                                 uint32_t nct, uint32_t ntg) {
   TileCoord tc;
-  const uint32_t ct = (kOrder & 1) ? tau % nct : tau / ntg;
-  tc.gt = (kOrder & 1) ? tau / nct : tau - ct * ntg;
+  uint32_t ct;
+  if (kOrder & 4) {
+    const uint32_t strip = tau / (kStrip * ntg);
+    const uint32_t width = nct - strip * kStrip < kStrip ? nct - strip * kStrip : kStrip;
+    const uint32_t rem = tau - strip * kStrip * ntg;
+    tc.gt = rem / width;
+    ct = strip * kStrip + (rem - tc.gt * width);
+  } else {
+    ct = (kOrder & 1) ? tau % nct : tau / ntg;
+    tc.gt = (kOrder & 1) ? tau / nct : tau - ct * ntg;
+  }
   tc.c0 = ct * kChannels;
   tc.t0 = tc.gt * kTileTokens;
   tc.nc = (int)(cols - tc.c0 < (uint32_t)kChannels ? cols - tc.c0 : kChannels);
@@ -238,57 +239,12 @@ __global__ __launch_bounds__(kThreads) void per_channel_t_kernel(
   process_tile(tc, raw, rows, ngroups, floor, sm, qT, sf);
 }
 
-// Persistent workgroups, software-pipelined: the loads of a workgroup's next
-// tile are issued before the current tile is reduced, encoded and stored,
-// so reads stay in flight while the writes drain. Workgroup b works on XCD
-// b mod 8 and walks that XCD's contiguous range of tiles.
-__global__ __launch_bounds__(kThreads) void per_channel_t_pipelined_kernel(
-    const uint16_t* __restrict__ x, uint32_t rows, uint32_t cols, uint32_t ngroups,
-    uint32_t nct, uint32_t ntiles, uint32_t per_xcd, float floor, uint8_t* __restrict__ qT,
-    float* __restrict__ sf) {
-  __shared__ __attribute__((aligned(16))) Smem sm;
-  const uint32_t ntg = ntiles / nct;
-  const uint32_t xcd = blockIdx.x % kXcds;
-  const uint32_t slot = blockIdx.x / kXcds;
-  const uint32_t nslots = gridDim.x / kXcds;
-  const uint32_t xcd_end = (xcd + 1) * per_xcd < ntiles ? (xcd + 1) * per_xcd : ntiles;
-  // Strided: tiles xcd*per_xcd + slot + i*nslots. Chunked: a run of
-  // ceil(per_xcd / nslots) consecutive tiles per slot.
-  const uint32_t run = (per_xcd + nslots - 1) / nslots;
-  uint32_t tau = kChunked ? xcd * per_xcd + slot * run : xcd * per_xcd + slot;
-  const uint32_t end = kChunked ? (tau + run < xcd_end ? tau + run : xcd_end) : xcd_end;
-  const uint32_t slots = kChunked ? 1 : nslots;
-  if (tau >= end) return;
-  // Two register buffers in turn: while one tile is processed, the next
-  // tile's loads are in flight in the other.
-  TileCoord ta = tile_coord(tau, ngroups, cols, nct, ntg), tb = ta;
-  u32x4 ra[kPasses][4], rb[kPasses][4];
-  load_tile(x, cols, ta, ra);
-  while (true) {
-    tau += slots;
-    const bool more_b = tau < end;
-    if (more_b) {
-      tb = tile_coord(tau, ngroups, cols, nct, ntg);
-      load_tile(x, cols, tb, rb);
-    }
-    process_tile(ta, ra, rows, ngroups, floor, sm, qT, sf);
-    if (!more_b) break;
-    tau += slots;
-    const bool more_a = tau < end;
-    if (more_a) {
-      ta = tile_coord(tau, ngroups, cols, nct, ntg);
-      load_tile(x, cols, ta, ra);
-    }
-    process_tile(tb, rb, rows, ngroups, floor, sm, qT, sf);
-    if (!more_a) break;
-  }
-}
-
 }  // namespace
 
 hipError_t launch_per_channel_T(const void* x, int64_t rows, int64_t cols, float floor,
                                 void* qT, float* sf, hipStream_t stream,
                                 const LaunchCaps& caps) {
+  (void)caps;
   const int64_t ngroups = rows / kGroupTokens;
   const int64_t ntg = (ngroups + kTG - 1) / kTG;
   const int64_t nct = (cols + kChannels - 1) / kChannels;
@@ -300,17 +256,6 @@ hipError_t launch_per_channel_T(const void* x, int64_t rows, int64_t cols, float
       (int64_t)kChannels * rows >= lim || rows >= lim || cols >= lim)
     return hipErrorInvalidValue;
   const int64_t per_xcd = (ntiles + kXcds - 1) / kXcds;
-  if (kPipe) {
-    // kXcds * slots workgroups; each XCD's slots walk its range of tiles.
-    int64_t slots = (int64_t)caps.num_cus * kPcWgPerCu / kXcds;
-    if (slots < 1) slots = 1;
-    if (slots > per_xcd) slots = per_xcd;
-    hipLaunchKernelGGL(per_channel_t_pipelined_kernel, dim3((unsigned)(slots * kXcds)),
-                       dim3(kThreads), 0, stream, static_cast<const uint16_t*>(x),
-                       (uint32_t)rows, (uint32_t)cols, (uint32_t)ngroups, (uint32_t)nct,
-                       (uint32_t)ntiles, (uint32_t)per_xcd, floor, static_cast<uint8_t*>(qT), sf);
-    return hipGetLastError();
-  }
   const int64_t grid = (kOrder & 2) ? ntiles : per_xcd * kXcds;
   hipLaunchKernelGGL(per_channel_t_kernel, dim3((unsigned)grid), dim3(kThreads), 0, stream,
                      static_cast<const uint16_t*>(x), (uint32_t)rows, (uint32_t)cols,
