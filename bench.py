@@ -246,6 +246,7 @@ def main():
             "median_us": round(ms[len(ms) // 2] * 1e3, 2),
             "GBps": round(b / (avg * 1e-3) / 1e9, 1),
             "frac": round(b / (avg * 1e-3) / 1e9 / PEAK_HBM_GBS, 4),
+            "rows_per_s": round(wl.rows / (avg * 1e-3)),
         }
     for row in ev:
         for e in row:

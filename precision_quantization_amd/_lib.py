@@ -1,7 +1,7 @@
 """Loading of libqcast.so and the ctypes signatures of its C ABI.
 
-The library must have been built in-tree (``__graft_entry__.build()`` or
-``python -m precision_quantization_amd.build``) from the sources beside it:
+The library must have been built in-tree (``python -m
+precision_quantization_amd.build``) from the sources beside it:
 a missing or stale library is an error, never a fallback.
 """
 import ctypes
@@ -40,7 +40,7 @@ def load():
         return _lib
     import os
     if not os.path.exists(_build.LIB):
-        raise QcastError(-1, f"{_build.LIB} is not built; run __graft_entry__.build()")
+        raise QcastError(-1, f"{_build.LIB} is not built; run python -m precision_quantization_amd.build")
     if not _build.is_current():
         raise QcastError(-1, f"{_build.LIB} was built from other sources; rebuild it")
     lib = ctypes.CDLL(_build.LIB)
