@@ -17,7 +17,10 @@ from . import build as _build
 
 FMT_E4M3 = 1
 FMT_E2M1 = 2
-_FMT_NAMES = {"e4m3": FMT_E4M3, "e2m1": FMT_E2M1}
+FMT_E5M2 = 3
+OUT_BF16 = 1
+OUT_F32 = 2
+_FMT_NAMES = {"e4m3": FMT_E4M3, "e2m1": FMT_E2M1, "e5m2": FMT_E5M2}
 
 _lib = None
 
@@ -57,6 +60,8 @@ def _load():
         "oracle_per_block": ([vp, i64, i64, i32, i32, f32, vp, vp], i32),
         "oracle_per_channel_T": ([vp, i64, i64, i32, i32, f32, vp, vp], i32),
         "oracle_dequant_per_token": ([vp, vp, i64, i64, i32, i32, vp], i32),
+        "oracle_cast_back": ([vp, vp, i64, i64, i32, i32, i32, vp], i32),
+        "oracle_f32_to_bf16": ([f32], ctypes.c_uint16),
     }
     for name, (args, res) in sig.items():
         fn = getattr(lib, name)
@@ -87,7 +92,7 @@ def _f32(x):
 
 
 def _code_shape(fmt, rows, cols):
-    return (rows, cols) if fmt == FMT_E4M3 else (rows, cols // 2)
+    return (rows, cols // 2) if fmt == FMT_E2M1 else (rows, cols)
 
 
 def format_max(fmt):
@@ -200,3 +205,24 @@ def dequant_per_token(q, sf, cols, fmt="e4m3", group=128):
     _check(_load().oracle_dequant_per_token(_ptr(q), _ptr(sf), rows, cols, f, group, _ptr(out)),
            "dequant_per_token")
     return out
+
+
+def cast_back(q, sf, cols, fmt="e4m3", group=128, out_dtype="bf16"):
+    """Per-token codes + scales -> bf16 (uint16 bit patterns) or fp32."""
+    f = fmt_id(fmt)
+    q = np.ascontiguousarray(q, dtype=np.uint8)
+    sf = _f32(sf)
+    rows = q.shape[0]
+    od = OUT_BF16 if out_dtype == "bf16" else OUT_F32
+    out = np.zeros((rows, cols), np.uint16 if od == OUT_BF16 else np.float32)
+    _check(_load().oracle_cast_back(_ptr(q), _ptr(sf), rows, cols, f, group, od, _ptr(out)),
+           "cast_back")
+    return out
+
+
+def f32_to_bf16(x):
+    """fp32 values -> bf16 bit patterns (uint16), round to nearest even."""
+    x = _f32(x)
+    lib = _load()
+    return np.array([lib.oracle_f32_to_bf16(float(v)) for v in x.ravel()],
+                    np.uint16).reshape(x.shape)

@@ -17,9 +17,10 @@
  *  [NEWS]  "刚刚！DeepSeek开源高性能GPU算子库TileKernels", item 2 (quant/:
  *          per-token, per-block and per-channel granularities).
  * The number formats are the ones [WALK] §3.1 names, float8_e4m3fn and
- * float4_e2m1fn; their bit layouts follow the OCP 8-bit floating point
- * specification (E4M3, "fn": no infinities, one NaN pattern per sign) and the
- * OCP Microscaling specification (E2M1: no infinities, no NaN).
+ * float4_e2m1fn, plus E5M2 from the format list of [SPLIT] §四 A; their bit
+ * layouts follow the OCP 8-bit floating point specification (E4M3, "fn": no
+ * infinities, one NaN pattern per sign; E5M2: IEEE-like with infinities and
+ * NaNs) and the OCP Microscaling specification (E2M1: no infinities, no NaN).
  *
  * Readings where the pages are silent (each is listed in the design notes):
  *  - rounding is to nearest, ties to the code with an even mantissa;
@@ -30,7 +31,11 @@
  *    ([WALK] §3.2 multiplies by the inverse scale);
  *  - SwiGLU values stay fp32 and are never rounded to bf16;
  *  - NaN inputs are not defined by the pages; this oracle maps them to the
- *    E4M3 NaN code and, for E2M1, to the saturated maximum (not graded).
+ *    E4M3 NaN code and, for E2M1, to the saturated maximum (not graded);
+ *  - [WALK] §3.1 gives floors for E4M3 and E2M1 only; E5M2, the other 8-bit
+ *    format, takes the E4M3 floor 1e-4;
+ *  - cast_back is the fp32 product decode(code) * sf, rounded to bf16 to
+ *    nearest even when bf16 output is asked for.
  *
  * Arithmetic discipline: plain C++ on one thread, fp32 where the method is
  * fp32 (the scale, the inverse, the scaled value, SwiGLU) with no
@@ -60,13 +65,14 @@ float bf16_value(uint16_t h) { return f32_from_bits(static_cast<uint32_t>(h) << 
 /* Formats                                                                   */
 /* ------------------------------------------------------------------------ */
 
-/* The non-negative finite values of a format, in code order. For both formats
+/* The non-negative finite values of a format, in code order. For every format
  * the codes 0..n-1 are ordered by magnitude, so index == code. */
 struct FormatTable {
   int n = 0;                 /* number of non-negative finite codes */
   double value[128] = {};    /* value[code] */
   uint8_t sign_bit = 0;      /* bit that makes a code negative */
   uint8_t nan_code = 0;      /* positive NaN code, or the max code if none */
+  int inf_code = -1;         /* positive infinity code, -1 if none */
   float max = 0.0f;          /* largest finite magnitude */
   float default_floor = 0.0f;
 };
@@ -103,6 +109,28 @@ FormatTable make_e4m3() {
   return t;
 }
 
+/* E5M2 (OCP FP8): s eeeee mm, exponent bias 15. Exponent field 0 holds the
+ * subnormals m * 2^-16; fields 1..30 hold (1 + m/4) * 2^(e-15); field 31 is
+ * infinity (m = 0) or NaN. */
+double e5m2_magnitude(int code7) {
+  const int e = (code7 >> 2) & 0x1F;
+  const int m = code7 & 0x3;
+  if (e == 0) return std::ldexp(static_cast<double>(m), -16);
+  return std::ldexp(1.0 + m / 4.0, e - 15);
+}
+
+FormatTable make_e5m2() {
+  FormatTable t;
+  t.n = 124; /* 0x00 .. 0x7B; 0x7C is infinity, 0x7D..0x7F NaN */
+  for (int c = 0; c < t.n; ++c) t.value[c] = e5m2_magnitude(c);
+  t.sign_bit = 0x80;
+  t.nan_code = 0x7F;
+  t.inf_code = 0x7C;
+  t.max = static_cast<float>(t.value[t.n - 1]); /* 57344 */
+  t.default_floor = 1e-4f;
+  return t;
+}
+
 FormatTable make_e2m1() {
   FormatTable t;
   t.n = 8;
@@ -119,8 +147,10 @@ FormatTable make_e2m1() {
 const FormatTable* table_for(int fmt) {
   static const FormatTable e4m3 = make_e4m3();
   static const FormatTable e2m1 = make_e2m1();
+  static const FormatTable e5m2 = make_e5m2();
   if (fmt == ORACLE_FMT_E4M3) return &e4m3;
   if (fmt == ORACLE_FMT_E2M1) return &e2m1;
+  if (fmt == ORACLE_FMT_E5M2) return &e5m2;
   return nullptr;
 }
 
@@ -152,6 +182,7 @@ uint8_t encode(const FormatTable& t, float y) {
 float decode(const FormatTable& t, uint8_t code) {
   const uint8_t magnitude_code = code & static_cast<uint8_t>(t.sign_bit - 1);
   const bool negative = (code & t.sign_bit) != 0;
+  if (magnitude_code == t.inf_code) return negative ? -HUGE_VALF : HUGE_VALF;
   if (magnitude_code >= t.n) return std::nanf("");
   const float v = static_cast<float>(t.value[magnitude_code]);
   return negative ? -v : v;
@@ -199,7 +230,7 @@ Scale scale_from_amax(const FormatTable& t, float amax, float floor) {
  * takes a byte per code; E2M1 packs column 2k into the low nibble and 2k+1
  * into the high nibble of byte k of the row. */
 void put_code(int fmt, uint8_t* q, int64_t cols, int64_t row, int64_t col, uint8_t code) {
-  if (fmt == ORACLE_FMT_E4M3) {
+  if (fmt != ORACLE_FMT_E2M1) {
     q[row * cols + col] = code;
   } else {
     uint8_t& b = q[row * (cols / 2) + col / 2];
@@ -209,7 +240,7 @@ void put_code(int fmt, uint8_t* q, int64_t cols, int64_t row, int64_t col, uint8
 }
 
 uint8_t get_code(int fmt, const uint8_t* q, int64_t cols, int64_t row, int64_t col) {
-  if (fmt == ORACLE_FMT_E4M3) return q[row * cols + col];
+  if (fmt != ORACLE_FMT_E2M1) return q[row * cols + col];
   const uint8_t b = q[row * (cols / 2) + col / 2];
   return (col % 2 == 0) ? (b & 0x0F) : (b >> 4);
 }
@@ -320,7 +351,7 @@ int oracle_per_token(const uint16_t* x, int64_t rows, int64_t cols, int fmt, int
   if (fmt == ORACLE_FMT_E2M1 && group % 2 != 0) return ORACLE_ERR_GROUP;
   const float floor = floor_for(*table_for(fmt), clamp_min);
   std::vector<float> row(static_cast<size_t>(cols));
-  const int64_t code_bytes = (fmt == ORACLE_FMT_E4M3) ? cols : cols / 2;
+  const int64_t code_bytes = (fmt == ORACLE_FMT_E2M1) ? cols / 2 : cols;
   const int64_t groups = cols / group;
   for (int64_t r = 0; r < rows; ++r) {
     for (int64_t c = 0; c < cols; ++c) row[c] = bf16_value(x[r * cols + c]);
@@ -359,7 +390,7 @@ int oracle_swiglu_per_token(const uint16_t* h, int64_t rows, int64_t cols, const
   if (fmt == ORACLE_FMT_E2M1 && group % 2 != 0) return ORACLE_ERR_GROUP;
   const float floor = floor_for(*table_for(fmt), clamp_min);
   std::vector<float> v(static_cast<size_t>(cols));
-  const int64_t code_bytes = (fmt == ORACLE_FMT_E4M3) ? cols : cols / 2;
+  const int64_t code_bytes = (fmt == ORACLE_FMT_E2M1) ? cols / 2 : cols;
   const int64_t groups = cols / group;
   for (int64_t r = 0; r < rows; ++r) {
     oracle_swiglu_values(h + r * 2 * cols, 1, cols, w ? w + r : nullptr, v.data());
@@ -435,6 +466,34 @@ int oracle_dequant_per_token(const uint8_t* q, const float* sf, int64_t rows, in
   for (int64_t r = 0; r < rows; ++r)
     for (int64_t c = 0; c < cols; ++c)
       out[r * cols + c] = decode(t, get_code(fmt, q, cols, r, c)) * sf[r * groups + c / group];
+  return ORACLE_OK;
+}
+
+uint16_t oracle_f32_to_bf16(float f) {
+  /* Round to nearest even on the 16 bits that are dropped: add 0x7FFF plus
+   * the lowest kept bit, then truncate. NaNs are returned quiet. */
+  uint32_t u;
+  std::memcpy(&u, &f, sizeof u);
+  if ((u & 0x7FFFFFFFu) > 0x7F800000u) return static_cast<uint16_t>((u >> 16) | 0x0040u);
+  const uint32_t lsb = (u >> 16) & 1u;
+  u += 0x7FFFu + lsb;
+  return static_cast<uint16_t>(u >> 16);
+}
+
+int oracle_cast_back(const uint8_t* q, const float* sf, int64_t rows, int64_t cols, int fmt,
+                     int group, int out_dtype, void* out) {
+  const int rc = check_common(q, sf, out, fmt, group);
+  if (rc != ORACLE_OK) return rc;
+  if (rows < 0 || cols < 0 || cols % group != 0) return ORACLE_ERR_SHAPE;
+  if (out_dtype != ORACLE_OUT_BF16 && out_dtype != ORACLE_OUT_F32) return ORACLE_ERR_FORMAT;
+  const FormatTable& t = *table_for(fmt);
+  const int64_t groups = cols / group;
+  for (int64_t r = 0; r < rows; ++r)
+    for (int64_t c = 0; c < cols; ++c) {
+      const float v = decode(t, get_code(fmt, q, cols, r, c)) * sf[r * groups + c / group];
+      if (out_dtype == ORACLE_OUT_F32) static_cast<float*>(out)[r * cols + c] = v;
+      else static_cast<uint16_t*>(out)[r * cols + c] = oracle_f32_to_bf16(v);
+    }
   return ORACLE_OK;
 }
 

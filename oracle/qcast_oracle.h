@@ -33,7 +33,8 @@ enum {
   ORACLE_ERR_FPENV = 7 /* FTZ/DAZ set or rounding mode not nearest */
 };
 
-enum { ORACLE_FMT_E4M3 = 1, ORACLE_FMT_E2M1 = 2 };
+enum { ORACLE_FMT_E4M3 = 1, ORACLE_FMT_E2M1 = 2, ORACLE_FMT_E5M2 = 3 };
+enum { ORACLE_OUT_BF16 = 1, ORACLE_OUT_F32 = 2 };
 
 int oracle_version(void);
 
@@ -83,6 +84,15 @@ int oracle_per_channel_T(const uint16_t* x, int64_t rows, int64_t cols, int fmt,
 /* Dequantize per-token codes: out[r][c] = decode(q[r][c]) * sf[r][c/group] (fp32). */
 int oracle_dequant_per_token(const uint8_t* q, const float* sf, int64_t rows, int64_t cols,
                              int fmt, int group, float* out);
+
+/* cast_back of per-token codes: the fp32 product decode(q) * sf, written as
+ * fp32 (out_dtype ORACLE_OUT_F32, out is float*) or rounded to bf16 with
+ * round-to-nearest-even (ORACLE_OUT_BF16, out is uint16_t* bit patterns). */
+int oracle_cast_back(const uint8_t* q, const float* sf, int64_t rows, int64_t cols, int fmt,
+                     int group, int out_dtype, void* out);
+
+/* fp32 -> bf16 bit pattern, round to nearest even (NaN kept quiet). */
+uint16_t oracle_f32_to_bf16(float f);
 
 #ifdef __cplusplus
 }

@@ -30,7 +30,19 @@ CASES = {
     "per_block_256x512": lambda: workloads.weight_block(rows=256, cols=512),
     "per_channel_T_256x384": lambda: workloads.activation_channel(rows=256, cols=384),
     "e2m1_r16": lambda: workloads.student_t(rows=16),
+    "per_token_hidden_r64_e5m2": lambda: _fmt(workloads.per_token_hidden(rows=64), "e5m2"),
+    "cast_back_bf16_r64": lambda: _op(workloads.per_token_hidden(rows=64), "cast_back"),
 }
+
+
+def _fmt(wl, fmt):
+    wl.fmt = fmt
+    return wl
+
+
+def _op(wl, op):
+    wl.op = op
+    return wl
 
 
 def digest(*arrays):
@@ -52,6 +64,9 @@ def run_case(wl):
         q, sf = oracle.per_block(x, wl.fmt, wl.group)
     elif wl.op == "per_channel_T":
         q, sf = oracle.per_channel_T(x, wl.fmt, wl.group)
+    elif wl.op == "cast_back":
+        q, sf = oracle.per_token(x, wl.fmt, wl.group)
+        q = oracle.cast_back(q, sf, x.shape[1], wl.fmt, wl.group, "bf16")
     else:
         raise ValueError(wl.op)
     return q, sf

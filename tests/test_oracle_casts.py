@@ -19,9 +19,9 @@ import oracle
 from precision_quantization_amd import workloads
 
 GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
-FMAX = {"e4m3": 448.0, "e2m1": 6.0}
-MAXCODE = {"e4m3": 0x7E, "e2m1": 0x7}
-SIGN = {"e4m3": 0x80, "e2m1": 0x08}
+FMAX = {"e4m3": 448.0, "e2m1": 6.0, "e5m2": 57344.0}
+MAXCODE = {"e4m3": 0x7E, "e2m1": 0x7, "e5m2": 0x7B}
+SIGN = {"e4m3": 0x80, "e2m1": 0x08, "e5m2": 0x80}
 
 
 def f32(x):
@@ -68,7 +68,7 @@ def test_page_facts_floors_and_shapes():
 
 # ------------------------------------------------------------ scale
 
-@pytest.mark.parametrize("fmt", ["e4m3", "e2m1"])
+@pytest.mark.parametrize("fmt", ["e4m3", "e2m1", "e5m2"])
 def test_scale_closed_form(fmt):
     # sf = RN(a / M) and sf_inv = RN(1 / sf): computing the quotient in double
     # and rounding once to fp32 gives the correctly rounded fp32 quotient
@@ -112,12 +112,11 @@ def small_rows(seed, rows, cols, scale=1.0):
 
 
 @pytest.mark.parametrize("fmt,group", [("e4m3", 128), ("e4m3", 32), ("e4m3", 64), ("e2m1", 32),
-                                       ("e2m1", 128)])
+                                       ("e2m1", 128), ("e5m2", 128), ("e5m2", 32)])
 def test_per_token_against_brute_force(fmt, group):
     """Brute force: scale from the abs-max in double, every element encoded by
     exhaustive nearest search (test_oracle_codec pins that search)."""
-    from test_oracle_codec import brute_force_encode, e4m3_magnitudes_from_torch, \
-        E2M1_MAGNITUDES
+    from test_oracle_codec import brute_force_encode, magnitudes
     x = small_rows(5, 6, 256)
     q, sf = oracle.per_token(x, fmt, group)
     xf = bf16_to_f32(x).reshape(6, 256 // group, group)
@@ -127,17 +126,16 @@ def test_per_token_against_brute_force(fmt, group):
     assert np.array_equal(sf.view(np.uint32), sf_ref.view(np.uint32))
     inv = (1.0 / sf_ref.astype(np.float64)).astype(np.float32)
     y = (xf.astype(np.float64) * inv[..., None].astype(np.float64)).astype(np.float32)
-    mags = e4m3_magnitudes_from_torch() if fmt == "e4m3" else E2M1_MAGNITUDES
-    codes = brute_force_encode(y.ravel(), mags, SIGN[fmt]).reshape(6, 256)
-    got = q if fmt == "e4m3" else unpack_e2m1(q)
+    codes = brute_force_encode(y.ravel(), magnitudes(fmt), SIGN[fmt]).reshape(6, 256)
+    got = unpack_e2m1(q) if fmt == "e2m1" else q
     assert np.array_equal(got, codes)
 
 
-@pytest.mark.parametrize("fmt,group", [("e4m3", 128), ("e2m1", 32)])
+@pytest.mark.parametrize("fmt,group", [("e4m3", 128), ("e2m1", 32), ("e5m2", 128)])
 def test_amax_element_maps_to_format_max(fmt, group):
     x = small_rows(8, 64, 512)
     q, sf = oracle.per_token(x, fmt, group)
-    codes = q if fmt == "e4m3" else unpack_e2m1(q)
+    codes = unpack_e2m1(q) if fmt == "e2m1" else q
     xf = bf16_to_f32(x).reshape(64, -1, group)
     c = codes.reshape(64, -1, group)
     arg = np.abs(xf).argmax(axis=2)
@@ -159,7 +157,7 @@ def test_error_bound(fmt, group):
     assert (np.abs(xf - deq) <= bound).all()
 
 
-@pytest.mark.parametrize("fmt,group", [("e4m3", 128), ("e2m1", 32)])
+@pytest.mark.parametrize("fmt,group", [("e4m3", 128), ("e2m1", 32), ("e5m2", 128)])
 def test_dequantize_requantize_idempotent(fmt, group):
     x = small_rows(10, 4, 256)
     # add a floor-active group
@@ -172,6 +170,25 @@ def test_dequantize_requantize_idempotent(fmt, group):
     assert ulp.max() <= 1
 
 
+@pytest.mark.parametrize("fmt,group", [("e4m3", 128), ("e2m1", 32), ("e5m2", 128)])
+@pytest.mark.parametrize("out_dtype", ["f32", "bf16"])
+def test_cast_back(fmt, group, out_dtype):
+    """fp32: decode(q) * sf, the product taken exactly in double and rounded
+    once (both factors are fp32, so the double product is exact); bf16: that
+    fp32 value through torch's float32 -> bfloat16 conversion."""
+    x = small_rows(14, 8, 256)
+    q, sf = oracle.per_token(x, fmt, group)
+    out = oracle.cast_back(q, sf, 256, fmt, group, out_dtype)
+    codes = q if fmt != "e2m1" else unpack_e2m1(q)
+    dec = oracle.decode(fmt, codes).astype(np.float64)
+    ref = (dec * np.repeat(sf.astype(np.float64), group, axis=1)).astype(np.float32)
+    if out_dtype == "f32":
+        assert np.array_equal(out.view(np.uint32), ref.view(np.uint32))
+    else:
+        theirs = torch.from_numpy(ref).to(torch.bfloat16).view(torch.int16).numpy().view(np.uint16)
+        assert np.array_equal(out, theirs)
+
+
 def test_zero_and_negative_zero_groups():
     x = np.zeros((2, 256), np.uint16)
     x[1] = 0x8000  # -0.0
@@ -181,6 +198,9 @@ def test_zero_and_negative_zero_groups():
     q, sf = oracle.per_token(x, "e2m1", 32)
     assert (q[0] == 0).all() and (q[1] == 0x88).all()
     assert (sf.view(np.uint32) == 0x00800000).all()
+    q, sf = oracle.per_token(x, "e5m2", 128)
+    assert (q[0] == 0).all() and (q[1] == 0x80).all()
+    assert (sf == np.float32(np.float32(1e-4) / np.float32(57344.0))).all()
 
 
 def test_power_of_two_scale_groups_hit_midpoints():
