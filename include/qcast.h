@@ -21,9 +21,11 @@
  *     sf_inv = 1 / sf                                fp32, IEEE division
  *     code_i = encode(x_i * sf_inv)                  fp32 product, then
  *              round to nearest (ties to even mantissa), saturating, sign kept
- * fmt_max is 448 for E4M3 and 6 for E2M1. The default floor
- * ([WALK] §3.1) is 1e-4f for E4M3 and 6 * 2^-126 for E2M1; a clamp_min > 0
- * replaces it.
+ * fmt_max is 448 for E4M3, 57344 for E5M2 and 6 for E2M1. The default floor
+ * ([WALK] §3.1) is 1e-4f for E4M3 and 6 * 2^-126 for E2M1; the page names no
+ * floor for E5M2, which takes the E4M3 one, 1e-4f. A clamp_min > 0 replaces
+ * the default. Formats: OCP E4M3 ("fn") and E5M2, OCP MX E2M1; E5M2 is in
+ * the format list of [SPLIT] §四 A.
  *
  * Conventions shared by every entry point:
  *  - Every data pointer is a DEVICE pointer on the current HIP device, owned
@@ -68,15 +70,20 @@ typedef enum {
   QCAST_ERR_DEVICE = 7  /* no usable HIP device */
 } qcast_status;
 
-typedef enum { QCAST_FMT_E4M3 = 1, QCAST_FMT_E2M1 = 2 } qcast_fmt;
+typedef enum { QCAST_FMT_E4M3 = 1, QCAST_FMT_E2M1 = 2, QCAST_FMT_E5M2 = 3 } qcast_fmt;
+
+/* Output type of qcast_cast_back. */
+typedef enum { QCAST_OUT_BF16 = 1, QCAST_OUT_F32 = 2 } qcast_out_dtype;
 
 /*
  * Per-token cast ([WALK] quick start and §3.2; [SPLIT] §二 per_token_cast).
  * One scale per run of `group` consecutive elements of a row (the page's
  * num_per_channels).
  *   x     [rows, cols] bf16.
- *   q     E4M3: [rows, cols] bytes.  E2M1: [rows, cols/2] bytes, column 2k in
- *         the low nibble of byte k and column 2k+1 in its high nibble.
+ *   fmt   QCAST_FMT_E4M3, QCAST_FMT_E5M2 or QCAST_FMT_E2M1.
+ *   q     E4M3 / E5M2: [rows, cols] bytes.  E2M1: [rows, cols/2] bytes,
+ *         column 2k in the low nibble of byte k and column 2k+1 in its high
+ *         nibble.
  *   sf    [rows, cols/group] fp32.
  *   group 32, 64 or 128; cols % group == 0.
  *   clamp_min  <= 0 selects the format's default floor.
@@ -100,10 +107,10 @@ QCAST_API int qcast_e2m1(const void* x, int64_t rows, int64_t cols, int group, f
  *   row_weight [rows] fp32 routing weight, or NULL for none.
  *   v[r][j] = (g / (1 + exp(-g))) * u * row_weight[r], fp32, never rounded
  *   to bf16; then the per-token cast of v with `group`.
- *   q [rows, cols] E4M3 bytes; sf [rows, cols/group] fp32.
- *   fmt must be QCAST_FMT_E4M3. The exponential and the division use the
- *   hardware's fast forms, so the codes may differ from an exact evaluation
- *   by one step where v lies next to a rounding midpoint.
+ *   q [rows, cols] bytes; sf [rows, cols/group] fp32.
+ *   fmt QCAST_FMT_E4M3 or QCAST_FMT_E5M2. The exponential and the division
+ *   use the hardware's fast forms, so the codes may differ from an exact
+ *   evaluation by one step where v lies next to a rounding midpoint.
  */
 QCAST_API int qcast_swiglu_per_token(const void* h, int64_t rows, int64_t cols, const float* row_weight,
                            int fmt, int group, float clamp_min, void* q, float* sf,
@@ -114,8 +121,8 @@ QCAST_API int qcast_swiglu_per_token(const void* h, int64_t rows, int64_t cols, 
  * "刚刚！DeepSeek开源高性能GPU算子库TileKernels", item 2, per-block granularity).
  * One scale per block x block tile.
  *   x  [rows, cols] bf16; rows % block == 0 and cols % block == 0.
- *   q  [rows, cols] E4M3 bytes; sf [rows/block, cols/block] fp32.
- *   block must be 128; fmt must be QCAST_FMT_E4M3.
+ *   q  [rows, cols] bytes; sf [rows/block, cols/block] fp32.
+ *   block must be 128; fmt QCAST_FMT_E4M3 or QCAST_FMT_E5M2.
  */
 QCAST_API int qcast_per_block(const void* x, int64_t rows, int64_t cols, int fmt, int block,
                     float clamp_min, void* q, float* sf, void* stream);
@@ -127,13 +134,25 @@ QCAST_API int qcast_per_block(const void* x, int64_t rows, int64_t cols, int fmt
  *   x   [rows, cols] bf16, rows = tokens, cols = channels.
  *   The scale groups run along tokens: group g of channel c is
  *   x[g*group .. g*group + group - 1][c].
- *   qT  [cols, rows] E4M3 bytes: qT[c][t] is the code of x[t][c].
+ *   qT  [cols, rows] bytes: qT[c][t] is the code of x[t][c].
  *   sf  [cols, rows/group] fp32.
  *   group must be 128; rows % group == 0; cols % 8 == 0;
- *   fmt must be QCAST_FMT_E4M3.
+ *   fmt QCAST_FMT_E4M3 or QCAST_FMT_E5M2.
  */
 QCAST_API int qcast_per_channel_T(const void* x, int64_t rows, int64_t cols, int fmt, int group,
                         float clamp_min, void* qT, float* sf, void* stream);
+
+/*
+ * cast_back: dequantize per-token codes ([SPLIT] §二 cast_back).
+ *   out[r][c] = decode(q[r][c]) * sf[r][c/group], one fp32 product, rounded
+ *   to bf16 (nearest even) when out_dtype is QCAST_OUT_BF16.
+ *   q    codes as qcast_per_token writes them for `fmt` and `group`.
+ *   sf   [rows, cols/group] fp32.
+ *   out  [rows, cols] bf16 (QCAST_OUT_BF16) or fp32 (QCAST_OUT_F32).
+ *   group 32, 64 or 128; cols % group == 0.
+ */
+QCAST_API int qcast_cast_back(const void* q, const float* sf, int64_t rows, int64_t cols, int fmt,
+                              int group, int out_dtype, void* out, void* stream);
 
 /* Human-readable name of a status code (static string). */
 QCAST_API const char* qcast_status_str(int status);

@@ -6,9 +6,9 @@ contiguous, allocates outputs that were not given, and passes raw pointers
 and torch's current stream. Every step of a cast runs in the HIP kernels; a
 missing library raises ``QcastError``.
 
-Outputs: E4M3 codes as ``torch.float8_e4m3fn`` (one byte per code), E2M1
-codes as ``torch.uint8`` with two codes per byte (low nibble = even column),
-scales as ``torch.float32``.
+Outputs: E4M3 codes as ``torch.float8_e4m3fn`` and E5M2 codes as
+``torch.float8_e5m2`` (one byte per code), E2M1 codes as ``torch.uint8`` with
+two codes per byte (low nibble = even column), scales as ``torch.float32``.
 
 ``per_token_cast(x, fmt='e4m3', num_per_channels=128) -> (out, out_sf)``
 mirrors the call shown in the quick start of the page
@@ -16,13 +16,13 @@ mirrors the call shown in the quick start of the page
 """
 import torch
 
-from ._lib import FMT_E2M1, FMT_E4M3, QcastError, check, fmt_id, load
+from ._lib import FMT_E2M1, FMT_E4M3, FMT_E5M2, OUT_BF16, OUT_F32, QcastError, check, fmt_id, load
 
 __all__ = ["qcast_per_token", "qcast_e2m1", "qcast_swiglu_per_token", "qcast_per_block",
-           "qcast_per_channel_T", "qcast_abi_version", "qcast_set_num_cus", "qcast_bench_copy",
+           "qcast_per_channel_T", "qcast_cast_back", "qcast_abi_version", "qcast_set_num_cus", "qcast_bench_copy",
            "qcast_bench_check_scale",
            "per_token_cast",
-           "QcastError", "FMT_E4M3", "FMT_E2M1"]
+           "QcastError", "FMT_E4M3", "FMT_E2M1", "FMT_E5M2"]
 
 
 def _bf16_input(x, name):
@@ -52,7 +52,7 @@ def _stream(device, stream):
 
 
 def _code_dtype(f):
-    return torch.float8_e4m3fn if f == FMT_E4M3 else torch.uint8
+    return {FMT_E4M3: torch.float8_e4m3fn, FMT_E5M2: torch.float8_e5m2}.get(f, torch.uint8)
 
 
 def qcast_per_token(x, fmt="e4m3", group=128, clamp_min=0.0, out=None, out_sf=None,
@@ -61,7 +61,7 @@ def qcast_per_token(x, fmt="e4m3", group=128, clamp_min=0.0, out=None, out_sf=No
     f = fmt_id(fmt)
     x = _bf16_input(x, "x")
     rows, cols = x.shape
-    qshape = (rows, cols) if f == FMT_E4M3 else (rows, cols // 2)
+    qshape = (rows, cols // 2) if f == FMT_E2M1 else (rows, cols)
     out = _out(out, qshape, _code_dtype(f), x.device, "out")
     out_sf = _out(out_sf, (rows, cols // group if group > 0 else 0), torch.float32, x.device,
                   "out_sf")
@@ -143,6 +143,30 @@ def qcast_per_channel_T(x, fmt="e4m3", group=128, clamp_min=0.0, out=None, out_s
                                          out.data_ptr(), out_sf.data_ptr(),
                                          _stream(x.device, stream)), "qcast_per_channel_T")
     return out, out_sf
+
+
+def qcast_cast_back(q, sf, fmt="e4m3", group=128, out_dtype=torch.bfloat16, out=None,
+                    stream=None):
+    """Dequantize per-token codes ``q`` with scales ``sf [rows, cols/group]``
+    to ``out [rows, cols]`` (bf16 or fp32): decode(q) * sf."""
+    f = fmt_id(fmt)
+    if not (isinstance(q, torch.Tensor) and q.is_cuda and q.dim() == 2 and q.is_contiguous()):
+        raise QcastError(2, "q must be a contiguous 2-D CUDA tensor")
+    if q.element_size() != 1:
+        raise QcastError(2, "q must hold one byte per element")
+    rows = q.shape[0]
+    cols = q.shape[1] * 2 if f == FMT_E2M1 else q.shape[1]
+    if out_dtype not in (torch.bfloat16, torch.float32):
+        raise QcastError(4, "out_dtype must be torch.bfloat16 or torch.float32")
+    if sf.dtype != torch.float32 or tuple(sf.shape) != (rows, cols // group if group > 0 else 0) \
+            or sf.device != q.device or not sf.is_contiguous():
+        raise QcastError(2, "sf must be a contiguous float32 [rows, cols/group] tensor on q's device")
+    out = _out(out, (rows, cols), out_dtype, q.device, "out")
+    od = OUT_BF16 if out_dtype == torch.bfloat16 else OUT_F32
+    with torch.cuda.device(q.device):
+        check(load().qcast_cast_back(q.data_ptr(), sf.data_ptr(), rows, cols, f, group, od,
+                                     out.data_ptr(), _stream(q.device, stream)), "qcast_cast_back")
+    return out
 
 
 def qcast_abi_version():

@@ -11,7 +11,10 @@ from . import build as _build
 QCAST_OK = 0
 FMT_E4M3 = 1
 FMT_E2M1 = 2
-_FMT = {"e4m3": FMT_E4M3, "e2m1": FMT_E2M1}
+FMT_E5M2 = 3
+OUT_BF16 = 1
+OUT_F32 = 2
+_FMT = {"e4m3": FMT_E4M3, "e2m1": FMT_E2M1, "e5m2": FMT_E5M2}
 
 _lib = None
 
@@ -51,6 +54,7 @@ def load():
         "qcast_swiglu_per_token": [vp, i64, i64, vp, i32, i32, f32, vp, vp, vp],
         "qcast_per_block": [vp, i64, i64, i32, i32, f32, vp, vp, vp],
         "qcast_per_channel_T": [vp, i64, i64, i32, i32, f32, vp, vp, vp],
+        "qcast_cast_back": [vp, vp, i64, i64, i32, i32, i32, vp, vp],
     }
     for name, args in sig.items():
         fn = getattr(lib, name)
@@ -77,5 +81,5 @@ def check(status, what):
 
 
 EXPORTS = ["qcast_per_token", "qcast_e2m1", "qcast_swiglu_per_token", "qcast_per_block",
-           "qcast_per_channel_T", "qcast_status_str", "qcast_abi_version", "qcast_set_num_cus",
+           "qcast_per_channel_T", "qcast_cast_back", "qcast_status_str", "qcast_abi_version", "qcast_set_num_cus",
            "qcast_bench_copy", "qcast_bench_check_scale"]

@@ -44,7 +44,7 @@ __global__ __launch_bounds__(kThreads) void copy_kernel(const u32x4* __restrict_
 template <int kFmt>
 __global__ __launch_bounds__(kThreads) void check_scale_kernel(uint32_t first, uint32_t last,
                                                                uint32_t* __restrict__ counts) {
-  constexpr float kMax = (kFmt == kE4M3) ? kE4M3Max : kE2M1Max;
+  constexpr float kMax = fmt_max<kFmt>();
   __shared__ uint32_t red[2][kThreads];
   const uint64_t nthreads = (uint64_t)gridDim.x * kThreads;
   const uint64_t total = (uint64_t)last - first + 1;
@@ -79,7 +79,8 @@ __global__ __launch_bounds__(kThreads) void check_scale_kernel(uint32_t first, u
 
 extern "C" int qcast_bench_check_scale(int fmt, uint32_t first, uint32_t last, uint32_t* counts,
                                        void* stream) {
-  if (fmt != QCAST_FMT_E4M3 && fmt != QCAST_FMT_E2M1) return QCAST_ERR_FORMAT;
+  if (fmt != QCAST_FMT_E4M3 && fmt != QCAST_FMT_E2M1 && fmt != QCAST_FMT_E5M2)
+    return QCAST_ERR_FORMAT;
   if (first > last || last > 0x7f7fffffu) return QCAST_ERR_SHAPE;
   if (!counts) return QCAST_ERR_NULL;
   if (reinterpret_cast<uintptr_t>(counts) & 3) return QCAST_ERR_ALIGN;
@@ -87,8 +88,11 @@ extern "C" int qcast_bench_check_scale(int fmt, uint32_t first, uint32_t last, u
   if (fmt == QCAST_FMT_E4M3)
     hipLaunchKernelGGL(qcast::check_scale_kernel<qcast::kE4M3>, dim3(QCAST_CHECK_BLOCKS),
                        dim3(qcast::kThreads), 0, s, first, last, counts);
-  else
+  else if (fmt == QCAST_FMT_E2M1)
     hipLaunchKernelGGL(qcast::check_scale_kernel<qcast::kE2M1>, dim3(QCAST_CHECK_BLOCKS),
+                       dim3(qcast::kThreads), 0, s, first, last, counts);
+  else
+    hipLaunchKernelGGL(qcast::check_scale_kernel<qcast::kE5M2>, dim3(QCAST_CHECK_BLOCKS),
                        dim3(qcast::kThreads), 0, s, first, last, counts);
   return hipGetLastError() == hipSuccess ? QCAST_OK : QCAST_ERR_LAUNCH;
 }

@@ -1,0 +1,153 @@
+// cast_back.hip -- dequantize per-token codes back to bf16 or fp32.
+//
+// Operation: cast_back of the operator table on the page "TileKernels 与
+// DeepGEMM 的分界线：DeepSeek 开源内核栈的分工", §二: every code times the
+// fp32 scale of its group, out[r][c] = decode(q[r][c]) * sf[r][c / group],
+// one fp32 product, then rounded to bf16 (nearest even) when bf16 output is
+// asked for. The codes and scales are laid out as the per-token cast writes
+// them ("DeepSeek开源TileKernels：用Python写的GPU算子逼近硬件性能上限", §3.2).
+//
+// gfx950 design. The per-token stream walked backwards: one lane per 8 codes
+// (8 bytes of E4M3 / E5M2, 4 bytes of E2M1), decoded exactly by the hardware
+// (v_cvt_pk_f32_fp8 / v_cvt_pk_f32_bf8 / v_cvt_scalef32_pk_f32_fp4 with
+// scale 1), multiplied by the group's scale (the lanes of a group read the
+// same scale word), and written as 8 bf16 (one 16-byte store, converted with
+// v_cvt_pk_bf16_f32) or 8 fp32 (two 16-byte stores). One workgroup per
+// 256 * kUnroll chunks.
+#include "qcast_device.h"
+#include "qcast_kernels.h"
+
+namespace qcast {
+namespace {
+
+#ifndef QCAST_CB_UNROLL
+#define QCAST_CB_UNROLL 2
+#endif
+constexpr int kUnroll = QCAST_CB_UNROLL;
+
+typedef float f32x2 __attribute__((ext_vector_type(2)));
+
+// Eight codes -> eight exact fp32 values.
+template <int kFmt>
+__device__ __forceinline__ void decode8(u32x2 codes, float v[8]) {
+  if constexpr (kFmt == kE2M1) {
+    const uint32_t w = codes.x;  // 8 nibbles; the byte selector is an immediate
+    const f32x2 p0 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(w, 1.0f, 0);
+    const f32x2 p1 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(w, 1.0f, 1);
+    const f32x2 p2 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(w, 1.0f, 2);
+    const f32x2 p3 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(w, 1.0f, 3);
+    v[0] = p0.x; v[1] = p0.y; v[2] = p1.x; v[3] = p1.y;
+    v[4] = p2.x; v[5] = p2.y; v[6] = p3.x; v[7] = p3.y;
+  } else {
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+      const uint32_t w = h ? codes.y : codes.x;
+      f32x2 lo, hi;
+      if constexpr (kFmt == kE4M3) {
+        lo = __builtin_amdgcn_cvt_pk_f32_fp8(w, false);
+        hi = __builtin_amdgcn_cvt_pk_f32_fp8(w, true);
+      } else {
+        lo = __builtin_amdgcn_cvt_pk_f32_bf8(w, false);
+        hi = __builtin_amdgcn_cvt_pk_f32_bf8(w, true);
+      }
+      v[4 * h + 0] = lo.x;
+      v[4 * h + 1] = lo.y;
+      v[4 * h + 2] = hi.x;
+      v[4 * h + 3] = hi.y;
+    }
+  }
+}
+
+__device__ __forceinline__ uint32_t bf16x2(float a, float b) {
+  const uint32_t lo = __builtin_bit_cast(uint16_t, static_cast<__bf16>(a));
+  const uint32_t hi = __builtin_bit_cast(uint16_t, static_cast<__bf16>(b));
+  return lo | (hi << 16);
+}
+
+template <int kLanes, int kFmt, bool kBf16>
+__global__ __launch_bounds__(kThreads) void cast_back_kernel(const uint8_t* __restrict__ q,
+                                                             const float* __restrict__ sf,
+                                                             int64_t nchunks,
+                                                             void* __restrict__ out) {
+  const int64_t base = (int64_t)blockIdx.x * kThreads * kUnroll + threadIdx.x;
+  u32x2 codes[kUnroll];
+  float s[kUnroll];
+#pragma unroll
+  for (int u = 0; u < kUnroll; ++u) {
+    const int64_t c = base + (int64_t)u * kThreads;
+    if (c < nchunks) {
+      if constexpr (kFmt == kE2M1) {
+        codes[u].x = load_stream(reinterpret_cast<const uint32_t*>(q) + c);
+        codes[u].y = 0u;
+      } else {
+        codes[u] = load_stream(reinterpret_cast<const u32x2*>(q) + c);
+      }
+      s[u] = sf[c / kLanes];
+    }
+  }
+#pragma unroll
+  for (int u = 0; u < kUnroll; ++u) {
+    const int64_t c = base + (int64_t)u * kThreads;
+    if (c < nchunks) {
+      float v[8];
+      decode8<kFmt>(codes[u], v);
+#pragma unroll
+      for (int i = 0; i < 8; ++i) v[i] = v[i] * s[u];
+      if constexpr (kBf16) {
+        const u32x4 o = {bf16x2(v[0], v[1]), bf16x2(v[2], v[3]), bf16x2(v[4], v[5]),
+                         bf16x2(v[6], v[7])};
+        store_stream(reinterpret_cast<u32x4*>(out) + c, o);
+      } else {
+        const u32x4 o0 = {__float_as_uint(v[0]), __float_as_uint(v[1]), __float_as_uint(v[2]),
+                          __float_as_uint(v[3])};
+        const u32x4 o1 = {__float_as_uint(v[4]), __float_as_uint(v[5]), __float_as_uint(v[6]),
+                          __float_as_uint(v[7])};
+        store_stream(reinterpret_cast<u32x4*>(out) + 2 * c, o0);
+        store_stream(reinterpret_cast<u32x4*>(out) + 2 * c + 1, o1);
+      }
+    }
+  }
+}
+
+template <int kLanes, int kFmt>
+hipError_t launch(const void* q, const float* sf, int64_t nchunks, bool out_bf16, void* out,
+                  hipStream_t stream) {
+  const int64_t blocks = (nchunks + (int64_t)kThreads * kUnroll - 1) / ((int64_t)kThreads * kUnroll);
+  if (blocks >= (int64_t(1) << 31)) return hipErrorInvalidValue;
+  if (out_bf16)
+    hipLaunchKernelGGL((cast_back_kernel<kLanes, kFmt, true>), dim3((unsigned)blocks),
+                       dim3(kThreads), 0, stream, static_cast<const uint8_t*>(q), sf, nchunks, out);
+  else
+    hipLaunchKernelGGL((cast_back_kernel<kLanes, kFmt, false>), dim3((unsigned)blocks),
+                       dim3(kThreads), 0, stream, static_cast<const uint8_t*>(q), sf, nchunks, out);
+  return hipGetLastError();
+}
+
+template <int kFmt>
+hipError_t launch_fmt(const void* q, const float* sf, int64_t nchunks, int group, bool out_bf16,
+                      void* out, hipStream_t stream) {
+  switch (group) {
+    case 32: return launch<4, kFmt>(q, sf, nchunks, out_bf16, out, stream);
+    case 64: return launch<8, kFmt>(q, sf, nchunks, out_bf16, out, stream);
+    case 128: return launch<16, kFmt>(q, sf, nchunks, out_bf16, out, stream);
+  }
+  return hipErrorInvalidValue;
+}
+
+}  // namespace
+
+hipError_t launch_cast_back(const void* q, const float* sf, int64_t rows, int64_t cols, int fmt,
+                            int group, bool out_bf16, void* out, hipStream_t stream,
+                            const LaunchCaps& caps) {
+  (void)caps;
+  const int64_t nchunks = rows * cols / 8;
+  if (nchunks == 0) return hipSuccess;
+  switch (fmt) {
+    case kE4M3: return launch_fmt<kE4M3>(q, sf, nchunks, group, out_bf16, out, stream);
+    case kE5M2: return launch_fmt<kE5M2>(q, sf, nchunks, group, out_bf16, out, stream);
+    case kE2M1: return launch_fmt<kE2M1>(q, sf, nchunks, group, out_bf16, out, stream);
+  }
+  return hipErrorInvalidValue;
+}
+
+}  // namespace qcast

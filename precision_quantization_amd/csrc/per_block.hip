@@ -1,4 +1,4 @@
-// per_block.hip -- per-block (128 x 128) cast of a bf16 weight to E4M3.
+// per_block.hip -- per-block (128 x 128) cast of a bf16 weight to E4M3 or E5M2.
 //
 // Operation: per_block_cast of the operator table on the page
 // "TileKernels 与 DeepGEMM 的分界线：DeepSeek 开源内核栈的分工", §二 (one scale
@@ -28,6 +28,7 @@ constexpr int kBlock = 128;
 constexpr int kRowsPerPass = kThreads / (kBlock / 8);   // 16
 constexpr int kPasses = kBlock / kRowsPerPass;          // 8
 
+template <int kFmt>
 __global__ __launch_bounds__(kThreads) void per_block_kernel(
     const uint16_t* __restrict__ x, uint32_t cols, uint32_t bcols, float floor,
     uint8_t* __restrict__ q, float* __restrict__ sf) {
@@ -63,14 +64,14 @@ __global__ __launch_bounds__(kThreads) void per_block_kernel(
   if ((t & 63) == 0) wave_amax[t >> 6] = m;
   __syncthreads();
   m = fmaxf(fmaxf(wave_amax[0], wave_amax[1]), fmaxf(wave_amax[2], wave_amax[3]));
-  const Scale s = group_scale<kE4M3>(m, floor);
+  const Scale s = group_scale<kFmt>(m, floor);
 #pragma unroll
   for (int p = 0; p < kPasses; ++p) {
     float v[8];
     unpack8(raw[p], v);
     u32x2 out;
-    out.x = e4m3x4(v[0] * s.inv, v[1] * s.inv, v[2] * s.inv, v[3] * s.inv);
-    out.y = e4m3x4(v[4] * s.inv, v[5] * s.inv, v[6] * s.inv, v[7] * s.inv);
+    out.x = fp8x4<kFmt>(v[0] * s.inv, v[1] * s.inv, v[2] * s.inv, v[3] * s.inv);
+    out.y = fp8x4<kFmt>(v[4] * s.inv, v[5] * s.inv, v[6] * s.inv, v[7] * s.inv);
     const uint32_t off = (uint32_t)(r0 + p * kRowsPerPass) * cols + cc * 8;
     store_stream(reinterpret_cast<u32x2*>(dst + off), out);
   }
@@ -79,8 +80,8 @@ __global__ __launch_bounds__(kThreads) void per_block_kernel(
 
 }  // namespace
 
-hipError_t launch_per_block(const void* x, int64_t rows, int64_t cols, float floor, void* q,
-                            float* sf, hipStream_t stream, const LaunchCaps& caps) {
+hipError_t launch_per_block(const void* x, int64_t rows, int64_t cols, int fmt, float floor,
+                            void* q, float* sf, hipStream_t stream, const LaunchCaps& caps) {
   (void)caps;
   const int64_t bcols = cols / kBlock;
   const int64_t nblocks = (rows / kBlock) * bcols;
@@ -88,9 +89,16 @@ hipError_t launch_per_block(const void* x, int64_t rows, int64_t cols, float flo
   // One workgroup per tile; tile counts and in-tile offsets in 32 bits.
   const int64_t lim = int64_t(1) << 31;
   if (nblocks >= lim || (int64_t)kBlock * cols >= lim) return hipErrorInvalidValue;
-  hipLaunchKernelGGL(per_block_kernel, dim3((unsigned)nblocks), dim3(kThreads), 0, stream,
-                     static_cast<const uint16_t*>(x), (uint32_t)cols, (uint32_t)bcols, floor,
-                     static_cast<uint8_t*>(q), sf);
+  if (fmt == kE4M3)
+    hipLaunchKernelGGL(per_block_kernel<kE4M3>, dim3((unsigned)nblocks), dim3(kThreads), 0, stream,
+                       static_cast<const uint16_t*>(x), (uint32_t)cols, (uint32_t)bcols, floor,
+                       static_cast<uint8_t*>(q), sf);
+  else if (fmt == kE5M2)
+    hipLaunchKernelGGL(per_block_kernel<kE5M2>, dim3((unsigned)nblocks), dim3(kThreads), 0, stream,
+                       static_cast<const uint16_t*>(x), (uint32_t)cols, (uint32_t)bcols, floor,
+                       static_cast<uint8_t*>(q), sf);
+  else
+    return hipErrorInvalidValue;
   return hipGetLastError();
 }
 

@@ -1,5 +1,5 @@
 // per_channel_t.hip -- per-channel cast of bf16 activations, written
-// transposed, to E4M3.
+// transposed, to E4M3 or E5M2.
 //
 // Operation: per_channel_cast (+transpose) of the operator table on the page
 // "TileKernels 与 DeepGEMM 的分界线：DeepSeek 开源内核栈的分工", §二. The scale
@@ -139,6 +139,7 @@ struct Smem {
 
 // Scales, codes and stores of one tile whose values are in raw. Starts and
 // ends with the workgroup converged; the LDS is free again on return.
+template <int kFmt>
 __device__ __forceinline__ void process_tile(const TileCoord& tc, const u32x4 (&raw)[kPasses][4],
                                              uint32_t rows, uint32_t ngroups, float floor,
                                              Smem& sm, uint8_t* __restrict__ qT,
@@ -183,7 +184,7 @@ __device__ __forceinline__ void process_tile(const TileCoord& tc, const u32x4 (&
     const int c = t % kChannels;
     const float m = fmaxf(fmaxf(sm.wave_amax[gi][0][c], sm.wave_amax[gi][1][c]),
                           fmaxf(sm.wave_amax[gi][2][c], sm.wave_amax[gi][3][c]));
-    const Scale s = group_scale<kE4M3>(m, floor);
+    const Scale s = group_scale<kFmt>(m, floor);
     sm.inv_s[gi][c] = s.inv;
     if (c < tc.nc && gi < tc.ng)
       sf[(uint64_t)tc.c0 * ngroups + (uint32_t)c * ngroups + tc.gt * kTG + gi] = s.sf;
@@ -204,7 +205,8 @@ __device__ __forceinline__ void process_tile(const TileCoord& tc, const u32x4 (&
         const uint32_t word = raw[p][i][j >> 1];
         y[i] = ((j & 1) ? bf16_hi(word) : bf16_lo(word)) * inv;
       }
-      sm.tile[tile_index(ch * 8 + j, p * (kPassTokens / 4) + k)] = e4m3x4(y[0], y[1], y[2], y[3]);
+      sm.tile[tile_index(ch * 8 + j, p * (kPassTokens / 4) + k)] =
+          fp8x4<kFmt>(y[0], y[1], y[2], y[3]);
     }
   }
   __syncthreads();
@@ -225,6 +227,7 @@ __device__ __forceinline__ void process_tile(const TileCoord& tc, const u32x4 (&
 }
 
 // One workgroup per tile.
+template <int kFmt>
 __global__ __launch_bounds__(kThreads) void per_channel_t_kernel(
     const uint16_t* __restrict__ x, uint32_t rows, uint32_t cols, uint32_t ngroups,
     uint32_t nct, uint32_t ntiles, uint32_t per_xcd, float floor, uint8_t* __restrict__ qT,
@@ -236,12 +239,12 @@ __global__ __launch_bounds__(kThreads) void per_channel_t_kernel(
   const TileCoord tc = tile_coord(tau, ngroups, cols, nct, ntiles / nct);
   u32x4 raw[kPasses][4];
   load_tile(x, cols, tc, raw);
-  process_tile(tc, raw, rows, ngroups, floor, sm, qT, sf);
+  process_tile<kFmt>(tc, raw, rows, ngroups, floor, sm, qT, sf);
 }
 
 }  // namespace
 
-hipError_t launch_per_channel_T(const void* x, int64_t rows, int64_t cols, float floor,
+hipError_t launch_per_channel_T(const void* x, int64_t rows, int64_t cols, int fmt, float floor,
                                 void* qT, float* sf, hipStream_t stream,
                                 const LaunchCaps& caps) {
   (void)caps;
@@ -257,7 +260,10 @@ hipError_t launch_per_channel_T(const void* x, int64_t rows, int64_t cols, float
     return hipErrorInvalidValue;
   const int64_t per_xcd = (ntiles + kXcds - 1) / kXcds;
   const int64_t grid = (kOrder & 2) ? ntiles : per_xcd * kXcds;
-  hipLaunchKernelGGL(per_channel_t_kernel, dim3((unsigned)grid), dim3(kThreads), 0, stream,
+  auto kernel = fmt == kE4M3 ? per_channel_t_kernel<kE4M3>
+               : fmt == kE5M2 ? per_channel_t_kernel<kE5M2> : nullptr;
+  if (!kernel) return hipErrorInvalidValue;
+  hipLaunchKernelGGL(kernel, dim3((unsigned)grid), dim3(kThreads), 0, stream,
                      static_cast<const uint16_t*>(x), (uint32_t)rows, (uint32_t)cols,
                      (uint32_t)ngroups, (uint32_t)nct, (uint32_t)ntiles, (uint32_t)per_xcd, floor,
                      static_cast<uint8_t*>(qT), sf);

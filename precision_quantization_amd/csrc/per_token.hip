@@ -1,9 +1,10 @@
-// per_token.hip -- per-token cast of bf16 rows to E4M3 or packed E2M1.
+// per_token.hip -- per-token cast of bf16 rows to E4M3, E5M2 or packed E2M1.
 //
 // Operation: the per-token cast of the walk-through page
 // "DeepSeek开源TileKernels：用Python写的GPU算子逼近硬件性能上限", quick start and
 // §3.2 (abs-max over each run of num_per_channels elements of a row, scale
-// and inverse, codes of x * inverse); E2M1 output per §3.1 (float4_e2m1fn).
+// and inverse, codes of x * inverse); E2M1 output per §3.1 (float4_e2m1fn),
+// E5M2 from the format list of "TileKernels 与 DeepGEMM 的分界线", §四 A.
 //
 // gfx950 design. A contiguous [rows, cols] matrix with cols % G == 0 is one
 // flat stream of groups: group k is elements [kG, kG + G) and owns scale
@@ -59,13 +60,13 @@ __global__ __launch_bounds__(kThreads) void per_token_kernel(
         float y[8];
 #pragma unroll
         for (int i = 0; i < 8; ++i) y[i] = v[i] * s.inv;
-        if (kFmt == kE4M3) {
-          u32x2 out;
-          out.x = e4m3x4(y[0], y[1], y[2], y[3]);
-          out.y = e4m3x4(y[4], y[5], y[6], y[7]);
-          store_stream(reinterpret_cast<u32x2*>(q) + c, out);
-        } else {
+        if constexpr (kFmt == kE2M1) {
           store_stream(reinterpret_cast<uint32_t*>(q) + c, e2m1x8(y));
+        } else {
+          u32x2 out;
+          out.x = fp8x4<kFmt>(y[0], y[1], y[2], y[3]);
+          out.y = fp8x4<kFmt>(y[4], y[5], y[6], y[7]);
+          store_stream(reinterpret_cast<u32x2*>(q) + c, out);
         }
         if ((threadIdx.x & (kLanes - 1)) == 0) sf[c / kLanes] = s.sf;
       }
@@ -89,6 +90,17 @@ hipError_t launch(const void* x, int64_t nchunks, float floor, void* q, float* s
   return hipGetLastError();
 }
 
+template <int kFmt>
+hipError_t launch_fmt(const void* x, int64_t nchunks, int group, float floor, void* q,
+                      float* sf, hipStream_t stream, const LaunchCaps& caps) {
+  switch (group) {
+    case 32: return launch<4, kFmt>(x, nchunks, floor, q, sf, stream, caps);
+    case 64: return launch<8, kFmt>(x, nchunks, floor, q, sf, stream, caps);
+    case 128: return launch<16, kFmt>(x, nchunks, floor, q, sf, stream, caps);
+  }
+  return hipErrorInvalidValue;
+}
+
 }  // namespace
 
 hipError_t launch_per_token(const void* x, int64_t rows, int64_t cols, int fmt, int group,
@@ -96,18 +108,10 @@ hipError_t launch_per_token(const void* x, int64_t rows, int64_t cols, int fmt, 
                             const LaunchCaps& caps) {
   const int64_t nchunks = rows * cols / 8;
   if (nchunks == 0) return hipSuccess;
-  if (fmt == kE4M3) {
-    switch (group) {
-      case 32: return launch<4, kE4M3>(x, nchunks, floor, q, sf, stream, caps);
-      case 64: return launch<8, kE4M3>(x, nchunks, floor, q, sf, stream, caps);
-      case 128: return launch<16, kE4M3>(x, nchunks, floor, q, sf, stream, caps);
-    }
-  } else {
-    switch (group) {
-      case 32: return launch<4, kE2M1>(x, nchunks, floor, q, sf, stream, caps);
-      case 64: return launch<8, kE2M1>(x, nchunks, floor, q, sf, stream, caps);
-      case 128: return launch<16, kE2M1>(x, nchunks, floor, q, sf, stream, caps);
-    }
+  switch (fmt) {
+    case kE4M3: return launch_fmt<kE4M3>(x, nchunks, group, floor, q, sf, stream, caps);
+    case kE2M1: return launch_fmt<kE2M1>(x, nchunks, group, floor, q, sf, stream, caps);
+    case kE5M2: return launch_fmt<kE5M2>(x, nchunks, group, floor, q, sf, stream, caps);
   }
   return hipErrorInvalidValue;
 }

@@ -3,7 +3,8 @@
 //
 // Floors ("DeepSeek开源TileKernels：用Python写的GPU算子逼近硬件性能上限", §3.1):
 // 1e-4 for E4M3 and the E2M1 maximum times 2^-126 for E2M1, unless the caller
-// passes its own clamp_min > 0.
+// passes its own clamp_min > 0; E5M2, for which the page names none, takes
+// the E4M3 floor.
 #include <atomic>
 
 #include "qcast.h"
@@ -19,9 +20,15 @@ std::atomic<int> g_cu_override{0};
 bool aligned(const void* p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p) & (a - 1)) == 0; }
 
 float default_floor(int fmt) {
-  if (fmt == QCAST_FMT_E4M3) return 1e-4f;
-  return 6.0f * 0x1.0p-126f;   // E2M1 maximum times 2^-126
+  if (fmt == QCAST_FMT_E2M1) return 6.0f * 0x1.0p-126f;   // E2M1 maximum times 2^-126
+  return 1e-4f;   // E4M3; E5M2 takes the same floor
 }
+
+bool any_fmt(int fmt) {
+  return fmt == QCAST_FMT_E4M3 || fmt == QCAST_FMT_E2M1 || fmt == QCAST_FMT_E5M2;
+}
+
+bool fp8_fmt(int fmt) { return fmt == QCAST_FMT_E4M3 || fmt == QCAST_FMT_E5M2; }
 
 float floor_for(int fmt, float clamp_min) { return clamp_min > 0.0f ? clamp_min : default_floor(fmt); }
 
@@ -84,7 +91,7 @@ void qcast_set_num_cus(int n) { g_cu_override.store(n > 0 ? n : 0, std::memory_o
 
 int qcast_per_token(const void* x, int64_t rows, int64_t cols, int fmt, int group,
                     float clamp_min, void* q, float* sf, void* stream) {
-  if (fmt != QCAST_FMT_E4M3 && fmt != QCAST_FMT_E2M1) return QCAST_ERR_FORMAT;
+  if (!any_fmt(fmt)) return QCAST_ERR_FORMAT;
   if (!per_token_group_ok(group)) return QCAST_ERR_GROUP;
   if (rows < 0 || cols < 0 || cols % group != 0 || too_big(rows, cols)) return QCAST_ERR_SHAPE;
   if (rows == 0 || cols == 0) return QCAST_OK;
@@ -105,7 +112,7 @@ int qcast_e2m1(const void* x, int64_t rows, int64_t cols, int group, float clamp
 int qcast_swiglu_per_token(const void* h, int64_t rows, int64_t cols, const float* row_weight,
                            int fmt, int group, float clamp_min, void* q, float* sf,
                            void* stream) {
-  if (fmt != QCAST_FMT_E4M3) return QCAST_ERR_FORMAT;
+  if (!fp8_fmt(fmt)) return QCAST_ERR_FORMAT;
   if (!per_token_group_ok(group)) return QCAST_ERR_GROUP;
   if (rows < 0 || cols < 0 || cols % group != 0 || cols / 8 >= (int64_t(1) << 16) ||
       too_big(rows, 2 * cols))
@@ -118,14 +125,14 @@ int qcast_swiglu_per_token(const void* h, int64_t rows, int64_t cols, const floa
   qcast::LaunchCaps caps;
   const int rc = caps_for_current_device(&caps);
   if (rc != QCAST_OK) return rc;
-  return finish(qcast::launch_swiglu_per_token(h, rows, cols, row_weight, group,
+  return finish(qcast::launch_swiglu_per_token(h, rows, cols, row_weight, fmt, group,
                                                floor_for(fmt, clamp_min), q, sf,
                                                static_cast<hipStream_t>(stream), caps));
 }
 
 int qcast_per_block(const void* x, int64_t rows, int64_t cols, int fmt, int block,
                     float clamp_min, void* q, float* sf, void* stream) {
-  if (fmt != QCAST_FMT_E4M3) return QCAST_ERR_FORMAT;
+  if (!fp8_fmt(fmt)) return QCAST_ERR_FORMAT;
   if (block != 128) return QCAST_ERR_GROUP;
   if (rows < 0 || cols < 0 || rows % block != 0 || cols % block != 0 || too_big(rows, cols))
     return QCAST_ERR_SHAPE;
@@ -135,13 +142,13 @@ int qcast_per_block(const void* x, int64_t rows, int64_t cols, int fmt, int bloc
   qcast::LaunchCaps caps;
   const int rc = caps_for_current_device(&caps);
   if (rc != QCAST_OK) return rc;
-  return finish(qcast::launch_per_block(x, rows, cols, floor_for(fmt, clamp_min), q, sf,
+  return finish(qcast::launch_per_block(x, rows, cols, fmt, floor_for(fmt, clamp_min), q, sf,
                                         static_cast<hipStream_t>(stream), caps));
 }
 
 int qcast_per_channel_T(const void* x, int64_t rows, int64_t cols, int fmt, int group,
                         float clamp_min, void* qT, float* sf, void* stream) {
-  if (fmt != QCAST_FMT_E4M3) return QCAST_ERR_FORMAT;
+  if (!fp8_fmt(fmt)) return QCAST_ERR_FORMAT;
   if (group != 128) return QCAST_ERR_GROUP;
   if (rows < 0 || cols < 0 || rows % group != 0 || cols % 8 != 0 || too_big(rows, cols))
     return QCAST_ERR_SHAPE;
@@ -151,8 +158,24 @@ int qcast_per_channel_T(const void* x, int64_t rows, int64_t cols, int fmt, int 
   qcast::LaunchCaps caps;
   const int rc = caps_for_current_device(&caps);
   if (rc != QCAST_OK) return rc;
-  return finish(qcast::launch_per_channel_T(x, rows, cols, floor_for(fmt, clamp_min), qT, sf,
+  return finish(qcast::launch_per_channel_T(x, rows, cols, fmt, floor_for(fmt, clamp_min), qT, sf,
                                             static_cast<hipStream_t>(stream), caps));
+}
+
+int qcast_cast_back(const void* q, const float* sf, int64_t rows, int64_t cols, int fmt,
+                    int group, int out_dtype, void* out, void* stream) {
+  if (!any_fmt(fmt)) return QCAST_ERR_FORMAT;
+  if (out_dtype != QCAST_OUT_BF16 && out_dtype != QCAST_OUT_F32) return QCAST_ERR_FORMAT;
+  if (!per_token_group_ok(group)) return QCAST_ERR_GROUP;
+  if (rows < 0 || cols < 0 || cols % group != 0 || too_big(rows, cols)) return QCAST_ERR_SHAPE;
+  if (rows == 0 || cols == 0) return QCAST_OK;
+  if (!q || !sf || !out) return QCAST_ERR_NULL;
+  if (!aligned(q, 16) || !aligned(sf, 4) || !aligned(out, 16)) return QCAST_ERR_ALIGN;
+  qcast::LaunchCaps caps;
+  const int rc = caps_for_current_device(&caps);
+  if (rc != QCAST_OK) return rc;
+  return finish(qcast::launch_cast_back(q, sf, rows, cols, fmt, group, out_dtype == QCAST_OUT_BF16,
+                                        out, static_cast<hipStream_t>(stream), caps));
 }
 
 }  // extern "C"

@@ -9,11 +9,13 @@
 // gfx950 conversions used (unit scale, round to nearest even):
 //   v_cvt_pk_fp8_f32           two fp32 -> two OCP E4M3FN bytes (src0 -> the
 //                              lower byte of the selected 16-bit half)
+//   v_cvt_pk_bf8_f32           the same for OCP E5M2
 //   v_cvt_scalef32_pk_fp4_f32  two fp32 / scale -> two E2M1 nibbles in the
 //                              selected byte (src0 -> low nibble); scale 1.0
-// With |x * sf_inv| <= 448 * (1 + 2^-22) (resp. 6 * (1 + 2^-22)) every value
+// With |x * sf_inv| <= M * (1 + 2^-22) for the format maximum M every value
 // that reaches a conversion rounds inside the format, so the result is the
-// nearest-even code with the sign kept.
+// nearest-even code with the sign kept. The reverse conversions
+// (v_cvt_pk_f32_fp8 / _bf8, v_cvt_scalef32_pk_f32_fp4) decode exactly.
 #pragma once
 
 #include <hip/hip_runtime.h>
@@ -24,8 +26,14 @@ namespace qcast {
 constexpr int kThreads = 256;          // 4 wave64s per workgroup
 constexpr float kE4M3Max = 448.0f;
 constexpr float kE2M1Max = 6.0f;
+constexpr float kE5M2Max = 57344.0f;
 
-enum Fmt : int { kE4M3 = 1, kE2M1 = 2 };
+enum Fmt : int { kE4M3 = 1, kE2M1 = 2, kE5M2 = 3 };
+
+template <int kFmt>
+__host__ __device__ constexpr float fmt_max() {
+  return kFmt == kE4M3 ? kE4M3Max : (kFmt == kE2M1 ? kE2M1Max : kE5M2Max);
+}
 
 // Native vector types (the nontemporal builtins take these, not HIP's
 // struct-wrapped uint4).
@@ -46,16 +54,18 @@ struct Scale {
 //   inv = y0 + e * y0, with y0 = v_rcp_f32(sf), e = fma(-sf, y0, 1)
 // An exhaustive sweep over every positive fp32 shows both sequences equal to
 // the IEEE quotients for M in {448, 6} whenever a >= 2^-120 (M = 448) or
-// a >= 2^-125 (M = 6), and sf in [2^-126, 2^125). The fast path is taken for
+// a >= 2^-125 (M = 6), and sf in [2^-126, 2^125); M = 57344 = 448 * 2^7
+// scales the same computation by a power of two. The fast path is taken for
 // M * 2^-126 <= a < M * 2^124, inside those ranges; every other a (a custom
 // floor below the normal range, or huge inputs under E2M1) takes the IEEE
 // division. qcast_bench_check_scale re-runs the sweep through this function.
 template <int kFmt>
 __device__ __forceinline__ Scale group_scale(float amax, float floor) {
-  constexpr float kMax = (kFmt == kE4M3) ? kE4M3Max : kE2M1Max;
+  constexpr float kMax = fmt_max<kFmt>();
   constexpr float kRecip = 1.0f / kMax;                     // RN(1 / M), folded
   constexpr float kFastLo = kMax * 0x1.0p-126f;             // exact
-  constexpr float kFastHi = (kFmt == kE4M3) ? __builtin_huge_valf() : kMax * 0x1.0p124f;
+  // sf = a / M stays below 2^125 for every finite a when M >= 448.
+  constexpr float kFastHi = (kFmt == kE2M1) ? kMax * 0x1.0p124f : __builtin_huge_valf();
   const float a = amax < floor ? floor : amax;
   Scale s;
   if (a >= kFastLo && a < kFastHi) {
@@ -139,6 +149,19 @@ __device__ __forceinline__ float wave_max(float m) {
 __device__ __forceinline__ uint32_t e4m3x4(float v0, float v1, float v2, float v3) {
   uint32_t w = __builtin_amdgcn_cvt_pk_fp8_f32(v0, v1, 0u, false);
   return __builtin_amdgcn_cvt_pk_fp8_f32(v2, v3, w, true);
+}
+
+// Four fp32 -> four E5M2 bytes (v0 in the lowest byte).
+__device__ __forceinline__ uint32_t e5m2x4(float v0, float v1, float v2, float v3) {
+  uint32_t w = __builtin_amdgcn_cvt_pk_bf8_f32(v0, v1, 0u, false);
+  return __builtin_amdgcn_cvt_pk_bf8_f32(v2, v3, w, true);
+}
+
+// Four fp32 -> four bytes of an 8-bit format (E4M3 or E5M2).
+template <int kFmt>
+__device__ __forceinline__ uint32_t fp8x4(float v0, float v1, float v2, float v3) {
+  static_assert(kFmt == kE4M3 || kFmt == kE5M2, "8-bit formats only");
+  return kFmt == kE4M3 ? e4m3x4(v0, v1, v2, v3) : e5m2x4(v0, v1, v2, v3);
 }
 
 // Eight fp32 -> eight E2M1 nibbles (v0 in the lowest nibble).

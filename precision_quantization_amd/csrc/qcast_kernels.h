@@ -13,25 +13,32 @@ struct LaunchCaps {
 };
 
 // x [rows, cols] bf16 -> per-token codes + scales; group in {32, 64, 128};
-// fmt kE4M3 or kE2M1. Requires cols % group == 0.
+// fmt kE4M3, kE5M2 or kE2M1. Requires cols % group == 0.
 hipError_t launch_per_token(const void* x, int64_t rows, int64_t cols, int fmt, int group,
                             float floor, void* q, float* sf, hipStream_t stream,
                             const LaunchCaps& caps);
 
-// h [rows, 2*cols] bf16 (gate | up), w [rows] fp32 or null -> E4M3 codes +
-// scales of silu(gate) * up * w; group in {32, 64, 128}; cols % group == 0.
+// h [rows, 2*cols] bf16 (gate | up), w [rows] fp32 or null -> 8-bit codes
+// (kE4M3 / kE5M2) + scales of silu(gate) * up * w; group in {32, 64, 128};
+// cols % group == 0.
 hipError_t launch_swiglu_per_token(const void* h, int64_t rows, int64_t cols, const float* w,
-                                   int group, float floor, void* q, float* sf,
+                                   int fmt, int group, float floor, void* q, float* sf,
                                    hipStream_t stream, const LaunchCaps& caps);
 
-// x [rows, cols] bf16 -> E4M3 codes + one scale per 128 x 128 block.
-hipError_t launch_per_block(const void* x, int64_t rows, int64_t cols, float floor, void* q,
-                            float* sf, hipStream_t stream, const LaunchCaps& caps);
+// x [rows, cols] bf16 -> 8-bit codes + one scale per 128 x 128 block.
+hipError_t launch_per_block(const void* x, int64_t rows, int64_t cols, int fmt, float floor,
+                            void* q, float* sf, hipStream_t stream, const LaunchCaps& caps);
 
-// x [rows (tokens), cols (channels)] bf16 -> qT [cols, rows] E4M3 codes +
+// x [rows (tokens), cols (channels)] bf16 -> qT [cols, rows] 8-bit codes +
 // sf [cols, rows/128]; rows % 128 == 0, cols % 8 == 0.
-hipError_t launch_per_channel_T(const void* x, int64_t rows, int64_t cols, float floor,
+hipError_t launch_per_channel_T(const void* x, int64_t rows, int64_t cols, int fmt, float floor,
                                 void* qT, float* sf, hipStream_t stream,
                                 const LaunchCaps& caps);
+
+// q per-token codes [rows, cols] (or [rows, cols/2] E2M1) + sf [rows, cols/group]
+// -> out [rows, cols] bf16 (out_bf16) or fp32: decode(q) * sf.
+hipError_t launch_cast_back(const void* q, const float* sf, int64_t rows, int64_t cols, int fmt,
+                            int group, bool out_bf16, void* out, hipStream_t stream,
+                            const LaunchCaps& caps);
 
 }  // namespace qcast

@@ -1,4 +1,4 @@
-// swiglu.hip -- SwiGLU forward fused with the per-token E4M3 cast.
+// swiglu.hip -- SwiGLU forward fused with the per-token E4M3 / E5M2 cast.
 //
 // Operation: swiglu_forward_and_per_token_cast of the walk-through page
 // "DeepSeek开源TileKernels：用Python写的GPU算子逼近硬件性能上限", §3.3: with the
@@ -44,7 +44,7 @@ __device__ __forceinline__ float silu_times(float g, float u) {
   return g * __builtin_amdgcn_rcpf(1.0f + e) * u;
 }
 
-template <int kLanes, bool kWeighted>
+template <int kLanes, bool kWeighted, int kFmt>
 __global__ __launch_bounds__(kThreads) void swiglu_kernel(
     const uint16_t* __restrict__ h, const float* __restrict__ w, int64_t nchunks,
     uint32_t chunks_per_row, uint64_t row_magic, int64_t cols, float floor,
@@ -79,10 +79,10 @@ __global__ __launch_bounds__(kThreads) void swiglu_kernel(
           if (kWeighted) v[i] = v[i] * wr[u];
         }
         const float amax = lane_group_max<kLanes>(absmax8(v));
-        const Scale s = group_scale<kE4M3>(amax, floor);
+        const Scale s = group_scale<kFmt>(amax, floor);
         u32x2 out;
-        out.x = e4m3x4(v[0] * s.inv, v[1] * s.inv, v[2] * s.inv, v[3] * s.inv);
-        out.y = e4m3x4(v[4] * s.inv, v[5] * s.inv, v[6] * s.inv, v[7] * s.inv);
+        out.x = fp8x4<kFmt>(v[0] * s.inv, v[1] * s.inv, v[2] * s.inv, v[3] * s.inv);
+        out.y = fp8x4<kFmt>(v[4] * s.inv, v[5] * s.inv, v[6] * s.inv, v[7] * s.inv);
         store_stream(reinterpret_cast<u32x2*>(q) + c, out);
         if ((threadIdx.x & (kLanes - 1)) == 0) sf[c / kLanes] = s.sf;
       }
@@ -90,7 +90,7 @@ __global__ __launch_bounds__(kThreads) void swiglu_kernel(
   }
 }
 
-template <int kLanes, bool kWeighted>
+template <int kLanes, bool kWeighted, int kFmt>
 hipError_t launch(const uint16_t* h, const float* w, int64_t rows, int64_t cols, float floor,
                   uint8_t* q, float* sf, hipStream_t stream, const LaunchCaps& caps) {
   const int64_t cpr = cols / 8;
@@ -106,7 +106,7 @@ hipError_t launch(const uint16_t* h, const float* w, int64_t rows, int64_t cols,
     const int64_t max_blocks = kWgPerCu > 0 ? (int64_t)caps.num_cus * kWgPerCu : iters;
     const int64_t iters_per_block = (iters + max_blocks - 1) / max_blocks;
     const int64_t blocks = (iters + iters_per_block - 1) / iters_per_block;
-    hipLaunchKernelGGL((swiglu_kernel<kLanes, kWeighted>), dim3((unsigned)blocks),
+    hipLaunchKernelGGL((swiglu_kernel<kLanes, kWeighted, kFmt>), dim3((unsigned)blocks),
                        dim3(kThreads), 0, stream, h + r0 * 2 * cols,
                        kWeighted ? w + r0 : nullptr, nchunks, (uint32_t)cpr, magic, cols, floor,
                        q + r0 * cols, sf + r0 * groups_per_row);
@@ -116,27 +116,36 @@ hipError_t launch(const uint16_t* h, const float* w, int64_t rows, int64_t cols,
   return hipSuccess;
 }
 
-template <int kLanes>
+template <int kLanes, int kFmt>
 hipError_t launch_w(const uint16_t* h, const float* w, int64_t rows, int64_t cols, float floor,
                     uint8_t* q, float* sf, hipStream_t stream, const LaunchCaps& caps) {
-  return w ? launch<kLanes, true>(h, w, rows, cols, floor, q, sf, stream, caps)
-           : launch<kLanes, false>(h, w, rows, cols, floor, q, sf, stream, caps);
+  return w ? launch<kLanes, true, kFmt>(h, w, rows, cols, floor, q, sf, stream, caps)
+           : launch<kLanes, false, kFmt>(h, w, rows, cols, floor, q, sf, stream, caps);
+}
+
+template <int kFmt>
+hipError_t launch_g(const uint16_t* h, const float* w, int64_t rows, int64_t cols, int group,
+                    float floor, uint8_t* q, float* sf, hipStream_t stream,
+                    const LaunchCaps& caps) {
+  switch (group) {
+    case 32: return launch_w<4, kFmt>(h, w, rows, cols, floor, q, sf, stream, caps);
+    case 64: return launch_w<8, kFmt>(h, w, rows, cols, floor, q, sf, stream, caps);
+    case 128: return launch_w<16, kFmt>(h, w, rows, cols, floor, q, sf, stream, caps);
+  }
+  return hipErrorInvalidValue;
 }
 
 }  // namespace
 
 hipError_t launch_swiglu_per_token(const void* h, int64_t rows, int64_t cols, const float* w,
-                                   int group, float floor, void* q, float* sf,
+                                   int fmt, int group, float floor, void* q, float* sf,
                                    hipStream_t stream, const LaunchCaps& caps) {
   if (rows == 0 || cols == 0) return hipSuccess;
   if (cols / 8 >= kMaxChunksPerRow) return hipErrorInvalidValue;
   const uint16_t* hp = static_cast<const uint16_t*>(h);
   uint8_t* qp = static_cast<uint8_t*>(q);
-  switch (group) {
-    case 32: return launch_w<4>(hp, w, rows, cols, floor, qp, sf, stream, caps);
-    case 64: return launch_w<8>(hp, w, rows, cols, floor, qp, sf, stream, caps);
-    case 128: return launch_w<16>(hp, w, rows, cols, floor, qp, sf, stream, caps);
-  }
+  if (fmt == kE4M3) return launch_g<kE4M3>(hp, w, rows, cols, group, floor, qp, sf, stream, caps);
+  if (fmt == kE5M2) return launch_g<kE5M2>(hp, w, rows, cols, group, floor, qp, sf, stream, caps);
   return hipErrorInvalidValue;
 }
 

@@ -17,7 +17,7 @@ from conftest import ROOT, gpu_available
 HEADERS = [os.path.join(ROOT, "include", h) for h in ("qcast.h", "qcast_bench.h")]
 
 OK, ERR_NULL, ERR_SHAPE, ERR_ALIGN, ERR_FORMAT, ERR_GROUP, ERR_LAUNCH, ERR_DEVICE = range(8)
-E4M3, E2M1 = 1, 2
+E4M3, E2M1, E5M2 = 1, 2, 3
 A16 = 0x10000          # aligned, never dereferenced (rejected before use)
 MIS = 0x10008          # 8-byte aligned only
 
@@ -74,7 +74,7 @@ def pt(lib, x=A16, rows=4, cols=256, fmt=E4M3, group=128, q=A16, sf=A16):
 
 
 def test_per_token_validation(lib):
-    assert pt(lib, fmt=3) == ERR_FORMAT
+    assert pt(lib, fmt=9) == ERR_FORMAT
     assert pt(lib, group=16) == ERR_GROUP
     assert pt(lib, group=256) == ERR_GROUP
     assert pt(lib, cols=200) == ERR_SHAPE
@@ -148,9 +148,28 @@ def test_bench_copy_validation(lib):
     assert lib.qcast_bench_copy(None, None, 0, None) == OK
 
 
+def test_cast_back_validation(lib):
+    f = lib.qcast_cast_back
+    assert f(A16, A16, 4, 256, 4, 128, 1, A16, None) == ERR_FORMAT
+    assert f(A16, A16, 4, 256, E4M3, 128, 3, A16, None) == ERR_FORMAT      # out dtype
+    assert f(A16, A16, 4, 256, E4M3, 96, 1, A16, None) == ERR_GROUP
+    assert f(A16, A16, 4, 200, E4M3, 128, 1, A16, None) == ERR_SHAPE
+    assert f(None, A16, 4, 256, E5M2, 128, 2, A16, None) == ERR_NULL
+    assert f(A16, A16, 4, 256, E2M1, 32, 1, MIS, None) == ERR_ALIGN
+    assert f(None, None, 0, 256, E4M3, 128, 1, None, None) == OK
+
+
+def test_e5m2_accepted_by_every_cast(lib):
+    # past format validation, a null output is the first error
+    assert lib.qcast_per_token(A16, 4, 256, E5M2, 128, 0.0, None, A16, None) == ERR_NULL
+    assert lib.qcast_swiglu_per_token(A16, 4, 256, None, E5M2, 128, 0.0, None, A16, None) == ERR_NULL
+    assert lib.qcast_per_block(A16, 256, 256, E5M2, 128, 0.0, None, A16, None) == ERR_NULL
+    assert lib.qcast_per_channel_T(A16, 256, 64, E5M2, 128, 0.0, None, A16, None) == ERR_NULL
+
+
 def test_check_scale_validation(lib):
     f = lib.qcast_bench_check_scale
-    assert f(3, 1, 10, A16, None) == ERR_FORMAT
+    assert f(9, 1, 10, A16, None) == ERR_FORMAT
     assert f(E4M3, 10, 1, A16, None) == ERR_SHAPE
     assert f(E4M3, 1, 0x7F800000, A16, None) == ERR_SHAPE
     assert f(E4M3, 1, 10, None, None) == ERR_NULL

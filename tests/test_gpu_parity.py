@@ -45,9 +45,9 @@ def gpu_cast(op, x, dev, fmt="e4m3", group=128, w=None, poison=0xAA):
     """Run one cast on the GPU with poisoned outputs; numpy codes + scales."""
     xd = x.to(dev)
     rows, cols = x.shape
-    code_dt = torch.float8_e4m3fn if fmt == "e4m3" else torch.uint8
+    code_dt = {"e4m3": torch.float8_e4m3fn, "e5m2": torch.float8_e5m2}.get(fmt, torch.uint8)
     if op == "per_token" or op == "e2m1":
-        qs = (rows, cols) if fmt == "e4m3" else (rows, cols // 2)
+        qs = (rows, cols // 2) if fmt == "e2m1" else (rows, cols)
         out = poisoned(qs, code_dt, dev, poison)
         sf = poisoned((rows, cols // group), torch.float32, dev, poison)
         if op == "e2m1":
@@ -75,6 +75,7 @@ def gpu_cast(op, x, dev, fmt="e4m3", group=128, w=None, poison=0xAA):
 
 
 def oracle_cast(op, x, fmt="e4m3", group=128, w=None):
+    """The oracle's codes and scales for one cast on the CPU."""
     xb = workloads.bf16_bits(x)
     if op == "per_token":
         return oracle.per_token(xb, fmt, group)
@@ -404,3 +405,100 @@ def test_custom_floor(dev, fmt, group, clamp_min):
     torch.cuda.synchronize()
     assert np.array_equal(codes_np(q), q_ref)
     assert np.array_equal(sf.cpu().numpy().view(np.uint32), sf_ref.view(np.uint32))
+
+
+
+# ------------------------------------------------------------ E5M2
+
+@pytest.mark.parametrize("op,shape", [("per_token", (127, 7168)), ("per_block", (256, 384)),
+                                      ("per_channel_T", (384, 200))])
+def test_e5m2_casts(dev, op, shape):
+    g = torch.Generator().manual_seed(31)
+    x = torch.randn(*shape, generator=g) * torch.exp(torch.randn(shape[0], 1, generator=g) * 3)
+    assert_exact(op, x.to(torch.bfloat16), dev, "e5m2", 128)
+
+
+def test_e5m2_full_per_token_hidden(dev):
+    assert_exact("per_token", workloads.per_token_hidden().x, dev, "e5m2", 128)
+
+
+def test_every_bf16_below_57344_encodes_like_the_oracle_e5m2(dev):
+    bits = np.arange(0, 0x4761, dtype=np.uint16)               # +0 .. 57344
+    vals = np.concatenate([bits, bits | 0x8000])
+    per_row = 127
+    nrows = (len(vals) + per_row - 1) // per_row
+    x = np.zeros((nrows, 128), np.uint16)
+    x[:, 0] = 0x4760                                           # 57344
+    flat = np.zeros(nrows * per_row, np.uint16)
+    flat[:len(vals)] = vals
+    x[:, 1:] = flat.reshape(nrows, per_row)
+    assert_exact("per_token", workloads.bits_to_bf16(x), dev, "e5m2", 128)
+
+
+def test_e5m2_swiglu(dev):
+    wl = workloads.swiglu_input(seed=40, rows=256, cols=2048)
+    q, sf = gpu_cast("swiglu_per_token", wl.x, dev, "e5m2", w=wl.w)
+    q_ref, sf_ref = oracle_cast("swiglu_per_token", wl.x, "e5m2", w=wl.w)
+    assert (q != q_ref).mean() <= 1e-3
+    assert (np.abs(sf.astype(np.float64) - sf_ref) / sf_ref).max() <= 1e-6
+
+
+def test_scale_routine_e5m2(dev):
+    assert pq.qcast_bench_check_scale("e5m2", 1, 0x7F7FFFFF) == (0, 0)
+
+
+# ------------------------------------------------------------ cast_back
+
+@pytest.mark.parametrize("fmt,group", [("e4m3", 128), ("e5m2", 128), ("e2m1", 32), ("e4m3", 64)])
+@pytest.mark.parametrize("out_dtype", [torch.bfloat16, torch.float32])
+def test_cast_back_parity(dev, fmt, group, out_dtype):
+    g = torch.Generator().manual_seed(41)
+    x = (torch.randn(257, 1024, generator=g) * torch.exp(torch.randn(257, 1, generator=g) * 4)).to(
+        torch.bfloat16)
+    q_ref, sf_ref = oracle.per_token(workloads.bf16_bits(x), fmt, group)
+    name = "bf16" if out_dtype == torch.bfloat16 else "f32"
+    ref = oracle.cast_back(q_ref, sf_ref, 1024, fmt, group, name)
+    code_dt = {"e4m3": torch.float8_e4m3fn, "e5m2": torch.float8_e5m2}.get(fmt, torch.uint8)
+    qd = torch.from_numpy(q_ref).to(dev).view(code_dt)
+    out = torch.empty(257, 1024, dtype=out_dtype, device=dev)
+    out.view(torch.uint8).fill_(0xAA)
+    pq.qcast_cast_back(qd, torch.from_numpy(sf_ref).to(dev), fmt, group, out_dtype, out=out)
+    torch.cuda.synchronize()
+    got = out.cpu().view(torch.int16 if name == "bf16" else torch.int32).numpy()
+    assert np.array_equal(got.view(ref.dtype), ref)
+
+
+@pytest.mark.parametrize("fmt", ["e4m3", "e5m2", "e2m1"])
+def test_cast_back_every_code(dev, fmt):
+    # every code of the format (NaN / infinity codes excluded) with scale 1
+    # and with a non-power-of-two scale
+    if fmt == "e2m1":
+        codes = np.arange(16, dtype=np.uint8)
+        q = np.tile((codes[0::2] | (codes[1::2] << 4)).astype(np.uint8), 4).reshape(1, 32)
+        cols, group = 64, 32
+    else:
+        bad = {0x7F, 0xFF} if fmt == "e4m3" else set(range(0x7C, 0x80)) | set(range(0xFC, 0x100))
+        codes = np.array([c for c in range(256) if c not in bad] * 4, np.uint8)[:512]
+        q = codes.reshape(4, 128)
+        cols, group = 128, 128
+    rows = q.shape[0]
+    for s in (1.0, 0.3371):
+        sf = np.full((rows, cols // group), s, np.float32)
+        code_dt = {"e4m3": torch.float8_e4m3fn, "e5m2": torch.float8_e5m2}.get(fmt, torch.uint8)
+        out = pq.qcast_cast_back(torch.from_numpy(q).to(dev).view(code_dt),
+                                 torch.from_numpy(sf).to(dev), fmt, group, torch.float32)
+        torch.cuda.synchronize()
+        ref = oracle.cast_back(q, sf, cols, fmt, group, "f32")
+        assert np.array_equal(out.cpu().numpy().view(np.uint32), ref.view(np.uint32))
+
+
+def test_cast_back_round_trip_full_size(dev):
+    # the GPU's own codes of the hidden-size workload, dequantized on the GPU
+    # and by the oracle
+    wl = workloads.per_token_hidden()
+    x = wl.x.to(dev)
+    q, sf = pq.qcast_per_token(x)
+    out = pq.qcast_cast_back(q, sf)
+    torch.cuda.synchronize()
+    ref = oracle.cast_back(codes_np(q), sf.cpu().numpy(), 7168, "e4m3", 128, "bf16")
+    assert np.array_equal(out.cpu().view(torch.int16).numpy().view(np.uint16), ref)
