@@ -20,6 +20,9 @@ FMT_E2M1 = 2
 FMT_E5M2 = 3
 OUT_BF16 = 1
 OUT_F32 = 2
+SF_ROUND_POW2 = 1
+SF_COL_MAJOR = 2
+SF_PACKED_UE8M0 = 4
 _FMT_NAMES = {"e4m3": FMT_E4M3, "e2m1": FMT_E2M1, "e5m2": FMT_E5M2}
 
 _lib = None
@@ -62,6 +65,8 @@ def _load():
         "oracle_dequant_per_token": ([vp, vp, i64, i64, i32, i32, vp], i32),
         "oracle_cast_back": ([vp, vp, i64, i64, i32, i32, i32, vp], i32),
         "oracle_f32_to_bf16": ([f32], ctypes.c_uint16),
+        "oracle_per_token_sf": ([vp, i64, i64, i32, i32, f32, i32, vp, vp], i32),
+        "oracle_swiglu_per_token_sf": ([vp, i64, i64, vp, i32, i32, f32, i32, vp, vp], i32),
     }
     for name, (args, res) in sig.items():
         fn = getattr(lib, name)
@@ -226,3 +231,42 @@ def f32_to_bf16(x):
     lib = _load()
     return np.array([lib.oracle_f32_to_bf16(float(v)) for v in x.ravel()],
                     np.uint16).reshape(x.shape)
+
+
+def sf_shape(rows, cols, group, sf_flags):
+    """Shape and dtype of the scale tensor for a layout."""
+    groups = cols // group
+    rows_pad = (rows + 3) // 4 * 4
+    if sf_flags & SF_PACKED_UE8M0:
+        shape = (groups // 4, rows_pad) if sf_flags & SF_COL_MAJOR else (rows, groups // 4)
+        return shape, np.uint32
+    shape = (groups, rows_pad) if sf_flags & SF_COL_MAJOR else (rows, groups)
+    return shape, np.float32
+
+
+def per_token_sf(x, fmt="e4m3", group=128, clamp_min=0.0, sf_flags=0, sf_fill=0):
+    """Per-token cast with a scale-factor layout; unwritten padding keeps
+    sf_fill."""
+    f = fmt_id(fmt)
+    x = _u16(x)
+    rows, cols = x.shape
+    q = np.zeros(_code_shape(f, rows, cols), np.uint8)
+    shape, dt = sf_shape(rows, cols, group, sf_flags)
+    sf = np.full(shape, sf_fill, dt)
+    _check(_load().oracle_per_token_sf(_ptr(x), rows, cols, f, group, clamp_min, sf_flags, _ptr(q),
+                                       _ptr(sf)), "per_token_sf")
+    return q, sf
+
+
+def swiglu_per_token_sf(h, w=None, fmt="e4m3", group=128, clamp_min=0.0, sf_flags=0, sf_fill=0):
+    f = fmt_id(fmt)
+    h = _u16(h)
+    rows, two_n = h.shape
+    cols = two_n // 2
+    w = None if w is None else _f32(w)
+    q = np.zeros(_code_shape(f, rows, cols), np.uint8)
+    shape, dt = sf_shape(rows, cols, group, sf_flags)
+    sf = np.full(shape, sf_fill, dt)
+    _check(_load().oracle_swiglu_per_token_sf(_ptr(h), rows, cols, _ptr(w), f, group, clamp_min,
+                                              sf_flags, _ptr(q), _ptr(sf)), "swiglu_per_token_sf")
+    return q, sf

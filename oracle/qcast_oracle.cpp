@@ -35,7 +35,15 @@
  *  - [WALK] §3.1 gives floors for E4M3 and E2M1 only; E5M2, the other 8-bit
  *    format, takes the E4M3 floor 1e-4;
  *  - cast_back is the fp32 product decode(code) * sf, rounded to bf16 to
- *    nearest even when bf16 output is asked for.
+ *    nearest even when bf16 output is asked for;
+ *  - round_sf ([WALK] §3.1) rounds sf UP to a power of two, so that no value
+ *    saturates ([SPLIT] §一 says the quant ops take exponents with bit
+ *    operations); a scale below 2^-126 becomes 2^-126;
+ *  - the layouts of [SPLIT] §四 C: "TMA-aligned column-major" stores the
+ *    scales group-major with the row count padded to a multiple of 4 (16
+ *    bytes of fp32 or of packed words); "packed UE8M0" stores each (power of
+ *    two) scale as its biased exponent byte, 4 per 32-bit word along the
+ *    groups of a row, lowest group in the lowest byte.
  *
  * Arithmetic discipline: plain C++ on one thread, fp32 where the method is
  * fp32 (the scale, the inverse, the scaled value, SwiGLU) with no
@@ -254,6 +262,21 @@ int check_common(const void* a, const void* b, const void* c, int fmt, int group
   return ORACLE_OK;
 }
 
+/* The smallest power of two that is >= sf and >= 2^-126 (round_sf). */
+float round_up_pow2(float sf) {
+  if (sf <= std::ldexp(1.0f, -126)) return std::ldexp(1.0f, -126);
+  int e = 0;
+  const float m = std::frexp(sf, &e); /* sf = m * 2^e, m in [0.5, 1) */
+  return (m == 0.5f) ? sf : std::ldexp(1.0f, e);
+}
+
+/* Biased exponent of a normal power of two (its UE8M0 byte). */
+uint8_t ue8m0_of(float pow2) {
+  int e = 0;
+  std::frexp(pow2, &e); /* pow2 = 0.5 * 2^e */
+  return static_cast<uint8_t>(e - 1 + 127);
+}
+
 /* Per-token cast of rows of fp32 values ([WALK] §3.2): for each row and each
  * run of `group` columns, the abs-max, the scale, then every element times
  * the inverse scale, encoded. */
@@ -278,6 +301,50 @@ void per_token_rows(const float* x, int64_t rows, int64_t cols, int fmt, int gro
       sf[r * groups + k] = s.sf;
     }
   }
+}
+
+/* Per-token cast of one row of fp32 values with the scale-factor options;
+ * stores the scales of row r into the chosen layout. */
+void per_token_row_sf(const float* xr, int64_t r, int64_t rows, int64_t cols, int fmt, int group,
+                      float floor, int flags, uint8_t* qr, void* sf) {
+  const FormatTable& t = *table_for(fmt);
+  const int64_t groups = cols / group;
+  const int64_t rows_pad = (rows + 3) / 4 * 4;
+  const bool round = (flags & (ORACLE_SF_ROUND_POW2 | ORACLE_SF_PACKED_UE8M0)) != 0;
+  for (int64_t k = 0; k < groups; ++k) {
+    float amax = 0.0f;
+    for (int64_t i = 0; i < group; ++i) {
+      const float m = std::fabs(xr[k * group + i]);
+      if (m > amax) amax = m;
+    }
+    Scale s = scale_from_amax(t, amax, floor);
+    if (round) {
+      s.sf = round_up_pow2(s.sf);
+      s.sf_inv = 1.0f / s.sf;
+    }
+    for (int64_t i = 0; i < group; ++i) {
+      const int64_t c = k * group + i;
+      put_code(fmt, qr, cols, 0, c, encode(t, xr[c] * s.sf_inv));
+    }
+    if (flags & ORACLE_SF_PACKED_UE8M0) {
+      uint32_t* words = static_cast<uint32_t*>(sf);
+      const int64_t word = (flags & ORACLE_SF_COL_MAJOR) ? (k / 4) * rows_pad + r
+                                                         : r * (groups / 4) + k / 4;
+      const int shift = 8 * static_cast<int>(k % 4);
+      words[word] = (words[word] & ~(0xFFu << shift)) |
+                    (static_cast<uint32_t>(ue8m0_of(s.sf)) << shift);
+    } else {
+      float* f = static_cast<float*>(sf);
+      f[(flags & ORACLE_SF_COL_MAJOR) ? k * rows_pad + r : r * groups + k] = s.sf;
+    }
+  }
+}
+
+int check_sf_flags(int flags, int64_t cols, int group) {
+  if (flags & ~(ORACLE_SF_ROUND_POW2 | ORACLE_SF_COL_MAJOR | ORACLE_SF_PACKED_UE8M0))
+    return ORACLE_ERR_FORMAT;
+  if ((flags & ORACLE_SF_PACKED_UE8M0) && (cols / group) % 4 != 0) return ORACLE_ERR_SHAPE;
+  return ORACLE_OK;
 }
 
 } /* namespace */
@@ -466,6 +533,41 @@ int oracle_dequant_per_token(const uint8_t* q, const float* sf, int64_t rows, in
   for (int64_t r = 0; r < rows; ++r)
     for (int64_t c = 0; c < cols; ++c)
       out[r * cols + c] = decode(t, get_code(fmt, q, cols, r, c)) * sf[r * groups + c / group];
+  return ORACLE_OK;
+}
+
+int oracle_per_token_sf(const uint16_t* x, int64_t rows, int64_t cols, int fmt, int group,
+                        float clamp_min, int sf_flags, uint8_t* q, void* sf) {
+  int rc = check_common(x, q, sf, fmt, group);
+  if (rc != ORACLE_OK) return rc;
+  if (rows < 0 || cols < 0 || cols % group != 0) return ORACLE_ERR_SHAPE;
+  if (fmt == ORACLE_FMT_E2M1 && group % 2 != 0) return ORACLE_ERR_GROUP;
+  if ((rc = check_sf_flags(sf_flags, cols, group)) != ORACLE_OK) return rc;
+  const float floor = floor_for(*table_for(fmt), clamp_min);
+  const int64_t code_bytes = (fmt == ORACLE_FMT_E2M1) ? cols / 2 : cols;
+  std::vector<float> row(static_cast<size_t>(cols));
+  for (int64_t r = 0; r < rows; ++r) {
+    for (int64_t c = 0; c < cols; ++c) row[c] = bf16_value(x[r * cols + c]);
+    per_token_row_sf(row.data(), r, rows, cols, fmt, group, floor, sf_flags, q + r * code_bytes, sf);
+  }
+  return ORACLE_OK;
+}
+
+int oracle_swiglu_per_token_sf(const uint16_t* h, int64_t rows, int64_t cols, const float* w,
+                               int fmt, int group, float clamp_min, int sf_flags, uint8_t* q,
+                               void* sf) {
+  int rc = check_common(h, q, sf, fmt, group);
+  if (rc != ORACLE_OK) return rc;
+  if (rows < 0 || cols < 0 || cols % group != 0) return ORACLE_ERR_SHAPE;
+  if (fmt == ORACLE_FMT_E2M1 && group % 2 != 0) return ORACLE_ERR_GROUP;
+  if ((rc = check_sf_flags(sf_flags, cols, group)) != ORACLE_OK) return rc;
+  const float floor = floor_for(*table_for(fmt), clamp_min);
+  const int64_t code_bytes = (fmt == ORACLE_FMT_E2M1) ? cols / 2 : cols;
+  std::vector<float> v(static_cast<size_t>(cols));
+  for (int64_t r = 0; r < rows; ++r) {
+    oracle_swiglu_values(h + r * 2 * cols, 1, cols, w ? w + r : nullptr, v.data());
+    per_token_row_sf(v.data(), r, rows, cols, fmt, group, floor, sf_flags, q + r * code_bytes, sf);
+  }
   return ORACLE_OK;
 }
 

@@ -35,6 +35,8 @@ enum {
 
 enum { ORACLE_FMT_E4M3 = 1, ORACLE_FMT_E2M1 = 2, ORACLE_FMT_E5M2 = 3 };
 enum { ORACLE_OUT_BF16 = 1, ORACLE_OUT_F32 = 2 };
+/* Scale-factor layout flags (see oracle_per_token_sf). */
+enum { ORACLE_SF_ROUND_POW2 = 1, ORACLE_SF_COL_MAJOR = 2, ORACLE_SF_PACKED_UE8M0 = 4 };
 
 int oracle_version(void);
 
@@ -90,6 +92,25 @@ int oracle_dequant_per_token(const uint8_t* q, const float* sf, int64_t rows, in
  * round-to-nearest-even (ORACLE_OUT_BF16, out is uint16_t* bit patterns). */
 int oracle_cast_back(const uint8_t* q, const float* sf, int64_t rows, int64_t cols, int fmt,
                      int group, int out_dtype, void* out);
+
+/* Per-token cast (fp32 values already widened from bf16, or SwiGLU values)
+ * with the scale-factor options of a cast config:
+ *   ORACLE_SF_ROUND_POW2   sf rounded up to the smallest power of two that is
+ *                          >= sf and >= 2^-126; codes use 1 / that power.
+ *   ORACLE_SF_COL_MAJOR    scales stored [cols/group][rows_pad] with
+ *                          rows_pad = ceil(rows / 4) * 4; padding untouched.
+ *   ORACLE_SF_PACKED_UE8M0 (implies ROUND_POW2) each scale stored as its
+ *                          biased exponent byte, 4 per uint32 along the
+ *                          groups of a row (group 4j + i in byte i of word j);
+ *                          requires (cols/group) % 4 == 0. Row-major
+ *                          [rows][cols/group/4], or with COL_MAJOR
+ *                          [cols/group/4][rows_pad].
+ * sf points to float or uint32 storage accordingly. */
+int oracle_per_token_sf(const uint16_t* x, int64_t rows, int64_t cols, int fmt, int group,
+                        float clamp_min, int sf_flags, uint8_t* q, void* sf);
+int oracle_swiglu_per_token_sf(const uint16_t* h, int64_t rows, int64_t cols, const float* w,
+                               int fmt, int group, float clamp_min, int sf_flags, uint8_t* q,
+                               void* sf);
 
 /* fp32 -> bf16 bit pattern, round to nearest even (NaN kept quiet). */
 uint16_t oracle_f32_to_bf16(float f);

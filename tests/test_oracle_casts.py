@@ -359,3 +359,77 @@ def test_swiglu_fp32_path_close_to_double_restatement():
     q, _ = oracle.swiglu_per_token(h, wl.w.numpy())
     qd, _ = oracle.per_token_f32(vd.astype(np.float32), "e4m3", 128)
     assert (q != qd).mean() < 1e-3
+
+
+# ------------------------------------------------------------ scale-factor layouts
+
+def pow2_ceil(sf):
+    """Smallest power of two >= sf and >= 2^-126 (closed form via frexp)."""
+    m, e = np.frexp(sf.astype(np.float64))
+    p = np.where(m == 0.5, sf.astype(np.float64), np.ldexp(1.0, e))
+    return np.maximum(p, 2.0 ** -126).astype(np.float32)
+
+
+@pytest.mark.parametrize("fmt,group", [("e4m3", 128), ("e2m1", 32), ("e5m2", 64)])
+def test_round_sf_is_the_next_power_of_two_and_codes_follow(fmt, group):
+    from test_oracle_codec import brute_force_encode, magnitudes
+    x = small_rows(20, 6, 512)
+    x[0, :group] = 0                                     # a floor-only group
+    _, sf_plain = oracle.per_token(x, fmt, group)
+    q, sf = oracle.per_token_sf(x, fmt, group, sf_flags=oracle.SF_ROUND_POW2)
+    assert np.array_equal(sf, pow2_ceil(sf_plain))
+    assert (sf >= sf_plain).all() and (sf < 2 * sf_plain + 2.0 ** -126).all()
+    xf = bf16_to_f32(x).reshape(6, -1, group).astype(np.float64)
+    y = (xf / sf[..., None].astype(np.float64)).astype(np.float32)   # exact: sf is 2^k
+    assert (np.abs(y) <= FMAX[fmt]).all()                # nothing saturates
+    codes = brute_force_encode(y.ravel(), magnitudes(fmt), SIGN[fmt]).reshape(6, 512)
+    got = unpack_e2m1(q) if fmt == "e2m1" else q
+    assert np.array_equal(got, codes)
+
+
+def test_col_major_layout_is_the_padded_transpose():
+    x = small_rows(21, 7, 512)                           # 7 rows -> padded to 8
+    _, sf_row = oracle.per_token_sf(x, "e4m3", 128, sf_flags=0)
+    _, sf_col = oracle.per_token_sf(x, "e4m3", 128, sf_flags=oracle.SF_COL_MAJOR, sf_fill=-1.0)
+    assert sf_col.shape == (4, 8)
+    assert np.array_equal(sf_col[:, :7], sf_row.T)
+    assert (sf_col[:, 7] == -1.0).all()                 # padding untouched
+
+
+def test_packed_ue8m0_hand_example_and_layouts():
+    # groups with amax 448, 896, 224 and 0 give sf = 1, 2, 0.5 and the floor
+    # 1e-4/448 rounded up to 2^-22: exponent bytes 127, 128, 126, 105.
+    row = np.zeros(512, np.float32)
+    row[0], row[128], row[256] = 448.0, 896.0, -224.0
+    x = bf16(np.stack([row, row * 2]))
+    _, w = oracle.per_token_sf(x, "e4m3", 128, sf_flags=oracle.SF_PACKED_UE8M0)
+    assert w.shape == (2, 1) and w.dtype == np.uint32
+    assert w[0, 0] == 127 | (128 << 8) | (126 << 16) | (105 << 24)
+    assert w[1, 0] == 128 | (129 << 8) | (127 << 16) | (105 << 24)
+    _, wc = oracle.per_token_sf(x, "e4m3", 128,
+                                sf_flags=oracle.SF_PACKED_UE8M0 | oracle.SF_COL_MAJOR, sf_fill=7)
+    assert wc.shape == (1, 4) and np.array_equal(wc[0, :2], w[:, 0]) and (wc[0, 2:] == 7).all()
+    # packed bytes are the exponents of the round_sf scales
+    x = small_rows(22, 5, 1024)
+    _, sf = oracle.per_token_sf(x, "e4m3", 128, sf_flags=oracle.SF_ROUND_POW2)
+    _, w = oracle.per_token_sf(x, "e4m3", 128, sf_flags=oracle.SF_PACKED_UE8M0)
+    bytes_ = w.view(np.uint8).reshape(5, 8)
+    assert np.array_equal(bytes_.astype(np.float64), np.log2(sf.astype(np.float64)) + 127)
+
+
+def test_packed_requires_groups_divisible_by_four():
+    with pytest.raises(oracle.OracleError):
+        oracle.per_token_sf(small_rows(23, 2, 384), "e4m3", 128,
+                            sf_flags=oracle.SF_PACKED_UE8M0)
+
+
+def test_swiglu_sf_layouts_agree_with_plain_swiglu():
+    wl = workloads.swiglu_input(seed=24, rows=12, cols=512)
+    h, w = workloads.bf16_bits(wl.x), wl.w.numpy()
+    q0, sf0 = oracle.swiglu_per_token(h, w)
+    q1, sf1 = oracle.swiglu_per_token_sf(h, w, sf_flags=0)
+    assert np.array_equal(q0, q1) and np.array_equal(sf0, sf1)
+    _, sfc = oracle.swiglu_per_token_sf(h, w, sf_flags=oracle.SF_COL_MAJOR)
+    assert np.array_equal(sfc[:, :12], sf0.T)
+    qr, sfr = oracle.swiglu_per_token_sf(h, w, sf_flags=oracle.SF_ROUND_POW2)
+    assert np.array_equal(sfr, pow2_ceil(sf0))
