@@ -72,6 +72,30 @@ typedef enum {
 
 typedef enum { QCAST_FMT_E4M3 = 1, QCAST_FMT_E2M1 = 2, QCAST_FMT_E5M2 = 3 } qcast_fmt;
 
+/*
+ * Scale-factor layout options of the *_sf entry points (the cast config of
+ * [WALK] §3.1 round_sf, and the layouts [SPLIT] §四 C says the casts write
+ * directly for the FP8 GEMMs that consume them). Let groups = cols / group
+ * and rows_pad = ceil(rows / 4) * 4 (16 bytes of 4-byte entries).
+ *   0                        fp32 sf[rows][groups] (the plain entry points)
+ *   QCAST_SF_ROUND_POW2      sf rounded UP to a power of two (at least
+ *                            2^-126) before the codes are formed, so no value
+ *                            saturates; codes use its exact inverse.
+ *   QCAST_SF_COL_MAJOR       fp32 sf[groups][rows_pad]; the padding entries
+ *                            are not written.
+ *   QCAST_SF_PACKED_UE8M0    implies ROUND_POW2; each scale stored as its
+ *                            biased exponent byte (UE8M0), 4 per uint32 along
+ *                            the groups of a row, group 4j+i in byte i of
+ *                            word j: uint32 [rows][groups/4], or with
+ *                            COL_MAJOR uint32 [groups/4][rows_pad]. Requires
+ *                            groups % 4 == 0.
+ */
+typedef enum {
+  QCAST_SF_ROUND_POW2 = 1,
+  QCAST_SF_COL_MAJOR = 2,
+  QCAST_SF_PACKED_UE8M0 = 4
+} qcast_sf_flags;
+
 /* Output type of qcast_cast_back. */
 typedef enum { QCAST_OUT_BF16 = 1, QCAST_OUT_F32 = 2 } qcast_out_dtype;
 
@@ -90,6 +114,11 @@ typedef enum { QCAST_OUT_BF16 = 1, QCAST_OUT_F32 = 2 } qcast_out_dtype;
  */
 QCAST_API int qcast_per_token(const void* x, int64_t rows, int64_t cols, int fmt, int group,
                     float clamp_min, void* q, float* sf, void* stream);
+
+/* qcast_per_token with a scale-factor layout (qcast_sf_flags); sf points to
+ * float or uint32 storage of the layout's shape (4-byte aligned). */
+QCAST_API int qcast_per_token_sf(const void* x, int64_t rows, int64_t cols, int fmt, int group,
+                                 float clamp_min, int sf_flags, void* q, void* sf, void* stream);
 
 /*
  * Per-token cast to packed FP4 E2M1 ([SPLIT] §四 A format list; [WALK] §3.1
@@ -115,6 +144,12 @@ QCAST_API int qcast_e2m1(const void* x, int64_t rows, int64_t cols, int group, f
 QCAST_API int qcast_swiglu_per_token(const void* h, int64_t rows, int64_t cols, const float* row_weight,
                            int fmt, int group, float clamp_min, void* q, float* sf,
                            void* stream);
+
+/* qcast_swiglu_per_token with a scale-factor layout (qcast_sf_flags). */
+QCAST_API int qcast_swiglu_per_token_sf(const void* h, int64_t rows, int64_t cols,
+                                        const float* row_weight, int fmt, int group,
+                                        float clamp_min, int sf_flags, void* q, void* sf,
+                                        void* stream);
 
 /*
  * Per-block cast of a weight ([SPLIT] §二 per_block_cast; [NEWS]

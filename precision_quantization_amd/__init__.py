@@ -16,10 +16,13 @@ mirrors the call shown in the quick start of the page
 """
 import torch
 
-from ._lib import FMT_E2M1, FMT_E4M3, FMT_E5M2, OUT_BF16, OUT_F32, QcastError, check, fmt_id, load
+from ._lib import (FMT_E2M1, FMT_E4M3, FMT_E5M2, OUT_BF16, OUT_F32, SF_COL_MAJOR,
+                   SF_PACKED_UE8M0, SF_ROUND_POW2, QcastError, check, fmt_id, load)
 
 __all__ = ["qcast_per_token", "qcast_e2m1", "qcast_swiglu_per_token", "qcast_per_block",
-           "qcast_per_channel_T", "qcast_cast_back", "qcast_abi_version", "qcast_set_num_cus", "qcast_bench_copy",
+           "qcast_per_channel_T", "qcast_cast_back", "qcast_per_token_sf",
+           "qcast_swiglu_per_token_sf", "sf_layout_shape", "SF_ROUND_POW2", "SF_COL_MAJOR",
+           "SF_PACKED_UE8M0", "qcast_abi_version", "qcast_set_num_cus", "qcast_bench_copy",
            "qcast_bench_check_scale",
            "per_token_cast",
            "QcastError", "FMT_E4M3", "FMT_E2M1", "FMT_E5M2"]
@@ -69,6 +72,59 @@ def qcast_per_token(x, fmt="e4m3", group=128, clamp_min=0.0, out=None, out_sf=No
         check(load().qcast_per_token(x.data_ptr(), rows, cols, f, group, clamp_min,
                                      out.data_ptr(), out_sf.data_ptr(), _stream(x.device, stream)),
               "qcast_per_token")
+    return out, out_sf
+
+
+def sf_layout_shape(rows, cols, group, sf_flags):
+    """(shape, dtype) of the scale tensor of a layout (include/qcast.h)."""
+    groups = cols // group
+    rows_pad = (rows + 3) // 4 * 4
+    if sf_flags & SF_PACKED_UE8M0:
+        shape = (groups // 4, rows_pad) if sf_flags & SF_COL_MAJOR else (rows, groups // 4)
+        return shape, torch.int32
+    shape = (groups, rows_pad) if sf_flags & SF_COL_MAJOR else (rows, groups)
+    return shape, torch.float32
+
+
+def qcast_per_token_sf(x, fmt="e4m3", group=128, clamp_min=0.0, sf_flags=0, out=None,
+                       out_sf=None, stream=None):
+    """qcast_per_token with a scale-factor layout; out_sf is float32 or int32
+    (packed UE8M0 words) of ``sf_layout_shape``."""
+    f = fmt_id(fmt)
+    x = _bf16_input(x, "x")
+    rows, cols = x.shape
+    qshape = (rows, cols // 2) if f == FMT_E2M1 else (rows, cols)
+    out = _out(out, qshape, _code_dtype(f), x.device, "out")
+    shape, dt = sf_layout_shape(rows, cols, group if group > 0 else 1, sf_flags)
+    out_sf = _out(out_sf, shape, dt, x.device, "out_sf")
+    with torch.cuda.device(x.device):
+        check(load().qcast_per_token_sf(x.data_ptr(), rows, cols, f, group, clamp_min, sf_flags,
+                                        out.data_ptr(), out_sf.data_ptr(),
+                                        _stream(x.device, stream)), "qcast_per_token_sf")
+    return out, out_sf
+
+
+def qcast_swiglu_per_token_sf(h, row_weight=None, fmt="e4m3", group=128, clamp_min=0.0,
+                              sf_flags=0, out=None, out_sf=None, stream=None):
+    """qcast_swiglu_per_token with a scale-factor layout."""
+    f = fmt_id(fmt)
+    h = _bf16_input(h, "h")
+    rows, two_n = h.shape
+    cols = two_n // 2
+    wptr = None
+    if row_weight is not None:
+        if row_weight.dtype != torch.float32 or tuple(row_weight.shape) != (rows,) or \
+                row_weight.device != h.device or not row_weight.is_contiguous():
+            raise QcastError(2, "row_weight must be a contiguous float32 [rows] tensor on h's device")
+        wptr = row_weight.data_ptr()
+    out = _out(out, (rows, cols), _code_dtype(f), h.device, "out")
+    shape, dt = sf_layout_shape(rows, cols, group if group > 0 else 1, sf_flags)
+    out_sf = _out(out_sf, shape, dt, h.device, "out_sf")
+    with torch.cuda.device(h.device):
+        check(load().qcast_swiglu_per_token_sf(h.data_ptr(), rows, cols, wptr, f, group, clamp_min,
+                                               sf_flags, out.data_ptr(), out_sf.data_ptr(),
+                                               _stream(h.device, stream)),
+              "qcast_swiglu_per_token_sf")
     return out, out_sf
 
 

@@ -14,6 +14,9 @@ FMT_E2M1 = 2
 FMT_E5M2 = 3
 OUT_BF16 = 1
 OUT_F32 = 2
+SF_ROUND_POW2 = 1
+SF_COL_MAJOR = 2
+SF_PACKED_UE8M0 = 4
 _FMT = {"e4m3": FMT_E4M3, "e2m1": FMT_E2M1, "e5m2": FMT_E5M2}
 
 _lib = None
@@ -55,6 +58,8 @@ def load():
         "qcast_per_block": [vp, i64, i64, i32, i32, f32, vp, vp, vp],
         "qcast_per_channel_T": [vp, i64, i64, i32, i32, f32, vp, vp, vp],
         "qcast_cast_back": [vp, vp, i64, i64, i32, i32, i32, vp, vp],
+        "qcast_per_token_sf": [vp, i64, i64, i32, i32, f32, i32, vp, vp, vp],
+        "qcast_swiglu_per_token_sf": [vp, i64, i64, vp, i32, i32, f32, i32, vp, vp, vp],
     }
     for name, args in sig.items():
         fn = getattr(lib, name)
@@ -81,5 +86,6 @@ def check(status, what):
 
 
 EXPORTS = ["qcast_per_token", "qcast_e2m1", "qcast_swiglu_per_token", "qcast_per_block",
-           "qcast_per_channel_T", "qcast_cast_back", "qcast_status_str", "qcast_abi_version", "qcast_set_num_cus",
+           "qcast_per_channel_T", "qcast_cast_back", "qcast_per_token_sf",
+           "qcast_swiglu_per_token_sf", "qcast_status_str", "qcast_abi_version", "qcast_set_num_cus",
            "qcast_bench_copy", "qcast_bench_check_scale"]

@@ -37,7 +37,7 @@ constexpr int kWgPerCu = QCAST_PT_WG_PER_CU;
 template <int kLanes, int kFmt>
 __global__ __launch_bounds__(kThreads) void per_token_kernel(
     const u32x4* __restrict__ x, int64_t nchunks, float floor, uint8_t* __restrict__ q,
-    float* __restrict__ sf) {
+    void* __restrict__ sf, SfLayout lay) {
   const int64_t step = (int64_t)gridDim.x * kThreads * kUnroll;
   for (int64_t base = (int64_t)blockIdx.x * kThreads * kUnroll + threadIdx.x; base < nchunks;
        base += step) {
@@ -56,7 +56,8 @@ __global__ __launch_bounds__(kThreads) void per_token_kernel(
         float v[8];
         unpack8(raw[u], v);
         const float amax = lane_group_max<kLanes>(absmax8(v));
-        const Scale s = group_scale<kFmt>(amax, floor);
+        Scale s = group_scale<kFmt>(amax, floor);
+        if (lay.flags & kSfRound) s = round_scale_pow2(s);
         float y[8];
 #pragma unroll
         for (int i = 0; i < 8; ++i) y[i] = v[i] * s.inv;
@@ -68,15 +69,15 @@ __global__ __launch_bounds__(kThreads) void per_token_kernel(
           out.y = fp8x4<kFmt>(y[4], y[5], y[6], y[7]);
           store_stream(reinterpret_cast<u32x2*>(q) + c, out);
         }
-        if ((threadIdx.x & (kLanes - 1)) == 0) sf[c / kLanes] = s.sf;
+        store_group_scale<kLanes>(sf, (uint32_t)(c / kLanes), s, lay);
       }
     }
   }
 }
 
 template <int kLanes, int kFmt>
-hipError_t launch(const void* x, int64_t nchunks, float floor, void* q, float* sf,
-                  hipStream_t stream, const LaunchCaps& caps) {
+hipError_t launch(const void* x, int64_t nchunks, float floor, void* q, void* sf,
+                  const SfLayout& lay, hipStream_t stream, const LaunchCaps& caps) {
   const int64_t per_block_iter = (int64_t)kThreads * kUnroll;
   const int64_t iters = (nchunks + per_block_iter - 1) / per_block_iter;
   // Persistent grid: at most kWgPerCu workgroups per CU, the same number of
@@ -86,17 +87,18 @@ hipError_t launch(const void* x, int64_t nchunks, float floor, void* q, float* s
   const int64_t blocks = (iters + iters_per_block - 1) / iters_per_block;
   hipLaunchKernelGGL((per_token_kernel<kLanes, kFmt>), dim3((unsigned)blocks), dim3(kThreads), 0,
                      stream, static_cast<const u32x4*>(x), nchunks, floor,
-                     static_cast<uint8_t*>(q), sf);
+                     static_cast<uint8_t*>(q), sf, lay);
   return hipGetLastError();
 }
 
 template <int kFmt>
 hipError_t launch_fmt(const void* x, int64_t nchunks, int group, float floor, void* q,
-                      float* sf, hipStream_t stream, const LaunchCaps& caps) {
+                      void* sf, const SfLayout& lay, hipStream_t stream,
+                      const LaunchCaps& caps) {
   switch (group) {
-    case 32: return launch<4, kFmt>(x, nchunks, floor, q, sf, stream, caps);
-    case 64: return launch<8, kFmt>(x, nchunks, floor, q, sf, stream, caps);
-    case 128: return launch<16, kFmt>(x, nchunks, floor, q, sf, stream, caps);
+    case 32: return launch<4, kFmt>(x, nchunks, floor, q, sf, lay, stream, caps);
+    case 64: return launch<8, kFmt>(x, nchunks, floor, q, sf, lay, stream, caps);
+    case 128: return launch<16, kFmt>(x, nchunks, floor, q, sf, lay, stream, caps);
   }
   return hipErrorInvalidValue;
 }
@@ -104,14 +106,16 @@ hipError_t launch_fmt(const void* x, int64_t nchunks, int group, float floor, vo
 }  // namespace
 
 hipError_t launch_per_token(const void* x, int64_t rows, int64_t cols, int fmt, int group,
-                            float floor, void* q, float* sf, hipStream_t stream,
-                            const LaunchCaps& caps) {
+                            float floor, uint32_t sf_flags, void* q, void* sf,
+                            hipStream_t stream, const LaunchCaps& caps) {
   const int64_t nchunks = rows * cols / 8;
   if (nchunks == 0) return hipSuccess;
+  if (rows * cols / group >= (int64_t(1) << 31)) return hipErrorInvalidValue;
+  const SfLayout lay = make_sf_layout(rows, cols, group, sf_flags);
   switch (fmt) {
-    case kE4M3: return launch_fmt<kE4M3>(x, nchunks, group, floor, q, sf, stream, caps);
-    case kE2M1: return launch_fmt<kE2M1>(x, nchunks, group, floor, q, sf, stream, caps);
-    case kE5M2: return launch_fmt<kE5M2>(x, nchunks, group, floor, q, sf, stream, caps);
+    case kE4M3: return launch_fmt<kE4M3>(x, nchunks, group, floor, q, sf, lay, stream, caps);
+    case kE2M1: return launch_fmt<kE2M1>(x, nchunks, group, floor, q, sf, lay, stream, caps);
+    case kE5M2: return launch_fmt<kE5M2>(x, nchunks, group, floor, q, sf, lay, stream, caps);
   }
   return hipErrorInvalidValue;
 }

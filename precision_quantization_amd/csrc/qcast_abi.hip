@@ -62,6 +62,19 @@ int finish(hipError_t err) { return err == hipSuccess ? QCAST_OK : QCAST_ERR_LAU
 
 bool per_token_group_ok(int group) { return group == 32 || group == 64 || group == 128; }
 
+bool sf_flags_ok(int flags) {
+  return (flags & ~(QCAST_SF_ROUND_POW2 | QCAST_SF_COL_MAJOR | QCAST_SF_PACKED_UE8M0)) == 0;
+}
+
+// Group indices are 32-bit in the scale store; packed words need whole
+// quadruples of groups in every row.
+bool sf_shape_ok(int64_t rows, int64_t cols, int group, int flags) {
+  if (cols > 0 && rows > ((int64_t(1) << 31) - 1) / (cols / group > 0 ? cols / group : 1))
+    return false;
+  if ((flags & QCAST_SF_PACKED_UE8M0) && (cols / group) % 4 != 0) return false;
+  return true;
+}
+
 // Element counts beyond 2^62 would overflow the kernels' int64 offsets.
 bool too_big(int64_t rows, int64_t cols) {
   return cols > 0 && rows > (int64_t(1) << 62) / cols;
@@ -89,19 +102,28 @@ const char* qcast_status_str(int status) {
 
 void qcast_set_num_cus(int n) { g_cu_override.store(n > 0 ? n : 0, std::memory_order_relaxed); }
 
-int qcast_per_token(const void* x, int64_t rows, int64_t cols, int fmt, int group,
-                    float clamp_min, void* q, float* sf, void* stream) {
+int qcast_per_token_sf(const void* x, int64_t rows, int64_t cols, int fmt, int group,
+                       float clamp_min, int sf_flags, void* q, void* sf, void* stream) {
   if (!any_fmt(fmt)) return QCAST_ERR_FORMAT;
+  if (!sf_flags_ok(sf_flags)) return QCAST_ERR_FORMAT;
   if (!per_token_group_ok(group)) return QCAST_ERR_GROUP;
-  if (rows < 0 || cols < 0 || cols % group != 0 || too_big(rows, cols)) return QCAST_ERR_SHAPE;
+  if (rows < 0 || cols < 0 || cols % group != 0 || too_big(rows, cols) ||
+      !sf_shape_ok(rows, cols, group, sf_flags))
+    return QCAST_ERR_SHAPE;
   if (rows == 0 || cols == 0) return QCAST_OK;
   if (!x || !q || !sf) return QCAST_ERR_NULL;
   if (!aligned(x, 16) || !aligned(q, 16) || !aligned(sf, 4)) return QCAST_ERR_ALIGN;
   qcast::LaunchCaps caps;
   const int rc = caps_for_current_device(&caps);
   if (rc != QCAST_OK) return rc;
-  return finish(qcast::launch_per_token(x, rows, cols, fmt, group, floor_for(fmt, clamp_min), q,
-                                        sf, static_cast<hipStream_t>(stream), caps));
+  return finish(qcast::launch_per_token(x, rows, cols, fmt, group, floor_for(fmt, clamp_min),
+                                        (uint32_t)sf_flags, q, sf,
+                                        static_cast<hipStream_t>(stream), caps));
+}
+
+int qcast_per_token(const void* x, int64_t rows, int64_t cols, int fmt, int group,
+                    float clamp_min, void* q, float* sf, void* stream) {
+  return qcast_per_token_sf(x, rows, cols, fmt, group, clamp_min, 0, q, sf, stream);
 }
 
 int qcast_e2m1(const void* x, int64_t rows, int64_t cols, int group, float clamp_min,
@@ -109,13 +131,14 @@ int qcast_e2m1(const void* x, int64_t rows, int64_t cols, int group, float clamp
   return qcast_per_token(x, rows, cols, QCAST_FMT_E2M1, group, clamp_min, q_packed, sf, stream);
 }
 
-int qcast_swiglu_per_token(const void* h, int64_t rows, int64_t cols, const float* row_weight,
-                           int fmt, int group, float clamp_min, void* q, float* sf,
-                           void* stream) {
+int qcast_swiglu_per_token_sf(const void* h, int64_t rows, int64_t cols,
+                              const float* row_weight, int fmt, int group, float clamp_min,
+                              int sf_flags, void* q, void* sf, void* stream) {
   if (!fp8_fmt(fmt)) return QCAST_ERR_FORMAT;
+  if (!sf_flags_ok(sf_flags)) return QCAST_ERR_FORMAT;
   if (!per_token_group_ok(group)) return QCAST_ERR_GROUP;
   if (rows < 0 || cols < 0 || cols % group != 0 || cols / 8 >= (int64_t(1) << 16) ||
-      too_big(rows, 2 * cols))
+      too_big(rows, 2 * cols) || !sf_shape_ok(rows, cols, group, sf_flags))
     return QCAST_ERR_SHAPE;
   if (rows == 0 || cols == 0) return QCAST_OK;
   if (!h || !q || !sf) return QCAST_ERR_NULL;
@@ -126,8 +149,15 @@ int qcast_swiglu_per_token(const void* h, int64_t rows, int64_t cols, const floa
   const int rc = caps_for_current_device(&caps);
   if (rc != QCAST_OK) return rc;
   return finish(qcast::launch_swiglu_per_token(h, rows, cols, row_weight, fmt, group,
-                                               floor_for(fmt, clamp_min), q, sf,
-                                               static_cast<hipStream_t>(stream), caps));
+                                               floor_for(fmt, clamp_min), (uint32_t)sf_flags, q,
+                                               sf, static_cast<hipStream_t>(stream), caps));
+}
+
+int qcast_swiglu_per_token(const void* h, int64_t rows, int64_t cols, const float* row_weight,
+                           int fmt, int group, float clamp_min, void* q, float* sf,
+                           void* stream) {
+  return qcast_swiglu_per_token_sf(h, rows, cols, row_weight, fmt, group, clamp_min, 0, q, sf,
+                                   stream);
 }
 
 int qcast_per_block(const void* x, int64_t rows, int64_t cols, int fmt, int block,

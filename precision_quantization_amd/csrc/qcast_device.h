@@ -80,6 +80,70 @@ __device__ __forceinline__ Scale group_scale(float amax, float floor) {
   return s;
 }
 
+// Scale-factor layout of the per-token casts (the options of the pages'
+// cast config: round_sf, TMA-aligned column-major, packed UE8M0).
+constexpr uint32_t kSfRound = 1;     // sf rounded up to a power of two
+constexpr uint32_t kSfColMajor = 2;  // [groups per row][rows_pad]
+constexpr uint32_t kSfPacked = 4;    // 4 exponent bytes per 32-bit word
+
+struct SfLayout {
+  uint32_t flags;     // kSf* bits; kSfPacked always comes with kSfRound
+  uint32_t gpr;       // groups per row
+  uint32_t rows_pad;  // rows rounded up to a multiple of 4
+  double inv_gpr;     // 1 / gpr, for the row of a group index
+};
+
+// round_sf: the smallest power of two >= sf and >= 2^-126, and its exact
+// inverse, by exponent arithmetic (sf <= 2^126 for every format here).
+__device__ __forceinline__ Scale round_scale_pow2(Scale s) {
+  uint32_t b = (__float_as_uint(s.sf) + 0x7fffffu) & 0x7f800000u;
+  b = b < 0x00800000u ? 0x00800000u : b;
+  s.sf = __uint_as_float(b);
+  s.inv = __uint_as_float((254u << 23) - b);
+  return s;
+}
+
+// Row of flat group index k (k < 2^31): a double-precision estimate, then
+// corrected by one in either direction.
+__device__ __forceinline__ uint32_t row_of_group(uint32_t k, const SfLayout& lay) {
+  uint32_t r = (uint32_t)((double)k * lay.inv_gpr);
+  if ((uint64_t)(r + 1) * lay.gpr <= k) ++r;
+  if ((uint64_t)r * lay.gpr > k) --r;
+  return r;
+}
+
+// Store the scale of flat group k held by this lane (lanes of a group are
+// kLanes consecutive lanes; every active lane calls this). Row-major fp32 is
+// sf[k]; the other layouts are chosen at run time.
+template <int kLanes>
+__device__ __forceinline__ void store_group_scale(void* sf, uint32_t k, const Scale& s,
+                                                  const SfLayout& lay) {
+  const int lane = threadIdx.x & 63;
+  if (lay.flags & kSfPacked) {
+    // 4 consecutive groups sit in 4 * kLanes consecutive lanes (aligned):
+    // the first lane gathers the exponent bytes and writes one word.
+    const uint32_t e = __float_as_uint(s.sf) >> 23;
+    const uint32_t w = e | ((uint32_t)__shfl((int)e, lane + kLanes) << 8) |
+                       ((uint32_t)__shfl((int)e, lane + 2 * kLanes) << 16) |
+                       ((uint32_t)__shfl((int)e, lane + 3 * kLanes) << 24);
+    if ((lane & (4 * kLanes - 1)) == 0) {
+      uint32_t idx = k / 4;
+      if (lay.flags & kSfColMajor) {
+        const uint32_t r = row_of_group(k, lay);
+        idx = ((k - r * lay.gpr) / 4) * lay.rows_pad + r;
+      }
+      static_cast<uint32_t*>(sf)[idx] = w;
+    }
+  } else if ((lane & (kLanes - 1)) == 0) {
+    uint32_t idx = k;
+    if (lay.flags & kSfColMajor) {
+      const uint32_t r = row_of_group(k, lay);
+      idx = (k - r * lay.gpr) * lay.rows_pad + r;
+    }
+    static_cast<float*>(sf)[idx] = s.sf;
+  }
+}
+
 // bf16 pair in one dword -> two fp32 (exact: a bf16 is the top half of an fp32).
 __device__ __forceinline__ float bf16_lo(uint32_t w) { return __uint_as_float(w << 16); }
 __device__ __forceinline__ float bf16_hi(uint32_t w) { return __uint_as_float(w & 0xffff0000u); }

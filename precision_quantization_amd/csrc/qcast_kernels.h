@@ -5,6 +5,8 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include "qcast_device.h"
+
 namespace qcast {
 
 // Launch shape knobs shared by the launchers.
@@ -12,18 +14,29 @@ struct LaunchCaps {
   int num_cus;          // compute units on the device (or the override)
 };
 
-// x [rows, cols] bf16 -> per-token codes + scales; group in {32, 64, 128};
-// fmt kE4M3, kE5M2 or kE2M1. Requires cols % group == 0.
+// The scale-factor layout of a per-token cast of [rows, cols] with `group`.
+inline SfLayout make_sf_layout(int64_t rows, int64_t cols, int group, uint32_t flags) {
+  SfLayout lay;
+  lay.flags = (flags & kSfPacked) ? (flags | kSfRound) : flags;
+  lay.gpr = (uint32_t)(cols / group);
+  lay.rows_pad = (uint32_t)((rows + 3) / 4 * 4);
+  lay.inv_gpr = lay.gpr ? 1.0 / (double)lay.gpr : 0.0;
+  return lay;
+}
+
+// x [rows, cols] bf16 -> per-token codes + scales in the layout sf_flags
+// (kSf* bits); group in {32, 64, 128}; fmt kE4M3, kE5M2 or kE2M1. Requires
+// cols % group == 0, and (cols / group) % 4 == 0 for kSfPacked.
 hipError_t launch_per_token(const void* x, int64_t rows, int64_t cols, int fmt, int group,
-                            float floor, void* q, float* sf, hipStream_t stream,
-                            const LaunchCaps& caps);
+                            float floor, uint32_t sf_flags, void* q, void* sf,
+                            hipStream_t stream, const LaunchCaps& caps);
 
 // h [rows, 2*cols] bf16 (gate | up), w [rows] fp32 or null -> 8-bit codes
 // (kE4M3 / kE5M2) + scales of silu(gate) * up * w; group in {32, 64, 128};
 // cols % group == 0.
 hipError_t launch_swiglu_per_token(const void* h, int64_t rows, int64_t cols, const float* w,
-                                   int fmt, int group, float floor, void* q, float* sf,
-                                   hipStream_t stream, const LaunchCaps& caps);
+                                   int fmt, int group, float floor, uint32_t sf_flags, void* q,
+                                   void* sf, hipStream_t stream, const LaunchCaps& caps);
 
 // x [rows, cols] bf16 -> 8-bit codes + one scale per 128 x 128 block.
 hipError_t launch_per_block(const void* x, int64_t rows, int64_t cols, int fmt, float floor,

@@ -48,7 +48,7 @@ template <int kLanes, bool kWeighted, int kFmt>
 __global__ __launch_bounds__(kThreads) void swiglu_kernel(
     const uint16_t* __restrict__ h, const float* __restrict__ w, int64_t nchunks,
     uint32_t chunks_per_row, uint64_t row_magic, int64_t cols, float floor,
-    uint8_t* __restrict__ q, float* __restrict__ sf) {
+    uint8_t* __restrict__ q, void* __restrict__ sf, SfLayout lay, uint32_t group0) {
   const int64_t step = (int64_t)gridDim.x * kThreads * kUnroll;
   for (int64_t base = (int64_t)blockIdx.x * kThreads * kUnroll + threadIdx.x; base < nchunks;
        base += step) {
@@ -79,12 +79,13 @@ __global__ __launch_bounds__(kThreads) void swiglu_kernel(
           if (kWeighted) v[i] = v[i] * wr[u];
         }
         const float amax = lane_group_max<kLanes>(absmax8(v));
-        const Scale s = group_scale<kFmt>(amax, floor);
+        Scale s = group_scale<kFmt>(amax, floor);
+        if (lay.flags & kSfRound) s = round_scale_pow2(s);
         u32x2 out;
         out.x = fp8x4<kFmt>(v[0] * s.inv, v[1] * s.inv, v[2] * s.inv, v[3] * s.inv);
         out.y = fp8x4<kFmt>(v[4] * s.inv, v[5] * s.inv, v[6] * s.inv, v[7] * s.inv);
         store_stream(reinterpret_cast<u32x2*>(q) + c, out);
-        if ((threadIdx.x & (kLanes - 1)) == 0) sf[c / kLanes] = s.sf;
+        store_group_scale<kLanes>(sf, group0 + (uint32_t)(c / kLanes), s, lay);
       }
     }
   }
@@ -92,7 +93,8 @@ __global__ __launch_bounds__(kThreads) void swiglu_kernel(
 
 template <int kLanes, bool kWeighted, int kFmt>
 hipError_t launch(const uint16_t* h, const float* w, int64_t rows, int64_t cols, float floor,
-                  uint8_t* q, float* sf, hipStream_t stream, const LaunchCaps& caps) {
+                  uint8_t* q, void* sf, const SfLayout& lay, hipStream_t stream,
+                  const LaunchCaps& caps) {
   const int64_t cpr = cols / 8;
   const uint64_t magic = ((uint64_t(1) << 40) + (uint64_t)cpr - 1) / (uint64_t)cpr;
   const int64_t groups_per_row = cols / (kLanes * 8);
@@ -109,7 +111,7 @@ hipError_t launch(const uint16_t* h, const float* w, int64_t rows, int64_t cols,
     hipLaunchKernelGGL((swiglu_kernel<kLanes, kWeighted, kFmt>), dim3((unsigned)blocks),
                        dim3(kThreads), 0, stream, h + r0 * 2 * cols,
                        kWeighted ? w + r0 : nullptr, nchunks, (uint32_t)cpr, magic, cols, floor,
-                       q + r0 * cols, sf + r0 * groups_per_row);
+                       q + r0 * cols, sf, lay, (uint32_t)(r0 * groups_per_row));
     const hipError_t err = hipGetLastError();
     if (err != hipSuccess) return err;
   }
@@ -118,19 +120,20 @@ hipError_t launch(const uint16_t* h, const float* w, int64_t rows, int64_t cols,
 
 template <int kLanes, int kFmt>
 hipError_t launch_w(const uint16_t* h, const float* w, int64_t rows, int64_t cols, float floor,
-                    uint8_t* q, float* sf, hipStream_t stream, const LaunchCaps& caps) {
-  return w ? launch<kLanes, true, kFmt>(h, w, rows, cols, floor, q, sf, stream, caps)
-           : launch<kLanes, false, kFmt>(h, w, rows, cols, floor, q, sf, stream, caps);
+                    uint8_t* q, void* sf, const SfLayout& lay, hipStream_t stream,
+                    const LaunchCaps& caps) {
+  return w ? launch<kLanes, true, kFmt>(h, w, rows, cols, floor, q, sf, lay, stream, caps)
+           : launch<kLanes, false, kFmt>(h, w, rows, cols, floor, q, sf, lay, stream, caps);
 }
 
 template <int kFmt>
 hipError_t launch_g(const uint16_t* h, const float* w, int64_t rows, int64_t cols, int group,
-                    float floor, uint8_t* q, float* sf, hipStream_t stream,
+                    float floor, uint8_t* q, void* sf, const SfLayout& lay, hipStream_t stream,
                     const LaunchCaps& caps) {
   switch (group) {
-    case 32: return launch_w<4, kFmt>(h, w, rows, cols, floor, q, sf, stream, caps);
-    case 64: return launch_w<8, kFmt>(h, w, rows, cols, floor, q, sf, stream, caps);
-    case 128: return launch_w<16, kFmt>(h, w, rows, cols, floor, q, sf, stream, caps);
+    case 32: return launch_w<4, kFmt>(h, w, rows, cols, floor, q, sf, lay, stream, caps);
+    case 64: return launch_w<8, kFmt>(h, w, rows, cols, floor, q, sf, lay, stream, caps);
+    case 128: return launch_w<16, kFmt>(h, w, rows, cols, floor, q, sf, lay, stream, caps);
   }
   return hipErrorInvalidValue;
 }
@@ -138,14 +141,18 @@ hipError_t launch_g(const uint16_t* h, const float* w, int64_t rows, int64_t col
 }  // namespace
 
 hipError_t launch_swiglu_per_token(const void* h, int64_t rows, int64_t cols, const float* w,
-                                   int fmt, int group, float floor, void* q, float* sf,
-                                   hipStream_t stream, const LaunchCaps& caps) {
+                                   int fmt, int group, float floor, uint32_t sf_flags, void* q,
+                                   void* sf, hipStream_t stream, const LaunchCaps& caps) {
   if (rows == 0 || cols == 0) return hipSuccess;
   if (cols / 8 >= kMaxChunksPerRow) return hipErrorInvalidValue;
+  if (rows * cols / group >= (int64_t(1) << 31)) return hipErrorInvalidValue;
+  const SfLayout lay = make_sf_layout(rows, cols, group, sf_flags);
   const uint16_t* hp = static_cast<const uint16_t*>(h);
   uint8_t* qp = static_cast<uint8_t*>(q);
-  if (fmt == kE4M3) return launch_g<kE4M3>(hp, w, rows, cols, group, floor, qp, sf, stream, caps);
-  if (fmt == kE5M2) return launch_g<kE5M2>(hp, w, rows, cols, group, floor, qp, sf, stream, caps);
+  if (fmt == kE4M3)
+    return launch_g<kE4M3>(hp, w, rows, cols, group, floor, qp, sf, lay, stream, caps);
+  if (fmt == kE5M2)
+    return launch_g<kE5M2>(hp, w, rows, cols, group, floor, qp, sf, lay, stream, caps);
   return hipErrorInvalidValue;
 }
 

@@ -148,6 +148,18 @@ def test_bench_copy_validation(lib):
     assert lib.qcast_bench_copy(None, None, 0, None) == OK
 
 
+def test_sf_layout_validation(lib):
+    f = lib.qcast_per_token_sf
+    assert f(A16, 4, 512, E4M3, 128, 0.0, 8, A16, A16, None) == ERR_FORMAT      # unknown flag
+    assert f(A16, 4, 384, E4M3, 128, 0.0, 4, A16, A16, None) == ERR_SHAPE      # 3 groups, packed
+    assert f(A16, 4, 512, E4M3, 128, 0.0, 7, None, A16, None) == ERR_NULL
+    assert f(A16, 4, 512, E2M1, 32, 0.0, 6, A16, A16 + 2, None) == ERR_ALIGN
+    g = lib.qcast_swiglu_per_token_sf
+    assert g(A16, 4, 512, None, E4M3, 128, 0.0, 16, A16, A16, None) == ERR_FORMAT
+    assert g(A16, 4, 384, None, E4M3, 128, 0.0, 4, A16, A16, None) == ERR_SHAPE
+    assert g(A16, 4, 512, None, E2M1, 32, 0.0, 4, A16, A16, None) == ERR_FORMAT
+
+
 def test_cast_back_validation(lib):
     f = lib.qcast_cast_back
     assert f(A16, A16, 4, 256, 4, 128, 1, A16, None) == ERR_FORMAT

@@ -502,3 +502,62 @@ def test_cast_back_round_trip_full_size(dev):
     torch.cuda.synchronize()
     ref = oracle.cast_back(codes_np(q), sf.cpu().numpy(), 7168, "e4m3", 128, "bf16")
     assert np.array_equal(out.cpu().view(torch.int16).numpy().view(np.uint16), ref)
+
+
+
+# ------------------------------------------------------------ scale-factor layouts
+
+SF_FLAG_SETS = [0, pq.SF_ROUND_POW2, pq.SF_COL_MAJOR, pq.SF_ROUND_POW2 | pq.SF_COL_MAJOR,
+                pq.SF_PACKED_UE8M0, pq.SF_PACKED_UE8M0 | pq.SF_COL_MAJOR]
+
+
+def gpu_sf_cast(x, dev, fmt, group, flags, swiglu_w=None, swiglu=False, poison=0x5A):
+    rows = x.shape[0]
+    cols = x.shape[1] // 2 if swiglu else x.shape[1]
+    shape, dt = pq.sf_layout_shape(rows, cols, group, flags)
+    sf = torch.empty(shape, dtype=dt, device=dev)
+    sf.view(torch.uint8).fill_(poison)
+    if swiglu:
+        q, _ = pq.qcast_swiglu_per_token_sf(x.to(dev), None if swiglu_w is None else swiglu_w.to(dev),
+                                            fmt, group, sf_flags=flags, out_sf=sf)
+    else:
+        q, _ = pq.qcast_per_token_sf(x.to(dev), fmt, group, sf_flags=flags, out_sf=sf)
+    torch.cuda.synchronize()
+    return codes_np(q), sf.cpu().numpy().view(np.uint32)
+
+
+@pytest.mark.parametrize("flags", SF_FLAG_SETS)
+@pytest.mark.parametrize("fmt,group,rows,cols", [("e4m3", 128, 127, 7168), ("e4m3", 64, 6, 1024),
+                                                 ("e2m1", 32, 33, 1024), ("e5m2", 128, 5, 512)])
+def test_per_token_sf_layouts(dev, flags, fmt, group, rows, cols):
+    g = torch.Generator().manual_seed(rows + cols + flags)
+    x = (torch.randn(rows, cols, generator=g) * torch.exp(torch.randn(rows, 1, generator=g) * 6))
+    x[0, :group] = 0.0
+    x = x.to(torch.bfloat16)
+    q_ref, sf_ref = oracle.per_token_sf(workloads.bf16_bits(x), fmt, group, sf_flags=flags,
+                                        sf_fill=0x5A5A5A5A if flags & pq.SF_PACKED_UE8M0 else
+                                        np.array([0x5A5A5A5A], np.uint32).view(np.float32)[0])
+    q, sf = gpu_sf_cast(x, dev, fmt, group, flags)
+    assert np.array_equal(q, q_ref)
+    assert np.array_equal(sf, sf_ref.view(np.uint32))      # padding still poisoned
+
+
+def test_per_token_sf_full_size_packed(dev):
+    wl = workloads.per_token_hidden()
+    flags = pq.SF_PACKED_UE8M0 | pq.SF_COL_MAJOR
+    q_ref, sf_ref = oracle.per_token_sf(workloads.bf16_bits(wl.x), "e4m3", 128, sf_flags=flags)
+    q, sf = gpu_sf_cast(wl.x, dev, "e4m3", 128, flags, poison=0)
+    assert np.array_equal(q, q_ref) and np.array_equal(sf, sf_ref)
+
+
+@pytest.mark.parametrize("flags", [pq.SF_ROUND_POW2 | pq.SF_COL_MAJOR,
+                                   pq.SF_PACKED_UE8M0 | pq.SF_COL_MAJOR, pq.SF_PACKED_UE8M0])
+def test_swiglu_sf_layouts(dev, flags):
+    wl = workloads.swiglu_input(seed=50, rows=130, cols=2048)
+    q_ref, sf_ref = oracle.swiglu_per_token_sf(workloads.bf16_bits(wl.x), wl.w.numpy(),
+                                               sf_flags=flags)
+    q, sf = gpu_sf_cast(wl.x, dev, "e4m3", 128, flags, swiglu_w=wl.w, swiglu=True, poison=0)
+    # power-of-two scales: equal unless v's abs-max straddles a power of two
+    # by an ulp; codes within the SwiGLU tolerance
+    assert (sf != sf_ref.view(np.uint32)).mean() <= 1e-3
+    assert (q != q_ref).mean() <= 1e-3
