@@ -67,6 +67,14 @@ def _load():
         "oracle_f32_to_bf16": ([f32], ctypes.c_uint16),
         "oracle_per_token_sf": ([vp, i64, i64, i32, i32, f32, i32, vp, vp], i32),
         "oracle_swiglu_per_token_sf": ([vp, i64, i64, vp, i32, i32, f32, i32, vp, vp], i32),
+        "oracle_swiglu_values_ex": ([vp, i64, i64, vp, f32, vp, vp], i32),
+        "oracle_swiglu_per_token_ex": ([vp, i64, i64, vp, i32, i32, f32, i32, f32, vp, vp, vp],
+                                       i32),
+        "oracle_swiglu_backward_values": ([vp, vp, i64, i64, vp, f32, vp], i32),
+        "oracle_swiglu_backward_per_token": ([vp, vp, i64, i64, vp, i32, i32, f32, f32, vp, vp],
+                                             i32),
+        "oracle_swiglu_per_channel_T": ([vp, i64, i64, vp, i32, i32, f32, f32, vp, vp], i32),
+        "oracle_per_channel": ([vp, i64, i64, i32, i32, f32, vp, vp], i32),
     }
     for name, (args, res) in sig.items():
         fn = getattr(lib, name)
@@ -269,4 +277,91 @@ def swiglu_per_token_sf(h, w=None, fmt="e4m3", group=128, clamp_min=0.0, sf_flag
     sf = np.full(shape, sf_fill, dt)
     _check(_load().oracle_swiglu_per_token_sf(_ptr(h), rows, cols, _ptr(w), f, group, clamp_min,
                                               sf_flags, _ptr(q), _ptr(sf)), "swiglu_per_token_sf")
+    return q, sf
+
+
+def swiglu_values_ex(h, w=None, swiglu_clamp=0.0):
+    """SwiGLU values with the clamp; returns (v, number of clamped values)."""
+    h = _u16(h)
+    rows, two_n = h.shape
+    cols = two_n // 2
+    w = None if w is None else _f32(w)
+    v = np.zeros((rows, cols), np.float32)
+    count = np.zeros(1, np.uint64)
+    _check(_load().oracle_swiglu_values_ex(_ptr(h), rows, cols, _ptr(w), swiglu_clamp, _ptr(v),
+                                           _ptr(count)), "swiglu_values_ex")
+    return v, int(count[0])
+
+
+def swiglu_per_token_ex(h, w=None, fmt="e4m3", group=128, clamp_min=0.0, sf_flags=0,
+                        swiglu_clamp=0.0, sf_fill=0):
+    """Clamped SwiGLU + per-token cast; returns (q, sf, clamp count)."""
+    f = fmt_id(fmt)
+    h = _u16(h)
+    rows, two_n = h.shape
+    cols = two_n // 2
+    w = None if w is None else _f32(w)
+    q = np.zeros(_code_shape(f, rows, cols), np.uint8)
+    shape, dt = sf_shape(rows, cols, group, sf_flags)
+    sf = np.full(shape, sf_fill, dt)
+    count = np.zeros(1, np.uint64)
+    _check(_load().oracle_swiglu_per_token_ex(_ptr(h), rows, cols, _ptr(w), f, group, clamp_min,
+                                              sf_flags, swiglu_clamp, _ptr(q), _ptr(sf),
+                                              _ptr(count)), "swiglu_per_token_ex")
+    return q, sf, int(count[0])
+
+
+def swiglu_backward_values(h, dv, w=None, swiglu_clamp=0.0):
+    """[dg | du] fp32 [rows, 2*cols] for the gradient dv [rows, cols] (bf16 bits)."""
+    h = _u16(h)
+    dv = _u16(dv)
+    rows, two_n = h.shape
+    cols = two_n // 2
+    w = None if w is None else _f32(w)
+    out = np.zeros((rows, two_n), np.float32)
+    _check(_load().oracle_swiglu_backward_values(_ptr(h), _ptr(dv), rows, cols, _ptr(w),
+                                                 swiglu_clamp, _ptr(out)),
+           "swiglu_backward_values")
+    return out
+
+
+def swiglu_backward_per_token(h, dv, w=None, fmt="e4m3", group=128, clamp_min=0.0,
+                              swiglu_clamp=0.0):
+    f = fmt_id(fmt)
+    h = _u16(h)
+    dv = _u16(dv)
+    rows, two_n = h.shape
+    cols = two_n // 2
+    w = None if w is None else _f32(w)
+    q = np.zeros((rows, two_n), np.uint8)
+    sf = np.zeros((rows, two_n // group if group > 0 else 0), np.float32)
+    _check(_load().oracle_swiglu_backward_per_token(_ptr(h), _ptr(dv), rows, cols, _ptr(w), f,
+                                                    group, clamp_min, swiglu_clamp, _ptr(q),
+                                                    _ptr(sf)), "swiglu_backward_per_token")
+    return q, sf
+
+
+def swiglu_per_channel_T(h, w=None, fmt="e4m3", group=128, clamp_min=0.0, swiglu_clamp=0.0):
+    f = fmt_id(fmt)
+    h = _u16(h)
+    rows, two_n = h.shape
+    cols = two_n // 2
+    w = None if w is None else _f32(w)
+    qT = np.zeros(_code_shape(f, cols, rows), np.uint8)
+    sf = np.zeros((cols, rows // group if group > 0 else 0), np.float32)
+    _check(_load().oracle_swiglu_per_channel_T(_ptr(h), rows, cols, _ptr(w), f, group, clamp_min,
+                                               swiglu_clamp, _ptr(qT), _ptr(sf)),
+           "swiglu_per_channel_T")
+    return qT, sf
+
+
+def per_channel(x, fmt="e4m3", group=128, clamp_min=0.0):
+    """Per-channel cast in the input layout: q [rows, cols], sf [rows/group, cols]."""
+    f = fmt_id(fmt)
+    x = _u16(x)
+    rows, cols = x.shape
+    q = np.zeros(_code_shape(f, rows, cols), np.uint8)
+    sf = np.zeros((rows // group if group > 0 else 0, cols), np.float32)
+    _check(_load().oracle_per_channel(_ptr(x), rows, cols, f, group, clamp_min, _ptr(q), _ptr(sf)),
+           "per_channel")
     return q, sf

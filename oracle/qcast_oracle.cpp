@@ -39,6 +39,13 @@
  *  - round_sf ([WALK] §3.1) rounds sf UP to a power of two, so that no value
  *    saturates ([SPLIT] §一 says the quant ops take exponents with bit
  *    operations); a scale below 2^-126 becomes 2^-126;
+ *  - the SwiGLU clamp counter counts every gate value and every up value the
+ *    clamp changes; the backward of SwiGLU (named in [SPLIT] §二 and §六 step
+ *    13, not written out on the pages) is the derivative of the forward, with
+ *    zero gradient where a value was clamped; the fused SwiGLU + cast +
+ *    transpose ([NEWS] item 2) is the per-channel cast of the SwiGLU values
+ *    written transposed; per_channel_cast without transpose keeps the input
+ *    layout and stores sf[group][channel];
  *  - the layouts of [SPLIT] §四 C: "TMA-aligned column-major" stores the
  *    scales group-major with the row count padded to a multiple of 4 (16
  *    bytes of fp32 or of packed words); "packed UE8M0" stores each (power of
@@ -340,6 +347,50 @@ void per_token_row_sf(const float* xr, int64_t r, int64_t rows, int64_t cols, in
   }
 }
 
+/* Per-channel cast of an fp32 matrix x [rows, cols]: groups of `group`
+ * tokens of one channel. transposed: code of x[t][c] at q[c][t], scale at
+ * sf[c][g]; otherwise at q[t][c] and sf[g][c]. */
+void per_channel_f32(const float* x, int64_t rows, int64_t cols, int fmt, int group, float floor,
+                     bool transposed, uint8_t* q, float* sf) {
+  const FormatTable& t = *table_for(fmt);
+  const int64_t groups = rows / group;
+  for (int64_t c = 0; c < cols; ++c) {
+    for (int64_t g = 0; g < groups; ++g) {
+      float amax = 0.0f;
+      for (int64_t tk = g * group; tk < (g + 1) * group; ++tk) {
+        const float m = std::fabs(x[tk * cols + c]);
+        if (m > amax) amax = m;
+      }
+      const Scale s = scale_from_amax(t, amax, floor);
+      for (int64_t tk = g * group; tk < (g + 1) * group; ++tk) {
+        const uint8_t code = encode(t, x[tk * cols + c] * s.sf_inv);
+        if (transposed) put_code(fmt, q, rows, c, tk, code);
+        else put_code(fmt, q, cols, tk, c, code);
+      }
+      if (transposed) sf[c * groups + g] = s.sf;
+      else sf[g * cols + c] = s.sf;
+    }
+  }
+}
+
+/* SwiGLU of one row with the clamp of [WALK] §3.3. */
+void swiglu_row(const uint16_t* hr, int64_t cols, float wr, bool weighted, float clamp,
+                float* v, uint64_t* count) {
+  for (int64_t j = 0; j < cols; ++j) {
+    float g = bf16_value(hr[j]);
+    float u = bf16_value(hr[cols + j]);
+    if (clamp > 0.0f) {
+      if (g > clamp) { g = clamp; if (count) ++*count; }
+      if (u > clamp) { u = clamp; if (count) ++*count; }
+      else if (u < -clamp) { u = -clamp; if (count) ++*count; }
+    }
+    const float silu = g / (1.0f + std::exp(-g));
+    float val = silu * u;
+    if (weighted) val = val * wr;
+    v[j] = val;
+  }
+}
+
 int check_sf_flags(int flags, int64_t cols, int group) {
   if (flags & ~(ORACLE_SF_ROUND_POW2 | ORACLE_SF_COL_MAJOR | ORACLE_SF_PACKED_UE8M0))
     return ORACLE_ERR_FORMAT;
@@ -429,23 +480,20 @@ int oracle_per_token(const uint16_t* x, int64_t rows, int64_t cols, int fmt, int
 
 int oracle_swiglu_values(const uint16_t* h, int64_t rows, int64_t cols, const float* w,
                          float* v) {
+  return oracle_swiglu_values_ex(h, rows, cols, w, 0.0f, v, nullptr);
+}
+
+int oracle_swiglu_values_ex(const uint16_t* h, int64_t rows, int64_t cols, const float* w,
+                            float swiglu_clamp, float* v, uint64_t* count) {
   if (!h || !v) return ORACLE_ERR_NULL;
   if (rows < 0 || cols < 0) return ORACLE_ERR_SHAPE;
   if (!fp_env_ok()) return ORACLE_ERR_FPENV;
   /* [WALK] §3.3: the left half is the SiLU input, the right half multiplies
    * it; SiLU is written g / (1 + exp(-g)); the routing weight multiplies last.
    * All in fp32. */
-  for (int64_t r = 0; r < rows; ++r) {
-    const uint16_t* hr = h + r * 2 * cols;
-    for (int64_t j = 0; j < cols; ++j) {
-      const float g = bf16_value(hr[j]);
-      const float u = bf16_value(hr[cols + j]);
-      const float silu = g / (1.0f + std::exp(-g));
-      float val = silu * u;
-      if (w) val = val * w[r];
-      v[r * cols + j] = val;
-    }
-  }
+  for (int64_t r = 0; r < rows; ++r)
+    swiglu_row(h + r * 2 * cols, cols, w ? w[r] : 1.0f, w != nullptr, swiglu_clamp,
+               v + r * cols, count);
   return ORACLE_OK;
 }
 
@@ -501,25 +549,23 @@ int oracle_per_channel_T(const uint16_t* x, int64_t rows, int64_t cols, int fmt,
   if (rc != ORACLE_OK) return rc;
   if (rows < 0 || cols < 0 || rows % group != 0) return ORACLE_ERR_SHAPE;
   if (fmt == ORACLE_FMT_E2M1 && group % 2 != 0) return ORACLE_ERR_GROUP;
-  const FormatTable& t = *table_for(fmt);
-  const float floor = floor_for(t, clamp_min);
-  const int64_t groups = rows / group;
-  /* Output row c of qT is channel c; its columns are the tokens. */
-  for (int64_t c = 0; c < cols; ++c) {
-    for (int64_t g = 0; g < groups; ++g) {
-      float amax = 0.0f;
-      for (int64_t tk = g * group; tk < (g + 1) * group; ++tk) {
-        const float m = std::fabs(bf16_value(x[tk * cols + c]));
-        if (m > amax) amax = m;
-      }
-      const Scale s = scale_from_amax(t, amax, floor);
-      for (int64_t tk = g * group; tk < (g + 1) * group; ++tk) {
-        const float y = bf16_value(x[tk * cols + c]) * s.sf_inv;
-        put_code(fmt, qT, rows, c, tk, encode(t, y));
-      }
-      sf[c * groups + g] = s.sf;
-    }
-  }
+  std::vector<float> xf(static_cast<size_t>(rows * cols));
+  for (int64_t i = 0; i < rows * cols; ++i) xf[i] = bf16_value(x[i]);
+  per_channel_f32(xf.data(), rows, cols, fmt, group, floor_for(*table_for(fmt), clamp_min), true,
+                  qT, sf);
+  return ORACLE_OK;
+}
+
+int oracle_per_channel(const uint16_t* x, int64_t rows, int64_t cols, int fmt, int group,
+                       float clamp_min, uint8_t* q, float* sf) {
+  const int rc = check_common(x, q, sf, fmt, group);
+  if (rc != ORACLE_OK) return rc;
+  if (rows < 0 || cols < 0 || rows % group != 0) return ORACLE_ERR_SHAPE;
+  if (fmt == ORACLE_FMT_E2M1 && cols % 2 != 0) return ORACLE_ERR_SHAPE;
+  std::vector<float> xf(static_cast<size_t>(rows * cols));
+  for (int64_t i = 0; i < rows * cols; ++i) xf[i] = bf16_value(x[i]);
+  per_channel_f32(xf.data(), rows, cols, fmt, group, floor_for(*table_for(fmt), clamp_min), false,
+                  q, sf);
   return ORACLE_OK;
 }
 
@@ -568,6 +614,85 @@ int oracle_swiglu_per_token_sf(const uint16_t* h, int64_t rows, int64_t cols, co
     oracle_swiglu_values(h + r * 2 * cols, 1, cols, w ? w + r : nullptr, v.data());
     per_token_row_sf(v.data(), r, rows, cols, fmt, group, floor, sf_flags, q + r * code_bytes, sf);
   }
+  return ORACLE_OK;
+}
+
+int oracle_swiglu_per_token_ex(const uint16_t* h, int64_t rows, int64_t cols, const float* w,
+                               int fmt, int group, float clamp_min, int sf_flags,
+                               float swiglu_clamp, uint8_t* q, void* sf, uint64_t* count) {
+  int rc = check_common(h, q, sf, fmt, group);
+  if (rc != ORACLE_OK) return rc;
+  if (rows < 0 || cols < 0 || cols % group != 0) return ORACLE_ERR_SHAPE;
+  if (fmt == ORACLE_FMT_E2M1 && group % 2 != 0) return ORACLE_ERR_GROUP;
+  if ((rc = check_sf_flags(sf_flags, cols, group)) != ORACLE_OK) return rc;
+  const float floor = floor_for(*table_for(fmt), clamp_min);
+  const int64_t code_bytes = (fmt == ORACLE_FMT_E2M1) ? cols / 2 : cols;
+  std::vector<float> v(static_cast<size_t>(cols));
+  for (int64_t r = 0; r < rows; ++r) {
+    swiglu_row(h + r * 2 * cols, cols, w ? w[r] : 1.0f, w != nullptr, swiglu_clamp, v.data(),
+               count);
+    per_token_row_sf(v.data(), r, rows, cols, fmt, group, floor, sf_flags, q + r * code_bytes, sf);
+  }
+  return ORACLE_OK;
+}
+
+int oracle_swiglu_backward_values(const uint16_t* h, const uint16_t* dv, int64_t rows,
+                                  int64_t cols, const float* w, float swiglu_clamp, float* out) {
+  if (!h || !dv || !out) return ORACLE_ERR_NULL;
+  if (rows < 0 || cols < 0) return ORACLE_ERR_SHAPE;
+  if (!fp_env_ok()) return ORACLE_ERR_FPENV;
+  for (int64_t r = 0; r < rows; ++r) {
+    const uint16_t* hr = h + r * 2 * cols;
+    float* o = out + r * 2 * cols;
+    for (int64_t j = 0; j < cols; ++j) {
+      float g = bf16_value(hr[j]);
+      float u = bf16_value(hr[cols + j]);
+      bool g_pass = true, u_pass = true;
+      if (swiglu_clamp > 0.0f) {
+        if (g > swiglu_clamp) { g = swiglu_clamp; g_pass = false; }
+        if (u > swiglu_clamp) { u = swiglu_clamp; u_pass = false; }
+        else if (u < -swiglu_clamp) { u = -swiglu_clamp; u_pass = false; }
+      }
+      const float e = std::exp(-g);
+      const float s = 1.0f / (1.0f + e);
+      const float silu = g * s;
+      const float dsilu = s + silu * (1.0f - s);
+      float dvw = bf16_value(dv[r * cols + j]);
+      if (w) dvw = dvw * w[r];
+      o[j] = g_pass ? dvw * u * dsilu : 0.0f;
+      o[cols + j] = u_pass ? dvw * silu : 0.0f;
+    }
+  }
+  return ORACLE_OK;
+}
+
+int oracle_swiglu_backward_per_token(const uint16_t* h, const uint16_t* dv, int64_t rows,
+                                     int64_t cols, const float* w, int fmt, int group,
+                                     float clamp_min, float swiglu_clamp, uint8_t* q,
+                                     float* sf) {
+  const int rc = check_common(h, q, sf, fmt, group);
+  if (rc != ORACLE_OK) return rc;
+  if (!dv) return ORACLE_ERR_NULL;
+  if (rows < 0 || cols < 0 || cols % group != 0) return ORACLE_ERR_SHAPE;
+  if (fmt == ORACLE_FMT_E2M1) return ORACLE_ERR_FORMAT;
+  std::vector<float> vals(static_cast<size_t>(rows * 2 * cols));
+  oracle_swiglu_backward_values(h, dv, rows, cols, w, swiglu_clamp, vals.data());
+  per_token_rows(vals.data(), rows, 2 * cols, fmt, group, floor_for(*table_for(fmt), clamp_min),
+                 q, sf);
+  return ORACLE_OK;
+}
+
+int oracle_swiglu_per_channel_T(const uint16_t* h, int64_t rows, int64_t cols, const float* w,
+                                int fmt, int group, float clamp_min, float swiglu_clamp,
+                                uint8_t* qT, float* sf) {
+  const int rc = check_common(h, qT, sf, fmt, group);
+  if (rc != ORACLE_OK) return rc;
+  if (rows < 0 || cols < 0 || rows % group != 0) return ORACLE_ERR_SHAPE;
+  if (fmt == ORACLE_FMT_E2M1 && group % 2 != 0) return ORACLE_ERR_GROUP;
+  std::vector<float> v(static_cast<size_t>(rows * cols));
+  oracle_swiglu_values_ex(h, rows, cols, w, swiglu_clamp, v.data(), nullptr);
+  per_channel_f32(v.data(), rows, cols, fmt, group, floor_for(*table_for(fmt), clamp_min), true,
+                  qT, sf);
   return ORACLE_OK;
 }
 

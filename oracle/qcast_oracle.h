@@ -112,6 +112,46 @@ int oracle_swiglu_per_token_sf(const uint16_t* h, int64_t rows, int64_t cols, co
                                int fmt, int group, float clamp_min, int sf_flags, uint8_t* q,
                                void* sf);
 
+/* ---- SwiGLU variants and per-channel without transpose ---- */
+
+/* SwiGLU values with the optional clamp of the walk-through page §3.3:
+ * g' = min(g, c), u' = min(max(u, -c), c) for swiglu_clamp = c > 0 (no
+ * clamp for c <= 0); *count (if not NULL) is increased by the number of gate
+ * and up values the clamp changed. v [rows, cols]. */
+int oracle_swiglu_values_ex(const uint16_t* h, int64_t rows, int64_t cols, const float* w,
+                            float swiglu_clamp, float* v, uint64_t* count);
+
+/* Forward SwiGLU (with clamp) + per-token cast with a scale layout. */
+int oracle_swiglu_per_token_ex(const uint16_t* h, int64_t rows, int64_t cols, const float* w,
+                               int fmt, int group, float clamp_min, int sf_flags,
+                               float swiglu_clamp, uint8_t* q, void* sf, uint64_t* count);
+
+/* SwiGLU backward values: dv [rows, cols] bf16 is the gradient of v; out
+ * [rows, 2*cols] fp32 = [dg | du] with
+ *   e = exp(-g'), s = 1 / (1 + e), silu = g' * s, dsilu = s + silu * (1 - s),
+ *   dvw = dv * w, dg = dvw * u' * dsilu, du = dvw * silu,
+ * where g', u' are the clamped values, and dg = 0 where g > c, du = 0 where
+ * |u| > c (the clamp's derivative). */
+int oracle_swiglu_backward_values(const uint16_t* h, const uint16_t* dv, int64_t rows,
+                                  int64_t cols, const float* w, float swiglu_clamp, float* out);
+
+/* SwiGLU backward + per-token cast of [dg | du]: q [rows, 2*cols] (E4M3 /
+ * E5M2 bytes), sf [rows, 2*cols/group]. */
+int oracle_swiglu_backward_per_token(const uint16_t* h, const uint16_t* dv, int64_t rows,
+                                     int64_t cols, const float* w, int fmt, int group,
+                                     float clamp_min, float swiglu_clamp, uint8_t* q, float* sf);
+
+/* Forward SwiGLU + per-channel cast written transposed (token groups of
+ * `group`): qT [cols, rows], sf [cols, rows/group]. */
+int oracle_swiglu_per_channel_T(const uint16_t* h, int64_t rows, int64_t cols, const float* w,
+                                int fmt, int group, float clamp_min, float swiglu_clamp,
+                                uint8_t* qT, float* sf);
+
+/* Per-channel cast in the input layout: groups of `group` tokens of one
+ * channel; q [rows, cols], sf [rows/group, cols]. */
+int oracle_per_channel(const uint16_t* x, int64_t rows, int64_t cols, int fmt, int group,
+                       float clamp_min, uint8_t* q, float* sf);
+
 /* fp32 -> bf16 bit pattern, round to nearest even (NaN kept quiet). */
 uint16_t oracle_f32_to_bf16(float f);
 

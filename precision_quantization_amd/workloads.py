@@ -117,6 +117,17 @@ def swiglu_input(seed=3, rows=8192, cols=2048, std=2.0, with_weight=True):
                                      weight="U(0,1) fp32" if with_weight else None))
 
 
+def swiglu_grad(seed=7, rows=8192, cols=2048, std=2.0, grad_std=1.0, with_weight=True):
+    """Inputs of the SwiGLU backward: H = [gate | up] N(0, std) and the
+    gradient dV [rows, cols] N(0, grad_std), both bf16; w ~ U(0, 1) fp32 or
+    None. Returns (h, dv, w)."""
+    g = _gen(seed)
+    h = torch.randn(rows, 2 * cols, generator=g, dtype=torch.float32) * std
+    dv = torch.randn(rows, cols, generator=g, dtype=torch.float32) * grad_std
+    w = torch.rand(rows, generator=g, dtype=torch.float32) if with_weight else None
+    return h.to(torch.bfloat16), dv.to(torch.bfloat16), w
+
+
 def weight_block(seed=4, rows=7168, cols=18432, std=0.02):
     """W ~ N(0, std), cast with one scale per 128 x 128 block."""
     g = _gen(seed)
