@@ -13,6 +13,8 @@
  *           per_block_cast, per_channel_cast (+transpose),
  *           swiglu_forward_and_per_token_cast), §四 A (E4M3 / E2M1 formats),
  *           §六 (where the casts sit in a MoE layer).
+ *   [NEWS]  "刚刚！DeepSeek开源高性能GPU算子库TileKernels" (info.datadowell.com):
+ *           item 2 (the quant/ module; SwiGLU fused with cast and transpose).
  *
  * What every cast computes, per scale group of elements x_i:
  *     amax   = max_i |x_i|
@@ -53,7 +55,7 @@
 extern "C" {
 #endif
 
-#define QCAST_ABI_VERSION 1
+#define QCAST_ABI_VERSION 2
 
 #ifndef QCAST_API
 #define QCAST_API __attribute__((visibility("default")))
@@ -67,7 +69,8 @@ typedef enum {
   QCAST_ERR_FORMAT = 4, /* format not supported by this entry point */
   QCAST_ERR_GROUP = 5,  /* group / block size not supported */
   QCAST_ERR_LAUNCH = 6, /* the kernel launch failed */
-  QCAST_ERR_DEVICE = 7  /* no usable HIP device */
+  QCAST_ERR_DEVICE = 7, /* no usable HIP device */
+  QCAST_ERR_VALUE = 8   /* a scalar argument is out of range (e.g. a NaN clamp) */
 } qcast_status;
 
 typedef enum { QCAST_FMT_E4M3 = 1, QCAST_FMT_E2M1 = 2, QCAST_FMT_E5M2 = 3 } qcast_fmt;
@@ -152,6 +155,60 @@ QCAST_API int qcast_swiglu_per_token_sf(const void* h, int64_t rows, int64_t col
                                         void* stream);
 
 /*
+ * SwiGLU forward with the optional clamp of [WALK] §3.3, fused with the
+ * per-token cast and a scale-factor layout.
+ *   swiglu_clamp  c > 0 replaces the gate g by min(g, c) and the up value u
+ *                 by min(max(u, -c), c) before the product; c <= 0 (or
+ *                 +inf) clamps nothing. NaN is rejected (QCAST_ERR_VALUE).
+ *   clamp_count   NULL, or a device uint64 (8-byte aligned) to which the
+ *                 number of gate and up values the clamp changed is ADDED
+ *                 (atomically; the caller zeroes it, or lets it accumulate
+ *                 over calls). Untouched when c <= 0.
+ *   Everything else as qcast_swiglu_per_token_sf.
+ */
+QCAST_API int qcast_swiglu_per_token_ex(const void* h, int64_t rows, int64_t cols,
+                                        const float* row_weight, int fmt, int group,
+                                        float clamp_min, int sf_flags, float swiglu_clamp,
+                                        void* q, void* sf, uint64_t* clamp_count, void* stream);
+
+/*
+ * SwiGLU backward fused with the per-token cast of the input gradient
+ * ([SPLIT] §二 swiglu_backward_and_per_token_cast; §六 step 13). The pages
+ * name the operation; the derivative is that of the forward of [WALK] §3.3:
+ * with g, u the (clamped) gate and up values of h and dv the gradient of v,
+ *   s = 1 / (1 + exp(-g)), silu = g * s, dsilu = s + silu * (1 - s),
+ *   dg = (dv * w) * u * dsilu,  du = (dv * w) * silu        (fp32)
+ * and dg = 0 where g > c, du = 0 where |u| > c when swiglu_clamp c > 0.
+ *   h   [rows, 2*cols] bf16 (gate | up); dv [rows, cols] bf16;
+ *   row_weight [rows] fp32 or NULL.
+ *   q   [rows, 2*cols] bytes: the codes of the row [dg | du].
+ *   sf  [rows, 2*cols/group] fp32 (the dg groups, then the du groups).
+ *   fmt QCAST_FMT_E4M3 or QCAST_FMT_E5M2; group 32, 64 or 128;
+ *   cols % group == 0. The exponential and reciprocal are the hardware's fast
+ *   forms (codes may differ by one step next to a rounding midpoint).
+ */
+QCAST_API int qcast_swiglu_backward_per_token(const void* h, const void* dv, int64_t rows,
+                                              int64_t cols, const float* row_weight, int fmt,
+                                              int group, float clamp_min, float swiglu_clamp,
+                                              void* q, float* sf, void* stream);
+
+/*
+ * SwiGLU forward fused with the per-channel cast and the transpose ([NEWS]
+ * item 2; the SwiGLU of [WALK] §3.3, the transposed per-channel layout of
+ * qcast_per_channel_T).
+ *   h   [rows, 2*cols] bf16 (gate | up), rows = tokens; row_weight as above.
+ *   v   = SwiGLU values [rows, cols] (clamped as in qcast_swiglu_per_token_ex)
+ *   qT  [cols, rows] bytes: qT[c][t] is the code of v[t][c].
+ *   sf  [cols, rows/group] fp32, groups of `group` tokens of one channel.
+ *   group must be 128; rows % group == 0; cols % 8 == 0;
+ *   fmt QCAST_FMT_E4M3 or QCAST_FMT_E5M2; clamp_count as above.
+ */
+QCAST_API int qcast_swiglu_per_channel_T(const void* h, int64_t rows, int64_t cols,
+                                         const float* row_weight, int fmt, int group,
+                                         float clamp_min, float swiglu_clamp, void* qT, float* sf,
+                                         uint64_t* clamp_count, void* stream);
+
+/*
  * Per-block cast of a weight ([SPLIT] §二 per_block_cast; [NEWS]
  * "刚刚！DeepSeek开源高性能GPU算子库TileKernels", item 2, per-block granularity).
  * One scale per block x block tile.
@@ -176,6 +233,19 @@ QCAST_API int qcast_per_block(const void* x, int64_t rows, int64_t cols, int fmt
  */
 QCAST_API int qcast_per_channel_T(const void* x, int64_t rows, int64_t cols, int fmt, int group,
                         float clamp_min, void* qT, float* sf, void* stream);
+
+/*
+ * Per-channel cast in the input layout ([SPLIT] §二 per_channel_cast without
+ * the transpose).
+ *   x   [rows, cols] bf16, rows = tokens, cols = channels.
+ *   q   [rows, cols] bytes: q[t][c] is the code of x[t][c].
+ *   sf  [rows/group, cols] fp32: sf[g][c] is the scale of tokens
+ *       g*group .. g*group + group - 1 of channel c.
+ *   group must be 128; rows % group == 0; cols % 8 == 0;
+ *   fmt QCAST_FMT_E4M3 or QCAST_FMT_E5M2.
+ */
+QCAST_API int qcast_per_channel(const void* x, int64_t rows, int64_t cols, int fmt, int group,
+                                float clamp_min, void* q, float* sf, void* stream);
 
 /*
  * cast_back: dequantize per-token codes ([SPLIT] §二 cast_back).

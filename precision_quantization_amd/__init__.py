@@ -21,7 +21,9 @@ from ._lib import (FMT_E2M1, FMT_E4M3, FMT_E5M2, OUT_BF16, OUT_F32, SF_COL_MAJOR
 
 __all__ = ["qcast_per_token", "qcast_e2m1", "qcast_swiglu_per_token", "qcast_per_block",
            "qcast_per_channel_T", "qcast_cast_back", "qcast_per_token_sf",
-           "qcast_swiglu_per_token_sf", "sf_layout_shape", "SF_ROUND_POW2", "SF_COL_MAJOR",
+           "qcast_swiglu_per_token_sf", "qcast_swiglu_per_token_ex",
+           "qcast_swiglu_backward_per_token", "qcast_swiglu_per_channel_T", "qcast_per_channel",
+           "sf_layout_shape", "SF_ROUND_POW2", "SF_COL_MAJOR",
            "SF_PACKED_UE8M0", "qcast_abi_version", "qcast_set_num_cus", "qcast_bench_copy",
            "qcast_bench_check_scale",
            "per_token_cast",
@@ -52,6 +54,26 @@ def _stream(device, stream):
     if stream is not None:
         return stream.cuda_stream if hasattr(stream, "cuda_stream") else int(stream)
     return torch.cuda.current_stream(device).cuda_stream
+
+
+def _row_weight(row_weight, rows, device):
+    if row_weight is None:
+        return None
+    if not isinstance(row_weight, torch.Tensor) or row_weight.dtype != torch.float32 or \
+            tuple(row_weight.shape) != (rows,) or row_weight.device != device or \
+            not row_weight.is_contiguous():
+        raise QcastError(2, "row_weight must be a contiguous float32 [rows] tensor on h's device")
+    return row_weight.data_ptr()
+
+
+def _counter(clamp_count, device):
+    """Device int64 [1] tensor the clamp count is added to (or None)."""
+    if clamp_count is None:
+        return None
+    if not isinstance(clamp_count, torch.Tensor) or clamp_count.dtype != torch.int64 or \
+            clamp_count.numel() != 1 or clamp_count.device != device:
+        raise QcastError(2, "clamp_count must be a one-element int64 tensor on h's device")
+    return clamp_count.data_ptr()
 
 
 def _code_dtype(f):
@@ -125,6 +147,95 @@ def qcast_swiglu_per_token_sf(h, row_weight=None, fmt="e4m3", group=128, clamp_m
                                                sf_flags, out.data_ptr(), out_sf.data_ptr(),
                                                _stream(h.device, stream)),
               "qcast_swiglu_per_token_sf")
+    return out, out_sf
+
+
+def qcast_swiglu_per_token_ex(h, row_weight=None, fmt="e4m3", group=128, clamp_min=0.0,
+                              sf_flags=0, swiglu_clamp=0.0, clamp_count=None, out=None,
+                              out_sf=None, stream=None):
+    """SwiGLU with the optional clamp (gate <= c, up in [-c, c]) fused with the
+    per-token cast. ``clamp_count``: an int64 [1] device tensor to which the
+    number of clamped values is added, or None."""
+    f = fmt_id(fmt)
+    h = _bf16_input(h, "h")
+    rows, two_n = h.shape
+    cols = two_n // 2
+    wptr = _row_weight(row_weight, rows, h.device)
+    cptr = _counter(clamp_count, h.device)
+    out = _out(out, (rows, cols), _code_dtype(f), h.device, "out")
+    shape, dt = sf_layout_shape(rows, cols, group if group > 0 else 1, sf_flags)
+    out_sf = _out(out_sf, shape, dt, h.device, "out_sf")
+    with torch.cuda.device(h.device):
+        check(load().qcast_swiglu_per_token_ex(h.data_ptr(), rows, cols, wptr, f, group, clamp_min,
+                                               sf_flags, swiglu_clamp, out.data_ptr(),
+                                               out_sf.data_ptr(), cptr,
+                                               _stream(h.device, stream)),
+              "qcast_swiglu_per_token_ex")
+    return out, out_sf
+
+
+def qcast_swiglu_backward_per_token(h, dv, row_weight=None, fmt="e4m3", group=128,
+                                    clamp_min=0.0, swiglu_clamp=0.0, out=None, out_sf=None,
+                                    stream=None):
+    """SwiGLU backward fused with the per-token cast of ``[dgate | dup]``:
+    ``out [rows, 2*cols]``, ``out_sf [rows, 2*cols/group]``."""
+    f = fmt_id(fmt)
+    h = _bf16_input(h, "h")
+    dv = _bf16_input(dv, "dv")
+    rows, two_n = h.shape
+    cols = two_n // 2
+    if tuple(dv.shape) != (rows, cols) or dv.device != h.device:
+        raise QcastError(2, f"dv must be [{rows}, {cols}] on h's device")
+    wptr = _row_weight(row_weight, rows, h.device)
+    out = _out(out, (rows, two_n), _code_dtype(f), h.device, "out")
+    out_sf = _out(out_sf, (rows, two_n // group if group > 0 else 0), torch.float32, h.device,
+                  "out_sf")
+    with torch.cuda.device(h.device):
+        check(load().qcast_swiglu_backward_per_token(h.data_ptr(), dv.data_ptr(), rows, cols,
+                                                     wptr, f, group, clamp_min, swiglu_clamp,
+                                                     out.data_ptr(), out_sf.data_ptr(),
+                                                     _stream(h.device, stream)),
+              "qcast_swiglu_backward_per_token")
+    return out, out_sf
+
+
+def qcast_swiglu_per_channel_T(h, row_weight=None, fmt="e4m3", group=128, clamp_min=0.0,
+                               swiglu_clamp=0.0, clamp_count=None, out=None, out_sf=None,
+                               stream=None):
+    """SwiGLU fused with the per-channel cast written transposed:
+    ``out [cols, rows]``, ``out_sf [cols, rows/group]``."""
+    f = fmt_id(fmt)
+    h = _bf16_input(h, "h")
+    rows, two_n = h.shape
+    cols = two_n // 2
+    wptr = _row_weight(row_weight, rows, h.device)
+    cptr = _counter(clamp_count, h.device)
+    out = _out(out, (cols, rows), _code_dtype(f), h.device, "out")
+    out_sf = _out(out_sf, (cols, rows // group if group > 0 else 0), torch.float32, h.device,
+                  "out_sf")
+    with torch.cuda.device(h.device):
+        check(load().qcast_swiglu_per_channel_T(h.data_ptr(), rows, cols, wptr, f, group,
+                                                clamp_min, swiglu_clamp, out.data_ptr(),
+                                                out_sf.data_ptr(), cptr,
+                                                _stream(h.device, stream)),
+              "qcast_swiglu_per_channel_T")
+    return out, out_sf
+
+
+def qcast_per_channel(x, fmt="e4m3", group=128, clamp_min=0.0, out=None, out_sf=None,
+                      stream=None):
+    """Per-channel cast in the input layout: ``out [tokens, channels]``,
+    ``out_sf [tokens/group, channels]``."""
+    f = fmt_id(fmt)
+    x = _bf16_input(x, "x")
+    rows, cols = x.shape
+    out = _out(out, (rows, cols), _code_dtype(f), x.device, "out")
+    out_sf = _out(out_sf, (rows // group if group > 0 else 0, cols), torch.float32, x.device,
+                  "out_sf")
+    with torch.cuda.device(x.device):
+        check(load().qcast_per_channel(x.data_ptr(), rows, cols, f, group, clamp_min,
+                                       out.data_ptr(), out_sf.data_ptr(),
+                                       _stream(x.device, stream)), "qcast_per_channel")
     return out, out_sf
 
 

@@ -31,6 +31,15 @@
 // and write neighbouring 128-byte pieces of the same qT rows and scale
 // lines (measured about 3% faster than walking token groups of one channel
 // tile, and much faster than walking channel tiles first).
+//
+// The same tile machinery serves SwiGLU fused with the cast and the
+// transpose (the three-way fusion of "刚刚！DeepSeek开源高性能GPU算子库
+// TileKernels", item 2, applied to the SwiGLU of the walk-through page,
+// §3.3): each lane loads the gate and up chunks of its tokens and the row
+// weights, forms
+// v = silu(g) * u * w in fp32 registers (clamped first when asked, counting
+// the changed values), and the tile continues from fp32 values instead of
+// packed bf16.
 #include "qcast_device.h"
 #include "qcast_kernels.h"
 
@@ -110,48 +119,38 @@ __device__ __forceinline__ TileCoord tile_coord(uint32_t tau, uint32_t ngroups, 
   return tc;
 }
 
-// Issue the lane's loads of a tile (zeros outside the tensor).
-__device__ __forceinline__ void load_tile(const uint16_t* __restrict__ x, uint32_t cols,
+// Issue the lane's loads of a tile of a bf16 matrix whose rows are `stride`
+// elements apart (zeros outside the tensor).
+__device__ __forceinline__ void load_tile(const uint16_t* __restrict__ x, uint32_t stride,
                                           const TileCoord& tc, u32x4 (&raw)[kPasses][4]) {
   const int t = threadIdx.x;
   const int ch = t % kCC;
   const int k = t / kCC;
   const bool valid_ch = ch * 8 < tc.nc;
   // 64-bit tile base, 32-bit offsets inside the tile
-  const uint16_t* base = x + (uint64_t)tc.t0 * cols + tc.c0;
+  const uint16_t* base = x + (uint64_t)tc.t0 * stride + tc.c0;
 #pragma unroll
   for (int p = 0; p < kPasses; ++p) {
     const bool valid = valid_ch && (p / kPassesPerGroup) < tc.ng;
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
-      const uint32_t off = (uint32_t)(p * kPassTokens + 4 * k + i) * cols + ch * 8;
+      const uint32_t off = (uint32_t)(p * kPassTokens + 4 * k + i) * stride + ch * 8;
       raw[p][i] = valid ? load_stream(reinterpret_cast<const u32x4*>(base + off))
                         : u32x4{0u, 0u, 0u, 0u};
     }
   }
 }
 
-struct Smem {
-  uint32_t tile[kChannels * kRowDw];
-  float wave_amax[kTG][4][kChannels];
-  float inv_s[kTG][kChannels];
-};
+// A tile's values as packed bf16 (the plain cast): word w of raw[p][i] holds
+// channels 8ch + 2w (low half) and 8ch + 2w + 1 of the lane's token i of
+// pass p.
+struct Bf16Tile {
+  u32x4 raw[kPasses][4];
 
-// Scales, codes and stores of one tile whose values are in raw. Starts and
-// ends with the workgroup converged; the LDS is free again on return.
-template <int kFmt>
-__device__ __forceinline__ void process_tile(const TileCoord& tc, const u32x4 (&raw)[kPasses][4],
-                                             uint32_t rows, uint32_t ngroups, float floor,
-                                             Smem& sm, uint8_t* __restrict__ qT,
-                                             float* __restrict__ sf) {
-  const int t = threadIdx.x;
-  const int ch = t % kCC;
-  const int k = t / kCC;
-  const int wave = t >> 6;
-  // Column abs-maxima per token group, as packed 16-bit magnitudes: word w
-  // of a lane holds channels 8ch + 2w (low half) and 8ch + 2w + 1.
-#pragma unroll
-  for (int gi = 0; gi < kTG; ++gi) {
+  // Abs-maxima of the lane's 8 channels over token group gi, reduced over
+  // the lanes holding the same channel chunk: packed 16-bit maxima of the
+  // magnitude bits (v_pk_max_u16), unpacked at the end.
+  __device__ __forceinline__ void group_amax(int gi, float out[8]) const {
     uint32_t m[4] = {0u, 0u, 0u, 0u};
 #pragma unroll
     for (int pp = 0; pp < kPassesPerGroup; ++pp) {
@@ -169,13 +168,116 @@ __device__ __forceinline__ void process_tile(const TileCoord& tc, const u32x4 (&
       if (kCC == 8) m[w] = pk_umax16(m[w], dpp<kDppRor8>(m[w]));
       m[w] = pk_umax16(m[w], (uint32_t)__shfl_xor((int)m[w], 16));
       m[w] = pk_umax16(m[w], (uint32_t)__shfl_xor((int)m[w], 32));
+      out[2 * w] = bf16_lo(m[w]);
+      out[2 * w + 1] = bf16_hi(m[w]);
     }
+  }
+
+  __device__ __forceinline__ float value(int p, int i, int j) const {
+    const uint32_t word = raw[p][i][j >> 1];
+    return (j & 1) ? bf16_hi(word) : bf16_lo(word);
+  }
+};
+
+// A tile's values as fp32 (the SwiGLU output).
+struct F32Tile {
+  float v[kPasses][4][8];
+
+  __device__ __forceinline__ void group_amax(int gi, float out[8]) const {
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      uint32_t m = 0u;
+#pragma unroll
+      for (int pp = 0; pp < kPassesPerGroup; ++pp) {
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+          m = umax(m, __float_as_uint(v[gi * kPassesPerGroup + pp][i][j]) & 0x7fffffffu);
+      }
+      if (kCC == 8) m = umax(m, dpp<kDppRor8>(m));
+      m = umax(m, (uint32_t)__shfl_xor((int)m, 16));
+      m = umax(m, (uint32_t)__shfl_xor((int)m, 32));
+      out[j] = __uint_as_float(m);
+    }
+  }
+
+  __device__ __forceinline__ float value(int p, int i, int j) const { return v[p][i][j]; }
+};
+
+constexpr float kLog2e = 1.4426950408889634f;
+
+// Load a tile of the SwiGLU input h [rows, 2 * cols] and form
+// v = silu(g) * u (* w[token]); returns the number of values the clamp
+// changed (clamp > 0 only). Tokens and channels outside the tensor give 0.
+template <bool kWeighted, bool kClamp>
+__device__ __forceinline__ uint32_t load_swiglu_tile(const uint16_t* __restrict__ h,
+                                                     const float* __restrict__ w, uint32_t cols,
+                                                     float clamp, const TileCoord& tc,
+                                                     F32Tile& tile) {
+  const int t = threadIdx.x;
+  const int ch = t % kCC;
+  const int k = t / kCC;
+  const bool valid_ch = ch * 8 < tc.nc;
+  u32x4 graw[kPasses][4], uraw[kPasses][4];
+  float wr[kPasses][4];
+  const uint16_t* base = h + (uint64_t)tc.t0 * 2 * cols + tc.c0;
+#pragma unroll
+  for (int p = 0; p < kPasses; ++p) {
+    const bool valid = valid_ch && (p / kPassesPerGroup) < tc.ng;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const uint32_t tok = (uint32_t)(p * kPassTokens + 4 * k + i);
+      const uint32_t off = tok * 2 * cols + ch * 8;
+      const u32x4 z = {0u, 0u, 0u, 0u};
+      graw[p][i] = valid ? load_stream(reinterpret_cast<const u32x4*>(base + off)) : z;
+      uraw[p][i] = valid ? load_stream(reinterpret_cast<const u32x4*>(base + off + cols)) : z;
+      wr[p][i] = (kWeighted && valid) ? w[tc.t0 + tok] : 1.0f;
+    }
+  }
+  uint32_t nclamp = 0;
+#pragma unroll
+  for (int p = 0; p < kPasses; ++p) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      float gv[8], uv[8];
+      unpack8(graw[p][i], gv);
+      unpack8(uraw[p][i], uv);
+#pragma unroll
+      for (int j = 0; j < 8; ++j) {
+        if (kClamp) nclamp += clamp_gate_up(gv[j], uv[j], clamp);
+        const float e = __builtin_amdgcn_exp2f(-gv[j] * kLog2e);
+        float val = gv[j] * __builtin_amdgcn_rcpf(1.0f + e) * uv[j];
+        if (kWeighted) val = val * wr[p][i];
+        tile.v[p][i][j] = val;
+      }
+    }
+  }
+  return nclamp;
+}
+
+struct Smem {
+  uint32_t tile[kChannels * kRowDw];
+  float wave_amax[kTG][4][kChannels];
+  float inv_s[kTG][kChannels];
+};
+
+// Scales, codes and stores of one tile whose values are in raw. Starts and
+// ends with the workgroup converged; the LDS is free again on return.
+template <int kFmt, class Tile>
+__device__ __forceinline__ void process_tile(const TileCoord& tc, const Tile& tile, uint32_t rows,
+                                             uint32_t ngroups, float floor, Smem& sm,
+                                             uint8_t* __restrict__ qT, float* __restrict__ sf) {
+  const int t = threadIdx.x;
+  const int ch = t % kCC;
+  const int k = t / kCC;
+  const int wave = t >> 6;
+  // Column abs-maxima per token group within each wave, then across waves.
+#pragma unroll
+  for (int gi = 0; gi < kTG; ++gi) {
+    float m[8];
+    tile.group_amax(gi, m);
     if ((t & 63) < kCC) {
 #pragma unroll
-      for (int w = 0; w < 4; ++w) {
-        sm.wave_amax[gi][wave][ch * 8 + 2 * w] = bf16_lo(m[w]);
-        sm.wave_amax[gi][wave][ch * 8 + 2 * w + 1] = bf16_hi(m[w]);
-      }
+      for (int j = 0; j < 8; ++j) sm.wave_amax[gi][wave][ch * 8 + j] = m[j];
     }
   }
   __syncthreads();
@@ -201,10 +303,7 @@ __device__ __forceinline__ void process_tile(const TileCoord& tc, const u32x4 (&
       const float inv = sm.inv_s[gi][ch * 8 + j];
       float y[4];
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const uint32_t word = raw[p][i][j >> 1];
-        y[i] = ((j & 1) ? bf16_hi(word) : bf16_lo(word)) * inv;
-      }
+      for (int i = 0; i < 4; ++i) y[i] = tile.value(p, i, j) * inv;
       sm.tile[tile_index(ch * 8 + j, p * (kPassTokens / 4) + k)] =
           fp8x4<kFmt>(y[0], y[1], y[2], y[3]);
     }
@@ -237,9 +336,78 @@ __global__ __launch_bounds__(kThreads) void per_channel_t_kernel(
   const uint32_t tau = (kOrder & 2) ? b : (b % kXcds) * per_xcd + b / kXcds;
   if (tau >= ntiles) return;
   const TileCoord tc = tile_coord(tau, ngroups, cols, nct, ntiles / nct);
-  u32x4 raw[kPasses][4];
-  load_tile(x, cols, tc, raw);
-  process_tile<kFmt>(tc, raw, rows, ngroups, floor, sm, qT, sf);
+  Bf16Tile tile;
+  load_tile(x, cols, tc, tile.raw);
+  process_tile<kFmt>(tc, tile, rows, ngroups, floor, sm, qT, sf);
+}
+
+// SwiGLU + the same cast: one workgroup per tile of the SwiGLU output.
+template <int kFmt, bool kWeighted, bool kClamp>
+__global__ __launch_bounds__(kThreads) void swiglu_per_channel_t_kernel(
+    const uint16_t* __restrict__ h, const float* __restrict__ w, uint32_t rows, uint32_t cols,
+    uint32_t ngroups, uint32_t nct, uint32_t ntiles, uint32_t per_xcd, float floor, float clamp,
+    unsigned long long* __restrict__ count, uint8_t* __restrict__ qT, float* __restrict__ sf) {
+  __shared__ __attribute__((aligned(16))) Smem sm;
+  const uint32_t b = blockIdx.x;
+  const uint32_t tau = (kOrder & 2) ? b : (b % kXcds) * per_xcd + b / kXcds;
+  if (tau >= ntiles) return;  // the whole workgroup leaves together
+  const TileCoord tc = tile_coord(tau, ngroups, cols, nct, ntiles / nct);
+  F32Tile tile;
+  const uint32_t n = load_swiglu_tile<kWeighted, kClamp>(h, w, cols, clamp, tc, tile);
+  process_tile<kFmt>(tc, tile, rows, ngroups, floor, sm, qT, sf);
+  if (kClamp && count) add_count(n, count);
+}
+
+struct Grid {
+  uint32_t ngroups, nct, ntiles, per_xcd, grid;
+};
+
+// Tile counts of a [rows, cols] cast; false when the kernels' 32-bit tile
+// and in-tile offsets would not hold (row_stride: elements between rows).
+bool make_grid(int64_t rows, int64_t cols, int64_t row_stride, Grid* g) {
+  const int64_t ngroups = rows / kGroupTokens;
+  const int64_t ntg = (ngroups + kTG - 1) / kTG;
+  const int64_t nct = (cols + kChannels - 1) / kChannels;
+  const int64_t ntiles = ntg * nct;
+  const int64_t lim = int64_t(1) << 31;
+  if (ntiles + 2 * kXcds >= lim || (int64_t)kTileTokens * row_stride >= lim ||
+      (int64_t)kChannels * rows >= lim || rows >= lim || row_stride >= lim)
+    return false;
+  const int64_t per_xcd = (ntiles + kXcds - 1) / kXcds;
+  g->ngroups = (uint32_t)ngroups;
+  g->nct = (uint32_t)nct;
+  g->ntiles = (uint32_t)ntiles;
+  g->per_xcd = (uint32_t)per_xcd;
+  g->grid = (uint32_t)((kOrder & 2) ? ntiles : per_xcd * kXcds);
+  return true;
+}
+
+template <int kFmt, bool kWeighted, bool kClamp>
+hipError_t launch_swiglu_t(const uint16_t* h, const float* w, int64_t rows, int64_t cols,
+                           const Grid& g, float floor, float clamp, unsigned long long* count,
+                           uint8_t* qT, float* sf, hipStream_t stream) {
+  hipLaunchKernelGGL((swiglu_per_channel_t_kernel<kFmt, kWeighted, kClamp>), dim3(g.grid),
+                     dim3(kThreads), 0, stream, h, w, (uint32_t)rows, (uint32_t)cols, g.ngroups,
+                     g.nct, g.ntiles, g.per_xcd, floor, clamp, count, qT, sf);
+  return hipGetLastError();
+}
+
+template <int kFmt>
+hipError_t launch_swiglu_t_fmt(const uint16_t* h, const float* w, int64_t rows, int64_t cols,
+                               const Grid& g, float floor, float clamp, unsigned long long* count,
+                               uint8_t* qT, float* sf, hipStream_t stream) {
+  if (w) {
+    return clamp > 0.0f
+               ? launch_swiglu_t<kFmt, true, true>(h, w, rows, cols, g, floor, clamp, count, qT,
+                                                   sf, stream)
+               : launch_swiglu_t<kFmt, true, false>(h, w, rows, cols, g, floor, clamp, count, qT,
+                                                    sf, stream);
+  }
+  return clamp > 0.0f
+             ? launch_swiglu_t<kFmt, false, true>(h, w, rows, cols, g, floor, clamp, count, qT,
+                                                  sf, stream)
+             : launch_swiglu_t<kFmt, false, false>(h, w, rows, cols, g, floor, clamp, count, qT,
+                                                   sf, stream);
 }
 
 }  // namespace
@@ -248,26 +416,36 @@ hipError_t launch_per_channel_T(const void* x, int64_t rows, int64_t cols, int f
                                 void* qT, float* sf, hipStream_t stream,
                                 const LaunchCaps& caps) {
   (void)caps;
-  const int64_t ngroups = rows / kGroupTokens;
-  const int64_t ntg = (ngroups + kTG - 1) / kTG;
-  const int64_t nct = (cols + kChannels - 1) / kChannels;
-  const int64_t ntiles = ntg * nct;
-  if (ntiles == 0) return hipSuccess;
+  Grid g;
   // The kernels index tiles, and offsets inside a tile's rows, in 32 bits.
-  const int64_t lim = int64_t(1) << 31;
-  if (ntiles + 2 * kXcds >= lim || (int64_t)kTileTokens * cols >= lim ||
-      (int64_t)kChannels * rows >= lim || rows >= lim || cols >= lim)
-    return hipErrorInvalidValue;
-  const int64_t per_xcd = (ntiles + kXcds - 1) / kXcds;
-  const int64_t grid = (kOrder & 2) ? ntiles : per_xcd * kXcds;
+  if (!make_grid(rows, cols, cols, &g)) return hipErrorInvalidValue;
+  if (g.ntiles == 0) return hipSuccess;
   auto kernel = fmt == kE4M3 ? per_channel_t_kernel<kE4M3>
                : fmt == kE5M2 ? per_channel_t_kernel<kE5M2> : nullptr;
   if (!kernel) return hipErrorInvalidValue;
-  hipLaunchKernelGGL(kernel, dim3((unsigned)grid), dim3(kThreads), 0, stream,
-                     static_cast<const uint16_t*>(x), (uint32_t)rows, (uint32_t)cols,
-                     (uint32_t)ngroups, (uint32_t)nct, (uint32_t)ntiles, (uint32_t)per_xcd, floor,
-                     static_cast<uint8_t*>(qT), sf);
+  hipLaunchKernelGGL(kernel, dim3(g.grid), dim3(kThreads), 0, stream,
+                     static_cast<const uint16_t*>(x), (uint32_t)rows, (uint32_t)cols, g.ngroups,
+                     g.nct, g.ntiles, g.per_xcd, floor, static_cast<uint8_t*>(qT), sf);
   return hipGetLastError();
+}
+
+hipError_t launch_swiglu_per_channel_T(const void* h, int64_t rows, int64_t cols, const float* w,
+                                       int fmt, float floor, float swiglu_clamp,
+                                       unsigned long long* clamp_count, void* qT, float* sf,
+                                       hipStream_t stream, const LaunchCaps& caps) {
+  (void)caps;
+  Grid g;
+  if (!make_grid(rows, cols, 2 * cols, &g)) return hipErrorInvalidValue;
+  if (g.ntiles == 0) return hipSuccess;
+  const uint16_t* hp = static_cast<const uint16_t*>(h);
+  uint8_t* qp = static_cast<uint8_t*>(qT);
+  if (fmt == kE4M3)
+    return launch_swiglu_t_fmt<kE4M3>(hp, w, rows, cols, g, floor, swiglu_clamp, clamp_count, qp,
+                                      sf, stream);
+  if (fmt == kE5M2)
+    return launch_swiglu_t_fmt<kE5M2>(hp, w, rows, cols, g, floor, swiglu_clamp, clamp_count, qp,
+                                      sf, stream);
+  return hipErrorInvalidValue;
 }
 
 }  // namespace qcast

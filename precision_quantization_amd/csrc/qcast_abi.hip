@@ -60,6 +60,9 @@ int caps_for_current_device(qcast::LaunchCaps* caps) {
 
 int finish(hipError_t err) { return err == hipSuccess ? QCAST_OK : QCAST_ERR_LAUNCH; }
 
+// A clamp bound of +inf clamps nothing; so does any bound <= 0.
+float clamp_value(float c) { return (c > 0.0f && c <= 3.4028235e38f) ? c : 0.0f; }
+
 bool per_token_group_ok(int group) { return group == 32 || group == 64 || group == 128; }
 
 bool sf_flags_ok(int flags) {
@@ -96,6 +99,7 @@ const char* qcast_status_str(int status) {
     case QCAST_ERR_GROUP: return "group or block size not supported";
     case QCAST_ERR_LAUNCH: return "kernel launch failed";
     case QCAST_ERR_DEVICE: return "no usable HIP device";
+    case QCAST_ERR_VALUE: return "a scalar argument is out of range";
   }
   return "unknown status";
 }
@@ -131,26 +135,80 @@ int qcast_e2m1(const void* x, int64_t rows, int64_t cols, int group, float clamp
   return qcast_per_token(x, rows, cols, QCAST_FMT_E2M1, group, clamp_min, q_packed, sf, stream);
 }
 
-int qcast_swiglu_per_token_sf(const void* h, int64_t rows, int64_t cols,
+int qcast_swiglu_per_token_ex(const void* h, int64_t rows, int64_t cols,
                               const float* row_weight, int fmt, int group, float clamp_min,
-                              int sf_flags, void* q, void* sf, void* stream) {
+                              int sf_flags, float swiglu_clamp, void* q, void* sf,
+                              uint64_t* clamp_count, void* stream) {
   if (!fp8_fmt(fmt)) return QCAST_ERR_FORMAT;
   if (!sf_flags_ok(sf_flags)) return QCAST_ERR_FORMAT;
   if (!per_token_group_ok(group)) return QCAST_ERR_GROUP;
   if (rows < 0 || cols < 0 || cols % group != 0 || cols / 8 >= (int64_t(1) << 16) ||
       too_big(rows, 2 * cols) || !sf_shape_ok(rows, cols, group, sf_flags))
     return QCAST_ERR_SHAPE;
+  if (swiglu_clamp != swiglu_clamp) return QCAST_ERR_VALUE;
   if (rows == 0 || cols == 0) return QCAST_OK;
   if (!h || !q || !sf) return QCAST_ERR_NULL;
   if (!aligned(h, 16) || !aligned(q, 16) || !aligned(sf, 4) ||
+      (row_weight && !aligned(row_weight, 4)) || (clamp_count && !aligned(clamp_count, 8)))
+    return QCAST_ERR_ALIGN;
+  qcast::LaunchCaps caps;
+  const int rc = caps_for_current_device(&caps);
+  if (rc != QCAST_OK) return rc;
+  return finish(qcast::launch_swiglu_per_token(
+      h, rows, cols, row_weight, fmt, group, floor_for(fmt, clamp_min), (uint32_t)sf_flags,
+      clamp_value(swiglu_clamp), reinterpret_cast<unsigned long long*>(clamp_count), q, sf,
+      static_cast<hipStream_t>(stream), caps));
+}
+
+int qcast_swiglu_per_token_sf(const void* h, int64_t rows, int64_t cols,
+                              const float* row_weight, int fmt, int group, float clamp_min,
+                              int sf_flags, void* q, void* sf, void* stream) {
+  return qcast_swiglu_per_token_ex(h, rows, cols, row_weight, fmt, group, clamp_min, sf_flags,
+                                   0.0f, q, sf, nullptr, stream);
+}
+
+int qcast_swiglu_backward_per_token(const void* h, const void* dv, int64_t rows, int64_t cols,
+                                    const float* row_weight, int fmt, int group, float clamp_min,
+                                    float swiglu_clamp, void* q, float* sf, void* stream) {
+  if (!fp8_fmt(fmt)) return QCAST_ERR_FORMAT;
+  if (!per_token_group_ok(group)) return QCAST_ERR_GROUP;
+  if (rows < 0 || cols < 0 || cols % group != 0 || cols / 8 >= (int64_t(1) << 16) ||
+      too_big(rows, 2 * cols))
+    return QCAST_ERR_SHAPE;
+  if (swiglu_clamp != swiglu_clamp) return QCAST_ERR_VALUE;
+  if (rows == 0 || cols == 0) return QCAST_OK;
+  if (!h || !dv || !q || !sf) return QCAST_ERR_NULL;
+  if (!aligned(h, 16) || !aligned(dv, 16) || !aligned(q, 16) || !aligned(sf, 4) ||
       (row_weight && !aligned(row_weight, 4)))
     return QCAST_ERR_ALIGN;
   qcast::LaunchCaps caps;
   const int rc = caps_for_current_device(&caps);
   if (rc != QCAST_OK) return rc;
-  return finish(qcast::launch_swiglu_per_token(h, rows, cols, row_weight, fmt, group,
-                                               floor_for(fmt, clamp_min), (uint32_t)sf_flags, q,
-                                               sf, static_cast<hipStream_t>(stream), caps));
+  return finish(qcast::launch_swiglu_backward(h, dv, rows, cols, row_weight, fmt, group,
+                                              floor_for(fmt, clamp_min), clamp_value(swiglu_clamp),
+                                              q, sf, static_cast<hipStream_t>(stream), caps));
+}
+
+int qcast_swiglu_per_channel_T(const void* h, int64_t rows, int64_t cols, const float* row_weight,
+                               int fmt, int group, float clamp_min, float swiglu_clamp, void* qT,
+                               float* sf, uint64_t* clamp_count, void* stream) {
+  if (!fp8_fmt(fmt)) return QCAST_ERR_FORMAT;
+  if (group != 128) return QCAST_ERR_GROUP;
+  if (rows < 0 || cols < 0 || rows % group != 0 || cols % 8 != 0 || too_big(rows, 2 * cols))
+    return QCAST_ERR_SHAPE;
+  if (swiglu_clamp != swiglu_clamp) return QCAST_ERR_VALUE;
+  if (rows == 0 || cols == 0) return QCAST_OK;
+  if (!h || !qT || !sf) return QCAST_ERR_NULL;
+  if (!aligned(h, 16) || !aligned(qT, 16) || !aligned(sf, 4) ||
+      (row_weight && !aligned(row_weight, 4)) || (clamp_count && !aligned(clamp_count, 8)))
+    return QCAST_ERR_ALIGN;
+  qcast::LaunchCaps caps;
+  const int rc = caps_for_current_device(&caps);
+  if (rc != QCAST_OK) return rc;
+  return finish(qcast::launch_swiglu_per_channel_T(
+      h, rows, cols, row_weight, fmt, floor_for(fmt, clamp_min), clamp_value(swiglu_clamp),
+      reinterpret_cast<unsigned long long*>(clamp_count), qT, sf,
+      static_cast<hipStream_t>(stream), caps));
 }
 
 int qcast_swiglu_per_token(const void* h, int64_t rows, int64_t cols, const float* row_weight,
@@ -190,6 +248,22 @@ int qcast_per_channel_T(const void* x, int64_t rows, int64_t cols, int fmt, int 
   if (rc != QCAST_OK) return rc;
   return finish(qcast::launch_per_channel_T(x, rows, cols, fmt, floor_for(fmt, clamp_min), qT, sf,
                                             static_cast<hipStream_t>(stream), caps));
+}
+
+int qcast_per_channel(const void* x, int64_t rows, int64_t cols, int fmt, int group,
+                      float clamp_min, void* q, float* sf, void* stream) {
+  if (!fp8_fmt(fmt)) return QCAST_ERR_FORMAT;
+  if (group != 128) return QCAST_ERR_GROUP;
+  if (rows < 0 || cols < 0 || rows % group != 0 || cols % 8 != 0 || too_big(rows, cols))
+    return QCAST_ERR_SHAPE;
+  if (rows == 0 || cols == 0) return QCAST_OK;
+  if (!x || !q || !sf) return QCAST_ERR_NULL;
+  if (!aligned(x, 16) || !aligned(q, 16) || !aligned(sf, 4)) return QCAST_ERR_ALIGN;
+  qcast::LaunchCaps caps;
+  const int rc = caps_for_current_device(&caps);
+  if (rc != QCAST_OK) return rc;
+  return finish(qcast::launch_per_channel(x, rows, cols, fmt, floor_for(fmt, clamp_min), q, sf,
+                                          static_cast<hipStream_t>(stream), caps));
 }
 
 int qcast_cast_back(const void* q, const float* sf, int64_t rows, int64_t cols, int fmt,

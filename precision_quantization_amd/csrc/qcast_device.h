@@ -238,6 +238,34 @@ __device__ __forceinline__ uint32_t e2m1x8(const float y[8]) {
   return w;
 }
 
+// Add a per-lane count into *count (a 64-bit counter in device memory that
+// the caller zeroed or accumulates into): a wave sum, a workgroup sum in
+// LDS, then one vector atomic per workgroup whose sum is not zero. Every
+// thread of the workgroup must call it (it holds a barrier).
+__device__ __forceinline__ void add_count(uint32_t n, unsigned long long* count) {
+  __shared__ uint32_t part[kThreads / 64];
+#pragma unroll
+  for (int o = 32; o >= 1; o >>= 1) n += (uint32_t)__shfl_xor((int)n, o);
+  if ((threadIdx.x & 63) == 0) part[threadIdx.x >> 6] = n;
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    uint32_t total = 0;
+#pragma unroll
+    for (int i = 0; i < kThreads / 64; ++i) total += part[i];
+    if (total) atomicAdd(count, (unsigned long long)total);
+  }
+}
+
+// The clamp of the SwiGLU inputs: the gate is bounded from above by c, the
+// up value to [-c, c]; returns how many of the two values it changed.
+// (Written as selects, so a NaN input passes through unclamped.)
+__device__ __forceinline__ uint32_t clamp_gate_up(float& g, float& u, float c) {
+  const uint32_t n = (uint32_t)(g > c) + (uint32_t)(u > c) + (uint32_t)(u < -c);
+  g = g > c ? c : g;
+  u = u > c ? c : (u < -c ? -c : u);
+  return n;
+}
+
 // Streaming accesses: the data is touched once.
 template <typename T>
 __device__ __forceinline__ T load_stream(const T* p) { return __builtin_nontemporal_load(p); }

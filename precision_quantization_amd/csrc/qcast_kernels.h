@@ -33,10 +33,19 @@ hipError_t launch_per_token(const void* x, int64_t rows, int64_t cols, int fmt, 
 
 // h [rows, 2*cols] bf16 (gate | up), w [rows] fp32 or null -> 8-bit codes
 // (kE4M3 / kE5M2) + scales of silu(gate) * up * w; group in {32, 64, 128};
-// cols % group == 0.
+// cols % group == 0. swiglu_clamp > 0 clamps gate and up first and adds the
+// number of changed values to *clamp_count (when not null).
 hipError_t launch_swiglu_per_token(const void* h, int64_t rows, int64_t cols, const float* w,
-                                   int fmt, int group, float floor, uint32_t sf_flags, void* q,
+                                   int fmt, int group, float floor, uint32_t sf_flags,
+                                   float swiglu_clamp, unsigned long long* clamp_count, void* q,
                                    void* sf, hipStream_t stream, const LaunchCaps& caps);
+
+// SwiGLU backward: h [rows, 2*cols] bf16, dv [rows, cols] bf16, w or null
+// -> q [rows, 2*cols] 8-bit codes of [dgate | dup], sf [rows, 2*cols/group].
+hipError_t launch_swiglu_backward(const void* h, const void* dv, int64_t rows, int64_t cols,
+                                  const float* w, int fmt, int group, float floor,
+                                  float swiglu_clamp, void* q, float* sf, hipStream_t stream,
+                                  const LaunchCaps& caps);
 
 // x [rows, cols] bf16 -> 8-bit codes + one scale per 128 x 128 block.
 hipError_t launch_per_block(const void* x, int64_t rows, int64_t cols, int fmt, float floor,
@@ -47,6 +56,19 @@ hipError_t launch_per_block(const void* x, int64_t rows, int64_t cols, int fmt, 
 hipError_t launch_per_channel_T(const void* x, int64_t rows, int64_t cols, int fmt, float floor,
                                 void* qT, float* sf, hipStream_t stream,
                                 const LaunchCaps& caps);
+
+// SwiGLU of h [rows, 2*cols] (clamped when swiglu_clamp > 0, changed values
+// added to *clamp_count when not null), then the per-channel cast written
+// transposed: qT [cols, rows], sf [cols, rows/128].
+hipError_t launch_swiglu_per_channel_T(const void* h, int64_t rows, int64_t cols, const float* w,
+                                       int fmt, float floor, float swiglu_clamp,
+                                       unsigned long long* clamp_count, void* qT, float* sf,
+                                       hipStream_t stream, const LaunchCaps& caps);
+
+// x [rows (tokens), cols (channels)] bf16 -> q [rows, cols] 8-bit codes in the
+// input layout + sf [rows/128, cols]; rows % 128 == 0, cols % 8 == 0.
+hipError_t launch_per_channel(const void* x, int64_t rows, int64_t cols, int fmt, float floor,
+                              void* q, float* sf, hipStream_t stream, const LaunchCaps& caps);
 
 // q per-token codes [rows, cols] (or [rows, cols/2] E2M1) + sf [rows, cols/group]
 // -> out [rows, cols] bf16 (out_bf16) or fp32: decode(q) * sf.

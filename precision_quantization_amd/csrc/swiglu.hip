@@ -17,6 +17,10 @@
 // which moves a code only where v lies next to a rounding midpoint. When
 // exp(-g) overflows, the reciprocal is 0 and v is a zero of the right sign,
 // as in the exact expression.
+//
+// The optional clamp of the same section bounds the gate from above and the
+// up value to [-c, c] before the product; the number of values it changed
+// is summed per workgroup and added to a 64-bit counter with one atomic.
 #include "qcast_device.h"
 #include "qcast_kernels.h"
 
@@ -44,11 +48,13 @@ __device__ __forceinline__ float silu_times(float g, float u) {
   return g * __builtin_amdgcn_rcpf(1.0f + e) * u;
 }
 
-template <int kLanes, bool kWeighted, int kFmt>
+template <int kLanes, bool kWeighted, int kFmt, bool kClamp>
 __global__ __launch_bounds__(kThreads) void swiglu_kernel(
     const uint16_t* __restrict__ h, const float* __restrict__ w, int64_t nchunks,
     uint32_t chunks_per_row, uint64_t row_magic, int64_t cols, float floor,
-    uint8_t* __restrict__ q, void* __restrict__ sf, SfLayout lay, uint32_t group0) {
+    uint8_t* __restrict__ q, void* __restrict__ sf, SfLayout lay, uint32_t group0,
+    float clamp, unsigned long long* __restrict__ count) {
+  uint32_t nclamp = 0;
   const int64_t step = (int64_t)gridDim.x * kThreads * kUnroll;
   for (int64_t base = (int64_t)blockIdx.x * kThreads * kUnroll + threadIdx.x; base < nchunks;
        base += step) {
@@ -75,6 +81,7 @@ __global__ __launch_bounds__(kThreads) void swiglu_kernel(
         unpack8(uraw[u], uv);
 #pragma unroll
         for (int i = 0; i < 8; ++i) {
+          if (kClamp) nclamp += clamp_gate_up(gv[i], uv[i], clamp);
           v[i] = silu_times(gv[i], uv[i]);
           if (kWeighted) v[i] = v[i] * wr[u];
         }
@@ -89,12 +96,18 @@ __global__ __launch_bounds__(kThreads) void swiglu_kernel(
       }
     }
   }
+  if (kClamp && count) add_count(nclamp, count);
 }
 
-template <int kLanes, bool kWeighted, int kFmt>
+struct ClampArgs {
+  float c;                    // > 0: clamp bound
+  unsigned long long* count;  // device counter or null
+};
+
+template <int kLanes, bool kWeighted, int kFmt, bool kClamp>
 hipError_t launch(const uint16_t* h, const float* w, int64_t rows, int64_t cols, float floor,
-                  uint8_t* q, void* sf, const SfLayout& lay, hipStream_t stream,
-                  const LaunchCaps& caps) {
+                  uint8_t* q, void* sf, const SfLayout& lay, const ClampArgs& ca,
+                  hipStream_t stream, const LaunchCaps& caps) {
   const int64_t cpr = cols / 8;
   const uint64_t magic = ((uint64_t(1) << 40) + (uint64_t)cpr - 1) / (uint64_t)cpr;
   const int64_t groups_per_row = cols / (kLanes * 8);
@@ -108,51 +121,67 @@ hipError_t launch(const uint16_t* h, const float* w, int64_t rows, int64_t cols,
     const int64_t max_blocks = kWgPerCu > 0 ? (int64_t)caps.num_cus * kWgPerCu : iters;
     const int64_t iters_per_block = (iters + max_blocks - 1) / max_blocks;
     const int64_t blocks = (iters + iters_per_block - 1) / iters_per_block;
-    hipLaunchKernelGGL((swiglu_kernel<kLanes, kWeighted, kFmt>), dim3((unsigned)blocks),
-                       dim3(kThreads), 0, stream, h + r0 * 2 * cols,
+    hipLaunchKernelGGL((swiglu_kernel<kLanes, kWeighted, kFmt, kClamp>),
+                       dim3((unsigned)blocks), dim3(kThreads), 0, stream, h + r0 * 2 * cols,
                        kWeighted ? w + r0 : nullptr, nchunks, (uint32_t)cpr, magic, cols, floor,
-                       q + r0 * cols, sf, lay, (uint32_t)(r0 * groups_per_row));
+                       q + r0 * cols, sf, lay, (uint32_t)(r0 * groups_per_row), ca.c, ca.count);
     const hipError_t err = hipGetLastError();
     if (err != hipSuccess) return err;
   }
   return hipSuccess;
 }
 
-template <int kLanes, int kFmt>
+template <int kLanes, int kFmt, bool kClamp>
 hipError_t launch_w(const uint16_t* h, const float* w, int64_t rows, int64_t cols, float floor,
-                    uint8_t* q, void* sf, const SfLayout& lay, hipStream_t stream,
-                    const LaunchCaps& caps) {
-  return w ? launch<kLanes, true, kFmt>(h, w, rows, cols, floor, q, sf, lay, stream, caps)
-           : launch<kLanes, false, kFmt>(h, w, rows, cols, floor, q, sf, lay, stream, caps);
+                    uint8_t* q, void* sf, const SfLayout& lay, const ClampArgs& ca,
+                    hipStream_t stream, const LaunchCaps& caps) {
+  return w ? launch<kLanes, true, kFmt, kClamp>(h, w, rows, cols, floor, q, sf, lay, ca, stream,
+                                                caps)
+           : launch<kLanes, false, kFmt, kClamp>(h, w, rows, cols, floor, q, sf, lay, ca, stream,
+                                                 caps);
+}
+
+template <int kFmt, bool kClamp>
+hipError_t launch_g(const uint16_t* h, const float* w, int64_t rows, int64_t cols, int group,
+                    float floor, uint8_t* q, void* sf, const SfLayout& lay, const ClampArgs& ca,
+                    hipStream_t stream, const LaunchCaps& caps) {
+  switch (group) {
+    case 32:
+      return launch_w<4, kFmt, kClamp>(h, w, rows, cols, floor, q, sf, lay, ca, stream, caps);
+    case 64:
+      return launch_w<8, kFmt, kClamp>(h, w, rows, cols, floor, q, sf, lay, ca, stream, caps);
+    case 128:
+      return launch_w<16, kFmt, kClamp>(h, w, rows, cols, floor, q, sf, lay, ca, stream, caps);
+  }
+  return hipErrorInvalidValue;
 }
 
 template <int kFmt>
-hipError_t launch_g(const uint16_t* h, const float* w, int64_t rows, int64_t cols, int group,
-                    float floor, uint8_t* q, void* sf, const SfLayout& lay, hipStream_t stream,
-                    const LaunchCaps& caps) {
-  switch (group) {
-    case 32: return launch_w<4, kFmt>(h, w, rows, cols, floor, q, sf, lay, stream, caps);
-    case 64: return launch_w<8, kFmt>(h, w, rows, cols, floor, q, sf, lay, stream, caps);
-    case 128: return launch_w<16, kFmt>(h, w, rows, cols, floor, q, sf, lay, stream, caps);
-  }
-  return hipErrorInvalidValue;
+hipError_t launch_c(const uint16_t* h, const float* w, int64_t rows, int64_t cols, int group,
+                    float floor, uint8_t* q, void* sf, const SfLayout& lay, const ClampArgs& ca,
+                    hipStream_t stream, const LaunchCaps& caps) {
+  return ca.c > 0.0f
+             ? launch_g<kFmt, true>(h, w, rows, cols, group, floor, q, sf, lay, ca, stream, caps)
+             : launch_g<kFmt, false>(h, w, rows, cols, group, floor, q, sf, lay, ca, stream, caps);
 }
 
 }  // namespace
 
 hipError_t launch_swiglu_per_token(const void* h, int64_t rows, int64_t cols, const float* w,
-                                   int fmt, int group, float floor, uint32_t sf_flags, void* q,
+                                   int fmt, int group, float floor, uint32_t sf_flags,
+                                   float swiglu_clamp, unsigned long long* clamp_count, void* q,
                                    void* sf, hipStream_t stream, const LaunchCaps& caps) {
   if (rows == 0 || cols == 0) return hipSuccess;
   if (cols / 8 >= kMaxChunksPerRow) return hipErrorInvalidValue;
   if (rows * cols / group >= (int64_t(1) << 31)) return hipErrorInvalidValue;
   const SfLayout lay = make_sf_layout(rows, cols, group, sf_flags);
+  const ClampArgs ca{swiglu_clamp, clamp_count};
   const uint16_t* hp = static_cast<const uint16_t*>(h);
   uint8_t* qp = static_cast<uint8_t*>(q);
   if (fmt == kE4M3)
-    return launch_g<kE4M3>(hp, w, rows, cols, group, floor, qp, sf, lay, stream, caps);
+    return launch_c<kE4M3>(hp, w, rows, cols, group, floor, qp, sf, lay, ca, stream, caps);
   if (fmt == kE5M2)
-    return launch_g<kE5M2>(hp, w, rows, cols, group, floor, qp, sf, lay, stream, caps);
+    return launch_c<kE5M2>(hp, w, rows, cols, group, floor, qp, sf, lay, ca, stream, caps);
   return hipErrorInvalidValue;
 }
 

@@ -16,7 +16,8 @@ from conftest import ROOT, gpu_available
 
 HEADERS = [os.path.join(ROOT, "include", h) for h in ("qcast.h", "qcast_bench.h")]
 
-OK, ERR_NULL, ERR_SHAPE, ERR_ALIGN, ERR_FORMAT, ERR_GROUP, ERR_LAUNCH, ERR_DEVICE = range(8)
+(OK, ERR_NULL, ERR_SHAPE, ERR_ALIGN, ERR_FORMAT, ERR_GROUP, ERR_LAUNCH, ERR_DEVICE,
+ ERR_VALUE) = range(9)
 E4M3, E2M1, E5M2 = 1, 2, 3
 A16 = 0x10000          # aligned, never dereferenced (rejected before use)
 MIS = 0x10008          # 8-byte aligned only
@@ -63,10 +64,11 @@ def test_binding_names_match_the_c_entry_points():
 
 
 def test_abi_version_and_status_strings(lib):
-    assert lib.qcast_abi_version() == 1
-    for s in range(8):
+    assert lib.qcast_abi_version() == 2
+    for s in range(9):
         assert lib.qcast_status_str(s).decode()
     assert lib.qcast_status_str(99).decode() == "unknown status"
+    assert "out of range" in lib.qcast_status_str(8).decode()
 
 
 def pt(lib, x=A16, rows=4, cols=256, fmt=E4M3, group=128, q=A16, sf=A16):
@@ -158,6 +160,56 @@ def test_sf_layout_validation(lib):
     assert g(A16, 4, 512, None, E4M3, 128, 0.0, 16, A16, A16, None) == ERR_FORMAT
     assert g(A16, 4, 384, None, E4M3, 128, 0.0, 4, A16, A16, None) == ERR_SHAPE
     assert g(A16, 4, 512, None, E2M1, 32, 0.0, 4, A16, A16, None) == ERR_FORMAT
+
+
+def test_swiglu_ex_validation(lib):
+    f = lib.qcast_swiglu_per_token_ex
+    nan = float("nan")
+    assert f(A16, 4, 256, None, E2M1, 32, 0.0, 0, 1.0, A16, A16, None, None) == ERR_FORMAT
+    assert f(A16, 4, 256, None, E4M3, 128, 0.0, 8, 1.0, A16, A16, None, None) == ERR_FORMAT
+    assert f(A16, 4, 256, None, E4M3, 100, 0.0, 0, 1.0, A16, A16, None, None) == ERR_GROUP
+    assert f(A16, 4, 200, None, E4M3, 128, 0.0, 0, 1.0, A16, A16, None, None) == ERR_SHAPE
+    assert f(A16, 4, 256, None, E4M3, 128, 0.0, 0, nan, A16, A16, None, None) == ERR_VALUE
+    assert f(A16, 0, 256, None, E4M3, 128, 0.0, 0, nan, None, None, None, None) == ERR_VALUE
+    assert f(None, 4, 256, None, E4M3, 128, 0.0, 0, 1.0, A16, A16, None, None) == ERR_NULL
+    assert f(A16, 4, 256, None, E4M3, 128, 0.0, 0, 1.0, A16, A16, A16 + 4, None) == ERR_ALIGN
+    assert f(None, 0, 256, None, E4M3, 128, 0.0, 0, 1.0, None, None, None, None) == OK
+
+
+def test_swiglu_backward_validation(lib):
+    f = lib.qcast_swiglu_backward_per_token
+    assert f(A16, A16, 4, 256, None, E2M1, 32, 0.0, 0.0, A16, A16, None) == ERR_FORMAT
+    assert f(A16, A16, 4, 256, None, E4M3, 16, 0.0, 0.0, A16, A16, None) == ERR_GROUP
+    assert f(A16, A16, 4, 200, None, E4M3, 128, 0.0, 0.0, A16, A16, None) == ERR_SHAPE
+    assert f(A16, A16, 4, 1 << 19, None, E4M3, 128, 0.0, 0.0, A16, A16, None) == ERR_SHAPE
+    assert f(A16, A16, 4, 256, None, E4M3, 128, 0.0, float("nan"), A16, A16, None) == ERR_VALUE
+    assert f(A16, None, 4, 256, None, E4M3, 128, 0.0, 0.0, A16, A16, None) == ERR_NULL
+    assert f(A16, MIS, 4, 256, None, E5M2, 128, 0.0, 0.0, A16, A16, None) == ERR_ALIGN
+    assert f(None, None, 0, 256, None, E4M3, 128, 0.0, 0.0, None, None, None) == OK
+
+
+def test_swiglu_per_channel_T_validation(lib):
+    f = lib.qcast_swiglu_per_channel_T
+    assert f(A16, 256, 64, None, E2M1, 128, 0.0, 0.0, A16, A16, None, None) == ERR_FORMAT
+    assert f(A16, 256, 64, None, E4M3, 32, 0.0, 0.0, A16, A16, None, None) == ERR_GROUP
+    assert f(A16, 200, 64, None, E4M3, 128, 0.0, 0.0, A16, A16, None, None) == ERR_SHAPE
+    assert f(A16, 256, 60, None, E4M3, 128, 0.0, 0.0, A16, A16, None, None) == ERR_SHAPE
+    assert f(A16, 256, 64, None, E4M3, 128, 0.0, float("nan"), A16, A16, None, None) == ERR_VALUE
+    assert f(A16, 256, 64, None, E4M3, 128, 0.0, 0.0, None, A16, None, None) == ERR_NULL
+    assert f(A16, 256, 64, A16 + 2, E4M3, 128, 0.0, 0.0, A16, A16, None, None) == ERR_ALIGN
+    assert f(A16, 256, 64, None, E4M3, 128, 0.0, 1.0, A16, A16, A16 + 4, None) == ERR_ALIGN
+    assert f(None, 0, 64, None, E4M3, 128, 0.0, 0.0, None, None, None, None) == OK
+
+
+def test_per_channel_validation(lib):
+    f = lib.qcast_per_channel
+    assert f(A16, 256, 64, E2M1, 128, 0.0, A16, A16, None) == ERR_FORMAT
+    assert f(A16, 256, 64, E4M3, 64, 0.0, A16, A16, None) == ERR_GROUP
+    assert f(A16, 200, 64, E4M3, 128, 0.0, A16, A16, None) == ERR_SHAPE
+    assert f(A16, 256, 60, E4M3, 128, 0.0, A16, A16, None) == ERR_SHAPE
+    assert f(A16, 256, 64, E4M3, 128, 0.0, A16, None, None) == ERR_NULL
+    assert f(A16, 256, 64, E5M2, 128, 0.0, MIS, A16, None) == ERR_ALIGN
+    assert f(None, 0, 64, E4M3, 128, 0.0, None, None, None) == OK
 
 
 def test_cast_back_validation(lib):
