@@ -18,6 +18,12 @@ steps. The roofline object is for the kernel with the largest share of the
 step. The CPU baseline is the oracle (single thread) on the first half of the
 rows of every workload, on this host.
 
+"other_kernels" times, after the step and outside `value`, the casts that
+are not among the five: cast_back of the per-token codes to bf16, the
+per-token cast with 1 x 32 groups and packed UE8M0 column-major scales,
+SwiGLU with the clamp and counter, SwiGLU + per-channel cast + transpose,
+the SwiGLU backward cast, and the per-channel cast in the input layout.
+
     python bench.py [--gpus 1] [--steps 50] [--warmup 5]
 """
 import argparse
@@ -125,6 +131,94 @@ def kernel_calls(wls, dev):
     return calls
 
 
+def extra_calls(wls, dev):
+    """The casts beyond the five of a step (timed separately, not part of
+    `value`): name, shape, algorithmic bytes, closure."""
+    import torch
+    import precision_quantization_amd as pq
+    from precision_quantization_amd import workloads as W
+    by = dict(wls)
+    calls = []
+    # cast_back: per-token E4M3 codes of the hidden-state workload -> bf16
+    x = by["per_token"].x.to(dev)
+    r, c = x.shape
+    q, sf = pq.qcast_per_token(x, "e4m3", 128)
+    out = torch.empty(r, c, dtype=torch.bfloat16, device=dev)
+    calls.append(("cast_back", [r, c], r * c + r * (c // 128) * 4 + r * c * 2,
+                  lambda q=q, sf=sf, out=out: pq.qcast_cast_back(q, sf, "e4m3", 128, out=out)))
+    # per-token cast with 1 x 32 groups and packed UE8M0 column-major scales
+    flags = pq.SF_PACKED_UE8M0 | pq.SF_COL_MAJOR
+    shape, dt = pq.sf_layout_shape(r, c, 32, flags)
+    qo = torch.empty(r, c, dtype=torch.float8_e4m3fn, device=dev)
+    so = torch.empty(shape, dtype=dt, device=dev)
+    calls.append(("per_token_ue8m0_g32", [r, c], 2 * r * c + r * c + shape[0] * shape[1] * 4,
+                  lambda x=x, qo=qo, so=so: pq.qcast_per_token_sf(x, "e4m3", 32, sf_flags=flags,
+                                                                  out=qo, out_sf=so)))
+    # SwiGLU with clamp and counter
+    wl = by["swiglu"]
+    h, w = wl.x.to(dev), wl.w.to(dev)
+    r, n = wl.rows, wl.cols
+    cnt = torch.zeros(1, dtype=torch.int64, device=dev)
+    qs = torch.empty(r, n, dtype=torch.float8_e4m3fn, device=dev)
+    ss = torch.empty(r, n // 128, dtype=torch.float32, device=dev)
+    calls.append(("swiglu_clamp", [r, 2 * n], wl.algorithmic_bytes(),
+                  lambda h=h, w=w, qs=qs, ss=ss, cnt=cnt: pq.qcast_swiglu_per_token_ex(
+                      h, w, "e4m3", 128, swiglu_clamp=5.0, clamp_count=cnt, out=qs, out_sf=ss)))
+    # SwiGLU + per-channel cast + transpose
+    qt = torch.empty(n, r, dtype=torch.float8_e4m3fn, device=dev)
+    st = torch.empty(n, r // 128, dtype=torch.float32, device=dev)
+    calls.append(("swiglu_per_channel_T", [r, 2 * n], r * 2 * n * 2 + r * 4 + n * r + n * r // 32,
+                  lambda h=h, w=w, qt=qt, st=st: pq.qcast_swiglu_per_channel_T(
+                      h, w, "e4m3", 128, out=qt, out_sf=st)))
+    # SwiGLU backward + per-token cast of [dgate | dup]
+    hg, dvg, wg = W.swiglu_grad()
+    hg, dvg, wg = hg.to(dev), dvg.to(dev), wg.to(dev)
+    qb = torch.empty(r, 2 * n, dtype=torch.float8_e4m3fn, device=dev)
+    sb = torch.empty(r, 2 * n // 128, dtype=torch.float32, device=dev)
+    calls.append(("swiglu_backward", [r, 2 * n],
+                  r * 2 * n * 2 + r * n * 2 + r * 4 + r * 2 * n + r * (2 * n // 128) * 4,
+                  lambda hg=hg, dvg=dvg, wg=wg, qb=qb, sb=sb: pq.qcast_swiglu_backward_per_token(
+                      hg, dvg, wg, "e4m3", 128, swiglu_clamp=6.0, out=qb, out_sf=sb)))
+    # per-channel cast in the input layout
+    a = by["per_channel_T"].x.to(dev)
+    r, c = a.shape
+    qc = torch.empty(r, c, dtype=torch.float8_e4m3fn, device=dev)
+    sc = torch.empty(r // 128, c, dtype=torch.float32, device=dev)
+    calls.append(("per_channel", [r, c], 2 * r * c + r * c + (r // 128) * c * 4,
+                  lambda a=a, qc=qc, sc=sc: pq.qcast_per_channel(a, "e4m3", 128, out=qc,
+                                                                 out_sf=sc)))
+    return calls
+
+
+def time_extras(extras, dev, steps, warmup):
+    import torch
+    for _ in range(warmup):
+        for *_, fn in extras:
+            fn()
+    torch.cuda.synchronize()
+    hev = HipEvents()
+    stream = torch.cuda.current_stream(dev).cuda_stream
+    n = len(extras)
+    ev = [[hev.create() for _ in range(n + 1)] for _ in range(steps)]
+    for s in range(steps):
+        hev.record(ev[s][0], stream)
+        for i, (*_, fn) in enumerate(extras):
+            fn()
+            hev.record(ev[s][i + 1], stream)
+    torch.cuda.synchronize()
+    out = {}
+    for i, (name, shape, b, _) in enumerate(extras):
+        ms = sorted(hev.elapsed_ms(ev[s][i], ev[s][i + 1]) for s in range(steps))
+        avg = sum(ms) / len(ms)
+        out[name] = {"shape": shape, "bytes": b, "avg_us": round(avg * 1e3, 2),
+                     "GBps": round(b / (avg * 1e-3) / 1e9, 1),
+                     "frac": round(b / (avg * 1e-3) / 1e9 / PEAK_HBM_GBS, 4)}
+    for row in ev:
+        for e in row:
+            hev.destroy(e)
+    return out
+
+
 def copy_ceiling(dev, nbytes):
     """Bandwidth of the library's streaming copy (include/qcast_bench.h)
     moving nbytes in total (half read, half written) after a 1 GiB flush:
@@ -200,6 +294,8 @@ def main():
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-extras", action="store_true",
+                    help="skip timing the casts that are not part of the step")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py measures one GPU; --gpus {args.gpus} is not supported: the casts shard "
@@ -282,6 +378,10 @@ def main():
         "kernels": kernels,
         "copy_ceiling_GBps": round(copy_gbs, 1),
     }
+    if not args.no_extras:
+        log("bench: timing the other casts")
+        result["other_kernels"] = time_extras(extra_calls(wls, dev), dev, args.steps,
+                                              args.warmup)
     if not args.no_cpu_baseline:
         log("bench: CPU baseline (oracle)")
         gbs, secs = cpu_baseline(wls)

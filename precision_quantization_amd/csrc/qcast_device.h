@@ -241,9 +241,10 @@ __device__ __forceinline__ uint32_t e2m1x8(const float y[8]) {
 // Add a per-lane count into *count (a 64-bit counter in device memory that
 // the caller zeroed or accumulates into): a wave sum, a workgroup sum in
 // LDS, then one vector atomic per workgroup whose sum is not zero. Every
-// thread of the workgroup must call it (it holds a barrier).
+// thread of the kBlock-thread workgroup must call it (it holds a barrier).
+template <int kBlock = kThreads>
 __device__ __forceinline__ void add_count(uint32_t n, unsigned long long* count) {
-  __shared__ uint32_t part[kThreads / 64];
+  __shared__ uint32_t part[kBlock / 64];
 #pragma unroll
   for (int o = 32; o >= 1; o >>= 1) n += (uint32_t)__shfl_xor((int)n, o);
   if ((threadIdx.x & 63) == 0) part[threadIdx.x >> 6] = n;
@@ -251,7 +252,7 @@ __device__ __forceinline__ void add_count(uint32_t n, unsigned long long* count)
   if (threadIdx.x == 0) {
     uint32_t total = 0;
 #pragma unroll
-    for (int i = 0; i < kThreads / 64; ++i) total += part[i];
+    for (int i = 0; i < kBlock / 64; ++i) total += part[i];
     if (total) atomicAdd(count, (unsigned long long)total);
   }
 }

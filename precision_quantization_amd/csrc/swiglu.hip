@@ -35,8 +35,21 @@ namespace {
 #ifndef QCAST_SW_WG_PER_CU
 #define QCAST_SW_WG_PER_CU 0
 #endif
+// With a clamp counter every workgroup ends in one atomic add on the same
+// 64-bit word, and those adds are serialized where the word lives (about
+// 8 ns each, measured), so the counting kernel runs a capped, grid-strided
+// grid of this many workgroups per CU, each of kCountBlock threads (large
+// workgroups keep the waves per CU up while the atomics stay few).
+#ifndef QCAST_SW_COUNT_WG_PER_CU
+#define QCAST_SW_COUNT_WG_PER_CU 1
+#endif
+#ifndef QCAST_SW_COUNT_BLOCK
+#define QCAST_SW_COUNT_BLOCK 1024
+#endif
+constexpr int kCountBlock = QCAST_SW_COUNT_BLOCK;
 constexpr int kUnroll = QCAST_SW_UNROLL;
 constexpr int kWgPerCu = QCAST_SW_WG_PER_CU;
+constexpr int kCountWgPerCu = QCAST_SW_COUNT_WG_PER_CU;
 constexpr float kLog2e = 1.4426950408889634f;
 // Chunk-to-row division: row = (c * magic) >> 40 is exact for c < 2^24 and
 // chunks-per-row d < 2^16 when magic = ceil(2^40 / d).
@@ -48,21 +61,21 @@ __device__ __forceinline__ float silu_times(float g, float u) {
   return g * __builtin_amdgcn_rcpf(1.0f + e) * u;
 }
 
-template <int kLanes, bool kWeighted, int kFmt, bool kClamp>
-__global__ __launch_bounds__(kThreads) void swiglu_kernel(
+template <int kLanes, bool kWeighted, int kFmt, bool kClamp, int kBlock>
+__global__ __launch_bounds__(kBlock) void swiglu_kernel(
     const uint16_t* __restrict__ h, const float* __restrict__ w, int64_t nchunks,
     uint32_t chunks_per_row, uint64_t row_magic, int64_t cols, float floor,
     uint8_t* __restrict__ q, void* __restrict__ sf, SfLayout lay, uint32_t group0,
     float clamp, unsigned long long* __restrict__ count) {
   uint32_t nclamp = 0;
-  const int64_t step = (int64_t)gridDim.x * kThreads * kUnroll;
-  for (int64_t base = (int64_t)blockIdx.x * kThreads * kUnroll + threadIdx.x; base < nchunks;
+  const int64_t step = (int64_t)gridDim.x * kBlock * kUnroll;
+  for (int64_t base = (int64_t)blockIdx.x * kBlock * kUnroll + threadIdx.x; base < nchunks;
        base += step) {
     u32x4 graw[kUnroll], uraw[kUnroll];
     float wr[kUnroll];
 #pragma unroll
     for (int u = 0; u < kUnroll; ++u) {
-      const int64_t c = base + (int64_t)u * kThreads;
+      const int64_t c = base + (int64_t)u * kBlock;
       if (c < nchunks) {
         const uint32_t row = (uint32_t)(((uint64_t)c * row_magic) >> 40);
         const uint32_t jc = (uint32_t)c - row * chunks_per_row;
@@ -74,7 +87,7 @@ __global__ __launch_bounds__(kThreads) void swiglu_kernel(
     }
 #pragma unroll
     for (int u = 0; u < kUnroll; ++u) {
-      const int64_t c = base + (int64_t)u * kThreads;
+      const int64_t c = base + (int64_t)u * kBlock;
       if (c < nchunks) {
         float gv[8], uv[8], v[8];
         unpack8(graw[u], gv);
@@ -96,7 +109,7 @@ __global__ __launch_bounds__(kThreads) void swiglu_kernel(
       }
     }
   }
-  if (kClamp && count) add_count(nclamp, count);
+  if (kClamp && count) add_count<kBlock>(nclamp, count);
 }
 
 struct ClampArgs {
@@ -116,15 +129,26 @@ hipError_t launch(const uint16_t* h, const float* w, int64_t rows, int64_t cols,
   for (int64_t r0 = 0; r0 < rows; r0 += slab_rows) {
     const int64_t nr = rows - r0 < slab_rows ? rows - r0 : slab_rows;
     const int64_t nchunks = nr * cpr;
-    const int64_t per_block_iter = (int64_t)kThreads * kUnroll;
+    const bool counting = kClamp && ca.count;
+    const int block = counting ? kCountBlock : kThreads;
+    const int64_t per_block_iter = (int64_t)block * kUnroll;
     const int64_t iters = (nchunks + per_block_iter - 1) / per_block_iter;
-    const int64_t max_blocks = kWgPerCu > 0 ? (int64_t)caps.num_cus * kWgPerCu : iters;
+    const int wg_per_cu = counting ? kCountWgPerCu : kWgPerCu;
+    const int64_t max_blocks = wg_per_cu > 0 ? (int64_t)caps.num_cus * wg_per_cu : iters;
     const int64_t iters_per_block = (iters + max_blocks - 1) / max_blocks;
     const int64_t blocks = (iters + iters_per_block - 1) / iters_per_block;
-    hipLaunchKernelGGL((swiglu_kernel<kLanes, kWeighted, kFmt, kClamp>),
-                       dim3((unsigned)blocks), dim3(kThreads), 0, stream, h + r0 * 2 * cols,
-                       kWeighted ? w + r0 : nullptr, nchunks, (uint32_t)cpr, magic, cols, floor,
-                       q + r0 * cols, sf, lay, (uint32_t)(r0 * groups_per_row), ca.c, ca.count);
+    if (counting)
+      hipLaunchKernelGGL((swiglu_kernel<kLanes, kWeighted, kFmt, kClamp, kCountBlock>),
+                         dim3((unsigned)blocks), dim3(kCountBlock), 0, stream, h + r0 * 2 * cols,
+                         kWeighted ? w + r0 : nullptr, nchunks, (uint32_t)cpr, magic, cols,
+                         floor, q + r0 * cols, sf, lay, (uint32_t)(r0 * groups_per_row), ca.c,
+                         ca.count);
+    else
+      hipLaunchKernelGGL((swiglu_kernel<kLanes, kWeighted, kFmt, kClamp, kThreads>),
+                         dim3((unsigned)blocks), dim3(kThreads), 0, stream, h + r0 * 2 * cols,
+                         kWeighted ? w + r0 : nullptr, nchunks, (uint32_t)cpr, magic, cols,
+                         floor, q + r0 * cols, sf, lay, (uint32_t)(r0 * groups_per_row), ca.c,
+                         ca.count);
     const hipError_t err = hipGetLastError();
     if (err != hipSuccess) return err;
   }
