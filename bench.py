@@ -377,6 +377,7 @@ def main():
         },
         "kernels": kernels,
         "copy_ceiling_GBps": round(copy_gbs, 1),
+        "copy_bytes": d["bytes"] // 2 // 16 * 16 * 2,
     }
     if not args.no_extras:
         log("bench: timing the other casts")
