@@ -18,12 +18,13 @@ from . import build as _build
 FMT_E4M3 = 1
 FMT_E2M1 = 2
 FMT_E5M2 = 3
+FMT_E5M6 = 4
 OUT_BF16 = 1
 OUT_F32 = 2
 SF_ROUND_POW2 = 1
 SF_COL_MAJOR = 2
 SF_PACKED_UE8M0 = 4
-_FMT_NAMES = {"e4m3": FMT_E4M3, "e2m1": FMT_E2M1, "e5m2": FMT_E5M2}
+_FMT_NAMES = {"e4m3": FMT_E4M3, "e2m1": FMT_E2M1, "e5m2": FMT_E5M2, "e5m6": FMT_E5M6}
 
 _lib = None
 
@@ -53,6 +54,10 @@ def _load():
         "oracle_encode": ([i32, f32], ctypes.c_uint8),
         "oracle_encode_array": ([i32, vp, i64, vp], None),
         "oracle_decode_array": ([i32, vp, i64, vp], None),
+        "oracle_decode16": ([i32, ctypes.c_uint16], f32),
+        "oracle_encode16": ([i32, f32], ctypes.c_uint16),
+        "oracle_encode_array16": ([i32, vp, i64, vp], None),
+        "oracle_decode_array16": ([i32, vp, i64, vp], None),
         "oracle_format_max": ([i32], f32),
         "oracle_default_floor": ([i32], f32),
         "oracle_scale": ([i32, f32, f32, vp, vp], i32),
@@ -105,7 +110,11 @@ def _f32(x):
 
 
 def _code_shape(fmt, rows, cols):
-    return (rows, cols // 2) if fmt == FMT_E2M1 else (rows, cols)
+    if fmt == FMT_E2M1:
+        return (rows, cols // 2)
+    if fmt == FMT_E5M6:
+        return (rows, cols // 2 * 3)
+    return (rows, cols)
 
 
 def format_max(fmt):
@@ -117,16 +126,39 @@ def default_floor(fmt):
 
 
 def encode(fmt, y):
+    """fp32 values -> codes (uint8; uint16 for E5M6)."""
+    f = fmt_id(fmt)
     y = _f32(y)
+    if f == FMT_E5M6:
+        out = np.empty(y.shape, np.uint16)
+        _load().oracle_encode_array16(f, _ptr(y), y.size, _ptr(out))
+        return out
     out = np.empty(y.shape, np.uint8)
-    _load().oracle_encode_array(fmt_id(fmt), _ptr(y), y.size, _ptr(out))
+    _load().oracle_encode_array(f, _ptr(y), y.size, _ptr(out))
     return out
 
 
 def decode(fmt, codes):
+    f = fmt_id(fmt)
+    if f == FMT_E5M6:
+        codes = np.ascontiguousarray(codes, dtype=np.uint16)
+        out = np.empty(codes.shape, np.float32)
+        _load().oracle_decode_array16(f, _ptr(codes), codes.size, _ptr(out))
+        return out
     codes = np.ascontiguousarray(codes, dtype=np.uint8)
     out = np.empty(codes.shape, np.float32)
-    _load().oracle_decode_array(fmt_id(fmt), _ptr(codes), codes.size, _ptr(out))
+    _load().oracle_decode_array(f, _ptr(codes), codes.size, _ptr(out))
+    return out
+
+
+def unpack_e5m6(q):
+    """Packed E5M6 rows (three bytes per column pair, little-endian bit
+    stream) -> uint16 codes, one per column."""
+    q = np.ascontiguousarray(q, dtype=np.uint8)
+    t = q.reshape(q.shape[:-1] + (q.shape[-1] // 3, 3)).astype(np.uint16)
+    out = np.empty(q.shape[:-1] + (q.shape[-1] // 3 * 2,), np.uint16)
+    out[..., 0::2] = t[..., 0] | ((t[..., 1] & 0xF) << 8)
+    out[..., 1::2] = (t[..., 1] >> 4) | (t[..., 2] << 4)
     return out
 
 

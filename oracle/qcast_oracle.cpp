@@ -46,6 +46,11 @@
  *    transpose ([NEWS] item 2) is the per-channel cast of the SwiGLU values
  *    written transposed; per_channel_cast without transpose keeps the input
  *    layout and stores sf[group][channel];
+ *  - E5M6 ([SPLIT] §二 per_token_cast_to_e5m6 / cast_back_e5m6, §四 A;
+ *    [NEWS] item 2: a custom format between FP8 and FP16 for attention
+ *    gradients) is read as the IEEE-like 12-bit format with a 5-bit exponent
+ *    (bias 15) and 6 mantissa bits, maximum 65024, floor 1e-4, and its codes
+ *    are stored as a little-endian bit stream (two per three bytes);
  *  - the layouts of [SPLIT] §四 C: "TMA-aligned column-major" stores the
  *    scales group-major with the row count padded to a multiple of 4 (16
  *    bytes of fp32 or of packed words); "packed UE8M0" stores each (power of
@@ -84,9 +89,9 @@ float bf16_value(uint16_t h) { return f32_from_bits(static_cast<uint32_t>(h) << 
  * the codes 0..n-1 are ordered by magnitude, so index == code. */
 struct FormatTable {
   int n = 0;                 /* number of non-negative finite codes */
-  double value[128] = {};    /* value[code] */
-  uint8_t sign_bit = 0;      /* bit that makes a code negative */
-  uint8_t nan_code = 0;      /* positive NaN code, or the max code if none */
+  std::vector<double> value; /* value[code] */
+  uint16_t sign_bit = 0;     /* bit that makes a code negative */
+  uint16_t nan_code = 0;     /* positive NaN code, or the max code if none */
   int inf_code = -1;         /* positive infinity code, -1 if none */
   float max = 0.0f;          /* largest finite magnitude */
   float default_floor = 0.0f;
@@ -114,6 +119,7 @@ double e2m1_magnitude(int code3) {
 FormatTable make_e4m3() {
   FormatTable t;
   t.n = 127; /* 0x00 .. 0x7E; 0x7F is NaN */
+  t.value.resize(t.n);
   for (int c = 0; c < t.n; ++c) t.value[c] = e4m3_magnitude(c);
   t.sign_bit = 0x80;
   t.nan_code = 0x7F;
@@ -137,6 +143,7 @@ double e5m2_magnitude(int code7) {
 FormatTable make_e5m2() {
   FormatTable t;
   t.n = 124; /* 0x00 .. 0x7B; 0x7C is infinity, 0x7D..0x7F NaN */
+  t.value.resize(t.n);
   for (int c = 0; c < t.n; ++c) t.value[c] = e5m2_magnitude(c);
   t.sign_bit = 0x80;
   t.nan_code = 0x7F;
@@ -146,9 +153,36 @@ FormatTable make_e5m2() {
   return t;
 }
 
+/* E5M6: s eeeee mmmmmm (12 bits), exponent bias 15, the same exponent field
+ * as E5M2 and fp16 with six mantissa bits. The pages name the format and its
+ * purpose (between FP8 and FP16 in precision, for attention gradients) but not
+ * its bit layout; this reading takes the IEEE-like layout of the other 5-bit
+ * exponent formats: field 0 holds the subnormals m * 2^-20, fields 1..30 hold
+ * (1 + m/64) * 2^(e-15), field 31 is infinity (m = 0) or NaN. */
+double e5m6_magnitude(int code11) {
+  const int e = (code11 >> 6) & 0x1F;
+  const int m = code11 & 0x3F;
+  if (e == 0) return std::ldexp(static_cast<double>(m), -20);
+  return std::ldexp(1.0 + m / 64.0, e - 15);
+}
+
+FormatTable make_e5m6() {
+  FormatTable t;
+  t.n = 0x7C0; /* 0x000 .. 0x7BF; 0x7C0 is infinity, 0x7C1..0x7FF NaN */
+  t.value.resize(t.n);
+  for (int c = 0; c < t.n; ++c) t.value[c] = e5m6_magnitude(c);
+  t.sign_bit = 0x800;
+  t.nan_code = 0x7FF;
+  t.inf_code = 0x7C0;
+  t.max = static_cast<float>(t.value[t.n - 1]); /* 65024 */
+  t.default_floor = 1e-4f;
+  return t;
+}
+
 FormatTable make_e2m1() {
   FormatTable t;
   t.n = 8;
+  t.value.resize(t.n);
   for (int c = 0; c < t.n; ++c) t.value[c] = e2m1_magnitude(c);
   t.sign_bit = 0x08;
   t.nan_code = 0x07;
@@ -163,6 +197,8 @@ const FormatTable* table_for(int fmt) {
   static const FormatTable e4m3 = make_e4m3();
   static const FormatTable e2m1 = make_e2m1();
   static const FormatTable e5m2 = make_e5m2();
+  static const FormatTable e5m6 = make_e5m6();
+  if (fmt == ORACLE_FMT_E5M6) return &e5m6;
   if (fmt == ORACLE_FMT_E4M3) return &e4m3;
   if (fmt == ORACLE_FMT_E2M1) return &e2m1;
   if (fmt == ORACLE_FMT_E5M2) return &e5m2;
@@ -173,7 +209,7 @@ const FormatTable* table_for(int fmt) {
  * code, saturating at the maximum, sign attached afterwards. Comparisons are
  * made in double, where every table value, every midpoint and every fp32 is
  * exact. */
-uint8_t encode(const FormatTable& t, float y) {
+uint16_t encode(const FormatTable& t, float y) {
   if (std::isnan(y)) return t.nan_code;
   const bool negative = std::signbit(y);
   const double a = std::fabs(static_cast<double>(y));
@@ -191,11 +227,11 @@ uint8_t encode(const FormatTable& t, float y) {
     else if (a > midpoint) code = hi;
     else code = (lo % 2 == 0) ? lo : hi;
   }
-  return static_cast<uint8_t>(code | (negative ? t.sign_bit : 0));
+  return static_cast<uint16_t>(code | (negative ? t.sign_bit : 0));
 }
 
-float decode(const FormatTable& t, uint8_t code) {
-  const uint8_t magnitude_code = code & static_cast<uint8_t>(t.sign_bit - 1);
+float decode(const FormatTable& t, uint16_t code) {
+  const uint16_t magnitude_code = code & static_cast<uint16_t>(t.sign_bit - 1);
   const bool negative = (code & t.sign_bit) != 0;
   if (magnitude_code == t.inf_code) return negative ? -HUGE_VALF : HUGE_VALF;
   if (magnitude_code >= t.n) return std::nanf("");
@@ -241,12 +277,33 @@ Scale scale_from_amax(const FormatTable& t, float amax, float floor) {
 /* Code storage                                                              */
 /* ------------------------------------------------------------------------ */
 
-/* Store a code at (row, col) of an output with `cols` logical columns. E4M3
- * takes a byte per code; E2M1 packs column 2k into the low nibble and 2k+1
- * into the high nibble of byte k of the row. */
-void put_code(int fmt, uint8_t* q, int64_t cols, int64_t row, int64_t col, uint8_t code) {
-  if (fmt != ORACLE_FMT_E2M1) {
-    q[row * cols + col] = code;
+/* Formats whose codes are packed two columns at a time (whole bytes per
+ * column pair), so rows need an even number of columns. */
+bool pairs(int fmt) { return fmt == ORACLE_FMT_E2M1 || fmt == ORACLE_FMT_E5M6; }
+
+/* Bytes of one row of codes with `cols` columns. */
+int64_t code_row_bytes(int fmt, int64_t cols) {
+  if (fmt == ORACLE_FMT_E2M1) return cols / 2;
+  if (fmt == ORACLE_FMT_E5M6) return cols / 2 * 3;
+  return cols;
+}
+
+/* Store a code at (row, col) of an output with `cols` logical columns. The
+ * 8-bit formats take a byte per code; E2M1 packs column 2k into the low
+ * nibble and 2k+1 into the high nibble of byte k of the row; E5M6 writes the
+ * row as a little-endian bit stream of 12-bit codes (column j in bits
+ * 12j .. 12j+11, lowest bit first: two codes per three bytes). */
+void put_code(int fmt, uint8_t* q, int64_t cols, int64_t row, int64_t col, uint16_t code) {
+  if (fmt == ORACLE_FMT_E5M6) {
+    uint8_t* r = q + row * code_row_bytes(fmt, cols);
+    for (int b = 0; b < 12; ++b) {
+      const int64_t bit = 12 * col + b;
+      const uint8_t mask = static_cast<uint8_t>(1u << (bit % 8));
+      if ((code >> b) & 1u) r[bit / 8] |= mask;
+      else r[bit / 8] &= static_cast<uint8_t>(~mask);
+    }
+  } else if (fmt != ORACLE_FMT_E2M1) {
+    q[row * cols + col] = static_cast<uint8_t>(code);
   } else {
     uint8_t& b = q[row * (cols / 2) + col / 2];
     if (col % 2 == 0) b = static_cast<uint8_t>((b & 0xF0) | (code & 0x0F));
@@ -254,7 +311,16 @@ void put_code(int fmt, uint8_t* q, int64_t cols, int64_t row, int64_t col, uint8
   }
 }
 
-uint8_t get_code(int fmt, const uint8_t* q, int64_t cols, int64_t row, int64_t col) {
+uint16_t get_code(int fmt, const uint8_t* q, int64_t cols, int64_t row, int64_t col) {
+  if (fmt == ORACLE_FMT_E5M6) {
+    const uint8_t* r = q + row * code_row_bytes(fmt, cols);
+    uint16_t code = 0;
+    for (int b = 0; b < 12; ++b) {
+      const int64_t bit = 12 * col + b;
+      code = static_cast<uint16_t>(code | (((r[bit / 8] >> (bit % 8)) & 1u) << b));
+    }
+    return code;
+  }
   if (fmt != ORACLE_FMT_E2M1) return q[row * cols + col];
   const uint8_t b = q[row * (cols / 2) + col / 2];
   return (col % 2 == 0) ? (b & 0x0F) : (b >> 4);
@@ -363,7 +429,7 @@ void per_channel_f32(const float* x, int64_t rows, int64_t cols, int fmt, int gr
       }
       const Scale s = scale_from_amax(t, amax, floor);
       for (int64_t tk = g * group; tk < (g + 1) * group; ++tk) {
-        const uint8_t code = encode(t, x[tk * cols + c] * s.sf_inv);
+        const uint16_t code = encode(t, x[tk * cols + c] * s.sf_inv);
         if (transposed) put_code(fmt, q, rows, c, tk, code);
         else put_code(fmt, q, cols, tk, c, code);
       }
@@ -408,23 +474,51 @@ extern "C" {
 
 int oracle_version(void) { return 1; }
 
+/* The byte forms serve the formats whose codes fit a byte; E5M6 codes go
+ * through the 16-bit forms. */
+const FormatTable* byte_table_for(int fmt) {
+  return fmt == ORACLE_FMT_E5M6 ? nullptr : table_for(fmt);
+}
+
 float oracle_decode(int fmt, uint8_t code) {
-  const FormatTable* t = table_for(fmt);
+  const FormatTable* t = byte_table_for(fmt);
   return t ? decode(*t, code) : std::nanf("");
 }
 
 uint8_t oracle_encode(int fmt, float y) {
+  const FormatTable* t = byte_table_for(fmt);
+  return t ? static_cast<uint8_t>(encode(*t, y)) : 0;
+}
+
+void oracle_encode_array(int fmt, const float* y, int64_t n, uint8_t* codes) {
+  const FormatTable* t = byte_table_for(fmt);
+  if (!t) return;
+  for (int64_t i = 0; i < n; ++i) codes[i] = static_cast<uint8_t>(encode(*t, y[i]));
+}
+
+void oracle_decode_array(int fmt, const uint8_t* codes, int64_t n, float* out) {
+  const FormatTable* t = byte_table_for(fmt);
+  if (!t) return;
+  for (int64_t i = 0; i < n; ++i) out[i] = decode(*t, codes[i]);
+}
+
+float oracle_decode16(int fmt, uint16_t code) {
+  const FormatTable* t = table_for(fmt);
+  return t ? decode(*t, code) : std::nanf("");
+}
+
+uint16_t oracle_encode16(int fmt, float y) {
   const FormatTable* t = table_for(fmt);
   return t ? encode(*t, y) : 0;
 }
 
-void oracle_encode_array(int fmt, const float* y, int64_t n, uint8_t* codes) {
+void oracle_encode_array16(int fmt, const float* y, int64_t n, uint16_t* codes) {
   const FormatTable* t = table_for(fmt);
   if (!t) return;
   for (int64_t i = 0; i < n; ++i) codes[i] = encode(*t, y[i]);
 }
 
-void oracle_decode_array(int fmt, const uint8_t* codes, int64_t n, float* out) {
+void oracle_decode_array16(int fmt, const uint16_t* codes, int64_t n, float* out) {
   const FormatTable* t = table_for(fmt);
   if (!t) return;
   for (int64_t i = 0; i < n; ++i) out[i] = decode(*t, codes[i]);
@@ -456,7 +550,7 @@ int oracle_per_token_f32(const float* x, int64_t rows, int64_t cols, int fmt, in
   const int rc = check_common(x, q, sf, fmt, group);
   if (rc != ORACLE_OK) return rc;
   if (rows < 0 || cols < 0 || cols % group != 0) return ORACLE_ERR_SHAPE;
-  if (fmt == ORACLE_FMT_E2M1 && group % 2 != 0) return ORACLE_ERR_GROUP;
+  if (pairs(fmt) && group % 2 != 0) return ORACLE_ERR_GROUP;
   per_token_rows(x, rows, cols, fmt, group, floor_for(*table_for(fmt), clamp_min), q, sf);
   return ORACLE_OK;
 }
@@ -466,10 +560,10 @@ int oracle_per_token(const uint16_t* x, int64_t rows, int64_t cols, int fmt, int
   const int rc = check_common(x, q, sf, fmt, group);
   if (rc != ORACLE_OK) return rc;
   if (rows < 0 || cols < 0 || cols % group != 0) return ORACLE_ERR_SHAPE;
-  if (fmt == ORACLE_FMT_E2M1 && group % 2 != 0) return ORACLE_ERR_GROUP;
+  if (pairs(fmt) && group % 2 != 0) return ORACLE_ERR_GROUP;
   const float floor = floor_for(*table_for(fmt), clamp_min);
   std::vector<float> row(static_cast<size_t>(cols));
-  const int64_t code_bytes = (fmt == ORACLE_FMT_E2M1) ? cols / 2 : cols;
+  const int64_t code_bytes = code_row_bytes(fmt, cols);
   const int64_t groups = cols / group;
   for (int64_t r = 0; r < rows; ++r) {
     for (int64_t c = 0; c < cols; ++c) row[c] = bf16_value(x[r * cols + c]);
@@ -502,10 +596,10 @@ int oracle_swiglu_per_token(const uint16_t* h, int64_t rows, int64_t cols, const
   const int rc = check_common(h, q, sf, fmt, group);
   if (rc != ORACLE_OK) return rc;
   if (rows < 0 || cols < 0 || cols % group != 0) return ORACLE_ERR_SHAPE;
-  if (fmt == ORACLE_FMT_E2M1 && group % 2 != 0) return ORACLE_ERR_GROUP;
+  if (pairs(fmt) && group % 2 != 0) return ORACLE_ERR_GROUP;
   const float floor = floor_for(*table_for(fmt), clamp_min);
   std::vector<float> v(static_cast<size_t>(cols));
-  const int64_t code_bytes = (fmt == ORACLE_FMT_E2M1) ? cols / 2 : cols;
+  const int64_t code_bytes = code_row_bytes(fmt, cols);
   const int64_t groups = cols / group;
   for (int64_t r = 0; r < rows; ++r) {
     oracle_swiglu_values(h + r * 2 * cols, 1, cols, w ? w + r : nullptr, v.data());
@@ -519,7 +613,7 @@ int oracle_per_block(const uint16_t* x, int64_t rows, int64_t cols, int fmt, int
   const int rc = check_common(x, q, sf, fmt, block);
   if (rc != ORACLE_OK) return rc;
   if (rows < 0 || cols < 0 || rows % block != 0 || cols % block != 0) return ORACLE_ERR_SHAPE;
-  if (fmt == ORACLE_FMT_E2M1 && block % 2 != 0) return ORACLE_ERR_GROUP;
+  if (pairs(fmt) && block % 2 != 0) return ORACLE_ERR_GROUP;
   const FormatTable& t = *table_for(fmt);
   const float floor = floor_for(t, clamp_min);
   const int64_t brows = rows / block, bcols = cols / block;
@@ -548,7 +642,7 @@ int oracle_per_channel_T(const uint16_t* x, int64_t rows, int64_t cols, int fmt,
   const int rc = check_common(x, qT, sf, fmt, group);
   if (rc != ORACLE_OK) return rc;
   if (rows < 0 || cols < 0 || rows % group != 0) return ORACLE_ERR_SHAPE;
-  if (fmt == ORACLE_FMT_E2M1 && group % 2 != 0) return ORACLE_ERR_GROUP;
+  if (pairs(fmt) && group % 2 != 0) return ORACLE_ERR_GROUP;
   std::vector<float> xf(static_cast<size_t>(rows * cols));
   for (int64_t i = 0; i < rows * cols; ++i) xf[i] = bf16_value(x[i]);
   per_channel_f32(xf.data(), rows, cols, fmt, group, floor_for(*table_for(fmt), clamp_min), true,
@@ -561,7 +655,7 @@ int oracle_per_channel(const uint16_t* x, int64_t rows, int64_t cols, int fmt, i
   const int rc = check_common(x, q, sf, fmt, group);
   if (rc != ORACLE_OK) return rc;
   if (rows < 0 || cols < 0 || rows % group != 0) return ORACLE_ERR_SHAPE;
-  if (fmt == ORACLE_FMT_E2M1 && cols % 2 != 0) return ORACLE_ERR_SHAPE;
+  if (pairs(fmt) && cols % 2 != 0) return ORACLE_ERR_SHAPE;
   std::vector<float> xf(static_cast<size_t>(rows * cols));
   for (int64_t i = 0; i < rows * cols; ++i) xf[i] = bf16_value(x[i]);
   per_channel_f32(xf.data(), rows, cols, fmt, group, floor_for(*table_for(fmt), clamp_min), false,
@@ -587,10 +681,10 @@ int oracle_per_token_sf(const uint16_t* x, int64_t rows, int64_t cols, int fmt, 
   int rc = check_common(x, q, sf, fmt, group);
   if (rc != ORACLE_OK) return rc;
   if (rows < 0 || cols < 0 || cols % group != 0) return ORACLE_ERR_SHAPE;
-  if (fmt == ORACLE_FMT_E2M1 && group % 2 != 0) return ORACLE_ERR_GROUP;
+  if (pairs(fmt) && group % 2 != 0) return ORACLE_ERR_GROUP;
   if ((rc = check_sf_flags(sf_flags, cols, group)) != ORACLE_OK) return rc;
   const float floor = floor_for(*table_for(fmt), clamp_min);
-  const int64_t code_bytes = (fmt == ORACLE_FMT_E2M1) ? cols / 2 : cols;
+  const int64_t code_bytes = code_row_bytes(fmt, cols);
   std::vector<float> row(static_cast<size_t>(cols));
   for (int64_t r = 0; r < rows; ++r) {
     for (int64_t c = 0; c < cols; ++c) row[c] = bf16_value(x[r * cols + c]);
@@ -605,10 +699,10 @@ int oracle_swiglu_per_token_sf(const uint16_t* h, int64_t rows, int64_t cols, co
   int rc = check_common(h, q, sf, fmt, group);
   if (rc != ORACLE_OK) return rc;
   if (rows < 0 || cols < 0 || cols % group != 0) return ORACLE_ERR_SHAPE;
-  if (fmt == ORACLE_FMT_E2M1 && group % 2 != 0) return ORACLE_ERR_GROUP;
+  if (pairs(fmt) && group % 2 != 0) return ORACLE_ERR_GROUP;
   if ((rc = check_sf_flags(sf_flags, cols, group)) != ORACLE_OK) return rc;
   const float floor = floor_for(*table_for(fmt), clamp_min);
-  const int64_t code_bytes = (fmt == ORACLE_FMT_E2M1) ? cols / 2 : cols;
+  const int64_t code_bytes = code_row_bytes(fmt, cols);
   std::vector<float> v(static_cast<size_t>(cols));
   for (int64_t r = 0; r < rows; ++r) {
     oracle_swiglu_values(h + r * 2 * cols, 1, cols, w ? w + r : nullptr, v.data());
@@ -623,10 +717,10 @@ int oracle_swiglu_per_token_ex(const uint16_t* h, int64_t rows, int64_t cols, co
   int rc = check_common(h, q, sf, fmt, group);
   if (rc != ORACLE_OK) return rc;
   if (rows < 0 || cols < 0 || cols % group != 0) return ORACLE_ERR_SHAPE;
-  if (fmt == ORACLE_FMT_E2M1 && group % 2 != 0) return ORACLE_ERR_GROUP;
+  if (pairs(fmt) && group % 2 != 0) return ORACLE_ERR_GROUP;
   if ((rc = check_sf_flags(sf_flags, cols, group)) != ORACLE_OK) return rc;
   const float floor = floor_for(*table_for(fmt), clamp_min);
-  const int64_t code_bytes = (fmt == ORACLE_FMT_E2M1) ? cols / 2 : cols;
+  const int64_t code_bytes = code_row_bytes(fmt, cols);
   std::vector<float> v(static_cast<size_t>(cols));
   for (int64_t r = 0; r < rows; ++r) {
     swiglu_row(h + r * 2 * cols, cols, w ? w[r] : 1.0f, w != nullptr, swiglu_clamp, v.data(),
@@ -674,7 +768,7 @@ int oracle_swiglu_backward_per_token(const uint16_t* h, const uint16_t* dv, int6
   if (rc != ORACLE_OK) return rc;
   if (!dv) return ORACLE_ERR_NULL;
   if (rows < 0 || cols < 0 || cols % group != 0) return ORACLE_ERR_SHAPE;
-  if (fmt == ORACLE_FMT_E2M1) return ORACLE_ERR_FORMAT;
+  if (fmt != ORACLE_FMT_E4M3 && fmt != ORACLE_FMT_E5M2) return ORACLE_ERR_FORMAT;
   std::vector<float> vals(static_cast<size_t>(rows * 2 * cols));
   oracle_swiglu_backward_values(h, dv, rows, cols, w, swiglu_clamp, vals.data());
   per_token_rows(vals.data(), rows, 2 * cols, fmt, group, floor_for(*table_for(fmt), clamp_min),
@@ -688,7 +782,7 @@ int oracle_swiglu_per_channel_T(const uint16_t* h, int64_t rows, int64_t cols, c
   const int rc = check_common(h, qT, sf, fmt, group);
   if (rc != ORACLE_OK) return rc;
   if (rows < 0 || cols < 0 || rows % group != 0) return ORACLE_ERR_SHAPE;
-  if (fmt == ORACLE_FMT_E2M1 && group % 2 != 0) return ORACLE_ERR_GROUP;
+  if (pairs(fmt) && group % 2 != 0) return ORACLE_ERR_GROUP;
   std::vector<float> v(static_cast<size_t>(rows * cols));
   oracle_swiglu_values_ex(h, rows, cols, w, swiglu_clamp, v.data(), nullptr);
   per_channel_f32(v.data(), rows, cols, fmt, group, floor_for(*table_for(fmt), clamp_min), true,

@@ -8,9 +8,10 @@
  * fallback for it.
  *
  * All pointers are HOST pointers, row-major and contiguous. Inputs are bf16
- * bit patterns (uint16_t). Codes are bytes (E4M3) or packed nibbles (E2M1:
- * byte k of a row holds column 2k in its low nibble, 2k+1 in its high nibble).
- * Scales are fp32.
+ * bit patterns (uint16_t). Codes are bytes (E4M3, E5M2), packed nibbles
+ * (E2M1: byte k of a row holds column 2k in its low nibble, 2k+1 in its high
+ * nibble) or a little-endian bit stream of 12-bit codes (E5M6: column j in
+ * bits 12j..12j+11 of the row, three bytes per column pair). Scales are fp32.
  *
  * Every cast returns ORACLE_OK or an error code; on an error nothing is
  * written.
@@ -33,7 +34,7 @@ enum {
   ORACLE_ERR_FPENV = 7 /* FTZ/DAZ set or rounding mode not nearest */
 };
 
-enum { ORACLE_FMT_E4M3 = 1, ORACLE_FMT_E2M1 = 2, ORACLE_FMT_E5M2 = 3 };
+enum { ORACLE_FMT_E4M3 = 1, ORACLE_FMT_E2M1 = 2, ORACLE_FMT_E5M2 = 3, ORACLE_FMT_E5M6 = 4 };
 enum { ORACLE_OUT_BF16 = 1, ORACLE_OUT_F32 = 2 };
 /* Scale-factor layout flags (see oracle_per_token_sf). */
 enum { ORACLE_SF_ROUND_POW2 = 1, ORACLE_SF_COL_MAJOR = 2, ORACLE_SF_PACKED_UE8M0 = 4 };
@@ -41,10 +42,16 @@ enum { ORACLE_SF_ROUND_POW2 = 1, ORACLE_SF_COL_MAJOR = 2, ORACLE_SF_PACKED_UE8M0
 int oracle_version(void);
 
 /* ---- format codecs (one element at a time, and array forms) ---- */
+/* Byte codes (E4M3, E5M2, E2M1; E5M6 is refused: NaN / 0 / nothing written). */
 float oracle_decode(int fmt, uint8_t code);     /* NaN for E4M3 0x7F/0xFF */
 uint8_t oracle_encode(int fmt, float y);        /* RNE, saturating, signed zero */
 void oracle_encode_array(int fmt, const float* y, int64_t n, uint8_t* codes);
 void oracle_decode_array(int fmt, const uint8_t* codes, int64_t n, float* out);
+/* 16-bit codes, every format (E5M6: sign bit 11, exponent bits 6-10). */
+float oracle_decode16(int fmt, uint16_t code);
+uint16_t oracle_encode16(int fmt, float y);
+void oracle_encode_array16(int fmt, const float* y, int64_t n, uint16_t* codes);
+void oracle_decode_array16(int fmt, const uint16_t* codes, int64_t n, float* out);
 float oracle_format_max(int fmt);
 float oracle_default_floor(int fmt);
 
