@@ -73,7 +73,21 @@ typedef enum {
   QCAST_ERR_VALUE = 8   /* a scalar argument is out of range (e.g. a NaN clamp) */
 } qcast_status;
 
-typedef enum { QCAST_FMT_E4M3 = 1, QCAST_FMT_E2M1 = 2, QCAST_FMT_E5M2 = 3 } qcast_fmt;
+/*
+ * QCAST_FMT_E5M6 ([SPLIT] §二 per_token_cast_to_e5m6 / cast_back_e5m6; [NEWS]
+ * item 2, a format between FP8 and FP16 for attention gradients). The pages
+ * give no bit layout; it is read as the IEEE-like 12-bit format with a 5-bit
+ * exponent (bias 15) and 6 mantissa bits -- the top 12 bits of an fp16
+ * pattern -- maximum 65024, floor 1e-4, codes saturating. A row of codes is
+ * a little-endian bit stream, column j in bits 12j .. 12j+11: two codes per
+ * three bytes, [rows, cols/2*3] bytes.
+ */
+typedef enum {
+  QCAST_FMT_E4M3 = 1,
+  QCAST_FMT_E2M1 = 2,
+  QCAST_FMT_E5M2 = 3,
+  QCAST_FMT_E5M6 = 4
+} qcast_fmt;
 
 /*
  * Scale-factor layout options of the *_sf entry points (the cast config of
@@ -107,10 +121,10 @@ typedef enum { QCAST_OUT_BF16 = 1, QCAST_OUT_F32 = 2 } qcast_out_dtype;
  * One scale per run of `group` consecutive elements of a row (the page's
  * num_per_channels).
  *   x     [rows, cols] bf16.
- *   fmt   QCAST_FMT_E4M3, QCAST_FMT_E5M2 or QCAST_FMT_E2M1.
+ *   fmt   QCAST_FMT_E4M3, QCAST_FMT_E5M2, QCAST_FMT_E2M1 or QCAST_FMT_E5M6.
  *   q     E4M3 / E5M2: [rows, cols] bytes.  E2M1: [rows, cols/2] bytes,
  *         column 2k in the low nibble of byte k and column 2k+1 in its high
- *         nibble.
+ *         nibble.  E5M6: [rows, cols/2*3] bytes (see QCAST_FMT_E5M6).
  *   sf    [rows, cols/group] fp32.
  *   group 32, 64 or 128; cols % group == 0.
  *   clamp_min  <= 0 selects the format's default floor.
@@ -251,7 +265,8 @@ QCAST_API int qcast_per_channel(const void* x, int64_t rows, int64_t cols, int f
  * cast_back: dequantize per-token codes ([SPLIT] §二 cast_back).
  *   out[r][c] = decode(q[r][c]) * sf[r][c/group], one fp32 product, rounded
  *   to bf16 (nearest even) when out_dtype is QCAST_OUT_BF16.
- *   q    codes as qcast_per_token writes them for `fmt` and `group`.
+ *   q    codes as qcast_per_token writes them for `fmt` and `group` (any of
+ *        the four formats; E5M6 is cast_back_e5m6 of [SPLIT] §二).
  *   sf   [rows, cols/group] fp32.
  *   out  [rows, cols] bf16 (QCAST_OUT_BF16) or fp32 (QCAST_OUT_F32).
  *   group 32, 64 or 128; cols % group == 0.

@@ -8,7 +8,9 @@ missing library raises ``QcastError``.
 
 Outputs: E4M3 codes as ``torch.float8_e4m3fn`` and E5M2 codes as
 ``torch.float8_e5m2`` (one byte per code), E2M1 codes as ``torch.uint8`` with
-two codes per byte (low nibble = even column), scales as ``torch.float32``.
+two codes per byte (low nibble = even column), E5M6 codes as ``torch.uint8``
+with two 12-bit codes per three bytes (a little-endian bit stream), scales as
+``torch.float32``.
 
 ``per_token_cast(x, fmt='e4m3', num_per_channels=128) -> (out, out_sf)``
 mirrors the call shown in the quick start of the page
@@ -16,7 +18,7 @@ mirrors the call shown in the quick start of the page
 """
 import torch
 
-from ._lib import (FMT_E2M1, FMT_E4M3, FMT_E5M2, OUT_BF16, OUT_F32, SF_COL_MAJOR,
+from ._lib import (FMT_E2M1, FMT_E4M3, FMT_E5M2, FMT_E5M6, OUT_BF16, OUT_F32, SF_COL_MAJOR,
                    SF_PACKED_UE8M0, SF_ROUND_POW2, QcastError, check, fmt_id, load)
 
 __all__ = ["qcast_per_token", "qcast_e2m1", "qcast_swiglu_per_token", "qcast_per_block",
@@ -27,7 +29,7 @@ __all__ = ["qcast_per_token", "qcast_e2m1", "qcast_swiglu_per_token", "qcast_per
            "SF_PACKED_UE8M0", "qcast_abi_version", "qcast_set_num_cus", "qcast_bench_copy",
            "qcast_bench_check_scale",
            "per_token_cast",
-           "QcastError", "FMT_E4M3", "FMT_E2M1", "FMT_E5M2"]
+           "QcastError", "FMT_E4M3", "FMT_E2M1", "FMT_E5M2", "FMT_E5M6", "code_shape"]
 
 
 def _bf16_input(x, name):
@@ -76,6 +78,16 @@ def _counter(clamp_count, device):
     return clamp_count.data_ptr()
 
 
+def code_shape(fmt, rows, cols):
+    """Shape of the uint8/float8 code tensor of a per-token cast."""
+    f = fmt_id(fmt)
+    if f == FMT_E2M1:
+        return (rows, cols // 2)
+    if f == FMT_E5M6:
+        return (rows, cols // 2 * 3)
+    return (rows, cols)
+
+
 def _code_dtype(f):
     return {FMT_E4M3: torch.float8_e4m3fn, FMT_E5M2: torch.float8_e5m2}.get(f, torch.uint8)
 
@@ -86,7 +98,7 @@ def qcast_per_token(x, fmt="e4m3", group=128, clamp_min=0.0, out=None, out_sf=No
     f = fmt_id(fmt)
     x = _bf16_input(x, "x")
     rows, cols = x.shape
-    qshape = (rows, cols // 2) if f == FMT_E2M1 else (rows, cols)
+    qshape = code_shape(f, rows, cols)
     out = _out(out, qshape, _code_dtype(f), x.device, "out")
     out_sf = _out(out_sf, (rows, cols // group if group > 0 else 0), torch.float32, x.device,
                   "out_sf")
@@ -115,7 +127,7 @@ def qcast_per_token_sf(x, fmt="e4m3", group=128, clamp_min=0.0, sf_flags=0, out=
     f = fmt_id(fmt)
     x = _bf16_input(x, "x")
     rows, cols = x.shape
-    qshape = (rows, cols // 2) if f == FMT_E2M1 else (rows, cols)
+    qshape = code_shape(f, rows, cols)
     out = _out(out, qshape, _code_dtype(f), x.device, "out")
     shape, dt = sf_layout_shape(rows, cols, group if group > 0 else 1, sf_flags)
     out_sf = _out(out_sf, shape, dt, x.device, "out_sf")
@@ -322,7 +334,7 @@ def qcast_cast_back(q, sf, fmt="e4m3", group=128, out_dtype=torch.bfloat16, out=
     if q.element_size() != 1:
         raise QcastError(2, "q must hold one byte per element")
     rows = q.shape[0]
-    cols = q.shape[1] * 2 if f == FMT_E2M1 else q.shape[1]
+    cols = {FMT_E2M1: q.shape[1] * 2, FMT_E5M6: q.shape[1] // 3 * 2}.get(f, q.shape[1])
     if out_dtype not in (torch.bfloat16, torch.float32):
         raise QcastError(4, "out_dtype must be torch.bfloat16 or torch.float32")
     if sf.dtype != torch.float32 or tuple(sf.shape) != (rows, cols // group if group > 0 else 0) \

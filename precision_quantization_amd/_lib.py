@@ -12,12 +12,13 @@ QCAST_OK = 0
 FMT_E4M3 = 1
 FMT_E2M1 = 2
 FMT_E5M2 = 3
+FMT_E5M6 = 4
 OUT_BF16 = 1
 OUT_F32 = 2
 SF_ROUND_POW2 = 1
 SF_COL_MAJOR = 2
 SF_PACKED_UE8M0 = 4
-_FMT = {"e4m3": FMT_E4M3, "e2m1": FMT_E2M1, "e5m2": FMT_E5M2}
+_FMT = {"e4m3": FMT_E4M3, "e2m1": FMT_E2M1, "e5m2": FMT_E5M2, "e5m6": FMT_E5M6}
 
 _lib = None
 

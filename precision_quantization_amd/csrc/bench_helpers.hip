@@ -79,7 +79,8 @@ __global__ __launch_bounds__(kThreads) void check_scale_kernel(uint32_t first, u
 
 extern "C" int qcast_bench_check_scale(int fmt, uint32_t first, uint32_t last, uint32_t* counts,
                                        void* stream) {
-  if (fmt != QCAST_FMT_E4M3 && fmt != QCAST_FMT_E2M1 && fmt != QCAST_FMT_E5M2)
+  if (fmt != QCAST_FMT_E4M3 && fmt != QCAST_FMT_E2M1 && fmt != QCAST_FMT_E5M2 &&
+      fmt != QCAST_FMT_E5M6)
     return QCAST_ERR_FORMAT;
   if (first > last || last > 0x7f7fffffu) return QCAST_ERR_SHAPE;
   if (!counts) return QCAST_ERR_NULL;
@@ -91,8 +92,11 @@ extern "C" int qcast_bench_check_scale(int fmt, uint32_t first, uint32_t last, u
   else if (fmt == QCAST_FMT_E2M1)
     hipLaunchKernelGGL(qcast::check_scale_kernel<qcast::kE2M1>, dim3(QCAST_CHECK_BLOCKS),
                        dim3(qcast::kThreads), 0, s, first, last, counts);
-  else
+  else if (fmt == QCAST_FMT_E5M2)
     hipLaunchKernelGGL(qcast::check_scale_kernel<qcast::kE5M2>, dim3(QCAST_CHECK_BLOCKS),
+                       dim3(qcast::kThreads), 0, s, first, last, counts);
+  else
+    hipLaunchKernelGGL(qcast::check_scale_kernel<qcast::kE5M6>, dim3(QCAST_CHECK_BLOCKS),
                        dim3(qcast::kThreads), 0, s, first, last, counts);
   return hipGetLastError() == hipSuccess ? QCAST_OK : QCAST_ERR_LAUNCH;
 }

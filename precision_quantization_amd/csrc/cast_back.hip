@@ -8,9 +8,11 @@
 // them ("DeepSeek开源TileKernels：用Python写的GPU算子逼近硬件性能上限", §3.2).
 //
 // gfx950 design. The per-token stream walked backwards: one lane per 8 codes
-// (8 bytes of E4M3 / E5M2, 4 bytes of E2M1), decoded exactly by the hardware
-// (v_cvt_pk_f32_fp8 / v_cvt_pk_f32_bf8 / v_cvt_scalef32_pk_f32_fp4 with
-// scale 1), multiplied by the group's scale (the lanes of a group read the
+// (8 bytes of E4M3 / E5M2, 4 bytes of E2M1, 12 bytes of E5M6), decoded
+// exactly by the hardware (v_cvt_pk_f32_fp8 / v_cvt_pk_f32_bf8 /
+// v_cvt_scalef32_pk_f32_fp4 with scale 1; v_cvt_f32_f16 of the E5M6 code
+// shifted to the top of an fp16 pattern -- cast_back_e5m6 of the same
+// table), multiplied by the group's scale (the lanes of a group read the
 // same scale word), and written as 8 bf16 (one 16-byte store, converted with
 // v_cvt_pk_bf16_f32) or 8 fp32 (two 16-byte stores). One workgroup per
 // 256 * kUnroll chunks.
@@ -27,10 +29,26 @@ constexpr int kUnroll = QCAST_CB_UNROLL;
 
 typedef float f32x2 __attribute__((ext_vector_type(2)));
 
-// Eight codes -> eight exact fp32 values.
+// One E5M6 code (low 12 bits of c) -> fp32: it is the top of an fp16
+// pattern, so v_cvt_f32_f16 of c << 4 is exact.
+__device__ __forceinline__ float e5m6_value(uint32_t c) {
+  return (float)__builtin_bit_cast(_Float16, (uint16_t)((c << 4) & 0xfff0u));
+}
+
+// Eight codes -> eight exact fp32 values (E5M6: 96 bits in codes.x, .y, .z).
 template <int kFmt>
-__device__ __forceinline__ void decode8(u32x2 codes, float v[8]) {
-  if constexpr (kFmt == kE2M1) {
+__device__ __forceinline__ void decode8(u32x4 codes, float v[8]) {
+  if constexpr (kFmt == kE5M6) {
+    const uint32_t w0 = codes.x, w1 = codes.y, w2 = codes.z;
+    v[0] = e5m6_value(w0);
+    v[1] = e5m6_value(w0 >> 12);
+    v[2] = e5m6_value((w0 >> 24) | (w1 << 8));
+    v[3] = e5m6_value(w1 >> 4);
+    v[4] = e5m6_value(w1 >> 16);
+    v[5] = e5m6_value((w1 >> 28) | (w2 << 4));
+    v[6] = e5m6_value(w2 >> 8);
+    v[7] = e5m6_value(w2 >> 20);
+  } else if constexpr (kFmt == kE2M1) {
     const uint32_t w = codes.x;  // 8 nibbles; the byte selector is an immediate
     const f32x2 p0 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(w, 1.0f, 0);
     const f32x2 p1 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(w, 1.0f, 1);
@@ -70,17 +88,24 @@ __global__ __launch_bounds__(kThreads) void cast_back_kernel(const uint8_t* __re
                                                              int64_t nchunks,
                                                              void* __restrict__ out) {
   const int64_t base = (int64_t)blockIdx.x * kThreads * kUnroll + threadIdx.x;
-  u32x2 codes[kUnroll];
+  u32x4 codes[kUnroll];
   float s[kUnroll];
 #pragma unroll
   for (int u = 0; u < kUnroll; ++u) {
     const int64_t c = base + (int64_t)u * kThreads;
     if (c < nchunks) {
+      codes[u] = u32x4{0u, 0u, 0u, 0u};
       if constexpr (kFmt == kE2M1) {
         codes[u].x = load_stream(reinterpret_cast<const uint32_t*>(q) + c);
-        codes[u].y = 0u;
+      } else if constexpr (kFmt == kE5M6) {
+        const uint32_t* p = reinterpret_cast<const uint32_t*>(q) + 3 * c;
+        codes[u].x = load_stream(p);
+        codes[u].y = load_stream(p + 1);
+        codes[u].z = load_stream(p + 2);
       } else {
-        codes[u] = load_stream(reinterpret_cast<const u32x2*>(q) + c);
+        const u32x2 w = load_stream(reinterpret_cast<const u32x2*>(q) + c);
+        codes[u].x = w.x;
+        codes[u].y = w.y;
       }
       s[u] = sf[c / kLanes];
     }
@@ -146,6 +171,7 @@ hipError_t launch_cast_back(const void* q, const float* sf, int64_t rows, int64_
     case kE4M3: return launch_fmt<kE4M3>(q, sf, nchunks, group, out_bf16, out, stream);
     case kE5M2: return launch_fmt<kE5M2>(q, sf, nchunks, group, out_bf16, out, stream);
     case kE2M1: return launch_fmt<kE2M1>(q, sf, nchunks, group, out_bf16, out, stream);
+    case kE5M6: return launch_fmt<kE5M6>(q, sf, nchunks, group, out_bf16, out, stream);
   }
   return hipErrorInvalidValue;
 }

@@ -1,10 +1,13 @@
-// per_token.hip -- per-token cast of bf16 rows to E4M3, E5M2 or packed E2M1.
+// per_token.hip -- per-token cast of bf16 rows to E4M3, E5M2, packed E2M1 or
+// packed E5M6.
 //
 // Operation: the per-token cast of the walk-through page
 // "DeepSeek开源TileKernels：用Python写的GPU算子逼近硬件性能上限", quick start and
 // §3.2 (abs-max over each run of num_per_channels elements of a row, scale
 // and inverse, codes of x * inverse); E2M1 output per §3.1 (float4_e2m1fn),
-// E5M2 from the format list of "TileKernels 与 DeepGEMM 的分界线", §四 A.
+// E5M2 from the format list of "TileKernels 与 DeepGEMM 的分界线", §四 A, and
+// E5M6 from per_token_cast_to_e5m6 of the operator table of the same page,
+// §二 (12-bit codes, two per three bytes).
 //
 // gfx950 design. A contiguous [rows, cols] matrix with cols % G == 0 is one
 // flat stream of groups: group k is elements [kG, kG + G) and owns scale
@@ -14,7 +17,8 @@
 // 2-4 step DPP reduction in registers and no LDS is touched. Each lane then
 // forms the scale, multiplies its 8 values and converts them with the
 // hardware pack-converts: 8 E4M3 bytes (one dwordx2 store) or 8 E2M1 nibbles
-// (one dword store). The first lane of each group stores the scale.
+// (one dword store); E5M6 codes are formed from the fp32 bits (no hardware
+// converter) and stored as 12 bytes. The first lane of each group stores the scale.
 // A workgroup keeps kUnroll chunks per lane in flight before using any.
 #include "qcast_device.h"
 #include "qcast_kernels.h"
@@ -63,6 +67,12 @@ __global__ __launch_bounds__(kThreads) void per_token_kernel(
         for (int i = 0; i < 8; ++i) y[i] = v[i] * s.inv;
         if constexpr (kFmt == kE2M1) {
           store_stream(reinterpret_cast<uint32_t*>(q) + c, e2m1x8(y));
+        } else if constexpr (kFmt == kE5M6) {
+          const E5M6x8 p = e5m6x8(y);
+          uint32_t* o = reinterpret_cast<uint32_t*>(q) + 3 * c;
+          store_stream(o, p.w0);
+          store_stream(o + 1, p.w1);
+          store_stream(o + 2, p.w2);
         } else {
           u32x2 out;
           out.x = fp8x4<kFmt>(y[0], y[1], y[2], y[3]);
@@ -116,6 +126,7 @@ hipError_t launch_per_token(const void* x, int64_t rows, int64_t cols, int fmt, 
     case kE4M3: return launch_fmt<kE4M3>(x, nchunks, group, floor, q, sf, lay, stream, caps);
     case kE2M1: return launch_fmt<kE2M1>(x, nchunks, group, floor, q, sf, lay, stream, caps);
     case kE5M2: return launch_fmt<kE5M2>(x, nchunks, group, floor, q, sf, lay, stream, caps);
+    case kE5M6: return launch_fmt<kE5M6>(x, nchunks, group, floor, q, sf, lay, stream, caps);
   }
   return hipErrorInvalidValue;
 }

@@ -3,8 +3,8 @@
 //
 // Floors ("DeepSeek开源TileKernels：用Python写的GPU算子逼近硬件性能上限", §3.1):
 // 1e-4 for E4M3 and the E2M1 maximum times 2^-126 for E2M1, unless the caller
-// passes its own clamp_min > 0; E5M2, for which the page names none, takes
-// the E4M3 floor.
+// passes its own clamp_min > 0; E5M2 and E5M6, for which the page names
+// none, take the E4M3 floor.
 #include <atomic>
 
 #include "qcast.h"
@@ -21,11 +21,12 @@ bool aligned(const void* p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p
 
 float default_floor(int fmt) {
   if (fmt == QCAST_FMT_E2M1) return 6.0f * 0x1.0p-126f;   // E2M1 maximum times 2^-126
-  return 1e-4f;   // E4M3; E5M2 takes the same floor
+  return 1e-4f;   // E4M3; E5M2 and E5M6 take the same floor
 }
 
 bool any_fmt(int fmt) {
-  return fmt == QCAST_FMT_E4M3 || fmt == QCAST_FMT_E2M1 || fmt == QCAST_FMT_E5M2;
+  return fmt == QCAST_FMT_E4M3 || fmt == QCAST_FMT_E2M1 || fmt == QCAST_FMT_E5M2 ||
+         fmt == QCAST_FMT_E5M6;
 }
 
 bool fp8_fmt(int fmt) { return fmt == QCAST_FMT_E4M3 || fmt == QCAST_FMT_E5M2; }

@@ -27,12 +27,15 @@ constexpr int kThreads = 256;          // 4 wave64s per workgroup
 constexpr float kE4M3Max = 448.0f;
 constexpr float kE2M1Max = 6.0f;
 constexpr float kE5M2Max = 57344.0f;
+constexpr float kE5M6Max = 65024.0f;   // (2 - 2^-6) * 2^15
 
-enum Fmt : int { kE4M3 = 1, kE2M1 = 2, kE5M2 = 3 };
+enum Fmt : int { kE4M3 = 1, kE2M1 = 2, kE5M2 = 3, kE5M6 = 4 };
 
 template <int kFmt>
 __host__ __device__ constexpr float fmt_max() {
-  return kFmt == kE4M3 ? kE4M3Max : (kFmt == kE2M1 ? kE2M1Max : kE5M2Max);
+  return kFmt == kE4M3 ? kE4M3Max
+       : kFmt == kE2M1 ? kE2M1Max
+       : kFmt == kE5M2 ? kE5M2Max : kE5M6Max;
 }
 
 // Native vector types (the nontemporal builtins take these, not HIP's
@@ -265,6 +268,46 @@ __device__ __forceinline__ uint32_t clamp_gate_up(float& g, float& u, float c) {
   g = g > c ? c : g;
   u = u > c ? c : (u < -c ? -c : u);
   return n;
+}
+
+// E5M6: the IEEE-like 12-bit format with a 5-bit exponent (bias 15) and 6
+// mantissa bits, sign in bit 11 -- the top 12 bits of an fp16 pattern. No
+// hardware conversion exists for it: the code is formed from the fp32 bits.
+// Normal range (|y| >= 2^-14): round the 23-bit mantissa to 6 bits, nearest
+// even, by integer addition (a carry moves into the exponent), then rebias
+// the exponent from 127 to 15; beyond the largest finite value the code
+// saturates. Subnormal range: the code is the integer nearest |y| / 2^-20
+// (an exact scaling by a power of two, then v_rndne_f32); 64 is the smallest
+// normal code. A NaN gives the NaN code 0x7ff with its sign.
+__device__ __forceinline__ uint32_t e5m6_code(float y) {
+  const uint32_t b = __float_as_uint(y);
+  const uint32_t a = b & 0x7fffffffu;
+  uint32_t mag;
+  if (a >= 0x38800000u) {
+    const uint32_t r = (a + 0xffffu + ((a >> 17) & 1u)) >> 17;
+    mag = r - (112u << 6);
+    mag = mag > 0x7bfu ? 0x7bfu : mag;
+    mag = a > 0x7f800000u ? 0x7ffu : mag;   // NaN stays NaN
+  } else {
+    mag = (uint32_t)__builtin_rintf(__uint_as_float(a) * 0x1.0p20f);
+  }
+  return ((b >> 20) & 0x800u) | mag;
+}
+
+// Eight fp32 -> eight E5M6 codes as a little-endian bit stream of 96 bits
+// (code i in bits 12i .. 12i+11).
+struct E5M6x8 {
+  uint32_t w0, w1, w2;
+};
+__device__ __forceinline__ E5M6x8 e5m6x8(const float y[8]) {
+  uint32_t c[8];
+#pragma unroll
+  for (int i = 0; i < 8; ++i) c[i] = e5m6_code(y[i]);
+  E5M6x8 p;
+  p.w0 = c[0] | (c[1] << 12) | (c[2] << 24);
+  p.w1 = (c[2] >> 8) | (c[3] << 4) | (c[4] << 16) | (c[5] << 28);
+  p.w2 = (c[5] >> 4) | (c[6] << 8) | (c[7] << 20);
+  return p;
 }
 
 // Streaming accesses: the data is touched once.

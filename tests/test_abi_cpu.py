@@ -212,9 +212,26 @@ def test_per_channel_validation(lib):
     assert f(None, 0, 64, E4M3, 128, 0.0, None, None, None) == OK
 
 
+def test_e5m6_formats(lib):
+    E5M6 = 4
+    # accepted by the per-token casts and cast_back (null output is the first error)
+    assert lib.qcast_per_token(A16, 4, 256, E5M6, 128, 0.0, None, A16, None) == ERR_NULL
+    assert lib.qcast_per_token_sf(A16, 4, 512, E5M6, 128, 0.0, 5, None, A16, None) == ERR_NULL
+    assert lib.qcast_cast_back(A16, A16, 4, 256, E5M6, 32, 1, None, None) == ERR_NULL
+    assert lib.qcast_per_token(A16, 4, 256, E5M6, 16, 0.0, A16, A16, None) == ERR_GROUP
+    # refused by the casts that write 8-bit codes only
+    assert lib.qcast_swiglu_per_token(A16, 4, 256, None, E5M6, 128, 0.0, A16, A16, None) == ERR_FORMAT
+    assert lib.qcast_per_block(A16, 256, 256, E5M6, 128, 0.0, A16, A16, None) == ERR_FORMAT
+    assert lib.qcast_per_channel_T(A16, 256, 64, E5M6, 128, 0.0, A16, A16, None) == ERR_FORMAT
+    assert lib.qcast_per_channel(A16, 256, 64, E5M6, 128, 0.0, A16, A16, None) == ERR_FORMAT
+    assert lib.qcast_e2m1(A16, 4, 256, 32, 0.0, None, A16, None) == ERR_NULL
+    assert lib.qcast_bench_check_scale(E5M6, 1, 0, A16, None) == ERR_SHAPE
+    assert lib.qcast_bench_check_scale(5, 1, 2, A16, None) == ERR_FORMAT
+
+
 def test_cast_back_validation(lib):
     f = lib.qcast_cast_back
-    assert f(A16, A16, 4, 256, 4, 128, 1, A16, None) == ERR_FORMAT
+    assert f(A16, A16, 4, 256, 9, 128, 1, A16, None) == ERR_FORMAT
     assert f(A16, A16, 4, 256, E4M3, 128, 3, A16, None) == ERR_FORMAT      # out dtype
     assert f(A16, A16, 4, 256, E4M3, 96, 1, A16, None) == ERR_GROUP
     assert f(A16, A16, 4, 200, E4M3, 128, 1, A16, None) == ERR_SHAPE
