@@ -20,7 +20,8 @@ rows of every workload, on this host.
 
 "other_kernels" times, after the step and outside `value`, the casts that
 are not among the five: cast_back of the per-token codes to bf16, the
-per-token cast with 1 x 32 groups and packed UE8M0 column-major scales,
+per-token cast with 1 x 32 groups and packed UE8M0 column-major scales, the
+per-token E5M6 cast and its cast_back,
 SwiGLU with the clamp and counter, SwiGLU + per-channel cast + transpose,
 the SwiGLU backward cast, and the per-channel cast in the input layout.
 
@@ -154,6 +155,16 @@ def extra_calls(wls, dev):
     calls.append(("per_token_ue8m0_g32", [r, c], 2 * r * c + r * c + shape[0] * shape[1] * 4,
                   lambda x=x, qo=qo, so=so: pq.qcast_per_token_sf(x, "e4m3", 32, sf_flags=flags,
                                                                   out=qo, out_sf=so)))
+    # E5M6 per-token cast of the hidden-state workload, and its cast_back
+    q6 = torch.empty(pq.code_shape("e5m6", r, c), dtype=torch.uint8, device=dev)
+    s6 = torch.empty(r, c // 128, dtype=torch.float32, device=dev)
+    e5m6_bytes = 2 * r * c + r * c * 3 // 2 + r * (c // 128) * 4
+    calls.append(("per_token_e5m6", [r, c], e5m6_bytes,
+                  lambda x=x, q6=q6, s6=s6: pq.qcast_per_token(x, "e5m6", 128, out=q6, out_sf=s6)))
+    pq.qcast_per_token(x, "e5m6", 128, out=q6, out_sf=s6)
+    o6 = torch.empty(r, c, dtype=torch.bfloat16, device=dev)
+    calls.append(("cast_back_e5m6", [r, c], e5m6_bytes,
+                  lambda q6=q6, s6=s6, o6=o6: pq.qcast_cast_back(q6, s6, "e5m6", 128, out=o6)))
     # SwiGLU with clamp and counter
     wl = by["swiglu"]
     h, w = wl.x.to(dev), wl.w.to(dev)
