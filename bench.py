@@ -13,8 +13,9 @@ inputs that the rest of the step has evicted.
 
 value = algorithmic bytes of the whole step (inputs read once, codes and
 scales written once) / time per step, in GB/s. Per-kernel durations come from
-HIP events recorded on the launch stream between the kernels of the timed
-steps. The roofline object is for the kernel with the largest share of the
+HIP events that kernels of the timed steps record from their own dispatch on
+the launch stream (qcast_bench_time_next): step s times kernel s mod 5, so
+with the default 50 steps every kernel is timed on 10 of its launches. The roofline object is for the kernel with the largest share of the
 step. The CPU baseline is the oracle (single thread) on the first half of the
 rows of every workload, on this host.
 
@@ -47,11 +48,12 @@ def log(msg):
 
 
 class HipEvents:
-    """HIP timing events without the system-scope fence on record
-    (hipEventDisableSystemFence). One event sits between consecutive
-    kernels of a step, so each kernel is bracketed by the events before and
-    after it on the launch stream; torch's events would add a fenced marker
-    pair per kernel, about 10 us each."""
+    """HIP events created without the system-scope fence on record
+    (hipEventDisableSystemFence). The kernels take them through
+    qcast_bench_time_next, so each pair is recorded by one kernel's dispatch
+    (hipExtLaunchKernel): its elapsed time is the kernel's own duration on
+    the launch stream, with no marker packets between the kernels of a
+    step."""
     DISABLE_SYSTEM_FENCE = 0x20000000
 
     def __init__(self):
@@ -60,7 +62,6 @@ class HipEvents:
         self.hip = ctypes.CDLL("libamdhip64.so")
         self.hip.hipEventCreateWithFlags.argtypes = [ctypes.POINTER(ctypes.c_void_p),
                                                      ctypes.c_uint]
-        self.hip.hipEventRecord.argtypes = [ctypes.c_void_p, ctypes.c_void_p]
         self.hip.hipEventElapsedTime.argtypes = [ctypes.POINTER(ctypes.c_float),
                                                  ctypes.c_void_p, ctypes.c_void_p]
         self.hip.hipEventDestroy.argtypes = [ctypes.c_void_p]
@@ -71,10 +72,6 @@ class HipEvents:
             raise RuntimeError("hipEventCreateWithFlags failed")
         return e
 
-    def record(self, e, stream):
-        if self.hip.hipEventRecord(e, stream) != 0:
-            raise RuntimeError("hipEventRecord failed")
-
     def elapsed_ms(self, a, b):
         f = self.ct.c_float()
         if self.hip.hipEventElapsedTime(self.ct.byref(f), a, b) != 0:
@@ -83,6 +80,43 @@ class HipEvents:
 
     def destroy(self, e):
         self.hip.hipEventDestroy(e)
+
+
+def make_events(hev, n, steps, rotate=True):
+    """Event pairs for the kernel launches that are timed: with at least two
+    steps per kernel, step s times kernel s mod n only (each timed launch
+    costs its dispatch about 1.6 us, so timing one launch per step keeps the
+    step close to an untimed one); with fewer steps every launch is timed."""
+    rotate = rotate and steps >= 2 * n
+    return [[(hev.create(), hev.create()) if (not rotate or i == s % n) else None
+             for i in range(n)] for s in range(steps)]
+
+
+def timed_runs(fns, ev):
+    """Run the closures `fns` in order once per row of `ev`; a kernel with an
+    event pair records it from its own dispatch."""
+    import precision_quantization_amd as pq
+    for row in ev:
+        for pair, fn in zip(row, fns):
+            if pair is not None:
+                pq.qcast_bench_time_next(*pair)
+            fn()
+
+
+def collect(ev, hev):
+    """Per-closure sorted durations in ms of the timed launches (after a
+    synchronize); frees the events."""
+    import torch
+    torch.cuda.synchronize()
+    n = len(ev[0])
+    out = [sorted(hev.elapsed_ms(*row[i]) for row in ev if row[i] is not None)
+           for i in range(n)]
+    for row in ev:
+        for pair in row:
+            if pair is not None:
+                hev.destroy(pair[0])
+                hev.destroy(pair[1])
+    return out
 
 
 def make_workloads():
@@ -208,32 +242,24 @@ def time_extras(extras, dev, steps, warmup):
             fn()
     torch.cuda.synchronize()
     hev = HipEvents()
-    stream = torch.cuda.current_stream(dev).cuda_stream
-    n = len(extras)
-    ev = [[hev.create() for _ in range(n + 1)] for _ in range(steps)]
-    for s in range(steps):
-        hev.record(ev[s][0], stream)
-        for i, (*_, fn) in enumerate(extras):
-            fn()
-            hev.record(ev[s][i + 1], stream)
-    torch.cuda.synchronize()
+    ev = make_events(hev, len(extras), steps, rotate=False)
+    timed_runs([fn for *_, fn in extras], ev)
+    ms_all = collect(ev, hev)
     out = {}
-    for i, (name, shape, b, _) in enumerate(extras):
-        ms = sorted(hev.elapsed_ms(ev[s][i], ev[s][i + 1]) for s in range(steps))
+    for (name, shape, b, _), ms in zip(extras, ms_all):
         avg = sum(ms) / len(ms)
         out[name] = {"shape": shape, "bytes": b, "avg_us": round(avg * 1e3, 2),
+                     "median_us": round(ms[len(ms) // 2] * 1e3, 2),
                      "GBps": round(b / (avg * 1e-3) / 1e9, 1),
                      "frac": round(b / (avg * 1e-3) / 1e9 / PEAK_HBM_GBS, 4)}
-    for row in ev:
-        for e in row:
-            hev.destroy(e)
     return out
 
 
 def copy_ceiling(dev, nbytes):
     """Bandwidth of the library's streaming copy (include/qcast_bench.h)
-    moving nbytes in total (half read, half written) after a 1 GiB flush:
-    the empirical ceiling for a streaming kernel of this shape."""
+    moving nbytes in total (half read, half written; the byte count of the
+    largest cast of the step) after a 1 GiB flush: the empirical ceiling for
+    a streaming kernel of this size."""
     import torch
     import precision_quantization_amd as pq
     half = nbytes // 2 // 16 * 16
@@ -241,18 +267,16 @@ def copy_ceiling(dev, nbytes):
     dst = torch.empty(half, dtype=torch.uint8, device=dev)
     flush = torch.empty(1 << 30, dtype=torch.uint8, device=dev)
     hev = HipEvents()
-    stream = torch.cuda.current_stream(dev).cuda_stream
-    a, b = hev.create(), hev.create()
     times = []
     for _ in range(6):
         flush.fill_(0)
-        hev.record(a, stream)
+        a, b = hev.create(), hev.create()
+        pq.qcast_bench_time_next(a, b)
         pq.qcast_bench_copy(src, dst)
-        hev.record(b, stream)
         torch.cuda.synchronize()
         times.append(hev.elapsed_ms(a, b))
-    hev.destroy(a)
-    hev.destroy(b)
+        hev.destroy(a)
+        hev.destroy(b)
     ms = sorted(times[1:])[len(times[1:]) // 2]
     return 2 * half / (ms * 1e-3) / 1e9
 
@@ -327,41 +351,34 @@ def main():
             fn()
     torch.cuda.synchronize()
 
-    n = len(calls)
     hev = HipEvents()
-    stream = torch.cuda.current_stream(dev).cuda_stream
-    ev = [[hev.create() for _ in range(n + 1)] for _ in range(args.steps)]
+    fns = [fn for _, _, fn in calls]
+    ev = make_events(hev, len(fns), args.steps)
     log(f"bench: timing {args.steps} steps")
     torch.cuda.synchronize()
     t0 = time.perf_counter()
-    for s in range(args.steps):
-        hev.record(ev[s][0], stream)
-        for i, (_, _, fn) in enumerate(calls):
-            fn()
-            hev.record(ev[s][i + 1], stream)
+    timed_runs(fns, ev)
     torch.cuda.synchronize()
     elapsed = time.perf_counter() - t0
     ms_per_step = elapsed * 1e3 / args.steps
 
     kernels = {}
-    for i, (name, wl, _) in enumerate(calls):
-        ms = sorted(hev.elapsed_ms(ev[s][i], ev[s][i + 1]) for s in range(args.steps))
+    for (name, wl, _), ms in zip(calls, collect(ev, hev)):
         avg = sum(ms) / len(ms)
         b = wl.algorithmic_bytes()
         kernels[name] = {
-            "shape": list(wl.x.shape), "bytes": b, "avg_us": round(avg * 1e3, 2),
+            "shape": list(wl.x.shape), "bytes": b, "timed_launches": len(ms),
+            "avg_us": round(avg * 1e3, 2),
             "median_us": round(ms[len(ms) // 2] * 1e3, 2),
             "GBps": round(b / (avg * 1e-3) / 1e9, 1),
             "frac": round(b / (avg * 1e-3) / 1e9 / PEAK_HBM_GBS, 4),
             "rows_per_s": round(wl.rows / (avg * 1e-3)),
         }
-    for row in ev:
-        for e in row:
-            hev.destroy(e)
     dominant = max(kernels, key=lambda k: kernels[k]["avg_us"])
     d = kernels[dominant]
     traffic = load_traffic(dominant)
-    copy_gbs = copy_ceiling(dev, d["bytes"])
+    copy_nbytes = max(k["bytes"] for k in kernels.values())
+    copy_gbs = copy_ceiling(dev, copy_nbytes)
     result = {
         "metric": METRIC,
         "value": round(step_bytes * args.steps / elapsed / 1e9, 1),
@@ -388,7 +405,7 @@ def main():
         },
         "kernels": kernels,
         "copy_ceiling_GBps": round(copy_gbs, 1),
-        "copy_bytes": d["bytes"] // 2 // 16 * 16 * 2,
+        "copy_bytes": copy_nbytes // 2 // 16 * 16 * 2,
     }
     if not args.no_extras:
         log("bench: timing the other casts")

@@ -8,6 +8,11 @@
  * counters to calibrate those of the casts (a copy of n bytes must read n
  * and write n bytes).
  *
+ * qcast_bench_time_next: hands a pair of HIP events to the next kernel the
+ * calling thread launches through the library, which records them from the
+ * dispatch itself (hipExtLaunchKernel): their elapsed time is that kernel's
+ * own duration, with no marker packets around it.
+ *
  * qcast_bench_check_scale: runs the kernels' own scale routine on a range of
  * fp32 bit patterns and counts where it differs from the IEEE quotients
  * a / fmt_max and 1 / sf. The casts compute sf and sf_inv with short FMA
@@ -30,6 +35,15 @@ extern "C" {
  * QCAST_ERR_NULL, QCAST_ERR_ALIGN or QCAST_ERR_SHAPE before any HIP call,
  * QCAST_ERR_LAUNCH if the launch fails. nbytes == 0 launches nothing. */
 QCAST_API int qcast_bench_copy(const void* src, void* dst, int64_t nbytes, void* stream);
+
+/* The next kernel launched by the calling thread through any entry point
+ * records start_event when it begins and stop_event when it ends (both
+ * hipEvent_t, created by the caller on the launch's device; the library
+ * keeps no reference after that launch). An entry point that launches
+ * several kernels (inputs split into slabs) times only its first; one that
+ * returns an error before launching leaves the events pending for the next
+ * launch. Returns QCAST_ERR_NULL if either event is null. */
+QCAST_API int qcast_bench_time_next(void* start_event, void* stop_event);
 
 /* Number of workgroups of qcast_bench_check_scale: `counts` holds two
  * uint32 per workgroup. */

@@ -27,7 +27,7 @@ __all__ = ["qcast_per_token", "qcast_e2m1", "qcast_swiglu_per_token", "qcast_per
            "qcast_swiglu_backward_per_token", "qcast_swiglu_per_channel_T", "qcast_per_channel",
            "sf_layout_shape", "SF_ROUND_POW2", "SF_COL_MAJOR",
            "SF_PACKED_UE8M0", "qcast_abi_version", "qcast_set_num_cus", "qcast_bench_copy",
-           "qcast_bench_check_scale",
+           "qcast_bench_check_scale", "qcast_bench_time_next",
            "per_token_cast",
            "QcastError", "FMT_E4M3", "FMT_E2M1", "FMT_E5M2", "FMT_E5M6", "code_shape"]
 
@@ -379,6 +379,13 @@ def qcast_bench_check_scale(fmt, first, last, device="cuda:0", stream=None):
                                              _stream(dev, stream)), "qcast_bench_check_scale")
         c = counts.view(2048, 2).sum(dim=0, dtype=torch.int64).cpu()
     return int(c[0]), int(c[1])
+
+
+def qcast_bench_time_next(start_event, stop_event):
+    """Measurement helper (include/qcast_bench.h): the next kernel this thread
+    launches through the library records these HIP events (raw hipEvent_t
+    handles) at its own start and end."""
+    check(load().qcast_bench_time_next(start_event, stop_event), "qcast_bench_time_next")
 
 
 def per_token_cast(x, fmt="e4m3", num_per_channels=128):

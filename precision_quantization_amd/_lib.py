@@ -80,6 +80,8 @@ def load():
     lib.qcast_bench_copy.restype = i32
     lib.qcast_bench_check_scale.argtypes = [i32, ctypes.c_uint32, ctypes.c_uint32, vp, vp]
     lib.qcast_bench_check_scale.restype = i32
+    lib.qcast_bench_time_next.argtypes = [vp, vp]
+    lib.qcast_bench_time_next.restype = i32
     lib.qcast_set_num_cus.argtypes = [i32]
     lib.qcast_set_num_cus.restype = None
     _lib = lib
@@ -97,4 +99,4 @@ EXPORTS = ["qcast_per_token", "qcast_e2m1", "qcast_swiglu_per_token", "qcast_per
            "qcast_swiglu_per_token_sf", "qcast_swiglu_per_token_ex",
            "qcast_swiglu_backward_per_token", "qcast_swiglu_per_channel_T", "qcast_per_channel",
            "qcast_status_str", "qcast_abi_version", "qcast_set_num_cus",
-           "qcast_bench_copy", "qcast_bench_check_scale"]
+           "qcast_bench_copy", "qcast_bench_check_scale", "qcast_bench_time_next"]

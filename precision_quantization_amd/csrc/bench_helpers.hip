@@ -1,4 +1,6 @@
 // bench_helpers.hip -- the helpers declared in include/qcast_bench.h:
+//  - start/stop events for the next kernel a thread launches, recorded by
+//    the dispatch itself (hipExtLaunchKernel), for per-kernel durations;
 //  - a streaming copy, the bandwidth ceiling and counter calibration for the
 //    cast kernels (16-byte non-temporal loads and stores, as the casts);
 //  - an exhaustive check of the kernels' scale routine against IEEE
@@ -7,8 +9,21 @@
 
 #include "qcast_bench.h"
 #include "qcast_device.h"
+#include "qcast_kernels.h"
 
 namespace qcast {
+
+namespace {
+// Timing events for the next launch of the calling thread.
+thread_local LaunchTiming t_timing = {nullptr, nullptr};
+}  // namespace
+
+LaunchTiming take_launch_timing() {
+  const LaunchTiming t = t_timing;
+  t_timing = LaunchTiming{nullptr, nullptr};
+  return t;
+}
+
 namespace {
 
 #ifndef QCAST_CP_UNROLL
@@ -87,17 +102,17 @@ extern "C" int qcast_bench_check_scale(int fmt, uint32_t first, uint32_t last, u
   if (reinterpret_cast<uintptr_t>(counts) & 3) return QCAST_ERR_ALIGN;
   hipStream_t s = static_cast<hipStream_t>(stream);
   if (fmt == QCAST_FMT_E4M3)
-    hipLaunchKernelGGL(qcast::check_scale_kernel<qcast::kE4M3>, dim3(QCAST_CHECK_BLOCKS),
-                       dim3(qcast::kThreads), 0, s, first, last, counts);
+    qcast::launch_kernel(qcast::check_scale_kernel<qcast::kE4M3>, dim3(QCAST_CHECK_BLOCKS),
+                         dim3(qcast::kThreads), 0, s, first, last, counts);
   else if (fmt == QCAST_FMT_E2M1)
-    hipLaunchKernelGGL(qcast::check_scale_kernel<qcast::kE2M1>, dim3(QCAST_CHECK_BLOCKS),
-                       dim3(qcast::kThreads), 0, s, first, last, counts);
+    qcast::launch_kernel(qcast::check_scale_kernel<qcast::kE2M1>, dim3(QCAST_CHECK_BLOCKS),
+                         dim3(qcast::kThreads), 0, s, first, last, counts);
   else if (fmt == QCAST_FMT_E5M2)
-    hipLaunchKernelGGL(qcast::check_scale_kernel<qcast::kE5M2>, dim3(QCAST_CHECK_BLOCKS),
-                       dim3(qcast::kThreads), 0, s, first, last, counts);
+    qcast::launch_kernel(qcast::check_scale_kernel<qcast::kE5M2>, dim3(QCAST_CHECK_BLOCKS),
+                         dim3(qcast::kThreads), 0, s, first, last, counts);
   else
-    hipLaunchKernelGGL(qcast::check_scale_kernel<qcast::kE5M6>, dim3(QCAST_CHECK_BLOCKS),
-                       dim3(qcast::kThreads), 0, s, first, last, counts);
+    qcast::launch_kernel(qcast::check_scale_kernel<qcast::kE5M6>, dim3(QCAST_CHECK_BLOCKS),
+                         dim3(qcast::kThreads), 0, s, first, last, counts);
   return hipGetLastError() == hipSuccess ? QCAST_OK : QCAST_ERR_LAUNCH;
 }
 
@@ -118,8 +133,15 @@ extern "C" int qcast_bench_copy(const void* src, void* dst, int64_t nbytes, void
   const int64_t max_blocks = qcast::kCopyWgPerCu > 0 ? (int64_t)cus * qcast::kCopyWgPerCu : iters;
   const int64_t ipb = (iters + max_blocks - 1) / max_blocks;
   const int64_t blocks = (iters + ipb - 1) / ipb;
-  hipLaunchKernelGGL(qcast::copy_kernel, dim3((unsigned)blocks), dim3(qcast::kThreads), 0,
-                     static_cast<hipStream_t>(stream), static_cast<const qcast::u32x4*>(src),
-                     static_cast<qcast::u32x4*>(dst), n);
+  qcast::launch_kernel(qcast::copy_kernel, dim3((unsigned)blocks), dim3(qcast::kThreads), 0,
+                       static_cast<hipStream_t>(stream), static_cast<const qcast::u32x4*>(src),
+                       static_cast<qcast::u32x4*>(dst), n);
   return hipGetLastError() == hipSuccess ? QCAST_OK : QCAST_ERR_LAUNCH;
+}
+
+extern "C" int qcast_bench_time_next(void* start_event, void* stop_event) {
+  if (!start_event || !stop_event) return QCAST_ERR_NULL;
+  qcast::t_timing = qcast::LaunchTiming{static_cast<hipEvent_t>(start_event),
+                                        static_cast<hipEvent_t>(stop_event)};
+  return QCAST_OK;
 }

@@ -140,11 +140,11 @@ hipError_t launch(const void* q, const float* sf, int64_t nchunks, bool out_bf16
   const int64_t blocks = (nchunks + (int64_t)kThreads * kUnroll - 1) / ((int64_t)kThreads * kUnroll);
   if (blocks >= (int64_t(1) << 31)) return hipErrorInvalidValue;
   if (out_bf16)
-    hipLaunchKernelGGL((cast_back_kernel<kLanes, kFmt, true>), dim3((unsigned)blocks),
-                       dim3(kThreads), 0, stream, static_cast<const uint8_t*>(q), sf, nchunks, out);
+    launch_kernel((cast_back_kernel<kLanes, kFmt, true>), dim3((unsigned)blocks),
+                  dim3(kThreads), 0, stream, static_cast<const uint8_t*>(q), sf, nchunks, out);
   else
-    hipLaunchKernelGGL((cast_back_kernel<kLanes, kFmt, false>), dim3((unsigned)blocks),
-                       dim3(kThreads), 0, stream, static_cast<const uint8_t*>(q), sf, nchunks, out);
+    launch_kernel((cast_back_kernel<kLanes, kFmt, false>), dim3((unsigned)blocks),
+                  dim3(kThreads), 0, stream, static_cast<const uint8_t*>(q), sf, nchunks, out);
   return hipGetLastError();
 }
 

@@ -90,13 +90,13 @@ hipError_t launch_per_block(const void* x, int64_t rows, int64_t cols, int fmt, 
   const int64_t lim = int64_t(1) << 31;
   if (nblocks >= lim || (int64_t)kBlock * cols >= lim) return hipErrorInvalidValue;
   if (fmt == kE4M3)
-    hipLaunchKernelGGL(per_block_kernel<kE4M3>, dim3((unsigned)nblocks), dim3(kThreads), 0, stream,
-                       static_cast<const uint16_t*>(x), (uint32_t)cols, (uint32_t)bcols, floor,
-                       static_cast<uint8_t*>(q), sf);
+    launch_kernel(per_block_kernel<kE4M3>, dim3((unsigned)nblocks), dim3(kThreads), 0, stream,
+                  static_cast<const uint16_t*>(x), (uint32_t)cols, (uint32_t)bcols, floor,
+                  static_cast<uint8_t*>(q), sf);
   else if (fmt == kE5M2)
-    hipLaunchKernelGGL(per_block_kernel<kE5M2>, dim3((unsigned)nblocks), dim3(kThreads), 0, stream,
-                       static_cast<const uint16_t*>(x), (uint32_t)cols, (uint32_t)bcols, floor,
-                       static_cast<uint8_t*>(q), sf);
+    launch_kernel(per_block_kernel<kE5M2>, dim3((unsigned)nblocks), dim3(kThreads), 0, stream,
+                  static_cast<const uint16_t*>(x), (uint32_t)cols, (uint32_t)bcols, floor,
+                  static_cast<uint8_t*>(q), sf);
   else
     return hipErrorInvalidValue;
   return hipGetLastError();

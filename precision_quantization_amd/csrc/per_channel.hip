@@ -119,9 +119,9 @@ hipError_t launch_per_channel(const void* x, int64_t rows, int64_t cols, int fmt
   auto kernel = fmt == kE4M3 ? per_channel_kernel<kE4M3>
                : fmt == kE5M2 ? per_channel_kernel<kE5M2> : nullptr;
   if (!kernel) return hipErrorInvalidValue;
-  hipLaunchKernelGGL(kernel, dim3((unsigned)ntiles), dim3(kThreads), 0, stream,
-                     static_cast<const uint16_t*>(x), (uint32_t)cols, (uint32_t)nct, floor,
-                     static_cast<uint8_t*>(q), sf);
+  launch_kernel(kernel, dim3((unsigned)ntiles), dim3(kThreads), 0, stream,
+                static_cast<const uint16_t*>(x), (uint32_t)cols, (uint32_t)nct, floor,
+                static_cast<uint8_t*>(q), sf);
   return hipGetLastError();
 }
 

@@ -341,27 +341,37 @@ __global__ __launch_bounds__(kThreads) void per_channel_t_kernel(
   process_tile<kFmt>(tc, tile, rows, ngroups, floor, sm, qT, sf);
 }
 
-// SwiGLU + the same cast. Without a clamp counter: one workgroup per tile
-// (vgrid == gridDim.x). With one, every workgroup ends in an atomic add on
-// the same word, serialized where the word lives, so a capped grid walks
-// the virtual workgroup indices [0, vgrid) with a stride of gridDim.x.
-template <int kFmt, bool kWeighted, bool kClamp>
+// SwiGLU + the same cast. Without a clamp counter (kCount false): one
+// workgroup per tile. With one, every workgroup ends in an atomic add on the
+// same word, serialized where the word lives, so a capped grid walks the
+// virtual workgroup indices [0, vgrid) with a stride of gridDim.x.
+template <int kFmt, bool kWeighted, bool kClamp, bool kCount>
 __global__ __launch_bounds__(kThreads) void swiglu_per_channel_t_kernel(
     const uint16_t* __restrict__ h, const float* __restrict__ w, uint32_t rows, uint32_t cols,
     uint32_t ngroups, uint32_t nct, uint32_t ntiles, uint32_t per_xcd, uint32_t vgrid,
     float floor, float clamp, unsigned long long* __restrict__ count, uint8_t* __restrict__ qT,
     float* __restrict__ sf) {
   __shared__ __attribute__((aligned(16))) Smem sm;
-  uint32_t n = 0;
-  for (uint32_t b = blockIdx.x; b < vgrid; b += gridDim.x) {
+  if constexpr (kCount) {
+    uint32_t n = 0;
+    for (uint32_t b = blockIdx.x; b < vgrid; b += gridDim.x) {
+      const uint32_t tau = (kOrder & 2) ? b : (b % kXcds) * per_xcd + b / kXcds;
+      if (tau >= ntiles) continue;  // uniform over the workgroup
+      const TileCoord tc = tile_coord(tau, ngroups, cols, nct, ntiles / nct);
+      F32Tile tile;
+      n += load_swiglu_tile<kWeighted, kClamp>(h, w, cols, clamp, tc, tile);
+      process_tile<kFmt>(tc, tile, rows, ngroups, floor, sm, qT, sf);
+    }
+    add_count(n, count);
+  } else {
+    const uint32_t b = blockIdx.x;
     const uint32_t tau = (kOrder & 2) ? b : (b % kXcds) * per_xcd + b / kXcds;
-    if (tau >= ntiles) continue;  // uniform over the workgroup
+    if (tau >= ntiles) return;
     const TileCoord tc = tile_coord(tau, ngroups, cols, nct, ntiles / nct);
     F32Tile tile;
-    n += load_swiglu_tile<kWeighted, kClamp>(h, w, cols, clamp, tc, tile);
+    load_swiglu_tile<kWeighted, kClamp>(h, w, cols, clamp, tc, tile);
     process_tile<kFmt>(tc, tile, rows, ngroups, floor, sm, qT, sf);
   }
-  if (kClamp && count) add_count(n, count);
 }
 
 struct Grid {
@@ -399,14 +409,20 @@ template <int kFmt, bool kWeighted, bool kClamp>
 hipError_t launch_swiglu_t(const uint16_t* h, const float* w, int64_t rows, int64_t cols,
                            const Grid& g, float floor, float clamp, unsigned long long* count,
                            uint8_t* qT, float* sf, hipStream_t stream, const LaunchCaps& caps) {
-  uint32_t grid = g.grid;
-  if (kClamp && count && QCAST_PC_COUNT_WG_PER_CU > 0) {
+  if (kClamp && count) {
+    uint32_t grid = g.grid;
     const int64_t cap = (int64_t)caps.num_cus * QCAST_PC_COUNT_WG_PER_CU;
-    if (cap < grid) grid = (uint32_t)cap;
+    if (QCAST_PC_COUNT_WG_PER_CU > 0 && cap < grid) grid = (uint32_t)cap;
+    launch_kernel((swiglu_per_channel_t_kernel<kFmt, kWeighted, kClamp, true>), dim3(grid),
+                  dim3(kThreads), 0, stream, h, w, (uint32_t)rows, (uint32_t)cols,
+                  g.ngroups, g.nct, g.ntiles, g.per_xcd, g.grid, floor, clamp, count, qT,
+                  sf);
+  } else {
+    launch_kernel((swiglu_per_channel_t_kernel<kFmt, kWeighted, kClamp, false>),
+                  dim3(g.grid), dim3(kThreads), 0, stream, h, w, (uint32_t)rows,
+                  (uint32_t)cols, g.ngroups, g.nct, g.ntiles, g.per_xcd, g.grid, floor,
+                  clamp, count, qT, sf);
   }
-  hipLaunchKernelGGL((swiglu_per_channel_t_kernel<kFmt, kWeighted, kClamp>), dim3(grid),
-                     dim3(kThreads), 0, stream, h, w, (uint32_t)rows, (uint32_t)cols, g.ngroups,
-                     g.nct, g.ntiles, g.per_xcd, g.grid, floor, clamp, count, qT, sf);
   return hipGetLastError();
 }
 
@@ -442,9 +458,9 @@ hipError_t launch_per_channel_T(const void* x, int64_t rows, int64_t cols, int f
   auto kernel = fmt == kE4M3 ? per_channel_t_kernel<kE4M3>
                : fmt == kE5M2 ? per_channel_t_kernel<kE5M2> : nullptr;
   if (!kernel) return hipErrorInvalidValue;
-  hipLaunchKernelGGL(kernel, dim3(g.grid), dim3(kThreads), 0, stream,
-                     static_cast<const uint16_t*>(x), (uint32_t)rows, (uint32_t)cols, g.ngroups,
-                     g.nct, g.ntiles, g.per_xcd, floor, static_cast<uint8_t*>(qT), sf);
+  launch_kernel(kernel, dim3(g.grid), dim3(kThreads), 0, stream,
+                static_cast<const uint16_t*>(x), (uint32_t)rows, (uint32_t)cols, g.ngroups,
+                g.nct, g.ntiles, g.per_xcd, floor, static_cast<uint8_t*>(qT), sf);
   return hipGetLastError();
 }
 

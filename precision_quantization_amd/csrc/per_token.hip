@@ -111,9 +111,9 @@ hipError_t launch(const void* x, int64_t nchunks, float floor, void* q, void* sf
     blocks = per_xcd * kXcds;
   }
   if (blocks >= (int64_t(1) << 31)) return hipErrorInvalidValue;
-  hipLaunchKernelGGL((per_token_kernel<kLanes, kFmt>), dim3((unsigned)blocks), dim3(kThreads), 0,
-                     stream, static_cast<const u32x4*>(x), nchunks, floor,
-                     static_cast<uint8_t*>(q), sf, lay, (uint32_t)per_xcd);
+  launch_kernel((per_token_kernel<kLanes, kFmt>), dim3((unsigned)blocks), dim3(kThreads), 0,
+                stream, static_cast<const u32x4*>(x), nchunks, floor,
+                static_cast<uint8_t*>(q), sf, lay, (uint32_t)per_xcd);
   return hipGetLastError();
 }
 

@@ -2,12 +2,32 @@
 // library; the C ABI in qcast_abi.hip validates arguments before calling).
 #pragma once
 
+#include <hip/hip_ext.h>
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
 #include "qcast_device.h"
 
 namespace qcast {
+
+// Start and stop events for the next kernel launched by the calling thread
+// (qcast_bench_time_next); both null when none were asked for. Taking them
+// clears them.
+struct LaunchTiming {
+  hipEvent_t start;
+  hipEvent_t stop;
+};
+LaunchTiming take_launch_timing();
+
+// Every kernel of the library is launched through here: with timing events
+// pending, hipExtLaunchKernel records them from the dispatch itself (the
+// kernel's own start and end, with no marker packets around it).
+template <typename... KArgs, typename... Args>
+inline void launch_kernel(void (*kernel)(KArgs...), dim3 grid, dim3 block, uint32_t shmem,
+                          hipStream_t stream, Args... args) {
+  const LaunchTiming t = take_launch_timing();
+  hipExtLaunchKernelGGL(kernel, grid, block, shmem, stream, t.start, t.stop, 0u, args...);
+}
 
 // Launch shape knobs shared by the launchers.
 struct LaunchCaps {

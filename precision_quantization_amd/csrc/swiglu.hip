@@ -138,17 +138,17 @@ hipError_t launch(const uint16_t* h, const float* w, int64_t rows, int64_t cols,
     const int64_t iters_per_block = (iters + max_blocks - 1) / max_blocks;
     const int64_t blocks = (iters + iters_per_block - 1) / iters_per_block;
     if (counting)
-      hipLaunchKernelGGL((swiglu_kernel<kLanes, kWeighted, kFmt, kClamp, kCountBlock>),
-                         dim3((unsigned)blocks), dim3(kCountBlock), 0, stream, h + r0 * 2 * cols,
-                         kWeighted ? w + r0 : nullptr, nchunks, (uint32_t)cpr, magic, cols,
-                         floor, q + r0 * cols, sf, lay, (uint32_t)(r0 * groups_per_row), ca.c,
-                         ca.count);
+      launch_kernel((swiglu_kernel<kLanes, kWeighted, kFmt, kClamp, kCountBlock>),
+                    dim3((unsigned)blocks), dim3(kCountBlock), 0, stream, h + r0 * 2 * cols,
+                    kWeighted ? w + r0 : nullptr, nchunks, (uint32_t)cpr, magic, cols,
+                    floor, q + r0 * cols, sf, lay, (uint32_t)(r0 * groups_per_row), ca.c,
+                    ca.count);
     else
-      hipLaunchKernelGGL((swiglu_kernel<kLanes, kWeighted, kFmt, kClamp, kThreads>),
-                         dim3((unsigned)blocks), dim3(kThreads), 0, stream, h + r0 * 2 * cols,
-                         kWeighted ? w + r0 : nullptr, nchunks, (uint32_t)cpr, magic, cols,
-                         floor, q + r0 * cols, sf, lay, (uint32_t)(r0 * groups_per_row), ca.c,
-                         ca.count);
+      launch_kernel((swiglu_kernel<kLanes, kWeighted, kFmt, kClamp, kThreads>),
+                    dim3((unsigned)blocks), dim3(kThreads), 0, stream, h + r0 * 2 * cols,
+                    kWeighted ? w + r0 : nullptr, nchunks, (uint32_t)cpr, magic, cols,
+                    floor, q + r0 * cols, sf, lay, (uint32_t)(r0 * groups_per_row), ca.c,
+                    ca.count);
     const hipError_t err = hipGetLastError();
     if (err != hipSuccess) return err;
   }

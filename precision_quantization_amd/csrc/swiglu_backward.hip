@@ -119,10 +119,10 @@ hipError_t launch(const uint16_t* h, const uint16_t* dv, const float* w, int64_t
     const int64_t nchunks = nr * cpr;
     const int64_t per_block = (int64_t)kThreads * kUnroll;
     const int64_t blocks = (nchunks + per_block - 1) / per_block;
-    hipLaunchKernelGGL((swiglu_backward_kernel<kLanes, kWeighted, kFmt, kClamp>),
-                       dim3((unsigned)blocks), dim3(kThreads), 0, stream, h + r0 * 2 * cols,
-                       dv + r0 * cols, kWeighted ? w + r0 : nullptr, nchunks, (uint32_t)cpr,
-                       magic, cols, floor, clamp, q + r0 * 2 * cols, sf + r0 * sf_per_row);
+    launch_kernel((swiglu_backward_kernel<kLanes, kWeighted, kFmt, kClamp>),
+                  dim3((unsigned)blocks), dim3(kThreads), 0, stream, h + r0 * 2 * cols,
+                  dv + r0 * cols, kWeighted ? w + r0 : nullptr, nchunks, (uint32_t)cpr,
+                  magic, cols, floor, clamp, q + r0 * 2 * cols, sf + r0 * sf_per_row);
     const hipError_t err = hipGetLastError();
     if (err != hipSuccess) return err;
   }

@@ -229,6 +229,11 @@ def test_e5m6_formats(lib):
     assert lib.qcast_bench_check_scale(5, 1, 2, A16, None) == ERR_FORMAT
 
 
+def test_time_next_validation(lib):
+    assert lib.qcast_bench_time_next(None, A16) == ERR_NULL
+    assert lib.qcast_bench_time_next(A16, None) == ERR_NULL
+
+
 def test_cast_back_validation(lib):
     f = lib.qcast_cast_back
     assert f(A16, A16, 4, 256, 9, 128, 1, A16, None) == ERR_FORMAT
