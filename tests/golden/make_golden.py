@@ -32,7 +32,22 @@ CASES = {
     "e2m1_r16": lambda: workloads.student_t(rows=16),
     "per_token_hidden_r64_e5m2": lambda: _fmt(workloads.per_token_hidden(rows=64), "e5m2"),
     "cast_back_bf16_r64": lambda: _op(workloads.per_token_hidden(rows=64), "cast_back"),
+    "per_token_hidden_r64_e5m6": lambda: _fmt(workloads.per_token_hidden(rows=64), "e5m6"),
+    "per_token_ue8m0_colmajor_r63": lambda: _op(_grp(workloads.per_token_hidden(rows=63), 32),
+                                                "per_token_ue8m0_cm"),
+    "swiglu_clamp_r32": lambda: _op(workloads.swiglu_input(rows=32), "swiglu_clamp"),
+    "swiglu_T_256x128": lambda: _op(workloads.swiglu_input(rows=256, cols=128), "swiglu_T"),
+    "per_channel_256x384": lambda: _op(workloads.activation_channel(rows=256, cols=384),
+                                       "per_channel"),
 }
+
+# The SwiGLU backward takes two inputs; its digests cover both.
+BACKWARD_CASE = dict(seed=7, rows=16, cols=256, swiglu_clamp=6.0)
+
+
+def _grp(wl, group):
+    wl.group = group
+    return wl
 
 
 def _fmt(wl, fmt):
@@ -67,6 +82,16 @@ def run_case(wl):
     elif wl.op == "cast_back":
         q, sf = oracle.per_token(x, wl.fmt, wl.group)
         q = oracle.cast_back(q, sf, x.shape[1], wl.fmt, wl.group, "bf16")
+    elif wl.op == "per_token_ue8m0_cm":
+        q, sf = oracle.per_token_sf(x, wl.fmt, wl.group,
+                                    sf_flags=oracle.SF_PACKED_UE8M0 | oracle.SF_COL_MAJOR)
+    elif wl.op == "swiglu_clamp":
+        q, sf, n = oracle.swiglu_per_token_ex(x, wl.w.numpy(), wl.fmt, wl.group, swiglu_clamp=3.0)
+        sf = np.concatenate([sf.ravel().view(np.uint8), np.array([n], np.uint64).view(np.uint8)])
+    elif wl.op == "swiglu_T":
+        q, sf = oracle.swiglu_per_channel_T(x, wl.w.numpy(), wl.fmt, wl.group, swiglu_clamp=5.0)
+    elif wl.op == "per_channel":
+        q, sf = oracle.per_channel(x, wl.fmt, wl.group)
     else:
         raise ValueError(wl.op)
     return q, sf
@@ -78,6 +103,14 @@ def compute():
         wl = make()
         q, sf = run_case(wl)
         out[name] = {"input": workloads.sha256(wl.x), "codes": digest(q), "scales": digest(sf)}
+    c = BACKWARD_CASE
+    h, dv, w = workloads.swiglu_grad(seed=c["seed"], rows=c["rows"], cols=c["cols"])
+    q, sf = oracle.swiglu_backward_per_token(workloads.bf16_bits(h), workloads.bf16_bits(dv),
+                                             w.numpy(), "e5m2", 128,
+                                             swiglu_clamp=c["swiglu_clamp"])
+    out["swiglu_backward_e5m2_r16"] = {"input": digest(workloads.bf16_bits(h),
+                                                       workloads.bf16_bits(dv), w.numpy()),
+                                       "codes": digest(q), "scales": digest(sf)}
     return out
 
 
