@@ -43,6 +43,9 @@
  *    HIP call; on an error nothing is launched and no output is touched.
  *    QCAST_ERR_LAUNCH reports a failed launch (hipGetLastError).
  *  - rows == 0 (or an empty row) is valid and launches nothing.
+ *  - Shapes past the kernels' 32-bit indexing return QCAST_ERR_SHAPE before
+ *    any HIP call: rows * cols / group < 2^31 scale groups for the per-token
+ *    casts; for the others, the limits stated with each entry point.
  *  - Calls on one stream are ordered; concurrent calls on different streams
  *    are independent (no shared mutable device state).
  */
@@ -216,6 +219,7 @@ QCAST_API int qcast_swiglu_backward_per_token(const void* h, const void* dv, int
  *   sf  [cols, rows/group] fp32, groups of `group` tokens of one channel.
  *   group must be 128; rows % group == 0; cols % 8 == 0;
  *   fmt QCAST_FMT_E4M3 or QCAST_FMT_E5M2; clamp_count as above.
+ *   Limits: 256 * cols < 2^31, 64 * rows < 2^31.
  */
 QCAST_API int qcast_swiglu_per_channel_T(const void* h, int64_t rows, int64_t cols,
                                          const float* row_weight, int fmt, int group,
@@ -229,6 +233,7 @@ QCAST_API int qcast_swiglu_per_channel_T(const void* h, int64_t rows, int64_t co
  *   x  [rows, cols] bf16; rows % block == 0 and cols % block == 0.
  *   q  [rows, cols] bytes; sf [rows/block, cols/block] fp32.
  *   block must be 128; fmt QCAST_FMT_E4M3 or QCAST_FMT_E5M2.
+ *   Limits: (rows/128) * (cols/128) < 2^31 and 128 * cols < 2^31.
  */
 QCAST_API int qcast_per_block(const void* x, int64_t rows, int64_t cols, int fmt, int block,
                     float clamp_min, void* q, float* sf, void* stream);
@@ -244,6 +249,7 @@ QCAST_API int qcast_per_block(const void* x, int64_t rows, int64_t cols, int fmt
  *   sf  [cols, rows/group] fp32.
  *   group must be 128; rows % group == 0; cols % 8 == 0;
  *   fmt QCAST_FMT_E4M3 or QCAST_FMT_E5M2.
+ *   Limits: 128 * cols < 2^31, 64 * rows < 2^31.
  */
 QCAST_API int qcast_per_channel_T(const void* x, int64_t rows, int64_t cols, int fmt, int group,
                         float clamp_min, void* qT, float* sf, void* stream);
@@ -257,6 +263,7 @@ QCAST_API int qcast_per_channel_T(const void* x, int64_t rows, int64_t cols, int
  *       g*group .. g*group + group - 1 of channel c.
  *   group must be 128; rows % group == 0; cols % 8 == 0;
  *   fmt QCAST_FMT_E4M3 or QCAST_FMT_E5M2.
+ *   Limits: 128 * cols < 2^31.
  */
 QCAST_API int qcast_per_channel(const void* x, int64_t rows, int64_t cols, int fmt, int group,
                                 float clamp_min, void* q, float* sf, void* stream);

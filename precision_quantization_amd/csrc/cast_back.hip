@@ -164,6 +164,11 @@ hipError_t launch_fmt(const void* q, const float* sf, int64_t nchunks, int group
 
 }  // namespace
 
+bool cast_back_fits(int64_t rows, int64_t cols) {
+  const int64_t per_block = (int64_t)kThreads * kUnroll;
+  return (rows * cols / 8 + per_block - 1) / per_block < (int64_t(1) << 31);
+}
+
 hipError_t launch_cast_back(const void* q, const float* sf, int64_t rows, int64_t cols, int fmt,
                             int group, bool out_bf16, void* out, hipStream_t stream,
                             const LaunchCaps& caps) {

@@ -80,6 +80,11 @@ __global__ __launch_bounds__(kThreads) void per_block_kernel(
 
 }  // namespace
 
+bool per_block_fits(int64_t rows, int64_t cols) {
+  const int64_t lim = int64_t(1) << 31;
+  return (rows / kBlock) * (cols / kBlock) < lim && (int64_t)kBlock * cols < lim;
+}
+
 hipError_t launch_per_block(const void* x, int64_t rows, int64_t cols, int fmt, float floor,
                             void* q, float* sf, hipStream_t stream, const LaunchCaps& caps) {
   (void)caps;
@@ -87,8 +92,7 @@ hipError_t launch_per_block(const void* x, int64_t rows, int64_t cols, int fmt, 
   const int64_t nblocks = (rows / kBlock) * bcols;
   if (nblocks == 0) return hipSuccess;
   // One workgroup per tile; tile counts and in-tile offsets in 32 bits.
-  const int64_t lim = int64_t(1) << 31;
-  if (nblocks >= lim || (int64_t)kBlock * cols >= lim) return hipErrorInvalidValue;
+  if (!per_block_fits(rows, cols)) return hipErrorInvalidValue;
   if (fmt == kE4M3)
     launch_kernel(per_block_kernel<kE4M3>, dim3((unsigned)nblocks), dim3(kThreads), 0, stream,
                   static_cast<const uint16_t*>(x), (uint32_t)cols, (uint32_t)bcols, floor,

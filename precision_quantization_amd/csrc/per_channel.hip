@@ -106,6 +106,12 @@ __global__ __launch_bounds__(kThreads) void per_channel_kernel(
 
 }  // namespace
 
+bool per_channel_fits(int64_t rows, int64_t cols) {
+  const int64_t lim = int64_t(1) << 31;
+  const int64_t nct = (cols + kTileChannels - 1) / kTileChannels;
+  return (rows / kGroupTokens) * nct < lim && (int64_t)kGroupTokens * cols < lim;
+}
+
 hipError_t launch_per_channel(const void* x, int64_t rows, int64_t cols, int fmt, float floor,
                               void* q, float* sf, hipStream_t stream, const LaunchCaps& caps) {
   (void)caps;
@@ -114,8 +120,7 @@ hipError_t launch_per_channel(const void* x, int64_t rows, int64_t cols, int fmt
   const int64_t ntiles = ngroups * nct;
   if (ntiles == 0) return hipSuccess;
   // Tile counts and in-tile offsets are 32-bit.
-  const int64_t lim = int64_t(1) << 31;
-  if (ntiles >= lim || (int64_t)kGroupTokens * cols >= lim) return hipErrorInvalidValue;
+  if (!per_channel_fits(rows, cols)) return hipErrorInvalidValue;
   auto kernel = fmt == kE4M3 ? per_channel_kernel<kE4M3>
                : fmt == kE5M2 ? per_channel_kernel<kE5M2> : nullptr;
   if (!kernel) return hipErrorInvalidValue;

@@ -447,6 +447,11 @@ hipError_t launch_swiglu_t_fmt(const uint16_t* h, const float* w, int64_t rows, 
 
 }  // namespace
 
+bool per_channel_t_fits(int64_t rows, int64_t cols, int64_t row_stride) {
+  Grid g;
+  return make_grid(rows, cols, row_stride, &g);
+}
+
 hipError_t launch_per_channel_T(const void* x, int64_t rows, int64_t cols, int fmt, float floor,
                                 void* qT, float* sf, hipStream_t stream,
                                 const LaunchCaps& caps) {

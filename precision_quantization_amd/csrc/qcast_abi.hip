@@ -195,7 +195,8 @@ int qcast_swiglu_per_channel_T(const void* h, int64_t rows, int64_t cols, const 
                                float* sf, uint64_t* clamp_count, void* stream) {
   if (!fp8_fmt(fmt)) return QCAST_ERR_FORMAT;
   if (group != 128) return QCAST_ERR_GROUP;
-  if (rows < 0 || cols < 0 || rows % group != 0 || cols % 8 != 0 || too_big(rows, 2 * cols))
+  if (rows < 0 || cols < 0 || rows % group != 0 || cols % 8 != 0 || too_big(rows, 2 * cols) ||
+      !qcast::per_channel_t_fits(rows, cols, 2 * cols))
     return QCAST_ERR_SHAPE;
   if (swiglu_clamp != swiglu_clamp) return QCAST_ERR_VALUE;
   if (rows == 0 || cols == 0) return QCAST_OK;
@@ -223,7 +224,8 @@ int qcast_per_block(const void* x, int64_t rows, int64_t cols, int fmt, int bloc
                     float clamp_min, void* q, float* sf, void* stream) {
   if (!fp8_fmt(fmt)) return QCAST_ERR_FORMAT;
   if (block != 128) return QCAST_ERR_GROUP;
-  if (rows < 0 || cols < 0 || rows % block != 0 || cols % block != 0 || too_big(rows, cols))
+  if (rows < 0 || cols < 0 || rows % block != 0 || cols % block != 0 || too_big(rows, cols) ||
+      !qcast::per_block_fits(rows, cols))
     return QCAST_ERR_SHAPE;
   if (rows == 0 || cols == 0) return QCAST_OK;
   if (!x || !q || !sf) return QCAST_ERR_NULL;
@@ -239,7 +241,8 @@ int qcast_per_channel_T(const void* x, int64_t rows, int64_t cols, int fmt, int 
                         float clamp_min, void* qT, float* sf, void* stream) {
   if (!fp8_fmt(fmt)) return QCAST_ERR_FORMAT;
   if (group != 128) return QCAST_ERR_GROUP;
-  if (rows < 0 || cols < 0 || rows % group != 0 || cols % 8 != 0 || too_big(rows, cols))
+  if (rows < 0 || cols < 0 || rows % group != 0 || cols % 8 != 0 || too_big(rows, cols) ||
+      !qcast::per_channel_t_fits(rows, cols, cols))
     return QCAST_ERR_SHAPE;
   if (rows == 0 || cols == 0) return QCAST_OK;
   if (!x || !qT || !sf) return QCAST_ERR_NULL;
@@ -255,7 +258,8 @@ int qcast_per_channel(const void* x, int64_t rows, int64_t cols, int fmt, int gr
                       float clamp_min, void* q, float* sf, void* stream) {
   if (!fp8_fmt(fmt)) return QCAST_ERR_FORMAT;
   if (group != 128) return QCAST_ERR_GROUP;
-  if (rows < 0 || cols < 0 || rows % group != 0 || cols % 8 != 0 || too_big(rows, cols))
+  if (rows < 0 || cols < 0 || rows % group != 0 || cols % 8 != 0 || too_big(rows, cols) ||
+      !qcast::per_channel_fits(rows, cols))
     return QCAST_ERR_SHAPE;
   if (rows == 0 || cols == 0) return QCAST_OK;
   if (!x || !q || !sf) return QCAST_ERR_NULL;
@@ -272,7 +276,9 @@ int qcast_cast_back(const void* q, const float* sf, int64_t rows, int64_t cols, 
   if (!any_fmt(fmt)) return QCAST_ERR_FORMAT;
   if (out_dtype != QCAST_OUT_BF16 && out_dtype != QCAST_OUT_F32) return QCAST_ERR_FORMAT;
   if (!per_token_group_ok(group)) return QCAST_ERR_GROUP;
-  if (rows < 0 || cols < 0 || cols % group != 0 || too_big(rows, cols)) return QCAST_ERR_SHAPE;
+  if (rows < 0 || cols < 0 || cols % group != 0 || too_big(rows, cols) ||
+      !qcast::cast_back_fits(rows, cols))
+    return QCAST_ERR_SHAPE;
   if (rows == 0 || cols == 0) return QCAST_OK;
   if (!q || !sf || !out) return QCAST_ERR_NULL;
   if (!aligned(q, 16) || !aligned(sf, 4) || !aligned(out, 16)) return QCAST_ERR_ALIGN;

@@ -29,6 +29,13 @@ inline void launch_kernel(void (*kernel)(KArgs...), dim3 grid, dim3 block, uint3
   hipExtLaunchKernelGGL(kernel, grid, block, shmem, stream, t.start, t.stop, 0u, args...);
 }
 
+// Whether a shape fits the kernels' 32-bit tile counts and in-tile offsets
+// (checked by the C ABI before any HIP call; the launchers check again).
+bool per_block_fits(int64_t rows, int64_t cols);
+bool per_channel_t_fits(int64_t rows, int64_t cols, int64_t row_stride);
+bool per_channel_fits(int64_t rows, int64_t cols);
+bool cast_back_fits(int64_t rows, int64_t cols);
+
 // Launch shape knobs shared by the launchers.
 struct LaunchCaps {
   int num_cus;          // compute units on the device (or the override)

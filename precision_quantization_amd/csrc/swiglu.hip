@@ -46,8 +46,12 @@ namespace {
 #ifndef QCAST_SW_COUNT_BLOCK
 #define QCAST_SW_COUNT_BLOCK 1024
 #endif
+#ifndef QCAST_SW_COUNT_UNROLL
+#define QCAST_SW_COUNT_UNROLL 1
+#endif
 constexpr int kCountBlock = QCAST_SW_COUNT_BLOCK;
-constexpr int kUnroll = QCAST_SW_UNROLL;
+constexpr int kCountUnroll = QCAST_SW_COUNT_UNROLL;
+constexpr int kStreamUnroll = QCAST_SW_UNROLL;
 constexpr int kWgPerCu = QCAST_SW_WG_PER_CU;
 constexpr int kCountWgPerCu = QCAST_SW_COUNT_WG_PER_CU;
 constexpr float kLog2e = 1.4426950408889634f;
@@ -61,7 +65,7 @@ __device__ __forceinline__ float silu_times(float g, float u) {
   return g * __builtin_amdgcn_rcpf(1.0f + e) * u;
 }
 
-template <int kLanes, bool kWeighted, int kFmt, bool kClamp, int kBlock>
+template <int kLanes, bool kWeighted, int kFmt, bool kClamp, int kBlock, int kUnroll>
 __global__ __launch_bounds__(kBlock) void swiglu_kernel(
     const uint16_t* __restrict__ h, const float* __restrict__ w, int64_t nchunks,
     uint32_t chunks_per_row, uint64_t row_magic, int64_t cols, float floor,
@@ -131,20 +135,20 @@ hipError_t launch(const uint16_t* h, const float* w, int64_t rows, int64_t cols,
     const int64_t nchunks = nr * cpr;
     const bool counting = kClamp && ca.count;
     const int block = counting ? kCountBlock : kThreads;
-    const int64_t per_block_iter = (int64_t)block * kUnroll;
+    const int64_t per_block_iter = (int64_t)block * (counting ? kCountUnroll : kStreamUnroll);
     const int64_t iters = (nchunks + per_block_iter - 1) / per_block_iter;
     const int wg_per_cu = counting ? kCountWgPerCu : kWgPerCu;
     const int64_t max_blocks = wg_per_cu > 0 ? (int64_t)caps.num_cus * wg_per_cu : iters;
     const int64_t iters_per_block = (iters + max_blocks - 1) / max_blocks;
     const int64_t blocks = (iters + iters_per_block - 1) / iters_per_block;
     if (counting)
-      launch_kernel((swiglu_kernel<kLanes, kWeighted, kFmt, kClamp, kCountBlock>),
+      launch_kernel((swiglu_kernel<kLanes, kWeighted, kFmt, kClamp, kCountBlock, kCountUnroll>),
                     dim3((unsigned)blocks), dim3(kCountBlock), 0, stream, h + r0 * 2 * cols,
                     kWeighted ? w + r0 : nullptr, nchunks, (uint32_t)cpr, magic, cols,
                     floor, q + r0 * cols, sf, lay, (uint32_t)(r0 * groups_per_row), ca.c,
                     ca.count);
     else
-      launch_kernel((swiglu_kernel<kLanes, kWeighted, kFmt, kClamp, kThreads>),
+      launch_kernel((swiglu_kernel<kLanes, kWeighted, kFmt, kClamp, kThreads, kStreamUnroll>),
                     dim3((unsigned)blocks), dim3(kThreads), 0, stream, h + r0 * 2 * cols,
                     kWeighted ? w + r0 : nullptr, nchunks, (uint32_t)cpr, magic, cols,
                     floor, q + r0 * cols, sf, lay, (uint32_t)(r0 * groups_per_row), ca.c,

@@ -229,6 +229,24 @@ def test_e5m6_formats(lib):
     assert lib.qcast_bench_check_scale(5, 1, 2, A16, None) == ERR_FORMAT
 
 
+def test_shapes_past_the_32_bit_indexing_are_refused_before_any_hip_call(lib):
+    big = 1 << 24                       # 128 * big = 2^31
+    assert lib.qcast_per_block(A16, 128, big, E4M3, 128, 0.0, A16, A16, None) == ERR_SHAPE
+    assert lib.qcast_per_channel_T(A16, 128, big, E4M3, 128, 0.0, A16, A16, None) == ERR_SHAPE
+    assert lib.qcast_per_channel_T(A16, 1 << 25, 64, E4M3, 128, 0.0, A16, A16, None) == ERR_SHAPE
+    assert lib.qcast_per_channel(A16, 128, big, E4M3, 128, 0.0, A16, A16, None) == ERR_SHAPE
+    assert lib.qcast_swiglu_per_channel_T(A16, 128, 1 << 23, None, E4M3, 128, 0.0, 0.0, A16, A16,
+                                          None, None) == ERR_SHAPE
+    assert lib.qcast_per_token(A16, 1 << 24, 1 << 12, E4M3, 32, 0.0, A16, A16, None) == ERR_SHAPE
+    assert lib.qcast_cast_back(A16, A16, 1 << 30, 1 << 13, E4M3, 128, 1, A16, None) == ERR_SHAPE
+    # the largest shapes that fit pass validation (then find no device here)
+    if not gpu_available():
+        assert lib.qcast_per_block(A16, 128, big - 128, E4M3, 128, 0.0, A16, A16, None) == ERR_DEVICE
+        assert lib.qcast_per_channel_T(A16, 128, big - 8, E4M3, 128, 0.0, A16, A16,
+                                       None) == ERR_DEVICE
+        assert lib.qcast_per_channel(A16, 128, big - 8, E4M3, 128, 0.0, A16, A16, None) == ERR_DEVICE
+
+
 def test_time_next_validation(lib):
     assert lib.qcast_bench_time_next(None, A16) == ERR_NULL
     assert lib.qcast_bench_time_next(A16, None) == ERR_NULL
