@@ -272,26 +272,32 @@ __device__ __forceinline__ uint32_t clamp_gate_up(float& g, float& u, float c) {
 
 // E5M6: the IEEE-like 12-bit format with a 5-bit exponent (bias 15) and 6
 // mantissa bits, sign in bit 11 -- the top 12 bits of an fp16 pattern. No
-// hardware conversion exists for it: the code is formed from the fp32 bits.
-// Normal range (|y| >= 2^-14): round the 23-bit mantissa to 6 bits, nearest
-// even, by integer addition (a carry moves into the exponent), then rebias
-// the exponent from 127 to 15; beyond the largest finite value the code
-// saturates. Subnormal range: the code is the integer nearest |y| / 2^-20
-// (an exact scaling by a power of two, then v_rndne_f32); 64 is the smallest
-// normal code. A NaN gives the NaN code 0x7ff with its sign.
-__device__ __forceinline__ uint32_t e5m6_code(float y) {
+// hardware conversion rounds to it, so each value is first rounded in fp32
+// onto the E5M6 grid (nearest, ties to even), after which the fp16
+// conversion is exact and the code is the fp16 pattern shifted right by 4.
+// The grid spacing is 2^(e-6) for |y| in [2^e, 2^(e+1)), e >= -14, and
+// 2^-20 below 2^-14 (the subnormals). With C = max(2^(e+17), 8), the fp32
+// sum |y| + C lies in [C, 2C], where fp32 spacing is exactly that grid
+// spacing, so (|y| + C) - C is |y| rounded to the grid with ties to even
+// (C is an even multiple of the spacing) and the subtraction is exact. The
+// sign is put back afterwards (tiny negatives stay -0), and y is first
+// clamped to the largest finite magnitude (saturation).
+__device__ __forceinline__ float e5m6_grid(float y) {
+  constexpr float kMax = 65024.0f;
+  y = __builtin_amdgcn_fmed3f(y, -kMax, kMax);
   const uint32_t b = __float_as_uint(y);
-  const uint32_t a = b & 0x7fffffffu;
-  uint32_t mag;
-  if (a >= 0x38800000u) {
-    const uint32_t r = (a + 0xffffu + ((a >> 17) & 1u)) >> 17;
-    mag = r - (112u << 6);
-    mag = mag > 0x7bfu ? 0x7bfu : mag;
-    mag = a > 0x7f800000u ? 0x7ffu : mag;   // NaN stays NaN
-  } else {
-    mag = (uint32_t)__builtin_rintf(__uint_as_float(a) * 0x1.0p20f);
-  }
-  return ((b >> 20) & 0x800u) | mag;
+  const uint32_t c_bits = (b & 0x7f800000u) + (17u << 23);
+  const float c = __uint_as_float(c_bits > 0x41000000u ? c_bits : 0x41000000u);  // >= 8
+  const float mag = (__builtin_fabsf(y) + c) - c;
+  return __uint_as_float(__float_as_uint(mag) | (b & 0x80000000u));
+}
+
+// Two fp32 on the E5M6 grid -> their two codes in bits 0..11 and 16..27
+// (v_cvt_pkrtz_f16_f32: exact here, so the rounding mode does not matter).
+__device__ __forceinline__ uint32_t e5m6_pair(float y0, float y1) {
+  typedef __fp16 f16x2 __attribute__((ext_vector_type(2)));
+  const f16x2 h = __builtin_amdgcn_cvt_pkrtz(e5m6_grid(y0), e5m6_grid(y1));
+  return (__builtin_bit_cast(uint32_t, h) >> 4) & 0x0fff0fffu;
 }
 
 // Eight fp32 -> eight E5M6 codes as a little-endian bit stream of 96 bits
@@ -300,13 +306,17 @@ struct E5M6x8 {
   uint32_t w0, w1, w2;
 };
 __device__ __forceinline__ E5M6x8 e5m6x8(const float y[8]) {
-  uint32_t c[8];
-#pragma unroll
-  for (int i = 0; i < 8; ++i) c[i] = e5m6_code(y[i]);
+  const uint32_t p0 = e5m6_pair(y[0], y[1]), p1 = e5m6_pair(y[2], y[3]);
+  const uint32_t p2 = e5m6_pair(y[4], y[5]), p3 = e5m6_pair(y[6], y[7]);
+  // p = c_even | c_odd << 16 -> c_even | c_odd << 12 (24 bits)
+  const uint32_t t0 = (p0 & 0xfffu) | ((p0 >> 4) & 0xfff000u);
+  const uint32_t t1 = (p1 & 0xfffu) | ((p1 >> 4) & 0xfff000u);
+  const uint32_t t2 = (p2 & 0xfffu) | ((p2 >> 4) & 0xfff000u);
+  const uint32_t t3 = (p3 & 0xfffu) | ((p3 >> 4) & 0xfff000u);
   E5M6x8 p;
-  p.w0 = c[0] | (c[1] << 12) | (c[2] << 24);
-  p.w1 = (c[2] >> 8) | (c[3] << 4) | (c[4] << 16) | (c[5] << 28);
-  p.w2 = (c[5] >> 4) | (c[6] << 8) | (c[7] << 20);
+  p.w0 = t0 | (t1 << 24);
+  p.w1 = (t1 >> 8) | (t2 << 16);
+  p.w2 = (t2 >> 16) | (t3 << 8);
   return p;
 }
 
