@@ -206,9 +206,10 @@ struct F32Tile {
 constexpr float kLog2e = 1.4426950408889634f;
 
 // Load a tile of the SwiGLU input h [rows, 2 * cols] and form
-// v = silu(g) * u (* w[token]); returns the number of values the clamp
-// changed (clamp > 0 only). Tokens and channels outside the tensor give 0.
-template <bool kWeighted, bool kClamp>
+// v = silu(g) * u (* w[token]); with kCount, returns the number of values the
+// clamp changed in the whole wave (the same in every lane). Tokens and
+// channels outside the tensor give 0 and are never counted.
+template <bool kWeighted, bool kClamp, bool kCount>
 __device__ __forceinline__ uint32_t load_swiglu_tile(const uint16_t* __restrict__ h,
                                                      const float* __restrict__ w, uint32_t cols,
                                                      float clamp, const TileCoord& tc,
@@ -243,7 +244,8 @@ __device__ __forceinline__ uint32_t load_swiglu_tile(const uint16_t* __restrict_
       unpack8(uraw[p][i], uv);
 #pragma unroll
       for (int j = 0; j < 8; ++j) {
-        if (kClamp) nclamp += clamp_gate_up(gv[j], uv[j], clamp);
+        if (kCount) nclamp += wave_clamp_count(gv[j], uv[j], clamp);
+        if (kClamp) clamp_gate_up(gv[j], uv[j], clamp);
         const float e = __builtin_amdgcn_exp2f(-gv[j] * kLog2e);
         float val = gv[j] * __builtin_amdgcn_rcpf(1.0f + e) * uv[j];
         if (kWeighted) val = val * wr[p][i];
@@ -359,17 +361,17 @@ __global__ __launch_bounds__(kThreads) void swiglu_per_channel_t_kernel(
       if (tau >= ntiles) continue;  // uniform over the workgroup
       const TileCoord tc = tile_coord(tau, ngroups, cols, nct, ntiles / nct);
       F32Tile tile;
-      n += load_swiglu_tile<kWeighted, kClamp>(h, w, cols, clamp, tc, tile);
+      n += load_swiglu_tile<kWeighted, kClamp, true>(h, w, cols, clamp, tc, tile);
       process_tile<kFmt>(tc, tile, rows, ngroups, floor, sm, qT, sf);
     }
-    add_count(n, count);
+    add_wave_counts(n, count);
   } else {
     const uint32_t b = blockIdx.x;
     const uint32_t tau = (kOrder & 2) ? b : (b % kXcds) * per_xcd + b / kXcds;
     if (tau >= ntiles) return;
     const TileCoord tc = tile_coord(tau, ngroups, cols, nct, ntiles / nct);
     F32Tile tile;
-    load_swiglu_tile<kWeighted, kClamp>(h, w, cols, clamp, tc, tile);
+    load_swiglu_tile<kWeighted, kClamp, false>(h, w, cols, clamp, tc, tile);
     process_tile<kFmt>(tc, tile, rows, ngroups, floor, sm, qT, sf);
   }
 }

@@ -241,16 +241,13 @@ __device__ __forceinline__ uint32_t e2m1x8(const float y[8]) {
   return w;
 }
 
-// Add a per-lane count into *count (a 64-bit counter in device memory that
-// the caller zeroed or accumulates into): a wave sum, a workgroup sum in
-// LDS, then one vector atomic per workgroup whose sum is not zero. Every
-// thread of the kBlock-thread workgroup must call it (it holds a barrier).
+// Add a wave-uniform count (the same value in every lane of each wave) into
+// *count: one LDS word per wave, then one vector atomic per workgroup whose
+// sum is not zero. Every thread of the kBlock-thread workgroup must call it.
 template <int kBlock = kThreads>
-__device__ __forceinline__ void add_count(uint32_t n, unsigned long long* count) {
+__device__ __forceinline__ void add_wave_counts(uint32_t wave_total, unsigned long long* count) {
   __shared__ uint32_t part[kBlock / 64];
-#pragma unroll
-  for (int o = 32; o >= 1; o >>= 1) n += (uint32_t)__shfl_xor((int)n, o);
-  if ((threadIdx.x & 63) == 0) part[threadIdx.x >> 6] = n;
+  if ((threadIdx.x & 63) == 0) part[threadIdx.x >> 6] = wave_total;
   __syncthreads();
   if (threadIdx.x == 0) {
     uint32_t total = 0;
@@ -260,14 +257,23 @@ __device__ __forceinline__ void add_count(uint32_t n, unsigned long long* count)
   }
 }
 
-// The clamp of the SwiGLU inputs: the gate is bounded from above by c, the
-// up value to [-c, c]; returns how many of the two values it changed.
-// (Written as selects, so a NaN input passes through unclamped.)
-__device__ __forceinline__ uint32_t clamp_gate_up(float& g, float& u, float c) {
-  const uint32_t n = (uint32_t)(g > c) + (uint32_t)(u > c) + (uint32_t)(u < -c);
-  g = g > c ? c : g;
-  u = u > c ? c : (u < -c ? -c : u);
-  return n;
+// Number of active lanes of the wave where pred holds (wave-uniform: a
+// ballot and a scalar bit count, no vector ALU work beyond the compare).
+__device__ __forceinline__ uint32_t wave_count(bool pred) {
+  return (uint32_t)__builtin_popcountll(__builtin_amdgcn_ballot_w64(pred));
+}
+
+// The clamp of the SwiGLU inputs: the gate is bounded from above by c
+// (v_min_f32), the up value to [-c, c] (v_med3_f32). A NaN input may come
+// out as a bound; NaN inputs are outside what the casts define.
+__device__ __forceinline__ void clamp_gate_up(float& g, float& u, float c) {
+  g = __builtin_fminf(g, c);
+  u = __builtin_amdgcn_fmed3f(u, -c, c);
+}
+
+// How many of the wave's active gate and up values the clamp changes.
+__device__ __forceinline__ uint32_t wave_clamp_count(float g, float u, float c) {
+  return wave_count(g > c) + wave_count(u > c) + wave_count(u < -c);
 }
 
 // E5M6: the IEEE-like 12-bit format with a 5-bit exponent (bias 15) and 6

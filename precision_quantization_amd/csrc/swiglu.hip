@@ -65,7 +65,8 @@ __device__ __forceinline__ float silu_times(float g, float u) {
   return g * __builtin_amdgcn_rcpf(1.0f + e) * u;
 }
 
-template <int kLanes, bool kWeighted, int kFmt, bool kClamp, int kBlock, int kUnroll>
+template <int kLanes, bool kWeighted, int kFmt, bool kClamp, bool kCount, int kBlock,
+          int kUnroll>
 __global__ __launch_bounds__(kBlock) void swiglu_kernel(
     const uint16_t* __restrict__ h, const float* __restrict__ w, int64_t nchunks,
     uint32_t chunks_per_row, uint64_t row_magic, int64_t cols, float floor,
@@ -98,7 +99,8 @@ __global__ __launch_bounds__(kBlock) void swiglu_kernel(
         unpack8(uraw[u], uv);
 #pragma unroll
         for (int i = 0; i < 8; ++i) {
-          if (kClamp) nclamp += clamp_gate_up(gv[i], uv[i], clamp);
+          if (kCount) nclamp += wave_clamp_count(gv[i], uv[i], clamp);
+          if (kClamp) clamp_gate_up(gv[i], uv[i], clamp);
           v[i] = silu_times(gv[i], uv[i]);
           if (kWeighted) v[i] = v[i] * wr[u];
         }
@@ -113,7 +115,7 @@ __global__ __launch_bounds__(kBlock) void swiglu_kernel(
       }
     }
   }
-  if (kClamp && count) add_count<kBlock>(nclamp, count);
+  if (kCount) add_wave_counts<kBlock>(nclamp, count);
 }
 
 struct ClampArgs {
@@ -142,13 +144,15 @@ hipError_t launch(const uint16_t* h, const float* w, int64_t rows, int64_t cols,
     const int64_t iters_per_block = (iters + max_blocks - 1) / max_blocks;
     const int64_t blocks = (iters + iters_per_block - 1) / iters_per_block;
     if (counting)
-      launch_kernel((swiglu_kernel<kLanes, kWeighted, kFmt, kClamp, kCountBlock, kCountUnroll>),
+      launch_kernel((swiglu_kernel<kLanes, kWeighted, kFmt, kClamp, kClamp, kCountBlock,
+                                   kCountUnroll>),
                     dim3((unsigned)blocks), dim3(kCountBlock), 0, stream, h + r0 * 2 * cols,
                     kWeighted ? w + r0 : nullptr, nchunks, (uint32_t)cpr, magic, cols,
                     floor, q + r0 * cols, sf, lay, (uint32_t)(r0 * groups_per_row), ca.c,
                     ca.count);
     else
-      launch_kernel((swiglu_kernel<kLanes, kWeighted, kFmt, kClamp, kThreads, kStreamUnroll>),
+      launch_kernel((swiglu_kernel<kLanes, kWeighted, kFmt, kClamp, false, kThreads,
+                                   kStreamUnroll>),
                     dim3((unsigned)blocks), dim3(kThreads), 0, stream, h + r0 * 2 * cols,
                     kWeighted ? w + r0 : nullptr, nchunks, (uint32_t)cpr, magic, cols,
                     floor, q + r0 * cols, sf, lay, (uint32_t)(r0 * groups_per_row), ca.c,
