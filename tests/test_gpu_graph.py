@@ -1,0 +1,80 @@
+"""The casts under HIP graph capture: a graph of one pass of the five casts
+(through the C ABI, on torch's capture stream) is replayed several times,
+with eager casts and synchronizations between the replays, and every replay
+must equal the eager result bit for bit. The library allocates nothing and
+records no memset, so its launches are capturable as they are.
+"""
+import pytest
+import torch
+
+import precision_quantization_amd as pq
+from precision_quantization_amd import workloads
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module")
+def dev():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    return torch.device("cuda:0")
+
+
+def five_casts(ins, outs):
+    x, h, w, wt, a, xt = ins
+    pq.qcast_per_token(x, "e4m3", 128, out=outs[0], out_sf=outs[1])
+    pq.qcast_swiglu_per_token(h, w, "e4m3", 128, out=outs[2], out_sf=outs[3])
+    pq.qcast_per_block(wt, "e4m3", 128, out=outs[4], out_sf=outs[5])
+    pq.qcast_per_channel_T(a, "e4m3", 128, out=outs[6], out_sf=outs[7])
+    pq.qcast_e2m1(xt, 32, out=outs[8], out_sf=outs[9])
+
+
+def test_graph_replays_match_eager(dev):
+    ins = (workloads.per_token_hidden(rows=256).x.to(dev),
+           workloads.swiglu_input(rows=512).x.to(dev), workloads.swiglu_input(rows=512).w.to(dev),
+           workloads.weight_block(rows=512, cols=1024).x.to(dev),
+           workloads.activation_channel(rows=1024, cols=512).x.to(dev),
+           workloads.student_t(rows=512, cols=1024).x.to(dev))
+    x, h, w, wt, a, xt = ins
+    f8 = torch.float8_e4m3fn
+
+    def alloc():
+        return [torch.empty(256, 7168, dtype=f8, device=dev),
+                torch.empty(256, 56, device=dev),
+                torch.empty(512, 2048, dtype=f8, device=dev),
+                torch.empty(512, 16, device=dev),
+                torch.empty(512, 1024, dtype=f8, device=dev),
+                torch.empty(4, 8, device=dev),
+                torch.empty(512, 1024, dtype=f8, device=dev),
+                torch.empty(512, 8, device=dev),
+                torch.empty(512, 512, dtype=torch.uint8, device=dev),
+                torch.empty(512, 32, device=dev)]
+
+    eager = alloc()
+    five_casts(ins, eager)
+    torch.cuda.synchronize()
+    ref = [t.view(torch.uint8).clone() for t in eager]
+
+    graph_outs = alloc()
+    for t in graph_outs:
+        t.view(torch.uint8).fill_(0xA5)
+    side = torch.cuda.Stream(dev)
+    side.wait_stream(torch.cuda.current_stream(dev))
+    with torch.cuda.stream(side):          # warm-up on the capture stream
+        five_casts(ins, graph_outs)
+    torch.cuda.current_stream(dev).wait_stream(side)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        five_casts(ins, graph_outs)
+    for replay in range(4):
+        for t in graph_outs:
+            t.view(torch.uint8).fill_(0x5A + replay)
+        torch.cuda.synchronize()
+        g.replay()
+        five_casts(ins, eager)               # eager work between the replays
+        torch.cuda.synchronize()
+        for i, (t, r) in enumerate(zip(graph_outs, ref)):
+            assert torch.equal(t.view(torch.uint8), r), (replay, i)
+        for t, r in zip(eager, ref):
+            assert torch.equal(t.view(torch.uint8), r)
