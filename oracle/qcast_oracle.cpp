@@ -57,6 +57,14 @@
  *    two) scale as its biased exponent byte, 4 per 32-bit word along the
  *    groups of a row, lowest group in the lowest byte.
  *
+ * Pins (tests/test_oracle_*.py) hold every function to sources other than
+ * itself. One step is parity unpinned at the bit level: the SwiGLU forms
+ * (forward, backward, fused) call the host libm's expf, which nothing here
+ * checks against a correctly rounded exponential; they are pinned to within
+ * 2^-21 relative by a double-precision restatement (forward) and by float64
+ * automatic differentiation (backward), and the GPU kernels are held to a
+ * tolerance there, not to bit equality.
+ *
  * Arithmetic discipline: plain C++ on one thread, fp32 where the method is
  * fp32 (the scale, the inverse, the scaled value, SwiGLU) with no
  * contraction, no fast-math, and denormals kept (checked at every entry).
