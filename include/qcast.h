@@ -67,7 +67,8 @@ extern "C" {
 typedef enum {
   QCAST_OK = 0,
   QCAST_ERR_NULL = 1,   /* a required pointer is NULL */
-  QCAST_ERR_SHAPE = 2,  /* negative size, or sizes not divisible as required */
+  QCAST_ERR_SHAPE = 2,  /* negative size, sizes not divisible as required, or past the
+                           32-bit indexing limits */
   QCAST_ERR_ALIGN = 3,  /* a pointer is not aligned as required */
   QCAST_ERR_FORMAT = 4, /* format not supported by this entry point */
   QCAST_ERR_GROUP = 5,  /* group / block size not supported */

@@ -94,7 +94,9 @@ const char* qcast_status_str(int status) {
   switch (status) {
     case QCAST_OK: return "ok";
     case QCAST_ERR_NULL: return "a required pointer is NULL";
-    case QCAST_ERR_SHAPE: return "unsupported shape (negative, or not divisible as required)";
+    case QCAST_ERR_SHAPE:
+      return "unsupported shape (negative, not divisible as required, or past the 32-bit "
+             "indexing limits)";
     case QCAST_ERR_ALIGN: return "pointer not aligned as required";
     case QCAST_ERR_FORMAT: return "format not supported by this entry point";
     case QCAST_ERR_GROUP: return "group or block size not supported";
