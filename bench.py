@@ -19,8 +19,9 @@ with the default 50 steps every kernel is timed on 10 of its launches. The roofl
 step. The CPU baseline is the oracle (single thread) on the first half of the
 rows of every workload, on this host.
 
-"other_kernels" times, after the step and outside `value`, the casts that
-are not among the five: cast_back of the per-token codes to bf16, the
+"other_kernels" times, after the step and outside `value`, the small
+per-token workload X[128, 512] next to the launch floor (a 16-byte copy),
+and the casts that are not among the five: cast_back of the per-token codes to bf16, the
 per-token cast with 1 x 32 groups and packed UE8M0 column-major scales, the
 per-token E5M6 cast and its cast_back,
 SwiGLU with the clamp and counter, SwiGLU + per-channel cast + transpose,
@@ -82,12 +83,12 @@ class HipEvents:
         self.hip.hipEventDestroy(e)
 
 
-def make_events(hev, n, steps, rotate=True):
+def make_events(hev, n, steps):
     """Event pairs for the kernel launches that are timed: with at least two
     steps per kernel, step s times kernel s mod n only (each timed launch
     costs its dispatch about 1.6 us, so timing one launch per step keeps the
     step close to an untimed one); with fewer steps every launch is timed."""
-    rotate = rotate and steps >= 2 * n
+    rotate = steps >= 2 * n
     return [[(hev.create(), hev.create()) if (not rotate or i == s % n) else None
              for i in range(n)] for s in range(steps)]
 
@@ -174,6 +175,17 @@ def extra_calls(wls, dev):
     from precision_quantization_amd import workloads as W
     by = dict(wls)
     calls = []
+    # the small per-token workload (128 x 512): far below the bandwidth
+    # regime, it measures the launch floor, next to a 16-byte copy
+    xs = W.per_token_small().x.to(dev)
+    qs0 = torch.empty(128, 512, dtype=torch.float8_e4m3fn, device=dev)
+    ss0 = torch.empty(128, 4, dtype=torch.float32, device=dev)
+    calls.append(("per_token_small", [128, 512], W.per_token_small().algorithmic_bytes(),
+                  lambda: pq.qcast_per_token(xs, "e4m3", 128, out=qs0, out_sf=ss0)))
+    tiny_src = torch.zeros(16, dtype=torch.uint8, device=dev)
+    tiny_dst = torch.empty(16, dtype=torch.uint8, device=dev)
+    calls.append(("launch_floor_copy16", [16], 32,
+                  lambda: pq.qcast_bench_copy(tiny_src, tiny_dst)))
     # cast_back: per-token E4M3 codes of the hidden-state workload -> bf16
     x = by["per_token"].x.to(dev)
     r, c = x.shape
@@ -242,13 +254,17 @@ def time_extras(extras, dev, steps, warmup):
             fn()
     torch.cuda.synchronize()
     hev = HipEvents()
-    ev = make_events(hev, len(extras), steps, rotate=False)
+    # the same one-timed-launch-per-pass rotation as the step, over enough
+    # passes to time every cast at least 10 times
+    passes = max(steps, 10 * len(extras))
+    ev = make_events(hev, len(extras), passes)
     timed_runs([fn for *_, fn in extras], ev)
     ms_all = collect(ev, hev)
     out = {}
     for (name, shape, b, _), ms in zip(extras, ms_all):
         avg = sum(ms) / len(ms)
-        out[name] = {"shape": shape, "bytes": b, "avg_us": round(avg * 1e3, 2),
+        out[name] = {"shape": shape, "bytes": b, "timed_launches": len(ms),
+                     "avg_us": round(avg * 1e3, 2),
                      "median_us": round(ms[len(ms) // 2] * 1e3, 2),
                      "GBps": round(b / (avg * 1e-3) / 1e9, 1),
                      "frac": round(b / (avg * 1e-3) / 1e9 / PEAK_HBM_GBS, 4)}
