@@ -73,27 +73,30 @@ __global__ __launch_bounds__(kBlock) void swiglu_kernel(
     uint8_t* __restrict__ q, void* __restrict__ sf, SfLayout lay, uint32_t group0,
     float clamp, unsigned long long* __restrict__ count) {
   uint32_t nclamp = 0;
-  const int64_t step = (int64_t)gridDim.x * kBlock * kUnroll;
-  for (int64_t base = (int64_t)blockIdx.x * kBlock * kUnroll + threadIdx.x; base < nchunks;
-       base += step) {
+  // nchunks < 2^24 per launch: every chunk index and in-slab offset is 32-bit
+  const uint32_t n32 = (uint32_t)nchunks;
+  const u32x4* h4 = reinterpret_cast<const u32x4*>(h);
+  const uint32_t row_chunks = 2 * chunks_per_row;
+  const uint32_t step = gridDim.x * kBlock * kUnroll;
+  for (uint32_t base = blockIdx.x * kBlock * kUnroll + threadIdx.x; base < n32; base += step) {
     u32x4 graw[kUnroll], uraw[kUnroll];
     float wr[kUnroll];
 #pragma unroll
     for (int u = 0; u < kUnroll; ++u) {
-      const int64_t c = base + (int64_t)u * kBlock;
-      if (c < nchunks) {
+      const uint32_t c = base + u * kBlock;
+      if (c < n32) {
         const uint32_t row = (uint32_t)(((uint64_t)c * row_magic) >> 40);
-        const uint32_t jc = (uint32_t)c - row * chunks_per_row;
-        const u32x4* g = reinterpret_cast<const u32x4*>(h + (int64_t)row * 2 * cols) + jc;
-        graw[u] = load_stream(g);
-        uraw[u] = load_stream(g + chunks_per_row);
+        const uint32_t jc = c - row * chunks_per_row;
+        const uint32_t gi = row * row_chunks + jc;
+        graw[u] = load_stream(h4 + gi);
+        uraw[u] = load_stream(h4 + (gi + chunks_per_row));
         wr[u] = kWeighted ? w[row] : 1.0f;
       }
     }
 #pragma unroll
     for (int u = 0; u < kUnroll; ++u) {
-      const int64_t c = base + (int64_t)u * kBlock;
-      if (c < nchunks) {
+      const uint32_t c = base + u * kBlock;
+      if (c < n32) {
         float gv[8], uv[8], v[8];
         unpack8(graw[u], gv);
         unpack8(uraw[u], uv);
@@ -107,11 +110,12 @@ __global__ __launch_bounds__(kBlock) void swiglu_kernel(
         const float amax = lane_group_max<kLanes>(absmax8(v));
         Scale s = group_scale<kFmt>(amax, floor);
         if (lay.flags & kSfRound) s = round_scale_pow2(s);
+        const float ys = s.inv;
         u32x2 out;
-        out.x = fp8x4<kFmt>(v[0] * s.inv, v[1] * s.inv, v[2] * s.inv, v[3] * s.inv);
-        out.y = fp8x4<kFmt>(v[4] * s.inv, v[5] * s.inv, v[6] * s.inv, v[7] * s.inv);
+        out.x = fp8x4<kFmt>(v[0] * ys, v[1] * ys, v[2] * ys, v[3] * ys);
+        out.y = fp8x4<kFmt>(v[4] * ys, v[5] * ys, v[6] * ys, v[7] * ys);
         store_stream(reinterpret_cast<u32x2*>(q) + c, out);
-        store_group_scale<kLanes>(sf, group0 + (uint32_t)(c / kLanes), s, lay);
+        store_group_scale<kLanes>(sf, group0 + c / kLanes, s, lay);
       }
     }
   }
