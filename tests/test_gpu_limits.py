@@ -71,8 +71,10 @@ def test_per_channel_at_the_column_limit(dev):
     torch.cuda.empty_cache()
 
 
-def test_per_block_at_the_column_limit(dev):
-    rows, cols = 256, (1 << 24) - 128        # 128 * cols just below 2^31
+# 128 * cols just below 2^31, with an odd and an even number of tile columns
+@pytest.mark.parametrize("cols", [(1 << 24) - 128, (1 << 24) - 256])
+def test_per_block_at_the_column_limit(dev, cols):
+    rows = 256
     x = big_input(dev, rows, cols, 103)
     q, sf = pq.qcast_per_block(x)
     for b in sample(cols // 128, 24, 1, 3):

@@ -180,7 +180,7 @@ def test_per_token_shapes(dev, fmt, group, rows, cols):
     assert_exact("per_token", x.to(torch.bfloat16), dev, fmt, group)
 
 
-@pytest.mark.parametrize("rows,cols", [(128, 128), (256, 384), (384, 1152)])
+@pytest.mark.parametrize("rows,cols", [(128, 128), (256, 384), (384, 1152), (128, 256), (640, 1280)])
 def test_per_block_shapes(dev, rows, cols):
     g = torch.Generator().manual_seed(rows + cols)
     x = torch.randn(rows, cols, generator=g)
