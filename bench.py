@@ -15,9 +15,10 @@ value = algorithmic bytes of the whole step (inputs read once, codes and
 scales written once) / time per step, in GB/s. Per-kernel durations come from
 HIP events that kernels of the timed steps record from their own dispatch on
 the launch stream (qcast_bench_time_next): step s times kernel s mod 5, so
-with the default 50 steps every kernel is timed on 10 of its launches. The roofline object is for the kernel with the largest share of the
-step. The CPU baseline is the oracle (single thread) on the first half of the
-rows of every workload, on this host.
+with the default 50 steps every kernel is timed on 10 of its launches (their
+average, median, 10th and 90th percentile). The roofline object is for the
+kernel with the largest share of the step. The CPU baseline is the oracle
+(single thread) on every workload in full, on this host (about 10 s).
 
 "other_kernels" times, after the step and outside `value`, the small
 per-token workload X[128, 512] next to the launch floor (a 16-byte copy),
@@ -31,6 +32,7 @@ the SwiGLU backward cast, and the per-channel cast in the input layout.
 """
 import argparse
 import json
+import math
 import os
 import platform
 import sys
@@ -118,6 +120,14 @@ def collect(ev, hev):
                 hev.destroy(pair[0])
                 hev.destroy(pair[1])
     return out
+
+
+def spread_us(ms):
+    """Median, 10th and 90th percentile (nearest rank) of sorted durations in
+    ms, as microseconds."""
+    def at(q):
+        return round(ms[min(len(ms) - 1, max(0, math.ceil(q * len(ms)) - 1))] * 1e3, 2)
+    return {"median_us": at(0.5), "p10_us": at(0.1), "p90_us": at(0.9)}
 
 
 def make_workloads():
@@ -264,8 +274,7 @@ def time_extras(extras, dev, steps, warmup):
     for (name, shape, b, _), ms in zip(extras, ms_all):
         avg = sum(ms) / len(ms)
         out[name] = {"shape": shape, "bytes": b, "timed_launches": len(ms),
-                     "avg_us": round(avg * 1e3, 2),
-                     "median_us": round(ms[len(ms) // 2] * 1e3, 2),
+                     "avg_us": round(avg * 1e3, 2), **spread_us(ms),
                      "GBps": round(b / (avg * 1e-3) / 1e9, 1),
                      "frac": round(b / (avg * 1e-3) / 1e9 / PEAK_HBM_GBS, 4)}
     return out
@@ -297,9 +306,10 @@ def copy_ceiling(dev, nbytes):
     return 2 * half / (ms * 1e-3) / 1e9
 
 
-def cpu_baseline(wls, fraction=0.5):
+def cpu_baseline(wls, fraction=1.0):
     """The oracle, single-threaded, on the first `fraction` of the rows of
-    every workload; GB/s over the same algorithmic bytes."""
+    every workload (all of them by default: about 10 s of CPU work); GB/s
+    over the same algorithmic bytes."""
     import oracle
     from precision_quantization_amd import workloads as W
     total_bytes = 0
@@ -384,8 +394,7 @@ def main():
         b = wl.algorithmic_bytes()
         kernels[name] = {
             "shape": list(wl.x.shape), "bytes": b, "timed_launches": len(ms),
-            "avg_us": round(avg * 1e3, 2),
-            "median_us": round(ms[len(ms) // 2] * 1e3, 2),
+            "avg_us": round(avg * 1e3, 2), **spread_us(ms),
             "GBps": round(b / (avg * 1e-3) / 1e9, 1),
             "frac": round(b / (avg * 1e-3) / 1e9 / PEAK_HBM_GBS, 4),
             "rows_per_s": round(wl.rows / (avg * 1e-3)),
@@ -432,7 +441,7 @@ def main():
         gbs, secs = cpu_baseline(wls)
         result["cpu_baseline"] = {
             "value": round(gbs, 4), "unit": "GB/s", "cores": 1, "kind": "oracle",
-            "sample": f"first half of the rows of each of the five workloads "
+            "sample": f"all rows of each of the five workloads, one oracle call each "
                       f"({secs:.1f} s on {platform.processor() or platform.machine()}, "
                       f"{os.cpu_count()} cores present)",
         }
