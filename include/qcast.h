@@ -58,7 +58,10 @@
 extern "C" {
 #endif
 
-#define QCAST_ABI_VERSION 2
+#define QCAST_ABI_VERSION 3
+
+/* Bytes of the optional clamp-count workspace (count_ws) of the SwiGLU casts. */
+#define QCAST_COUNT_WS_BYTES 8192
 
 #ifndef QCAST_API
 #define QCAST_API __attribute__((visibility("default")))
@@ -182,12 +185,23 @@ QCAST_API int qcast_swiglu_per_token_sf(const void* h, int64_t rows, int64_t col
  *                 number of gate and up values the clamp changed is ADDED
  *                 (atomically; the caller zeroes it, or lets it accumulate
  *                 over calls). Untouched when c <= 0.
+ *   count_ws      NULL, or QCAST_COUNT_WS_BYTES of device memory (128-byte
+ *                 aligned) that is all zero before the call; the call leaves
+ *                 it all zero again once its kernels end. With it the
+ *                 counting kernel spreads its atomics over the workspace and
+ *                 runs the full grid (measured 20% faster on 8192 x 2048
+ *                 outputs); without it, a capped grid adds into clamp_count
+ *                 directly. Calls that may run at the same time (on
+ *                 different streams) need different workspaces; calls in
+ *                 order on one stream may share one. Ignored unless
+ *                 clamp_count is given and c > 0.
  *   Everything else as qcast_swiglu_per_token_sf.
  */
 QCAST_API int qcast_swiglu_per_token_ex(const void* h, int64_t rows, int64_t cols,
                                         const float* row_weight, int fmt, int group,
                                         float clamp_min, int sf_flags, float swiglu_clamp,
-                                        void* q, void* sf, uint64_t* clamp_count, void* stream);
+                                        void* q, void* sf, uint64_t* clamp_count,
+                                        void* count_ws, void* stream);
 
 /*
  * SwiGLU backward fused with the per-token cast of the input gradient
@@ -219,13 +233,13 @@ QCAST_API int qcast_swiglu_backward_per_token(const void* h, const void* dv, int
  *   qT  [cols, rows] bytes: qT[c][t] is the code of v[t][c].
  *   sf  [cols, rows/group] fp32, groups of `group` tokens of one channel.
  *   group must be 128; rows % group == 0; cols % 8 == 0;
- *   fmt QCAST_FMT_E4M3 or QCAST_FMT_E5M2; clamp_count as above.
+ *   fmt QCAST_FMT_E4M3 or QCAST_FMT_E5M2; clamp_count and count_ws as above.
  *   Limits: 256 * cols < 2^31, 64 * rows < 2^31.
  */
 QCAST_API int qcast_swiglu_per_channel_T(const void* h, int64_t rows, int64_t cols,
                                          const float* row_weight, int fmt, int group,
                                          float clamp_min, float swiglu_clamp, void* qT, float* sf,
-                                         uint64_t* clamp_count, void* stream);
+                                         uint64_t* clamp_count, void* count_ws, void* stream);
 
 /*
  * Per-block cast of a weight ([SPLIT] §二 per_block_cast; [NEWS]

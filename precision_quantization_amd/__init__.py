@@ -78,6 +78,37 @@ def _counter(clamp_count, device):
     return clamp_count.data_ptr()
 
 
+COUNT_WS_BYTES = 8192           # QCAST_COUNT_WS_BYTES
+_count_ws_cache = {}
+
+
+def _count_ws(count_workspace, clamp_count, device, stream_handle):
+    """Device pointer of the clamp-count workspace (QCAST_COUNT_WS_BYTES,
+    zero between calls): the caller's tensor; none when ``count_workspace``
+    is False, when nothing is counted, or (for the default None) under graph
+    capture without a workspace made for that stream beforehand; else, for
+    None, one zeroed int64 tensor kept per device and stream (each call
+    leaves it zeroed, and calls on one stream are ordered)."""
+    if clamp_count is None or count_workspace is False:
+        return None
+    if count_workspace is None:
+        key = (device, stream_handle)
+        ws = _count_ws_cache.get(key)
+        if ws is None:
+            if torch.cuda.is_current_stream_capturing():
+                return None
+            ws = torch.zeros(COUNT_WS_BYTES // 8, dtype=torch.int64, device=device)
+            torch.cuda.synchronize(device)   # zeroed before any stream uses it
+            _count_ws_cache[key] = ws
+        return ws.data_ptr()
+    if not isinstance(count_workspace, torch.Tensor) or count_workspace.device != device or \
+            not count_workspace.is_contiguous() or \
+            count_workspace.numel() * count_workspace.element_size() < COUNT_WS_BYTES:
+        raise QcastError(2, f"count_workspace must be a contiguous tensor of at least "
+                            f"{COUNT_WS_BYTES} bytes on h's device")
+    return count_workspace.data_ptr()
+
+
 def code_shape(fmt, rows, cols):
     """Shape of the uint8/float8 code tensor of a per-token cast."""
     f = fmt_id(fmt)
@@ -164,10 +195,11 @@ def qcast_swiglu_per_token_sf(h, row_weight=None, fmt="e4m3", group=128, clamp_m
 
 def qcast_swiglu_per_token_ex(h, row_weight=None, fmt="e4m3", group=128, clamp_min=0.0,
                               sf_flags=0, swiglu_clamp=0.0, clamp_count=None, out=None,
-                              out_sf=None, stream=None):
+                              out_sf=None, stream=None, count_workspace=None):
     """SwiGLU with the optional clamp (gate <= c, up in [-c, c]) fused with the
     per-token cast. ``clamp_count``: an int64 [1] device tensor to which the
-    number of clamped values is added, or None."""
+    number of clamped values is added, or None. ``count_workspace``: see
+    ``_count_ws`` (the default keeps one per device and stream)."""
     f = fmt_id(fmt)
     h = _bf16_input(h, "h")
     rows, two_n = h.shape
@@ -178,10 +210,11 @@ def qcast_swiglu_per_token_ex(h, row_weight=None, fmt="e4m3", group=128, clamp_m
     shape, dt = sf_layout_shape(rows, cols, group if group > 0 else 1, sf_flags)
     out_sf = _out(out_sf, shape, dt, h.device, "out_sf")
     with torch.cuda.device(h.device):
+        sh = _stream(h.device, stream)
+        wsptr = _count_ws(count_workspace, clamp_count, h.device, sh)
         check(load().qcast_swiglu_per_token_ex(h.data_ptr(), rows, cols, wptr, f, group, clamp_min,
                                                sf_flags, swiglu_clamp, out.data_ptr(),
-                                               out_sf.data_ptr(), cptr,
-                                               _stream(h.device, stream)),
+                                               out_sf.data_ptr(), cptr, wsptr, sh),
               "qcast_swiglu_per_token_ex")
     return out, out_sf
 
@@ -213,9 +246,10 @@ def qcast_swiglu_backward_per_token(h, dv, row_weight=None, fmt="e4m3", group=12
 
 def qcast_swiglu_per_channel_T(h, row_weight=None, fmt="e4m3", group=128, clamp_min=0.0,
                                swiglu_clamp=0.0, clamp_count=None, out=None, out_sf=None,
-                               stream=None):
+                               stream=None, count_workspace=None):
     """SwiGLU fused with the per-channel cast written transposed:
-    ``out [cols, rows]``, ``out_sf [cols, rows/group]``."""
+    ``out [cols, rows]``, ``out_sf [cols, rows/group]``; ``clamp_count`` and
+    ``count_workspace`` as in qcast_swiglu_per_token_ex."""
     f = fmt_id(fmt)
     h = _bf16_input(h, "h")
     rows, two_n = h.shape
@@ -226,10 +260,11 @@ def qcast_swiglu_per_channel_T(h, row_weight=None, fmt="e4m3", group=128, clamp_
     out_sf = _out(out_sf, (cols, rows // group if group > 0 else 0), torch.float32, h.device,
                   "out_sf")
     with torch.cuda.device(h.device):
+        sh = _stream(h.device, stream)
+        wsptr = _count_ws(count_workspace, clamp_count, h.device, sh)
         check(load().qcast_swiglu_per_channel_T(h.data_ptr(), rows, cols, wptr, f, group,
                                                 clamp_min, swiglu_clamp, out.data_ptr(),
-                                                out_sf.data_ptr(), cptr,
-                                                _stream(h.device, stream)),
+                                                out_sf.data_ptr(), cptr, wsptr, sh),
               "qcast_swiglu_per_channel_T")
     return out, out_sf
 

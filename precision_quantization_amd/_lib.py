@@ -62,10 +62,11 @@ def load():
         "qcast_per_token_sf": [vp, i64, i64, i32, i32, f32, i32, vp, vp, vp],
         "qcast_swiglu_per_token_sf": [vp, i64, i64, vp, i32, i32, f32, i32, vp, vp, vp],
         "qcast_swiglu_per_token_ex": [vp, i64, i64, vp, i32, i32, f32, i32, f32, vp, vp, vp,
-                                      vp],
+                                      vp, vp],
         "qcast_swiglu_backward_per_token": [vp, vp, i64, i64, vp, i32, i32, f32, f32, vp, vp,
                                             vp],
-        "qcast_swiglu_per_channel_T": [vp, i64, i64, vp, i32, i32, f32, f32, vp, vp, vp, vp],
+        "qcast_swiglu_per_channel_T": [vp, i64, i64, vp, i32, i32, f32, f32, vp, vp, vp, vp,
+                                       vp],
         "qcast_per_channel": [vp, i64, i64, i32, i32, f32, vp, vp, vp],
     }
     for name, args in sig.items():

@@ -343,18 +343,21 @@ __global__ __launch_bounds__(kThreads) void per_channel_t_kernel(
   process_tile<kFmt>(tc, tile, rows, ngroups, floor, sm, qT, sf);
 }
 
-// SwiGLU + the same cast. Without a clamp counter (kCount false): one
-// workgroup per tile. With one, every workgroup ends in an atomic add on the
-// same word, serialized where the word lives, so a capped grid walks the
-// virtual workgroup indices [0, vgrid) with a stride of gridDim.x.
-template <int kFmt, bool kWeighted, bool kClamp, bool kCount>
+// SwiGLU + the same cast. Without a clamp counter (kCountNone): one
+// workgroup per tile. With a counter and a count workspace (kCountSlotted):
+// the same, every workgroup (also one past the last tile) ending in one
+// atomic on a workspace slot. With a counter alone (kCountDirect): every
+// workgroup ends in an atomic add on the same word, serialized where the
+// word lives, so a capped grid walks the virtual workgroup indices
+// [0, vgrid) with a stride of gridDim.x.
+template <int kFmt, bool kWeighted, bool kClamp, int kCount>
 __global__ __launch_bounds__(kThreads) void swiglu_per_channel_t_kernel(
     const uint16_t* __restrict__ h, const float* __restrict__ w, uint32_t rows, uint32_t cols,
     uint32_t ngroups, uint32_t nct, uint32_t ntiles, uint32_t per_xcd, uint32_t vgrid,
-    float floor, float clamp, unsigned long long* __restrict__ count, uint8_t* __restrict__ qT,
-    float* __restrict__ sf) {
+    float floor, float clamp, unsigned long long* __restrict__ count,
+    unsigned long long* __restrict__ slots, uint8_t* __restrict__ qT, float* __restrict__ sf) {
   __shared__ __attribute__((aligned(16))) Smem sm;
-  if constexpr (kCount) {
+  if constexpr (kCount == kCountDirect) {
     uint32_t n = 0;
     for (uint32_t b = blockIdx.x; b < vgrid; b += gridDim.x) {
       const uint32_t tau = (kOrder & 2) ? b : (b % kXcds) * per_xcd + b / kXcds;
@@ -368,11 +371,15 @@ __global__ __launch_bounds__(kThreads) void swiglu_per_channel_t_kernel(
   } else {
     const uint32_t b = blockIdx.x;
     const uint32_t tau = (kOrder & 2) ? b : (b % kXcds) * per_xcd + b / kXcds;
-    if (tau >= ntiles) return;
-    const TileCoord tc = tile_coord(tau, ngroups, cols, nct, ntiles / nct);
-    F32Tile tile;
-    load_swiglu_tile<kWeighted, kClamp, false>(h, w, cols, clamp, tc, tile);
-    process_tile<kFmt>(tc, tile, rows, ngroups, floor, sm, qT, sf);
+    uint32_t n = 0;
+    if (tau < ntiles) {  // uniform over the workgroup
+      const TileCoord tc = tile_coord(tau, ngroups, cols, nct, ntiles / nct);
+      F32Tile tile;
+      n = load_swiglu_tile<kWeighted, kClamp, kCount == kCountSlotted>(h, w, cols, clamp, tc,
+                                                                        tile);
+      process_tile<kFmt>(tc, tile, rows, ngroups, floor, sm, qT, sf);
+    }
+    if constexpr (kCount == kCountSlotted) add_wave_counts_slotted(n, slots, count);
   }
 }
 
@@ -407,43 +414,62 @@ bool make_grid(int64_t rows, int64_t cols, int64_t row_stride, Grid* g) {
 #define QCAST_PC_COUNT_WG_PER_CU 4
 #endif
 
+struct CountArgs {
+  unsigned long long* count;  // device counter or null
+  unsigned long long* slots;  // count workspace or null
+};
+
 template <int kFmt, bool kWeighted, bool kClamp>
 hipError_t launch_swiglu_t(const uint16_t* h, const float* w, int64_t rows, int64_t cols,
-                           const Grid& g, float floor, float clamp, unsigned long long* count,
+                           const Grid& g, float floor, float clamp, const CountArgs& ca,
                            uint8_t* qT, float* sf, hipStream_t stream, const LaunchCaps& caps) {
-  if (kClamp && count) {
-    uint32_t grid = g.grid;
-    const int64_t cap = (int64_t)caps.num_cus * QCAST_PC_COUNT_WG_PER_CU;
-    if (QCAST_PC_COUNT_WG_PER_CU > 0 && cap < grid) grid = (uint32_t)cap;
-    launch_kernel((swiglu_per_channel_t_kernel<kFmt, kWeighted, kClamp, true>), dim3(grid),
-                  dim3(kThreads), 0, stream, h, w, (uint32_t)rows, (uint32_t)cols,
-                  g.ngroups, g.nct, g.ntiles, g.per_xcd, g.grid, floor, clamp, count, qT,
-                  sf);
-  } else {
-    launch_kernel((swiglu_per_channel_t_kernel<kFmt, kWeighted, kClamp, false>),
-                  dim3(g.grid), dim3(kThreads), 0, stream, h, w, (uint32_t)rows,
-                  (uint32_t)cols, g.ngroups, g.nct, g.ntiles, g.per_xcd, g.grid, floor,
-                  clamp, count, qT, sf);
+  if constexpr (kClamp) {
+    // The slots count the workgroups that reach them in 24 bits (and the
+    // clamped values in 40: at most 2 * rows * cols, under 2^37 for any h
+    // that fits in memory).
+    const bool slotted =
+        ca.slots && (int64_t)g.grid < (int64_t(kCountSlots) << (64 - kSlotArrivalShift));
+    if (ca.count && slotted) {
+      launch_kernel((swiglu_per_channel_t_kernel<kFmt, kWeighted, true, kCountSlotted>),
+                    dim3(g.grid), dim3(kThreads), 0, stream, h, w, (uint32_t)rows,
+                    (uint32_t)cols, g.ngroups, g.nct, g.ntiles, g.per_xcd, g.grid, floor, clamp,
+                    ca.count, ca.slots, qT, sf);
+      return hipGetLastError();
+    }
+    if (ca.count) {
+      uint32_t grid = g.grid;
+      const int64_t cap = (int64_t)caps.num_cus * QCAST_PC_COUNT_WG_PER_CU;
+      if (QCAST_PC_COUNT_WG_PER_CU > 0 && cap < grid) grid = (uint32_t)cap;
+      launch_kernel((swiglu_per_channel_t_kernel<kFmt, kWeighted, true, kCountDirect>),
+                    dim3(grid), dim3(kThreads), 0, stream, h, w, (uint32_t)rows,
+                    (uint32_t)cols, g.ngroups, g.nct, g.ntiles, g.per_xcd, g.grid, floor, clamp,
+                    ca.count, ca.slots, qT, sf);
+      return hipGetLastError();
+    }
   }
+  launch_kernel((swiglu_per_channel_t_kernel<kFmt, kWeighted, kClamp, kCountNone>),
+                dim3(g.grid), dim3(kThreads), 0, stream, h, w, (uint32_t)rows, (uint32_t)cols,
+                g.ngroups, g.nct, g.ntiles, g.per_xcd, g.grid, floor, clamp, ca.count, ca.slots,
+                qT, sf);
   return hipGetLastError();
 }
 
 template <int kFmt>
 hipError_t launch_swiglu_t_fmt(const uint16_t* h, const float* w, int64_t rows, int64_t cols,
-                               const Grid& g, float floor, float clamp, unsigned long long* count,
+                               const Grid& g, float floor, float clamp, const CountArgs& ca,
                                uint8_t* qT, float* sf, hipStream_t stream,
                                const LaunchCaps& caps) {
   if (w) {
     return clamp > 0.0f
-               ? launch_swiglu_t<kFmt, true, true>(h, w, rows, cols, g, floor, clamp, count, qT,
-                                                   sf, stream, caps)
-               : launch_swiglu_t<kFmt, true, false>(h, w, rows, cols, g, floor, clamp, count, qT,
+               ? launch_swiglu_t<kFmt, true, true>(h, w, rows, cols, g, floor, clamp, ca, qT, sf,
+                                                   stream, caps)
+               : launch_swiglu_t<kFmt, true, false>(h, w, rows, cols, g, floor, clamp, ca, qT,
                                                     sf, stream, caps);
   }
   return clamp > 0.0f
-             ? launch_swiglu_t<kFmt, false, true>(h, w, rows, cols, g, floor, clamp, count, qT,
-                                                  sf, stream, caps)
-             : launch_swiglu_t<kFmt, false, false>(h, w, rows, cols, g, floor, clamp, count, qT,
+             ? launch_swiglu_t<kFmt, false, true>(h, w, rows, cols, g, floor, clamp, ca, qT, sf,
+                                                  stream, caps)
+             : launch_swiglu_t<kFmt, false, false>(h, w, rows, cols, g, floor, clamp, ca, qT,
                                                    sf, stream, caps);
 }
 
@@ -473,19 +499,21 @@ hipError_t launch_per_channel_T(const void* x, int64_t rows, int64_t cols, int f
 
 hipError_t launch_swiglu_per_channel_T(const void* h, int64_t rows, int64_t cols, const float* w,
                                        int fmt, float floor, float swiglu_clamp,
-                                       unsigned long long* clamp_count, void* qT, float* sf,
+                                       unsigned long long* clamp_count,
+                                       unsigned long long* count_ws, void* qT, float* sf,
                                        hipStream_t stream, const LaunchCaps& caps) {
   Grid g;
   if (!make_grid(rows, cols, 2 * cols, &g)) return hipErrorInvalidValue;
   if (g.ntiles == 0) return hipSuccess;
   const uint16_t* hp = static_cast<const uint16_t*>(h);
   uint8_t* qp = static_cast<uint8_t*>(qT);
+  const CountArgs ca{clamp_count, count_ws};
   if (fmt == kE4M3)
-    return launch_swiglu_t_fmt<kE4M3>(hp, w, rows, cols, g, floor, swiglu_clamp, clamp_count, qp,
-                                      sf, stream, caps);
+    return launch_swiglu_t_fmt<kE4M3>(hp, w, rows, cols, g, floor, swiglu_clamp, ca, qp, sf,
+                                      stream, caps);
   if (fmt == kE5M2)
-    return launch_swiglu_t_fmt<kE5M2>(hp, w, rows, cols, g, floor, swiglu_clamp, clamp_count, qp,
-                                      sf, stream, caps);
+    return launch_swiglu_t_fmt<kE5M2>(hp, w, rows, cols, g, floor, swiglu_clamp, ca, qp, sf,
+                                      stream, caps);
   return hipErrorInvalidValue;
 }
 

@@ -13,6 +13,9 @@
 
 namespace {
 
+static_assert(qcast::kCountSlots * qcast::kSlotWords * sizeof(uint64_t) == QCAST_COUNT_WS_BYTES,
+              "count workspace size");
+
 constexpr int kMaxDevices = 64;
 std::atomic<int> g_cu_count[kMaxDevices];   // 0 = not queried yet
 std::atomic<int> g_cu_override{0};
@@ -141,7 +144,7 @@ int qcast_e2m1(const void* x, int64_t rows, int64_t cols, int group, float clamp
 int qcast_swiglu_per_token_ex(const void* h, int64_t rows, int64_t cols,
                               const float* row_weight, int fmt, int group, float clamp_min,
                               int sf_flags, float swiglu_clamp, void* q, void* sf,
-                              uint64_t* clamp_count, void* stream) {
+                              uint64_t* clamp_count, void* count_ws, void* stream) {
   if (!fp8_fmt(fmt)) return QCAST_ERR_FORMAT;
   if (!sf_flags_ok(sf_flags)) return QCAST_ERR_FORMAT;
   if (!per_token_group_ok(group)) return QCAST_ERR_GROUP;
@@ -152,22 +155,23 @@ int qcast_swiglu_per_token_ex(const void* h, int64_t rows, int64_t cols,
   if (rows == 0 || cols == 0) return QCAST_OK;
   if (!h || !q || !sf) return QCAST_ERR_NULL;
   if (!aligned(h, 16) || !aligned(q, 16) || !aligned(sf, 4) ||
-      (row_weight && !aligned(row_weight, 4)) || (clamp_count && !aligned(clamp_count, 8)))
+      (row_weight && !aligned(row_weight, 4)) || (clamp_count && !aligned(clamp_count, 8)) ||
+      (count_ws && !aligned(count_ws, 128)))
     return QCAST_ERR_ALIGN;
   qcast::LaunchCaps caps;
   const int rc = caps_for_current_device(&caps);
   if (rc != QCAST_OK) return rc;
   return finish(qcast::launch_swiglu_per_token(
       h, rows, cols, row_weight, fmt, group, floor_for(fmt, clamp_min), (uint32_t)sf_flags,
-      clamp_value(swiglu_clamp), reinterpret_cast<unsigned long long*>(clamp_count), q, sf,
-      static_cast<hipStream_t>(stream), caps));
+      clamp_value(swiglu_clamp), reinterpret_cast<unsigned long long*>(clamp_count),
+      static_cast<unsigned long long*>(count_ws), q, sf, static_cast<hipStream_t>(stream), caps));
 }
 
 int qcast_swiglu_per_token_sf(const void* h, int64_t rows, int64_t cols,
                               const float* row_weight, int fmt, int group, float clamp_min,
                               int sf_flags, void* q, void* sf, void* stream) {
   return qcast_swiglu_per_token_ex(h, rows, cols, row_weight, fmt, group, clamp_min, sf_flags,
-                                   0.0f, q, sf, nullptr, stream);
+                                   0.0f, q, sf, nullptr, nullptr, stream);
 }
 
 int qcast_swiglu_backward_per_token(const void* h, const void* dv, int64_t rows, int64_t cols,
@@ -194,7 +198,8 @@ int qcast_swiglu_backward_per_token(const void* h, const void* dv, int64_t rows,
 
 int qcast_swiglu_per_channel_T(const void* h, int64_t rows, int64_t cols, const float* row_weight,
                                int fmt, int group, float clamp_min, float swiglu_clamp, void* qT,
-                               float* sf, uint64_t* clamp_count, void* stream) {
+                               float* sf, uint64_t* clamp_count, void* count_ws,
+                               void* stream) {
   if (!fp8_fmt(fmt)) return QCAST_ERR_FORMAT;
   if (group != 128) return QCAST_ERR_GROUP;
   if (rows < 0 || cols < 0 || rows % group != 0 || cols % 8 != 0 || too_big(rows, 2 * cols) ||
@@ -204,15 +209,17 @@ int qcast_swiglu_per_channel_T(const void* h, int64_t rows, int64_t cols, const 
   if (rows == 0 || cols == 0) return QCAST_OK;
   if (!h || !qT || !sf) return QCAST_ERR_NULL;
   if (!aligned(h, 16) || !aligned(qT, 16) || !aligned(sf, 4) ||
-      (row_weight && !aligned(row_weight, 4)) || (clamp_count && !aligned(clamp_count, 8)))
+      (row_weight && !aligned(row_weight, 4)) || (clamp_count && !aligned(clamp_count, 8)) ||
+      (count_ws && !aligned(count_ws, 128)))
     return QCAST_ERR_ALIGN;
   qcast::LaunchCaps caps;
   const int rc = caps_for_current_device(&caps);
   if (rc != QCAST_OK) return rc;
   return finish(qcast::launch_swiglu_per_channel_T(
       h, rows, cols, row_weight, fmt, floor_for(fmt, clamp_min), clamp_value(swiglu_clamp),
-      reinterpret_cast<unsigned long long*>(clamp_count), qT, sf,
-      static_cast<hipStream_t>(stream), caps));
+      reinterpret_cast<unsigned long long*>(clamp_count),
+      static_cast<unsigned long long*>(count_ws), qT, sf, static_cast<hipStream_t>(stream),
+      caps));
 }
 
 int qcast_swiglu_per_token(const void* h, int64_t rows, int64_t cols, const float* row_weight,

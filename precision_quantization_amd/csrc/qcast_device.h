@@ -257,6 +257,51 @@ __device__ __forceinline__ void add_wave_counts(uint32_t wave_total, unsigned lo
   }
 }
 
+// How a kernel counts clamped values: not at all, one atomic per workgroup
+// on the counter, or through a workspace of slots (add_wave_counts_slotted).
+constexpr int kCountNone = 0;
+constexpr int kCountDirect = 1;
+constexpr int kCountSlotted = 2;
+
+// Clamp-count workspace: kCountSlots 64-bit slots, kSlotWords words (128
+// bytes) apart, all zero between kernels.
+constexpr uint32_t kCountSlots = 64;
+constexpr uint32_t kSlotWords = 16;
+constexpr int kSlotArrivalShift = 40;  // low 40 bits: count; high 24: arrivals
+
+// Add a wave-uniform count into *count through the workspace `slots`, for
+// grids too large for one atomic per workgroup on a single word (atomics on
+// one address are serialized where it lives, about 12 ns each). Workgroup b
+// adds (1 << 40) + its count to slot b mod kCountSlots and reads the old
+// value back; the workgroup whose add completes the slot's arrivals (the
+// number of workgroups of the grid that use that slot) adds the slot's count
+// to *count and clears the slot, so the workspace is zero again when the
+// kernel ends. Every thread of every workgroup of the grid must call it
+// exactly once; the grid must be under 2^24 * kCountSlots workgroups and the
+// grid's total count under 2^40.
+template <int kBlock = kThreads>
+__device__ __forceinline__ void add_wave_counts_slotted(uint32_t wave_total,
+                                                        unsigned long long* slots,
+                                                        unsigned long long* count) {
+  __shared__ uint32_t part[kBlock / 64];
+  if ((threadIdx.x & 63) == 0) part[threadIdx.x >> 6] = wave_total;
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    uint32_t total = 0;
+#pragma unroll
+    for (int i = 0; i < kBlock / 64; ++i) total += part[i];
+    const uint32_t s = blockIdx.x % kCountSlots;
+    const uint32_t arrivals = (gridDim.x - s + kCountSlots - 1) / kCountSlots;
+    const unsigned long long add = (1ull << kSlotArrivalShift) | total;
+    const unsigned long long old = atomicAdd(slots + s * kSlotWords, add);
+    if ((uint32_t)(old >> kSlotArrivalShift) + 1u == arrivals) {
+      const unsigned long long sum = (old + add) & ((1ull << kSlotArrivalShift) - 1);
+      if (sum) atomicAdd(count, sum);
+      slots[s * kSlotWords] = 0ull;
+    }
+  }
+}
+
 // Number of active lanes of the wave where pred holds (wave-uniform: a
 // ballot and a scalar bit count, no vector ALU work beyond the compare).
 __device__ __forceinline__ uint32_t wave_count(bool pred) {
@@ -271,9 +316,10 @@ __device__ __forceinline__ void clamp_gate_up(float& g, float& u, float c) {
   u = __builtin_amdgcn_fmed3f(u, -c, c);
 }
 
-// How many of the wave's active gate and up values the clamp changes.
+// How many of the wave's active gate and up values the clamp changes (u
+// changes exactly when |u| > c).
 __device__ __forceinline__ uint32_t wave_clamp_count(float g, float u, float c) {
-  return wave_count(g > c) + wave_count(u > c) + wave_count(u < -c);
+  return wave_count(g > c) + wave_count(__builtin_fabsf(u) > c);
 }
 
 // E5M6: the IEEE-like 12-bit format with a 5-bit exponent (bias 15) and 6

@@ -61,11 +61,14 @@ hipError_t launch_per_token(const void* x, int64_t rows, int64_t cols, int fmt, 
 // h [rows, 2*cols] bf16 (gate | up), w [rows] fp32 or null -> 8-bit codes
 // (kE4M3 / kE5M2) + scales of silu(gate) * up * w; group in {32, 64, 128};
 // cols % group == 0. swiglu_clamp > 0 clamps gate and up first and adds the
-// number of changed values to *clamp_count (when not null).
+// number of changed values to *clamp_count (when not null), through the
+// zeroed count workspace count_ws (kCountSlots slots, left zeroed) when that
+// is not null, else with one atomic per workgroup of a capped grid.
 hipError_t launch_swiglu_per_token(const void* h, int64_t rows, int64_t cols, const float* w,
                                    int fmt, int group, float floor, uint32_t sf_flags,
-                                   float swiglu_clamp, unsigned long long* clamp_count, void* q,
-                                   void* sf, hipStream_t stream, const LaunchCaps& caps);
+                                   float swiglu_clamp, unsigned long long* clamp_count,
+                                   unsigned long long* count_ws, void* q, void* sf,
+                                   hipStream_t stream, const LaunchCaps& caps);
 
 // SwiGLU backward: h [rows, 2*cols] bf16, dv [rows, cols] bf16, w or null
 // -> q [rows, 2*cols] 8-bit codes of [dgate | dup], sf [rows, 2*cols/group].
@@ -85,11 +88,12 @@ hipError_t launch_per_channel_T(const void* x, int64_t rows, int64_t cols, int f
                                 const LaunchCaps& caps);
 
 // SwiGLU of h [rows, 2*cols] (clamped when swiglu_clamp > 0, changed values
-// added to *clamp_count when not null), then the per-channel cast written
-// transposed: qT [cols, rows], sf [cols, rows/128].
+// added to *clamp_count when not null, through count_ws as above), then the
+// per-channel cast written transposed: qT [cols, rows], sf [cols, rows/128].
 hipError_t launch_swiglu_per_channel_T(const void* h, int64_t rows, int64_t cols, const float* w,
                                        int fmt, float floor, float swiglu_clamp,
-                                       unsigned long long* clamp_count, void* qT, float* sf,
+                                       unsigned long long* clamp_count,
+                                       unsigned long long* count_ws, void* qT, float* sf,
                                        hipStream_t stream, const LaunchCaps& caps);
 
 // x [rows (tokens), cols (channels)] bf16 -> q [rows, cols] 8-bit codes in the

@@ -35,11 +35,13 @@ namespace {
 #ifndef QCAST_SW_WG_PER_CU
 #define QCAST_SW_WG_PER_CU 0
 #endif
-// With a clamp counter every workgroup ends in one atomic add on the same
-// 64-bit word, and those adds are serialized where the word lives (about
-// 8 ns each, measured), so the counting kernel runs a capped, grid-strided
-// grid of this many workgroups per CU, each of kCountBlock threads (large
-// workgroups keep the waves per CU up while the atomics stay few).
+// With a clamp counter and no workspace, every workgroup ends in one atomic
+// add on the same 64-bit word, and those adds are serialized where the word
+// lives (about 12 ns each, measured), so the counting kernel runs a capped,
+// grid-strided grid of this many workgroups per CU, each of kCountBlock
+// threads (large workgroups keep the waves per CU up while the atomics stay
+// few). With a workspace the adds are spread over its slots and the grid is
+// uncapped, with kSlotUnroll chunks per lane (2 measured fastest of 1, 2, 4).
 #ifndef QCAST_SW_COUNT_WG_PER_CU
 #define QCAST_SW_COUNT_WG_PER_CU 1
 #endif
@@ -49,6 +51,10 @@ namespace {
 #ifndef QCAST_SW_COUNT_UNROLL
 #define QCAST_SW_COUNT_UNROLL 1
 #endif
+#ifndef QCAST_SW_SLOT_UNROLL
+#define QCAST_SW_SLOT_UNROLL 2
+#endif
+constexpr int kSlotUnroll = QCAST_SW_SLOT_UNROLL;
 constexpr int kCountBlock = QCAST_SW_COUNT_BLOCK;
 constexpr int kCountUnroll = QCAST_SW_COUNT_UNROLL;
 constexpr int kStreamUnroll = QCAST_SW_UNROLL;
@@ -65,13 +71,13 @@ __device__ __forceinline__ float silu_times(float g, float u) {
   return g * __builtin_amdgcn_rcpf(1.0f + e) * u;
 }
 
-template <int kLanes, bool kWeighted, int kFmt, bool kClamp, bool kCount, int kBlock,
+template <int kLanes, bool kWeighted, int kFmt, bool kClamp, int kCount, int kBlock,
           int kUnroll>
 __global__ __launch_bounds__(kBlock) void swiglu_kernel(
     const uint16_t* __restrict__ h, const float* __restrict__ w, int64_t nchunks,
     uint32_t chunks_per_row, uint64_t row_magic, int64_t cols, float floor,
     uint8_t* __restrict__ q, void* __restrict__ sf, SfLayout lay, uint32_t group0,
-    float clamp, unsigned long long* __restrict__ count) {
+    float clamp, unsigned long long* __restrict__ count, unsigned long long* __restrict__ slots) {
   uint32_t nclamp = 0;
   // nchunks < 2^24 per launch: every chunk index and in-slab offset is 32-bit
   const uint32_t n32 = (uint32_t)nchunks;
@@ -119,12 +125,22 @@ __global__ __launch_bounds__(kBlock) void swiglu_kernel(
       }
     }
   }
-  if (kCount) add_wave_counts<kBlock>(nclamp, count);
+  if constexpr (kCount == kCountDirect) add_wave_counts<kBlock>(nclamp, count);
+  if constexpr (kCount == kCountSlotted) add_wave_counts_slotted<kBlock>(nclamp, slots, count);
 }
 
 struct ClampArgs {
   float c;                    // > 0: clamp bound
   unsigned long long* count;  // device counter or null
+  unsigned long long* slots;  // count workspace or null
+};
+
+// Pointers and first scale-group index of one slab of rows.
+struct SlabArgs {
+  const uint16_t* h;
+  const float* w;
+  uint8_t* q;
+  uint32_t group0;
 };
 
 template <int kLanes, bool kWeighted, int kFmt, bool kClamp>
@@ -140,27 +156,44 @@ hipError_t launch(const uint16_t* h, const float* w, int64_t rows, int64_t cols,
     const int64_t nr = rows - r0 < slab_rows ? rows - r0 : slab_rows;
     const int64_t nchunks = nr * cpr;
     const bool counting = kClamp && ca.count;
-    const int block = counting ? kCountBlock : kThreads;
-    const int64_t per_block_iter = (int64_t)block * (counting ? kCountUnroll : kStreamUnroll);
+    // Slotted: at most 2^24 / (kThreads * kSlotUnroll) workgroups and 2^28
+    // clamped values per slab, within the slots' 24 and 40 bits.
+    const bool slotted = counting && ca.slots;
+    const int block = counting && !slotted ? kCountBlock : kThreads;
+    const int unroll = slotted ? kSlotUnroll : counting ? kCountUnroll : kStreamUnroll;
+    const int64_t per_block_iter = (int64_t)block * unroll;
     const int64_t iters = (nchunks + per_block_iter - 1) / per_block_iter;
-    const int wg_per_cu = counting ? kCountWgPerCu : kWgPerCu;
+    const int wg_per_cu = slotted ? 0 : counting ? kCountWgPerCu : kWgPerCu;
     const int64_t max_blocks = wg_per_cu > 0 ? (int64_t)caps.num_cus * wg_per_cu : iters;
     const int64_t iters_per_block = (iters + max_blocks - 1) / max_blocks;
     const int64_t blocks = (iters + iters_per_block - 1) / iters_per_block;
-    if (counting)
-      launch_kernel((swiglu_kernel<kLanes, kWeighted, kFmt, kClamp, kClamp, kCountBlock,
-                                   kCountUnroll>),
-                    dim3((unsigned)blocks), dim3(kCountBlock), 0, stream, h + r0 * 2 * cols,
-                    kWeighted ? w + r0 : nullptr, nchunks, (uint32_t)cpr, magic, cols,
-                    floor, q + r0 * cols, sf, lay, (uint32_t)(r0 * groups_per_row), ca.c,
-                    ca.count);
-    else
-      launch_kernel((swiglu_kernel<kLanes, kWeighted, kFmt, kClamp, false, kThreads,
+    const SlabArgs args{h + r0 * 2 * cols, kWeighted ? w + r0 : nullptr, q + r0 * cols,
+                        (uint32_t)(r0 * groups_per_row)};
+    auto plain = [&] {
+      launch_kernel((swiglu_kernel<kLanes, kWeighted, kFmt, kClamp, kCountNone, kThreads,
                                    kStreamUnroll>),
-                    dim3((unsigned)blocks), dim3(kThreads), 0, stream, h + r0 * 2 * cols,
-                    kWeighted ? w + r0 : nullptr, nchunks, (uint32_t)cpr, magic, cols,
-                    floor, q + r0 * cols, sf, lay, (uint32_t)(r0 * groups_per_row), ca.c,
-                    ca.count);
+                    dim3((unsigned)blocks), dim3(kThreads), 0, stream, args.h, args.w, nchunks,
+                    (uint32_t)cpr, magic, cols, floor, args.q, sf, lay, args.group0, ca.c,
+                    ca.count, ca.slots);
+    };
+    if constexpr (kClamp) {
+      if (slotted)
+        launch_kernel((swiglu_kernel<kLanes, kWeighted, kFmt, true, kCountSlotted, kThreads,
+                                     kSlotUnroll>),
+                      dim3((unsigned)blocks), dim3(kThreads), 0, stream, args.h, args.w, nchunks,
+                      (uint32_t)cpr, magic, cols, floor, args.q, sf, lay, args.group0, ca.c,
+                      ca.count, ca.slots);
+      else if (counting)
+        launch_kernel((swiglu_kernel<kLanes, kWeighted, kFmt, true, kCountDirect, kCountBlock,
+                                     kCountUnroll>),
+                      dim3((unsigned)blocks), dim3(kCountBlock), 0, stream, args.h, args.w,
+                      nchunks, (uint32_t)cpr, magic, cols, floor, args.q, sf, lay, args.group0,
+                      ca.c, ca.count, ca.slots);
+      else
+        plain();
+    } else {
+      plain();
+    }
     const hipError_t err = hipGetLastError();
     if (err != hipSuccess) return err;
   }
@@ -205,13 +238,14 @@ hipError_t launch_c(const uint16_t* h, const float* w, int64_t rows, int64_t col
 
 hipError_t launch_swiglu_per_token(const void* h, int64_t rows, int64_t cols, const float* w,
                                    int fmt, int group, float floor, uint32_t sf_flags,
-                                   float swiglu_clamp, unsigned long long* clamp_count, void* q,
-                                   void* sf, hipStream_t stream, const LaunchCaps& caps) {
+                                   float swiglu_clamp, unsigned long long* clamp_count,
+                                   unsigned long long* count_ws, void* q, void* sf,
+                                   hipStream_t stream, const LaunchCaps& caps) {
   if (rows == 0 || cols == 0) return hipSuccess;
   if (cols / 8 >= kMaxChunksPerRow) return hipErrorInvalidValue;
   if (rows * cols / group >= (int64_t(1) << 31)) return hipErrorInvalidValue;
   const SfLayout lay = make_sf_layout(rows, cols, group, sf_flags);
-  const ClampArgs ca{swiglu_clamp, clamp_count};
+  const ClampArgs ca{swiglu_clamp, clamp_count, count_ws};
   const uint16_t* hp = static_cast<const uint16_t*>(h);
   uint8_t* qp = static_cast<uint8_t*>(q);
   if (fmt == kE4M3)

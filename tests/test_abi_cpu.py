@@ -64,7 +64,7 @@ def test_binding_names_match_the_c_entry_points():
 
 
 def test_abi_version_and_status_strings(lib):
-    assert lib.qcast_abi_version() == 2
+    assert lib.qcast_abi_version() == 3
     for s in range(9):
         assert lib.qcast_status_str(s).decode()
     assert lib.qcast_status_str(99).decode() == "unknown status"
@@ -165,15 +165,17 @@ def test_sf_layout_validation(lib):
 def test_swiglu_ex_validation(lib):
     f = lib.qcast_swiglu_per_token_ex
     nan = float("nan")
-    assert f(A16, 4, 256, None, E2M1, 32, 0.0, 0, 1.0, A16, A16, None, None) == ERR_FORMAT
-    assert f(A16, 4, 256, None, E4M3, 128, 0.0, 8, 1.0, A16, A16, None, None) == ERR_FORMAT
-    assert f(A16, 4, 256, None, E4M3, 100, 0.0, 0, 1.0, A16, A16, None, None) == ERR_GROUP
-    assert f(A16, 4, 200, None, E4M3, 128, 0.0, 0, 1.0, A16, A16, None, None) == ERR_SHAPE
-    assert f(A16, 4, 256, None, E4M3, 128, 0.0, 0, nan, A16, A16, None, None) == ERR_VALUE
-    assert f(A16, 0, 256, None, E4M3, 128, 0.0, 0, nan, None, None, None, None) == ERR_VALUE
-    assert f(None, 4, 256, None, E4M3, 128, 0.0, 0, 1.0, A16, A16, None, None) == ERR_NULL
-    assert f(A16, 4, 256, None, E4M3, 128, 0.0, 0, 1.0, A16, A16, A16 + 4, None) == ERR_ALIGN
-    assert f(None, 0, 256, None, E4M3, 128, 0.0, 0, 1.0, None, None, None, None) == OK
+    assert f(A16, 4, 256, None, E2M1, 32, 0.0, 0, 1.0, A16, A16, None, None, None) == ERR_FORMAT
+    assert f(A16, 4, 256, None, E4M3, 128, 0.0, 8, 1.0, A16, A16, None, None, None) == ERR_FORMAT
+    assert f(A16, 4, 256, None, E4M3, 100, 0.0, 0, 1.0, A16, A16, None, None, None) == ERR_GROUP
+    assert f(A16, 4, 200, None, E4M3, 128, 0.0, 0, 1.0, A16, A16, None, None, None) == ERR_SHAPE
+    assert f(A16, 4, 256, None, E4M3, 128, 0.0, 0, nan, A16, A16, None, None, None) == ERR_VALUE
+    assert f(A16, 0, 256, None, E4M3, 128, 0.0, 0, nan, None, None, None, None, None) == ERR_VALUE
+    assert f(None, 4, 256, None, E4M3, 128, 0.0, 0, 1.0, A16, A16, None, None, None) == ERR_NULL
+    assert f(A16, 4, 256, None, E4M3, 128, 0.0, 0, 1.0, A16, A16, A16 + 4, None, None) == ERR_ALIGN
+    assert f(None, 0, 256, None, E4M3, 128, 0.0, 0, 1.0, None, None, None, None, None) == OK
+    # the count workspace is 128-byte aligned
+    assert f(A16, 4, 256, None, E4M3, 128, 0.0, 0, 1.0, A16, A16, A16, A16 + 64, None) == ERR_ALIGN
 
 
 def test_swiglu_backward_validation(lib):
@@ -190,15 +192,16 @@ def test_swiglu_backward_validation(lib):
 
 def test_swiglu_per_channel_T_validation(lib):
     f = lib.qcast_swiglu_per_channel_T
-    assert f(A16, 256, 64, None, E2M1, 128, 0.0, 0.0, A16, A16, None, None) == ERR_FORMAT
-    assert f(A16, 256, 64, None, E4M3, 32, 0.0, 0.0, A16, A16, None, None) == ERR_GROUP
-    assert f(A16, 200, 64, None, E4M3, 128, 0.0, 0.0, A16, A16, None, None) == ERR_SHAPE
-    assert f(A16, 256, 60, None, E4M3, 128, 0.0, 0.0, A16, A16, None, None) == ERR_SHAPE
-    assert f(A16, 256, 64, None, E4M3, 128, 0.0, float("nan"), A16, A16, None, None) == ERR_VALUE
-    assert f(A16, 256, 64, None, E4M3, 128, 0.0, 0.0, None, A16, None, None) == ERR_NULL
-    assert f(A16, 256, 64, A16 + 2, E4M3, 128, 0.0, 0.0, A16, A16, None, None) == ERR_ALIGN
-    assert f(A16, 256, 64, None, E4M3, 128, 0.0, 1.0, A16, A16, A16 + 4, None) == ERR_ALIGN
-    assert f(None, 0, 64, None, E4M3, 128, 0.0, 0.0, None, None, None, None) == OK
+    assert f(A16, 256, 64, None, E2M1, 128, 0.0, 0.0, A16, A16, None, None, None) == ERR_FORMAT
+    assert f(A16, 256, 64, None, E4M3, 32, 0.0, 0.0, A16, A16, None, None, None) == ERR_GROUP
+    assert f(A16, 200, 64, None, E4M3, 128, 0.0, 0.0, A16, A16, None, None, None) == ERR_SHAPE
+    assert f(A16, 256, 60, None, E4M3, 128, 0.0, 0.0, A16, A16, None, None, None) == ERR_SHAPE
+    assert f(A16, 256, 64, None, E4M3, 128, 0.0, float("nan"), A16, A16, None, None, None) == ERR_VALUE
+    assert f(A16, 256, 64, None, E4M3, 128, 0.0, 0.0, None, A16, None, None, None) == ERR_NULL
+    assert f(A16, 256, 64, A16 + 2, E4M3, 128, 0.0, 0.0, A16, A16, None, None, None) == ERR_ALIGN
+    assert f(A16, 256, 64, None, E4M3, 128, 0.0, 1.0, A16, A16, A16 + 4, None, None) == ERR_ALIGN
+    assert f(None, 0, 64, None, E4M3, 128, 0.0, 0.0, None, None, None, None, None) == OK
+    assert f(A16, 256, 64, None, E4M3, 128, 0.0, 1.0, A16, A16, A16, A16 + 16, None) == ERR_ALIGN
 
 
 def test_per_channel_validation(lib):
@@ -236,7 +239,7 @@ def test_shapes_past_the_32_bit_indexing_are_refused_before_any_hip_call(lib):
     assert lib.qcast_per_channel_T(A16, 1 << 25, 64, E4M3, 128, 0.0, A16, A16, None) == ERR_SHAPE
     assert lib.qcast_per_channel(A16, 128, big, E4M3, 128, 0.0, A16, A16, None) == ERR_SHAPE
     assert lib.qcast_swiglu_per_channel_T(A16, 128, 1 << 23, None, E4M3, 128, 0.0, 0.0, A16, A16,
-                                          None, None) == ERR_SHAPE
+                                          None, None, None) == ERR_SHAPE
     assert lib.qcast_per_token(A16, 1 << 24, 1 << 12, E4M3, 32, 0.0, A16, A16, None) == ERR_SHAPE
     assert lib.qcast_cast_back(A16, A16, 1 << 30, 1 << 13, E4M3, 128, 1, A16, None) == ERR_SHAPE
     # the largest shapes that fit pass validation (then find no device here)

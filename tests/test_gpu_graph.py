@@ -78,3 +78,49 @@ def test_graph_replays_match_eager(dev):
             assert torch.equal(t.view(torch.uint8), r), (replay, i)
         for t, r in zip(eager, ref):
             assert torch.equal(t.view(torch.uint8), r)
+
+
+def test_graph_replays_count_through_a_workspace(dev):
+    # the clamp counters under capture: every replay adds the same count, and
+    # the workspace the counting kernels share is zero again after each
+    wl = workloads.swiglu_input(rows=1024, cols=2048)
+    h, w = wl.x.to(dev), wl.w.to(dev)
+    ws = torch.zeros(pq.COUNT_WS_BYTES // 8, dtype=torch.int64, device=dev)
+    f8 = torch.float8_e4m3fn
+    q = torch.empty(1024, 2048, dtype=f8, device=dev)
+    sf = torch.empty(1024, 16, device=dev)
+    qt = torch.empty(2048, 1024, dtype=f8, device=dev)
+    sft = torch.empty(2048, 8, device=dev)
+    counts = torch.zeros(2, dtype=torch.int64, device=dev)
+
+    def counted():
+        pq.qcast_swiglu_per_token_ex(h, w, "e4m3", 128, swiglu_clamp=3.0,
+                                     clamp_count=counts[0:1], out=q, out_sf=sf,
+                                     count_workspace=ws)
+        pq.qcast_swiglu_per_channel_T(h, w, "e4m3", 128, swiglu_clamp=3.0,
+                                      clamp_count=counts[1:2], out=qt, out_sf=sft,
+                                      count_workspace=ws)
+
+    counted()
+    torch.cuda.synchronize()
+    per_call = counts.clone()
+    assert per_call[0] == per_call[1] > 0          # the same values are clamped
+    ref = [q.view(torch.uint8).clone(), sf.clone(), qt.view(torch.uint8).clone(), sft.clone()]
+    side = torch.cuda.Stream(dev)
+    side.wait_stream(torch.cuda.current_stream(dev))
+    with torch.cuda.stream(side):
+        counted()
+    torch.cuda.current_stream(dev).wait_stream(side)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        counted()
+    counts.zero_()
+    torch.cuda.synchronize()
+    for replay in range(1, 5):
+        g.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(counts, replay * per_call), replay
+        assert not ws.any(), replay
+        got = [q.view(torch.uint8), sf, qt.view(torch.uint8), sft]
+        assert all(torch.equal(a, b) for a, b in zip(got, ref)), replay

@@ -108,31 +108,83 @@ def test_per_channel_equals_transpose_of_per_channel_T_on_gpu(dev):
 
 # ------------------------------------------------- SwiGLU forward with clamp
 
-def gpu_swiglu_ex(wl, dev, clamp, flags=0, fmt="e4m3", group=128, count=None):
+# How the clamp count reaches the counter: through the binding's own
+# workspace per stream (the default), with one atomic per workgroup of a
+# capped grid (no workspace), or through a workspace the caller passes.
+WS_MODES = ["default", "direct", "caller"]
+
+
+def count_workspace(mode, dev):
+    if mode == "default":
+        return None
+    if mode == "direct":
+        return False
+    return torch.zeros(pq.COUNT_WS_BYTES // 8, dtype=torch.int64, device=dev)
+
+
+def gpu_swiglu_ex(wl, dev, clamp, flags=0, fmt="e4m3", group=128, count=None, ws=None):
     rows, n = wl.rows, wl.cols
     out = poisoned((rows, n), CODE_DT[fmt], dev)
     shape, dt = pq.sf_layout_shape(rows, n, group, flags)
     sf = poisoned(shape, dt, dev)
     pq.qcast_swiglu_per_token_ex(wl.x.to(dev), None if wl.w is None else wl.w.to(dev), fmt,
                                  group, sf_flags=flags, swiglu_clamp=clamp, clamp_count=count,
-                                 out=out, out_sf=sf)
+                                 out=out, out_sf=sf, count_workspace=ws)
     torch.cuda.synchronize()
     return codes_np(out), sf.cpu().numpy()
 
 
+@pytest.mark.parametrize("ws_mode", WS_MODES)
 @pytest.mark.parametrize("clamp", [1.5, 4.0, 7.0])
 @pytest.mark.parametrize("weighted", [True, False])
-def test_swiglu_clamp_parity_and_count(dev, clamp, weighted):
+def test_swiglu_clamp_parity_and_count(dev, clamp, weighted, ws_mode):
     wl = workloads.swiglu_input(seed=71, rows=257, cols=1024, with_weight=weighted)
     w = None if wl.w is None else wl.w.numpy()
     q_ref, sf_ref, n_ref = oracle.swiglu_per_token_ex(bits(wl.x), w, swiglu_clamp=clamp)
     count = torch.zeros(1, dtype=torch.int64, device=dev)
-    q, sf = gpu_swiglu_ex(wl, dev, clamp, count=count)
+    ws = count_workspace(ws_mode, dev)
+    q, sf = gpu_swiglu_ex(wl, dev, clamp, count=count, ws=ws)
     assert int(count.item()) == n_ref > 0
     assert_swiglu_bar(q, sf, q_ref, sf_ref, f"clamp {clamp}")
     # the counter accumulates over calls
-    gpu_swiglu_ex(wl, dev, clamp, count=count)
+    gpu_swiglu_ex(wl, dev, clamp, count=count, ws=ws)
     assert int(count.item()) == 2 * n_ref
+    if ws_mode == "caller":
+        assert not ws.any()              # left zeroed
+
+
+def test_count_workspace_over_calls_of_different_sizes(dev):
+    # one workspace through a large call, a small one (fewer workgroups than
+    # slots), the fused transpose, and a large one again: each count exact,
+    # the workspace zero after each
+    ws = count_workspace("caller", dev)
+    cases = [(workloads.swiglu_input(seed=91, rows=2048, cols=2048), 3.0, "token"),
+             (workloads.swiglu_input(seed=92, rows=3, cols=128), 1.0, "token"),
+             (workloads.swiglu_input(seed=93, rows=384, cols=136), 2.0, "channel"),
+             (workloads.swiglu_input(seed=94, rows=128, cols=8), 2.0, "channel"),
+             (workloads.swiglu_input(seed=95, rows=2048, cols=2048, with_weight=False), 0.5,
+              "token")]
+    for wl, clamp, kind in cases:
+        w = None if wl.w is None else wl.w.numpy()
+        _, n_ref = oracle.swiglu_values_ex(bits(wl.x), w, swiglu_clamp=clamp)
+        count = torch.zeros(1, dtype=torch.int64, device=dev)
+        if kind == "token":
+            gpu_swiglu_ex(wl, dev, clamp, count=count, ws=ws)
+        else:
+            gpu_swiglu_T(wl, dev, clamp=clamp, count=count, ws=ws)
+        assert int(count.item()) == n_ref > 0, (wl.rows, wl.cols, kind)
+        assert not ws.any(), (wl.rows, wl.cols, kind)
+
+
+def test_count_workspace_is_checked(dev):
+    wl = workloads.swiglu_input(seed=96, rows=4, cols=128)
+    count = torch.zeros(1, dtype=torch.int64, device=dev)
+    small = torch.zeros(16, dtype=torch.int64, device=dev)
+    with pytest.raises(pq.QcastError):
+        gpu_swiglu_ex(wl, dev, 1.0, count=count, ws=small)
+    offset = torch.zeros(pq.COUNT_WS_BYTES // 8 + 8, dtype=torch.int64, device=dev)[1:]
+    with pytest.raises(pq.QcastError):           # 8-byte, not 128-byte aligned
+        gpu_swiglu_ex(wl, dev, 1.0, count=count, ws=offset)
 
 
 def test_swiglu_clamp_off_matches_plain_swiglu_exactly(dev):
@@ -154,6 +206,9 @@ def test_swiglu_clamp_full_size_with_layout(dev):
                                                       swiglu_clamp=5.0)
     count = torch.zeros(1, dtype=torch.int64, device=dev)
     q, sf = gpu_swiglu_ex(wl, dev, 5.0, flags=flags, count=count)
+    assert int(count.item()) == n_ref
+    count.zero_()
+    gpu_swiglu_ex(wl, dev, 5.0, flags=flags, count=count, ws=False)
     assert int(count.item()) == n_ref
     # power-of-two exponent bytes: equal unless an abs-max straddles a power
     # of two by an ulp
@@ -204,29 +259,34 @@ def test_swiglu_backward_full_size(dev):
 
 # ------------------------------------------- SwiGLU + per-channel + transpose
 
-def gpu_swiglu_T(wl, dev, fmt="e4m3", clamp=0.0, count=None):
+def gpu_swiglu_T(wl, dev, fmt="e4m3", clamp=0.0, count=None, ws=None):
     rows, n = wl.rows, wl.cols
     out = poisoned((n, rows), CODE_DT[fmt], dev)
     sf = poisoned((n, rows // 128), torch.float32, dev)
     pq.qcast_swiglu_per_channel_T(wl.x.to(dev), None if wl.w is None else wl.w.to(dev), fmt, 128,
-                                  swiglu_clamp=clamp, clamp_count=count, out=out, out_sf=sf)
+                                  swiglu_clamp=clamp, clamp_count=count, out=out, out_sf=sf,
+                                  count_workspace=ws)
     torch.cuda.synchronize()
     return codes_np(out), sf.cpu().numpy()
 
 
+@pytest.mark.parametrize("ws_mode", WS_MODES)
 @pytest.mark.parametrize("fmt", ["e4m3", "e5m2"])
 @pytest.mark.parametrize("clamp", [0.0, 2.5])
 @pytest.mark.parametrize("rows,cols,weighted", [(128, 8, True), (256, 200, False),
                                                 (384, 136, True), (1024, 2048, True)])
-def test_swiglu_per_channel_T_shapes(dev, fmt, clamp, rows, cols, weighted):
+def test_swiglu_per_channel_T_shapes(dev, fmt, clamp, rows, cols, weighted, ws_mode):
     wl = workloads.swiglu_input(seed=rows + 2 * cols, rows=rows, cols=cols, with_weight=weighted)
     w = None if wl.w is None else wl.w.numpy()
     q_ref, sf_ref = oracle.swiglu_per_channel_T(bits(wl.x), w, fmt, swiglu_clamp=clamp)
     count = torch.zeros(1, dtype=torch.int64, device=dev)
-    q, sf = gpu_swiglu_T(wl, dev, fmt, clamp, count)
+    ws = count_workspace(ws_mode, dev)
+    q, sf = gpu_swiglu_T(wl, dev, fmt, clamp, count, ws)
     assert_swiglu_bar(q, sf, q_ref, sf_ref, f"swiglu_T {fmt} c{clamp} {rows}x{cols}")
     _, n_ref = oracle.swiglu_values_ex(bits(wl.x), w, swiglu_clamp=clamp)
     assert int(count.item()) == n_ref
+    if ws_mode == "caller":
+        assert not ws.any()
 
 
 def test_swiglu_per_channel_T_full_size(dev):
