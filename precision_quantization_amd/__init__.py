@@ -86,17 +86,17 @@ def _count_ws(count_workspace, clamp_count, device, stream_handle):
     """Device pointer of the clamp-count workspace (QCAST_COUNT_WS_BYTES,
     zero between calls): the caller's tensor; none when ``count_workspace``
     is False, when nothing is counted, or (for the default None) under graph
-    capture without a workspace made for that stream beforehand; else, for
-    None, one zeroed int64 tensor kept per device and stream (each call
-    leaves it zeroed, and calls on one stream are ordered)."""
+    capture, since a graph may be replayed on any stream; else, for None,
+    one zeroed int64 tensor kept per device and stream (each call leaves it
+    zeroed, and calls on one stream are ordered)."""
     if clamp_count is None or count_workspace is False:
         return None
     if count_workspace is None:
+        if torch.cuda.is_current_stream_capturing():
+            return None     # a graph may replay on any stream: no shared workspace
         key = (device, stream_handle)
         ws = _count_ws_cache.get(key)
         if ws is None:
-            if torch.cuda.is_current_stream_capturing():
-                return None
             ws = torch.zeros(COUNT_WS_BYTES // 8, dtype=torch.int64, device=device)
             torch.cuda.synchronize(device)   # zeroed before any stream uses it
             _count_ws_cache[key] = ws
