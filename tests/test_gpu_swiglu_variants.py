@@ -296,3 +296,27 @@ def test_swiglu_per_channel_T_full_size(dev):
     frac = assert_swiglu_bar(q, sf, q_ref, sf_ref, "swiglu_T full")
     print(f"swiglu + transpose full: {frac:.5%} of codes differ from the oracle")
 
+
+
+def test_count_workspaces_per_stream_under_concurrency(dev):
+    # two streams at once, each with the binding's own workspace for it:
+    # every count exact, both workspaces zero afterwards
+    wls = [workloads.swiglu_input(seed=97 + i, rows=2048, cols=2048) for i in range(2)]
+    clamps = [2.0, 3.0]
+    refs = [oracle.swiglu_values_ex(bits(wl.x), wl.w.numpy(), swiglu_clamp=c)[1]
+            for wl, c in zip(wls, clamps)]
+    ins = [(wl.x.to(dev), wl.w.to(dev)) for wl in wls]
+    streams = [torch.cuda.Stream(dev) for _ in wls]
+    counts = [torch.zeros(1, dtype=torch.int64, device=dev) for _ in wls]
+    torch.cuda.synchronize()
+    for _ in range(3):
+        for (h, w), c, s, n in zip(ins, clamps, streams, counts):
+            with torch.cuda.stream(s):
+                pq.qcast_swiglu_per_token_ex(h, w, "e4m3", 128, swiglu_clamp=c, clamp_count=n)
+                pq.qcast_swiglu_per_channel_T(h, w, "e4m3", 128, swiglu_clamp=c, clamp_count=n)
+    torch.cuda.synchronize()
+    for n, ref in zip(counts, refs):
+        assert int(n.item()) == 6 * ref > 0
+    for s in streams:
+        ws = pq._count_ws_cache[(dev, s.cuda_stream)]
+        assert not ws.any()
