@@ -17,8 +17,11 @@ HIP events that kernels of the timed steps record from their own dispatch on
 the launch stream (qcast_bench_time_next): step s times kernel s mod 5, so
 with the default 50 steps every kernel is timed on 10 of its launches (their
 average, median, 10th and 90th percentile). The roofline object is for the
-kernel with the largest share of the step. The CPU baseline is the oracle
-(single thread) on every workload in full, on this host (about 10 s).
+kernel with the largest share of the step. Each step kernel also carries
+copy_GBps, the library's streaming copy moving the same byte count after a
+1 GiB flush, and of_copy, its own rate over that ceiling. The CPU baseline
+is the oracle (single thread) on every workload in full, on this host (about
+10 s).
 
 "other_kernels" times, after the step and outside `value`, the small
 per-token workload X[128, 512] next to the launch floor (a 16-byte copy),
@@ -280,30 +283,34 @@ def time_extras(extras, dev, steps, warmup):
     return out
 
 
-def copy_ceiling(dev, nbytes):
+def copy_ceilings(dev, sizes):
     """Bandwidth of the library's streaming copy (include/qcast_bench.h)
-    moving nbytes in total (half read, half written; the byte count of the
-    largest cast of the step) after a 1 GiB flush: the empirical ceiling for
-    a streaming kernel of this size."""
+    moving each byte count in `sizes` in total (half read, half written)
+    after a 1 GiB flush, median of 5 timed runs: the empirical ceiling for a
+    streaming kernel of that size. Returns {nbytes: GB/s}."""
     import torch
     import precision_quantization_amd as pq
-    half = nbytes // 2 // 16 * 16
-    src = torch.empty(half, dtype=torch.uint8, device=dev).fill_(1)
-    dst = torch.empty(half, dtype=torch.uint8, device=dev)
     flush = torch.empty(1 << 30, dtype=torch.uint8, device=dev)
     hev = HipEvents()
-    times = []
-    for _ in range(6):
-        flush.fill_(0)
-        a, b = hev.create(), hev.create()
-        pq.qcast_bench_time_next(a, b)
-        pq.qcast_bench_copy(src, dst)
-        torch.cuda.synchronize()
-        times.append(hev.elapsed_ms(a, b))
-        hev.destroy(a)
-        hev.destroy(b)
-    ms = sorted(times[1:])[len(times[1:]) // 2]
-    return 2 * half / (ms * 1e-3) / 1e9
+    out = {}
+    for nbytes in sorted(set(sizes)):
+        half = nbytes // 2 // 16 * 16
+        src = torch.empty(half, dtype=torch.uint8, device=dev).fill_(1)
+        dst = torch.empty(half, dtype=torch.uint8, device=dev)
+        times = []
+        for _ in range(6):
+            flush.fill_(0)
+            a, b = hev.create(), hev.create()
+            pq.qcast_bench_time_next(a, b)
+            pq.qcast_bench_copy(src, dst)
+            torch.cuda.synchronize()
+            times.append(hev.elapsed_ms(a, b))
+            hev.destroy(a)
+            hev.destroy(b)
+        ms = sorted(times[1:])[len(times[1:]) // 2]
+        out[nbytes] = 2 * half / (ms * 1e-3) / 1e9
+        del src, dst
+    return out
 
 
 def cpu_baseline(wls, fraction=1.0):
@@ -402,8 +409,14 @@ def main():
     dominant = max(kernels, key=lambda k: kernels[k]["avg_us"])
     d = kernels[dominant]
     traffic = load_traffic(dominant)
+    # the largest size last, so the copy the counter runs calibrate on is the
+    # last copy of the run
     copy_nbytes = max(k["bytes"] for k in kernels.values())
-    copy_gbs = copy_ceiling(dev, copy_nbytes)
+    ceilings = copy_ceilings(dev, [k["bytes"] for k in kernels.values()])
+    copy_gbs = ceilings[copy_nbytes]
+    for k in kernels.values():
+        k["copy_GBps"] = round(ceilings[k["bytes"]], 1)
+        k["of_copy"] = round(k["GBps"] / ceilings[k["bytes"]], 4)
     result = {
         "metric": METRIC,
         "value": round(step_bytes * args.steps / elapsed / 1e9, 1),
