@@ -21,7 +21,7 @@ kernel with the largest share of the step. Each step kernel also carries
 copy_GBps, the library's streaming copy moving the same byte count after a
 1 GiB flush, and of_copy, its own rate over that ceiling. The CPU baseline
 is the oracle (single thread) on every workload in full, on this host (about
-10 s).
+10 s); cpu_baseline_all_cores splits the same work over up to 16 cores.
 
 "other_kernels" times, after the step and outside `value`, the small
 per-token workload X[128, 512] next to the launch floor (a 16-byte copy),
@@ -313,11 +313,25 @@ def copy_ceilings(dev, sizes):
     return out
 
 
+def _oracle_cast(name, xb, w):
+    """One oracle call of the named step cast on bf16 bits xb (and weights w)."""
+    import oracle
+    if name == "per_token":
+        oracle.per_token(xb, "e4m3", 128)
+    elif name == "swiglu":
+        oracle.swiglu_per_token(xb, w, "e4m3", 128)
+    elif name == "per_block":
+        oracle.per_block(xb, "e4m3", 128)
+    elif name == "per_channel_T":
+        oracle.per_channel_T(xb, "e4m3", 128)
+    elif name == "e2m1":
+        oracle.e2m1(xb, 32)
+
+
 def cpu_baseline(wls, fraction=1.0):
     """The oracle, single-threaded, on the first `fraction` of the rows of
     every workload (all of them by default: about 10 s of CPU work); GB/s
     over the same algorithmic bytes."""
-    import oracle
     from precision_quantization_amd import workloads as W
     total_bytes = 0
     total_s = 0.0
@@ -326,20 +340,41 @@ def cpu_baseline(wls, fraction=1.0):
         sub = W.Workload(wl.name, wl.op, wl.x[:n], wl.fmt, wl.group,
                          w=None if wl.w is None else wl.w[:n])
         xb = W.bf16_bits(sub.x)
+        w = None if sub.w is None else sub.w.numpy()
         t0 = time.perf_counter()
-        if name == "per_token":
-            oracle.per_token(xb, "e4m3", 128)
-        elif name == "swiglu":
-            oracle.swiglu_per_token(xb, sub.w.numpy(), "e4m3", 128)
-        elif name == "per_block":
-            oracle.per_block(xb, "e4m3", 128)
-        elif name == "per_channel_T":
-            oracle.per_channel_T(xb, "e4m3", 128)
-        elif name == "e2m1":
-            oracle.e2m1(xb, 32)
+        _oracle_cast(name, xb, w)
         total_s += time.perf_counter() - t0
         total_bytes += sub.algorithmic_bytes()
     return total_bytes / total_s / 1e9, total_s
+
+
+def cpu_baseline_all_cores(wls, max_threads=16):
+    """The same oracle calls over a static split of every workload's rows
+    into whole 128-row parts, one Python thread per part on the cores this
+    process may use (at most max_threads; the oracle's C calls release the
+    GIL); GB/s over the same algorithmic bytes, and the threads used."""
+    import threading
+    from precision_quantization_amd import workloads as W
+    nthreads = max(1, min(max_threads, len(os.sched_getaffinity(0))))
+    total_bytes = 0
+    total_s = 0.0
+    for name, wl in wls:
+        xb = W.bf16_bits(wl.x)
+        w = None if wl.w is None else wl.w.numpy()
+        groups = wl.rows // 128
+        parts = min(nthreads, groups)
+        bounds = [128 * (groups * i // parts) for i in range(parts + 1)]
+        threads = [threading.Thread(target=_oracle_cast,
+                                    args=(name, xb[a:b], None if w is None else w[a:b]))
+                   for a, b in zip(bounds[:-1], bounds[1:])]
+        t0 = time.perf_counter()
+        for t in threads:
+            t.start()
+        for t in threads:
+            t.join()
+        total_s += time.perf_counter() - t0
+        total_bytes += wl.algorithmic_bytes()
+    return total_bytes / total_s / 1e9, total_s, nthreads
 
 
 def load_traffic(dominant):
@@ -457,6 +492,13 @@ def main():
             "sample": f"all rows of each of the five workloads, one oracle call each "
                       f"({secs:.1f} s on {platform.processor() or platform.machine()}, "
                       f"{os.cpu_count()} cores present)",
+        }
+        log("bench: CPU baseline over all cores (oracle)")
+        gbs_n, secs_n, threads = cpu_baseline_all_cores(wls)
+        result["cpu_baseline_all_cores"] = {
+            "value": round(gbs_n, 4), "unit": "GB/s", "cores": threads, "kind": "oracle",
+            "sample": f"all rows of each of the five workloads, split into {threads} parts of "
+                      f"whole 128-row groups, one thread each ({secs_n:.1f} s)",
         }
     print(json.dumps(result), flush=True)
 
