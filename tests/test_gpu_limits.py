@@ -122,3 +122,37 @@ def test_swiglu_rows_at_the_length_limit(dev, op):
     sf = sf.cpu().numpy()
     assert (np.abs(sf.astype(np.float64) - sf_ref) / sf_ref).max() <= 1e-6
     assert (q != q_ref).mean() <= 1e-3
+
+
+@pytest.mark.parametrize("ws", [None, False])
+def test_swiglu_clamp_count_over_several_launches(dev, ws):
+    # 66,536 rows of 2048 outputs: past the 2^24 chunks of one launch, so the
+    # cast runs as two launches that count through the same workspace (or,
+    # with ws=False, on capped grids); the count is additive over rows, so
+    # the oracle counts slabs of rows
+    rows, cols, clamp = 65536 + 1000, 2048, 3.0
+    g = torch.Generator().manual_seed(107)
+    h = (torch.randn(rows, 2 * cols, generator=g) * 2).to(torch.bfloat16)
+    w = torch.rand(rows, generator=g)
+    count = torch.zeros(1, dtype=torch.int64, device=dev)
+    q, sf = pq.qcast_swiglu_per_token_ex(h.to(dev), w.to(dev), "e4m3", 128, swiglu_clamp=clamp,
+                                         clamp_count=count, count_workspace=ws)
+    torch.cuda.synchronize()
+    hb = workloads.bf16_bits(h)
+    wn = w.numpy()
+    n_ref = 0
+    for r0 in range(0, rows, 8192):
+        n_ref += oracle.swiglu_values_ex(hb[r0:r0 + 8192], wn[r0:r0 + 8192],
+                                         swiglu_clamp=clamp)[1]
+    assert int(count.item()) == n_ref > 0
+    # codes and scales of sampled rows in both launches
+    for r in sample(rows, 12, 1, 108):
+        r = int(r)
+        q_ref, sf_ref, _ = oracle.swiglu_per_token_ex(hb[r:r + 1], wn[r:r + 1],
+                                                      swiglu_clamp=clamp)
+        got = q[r:r + 1].view(torch.uint8).cpu().numpy()
+        assert (got != q_ref).mean() <= 1e-3, r
+        s = sf[r:r + 1].cpu().numpy().astype(np.float64)
+        assert (np.abs(s - sf_ref) / sf_ref).max() <= 1e-6, r
+    del q, sf
+    torch.cuda.empty_cache()
