@@ -297,7 +297,9 @@ __device__ __forceinline__ void add_wave_counts_slotted(uint32_t wave_total,
     if ((uint32_t)(old >> kSlotArrivalShift) + 1u == arrivals) {
       const unsigned long long sum = (old + add) & ((1ull << kSlotArrivalShift) - 1);
       if (sum) atomicAdd(count, sum);
-      slots[s * kSlotWords] = 0ull;
+      // cleared with an atomic too, so every access to a slot is made where
+      // the slot's atomics are performed
+      atomicExch(slots + s * kSlotWords, 0ull);
     }
   }
 }
