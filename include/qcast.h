@@ -36,7 +36,8 @@
  *  - Tensors are row-major and contiguous. bf16 inputs are passed as raw
  *    16-bit patterns. Inputs must not overlap outputs.
  *  - Alignment: inputs and code outputs 16 bytes, scale outputs 4 bytes,
- *    the optional row weight 4 bytes.
+ *    the optional row weight 4 bytes, a clamp counter 8 bytes, a count
+ *    workspace 128 bytes.
  *  - Work is enqueued on `stream` (a hipStream_t passed as void*; NULL is
  *    the default stream) and the call returns at once.
  *  - The return value is a qcast_status. Arguments are checked before any
@@ -47,7 +48,8 @@
  *    any HIP call: rows * cols / group < 2^31 scale groups for the per-token
  *    casts; for the others, the limits stated with each entry point.
  *  - Calls on one stream are ordered; concurrent calls on different streams
- *    are independent (no shared mutable device state).
+ *    are independent (the library holds no mutable device state; a count
+ *    workspace is the caller's, and concurrent calls need different ones).
  */
 #ifndef QCAST_H
 #define QCAST_H
