@@ -3,8 +3,8 @@
 Every ``csrc/*.hip`` file is compiled for gfx950 with hipcc, in parallel, and
 linked into ``precision_quantization_amd/libqcast.so``. A stamp file beside
 the library records the SHA-256 of the sources, the public header and the
-flags; the loader refuses a library whose stamp does not match the sources it
-sits beside.
+flags (their code: comments and layout do not count); the loader refuses a
+library whose stamp does not match the sources it sits beside.
 
     python -m precision_quantization_amd.build
 """
@@ -42,13 +42,50 @@ def sources():
     return sorted(glob.glob(os.path.join(CSRC, "*.hip")))
 
 
+def code_tokens(text):
+    """C/C++ source with its comments removed and every run of whitespace
+    made one space (string and character literals kept as written), so that
+    edits to comments or layout leave the digest alone."""
+    out = []
+    i, n = 0, len(text)
+    while i < n:
+        c = text[i]
+        if text.startswith("//", i):
+            j = text.find("\n", i)
+            i = n if j < 0 else j
+        elif text.startswith("/*", i):
+            j = text.find("*/", i + 2)
+            i = n if j < 0 else j + 2
+            out.append(" ")
+        elif c in "\"'":
+            j = i + 1
+            while j < n and text[j] != c:
+                j += 2 if text[j] == "\\" else 1
+            out.append(text[i:j + 1])
+            i = j + 1
+        elif c.isspace():
+            j = i
+            while j < n and text[j].isspace():
+                j += 1
+            # keep line structure where the preprocessor needs it
+            out.append("\n" if "\n" in text[i:j] else " ")
+            i = j
+        else:
+            out.append(c)
+            i += 1
+    return "".join(out)
+
+
 def source_digest():
+    """SHA-256 of the code (comments and layout aside) of the sources, the
+    headers and the flags."""
     h = hashlib.sha256()
     files = sources() + sorted(glob.glob(os.path.join(CSRC, "*.h"))) + \
         sorted(glob.glob(os.path.join(INCLUDE, "*.h")))
     for path in files:
-        with open(path, "rb") as f:
-            h.update(os.path.basename(path).encode() + b"\0" + f.read())
+        with open(path, encoding="utf-8") as f:
+            code = code_tokens(f.read())
+        h.update(os.path.basename(path).encode() + b"\0" + code.encode())
     h.update(" ".join(FLAGS).encode())
     return h.hexdigest()
 
