@@ -43,9 +43,10 @@ def sources():
 
 
 def code_tokens(text):
-    """C/C++ source with its comments removed and every run of whitespace
-    made one space (string and character literals kept as written), so that
-    edits to comments or layout leave the digest alone."""
+    """C/C++ source with its comments removed (comment markers inside string
+    and character literals are code), every line's whitespace runs made one
+    space, and empty lines dropped, so that edits to comments or layout leave
+    the digest alone."""
     out = []
     i, n = 0, len(text)
     while i < n:
@@ -63,17 +64,15 @@ def code_tokens(text):
                 j += 2 if text[j] == "\\" else 1
             out.append(text[i:j + 1])
             i = j + 1
-        elif c.isspace():
-            j = i
-            while j < n and text[j].isspace():
-                j += 1
-            # keep line structure where the preprocessor needs it
-            out.append("\n" if "\n" in text[i:j] else " ")
-            i = j
         else:
             out.append(c)
             i += 1
-    return "".join(out)
+    lines = []
+    for line in "".join(out).split("\n"):
+        words = line.split()
+        if words:
+            lines.append(" ".join(words))
+    return "\n".join(lines)
 
 
 def source_digest():
