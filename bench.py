@@ -19,7 +19,11 @@ with the default 50 steps every kernel is timed on 10 of its launches (their
 average, median, 10th and 90th percentile). The roofline object is for the
 kernel with the largest share of the step. Each step kernel also carries
 copy_GBps, the library's streaming copy moving the same byte count after a
-1 GiB flush, and of_copy, its own rate over that ceiling. The CPU baseline
+1 GiB flush, and of_copy, its own rate over that ceiling; per_channel_T also
+carries pattern_us, its own loads and transposed stores without the
+arithmetic (qcast_bench_per_channel_T_traffic), flushed_us, the cast timed
+the same way (alternating with it, each after the flush), and of_pattern,
+their ratio. The CPU baseline
 is the oracle (single thread) on every workload in full, on this host (about
 10 s); cpu_baseline_all_cores splits the same work over up to 16 cores.
 
@@ -328,6 +332,37 @@ def _oracle_cast(name, xb, w):
         oracle.e2m1(xb, 32)
 
 
+def pattern_ceiling(dev, x):
+    """The transposed per-channel cast against its memory traffic alone
+    (include/qcast_bench.h: the same loads and qT stores, no arithmetic), on
+    the cast's input x, the two alternating, each after a 1 GiB flush;
+    medians of 5 timed runs each, in us: (traffic alone, the cast)."""
+    import torch
+    import precision_quantization_amd as pq
+    rows, cols = x.shape
+    out = torch.empty(cols, rows, dtype=torch.uint8, device=dev)
+    q = torch.empty(cols, rows, dtype=torch.float8_e4m3fn, device=dev)
+    sf = torch.empty(cols, rows // 128, dtype=torch.float32, device=dev)
+    flush = torch.empty(1 << 30, dtype=torch.uint8, device=dev)
+    hev = HipEvents()
+    times = ([], [])
+    for _ in range(6):
+        for i in range(2):
+            flush.fill_(0)
+            a, b = hev.create(), hev.create()
+            pq.qcast_bench_time_next(a, b)
+            if i == 0:
+                pq.qcast_bench_per_channel_T_traffic(x, out=out)
+            else:
+                pq.qcast_per_channel_T(x, "e4m3", 128, out=q, out_sf=sf)
+            torch.cuda.synchronize()
+            times[i].append(hev.elapsed_ms(a, b))
+            hev.destroy(a)
+            hev.destroy(b)
+    med = [sorted(t[1:])[len(t[1:]) // 2] * 1e3 for t in times]
+    return med[0], med[1]
+
+
 def cpu_baseline(wls, fraction=1.0):
     """The oracle, single-threaded, on the first `fraction` of the rows of
     every workload (all of them by default: about 10 s of CPU work); GB/s
@@ -452,6 +487,13 @@ def main():
     for k in kernels.values():
         k["copy_GBps"] = round(ceilings[k["bytes"]], 1)
         k["of_copy"] = round(k["GBps"] / ceilings[k["bytes"]], 4)
+    pt = kernels["per_channel_T"]
+    pc_x = next(wl for name, wl in wls if name == "per_channel_T").x.to(dev)
+    pattern_us, flushed_us = pattern_ceiling(dev, pc_x)
+    pt["pattern_us"] = round(pattern_us, 2)
+    pt["flushed_us"] = round(flushed_us, 2)
+    pt["of_pattern"] = round(pattern_us / flushed_us, 4)
+    del pc_x
     result = {
         "metric": METRIC,
         "value": round(step_bytes * args.steps / elapsed / 1e9, 1),

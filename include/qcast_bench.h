@@ -13,6 +13,11 @@
  * dispatch itself (hipExtLaunchKernel): their elapsed time is that kernel's
  * own duration, with no marker packets around it.
  *
+ * qcast_bench_per_channel_T_traffic: the memory traffic of qcast_per_channel_T
+ * alone -- its workgroup-to-tile walk, its loads and its qT stores, with no
+ * arithmetic -- so that bench.py can time the ceiling the transposed layout
+ * sets for that cast, next to the copy's.
+ *
  * qcast_bench_check_scale: runs the kernels' own scale routine on a range of
  * fp32 bit patterns and counts where it differs from the IEEE quotients
  * a / fmt_max and 1 / sf. The casts compute sf and sf_inv with short FMA
@@ -44,6 +49,18 @@ QCAST_API int qcast_bench_copy(const void* src, void* dst, int64_t nbytes, void*
  * returns an error before launching leaves the events pending for the next
  * launch. Returns QCAST_ERR_NULL if either event is null. */
 QCAST_API int qcast_bench_time_next(void* start_event, void* stop_event);
+
+/* Loads x [rows, cols] bf16 and stores qT [cols, rows] bytes exactly as
+ * qcast_per_channel_T with group 128 does (same launch, same addresses);
+ * every stored 16 bytes is the XOR of two 16-byte vectors the same lane
+ * loaded. With cols a multiple of 64 (whole channel tiles) every loaded
+ * vector goes into exactly one store, so the XOR of all of qT's 16-byte
+ * vectors equals that of all of x's. No scales are written. Same
+ * shape, limit and alignment rules as qcast_per_channel_T: QCAST_ERR_SHAPE,
+ * QCAST_ERR_NULL or QCAST_ERR_ALIGN before any HIP call, QCAST_ERR_LAUNCH if
+ * the launch fails; rows == 0 or cols == 0 launches nothing. */
+QCAST_API int qcast_bench_per_channel_T_traffic(const void* x, int64_t rows, int64_t cols,
+                                                void* qT, void* stream);
 
 /* Number of workgroups of qcast_bench_check_scale: `counts` holds two
  * uint32 per workgroup. */

@@ -28,6 +28,7 @@ __all__ = ["qcast_per_token", "qcast_e2m1", "qcast_swiglu_per_token", "qcast_per
            "sf_layout_shape", "SF_ROUND_POW2", "SF_COL_MAJOR",
            "SF_PACKED_UE8M0", "qcast_abi_version", "qcast_set_num_cus", "qcast_bench_copy",
            "qcast_bench_check_scale", "qcast_bench_time_next",
+           "qcast_bench_per_channel_T_traffic",
            "per_token_cast",
            "QcastError", "FMT_E4M3", "FMT_E2M1", "FMT_E5M2", "FMT_E5M6", "code_shape"]
 
@@ -401,6 +402,20 @@ def qcast_bench_copy(src, dst, stream=None):
     with torch.cuda.device(src.device):
         check(load().qcast_bench_copy(src.data_ptr(), dst.data_ptr(), n, _stream(src.device, stream)),
               "qcast_bench_copy")
+
+
+def qcast_bench_per_channel_T_traffic(x, out=None, stream=None):
+    """Measurement helper (include/qcast_bench.h): the loads and qT stores of
+    qcast_per_channel_T on bf16 ``x [tokens, channels]`` without its
+    arithmetic; ``out [channels, tokens]`` bytes receives meaningless data."""
+    x = _bf16_input(x, "x")
+    rows, cols = x.shape
+    out = _out(out, (cols, rows), torch.uint8, x.device, "out")
+    with torch.cuda.device(x.device):
+        check(load().qcast_bench_per_channel_T_traffic(x.data_ptr(), rows, cols, out.data_ptr(),
+                                                       _stream(x.device, stream)),
+              "qcast_bench_per_channel_T_traffic")
+    return out
 
 
 def qcast_bench_check_scale(fmt, first, last, device="cuda:0", stream=None):

@@ -83,6 +83,8 @@ def load():
     lib.qcast_bench_check_scale.restype = i32
     lib.qcast_bench_time_next.argtypes = [vp, vp]
     lib.qcast_bench_time_next.restype = i32
+    lib.qcast_bench_per_channel_T_traffic.argtypes = [vp, i64, i64, vp, vp]
+    lib.qcast_bench_per_channel_T_traffic.restype = i32
     lib.qcast_set_num_cus.argtypes = [i32]
     lib.qcast_set_num_cus.restype = None
     _lib = lib
@@ -100,4 +102,5 @@ EXPORTS = ["qcast_per_token", "qcast_e2m1", "qcast_swiglu_per_token", "qcast_per
            "qcast_swiglu_per_token_sf", "qcast_swiglu_per_token_ex",
            "qcast_swiglu_backward_per_token", "qcast_swiglu_per_channel_T", "qcast_per_channel",
            "qcast_status_str", "qcast_abi_version", "qcast_set_num_cus",
-           "qcast_bench_copy", "qcast_bench_check_scale", "qcast_bench_time_next"]
+           "qcast_bench_copy", "qcast_bench_check_scale", "qcast_bench_time_next",
+           "qcast_bench_per_channel_T_traffic"]

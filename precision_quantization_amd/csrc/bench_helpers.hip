@@ -4,7 +4,9 @@
 //  - a streaming copy, the bandwidth ceiling and counter calibration for the
 //    cast kernels (16-byte non-temporal loads and stores, as the casts);
 //  - an exhaustive check of the kernels' scale routine against IEEE
-//    division.
+//    division;
+//  - the transposed per-channel cast's memory traffic without its
+//    arithmetic (the kernel lives beside the cast, in per_channel_t.hip).
 #include <atomic>
 
 #include "qcast_bench.h"
@@ -137,6 +139,23 @@ extern "C" int qcast_bench_copy(const void* src, void* dst, int64_t nbytes, void
                        static_cast<hipStream_t>(stream), static_cast<const qcast::u32x4*>(src),
                        static_cast<qcast::u32x4*>(dst), n);
   return hipGetLastError() == hipSuccess ? QCAST_OK : QCAST_ERR_LAUNCH;
+}
+
+extern "C" int qcast_bench_per_channel_T_traffic(const void* x, int64_t rows, int64_t cols,
+                                                 void* qT, void* stream) {
+  if (rows < 0 || cols < 0 || rows % 128 != 0 || cols % 8 != 0 ||
+      !qcast::per_channel_t_fits(rows, cols, cols))
+    return QCAST_ERR_SHAPE;
+  if (rows == 0 || cols == 0) return QCAST_OK;
+  if (!x || !qT) return QCAST_ERR_NULL;
+  if ((reinterpret_cast<uintptr_t>(x) | reinterpret_cast<uintptr_t>(qT)) & 15)
+    return QCAST_ERR_ALIGN;
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess) return QCAST_ERR_DEVICE;
+  return qcast::launch_per_channel_T_traffic(x, rows, cols, qT,
+                                             static_cast<hipStream_t>(stream)) == hipSuccess
+             ? QCAST_OK
+             : QCAST_ERR_LAUNCH;
 }
 
 extern "C" int qcast_bench_time_next(void* start_event, void* stop_event) {

@@ -343,6 +343,34 @@ __global__ __launch_bounds__(kThreads) void per_channel_t_kernel(
   process_tile<kFmt>(tc, tile, rows, ngroups, floor, sm, qT, sf);
 }
 
+// The cast's memory traffic alone, for measurement: the same workgroup ->
+// tile walk, the same loads, and the same qT stores (each stored 16 bytes
+// the XOR of two loaded vectors of the lane, so every loaded vector reaches
+// exactly one store), with no scale, code or LDS work.
+__global__ __launch_bounds__(kThreads) void per_channel_t_traffic_kernel(
+    const uint16_t* __restrict__ x, uint32_t rows, uint32_t cols, uint32_t ngroups,
+    uint32_t nct, uint32_t ntiles, uint32_t per_xcd, uint8_t* __restrict__ qT) {
+  static_assert(kPasses * 4 == 2 * kReadPasses, "two loaded vectors per stored one");
+  const uint32_t b = blockIdx.x;
+  const uint32_t tau = (kOrder & 2) ? b : (b % kXcds) * per_xcd + b / kXcds;
+  if (tau >= ntiles) return;
+  const TileCoord tc = tile_coord(tau, ngroups, cols, nct, ntiles / nct);
+  u32x4 raw[kPasses][4];
+  load_tile(x, cols, tc, raw);
+  const int t = threadIdx.x;
+  uint8_t* out = qT + (uint64_t)tc.c0 * rows + tc.t0;
+#pragma unroll
+  for (int r = 0; r < kReadPasses; ++r) {
+    const int idx = t + r * kThreads;
+    const int c = idx / kRowVec;
+    const int mv = idx % kRowVec;
+    if (c < tc.nc && mv * 16 < tc.ng * kGroupTokens) {
+      const u32x4 val = raw[(2 * r) / 4][(2 * r) % 4] ^ raw[(2 * r + 1) / 4][(2 * r + 1) % 4];
+      store_stream(reinterpret_cast<u32x4*>(out + (uint32_t)c * rows + mv * 16), val);
+    }
+  }
+}
+
 // SwiGLU + the same cast. Without a clamp counter (kCountNone): one
 // workgroup per tile. With a counter and a count workspace (kCountSlotted):
 // the same, every workgroup (also one past the last tile) ending in one
@@ -494,6 +522,17 @@ hipError_t launch_per_channel_T(const void* x, int64_t rows, int64_t cols, int f
   launch_kernel(kernel, dim3(g.grid), dim3(kThreads), 0, stream,
                 static_cast<const uint16_t*>(x), (uint32_t)rows, (uint32_t)cols, g.ngroups,
                 g.nct, g.ntiles, g.per_xcd, floor, static_cast<uint8_t*>(qT), sf);
+  return hipGetLastError();
+}
+
+hipError_t launch_per_channel_T_traffic(const void* x, int64_t rows, int64_t cols, void* qT,
+                                        hipStream_t stream) {
+  Grid g;
+  if (!make_grid(rows, cols, cols, &g)) return hipErrorInvalidValue;
+  if (g.ntiles == 0) return hipSuccess;
+  launch_kernel(per_channel_t_traffic_kernel, dim3(g.grid), dim3(kThreads), 0, stream,
+                static_cast<const uint16_t*>(x), (uint32_t)rows, (uint32_t)cols, g.ngroups,
+                g.nct, g.ntiles, g.per_xcd, static_cast<uint8_t*>(qT));
   return hipGetLastError();
 }
 

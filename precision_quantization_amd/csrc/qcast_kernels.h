@@ -87,6 +87,11 @@ hipError_t launch_per_channel_T(const void* x, int64_t rows, int64_t cols, int f
                                 void* qT, float* sf, hipStream_t stream,
                                 const LaunchCaps& caps);
 
+// The memory traffic of launch_per_channel_T alone (same grid, loads and
+// qT stores; meaningless bytes, no scales), for measurement.
+hipError_t launch_per_channel_T_traffic(const void* x, int64_t rows, int64_t cols, void* qT,
+                                        hipStream_t stream);
+
 // SwiGLU of h [rows, 2*cols] (clamped when swiglu_clamp > 0, changed values
 // added to *clamp_count when not null, through count_ws as above), then the
 // per-channel cast written transposed: qT [cols, rows], sf [cols, rows/128].

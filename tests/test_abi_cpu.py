@@ -289,3 +289,14 @@ def test_missing_library_fails_loudly(monkeypatch, tmp_path):
     monkeypatch.setattr(_lib, "_lib", None)
     with pytest.raises(_lib.QcastError):
         _lib.load()
+
+
+def test_per_channel_T_traffic_validation(lib):
+    f = lib.qcast_bench_per_channel_T_traffic
+    assert f(A16, 200, 64, A16, None) == ERR_SHAPE          # tokens not a multiple of 128
+    assert f(A16, 256, 60, A16, None) == ERR_SHAPE          # channels not a multiple of 8
+    assert f(A16, 128, 1 << 24, A16, None) == ERR_SHAPE     # past the 32-bit tile offsets
+    assert f(A16, -128, 64, A16, None) == ERR_SHAPE
+    assert f(None, 256, 64, A16, None) == ERR_NULL
+    assert f(A16, 256, 64, MIS, None) == ERR_ALIGN
+    assert f(None, 0, 64, None, None) == OK

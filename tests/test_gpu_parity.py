@@ -588,3 +588,20 @@ def test_time_next_records_the_kernel(dev):
     assert torch.equal(q.view(torch.uint8), q2.view(torch.uint8))
     hip.hipEventDestroy(a)
     hip.hipEventDestroy(b)
+
+
+@pytest.mark.parametrize("rows,cols", [(256, 192), (1024, 512), (16384, 7168)])
+def test_per_channel_T_traffic_moves_every_vector_once(dev, rows, cols):
+    # the measurement helper loads and stores what the cast does: with whole
+    # channel tiles every loaded 16-byte vector lands in exactly one stored
+    # one, so the XOR over all vectors is preserved; nothing past qT is written
+    g = torch.Generator().manual_seed(rows + cols)
+    x = torch.randn(rows, cols, generator=g).to(torch.bfloat16)
+    big = torch.full((cols * rows + 4096,), 0xA5, dtype=torch.uint8, device=dev)
+    out = big[:cols * rows].view(cols, rows)
+    pq.qcast_bench_per_channel_T_traffic(x.to(dev), out=out)
+    torch.cuda.synchronize()
+    xv = x.contiguous().view(torch.int32).numpy().reshape(-1, 4)
+    ov = out.view(torch.int32).cpu().numpy().reshape(-1, 4)
+    assert np.array_equal(np.bitwise_xor.reduce(xv, axis=0), np.bitwise_xor.reduce(ov, axis=0))
+    assert bool((big[cols * rows:] == 0xA5).all())
