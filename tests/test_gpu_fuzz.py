@@ -1,0 +1,156 @@
+"""Seeded random cases for every pure cast, each bit-exact against the oracle.
+
+The fixed-shape parity tests pin the configurations and the edge cases one by
+one; these draw shapes, formats, group sizes and scale layouts at random (from
+a fixed seed, so every run sees the same cases) and plant the special groups
+the method has -- all +0, all -0, floor-active magnitudes, a single nonzero,
+the largest bf16, bf16 subnormals -- at random places, to catch an indexing
+or tail mistake that the hand-picked shapes miss.
+"""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import precision_quantization_amd as pq
+from precision_quantization_amd import workloads
+
+pytestmark = pytest.mark.gpu
+
+FORMATS = ["e4m3", "e5m2", "e2m1", "e5m6"]
+SF_FLAG_SETS = [0, pq.SF_ROUND_POW2, pq.SF_COL_MAJOR, pq.SF_ROUND_POW2 | pq.SF_COL_MAJOR,
+                pq.SF_PACKED_UE8M0, pq.SF_PACKED_UE8M0 | pq.SF_COL_MAJOR]
+BF16_MAX = 3.3895313892515355e38
+
+
+@pytest.fixture(scope="module")
+def dev():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    return torch.device("cuda:0")
+
+
+def random_input(rng, rows, cols, group, scale=None):
+    """bf16 [rows, cols]: per-row magnitudes over many octaves (times
+    `scale`, an array broadcast over [rows, cols], if given), with special
+    groups planted along the rows afterwards (group = the cast's scale group
+    width). Every value is finite: the casts define none other."""
+    x = rng.standard_normal((rows, cols)).astype(np.float32)
+    x *= np.exp(rng.standard_normal((rows, 1)) * 5).astype(np.float32)
+    if scale is not None:
+        x *= scale
+    groups = cols // group
+    for _ in range(max(1, rows * groups // 8)):
+        r, gi = int(rng.integers(rows)), int(rng.integers(groups))
+        seg = slice(gi * group, (gi + 1) * group)
+        kind = int(rng.integers(6))
+        if kind == 0:
+            x[r, seg] = 0.0
+        elif kind == 1:
+            x[r, seg] = -0.0
+        elif kind == 2:
+            x[r, seg] = rng.standard_normal(group) * 2e-5          # under the 1e-4 floor
+        elif kind == 3:
+            x[r, seg] = 0.0
+            x[r, gi * group + int(rng.integers(group))] = float(rng.standard_normal()) * 3
+        elif kind == 4:
+            x[r, gi * group + int(rng.integers(group))] = BF16_MAX * (1 if rng.random() < .5 else -1)
+        else:
+            x[r, seg] = rng.standard_normal(group) * 2.0 ** -130    # bf16 subnormals
+    xb = torch.from_numpy(x).to(torch.bfloat16)
+    assert bool(torch.isfinite(xb).all())
+    return xb
+
+
+def per_token_cases():
+    rng = np.random.default_rng(20261202)
+    cases = []
+    for i in range(48):
+        fmt = FORMATS[i % 4]
+        group = int(rng.choice([32, 64, 128]))
+        flags = int(rng.choice(SF_FLAG_SETS))
+        k = int(rng.integers(1, 48))
+        if flags & pq.SF_PACKED_UE8M0:
+            k = 4 * max(1, k // 4)
+        cases.append((fmt, group, flags, int(rng.integers(1, 260)), group * k, 1000 + i))
+    return cases
+
+
+@pytest.mark.parametrize("fmt,group,flags,rows,cols,seed", per_token_cases())
+def test_per_token_random(dev, fmt, group, flags, rows, cols, seed):
+    x = random_input(np.random.default_rng(seed), rows, cols, group)
+    fill = 0x5A5A5A5A
+    q_ref, sf_ref = oracle.per_token_sf(
+        workloads.bf16_bits(x), fmt, group, sf_flags=flags,
+        sf_fill=fill if flags & pq.SF_PACKED_UE8M0 else np.array([fill], np.uint32).view(np.float32)[0])
+    shape, dt = pq.sf_layout_shape(rows, cols, group, flags)
+    sf = torch.empty(shape, dtype=dt, device=dev)
+    sf.view(torch.uint8).fill_(0x5A)                     # unwritten padding stays 0x5A
+    q, _ = pq.qcast_per_token_sf(x.to(dev), fmt, group, sf_flags=flags, out_sf=sf)
+    torch.cuda.synchronize()
+    assert np.array_equal(q.view(torch.uint8).cpu().numpy(), q_ref)
+    assert np.array_equal(sf.cpu().numpy().view(np.uint32), sf_ref.view(np.uint32))
+
+
+def block_cases():
+    rng = np.random.default_rng(20261203)
+    return [(str(rng.choice(["e4m3", "e5m2"])), 128 * int(rng.integers(1, 7)),
+             128 * int(rng.integers(1, 10)), 2000 + i) for i in range(16)]
+
+
+@pytest.mark.parametrize("fmt,rows,cols,seed", block_cases())
+def test_per_block_random(dev, fmt, rows, cols, seed):
+    rng = np.random.default_rng(seed)
+    # a magnitude per 128 x 128 block as well
+    block = np.exp(rng.standard_normal((rows // 128, 1, cols // 128, 1)) * 3).astype(np.float32)
+    block = np.broadcast_to(block, (rows // 128, 128, cols // 128, 128)).reshape(rows, cols)
+    x = random_input(rng, rows, cols, 128, scale=block)
+    q_ref, sf_ref = oracle.per_block(workloads.bf16_bits(x), fmt, 128)
+    q, sf = pq.qcast_per_block(x.to(dev), fmt, 128)
+    torch.cuda.synchronize()
+    assert np.array_equal(q.view(torch.uint8).cpu().numpy(), q_ref)
+    assert np.array_equal(sf.cpu().numpy().view(np.uint32), sf_ref.view(np.uint32))
+
+
+def channel_cases():
+    rng = np.random.default_rng(20261204)
+    return [(str(rng.choice(["e4m3", "e5m2"])), 128 * int(rng.integers(1, 7)),
+             8 * int(rng.integers(1, 100)), 3000 + i) for i in range(16)]
+
+
+@pytest.mark.parametrize("fmt,rows,cols,seed", channel_cases())
+def test_per_channel_random(dev, fmt, rows, cols, seed):
+    # groups run along the tokens: plant the special groups in the transpose
+    x = random_input(np.random.default_rng(seed), cols, rows, 128).t().contiguous()
+    xb = workloads.bf16_bits(x)
+    qT_ref, sfT_ref = oracle.per_channel_T(xb, fmt, 128)
+    qT, sfT = pq.qcast_per_channel_T(x.to(dev), fmt, 128)
+    q, sf = pq.qcast_per_channel(x.to(dev), fmt, 128)
+    torch.cuda.synchronize()
+    assert np.array_equal(qT.view(torch.uint8).cpu().numpy(), qT_ref)
+    assert np.array_equal(sfT.cpu().numpy().view(np.uint32), sfT_ref.view(np.uint32))
+    q_ref, sf_ref = oracle.per_channel(xb, fmt, 128)
+    assert np.array_equal(q.view(torch.uint8).cpu().numpy(), q_ref)
+    assert np.array_equal(sf.cpu().numpy().view(np.uint32), sf_ref.view(np.uint32))
+
+
+def cast_back_cases():
+    rng = np.random.default_rng(20261205)
+    return [(FORMATS[i % 4], int(rng.choice([32, 64, 128])), bool(rng.random() < .5),
+             int(rng.integers(1, 200)), int(rng.integers(1, 40)), 4000 + i) for i in range(16)]
+
+
+@pytest.mark.parametrize("fmt,group,bf16_out,rows,k,seed", cast_back_cases())
+def test_cast_back_random(dev, fmt, group, bf16_out, rows, k, seed):
+    cols = group * k
+    x = random_input(np.random.default_rng(seed), rows, cols, group)
+    q_ref, sf_ref = oracle.per_token(workloads.bf16_bits(x), fmt, group)
+    out_ref = oracle.cast_back(q_ref, sf_ref, cols, fmt, group, "bf16" if bf16_out else "f32")
+    q = torch.from_numpy(q_ref).to(dev)
+    sf = torch.from_numpy(sf_ref).to(dev)
+    out = pq.qcast_cast_back(q, sf, fmt, group, torch.bfloat16 if bf16_out else torch.float32)
+    torch.cuda.synchronize()
+    got = out.cpu()
+    got = got.view(torch.int16).numpy().view(np.uint16) if bf16_out else got.numpy()
+    assert np.array_equal(got.view(np.uint16 if bf16_out else np.uint32),
+                          out_ref.view(np.uint16 if bf16_out else np.uint32))
