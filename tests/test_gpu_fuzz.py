@@ -1,4 +1,5 @@
-"""Seeded random cases for every pure cast, each bit-exact against the oracle.
+"""Seeded random cases for every cast: the pure casts bit-exact against the
+oracle, the SwiGLU forms within their tolerance with exact clamp counts.
 
 The fixed-shape parity tests pin the configurations and the edge cases one by
 one; these draw shapes, formats, group sizes and scale layouts at random (from
@@ -154,3 +155,87 @@ def test_cast_back_random(dev, fmt, group, bf16_out, rows, k, seed):
     got = got.view(torch.int16).numpy().view(np.uint16) if bf16_out else got.numpy()
     assert np.array_equal(got.view(np.uint16 if bf16_out else np.uint32),
                           out_ref.view(np.uint16 if bf16_out else np.uint32))
+
+
+# ------------------------------------------------------- the SwiGLU forms
+# These use the hardware's fast exp and reciprocal, so they are held to the
+# SwiGLU bar: scales within 1e-6 relative, at most 0.1% of codes (and at
+# least one) one step away, none further; clamp counts exact.
+
+def signed_code(c):
+    c = c.astype(np.int64)
+    return np.where(c & 0x80, -(c & 0x7F), c & 0x7F)
+
+
+def assert_swiglu_bar(q, sf, q_ref, sf_ref, what):
+    assert q.shape == q_ref.shape and sf.shape == sf_ref.shape, what
+    rel = np.abs(sf.astype(np.float64) - sf_ref) / sf_ref
+    assert rel.max() <= 1e-6, f"{what}: scale relative error {rel.max():.3g}"
+    diff = q != q_ref
+    assert diff.mean() <= 1e-3 + 1.0 / q.size, f"{what}: {diff.mean():.3%} of codes differ"
+    step = np.abs(signed_code(q[diff]) - signed_code(q_ref[diff]))
+    assert step.max(initial=0) <= 1, f"{what}: codes {step.max()} steps apart"
+
+
+def swiglu_random_input(rng, rows, cols):
+    """h [rows, 2*cols] bf16 ~ N(0, 2) with planted rows (a zero gate, a
+    +-100 gate, a zero up half) and w [rows] ~ U(0, 1) with one zero."""
+    h = rng.standard_normal((rows, 2 * cols)).astype(np.float32) * 2
+    for _ in range(max(1, rows // 16)):
+        r, kind = int(rng.integers(rows)), int(rng.integers(3))
+        if kind == 0:
+            h[r, :cols] = 0.0
+        elif kind == 1:
+            h[r, :cols] = np.where(rng.random(cols) < .5, -100.0, 100.0)
+        else:
+            h[r, cols:] = 0.0
+    w = rng.random(rows).astype(np.float32)
+    w[int(rng.integers(rows))] = 0.0
+    return torch.from_numpy(h).to(torch.bfloat16), torch.from_numpy(w)
+
+
+def swiglu_cases():
+    rng = np.random.default_rng(20261206)
+    cases = []
+    for i in range(24):
+        kind = ["forward", "backward", "transpose"][i % 3]
+        fmt = str(rng.choice(["e4m3", "e5m2"]))
+        clamp = 0.0 if rng.random() < .3 else float(np.round(rng.uniform(0.5, 8), 3))
+        weighted = bool(rng.random() < .7)
+        if kind == "transpose":
+            group, rows, cols = 128, 128 * int(rng.integers(1, 5)), 8 * int(rng.integers(1, 80))
+        else:
+            group = int(rng.choice([32, 64, 128]))
+            rows, cols = int(rng.integers(1, 200)), group * int(rng.integers(1, 24))
+        cases.append((kind, fmt, group, clamp, weighted, rows, cols, 5000 + i))
+    return cases
+
+
+@pytest.mark.parametrize("kind,fmt,group,clamp,weighted,rows,cols,seed", swiglu_cases())
+def test_swiglu_random(dev, kind, fmt, group, clamp, weighted, rows, cols, seed):
+    rng = np.random.default_rng(seed)
+    h, w = swiglu_random_input(rng, rows, cols)
+    hb = workloads.bf16_bits(h)
+    wn = w.numpy() if weighted else None
+    wd = w.to(dev) if weighted else None
+    count = torch.zeros(1, dtype=torch.int64, device=dev)
+    what = f"{kind} {fmt} g{group} c{clamp} {rows}x{cols}"
+    if kind == "forward":
+        q_ref, sf_ref, n_ref = oracle.swiglu_per_token_ex(hb, wn, fmt, group, swiglu_clamp=clamp)
+        q, sf = pq.qcast_swiglu_per_token_ex(h.to(dev), wd, fmt, group, swiglu_clamp=clamp,
+                                             clamp_count=count)
+    elif kind == "backward":
+        dv = torch.from_numpy(rng.standard_normal((rows, cols)).astype(np.float32)).to(torch.bfloat16)
+        q_ref, sf_ref = oracle.swiglu_backward_per_token(hb, workloads.bf16_bits(dv), wn, fmt,
+                                                         group, swiglu_clamp=clamp)
+        q, sf = pq.qcast_swiglu_backward_per_token(h.to(dev), dv.to(dev), wd, fmt, group,
+                                                   swiglu_clamp=clamp)
+        n_ref = 0
+    else:
+        q_ref, sf_ref = oracle.swiglu_per_channel_T(hb, wn, fmt, 128, swiglu_clamp=clamp)
+        n_ref = oracle.swiglu_values_ex(hb, wn, swiglu_clamp=clamp)[1]
+        q, sf = pq.qcast_swiglu_per_channel_T(h.to(dev), wd, fmt, 128, swiglu_clamp=clamp,
+                                              clamp_count=count)
+    torch.cuda.synchronize()
+    assert_swiglu_bar(q.view(torch.uint8).cpu().numpy(), sf.cpu().numpy(), q_ref, sf_ref, what)
+    assert int(count.item()) == n_ref, what
