@@ -40,6 +40,9 @@
 // v = silu(g) * u * w in fp32 registers (clamped first when asked, counting
 // the changed values), and the tile continues from fp32 values instead of
 // packed bf16.
+//
+// A traffic-only twin of the cast (per_channel_t_traffic_kernel: the same
+// walk, loads and qT stores, no arithmetic) serves measurement only.
 #include "qcast_device.h"
 #include "qcast_kernels.h"
 

@@ -20,7 +20,9 @@
 //
 // The optional clamp of the same section bounds the gate from above and the
 // up value to [-c, c] before the product; the number of values it changed
-// is summed per workgroup and added to a 64-bit counter with one atomic.
+// is summed per workgroup and reaches a 64-bit counter either through the
+// slots of a caller's count workspace (full grid) or with one atomic per
+// workgroup of a capped grid (no workspace).
 #include "qcast_device.h"
 #include "qcast_kernels.h"
 
