@@ -23,7 +23,9 @@ copy_GBps, the library's streaming copy moving the same byte count after a
 carries pattern_us, its own loads and transposed stores without the
 arithmetic (qcast_bench_per_channel_T_traffic), flushed_us, the cast timed
 the same way (alternating with it, each after the flush), and of_pattern,
-their ratio. The CPU baseline
+their ratio. Each step kernel also carries "flushed": 30 dispatches, each
+after a 1 GiB flush on the same stream (median, p10, p90 and GB/s at the
+median), the cold-cache protocol beside the in-step timing. The CPU baseline
 is the oracle (single thread) on every workload in full, on this host (about
 10 s); cpu_baseline_all_cores splits the same work over up to 16 cores.
 
@@ -332,6 +334,28 @@ def _oracle_cast(name, xb, w):
         oracle.e2m1(xb, 32)
 
 
+def flushed_runs(fns, dev, runs=30):
+    """Each closure timed on `runs` dispatches, every one after a 1 GiB flush
+    on the same stream (the cold-cache protocol), the closures interleaved;
+    per closure the sorted durations in ms."""
+    import torch
+    import precision_quantization_amd as pq
+    flush = torch.empty(1 << 30, dtype=torch.uint8, device=dev)
+    hev = HipEvents()
+    out = [[] for _ in fns]
+    for r in range(runs):
+        for i, fn in enumerate(fns):
+            flush.fill_(r & 0xFF)
+            a, b = hev.create(), hev.create()
+            pq.qcast_bench_time_next(a, b)
+            fn()
+            torch.cuda.synchronize()
+            out[i].append(hev.elapsed_ms(a, b))
+            hev.destroy(a)
+            hev.destroy(b)
+    return [sorted(t) for t in out]
+
+
 def pattern_ceiling(dev, x):
     """The transposed per-channel cast against its memory traffic alone
     (include/qcast_bench.h: the same loads and qT stores, no arithmetic), on
@@ -487,6 +511,12 @@ def main():
     for k in kernels.values():
         k["copy_GBps"] = round(ceilings[k["bytes"]], 1)
         k["of_copy"] = round(k["GBps"] / ceilings[k["bytes"]], 4)
+    for (name, wl, _), ms in zip(calls, flushed_runs([fn for _, _, fn in calls], dev)):
+        k = kernels[name]
+        sp = spread_us(ms)
+        k["flushed"] = {"runs": len(ms), "median_us": sp["median_us"], "p10_us": sp["p10_us"],
+                        "p90_us": sp["p90_us"],
+                        "GBps": round(k["bytes"] / (sp["median_us"] * 1e-6) / 1e9, 1)}
     pt = kernels["per_channel_T"]
     pc_x = next(wl for name, wl in wls if name == "per_channel_T").x.to(dev)
     pattern_us, flushed_us = pattern_ceiling(dev, pc_x)
