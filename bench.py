@@ -15,7 +15,7 @@ value = algorithmic bytes of the whole step (inputs read once, codes and
 scales written once) / time per step, in GB/s. Per-kernel durations come from
 HIP events that kernels of the timed steps record from their own dispatch on
 the launch stream (qcast_bench_time_next): step s times kernel s mod 5, so
-with the default 50 steps every kernel is timed on 10 of its launches (their
+with the default 200 steps every kernel is timed on 40 of its launches (their
 average, median, 10th and 90th percentile). The roofline object is for the
 kernel with the largest share of the step. Each step kernel also carries
 copy_GBps, the library's streaming copy moving the same byte count after a
@@ -37,7 +37,7 @@ per-token E5M6 cast and its cast_back,
 SwiGLU with the clamp and counter, SwiGLU + per-channel cast + transpose,
 the SwiGLU backward cast, and the per-channel cast in the input layout.
 
-    python bench.py [--gpus 1] [--steps 50] [--warmup 5]
+    python bench.py [--gpus 1] [--steps 200] [--warmup 10]
 """
 import argparse
 import json
@@ -453,8 +453,8 @@ def load_traffic(dominant):
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=50)
-    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--steps", type=int, default=200)
+    ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-extras", action="store_true",
                     help="skip timing the casts that are not part of the step")
