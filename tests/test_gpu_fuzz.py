@@ -22,6 +22,9 @@ FORMATS = ["e4m3", "e5m2", "e2m1", "e5m6"]
 SF_FLAG_SETS = [0, pq.SF_ROUND_POW2, pq.SF_COL_MAJOR, pq.SF_ROUND_POW2 | pq.SF_COL_MAJOR,
                 pq.SF_PACKED_UE8M0, pq.SF_PACKED_UE8M0 | pq.SF_COL_MAJOR]
 BF16_MAX = 3.3895313892515355e38
+# clamp_min values: the format's default (0), and caller floors above and
+# below it (the planted groups of magnitude 2e-5 sit between them)
+FLOORS = [0.0, 0.0, 1e-6, 3e-3, 0.25]
 
 
 @pytest.fixture(scope="module")
@@ -73,21 +76,23 @@ def per_token_cases():
         k = int(rng.integers(1, 48))
         if flags & pq.SF_PACKED_UE8M0:
             k = 4 * max(1, k // 4)
-        cases.append((fmt, group, flags, int(rng.integers(1, 260)), group * k, 1000 + i))
+        cases.append((fmt, group, flags, int(rng.integers(1, 260)), group * k,
+                      float(rng.choice(FLOORS)), 1000 + i))
     return cases
 
 
-@pytest.mark.parametrize("fmt,group,flags,rows,cols,seed", per_token_cases())
-def test_per_token_random(dev, fmt, group, flags, rows, cols, seed):
+@pytest.mark.parametrize("fmt,group,flags,rows,cols,floor,seed", per_token_cases())
+def test_per_token_random(dev, fmt, group, flags, rows, cols, floor, seed):
     x = random_input(np.random.default_rng(seed), rows, cols, group)
     fill = 0x5A5A5A5A
     q_ref, sf_ref = oracle.per_token_sf(
-        workloads.bf16_bits(x), fmt, group, sf_flags=flags,
+        workloads.bf16_bits(x), fmt, group, clamp_min=floor, sf_flags=flags,
         sf_fill=fill if flags & pq.SF_PACKED_UE8M0 else np.array([fill], np.uint32).view(np.float32)[0])
     shape, dt = pq.sf_layout_shape(rows, cols, group, flags)
     sf = torch.empty(shape, dtype=dt, device=dev)
     sf.view(torch.uint8).fill_(0x5A)                     # unwritten padding stays 0x5A
-    q, _ = pq.qcast_per_token_sf(x.to(dev), fmt, group, sf_flags=flags, out_sf=sf)
+    q, _ = pq.qcast_per_token_sf(x.to(dev), fmt, group, clamp_min=floor, sf_flags=flags,
+                                 out_sf=sf)
     torch.cuda.synchronize()
     assert np.array_equal(q.view(torch.uint8).cpu().numpy(), q_ref)
     assert np.array_equal(sf.cpu().numpy().view(np.uint32), sf_ref.view(np.uint32))
@@ -96,18 +101,19 @@ def test_per_token_random(dev, fmt, group, flags, rows, cols, seed):
 def block_cases():
     rng = np.random.default_rng(20261203)
     return [(str(rng.choice(["e4m3", "e5m2"])), 128 * int(rng.integers(1, 7)),
-             128 * int(rng.integers(1, 10)), 2000 + i) for i in range(16)]
+             128 * int(rng.integers(1, 10)), float(rng.choice(FLOORS)), 2000 + i)
+            for i in range(16)]
 
 
-@pytest.mark.parametrize("fmt,rows,cols,seed", block_cases())
-def test_per_block_random(dev, fmt, rows, cols, seed):
+@pytest.mark.parametrize("fmt,rows,cols,floor,seed", block_cases())
+def test_per_block_random(dev, fmt, rows, cols, floor, seed):
     rng = np.random.default_rng(seed)
     # a magnitude per 128 x 128 block as well
     block = np.exp(rng.standard_normal((rows // 128, 1, cols // 128, 1)) * 3).astype(np.float32)
     block = np.broadcast_to(block, (rows // 128, 128, cols // 128, 128)).reshape(rows, cols)
     x = random_input(rng, rows, cols, 128, scale=block)
-    q_ref, sf_ref = oracle.per_block(workloads.bf16_bits(x), fmt, 128)
-    q, sf = pq.qcast_per_block(x.to(dev), fmt, 128)
+    q_ref, sf_ref = oracle.per_block(workloads.bf16_bits(x), fmt, 128, clamp_min=floor)
+    q, sf = pq.qcast_per_block(x.to(dev), fmt, 128, clamp_min=floor)
     torch.cuda.synchronize()
     assert np.array_equal(q.view(torch.uint8).cpu().numpy(), q_ref)
     assert np.array_equal(sf.cpu().numpy().view(np.uint32), sf_ref.view(np.uint32))
@@ -116,21 +122,22 @@ def test_per_block_random(dev, fmt, rows, cols, seed):
 def channel_cases():
     rng = np.random.default_rng(20261204)
     return [(str(rng.choice(["e4m3", "e5m2"])), 128 * int(rng.integers(1, 7)),
-             8 * int(rng.integers(1, 100)), 3000 + i) for i in range(16)]
+             8 * int(rng.integers(1, 100)), float(rng.choice(FLOORS)), 3000 + i)
+            for i in range(16)]
 
 
-@pytest.mark.parametrize("fmt,rows,cols,seed", channel_cases())
-def test_per_channel_random(dev, fmt, rows, cols, seed):
+@pytest.mark.parametrize("fmt,rows,cols,floor,seed", channel_cases())
+def test_per_channel_random(dev, fmt, rows, cols, floor, seed):
     # groups run along the tokens: plant the special groups in the transpose
     x = random_input(np.random.default_rng(seed), cols, rows, 128).t().contiguous()
     xb = workloads.bf16_bits(x)
-    qT_ref, sfT_ref = oracle.per_channel_T(xb, fmt, 128)
-    qT, sfT = pq.qcast_per_channel_T(x.to(dev), fmt, 128)
-    q, sf = pq.qcast_per_channel(x.to(dev), fmt, 128)
+    qT_ref, sfT_ref = oracle.per_channel_T(xb, fmt, 128, clamp_min=floor)
+    qT, sfT = pq.qcast_per_channel_T(x.to(dev), fmt, 128, clamp_min=floor)
+    q, sf = pq.qcast_per_channel(x.to(dev), fmt, 128, clamp_min=floor)
     torch.cuda.synchronize()
     assert np.array_equal(qT.view(torch.uint8).cpu().numpy(), qT_ref)
     assert np.array_equal(sfT.cpu().numpy().view(np.uint32), sfT_ref.view(np.uint32))
-    q_ref, sf_ref = oracle.per_channel(xb, fmt, 128)
+    q_ref, sf_ref = oracle.per_channel(xb, fmt, 128, clamp_min=floor)
     assert np.array_equal(q.view(torch.uint8).cpu().numpy(), q_ref)
     assert np.array_equal(sf.cpu().numpy().view(np.uint32), sf_ref.view(np.uint32))
 
