@@ -265,9 +265,10 @@ struct Smem {
   float inv_s[kTG][kChannels];
 };
 
-// Scales, codes and stores of one tile whose values are in raw. Starts and
-// ends with the workgroup converged; the LDS is free again on return.
-template <int kFmt, class Tile>
+// Scales, codes and stores of one tile whose values are in raw. Starts with
+// the workgroup converged; with kReuse (a workgroup that goes on to another
+// tile) it also ends converged, with the LDS free again.
+template <int kFmt, bool kReuse, class Tile>
 __device__ __forceinline__ void process_tile(const TileCoord& tc, const Tile& tile, uint32_t rows,
                                              uint32_t ngroups, float floor, Smem& sm,
                                              uint8_t* __restrict__ qT, float* __restrict__ sf) {
@@ -327,7 +328,7 @@ __device__ __forceinline__ void process_tile(const TileCoord& tc, const Tile& ti
       store_stream(reinterpret_cast<u32x4*>(out + (uint32_t)c * rows + mv * 16), val);
     }
   }
-  __syncthreads();  // the LDS tile is reused by the next tile
+  if (kReuse) __syncthreads();  // the LDS tile is reused by the next tile
 }
 
 // One workgroup per tile.
@@ -343,7 +344,7 @@ __global__ __launch_bounds__(kThreads) void per_channel_t_kernel(
   const TileCoord tc = tile_coord(tau, ngroups, cols, nct, ntiles / nct);
   Bf16Tile tile;
   load_tile(x, cols, tc, tile.raw);
-  process_tile<kFmt>(tc, tile, rows, ngroups, floor, sm, qT, sf);
+  process_tile<kFmt, false>(tc, tile, rows, ngroups, floor, sm, qT, sf);
 }
 
 // The cast's memory traffic alone, for measurement: the same workgroup ->
@@ -396,7 +397,7 @@ __global__ __launch_bounds__(kThreads) void swiglu_per_channel_t_kernel(
       const TileCoord tc = tile_coord(tau, ngroups, cols, nct, ntiles / nct);
       F32Tile tile;
       n += load_swiglu_tile<kWeighted, kClamp, true>(h, w, cols, clamp, tc, tile);
-      process_tile<kFmt>(tc, tile, rows, ngroups, floor, sm, qT, sf);
+      process_tile<kFmt, true>(tc, tile, rows, ngroups, floor, sm, qT, sf);
     }
     add_wave_counts(n, count);
   } else {
@@ -408,7 +409,7 @@ __global__ __launch_bounds__(kThreads) void swiglu_per_channel_t_kernel(
       F32Tile tile;
       n = load_swiglu_tile<kWeighted, kClamp, kCount == kCountSlotted>(h, w, cols, clamp, tc,
                                                                         tile);
-      process_tile<kFmt>(tc, tile, rows, ngroups, floor, sm, qT, sf);
+      process_tile<kFmt, false>(tc, tile, rows, ngroups, floor, sm, qT, sf);
     }
     if constexpr (kCount == kCountSlotted) add_wave_counts_slotted(n, slots, count);
   }
