@@ -124,3 +124,68 @@ def test_graph_replays_count_through_a_workspace(dev):
         assert not ws.any(), replay
         got = [q.view(torch.uint8), sf, qt.view(torch.uint8), sft]
         assert all(torch.equal(a, b) for a, b in zip(got, ref)), replay
+
+
+def test_graph_replays_of_the_other_casts(dev):
+    # every other entry point under capture: cast_back, E5M6 and its
+    # cast_back, packed column-major scales, the SwiGLU backward, the
+    # per-channel cast in the input layout and the fused SwiGLU transpose
+    x = workloads.per_token_hidden(rows=256).x.to(dev)
+    h = workloads.swiglu_input(rows=256, cols=1024).x.to(dev)
+    w = workloads.swiglu_input(rows=256, cols=1024).w.to(dev)
+    hg, dv, wg = workloads.swiglu_grad(rows=256, cols=1024)
+    hg, dv, wg = hg.to(dev), dv.to(dev), wg.to(dev)
+    a = workloads.activation_channel(rows=512, cols=384).x.to(dev)
+    q8, sf8 = pq.qcast_per_token(x)
+    q6, sf6 = pq.qcast_per_token(x, "e5m6", 128)
+    torch.cuda.synchronize()
+    flags = pq.SF_PACKED_UE8M0 | pq.SF_COL_MAJOR
+    sshape, sdt = pq.sf_layout_shape(256, 7168, 32, flags)
+    f8 = torch.float8_e4m3fn
+
+    def alloc():
+        return [torch.empty(256, 7168, dtype=torch.bfloat16, device=dev),
+                torch.empty(256, 7168, dtype=torch.bfloat16, device=dev),
+                torch.empty(256, 7168, dtype=f8, device=dev),
+                torch.empty(sshape, dtype=sdt, device=dev),
+                torch.empty(256, 2048, dtype=f8, device=dev),
+                torch.empty(256, 16, device=dev),
+                torch.empty(512, 384, dtype=f8, device=dev),
+                torch.empty(4, 384, device=dev),
+                torch.empty(1024, 256, dtype=f8, device=dev),
+                torch.empty(1024, 2, device=dev)]
+
+    def casts(o):
+        pq.qcast_cast_back(q8, sf8, "e4m3", 128, out=o[0])
+        pq.qcast_cast_back(q6, sf6, "e5m6", 128, out=o[1])
+        pq.qcast_per_token_sf(x, "e4m3", 32, sf_flags=flags, out=o[2], out_sf=o[3])
+        pq.qcast_swiglu_backward_per_token(hg, dv, wg, "e4m3", 128, swiglu_clamp=6.0,
+                                           out=o[4], out_sf=o[5])
+        pq.qcast_per_channel(a, "e4m3", 128, out=o[6], out_sf=o[7])
+        pq.qcast_swiglu_per_channel_T(h, w, "e4m3", 128, out=o[8], out_sf=o[9])
+
+    eager = alloc()
+    casts(eager)
+    torch.cuda.synchronize()
+    ref = [t.view(torch.uint8).clone() for t in eager]
+    graph_outs = alloc()
+    for t in graph_outs:
+        t.view(torch.uint8).fill_(0xA5)
+    side = torch.cuda.Stream(dev)
+    side.wait_stream(torch.cuda.current_stream(dev))
+    with torch.cuda.stream(side):
+        casts(graph_outs)
+    torch.cuda.current_stream(dev).wait_stream(side)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        casts(graph_outs)
+    for replay in range(4):
+        for t in graph_outs:
+            t.view(torch.uint8).fill_(0x5A + replay)
+        torch.cuda.synchronize()
+        g.replay()
+        casts(eager)                       # eager work between the replays
+        torch.cuda.synchronize()
+        for i, (t, r) in enumerate(zip(graph_outs, ref)):
+            assert torch.equal(t.view(torch.uint8), r), (replay, i)
