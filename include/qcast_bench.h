@@ -1,6 +1,6 @@
 /*
  * qcast_bench.h -- measurement and self-check helpers exported by
- * libqcast.so. Neither is part of the quantization method.
+ * libqcast.so. None is part of the quantization method.
  *
  * qcast_bench_copy: a plain streaming copy with the casts' access pattern
  * (16-byte non-temporal loads and stores, 256-thread workgroups). bench.py
