@@ -459,6 +459,8 @@ def main():
     ap.add_argument("--no-extras", action="store_true",
                     help="skip timing the casts that are not part of the step")
     args = ap.parse_args()
+    if args.steps < 1 or args.warmup < 0:
+        ap.error("--steps must be at least 1 and --warmup at least 0")
     if args.gpus != 1:
         print(f"bench.py measures one GPU; --gpus {args.gpus} is not supported: the casts shard "
               "by rows with no exchange between GPUs, so a multi-GPU run adds nothing to "
