@@ -583,8 +583,9 @@ def test_time_next_records_the_kernel(dev):
     torch.cuda.synchronize()
     ms = ctypes.c_float()
     assert hip.hipEventElapsedTime(ctypes.byref(ms), a, b) == 0
-    # 89 MB at no more than the 8 TB/s peak takes at least 11 us
-    assert 0.011 <= ms.value < 10.0
+    # the events bracket the kernel: 89 MB cannot move in under 2 us (44 TB/s,
+    # beyond HBM and the last-level cache alike, which may hold the fresh input)
+    assert 0.002 <= ms.value < 10.0
     assert torch.equal(q.view(torch.uint8), q2.view(torch.uint8))
     hip.hipEventDestroy(a)
     hip.hipEventDestroy(b)
