@@ -321,6 +321,30 @@ def test_empty_input_is_a_no_op(dev):
     assert out.shape == (0, 256) and sf.shape == (0, 2)
 
 
+def test_every_entry_point_accepts_empty_inputs(dev):
+    bf = torch.bfloat16
+    e = lambda r, c: torch.empty(r, c, dtype=bf, device=dev)
+    assert pq.qcast_e2m1(e(0, 256), 32)[0].shape == (0, 128)
+    assert pq.qcast_per_token(e(0, 256), "e5m6", 128)[0].shape == (0, 384)
+    assert pq.qcast_per_token_sf(e(0, 512), "e4m3", 32, sf_flags=pq.SF_PACKED_UE8M0)[0].shape == (0, 512)
+    assert pq.qcast_per_block(e(0, 256))[0].shape == (0, 256)
+    assert pq.qcast_per_channel_T(e(0, 64))[0].shape == (64, 0)
+    assert pq.qcast_per_channel_T(e(128, 0))[0].shape == (0, 128)
+    assert pq.qcast_per_channel(e(0, 64))[0].shape == (0, 64)
+    count = torch.full((1,), 7, dtype=torch.int64, device=dev)
+    w = torch.empty(0, device=dev)
+    assert pq.qcast_swiglu_per_token(e(0, 512), w)[0].shape == (0, 256)
+    assert pq.qcast_swiglu_per_token_ex(e(0, 512), w, swiglu_clamp=1.0,
+                                        clamp_count=count)[0].shape == (0, 256)
+    assert pq.qcast_swiglu_per_channel_T(e(0, 512), w, swiglu_clamp=1.0,
+                                         clamp_count=count)[0].shape == (256, 0)
+    assert pq.qcast_swiglu_backward_per_token(e(0, 512), e(0, 256), w)[0].shape == (0, 512)
+    q = torch.empty(0, 256, dtype=torch.float8_e4m3fn, device=dev)
+    assert pq.qcast_cast_back(q, torch.empty(0, 2, device=dev)).shape == (0, 256)
+    torch.cuda.synchronize()
+    assert int(count.item()) == 7                        # untouched
+
+
 def test_side_stream_and_repeat_determinism(dev):
     wl = workloads.per_token_hidden(rows=512)
     x = wl.x.to(dev)
