@@ -58,6 +58,7 @@ def _load():
         "oracle_encode16": ([i32, f32], ctypes.c_uint16),
         "oracle_encode_array16": ([i32, vp, i64, vp], None),
         "oracle_decode_array16": ([i32, vp, i64, vp], None),
+        "oracle_exp_array": ([vp, i64, vp], None),
         "oracle_format_max": ([i32], f32),
         "oracle_default_floor": ([i32], f32),
         "oracle_scale": ([i32, f32, f32, vp, vp], i32),
@@ -115,6 +116,14 @@ def _code_shape(fmt, rows, cols):
     if fmt == FMT_E5M6:
         return (rows, cols // 2 * 3)
     return (rows, cols)
+
+
+def exp_f32(x):
+    """e^x rounded to the nearest fp32 value, for fp32 x (SiLU's exponential)."""
+    x = _f32(x)
+    out = np.empty_like(x)
+    _load().oracle_exp_array(_ptr(x), x.size, _ptr(out))
+    return out
 
 
 def format_max(fmt):

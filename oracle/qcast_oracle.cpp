@@ -57,13 +57,14 @@
  *    two) scale as its biased exponent byte, 4 per 32-bit word along the
  *    groups of a row, lowest group in the lowest byte.
  *
+ *  - the exponential in SiLU ([WALK] §3.3) is exp(-g) rounded once to the
+ *    nearest fp32 value (exp_f32 below), so the SwiGLU forms are a fixed
+ *    sequence of correctly rounded fp32 operations.
+ *
  * Pins (tests/test_oracle_*.py) hold every function to sources other than
- * itself. One step is parity unpinned at the bit level: the SwiGLU forms
- * (forward, backward, fused) call the host libm's expf, which nothing here
- * checks against a correctly rounded exponential; they are pinned to within
- * 2^-21 relative by a double-precision restatement (forward) and by float64
- * automatic differentiation (backward), and the GPU kernels are held to a
- * tolerance there, not to bit equality.
+ * itself; exp_f32 is pinned to a correctly rounded decimal exponential. The
+ * GPU's SwiGLU kernels use the hardware exponential, so they are held to a
+ * tolerance against these values, not to bit equality.
  *
  * Arithmetic discipline: plain C++ on one thread, fp32 where the method is
  * fp32 (the scale, the inverse, the scaled value, SwiGLU) with no
@@ -73,6 +74,7 @@
  */
 #include "qcast_oracle.h"
 
+#include <cfloat>
 #include <cmath>
 #include <cstring>
 #include <vector>
@@ -257,6 +259,37 @@ float decode(const FormatTable& t, uint16_t code) {
 bool fp_env_ok() {
   const unsigned csr = _mm_getcsr();
   return (csr & 0x8000u) == 0 && (csr & 0x0040u) == 0 && (csr & 0x6000u) == 0;
+}
+
+/* ------------------------------------------------------------------------ */
+/* Exponential                                                               */
+/* ------------------------------------------------------------------------ */
+
+/* e^x rounded to the nearest fp32 value. The double exponential lies within
+ * about one double ulp of e^x, so rounding it to fp32 picks the correctly
+ * rounded value unless it sits next to a midpoint between two fp32 values.
+ * There (within 2^-45 relative, which happens for 370 of the 2^32 inputs)
+ * the 64-bit-mantissa expl decides; over every fp32 input, the closest any
+ * double result comes to a midpoint is 2^-53 relative, about 2^11 expl ulps.
+ * 2^128 stands for the value after FLT_MAX: a result rounded up to it
+ * overflows to infinity. */
+float exp_f32(float x) {
+  const double d = std::exp(static_cast<double>(x));
+  const float f = static_cast<float>(d);
+  if (static_cast<double>(f) == d) return f; /* exact: x == 0, or +inf / 0 limits */
+  double lo, hi; /* the two fp32 values (or 2^128) around d */
+  if (static_cast<double>(f) < d) {
+    lo = f;
+    hi = (f == FLT_MAX) ? 0x1p128 : nextafterf(f, INFINITY);
+  } else {
+    hi = std::isinf(f) ? 0x1p128 : static_cast<double>(f);
+    lo = std::isinf(f) ? FLT_MAX : nextafterf(f, 0.0f);
+  }
+  const double mid = 0.5 * (lo + hi); /* exact */
+  if (std::fabs(d - mid) > 0x1p-45 * mid) return f;
+  const long double e = expl(static_cast<long double>(x));
+  const double pick = (e > static_cast<long double>(mid)) ? hi : lo;
+  return pick == 0x1p128 ? INFINITY : static_cast<float>(pick);
 }
 
 /* ------------------------------------------------------------------------ */
@@ -458,7 +491,7 @@ void swiglu_row(const uint16_t* hr, int64_t cols, float wr, bool weighted, float
       if (u > clamp) { u = clamp; if (count) ++*count; }
       else if (u < -clamp) { u = -clamp; if (count) ++*count; }
     }
-    const float silu = g / (1.0f + std::exp(-g));
+    const float silu = g / (1.0f + exp_f32(-g));
     float val = silu * u;
     if (weighted) val = val * wr;
     v[j] = val;
@@ -481,6 +514,10 @@ int check_sf_flags(int flags, int64_t cols, int group) {
 extern "C" {
 
 int oracle_version(void) { return 1; }
+
+void oracle_exp_array(const float* x, int64_t n, float* out) {
+  for (int64_t i = 0; i < n; ++i) out[i] = exp_f32(x[i]);
+}
 
 /* The byte forms serve the formats whose codes fit a byte; E5M6 codes go
  * through the 16-bit forms. */
@@ -755,7 +792,7 @@ int oracle_swiglu_backward_values(const uint16_t* h, const uint16_t* dv, int64_t
         if (u > swiglu_clamp) { u = swiglu_clamp; u_pass = false; }
         else if (u < -swiglu_clamp) { u = -swiglu_clamp; u_pass = false; }
       }
-      const float e = std::exp(-g);
+      const float e = exp_f32(-g);
       const float s = 1.0f / (1.0f + e);
       const float silu = g * s;
       const float dsilu = s + silu * (1.0f - s);

@@ -52,6 +52,8 @@ float oracle_decode16(int fmt, uint16_t code);
 uint16_t oracle_encode16(int fmt, float y);
 void oracle_encode_array16(int fmt, const float* y, int64_t n, uint16_t* codes);
 void oracle_decode_array16(int fmt, const uint16_t* codes, int64_t n, float* out);
+/* e^x rounded to the nearest fp32 value (the exponential of SiLU). */
+void oracle_exp_array(const float* x, int64_t n, float* out);
 float oracle_format_max(int fmt);
 float oracle_default_floor(int fmt);
 
