@@ -77,7 +77,7 @@ template <int kLanes, bool kWeighted, int kFmt, bool kClamp, int kCount, int kBl
           int kUnroll>
 __global__ __launch_bounds__(kBlock) void swiglu_kernel(
     const uint16_t* __restrict__ h, const float* __restrict__ w, int64_t nchunks,
-    uint32_t chunks_per_row, uint64_t row_magic, int64_t cols, float floor,
+    uint32_t chunks_per_row, uint64_t row_magic, float floor,
     uint8_t* __restrict__ q, void* __restrict__ sf, SfLayout lay, uint32_t group0,
     float clamp, unsigned long long* __restrict__ count, unsigned long long* __restrict__ slots) {
   uint32_t nclamp = 0;
@@ -175,7 +175,7 @@ hipError_t launch(const uint16_t* h, const float* w, int64_t rows, int64_t cols,
       launch_kernel((swiglu_kernel<kLanes, kWeighted, kFmt, kClamp, kCountNone, kThreads,
                                    kStreamUnroll>),
                     dim3((unsigned)blocks), dim3(kThreads), 0, stream, args.h, args.w, nchunks,
-                    (uint32_t)cpr, magic, cols, floor, args.q, sf, lay, args.group0, ca.c,
+                    (uint32_t)cpr, magic, floor, args.q, sf, lay, args.group0, ca.c,
                     ca.count, ca.slots);
     };
     if constexpr (kClamp) {
@@ -183,13 +183,13 @@ hipError_t launch(const uint16_t* h, const float* w, int64_t rows, int64_t cols,
         launch_kernel((swiglu_kernel<kLanes, kWeighted, kFmt, true, kCountSlotted, kThreads,
                                      kSlotUnroll>),
                       dim3((unsigned)blocks), dim3(kThreads), 0, stream, args.h, args.w, nchunks,
-                      (uint32_t)cpr, magic, cols, floor, args.q, sf, lay, args.group0, ca.c,
+                      (uint32_t)cpr, magic, floor, args.q, sf, lay, args.group0, ca.c,
                       ca.count, ca.slots);
       else if (counting)
         launch_kernel((swiglu_kernel<kLanes, kWeighted, kFmt, true, kCountDirect, kCountBlock,
                                      kCountUnroll>),
                       dim3((unsigned)blocks), dim3(kCountBlock), 0, stream, args.h, args.w,
-                      nchunks, (uint32_t)cpr, magic, cols, floor, args.q, sf, lay, args.group0,
+                      nchunks, (uint32_t)cpr, magic, floor, args.q, sf, lay, args.group0,
                       ca.c, ca.count, ca.slots);
       else
         plain();
