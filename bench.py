@@ -468,6 +468,7 @@ def main():
         sys.exit(2)
 
     import torch
+    from precision_quantization_amd import workloads as W
     dev = torch.device("cuda:0")
     log("bench: generating workloads")
     wls = make_workloads()
@@ -501,7 +502,10 @@ def main():
             "GBps": round(b / (avg * 1e-3) / 1e9, 1),
             "frac": round(b / (avg * 1e-3) / 1e9 / PEAK_HBM_GBS, 4),
             "rows_per_s": round(wl.rows / (avg * 1e-3)),
+            "input_sha256": W.sha256(wl.x),
         }
+        if getattr(wl, "w", None) is not None:
+            kernels[name]["weight_sha256"] = W.sha256(wl.w)
     dominant = max(kernels, key=lambda k: kernels[k]["avg_us"])
     d = kernels[dominant]
     traffic = load_traffic(dominant)
