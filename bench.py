@@ -139,6 +139,18 @@ def spread_us(ms):
     return {"median_us": at(0.5), "p10_us": at(0.1), "p90_us": at(0.9)}
 
 
+def cpu_model():
+    """The host CPU's model name (from /proc/cpuinfo), else the machine type."""
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return platform.processor() or platform.machine()
+
+
 def make_workloads():
     from precision_quantization_amd import workloads as W
     return [
@@ -568,7 +580,7 @@ def main():
         result["cpu_baseline"] = {
             "value": round(gbs, 4), "unit": "GB/s", "cores": 1, "kind": "oracle",
             "sample": f"all rows of each of the five workloads, one oracle call each "
-                      f"({secs:.1f} s on {platform.processor() or platform.machine()}, "
+                      f"({secs:.1f} s on {cpu_model()}, "
                       f"{os.cpu_count()} cores present)",
         }
         log("bench: CPU baseline over all cores (oracle)")
