@@ -50,6 +50,9 @@
  *  - Calls on one stream are ordered; concurrent calls on different streams
  *    are independent (the library holds no mutable device state; a count
  *    workspace is the caller's, and concurrent calls need different ones).
+ *  - Entry points may be called from several host threads at once: the
+ *    library's host-side state (cached CU counts, the CU override, the
+ *    measurement events of qcast_bench_time_next) is atomic or per thread.
  */
 #ifndef QCAST_H
 #define QCAST_H
