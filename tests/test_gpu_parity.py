@@ -566,12 +566,15 @@ def test_per_token_sf_layouts(dev, flags, fmt, group, rows, cols):
     assert np.array_equal(sf, sf_ref.view(np.uint32))      # padding still poisoned
 
 
-def test_per_token_sf_full_size_packed(dev):
+@pytest.mark.parametrize("group,flags", [
+    (128, pq.SF_PACKED_UE8M0 | pq.SF_COL_MAJOR), (32, pq.SF_PACKED_UE8M0 | pq.SF_COL_MAJOR),
+    (32, pq.SF_COL_MAJOR), (128, pq.SF_COL_MAJOR), (128, pq.SF_ROUND_POW2)])
+def test_per_token_sf_full_size_layouts(dev, group, flags):
+    """Every scale word of the 4096 x 7168 workload in each layout (no padding rows)."""
     wl = workloads.per_token_hidden()
-    flags = pq.SF_PACKED_UE8M0 | pq.SF_COL_MAJOR
-    q_ref, sf_ref = oracle.per_token_sf(workloads.bf16_bits(wl.x), "e4m3", 128, sf_flags=flags)
-    q, sf = gpu_sf_cast(wl.x, dev, "e4m3", 128, flags, poison=0)
-    assert np.array_equal(q, q_ref) and np.array_equal(sf, sf_ref)
+    q_ref, sf_ref = oracle.per_token_sf(workloads.bf16_bits(wl.x), "e4m3", group, sf_flags=flags)
+    q, sf = gpu_sf_cast(wl.x, dev, "e4m3", group, flags, poison=0)
+    assert np.array_equal(q, q_ref) and np.array_equal(sf, sf_ref.view(np.uint32))
 
 
 @pytest.mark.parametrize("flags", [pq.SF_ROUND_POW2 | pq.SF_COL_MAJOR,
