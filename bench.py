@@ -12,14 +12,20 @@ Inputs are resident in HBM before timing starts; the step touches about
 inputs that the rest of the step has evicted.
 
 value = algorithmic bytes of the whole step (inputs read once, codes and
-scales written once) / time per step, in GB/s. Per-kernel durations come from
-HIP events that kernels of the timed steps record from their own dispatch on
-the launch stream (qcast_bench_time_next): step s times kernel s mod 5, so
-with the default 200 steps every kernel is timed on 40 of its launches (their
-average, median, 10th and 90th percentile). The roofline object is for the
-kernel with the largest share of the step. Each step kernel also carries
-copy_GBps, the library's streaming copy moving the same byte count after a
-1 GiB flush, and of_copy, its own rate over that ceiling; per_channel_T also
+scales written once) / time per step, in GB/s, over the K timed steps, which
+carry no timing events. Per-kernel durations come from further steps, after
+those and outside `value`, in which one kernel records HIP events from its own
+dispatch on the launch stream (qcast_bench_time_next): step s times kernel
+s mod 5, over max(K, 150) steps, so every kernel is timed on at least 30 of
+its launches whatever K is (their average, median, 10th and 90th
+percentile). The roofline object is for the kernel with the largest share of
+the step. Each step kernel also carries copy_GBps, the library's streaming
+copy moving the same byte count after a 1 GiB flush, and of_copy, its own
+rate over that ceiling; runtime_copy_GBps is the HIP runtime's own
+device-to-device hipMemcpyAsync of the same bytes and library_copy_marker_GBps
+the library copy, both timed by events recorded around the call (the same
+method for both, so the runtime copy is a ceiling independent of this
+library); per_channel_T also
 carries pattern_us, its own loads and transposed stores without the
 arithmetic (qcast_bench_per_channel_T_traffic), flushed_us, the cast timed
 the same way (alternating with it, each after the flush), and of_pattern,
@@ -51,6 +57,7 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
 PEAK_HBM_GBS = 8000.0
+MIN_TIMED_LAUNCHES = 30
 METRIC = "achieved HBM GB/s (bytes in+out) and % of MI355X peak, per cast kernel"
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic.json")
 
@@ -301,11 +308,19 @@ def time_extras(extras, dev, steps, warmup):
     return out
 
 
-def copy_ceilings(dev, sizes):
-    """Bandwidth of the library's streaming copy (include/qcast_bench.h)
-    moving each byte count in `sizes` in total (half read, half written)
-    after a 1 GiB flush, median of 5 timed runs: the empirical ceiling for a
-    streaming kernel of that size. Returns {nbytes: GB/s}."""
+def copy_ceilings(dev, sizes, runs=11):
+    """Copies moving each byte count in `sizes` in total (half read, half
+    written), each after a 1 GiB flush, median of `runs` - 1 timed runs
+    (the first is dropped). Returns {nbytes: {...}} in GB/s:
+      "library": the library's streaming copy (include/qcast_bench.h), timed
+                 by events its own dispatch records, like the casts;
+      "library_marker", "runtime_marker": the library copy and the HIP
+                 runtime's device-to-device hipMemcpyAsync (torch's copy_
+                 between two same-device tensors), both timed by events
+                 recorded on the stream around the call, so that the two
+                 copies are compared with the same timing method: the
+                 runtime's copy is a ceiling that owes nothing to this
+                 library."""
     import torch
     import precision_quantization_amd as pq
     flush = torch.empty(1 << 30, dtype=torch.uint8, device=dev)
@@ -315,18 +330,30 @@ def copy_ceilings(dev, sizes):
         half = nbytes // 2 // 16 * 16
         src = torch.empty(half, dtype=torch.uint8, device=dev).fill_(1)
         dst = torch.empty(half, dtype=torch.uint8, device=dev)
-        times = []
-        for _ in range(6):
+        times = {"library": [], "library_marker": [], "runtime_marker": []}
+        for _ in range(runs):
             flush.fill_(0)
             a, b = hev.create(), hev.create()
             pq.qcast_bench_time_next(a, b)
             pq.qcast_bench_copy(src, dst)
             torch.cuda.synchronize()
-            times.append(hev.elapsed_ms(a, b))
+            times["library"].append(hev.elapsed_ms(a, b))
             hev.destroy(a)
             hev.destroy(b)
-        ms = sorted(times[1:])[len(times[1:]) // 2]
-        out[nbytes] = 2 * half / (ms * 1e-3) / 1e9
+            for name, fn in (("library_marker", lambda: pq.qcast_bench_copy(src, dst)),
+                             ("runtime_marker", lambda: dst.copy_(src))):
+                flush.fill_(0)
+                e0 = torch.cuda.Event(enable_timing=True)
+                e1 = torch.cuda.Event(enable_timing=True)
+                e0.record()
+                fn()
+                e1.record()
+                torch.cuda.synchronize()
+                times[name].append(e0.elapsed_time(e1))
+        out[nbytes] = {}
+        for name, t in times.items():
+            ms = sorted(t[1:])[len(t[1:]) // 2]
+            out[nbytes][name] = 2 * half / (ms * 1e-3) / 1e9
         del src, dst
     return out
 
@@ -493,16 +520,25 @@ def main():
             fn()
     torch.cuda.synchronize()
 
-    hev = HipEvents()
     fns = [fn for _, _, fn in calls]
-    ev = make_events(hev, len(fns), args.steps)
     log(f"bench: timing {args.steps} steps")
     torch.cuda.synchronize()
     t0 = time.perf_counter()
-    timed_runs(fns, ev)
+    for _ in range(args.steps):
+        for fn in fns:
+            fn()
     torch.cuda.synchronize()
     elapsed = time.perf_counter() - t0
     ms_per_step = elapsed * 1e3 / args.steps
+
+    # per-kernel durations: after the headline loop and outside `value`,
+    # steps in which kernel s mod n records events from its own dispatch,
+    # enough of them for every kernel to be timed MIN_TIMED_LAUNCHES times
+    hev = HipEvents()
+    rot_steps = max(args.steps, MIN_TIMED_LAUNCHES * len(fns))
+    log(f"bench: per-kernel timing over {rot_steps} steps")
+    ev = make_events(hev, len(fns), rot_steps)
+    timed_runs(fns, ev)
 
     kernels = {}
     for (name, wl, _), ms in zip(calls, collect(ev, hev)):
@@ -524,11 +560,15 @@ def main():
     # the largest size last, so the copy the counter runs calibrate on is the
     # last copy of the run
     copy_nbytes = max(k["bytes"] for k in kernels.values())
+    log("bench: copy ceilings (library copy and the runtime's hipMemcpyAsync)")
     ceilings = copy_ceilings(dev, [k["bytes"] for k in kernels.values()])
-    copy_gbs = ceilings[copy_nbytes]
+    copy_gbs = ceilings[copy_nbytes]["library"]
     for k in kernels.values():
-        k["copy_GBps"] = round(ceilings[k["bytes"]], 1)
-        k["of_copy"] = round(k["GBps"] / ceilings[k["bytes"]], 4)
+        c = ceilings[k["bytes"]]
+        k["copy_GBps"] = round(c["library"], 1)
+        k["of_copy"] = round(k["GBps"] / c["library"], 4)
+        k["runtime_copy_GBps"] = round(c["runtime_marker"], 1)
+        k["library_copy_marker_GBps"] = round(c["library_marker"], 1)
     for (name, wl, _), ms in zip(calls, flushed_runs([fn for _, _, fn in calls], dev)):
         k = kernels[name]
         sp = spread_us(ms)
@@ -569,6 +609,8 @@ def main():
         "kernels": kernels,
         "copy_ceiling_GBps": round(copy_gbs, 1),
         "copy_bytes": copy_nbytes // 2 // 16 * 16 * 2,
+        "runtime_copy_ceiling_GBps": round(ceilings[copy_nbytes]["runtime_marker"], 1),
+        "library_copy_marker_GBps": round(ceilings[copy_nbytes]["library_marker"], 1),
     }
     if not args.no_extras:
         log("bench: timing the other casts")

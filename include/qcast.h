@@ -26,8 +26,9 @@
  * fmt_max is 448 for E4M3, 57344 for E5M2 and 6 for E2M1. The default floor
  * ([WALK] §3.1) is 1e-4f for E4M3 and 6 * 2^-126 for E2M1; the page names no
  * floor for E5M2, which takes the E4M3 one, 1e-4f. A clamp_min > 0 replaces
- * the default. Formats: OCP E4M3 ("fn") and E5M2, OCP MX E2M1; E5M2 is in
- * the format list of [SPLIT] §四 A.
+ * the default; clamp_min <= 0 (-inf included) keeps it; a NaN or +inf
+ * clamp_min is rejected with QCAST_ERR_VALUE. Formats: OCP E4M3 ("fn") and
+ * E5M2, OCP MX E2M1; E5M2 is in the format list of [SPLIT] §四 A.
  *
  * Conventions shared by every entry point:
  *  - Every data pointer is a DEVICE pointer on the current HIP device, owned
@@ -82,7 +83,8 @@ typedef enum {
   QCAST_ERR_GROUP = 5,  /* group / block size not supported */
   QCAST_ERR_LAUNCH = 6, /* the kernel launch failed */
   QCAST_ERR_DEVICE = 7, /* no usable HIP device */
-  QCAST_ERR_VALUE = 8   /* a scalar argument is out of range (e.g. a NaN clamp) */
+  QCAST_ERR_VALUE = 8   /* a scalar argument is out of range (a NaN SwiGLU clamp, a NaN or
+                           +inf clamp_min) */
 } qcast_status;
 
 /*
@@ -139,7 +141,8 @@ typedef enum { QCAST_OUT_BF16 = 1, QCAST_OUT_F32 = 2 } qcast_out_dtype;
  *         nibble.  E5M6: [rows, cols/2*3] bytes (see QCAST_FMT_E5M6).
  *   sf    [rows, cols/group] fp32.
  *   group 32, 64 or 128; cols % group == 0.
- *   clamp_min  <= 0 selects the format's default floor.
+ *   clamp_min  <= 0 selects the format's default floor; NaN or +inf returns
+ *              QCAST_ERR_VALUE.
  */
 QCAST_API int qcast_per_token(const void* x, int64_t rows, int64_t cols, int fmt, int group,
                     float clamp_min, void* q, float* sf, void* stream);
@@ -311,6 +314,11 @@ QCAST_API int qcast_abi_version(void);
  * Override the compute-unit count used to size the persistent grids
  * (the pages' config.py get_num_sms() override, [WALK] §1.2). 0 restores the
  * device's own count. Affects later launches only; results never depend on it.
+ * The only grids sized by it are the capped ones of the counting SwiGLU casts
+ * run without a count workspace (qcast_swiglu_per_token_ex and
+ * qcast_swiglu_per_channel_T with clamp_count given, swiglu_clamp > 0 and
+ * count_ws NULL); every other launch takes one workgroup per unit of work and
+ * ignores it.
  */
 QCAST_API void qcast_set_num_cus(int n);
 

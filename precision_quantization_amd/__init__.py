@@ -43,6 +43,18 @@ def _bf16_input(x, name):
     return x
 
 
+def _gate_up(h, name="h"):
+    """A SwiGLU input ``[rows, 2*cols]`` (gate | up): (h, rows, cols). The
+    width must be even, or the C ABI would walk h with a row stride one
+    element short."""
+    if isinstance(h, torch.Tensor) and h.dim() == 2 and h.shape[1] % 2:
+        raise QcastError(2, f"{name} must have an even number of columns (gate | up), "
+                            f"got {h.shape[1]}")
+    h = _bf16_input(h, name)
+    rows, two_n = h.shape
+    return h, rows, two_n // 2
+
+
 def _out(t, shape, dtype, device, name):
     if t is None:
         return torch.empty(shape, dtype=dtype, device=device)
@@ -88,8 +100,14 @@ def _count_ws(count_workspace, clamp_count, device, stream_handle):
     zero between calls): the caller's tensor; none when ``count_workspace``
     is False, when nothing is counted, or (for the default None) under graph
     capture, since a graph may be replayed on any stream; else, for None,
-    one zeroed int64 tensor kept per device and stream (each call leaves it
-    zeroed, and calls on one stream are ordered)."""
+    one int64 tensor kept per device and stream (each call leaves it
+    zeroed, and calls on one stream are ordered).
+
+    The first counting call on a (device, stream) allocates that tensor
+    (8 KB) and zeroes it with a fill kernel enqueued on the same stream,
+    ahead of the cast: nothing waits on the host. Callers that must not
+    allocate inside the call pass their own ``count_workspace``, or
+    ``False`` (the capped grid, no workspace)."""
     if clamp_count is None or count_workspace is False:
         return None
     if count_workspace is None:
@@ -98,8 +116,12 @@ def _count_ws(count_workspace, clamp_count, device, stream_handle):
         key = (device, stream_handle)
         ws = _count_ws_cache.get(key)
         if ws is None:
-            ws = torch.zeros(COUNT_WS_BYTES // 8, dtype=torch.int64, device=device)
-            torch.cuda.synchronize(device)   # zeroed before any stream uses it
+            # allocated for, and zeroed on, the stream the cast runs on
+            if torch.cuda.current_stream(device).cuda_stream == stream_handle:
+                ws = torch.zeros(COUNT_WS_BYTES // 8, dtype=torch.int64, device=device)
+            else:
+                with torch.cuda.stream(torch.cuda.ExternalStream(stream_handle, device=device)):
+                    ws = torch.zeros(COUNT_WS_BYTES // 8, dtype=torch.int64, device=device)
             _count_ws_cache[key] = ws
         return ws.data_ptr()
     if not isinstance(count_workspace, torch.Tensor) or count_workspace.device != device or \
@@ -174,9 +196,7 @@ def qcast_swiglu_per_token_sf(h, row_weight=None, fmt="e4m3", group=128, clamp_m
                               sf_flags=0, out=None, out_sf=None, stream=None):
     """qcast_swiglu_per_token with a scale-factor layout."""
     f = fmt_id(fmt)
-    h = _bf16_input(h, "h")
-    rows, two_n = h.shape
-    cols = two_n // 2
+    h, rows, cols = _gate_up(h)
     wptr = None
     if row_weight is not None:
         if row_weight.dtype != torch.float32 or tuple(row_weight.shape) != (rows,) or \
@@ -202,9 +222,7 @@ def qcast_swiglu_per_token_ex(h, row_weight=None, fmt="e4m3", group=128, clamp_m
     number of clamped values is added, or None. ``count_workspace``: see
     ``_count_ws`` (the default keeps one per device and stream)."""
     f = fmt_id(fmt)
-    h = _bf16_input(h, "h")
-    rows, two_n = h.shape
-    cols = two_n // 2
+    h, rows, cols = _gate_up(h)
     wptr = _row_weight(row_weight, rows, h.device)
     cptr = _counter(clamp_count, h.device)
     out = _out(out, (rows, cols), _code_dtype(f), h.device, "out")
@@ -226,10 +244,9 @@ def qcast_swiglu_backward_per_token(h, dv, row_weight=None, fmt="e4m3", group=12
     """SwiGLU backward fused with the per-token cast of ``[dgate | dup]``:
     ``out [rows, 2*cols]``, ``out_sf [rows, 2*cols/group]``."""
     f = fmt_id(fmt)
-    h = _bf16_input(h, "h")
+    h, rows, cols = _gate_up(h)
+    two_n = 2 * cols
     dv = _bf16_input(dv, "dv")
-    rows, two_n = h.shape
-    cols = two_n // 2
     if tuple(dv.shape) != (rows, cols) or dv.device != h.device:
         raise QcastError(2, f"dv must be [{rows}, {cols}] on h's device")
     wptr = _row_weight(row_weight, rows, h.device)
@@ -252,9 +269,7 @@ def qcast_swiglu_per_channel_T(h, row_weight=None, fmt="e4m3", group=128, clamp_
     ``out [cols, rows]``, ``out_sf [cols, rows/group]``; ``clamp_count`` and
     ``count_workspace`` as in qcast_swiglu_per_token_ex."""
     f = fmt_id(fmt)
-    h = _bf16_input(h, "h")
-    rows, two_n = h.shape
-    cols = two_n // 2
+    h, rows, cols = _gate_up(h)
     wptr = _row_weight(row_weight, rows, h.device)
     cptr = _counter(clamp_count, h.device)
     out = _out(out, (cols, rows), _code_dtype(f), h.device, "out")
@@ -305,11 +320,7 @@ def qcast_swiglu_per_token(h, row_weight=None, fmt="e4m3", group=128, clamp_min=
     """SwiGLU of ``h [rows, 2N]`` (gate | up) times ``row_weight [rows]`` (fp32
     or None), cast per token: ``out [rows, N]``, ``out_sf [rows, N/group]``."""
     f = fmt_id(fmt)
-    h = _bf16_input(h, "h")
-    rows, two_n = h.shape
-    if two_n % 2:
-        raise QcastError(2, "h must have an even number of columns (gate | up)")
-    cols = two_n // 2
+    h, rows, cols = _gate_up(h)
     wptr = None
     if row_weight is not None:
         if row_weight.dtype != torch.float32 or tuple(row_weight.shape) != (rows,) or \
@@ -365,6 +376,9 @@ def qcast_cast_back(q, sf, fmt="e4m3", group=128, out_dtype=torch.bfloat16, out=
     """Dequantize per-token codes ``q`` with scales ``sf [rows, cols/group]``
     to ``out [rows, cols]`` (bf16 or fp32): decode(q) * sf."""
     f = fmt_id(fmt)
+    if isinstance(q, torch.Tensor) and q.dim() == 2 and f == FMT_E5M6 and q.shape[1] % 3:
+        raise QcastError(2, f"E5M6 codes take three bytes per pair of columns: q's width "
+                            f"{q.shape[1]} is not a multiple of 3")
     if not (isinstance(q, torch.Tensor) and q.is_cuda and q.dim() == 2 and q.is_contiguous()):
         raise QcastError(2, "q must be a contiguous 2-D CUDA tensor")
     if q.element_size() != 1:

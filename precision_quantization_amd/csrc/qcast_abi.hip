@@ -36,6 +36,11 @@ bool fp8_fmt(int fmt) { return fmt == QCAST_FMT_E4M3 || fmt == QCAST_FMT_E5M2; }
 
 float floor_for(int fmt, float clamp_min) { return clamp_min > 0.0f ? clamp_min : default_floor(fmt); }
 
+// A caller's floor must be a number below +inf: NaN would silently select the
+// default, and +inf would make every scale infinite (and, rounded to a power
+// of two, wrap its inverse's exponent).
+bool clamp_min_ok(float c) { return c == c && c <= 3.4028235e38f; }
+
 int caps_for_current_device(qcast::LaunchCaps* caps) {
   const int override_n = g_cu_override.load(std::memory_order_relaxed);
   if (override_n > 0) {
@@ -120,6 +125,7 @@ int qcast_per_token_sf(const void* x, int64_t rows, int64_t cols, int fmt, int g
   if (rows < 0 || cols < 0 || cols % group != 0 || too_big(rows, cols) ||
       !sf_shape_ok(rows, cols, group, sf_flags))
     return QCAST_ERR_SHAPE;
+  if (!clamp_min_ok(clamp_min)) return QCAST_ERR_VALUE;
   if (rows == 0 || cols == 0) return QCAST_OK;
   if (!x || !q || !sf) return QCAST_ERR_NULL;
   if (!aligned(x, 16) || !aligned(q, 16) || !aligned(sf, 4)) return QCAST_ERR_ALIGN;
@@ -152,6 +158,7 @@ int qcast_swiglu_per_token_ex(const void* h, int64_t rows, int64_t cols,
       too_big(rows, 2 * cols) || !sf_shape_ok(rows, cols, group, sf_flags))
     return QCAST_ERR_SHAPE;
   if (swiglu_clamp != swiglu_clamp) return QCAST_ERR_VALUE;
+  if (!clamp_min_ok(clamp_min)) return QCAST_ERR_VALUE;
   if (rows == 0 || cols == 0) return QCAST_OK;
   if (!h || !q || !sf) return QCAST_ERR_NULL;
   if (!aligned(h, 16) || !aligned(q, 16) || !aligned(sf, 4) ||
@@ -183,6 +190,7 @@ int qcast_swiglu_backward_per_token(const void* h, const void* dv, int64_t rows,
       too_big(rows, 2 * cols))
     return QCAST_ERR_SHAPE;
   if (swiglu_clamp != swiglu_clamp) return QCAST_ERR_VALUE;
+  if (!clamp_min_ok(clamp_min)) return QCAST_ERR_VALUE;
   if (rows == 0 || cols == 0) return QCAST_OK;
   if (!h || !dv || !q || !sf) return QCAST_ERR_NULL;
   if (!aligned(h, 16) || !aligned(dv, 16) || !aligned(q, 16) || !aligned(sf, 4) ||
@@ -206,6 +214,7 @@ int qcast_swiglu_per_channel_T(const void* h, int64_t rows, int64_t cols, const 
       !qcast::per_channel_t_fits(rows, cols, 2 * cols))
     return QCAST_ERR_SHAPE;
   if (swiglu_clamp != swiglu_clamp) return QCAST_ERR_VALUE;
+  if (!clamp_min_ok(clamp_min)) return QCAST_ERR_VALUE;
   if (rows == 0 || cols == 0) return QCAST_OK;
   if (!h || !qT || !sf) return QCAST_ERR_NULL;
   if (!aligned(h, 16) || !aligned(qT, 16) || !aligned(sf, 4) ||
@@ -236,6 +245,7 @@ int qcast_per_block(const void* x, int64_t rows, int64_t cols, int fmt, int bloc
   if (rows < 0 || cols < 0 || rows % block != 0 || cols % block != 0 || too_big(rows, cols) ||
       !qcast::per_block_fits(rows, cols))
     return QCAST_ERR_SHAPE;
+  if (!clamp_min_ok(clamp_min)) return QCAST_ERR_VALUE;
   if (rows == 0 || cols == 0) return QCAST_OK;
   if (!x || !q || !sf) return QCAST_ERR_NULL;
   if (!aligned(x, 16) || !aligned(q, 16) || !aligned(sf, 4)) return QCAST_ERR_ALIGN;
@@ -253,6 +263,7 @@ int qcast_per_channel_T(const void* x, int64_t rows, int64_t cols, int fmt, int 
   if (rows < 0 || cols < 0 || rows % group != 0 || cols % 8 != 0 || too_big(rows, cols) ||
       !qcast::per_channel_t_fits(rows, cols, cols))
     return QCAST_ERR_SHAPE;
+  if (!clamp_min_ok(clamp_min)) return QCAST_ERR_VALUE;
   if (rows == 0 || cols == 0) return QCAST_OK;
   if (!x || !qT || !sf) return QCAST_ERR_NULL;
   if (!aligned(x, 16) || !aligned(qT, 16) || !aligned(sf, 4)) return QCAST_ERR_ALIGN;
@@ -270,6 +281,7 @@ int qcast_per_channel(const void* x, int64_t rows, int64_t cols, int fmt, int gr
   if (rows < 0 || cols < 0 || rows % group != 0 || cols % 8 != 0 || too_big(rows, cols) ||
       !qcast::per_channel_fits(rows, cols))
     return QCAST_ERR_SHAPE;
+  if (!clamp_min_ok(clamp_min)) return QCAST_ERR_VALUE;
   if (rows == 0 || cols == 0) return QCAST_OK;
   if (!x || !q || !sf) return QCAST_ERR_NULL;
   if (!aligned(x, 16) || !aligned(q, 16) || !aligned(sf, 4)) return QCAST_ERR_ALIGN;

@@ -300,3 +300,52 @@ def test_per_channel_T_traffic_validation(lib):
     assert f(None, 256, 64, A16, None) == ERR_NULL
     assert f(A16, 256, 64, MIS, None) == ERR_ALIGN
     assert f(None, 0, 64, None, None) == OK
+
+
+def test_non_finite_clamp_min_is_refused_by_every_cast(lib):
+    nan, inf = float("nan"), float("inf")
+    for c in (nan, inf):
+        assert lib.qcast_per_token(A16, 4, 256, E4M3, 128, c, A16, A16, None) == ERR_VALUE
+        assert lib.qcast_per_token_sf(A16, 4, 512, E4M3, 128, c, 5, A16, A16, None) == ERR_VALUE
+        assert lib.qcast_e2m1(A16, 4, 256, 32, c, A16, A16, None) == ERR_VALUE
+        assert lib.qcast_swiglu_per_token(A16, 4, 256, None, E4M3, 128, c, A16, A16,
+                                          None) == ERR_VALUE
+        assert lib.qcast_swiglu_per_token_sf(A16, 4, 256, None, E4M3, 128, c, 1, A16, A16,
+                                             None) == ERR_VALUE
+        assert lib.qcast_swiglu_per_token_ex(A16, 4, 256, None, E4M3, 128, c, 0, 1.0, A16, A16,
+                                             None, None, None) == ERR_VALUE
+        assert lib.qcast_swiglu_backward_per_token(A16, A16, 4, 256, None, E4M3, 128, c, 0.0,
+                                                   A16, A16, None) == ERR_VALUE
+        assert lib.qcast_swiglu_per_channel_T(A16, 256, 64, None, E4M3, 128, c, 0.0, A16, A16,
+                                              None, None, None) == ERR_VALUE
+        assert lib.qcast_per_block(A16, 256, 256, E4M3, 128, c, A16, A16, None) == ERR_VALUE
+        assert lib.qcast_per_channel_T(A16, 256, 64, E4M3, 128, c, A16, A16, None) == ERR_VALUE
+        assert lib.qcast_per_channel(A16, 256, 64, E4M3, 128, c, A16, A16, None) == ERR_VALUE
+        # refused even for an empty input
+        assert lib.qcast_per_token(None, 0, 256, E4M3, 128, c, None, None, None) == ERR_VALUE
+    # zero and negative floors (-inf included) select the default: past this check, a null
+    # output is the first error
+    for c in (0.0, -1.0, -inf):
+        assert lib.qcast_per_token(A16, 4, 256, E4M3, 128, c, None, A16, None) == ERR_NULL
+    # the largest finite floor is accepted
+    assert lib.qcast_per_token(A16, 4, 256, E4M3, 128, 3.4028235e38, None, A16, None) == ERR_NULL
+
+
+def test_binding_rejects_an_odd_gate_up_width():
+    import torch
+    import precision_quantization_amd as pq
+    h = torch.zeros(4, 513, dtype=torch.bfloat16)
+    for fn in (pq.qcast_swiglu_per_token, pq.qcast_swiglu_per_token_sf,
+               pq.qcast_swiglu_per_token_ex, pq.qcast_swiglu_per_channel_T):
+        with pytest.raises(pq.QcastError, match="even number of columns"):
+            fn(h)
+    with pytest.raises(pq.QcastError, match="even number of columns"):
+        pq.qcast_swiglu_backward_per_token(h, torch.zeros(4, 256, dtype=torch.bfloat16))
+
+
+def test_binding_rejects_e5m6_codes_whose_width_is_not_a_multiple_of_3():
+    import torch
+    import precision_quantization_amd as pq
+    q = torch.zeros(4, 100, dtype=torch.uint8)
+    with pytest.raises(pq.QcastError, match="multiple of 3"):
+        pq.qcast_cast_back(q, torch.zeros(4, 2), "e5m6", 32)

@@ -15,6 +15,7 @@ import torch
 import oracle
 import precision_quantization_amd as pq
 from precision_quantization_amd import workloads
+from swiglu_bar import check_swiglu_bar
 
 pytestmark = pytest.mark.gpu
 
@@ -169,21 +170,6 @@ def test_cast_back_random(dev, fmt, group, bf16_out, rows, k, seed):
 # SwiGLU bar: scales within 1e-6 relative, at most 0.1% of codes (and at
 # least one) one step away, none further; clamp counts exact.
 
-def signed_code(c):
-    c = c.astype(np.int64)
-    return np.where(c & 0x80, -(c & 0x7F), c & 0x7F)
-
-
-def assert_swiglu_bar(q, sf, q_ref, sf_ref, what):
-    assert q.shape == q_ref.shape and sf.shape == sf_ref.shape, what
-    rel = np.abs(sf.astype(np.float64) - sf_ref) / sf_ref
-    assert rel.max() <= 1e-6, f"{what}: scale relative error {rel.max():.3g}"
-    diff = q != q_ref
-    assert diff.mean() <= 1e-3 + 1.0 / q.size, f"{what}: {diff.mean():.3%} of codes differ"
-    step = np.abs(signed_code(q[diff]) - signed_code(q_ref[diff]))
-    assert step.max(initial=0) <= 1, f"{what}: codes {step.max()} steps apart"
-
-
 def swiglu_random_input(rng, rows, cols):
     """h [rows, 2*cols] bf16 ~ N(0, 2) with planted rows (a zero gate, a
     +-100 gate, a zero up half) and w [rows] ~ U(0, 1) with one zero."""
@@ -231,18 +217,22 @@ def test_swiglu_random(dev, kind, fmt, group, clamp, weighted, rows, cols, seed)
         q_ref, sf_ref, n_ref = oracle.swiglu_per_token_ex(hb, wn, fmt, group, swiglu_clamp=clamp)
         q, sf = pq.qcast_swiglu_per_token_ex(h.to(dev), wd, fmt, group, swiglu_clamp=clamp,
                                              clamp_count=count)
+        v = oracle.swiglu_values_ex(hb, wn, swiglu_clamp=clamp)[0]
     elif kind == "backward":
         dv = torch.from_numpy(rng.standard_normal((rows, cols)).astype(np.float32)).to(torch.bfloat16)
         q_ref, sf_ref = oracle.swiglu_backward_per_token(hb, workloads.bf16_bits(dv), wn, fmt,
                                                          group, swiglu_clamp=clamp)
         q, sf = pq.qcast_swiglu_backward_per_token(h.to(dev), dv.to(dev), wd, fmt, group,
                                                    swiglu_clamp=clamp)
+        v = oracle.swiglu_backward_values(hb, workloads.bf16_bits(dv), wn, swiglu_clamp=clamp)
         n_ref = 0
     else:
         q_ref, sf_ref = oracle.swiglu_per_channel_T(hb, wn, fmt, 128, swiglu_clamp=clamp)
-        n_ref = oracle.swiglu_values_ex(hb, wn, swiglu_clamp=clamp)[1]
+        v, n_ref = oracle.swiglu_values_ex(hb, wn, swiglu_clamp=clamp)
+        v = v.T                    # groups run along tokens
         q, sf = pq.qcast_swiglu_per_channel_T(h.to(dev), wd, fmt, 128, swiglu_clamp=clamp,
                                               clamp_count=count)
     torch.cuda.synchronize()
-    assert_swiglu_bar(q.view(torch.uint8).cpu().numpy(), sf.cpu().numpy(), q_ref, sf_ref, what)
+    check_swiglu_bar(q.view(torch.uint8).cpu().numpy(), sf.cpu().numpy(), q_ref, sf_ref, v, fmt,
+                     group, what=what)
     assert int(count.item()) == n_ref, what
