@@ -374,7 +374,7 @@ def swiglu_backward_per_token(h, dv, w=None, fmt="e4m3", group=128, clamp_min=0.
     rows, two_n = h.shape
     cols = two_n // 2
     w = None if w is None else _f32(w)
-    q = np.zeros((rows, two_n), np.uint8)
+    q = np.zeros(_code_shape(f, rows, two_n), np.uint8)
     sf = np.zeros((rows, two_n // group if group > 0 else 0), np.float32)
     _check(_load().oracle_swiglu_backward_per_token(_ptr(h), _ptr(dv), rows, cols, _ptr(w), f,
                                                     group, clamp_min, swiglu_clamp, _ptr(q),

@@ -813,7 +813,10 @@ int oracle_swiglu_backward_per_token(const uint16_t* h, const uint16_t* dv, int6
   if (rc != ORACLE_OK) return rc;
   if (!dv) return ORACLE_ERR_NULL;
   if (rows < 0 || cols < 0 || cols % group != 0) return ORACLE_ERR_SHAPE;
-  if (fmt != ORACLE_FMT_E4M3 && fmt != ORACLE_FMT_E5M2) return ORACLE_ERR_FORMAT;
+  /* Every format of the forward cast: [SPLIT] §四 A pairs the SwiGLU cast
+   * (E4M3 / E5M2 / E2M1 / E5M6) with a matching backward. The row [dg | du]
+   * is one row of 2 * cols codes. */
+  if (pairs(fmt) && group % 2 != 0) return ORACLE_ERR_GROUP;
   std::vector<float> vals(static_cast<size_t>(rows * 2 * cols));
   oracle_swiglu_backward_values(h, dv, rows, cols, w, swiglu_clamp, vals.data());
   per_token_rows(vals.data(), rows, 2 * cols, fmt, group, floor_for(*table_for(fmt), clamp_min),

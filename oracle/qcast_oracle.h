@@ -144,8 +144,9 @@ int oracle_swiglu_per_token_ex(const uint16_t* h, int64_t rows, int64_t cols, co
 int oracle_swiglu_backward_values(const uint16_t* h, const uint16_t* dv, int64_t rows,
                                   int64_t cols, const float* w, float swiglu_clamp, float* out);
 
-/* SwiGLU backward + per-token cast of [dg | du]: q [rows, 2*cols] (E4M3 /
- * E5M2 bytes), sf [rows, 2*cols/group]. */
+/* SwiGLU backward + per-token cast of [dg | du]: q holds one code row of
+ * 2*cols columns per row (any format, stored as the per-token cast stores
+ * it), sf [rows, 2*cols/group]. */
 int oracle_swiglu_backward_per_token(const uint16_t* h, const uint16_t* dv, int64_t rows,
                                      int64_t cols, const float* w, int fmt, int group,
                                      float clamp_min, float swiglu_clamp, uint8_t* q, float* sf);

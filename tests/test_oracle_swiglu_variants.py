@@ -170,10 +170,14 @@ def test_backward_cast_is_per_token_of_backward_values(fmt, group):
     assert q.shape == (24, 1024) and sf.shape == (24, 1024 // group)
 
 
-def test_backward_rejects_e2m1():
-    h, dv, w = small_grad(rows=4, cols=128)
-    with pytest.raises(oracle.OracleError):
-        oracle.swiglu_backward_per_token(h, dv, w, fmt="e2m1", group=32)
+@pytest.mark.parametrize("fmt", ["e2m1", "e5m6"])
+def test_backward_cast_in_the_packed_formats_is_per_token_of_backward_values(fmt):
+    h, dv, w = small_grad(seed=42, rows=8, cols=256)
+    q, sf = oracle.swiglu_backward_per_token(h, dv, w, fmt=fmt, group=32, swiglu_clamp=4.0)
+    vals = oracle.swiglu_backward_values(h, dv, w, swiglu_clamp=4.0)
+    qv, sfv = oracle.per_token_f32(vals, fmt=fmt, group=32)
+    np.testing.assert_array_equal(q, qv)
+    np.testing.assert_array_equal(sf, sfv)
 
 
 # ------------------------------------------------- fused SwiGLU + transpose
