@@ -168,8 +168,10 @@ QCAST_API int qcast_e2m1(const void* x, int64_t rows, int64_t cols, int group, f
  *   row_weight [rows] fp32 routing weight, or NULL for none.
  *   v[r][j] = (g / (1 + exp(-g))) * u * row_weight[r], fp32, never rounded
  *   to bf16; then the per-token cast of v with `group`.
- *   q [rows, cols] bytes; sf [rows, cols/group] fp32.
- *   fmt QCAST_FMT_E4M3 or QCAST_FMT_E5M2. The exponential and the division
+ *   q    codes of [rows, cols] values stored as qcast_per_token stores them
+ *        for `fmt`; sf [rows, cols/group] fp32.
+ *   fmt  any of the four formats ([SPLIT] §四 A lists E4M3 / E5M2 / E2M1 /
+ *        E5M6 for this cast). The exponential and the division
  *   use the hardware's fast forms, so the codes may differ from an exact
  *   evaluation by one step where v lies next to a rounding midpoint.
  */
@@ -221,9 +223,11 @@ QCAST_API int qcast_swiglu_per_token_ex(const void* h, int64_t rows, int64_t col
  * and dg = 0 where g > c, du = 0 where |u| > c when swiglu_clamp c > 0.
  *   h   [rows, 2*cols] bf16 (gate | up); dv [rows, cols] bf16;
  *   row_weight [rows] fp32 or NULL.
- *   q   [rows, 2*cols] bytes: the codes of the row [dg | du].
+ *   q   the codes of the row [dg | du], one code row of 2*cols columns per
+ *       row, stored as qcast_per_token stores them for `fmt`.
  *   sf  [rows, 2*cols/group] fp32 (the dg groups, then the du groups).
- *   fmt QCAST_FMT_E4M3 or QCAST_FMT_E5M2; group 32, 64 or 128;
+ *   fmt any of the four formats ([SPLIT] §四 A pairs the SwiGLU cast's
+ *       formats with a matching backward); group 32, 64 or 128;
  *   cols % group == 0. The exponential and reciprocal are the hardware's fast
  *   forms (codes may differ by one step next to a rounding midpoint).
  */
@@ -238,10 +242,13 @@ QCAST_API int qcast_swiglu_backward_per_token(const void* h, const void* dv, int
  * qcast_per_channel_T).
  *   h   [rows, 2*cols] bf16 (gate | up), rows = tokens; row_weight as above.
  *   v   = SwiGLU values [rows, cols] (clamped as in qcast_swiglu_per_token_ex)
- *   qT  [cols, rows] bytes: qT[c][t] is the code of v[t][c].
+ *   qT  one code row of `rows` codes per channel c, holding the codes of
+ *       v[0..rows-1][c] stored as qcast_per_token stores a row for `fmt`
+ *       ([cols, rows] bytes for E4M3 / E5M2, [cols, rows/2] E2M1 with the
+ *       even token in the low nibble, [cols, rows/2*3] E5M6).
  *   sf  [cols, rows/group] fp32, groups of `group` tokens of one channel.
- *   group must be 128; rows % group == 0; cols % 8 == 0;
- *   fmt QCAST_FMT_E4M3 or QCAST_FMT_E5M2; clamp_count and count_ws as above.
+ *   group must be 128; rows % group == 0; cols % 8 == 0; any format;
+ *   clamp_count and count_ws as above.
  *   Limits: 256 * cols < 2^31, 64 * rows < 2^31.
  */
 QCAST_API int qcast_swiglu_per_channel_T(const void* h, int64_t rows, int64_t cols,
@@ -254,8 +261,10 @@ QCAST_API int qcast_swiglu_per_channel_T(const void* h, int64_t rows, int64_t co
  * "刚刚！DeepSeek开源高性能GPU算子库TileKernels", item 2, per-block granularity).
  * One scale per block x block tile.
  *   x  [rows, cols] bf16; rows % block == 0 and cols % block == 0.
- *   q  [rows, cols] bytes; sf [rows/block, cols/block] fp32.
- *   block must be 128; fmt QCAST_FMT_E4M3 or QCAST_FMT_E5M2.
+ *   q  codes stored as qcast_per_token stores them for `fmt` (any of the
+ *      four formats: the TileKernels overview of "DeepSeek 的 GPU 内核帝国"
+ *      lists FP8 / FP4 / E5M6 at per-block granularity);
+ *   sf [rows/block, cols/block] fp32. block must be 128.
  *   Limits: (rows/128) * (cols/128) < 2^31 and 128 * cols < 2^31.
  */
 QCAST_API int qcast_per_block(const void* x, int64_t rows, int64_t cols, int fmt, int block,
@@ -268,11 +277,14 @@ QCAST_API int qcast_per_block(const void* x, int64_t rows, int64_t cols, int fmt
  *   x   [rows, cols] bf16, rows = tokens, cols = channels.
  *   The scale groups run along tokens: group g of channel c is
  *   x[g*group .. g*group + group - 1][c].
- *   qT  [cols, rows] bytes: qT[c][t] is the code of x[t][c].
+ *   qT  one code row of `rows` codes per channel c, holding the codes of
+ *       x[0..rows-1][c] stored as qcast_per_token stores a row for `fmt`
+ *       ([cols, rows] bytes for E4M3 / E5M2: qT[c][t] is the code of x[t][c];
+ *       [cols, rows/2] E2M1, even token in the low nibble; [cols, rows/2*3]
+ *       E5M6).
  *   sf  [cols, rows/group] fp32.
- *   group must be 128; rows % group == 0; cols % 8 == 0;
- *   fmt QCAST_FMT_E4M3 or QCAST_FMT_E5M2.
- *   Limits: 128 * cols < 2^31, 64 * rows < 2^31.
+ *   group must be 128; rows % group == 0; cols % 8 == 0; any format.
+ *   Limits: 128 * cols < 2^31, 64 * rows < 2^31 (96 * rows for E5M6).
  */
 QCAST_API int qcast_per_channel_T(const void* x, int64_t rows, int64_t cols, int fmt, int group,
                         float clamp_min, void* qT, float* sf, void* stream);
@@ -281,11 +293,11 @@ QCAST_API int qcast_per_channel_T(const void* x, int64_t rows, int64_t cols, int
  * Per-channel cast in the input layout ([SPLIT] §二 per_channel_cast without
  * the transpose).
  *   x   [rows, cols] bf16, rows = tokens, cols = channels.
- *   q   [rows, cols] bytes: q[t][c] is the code of x[t][c].
+ *   q   codes of x in its own layout, stored as qcast_per_token stores them
+ *       for `fmt` (for E4M3 / E5M2 q[t][c] is the code of x[t][c]).
  *   sf  [rows/group, cols] fp32: sf[g][c] is the scale of tokens
  *       g*group .. g*group + group - 1 of channel c.
- *   group must be 128; rows % group == 0; cols % 8 == 0;
- *   fmt QCAST_FMT_E4M3 or QCAST_FMT_E5M2.
+ *   group must be 128; rows % group == 0; cols % 8 == 0; any format.
  *   Limits: 128 * cols < 2^31.
  */
 QCAST_API int qcast_per_channel(const void* x, int64_t rows, int64_t cols, int fmt, int group,

@@ -10,7 +10,9 @@ Outputs: E4M3 codes as ``torch.float8_e4m3fn`` and E5M2 codes as
 ``torch.float8_e5m2`` (one byte per code), E2M1 codes as ``torch.uint8`` with
 two codes per byte (low nibble = even column), E5M6 codes as ``torch.uint8``
 with two 12-bit codes per three bytes (a little-endian bit stream), scales as
-``torch.float32``.
+``torch.float32``. Every cast takes every format; codes are packed along the
+rows of its output (``code_shape``): columns for the per-token, SwiGLU,
+per-block and per-channel casts, tokens for the transposed per-channel ones.
 
 ``per_token_cast(x, fmt='e4m3', num_per_channels=128) -> (out, out_sf)``
 mirrors the call shown in the quick start of the page
@@ -203,7 +205,7 @@ def qcast_swiglu_per_token_sf(h, row_weight=None, fmt="e4m3", group=128, clamp_m
                 row_weight.device != h.device or not row_weight.is_contiguous():
             raise QcastError(2, "row_weight must be a contiguous float32 [rows] tensor on h's device")
         wptr = row_weight.data_ptr()
-    out = _out(out, (rows, cols), _code_dtype(f), h.device, "out")
+    out = _out(out, code_shape(f, rows, cols), _code_dtype(f), h.device, "out")
     shape, dt = sf_layout_shape(rows, cols, group if group > 0 else 1, sf_flags)
     out_sf = _out(out_sf, shape, dt, h.device, "out_sf")
     with torch.cuda.device(h.device):
@@ -225,7 +227,7 @@ def qcast_swiglu_per_token_ex(h, row_weight=None, fmt="e4m3", group=128, clamp_m
     h, rows, cols = _gate_up(h)
     wptr = _row_weight(row_weight, rows, h.device)
     cptr = _counter(clamp_count, h.device)
-    out = _out(out, (rows, cols), _code_dtype(f), h.device, "out")
+    out = _out(out, code_shape(f, rows, cols), _code_dtype(f), h.device, "out")
     shape, dt = sf_layout_shape(rows, cols, group if group > 0 else 1, sf_flags)
     out_sf = _out(out_sf, shape, dt, h.device, "out_sf")
     with torch.cuda.device(h.device):
@@ -250,7 +252,7 @@ def qcast_swiglu_backward_per_token(h, dv, row_weight=None, fmt="e4m3", group=12
     if tuple(dv.shape) != (rows, cols) or dv.device != h.device:
         raise QcastError(2, f"dv must be [{rows}, {cols}] on h's device")
     wptr = _row_weight(row_weight, rows, h.device)
-    out = _out(out, (rows, two_n), _code_dtype(f), h.device, "out")
+    out = _out(out, code_shape(f, rows, two_n), _code_dtype(f), h.device, "out")
     out_sf = _out(out_sf, (rows, two_n // group if group > 0 else 0), torch.float32, h.device,
                   "out_sf")
     with torch.cuda.device(h.device):
@@ -272,7 +274,7 @@ def qcast_swiglu_per_channel_T(h, row_weight=None, fmt="e4m3", group=128, clamp_
     h, rows, cols = _gate_up(h)
     wptr = _row_weight(row_weight, rows, h.device)
     cptr = _counter(clamp_count, h.device)
-    out = _out(out, (cols, rows), _code_dtype(f), h.device, "out")
+    out = _out(out, code_shape(f, cols, rows), _code_dtype(f), h.device, "out")
     out_sf = _out(out_sf, (cols, rows // group if group > 0 else 0), torch.float32, h.device,
                   "out_sf")
     with torch.cuda.device(h.device):
@@ -292,7 +294,7 @@ def qcast_per_channel(x, fmt="e4m3", group=128, clamp_min=0.0, out=None, out_sf=
     f = fmt_id(fmt)
     x = _bf16_input(x, "x")
     rows, cols = x.shape
-    out = _out(out, (rows, cols), _code_dtype(f), x.device, "out")
+    out = _out(out, code_shape(f, rows, cols), _code_dtype(f), x.device, "out")
     out_sf = _out(out_sf, (rows // group if group > 0 else 0, cols), torch.float32, x.device,
                   "out_sf")
     with torch.cuda.device(x.device):
@@ -327,7 +329,7 @@ def qcast_swiglu_per_token(h, row_weight=None, fmt="e4m3", group=128, clamp_min=
                 row_weight.device != h.device or not row_weight.is_contiguous():
             raise QcastError(2, "row_weight must be a contiguous float32 [rows] tensor on h's device")
         wptr = row_weight.data_ptr()
-    out = _out(out, (rows, cols), _code_dtype(f), h.device, "out")
+    out = _out(out, code_shape(f, rows, cols), _code_dtype(f), h.device, "out")
     out_sf = _out(out_sf, (rows, cols // group if group > 0 else 0), torch.float32, h.device,
                   "out_sf")
     with torch.cuda.device(h.device):
@@ -344,7 +346,7 @@ def qcast_per_block(x, fmt="e4m3", block=128, clamp_min=0.0, out=None, out_sf=No
     f = fmt_id(fmt)
     x = _bf16_input(x, "x")
     rows, cols = x.shape
-    out = _out(out, (rows, cols), _code_dtype(f), x.device, "out")
+    out = _out(out, code_shape(f, rows, cols), _code_dtype(f), x.device, "out")
     out_sf = _out(out_sf, (rows // block if block > 0 else 0, cols // block if block > 0 else 0),
                   torch.float32, x.device, "out_sf")
     with torch.cuda.device(x.device):
@@ -361,7 +363,7 @@ def qcast_per_channel_T(x, fmt="e4m3", group=128, clamp_min=0.0, out=None, out_s
     f = fmt_id(fmt)
     x = _bf16_input(x, "x")
     rows, cols = x.shape
-    out = _out(out, (cols, rows), _code_dtype(f), x.device, "out")
+    out = _out(out, code_shape(f, cols, rows), _code_dtype(f), x.device, "out")
     out_sf = _out(out_sf, (cols, rows // group if group > 0 else 0), torch.float32, x.device,
                   "out_sf")
     with torch.cuda.device(x.device):

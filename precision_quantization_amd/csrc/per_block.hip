@@ -1,4 +1,5 @@
-// per_block.hip -- per-block (128 x 128) cast of a bf16 weight to E4M3 or E5M2.
+// per_block.hip -- per-block (128 x 128) cast of a bf16 weight to E4M3, E5M2,
+// packed E2M1 or packed E5M6.
 //
 // Operation: per_block_cast of the operator table on the page
 // "TileKernels 与 DeepGEMM 的分界线：DeepSeek 开源内核栈的分工", §二 (one scale
@@ -16,7 +17,10 @@
 // packed 16-bit max of their magnitude bits (v_pk_max_u16), a DPP reduction
 // inside each 16-lane row (one tile's columns of one row), one cross-row
 // shuffle, and a 4-wave LDS exchange. Every lane then forms its tile's
-// scale, converts its 128 values and stores 16 dwordx2; the first lane of
+// scale, converts its 128 values and stores 16 chunks of 8 codes (dwordx2
+// for the 8-bit formats, a dword of E2M1 nibbles, 12 bytes of E5M6 codes; the
+// formats of the TileKernels overview of "DeepSeek 的 GPU 内核帝国", quant/:
+// FP8 / FP4 / E5M6 at per-block granularity); the first lane of
 // each tile stores the tile's scale. Tiles are independent, so the grid is
 // one workgroup per pair and the hardware balances them across the CUs.
 // Tile indices and in-tile offsets are 32-bit; only the tile base is 64-bit.
@@ -49,7 +53,7 @@ __global__ __launch_bounds__(kThreads) void per_block_kernel(
   // 64-bit tile base, 32-bit offsets inside the tiles (checked by the launcher)
   const uint64_t tile = (uint64_t)bi * kBlock * cols + (uint64_t)bj * kBlock;
   const uint16_t* src = x + tile;
-  uint8_t* dst = q + tile;
+  uint8_t* dst = q + code_bytes<kFmt>(tile);
   u32x4 raw[kPasses];
 #pragma unroll
   for (int p = 0; p < kPasses; ++p) {
@@ -80,11 +84,10 @@ __global__ __launch_bounds__(kThreads) void per_block_kernel(
   for (int p = 0; p < kPasses; ++p) {
     float v[8];
     unpack8(raw[p], v);
-    u32x2 out;
-    out.x = fp8x4<kFmt>(v[0] * s.inv, v[1] * s.inv, v[2] * s.inv, v[3] * s.inv);
-    out.y = fp8x4<kFmt>(v[4] * s.inv, v[5] * s.inv, v[6] * s.inv, v[7] * s.inv);
+#pragma unroll
+    for (int i = 0; i < 8; ++i) v[i] *= s.inv;
     const uint32_t off = (uint32_t)(r0 + p * kRowsPerPass) * cols + cc * 8;
-    store_stream(reinterpret_cast<u32x2*>(dst + off), out);
+    store_chunk8<kFmt>(dst, off / 8, v);
   }
   if (t < kChunksPerRow && (t & 15) == 0) sf[(uint64_t)bi * bcols + bj + ti] = s.sf;
 }
@@ -118,8 +121,12 @@ hipError_t launch_per_block(const void* x, int64_t rows, int64_t cols, int fmt, 
   if (!per_block_fits(rows, cols)) return hipErrorInvalidValue;
   const uint16_t* xp = static_cast<const uint16_t*>(x);
   uint8_t* qp = static_cast<uint8_t*>(q);
-  if (fmt == kE4M3) return launch_fmt<kE4M3>(xp, nblocks, cols, bcols, floor, qp, sf, stream);
-  if (fmt == kE5M2) return launch_fmt<kE5M2>(xp, nblocks, cols, bcols, floor, qp, sf, stream);
+  switch (fmt) {
+    case kE4M3: return launch_fmt<kE4M3>(xp, nblocks, cols, bcols, floor, qp, sf, stream);
+    case kE5M2: return launch_fmt<kE5M2>(xp, nblocks, cols, bcols, floor, qp, sf, stream);
+    case kE2M1: return launch_fmt<kE2M1>(xp, nblocks, cols, bcols, floor, qp, sf, stream);
+    case kE5M6: return launch_fmt<kE5M6>(xp, nblocks, cols, bcols, floor, qp, sf, stream);
+  }
   return hipErrorInvalidValue;
 }
 

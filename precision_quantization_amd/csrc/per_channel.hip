@@ -1,5 +1,5 @@
-// per_channel.hip -- per-channel cast of bf16 activations to E4M3 or E5M2,
-// codes kept in the input layout.
+// per_channel.hip -- per-channel cast of bf16 activations to E4M3, E5M2,
+// packed E2M1 or packed E5M6, codes kept in the input layout.
 //
 // Operation: per_channel_cast (without the transpose) of the operator table
 // on the page "TileKernels 与 DeepGEMM 的分界线：DeepSeek 开源内核栈的分工", §二:
@@ -19,7 +19,8 @@
 // inside the wave, then a 4-wave exchange in LDS; thread t forms the scale of
 // channel t and writes the workgroup's 256 scales as one contiguous line.
 // Each lane then converts its own values and writes 8 codes per token: each
-// store instruction of a wave covers two 256-byte row segments of q.
+// store instruction of a wave covers two 256-byte row segments of q (128-byte
+// segments of E2M1 nibbles, 384-byte segments of E5M6 codes).
 #include "qcast_device.h"
 #include "qcast_kernels.h"
 
@@ -91,16 +92,15 @@ __global__ __launch_bounds__(kThreads) void per_channel_kernel(
   float inv[8];
   *reinterpret_cast<float4*>(&inv[0]) = *reinterpret_cast<const float4*>(&inv_s[8 * ch]);
   *reinterpret_cast<float4*>(&inv[4]) = *reinterpret_cast<const float4*>(&inv_s[8 * ch + 4]);
-  uint8_t* qb = q + tile_base;
+  uint8_t* qb = q + code_bytes<kFmt>(tile_base);
 #pragma unroll
   for (int j = 0; j < kTokensPerLane; ++j) {
     float v[8];
     unpack8(raw[j], v);
-    u32x2 out;
-    out.x = fp8x4<kFmt>(v[0] * inv[0], v[1] * inv[1], v[2] * inv[2], v[3] * inv[3]);
-    out.y = fp8x4<kFmt>(v[4] * inv[4], v[5] * inv[5], v[6] * inv[6], v[7] * inv[7]);
+#pragma unroll
+    for (int i = 0; i < 8; ++i) v[i] *= inv[i];
     const uint32_t off = (uint32_t)(k + kSlices * j) * cols + 8 * ch;
-    store_stream(reinterpret_cast<u32x2*>(qb + off), out);
+    store_chunk8<kFmt>(qb, off / 8, v);
   }
 }
 
@@ -122,7 +122,9 @@ hipError_t launch_per_channel(const void* x, int64_t rows, int64_t cols, int fmt
   // Tile counts and in-tile offsets are 32-bit.
   if (!per_channel_fits(rows, cols)) return hipErrorInvalidValue;
   auto kernel = fmt == kE4M3 ? per_channel_kernel<kE4M3>
-               : fmt == kE5M2 ? per_channel_kernel<kE5M2> : nullptr;
+               : fmt == kE5M2 ? per_channel_kernel<kE5M2>
+               : fmt == kE2M1 ? per_channel_kernel<kE2M1>
+               : fmt == kE5M6 ? per_channel_kernel<kE5M6> : nullptr;
   if (!kernel) return hipErrorInvalidValue;
   launch_kernel(kernel, dim3((unsigned)ntiles), dim3(kThreads), 0, stream,
                 static_cast<const uint16_t*>(x), (uint32_t)cols, (uint32_t)nct, floor,

@@ -78,6 +78,11 @@ constexpr int kXcds = 8;
 #ifndef QCAST_PC_SW_STRIP
 #define QCAST_PC_SW_STRIP 1
 #endif
+// 1: the 8-bit formats also take the register-transpose kernel.
+#ifndef QCAST_PC_WAVE_FP8
+#define QCAST_PC_WAVE_FP8 0
+#endif
+constexpr bool kWaveFp8 = QCAST_PC_WAVE_FP8;
 constexpr uint32_t kStrip = QCAST_PC_STRIP;
 constexpr uint32_t kSwStrip = QCAST_PC_SW_STRIP;
 constexpr int kTG = QCAST_PC_TG;
@@ -525,6 +530,10 @@ hipError_t launch_per_channel_T(const void* x, int64_t rows, int64_t cols, int f
                                 void* qT, float* sf, hipStream_t stream,
                                 const LaunchCaps& caps) {
   (void)caps;
+  // E2M1 and E5M6 runs of tokens are not whole bytes per lane of this tile:
+  // the register-transpose kernel (per_channel_t_wave.hip) casts them.
+  if (fmt == kE2M1 || fmt == kE5M6 || kWaveFp8)
+    return launch_per_channel_T_wave(x, rows, cols, fmt, floor, qT, sf, stream);
   Grid g;
   // The kernels index tiles, and offsets inside a tile's rows, in 32 bits.
   if (!make_grid(rows, cols, cols, &g)) return hipErrorInvalidValue;
@@ -554,6 +563,9 @@ hipError_t launch_swiglu_per_channel_T(const void* h, int64_t rows, int64_t cols
                                        unsigned long long* clamp_count,
                                        unsigned long long* count_ws, void* qT, float* sf,
                                        hipStream_t stream, const LaunchCaps& caps) {
+  if (fmt == kE2M1 || fmt == kE5M6 || kWaveFp8)
+    return launch_swiglu_per_channel_T_wave(h, rows, cols, w, fmt, floor, swiglu_clamp,
+                                            clamp_count, count_ws, qT, sf, stream, caps);
   Grid g;
   if (!make_grid(rows, cols, 2 * cols, &g)) return hipErrorInvalidValue;
   if (g.ntiles == 0) return hipSuccess;

@@ -32,8 +32,6 @@ bool any_fmt(int fmt) {
          fmt == QCAST_FMT_E5M6;
 }
 
-bool fp8_fmt(int fmt) { return fmt == QCAST_FMT_E4M3 || fmt == QCAST_FMT_E5M2; }
-
 float floor_for(int fmt, float clamp_min) { return clamp_min > 0.0f ? clamp_min : default_floor(fmt); }
 
 // A caller's floor must be a number below +inf: NaN would silently select the
@@ -151,7 +149,7 @@ int qcast_swiglu_per_token_ex(const void* h, int64_t rows, int64_t cols,
                               const float* row_weight, int fmt, int group, float clamp_min,
                               int sf_flags, float swiglu_clamp, void* q, void* sf,
                               uint64_t* clamp_count, void* count_ws, void* stream) {
-  if (!fp8_fmt(fmt)) return QCAST_ERR_FORMAT;
+  if (!any_fmt(fmt)) return QCAST_ERR_FORMAT;
   if (!sf_flags_ok(sf_flags)) return QCAST_ERR_FORMAT;
   if (!per_token_group_ok(group)) return QCAST_ERR_GROUP;
   if (rows < 0 || cols < 0 || cols % group != 0 || cols / 8 >= (int64_t(1) << 16) ||
@@ -184,7 +182,7 @@ int qcast_swiglu_per_token_sf(const void* h, int64_t rows, int64_t cols,
 int qcast_swiglu_backward_per_token(const void* h, const void* dv, int64_t rows, int64_t cols,
                                     const float* row_weight, int fmt, int group, float clamp_min,
                                     float swiglu_clamp, void* q, float* sf, void* stream) {
-  if (!fp8_fmt(fmt)) return QCAST_ERR_FORMAT;
+  if (!any_fmt(fmt)) return QCAST_ERR_FORMAT;
   if (!per_token_group_ok(group)) return QCAST_ERR_GROUP;
   if (rows < 0 || cols < 0 || cols % group != 0 || cols / 8 >= (int64_t(1) << 16) ||
       too_big(rows, 2 * cols))
@@ -208,10 +206,11 @@ int qcast_swiglu_per_channel_T(const void* h, int64_t rows, int64_t cols, const 
                                int fmt, int group, float clamp_min, float swiglu_clamp, void* qT,
                                float* sf, uint64_t* clamp_count, void* count_ws,
                                void* stream) {
-  if (!fp8_fmt(fmt)) return QCAST_ERR_FORMAT;
+  if (!any_fmt(fmt)) return QCAST_ERR_FORMAT;
   if (group != 128) return QCAST_ERR_GROUP;
   if (rows < 0 || cols < 0 || rows % group != 0 || cols % 8 != 0 || too_big(rows, 2 * cols) ||
-      !qcast::per_channel_t_fits(rows, cols, 2 * cols))
+      !qcast::per_channel_t_fits(rows, cols, 2 * cols) ||
+      !qcast::per_channel_t_wave_fits(rows, cols, 2 * cols, fmt, true))
     return QCAST_ERR_SHAPE;
   if (swiglu_clamp != swiglu_clamp) return QCAST_ERR_VALUE;
   if (!clamp_min_ok(clamp_min)) return QCAST_ERR_VALUE;
@@ -240,7 +239,7 @@ int qcast_swiglu_per_token(const void* h, int64_t rows, int64_t cols, const floa
 
 int qcast_per_block(const void* x, int64_t rows, int64_t cols, int fmt, int block,
                     float clamp_min, void* q, float* sf, void* stream) {
-  if (!fp8_fmt(fmt)) return QCAST_ERR_FORMAT;
+  if (!any_fmt(fmt)) return QCAST_ERR_FORMAT;
   if (block != 128) return QCAST_ERR_GROUP;
   if (rows < 0 || cols < 0 || rows % block != 0 || cols % block != 0 || too_big(rows, cols) ||
       !qcast::per_block_fits(rows, cols))
@@ -258,10 +257,11 @@ int qcast_per_block(const void* x, int64_t rows, int64_t cols, int fmt, int bloc
 
 int qcast_per_channel_T(const void* x, int64_t rows, int64_t cols, int fmt, int group,
                         float clamp_min, void* qT, float* sf, void* stream) {
-  if (!fp8_fmt(fmt)) return QCAST_ERR_FORMAT;
+  if (!any_fmt(fmt)) return QCAST_ERR_FORMAT;
   if (group != 128) return QCAST_ERR_GROUP;
   if (rows < 0 || cols < 0 || rows % group != 0 || cols % 8 != 0 || too_big(rows, cols) ||
-      !qcast::per_channel_t_fits(rows, cols, cols))
+      !qcast::per_channel_t_fits(rows, cols, cols) ||
+      !qcast::per_channel_t_wave_fits(rows, cols, cols, fmt, false))
     return QCAST_ERR_SHAPE;
   if (!clamp_min_ok(clamp_min)) return QCAST_ERR_VALUE;
   if (rows == 0 || cols == 0) return QCAST_OK;
@@ -276,7 +276,7 @@ int qcast_per_channel_T(const void* x, int64_t rows, int64_t cols, int fmt, int 
 
 int qcast_per_channel(const void* x, int64_t rows, int64_t cols, int fmt, int group,
                       float clamp_min, void* q, float* sf, void* stream) {
-  if (!fp8_fmt(fmt)) return QCAST_ERR_FORMAT;
+  if (!any_fmt(fmt)) return QCAST_ERR_FORMAT;
   if (group != 128) return QCAST_ERR_GROUP;
   if (rows < 0 || cols < 0 || rows % group != 0 || cols % 8 != 0 || too_big(rows, cols) ||
       !qcast::per_channel_fits(rows, cols))

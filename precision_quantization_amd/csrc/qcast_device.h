@@ -380,4 +380,35 @@ __device__ __forceinline__ T load_stream(const T* p) { return __builtin_nontempo
 template <typename T>
 __device__ __forceinline__ void store_stream(T* p, T v) { __builtin_nontemporal_store(v, p); }
 
+// Bytes taken by the codes of n elements of a row whose length is even: one
+// byte each for the 8-bit formats, a nibble for E2M1, 12 bits for E5M6. A
+// code stream of such rows is one flat stream, so element offsets map to
+// byte offsets by the same rule.
+template <int kFmt, typename I>
+__host__ __device__ constexpr I code_bytes(I n) {
+  return kFmt == kE2M1 ? n / 2 : kFmt == kE5M6 ? n / 2 * 3 : n;
+}
+
+// Codes of the 8 consecutive elements of chunk c (elements 8c .. 8c+7) of a
+// code stream starting at q, stored non-temporally: 8 bytes of an 8-bit
+// format, 4 bytes of E2M1 nibbles (element 8c in the lowest), or 12 bytes of
+// E5M6 codes.
+template <int kFmt, typename I>
+__device__ __forceinline__ void store_chunk8(uint8_t* q, I c, const float y[8]) {
+  if constexpr (kFmt == kE2M1) {
+    store_stream(reinterpret_cast<uint32_t*>(q) + c, e2m1x8(y));
+  } else if constexpr (kFmt == kE5M6) {
+    const E5M6x8 p = e5m6x8(y);
+    uint32_t* o = reinterpret_cast<uint32_t*>(q) + 3 * c;
+    store_stream(o, p.w0);
+    store_stream(o + 1, p.w1);
+    store_stream(o + 2, p.w2);
+  } else {
+    u32x2 out;
+    out.x = fp8x4<kFmt>(y[0], y[1], y[2], y[3]);
+    out.y = fp8x4<kFmt>(y[4], y[5], y[6], y[7]);
+    store_stream(reinterpret_cast<u32x2*>(q) + c, out);
+  }
+}
+
 }  // namespace qcast

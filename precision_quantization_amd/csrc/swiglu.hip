@@ -1,4 +1,6 @@
-// swiglu.hip -- SwiGLU forward fused with the per-token E4M3 / E5M2 cast.
+// swiglu.hip -- SwiGLU forward fused with the per-token cast (E4M3, E5M2,
+// packed E2M1 or packed E5M6: the format list the page "TileKernels 与
+// DeepGEMM 的分界线：DeepSeek 开源内核栈的分工", §四 A, gives for this cast).
 //
 // Operation: swiglu_forward_and_per_token_cast of the walk-through page
 // "DeepSeek开源TileKernels：用Python写的GPU算子逼近硬件性能上限", §3.3: with the
@@ -118,11 +120,9 @@ __global__ __launch_bounds__(kBlock) void swiglu_kernel(
         const float amax = lane_group_max<kLanes>(absmax8(v));
         Scale s = group_scale<kFmt>(amax, floor);
         if (lay.flags & kSfRound) s = round_scale_pow2(s);
-        const float ys = s.inv;
-        u32x2 out;
-        out.x = fp8x4<kFmt>(v[0] * ys, v[1] * ys, v[2] * ys, v[3] * ys);
-        out.y = fp8x4<kFmt>(v[4] * ys, v[5] * ys, v[6] * ys, v[7] * ys);
-        store_stream(reinterpret_cast<u32x2*>(q) + c, out);
+#pragma unroll
+        for (int i = 0; i < 8; ++i) v[i] = v[i] * s.inv;
+        store_chunk8<kFmt>(q, c, v);
         store_group_scale<kLanes>(sf, group0 + c / kLanes, s, lay);
       }
     }
@@ -169,8 +169,8 @@ hipError_t launch(const uint16_t* h, const float* w, int64_t rows, int64_t cols,
     const int64_t max_blocks = wg_per_cu > 0 ? (int64_t)caps.num_cus * wg_per_cu : iters;
     const int64_t iters_per_block = (iters + max_blocks - 1) / max_blocks;
     const int64_t blocks = (iters + iters_per_block - 1) / iters_per_block;
-    const SlabArgs args{h + r0 * 2 * cols, kWeighted ? w + r0 : nullptr, q + r0 * cols,
-                        (uint32_t)(r0 * groups_per_row)};
+    const SlabArgs args{h + r0 * 2 * cols, kWeighted ? w + r0 : nullptr,
+                        q + code_bytes<kFmt>(r0 * cols), (uint32_t)(r0 * groups_per_row)};
     auto plain = [&] {
       launch_kernel((swiglu_kernel<kLanes, kWeighted, kFmt, kClamp, kCountNone, kThreads,
                                    kStreamUnroll>),
@@ -250,10 +250,16 @@ hipError_t launch_swiglu_per_token(const void* h, int64_t rows, int64_t cols, co
   const ClampArgs ca{swiglu_clamp, clamp_count, count_ws};
   const uint16_t* hp = static_cast<const uint16_t*>(h);
   uint8_t* qp = static_cast<uint8_t*>(q);
-  if (fmt == kE4M3)
-    return launch_c<kE4M3>(hp, w, rows, cols, group, floor, qp, sf, lay, ca, stream, caps);
-  if (fmt == kE5M2)
-    return launch_c<kE5M2>(hp, w, rows, cols, group, floor, qp, sf, lay, ca, stream, caps);
+  switch (fmt) {
+    case kE4M3:
+      return launch_c<kE4M3>(hp, w, rows, cols, group, floor, qp, sf, lay, ca, stream, caps);
+    case kE5M2:
+      return launch_c<kE5M2>(hp, w, rows, cols, group, floor, qp, sf, lay, ca, stream, caps);
+    case kE2M1:
+      return launch_c<kE2M1>(hp, w, rows, cols, group, floor, qp, sf, lay, ca, stream, caps);
+    case kE5M6:
+      return launch_c<kE5M6>(hp, w, rows, cols, group, floor, qp, sf, lay, ca, stream, caps);
+  }
   return hipErrorInvalidValue;
 }
 

@@ -1,5 +1,5 @@
-// swiglu_backward.hip -- SwiGLU backward fused with the per-token E4M3 / E5M2
-// cast of the two input gradients.
+// swiglu_backward.hip -- SwiGLU backward fused with the per-token cast (E4M3,
+// E5M2, packed E2M1 or packed E5M6) of the two input gradients.
 //
 // Operation: swiglu_backward_and_per_token_cast of the operator table on the
 // page "TileKernels 与 DeepGEMM 的分界线：DeepSeek 开源内核栈的分工", §二 (the
@@ -11,10 +11,12 @@
 // evaluated in fp32 on the clamped g, u when a clamp c > 0 is given, with a
 // zero gradient where the clamp changed the value (g > c; |u| > c). The row
 // [dg | du] (2 * cols values) is then cast per token like any other row:
-// codes [rows, 2 * cols], scales [rows, 2 * cols / group].
+// one code row of 2 * cols columns per row, scales [rows, 2 * cols / group].
+// The same page, §四 A, pairs the SwiGLU cast's four formats with this
+// backward.
 //
 // gfx950 design. A lane owns 8 consecutive columns j of one row: three
-// 16-byte loads (gate, up, dv) and two 8-byte code stores, dg at column j and
+// 16-byte loads (gate, up, dv) and two stores of 8 codes, dg at column j and
 // du at column cols + j. The G / 8 lanes of a column group hold both the dg
 // group and the du group over the same columns, so both abs-maxima come from
 // the same DPP reduction pattern and each lane group writes two scales.
@@ -89,14 +91,15 @@ __global__ __launch_bounds__(kThreads) void swiglu_backward_kernel(
       const float amax_u = lane_group_max<kLanes>(absmax8(du));
       const Scale sg = group_scale<kFmt>(amax_g, floor);
       const Scale su = group_scale<kFmt>(amax_u, floor);
-      u32x2 og, ou;
-      og.x = fp8x4<kFmt>(dg[0] * sg.inv, dg[1] * sg.inv, dg[2] * sg.inv, dg[3] * sg.inv);
-      og.y = fp8x4<kFmt>(dg[4] * sg.inv, dg[5] * sg.inv, dg[6] * sg.inv, dg[7] * sg.inv);
-      ou.x = fp8x4<kFmt>(du[0] * su.inv, du[1] * su.inv, du[2] * su.inv, du[3] * su.inv);
-      ou.y = fp8x4<kFmt>(du[4] * su.inv, du[5] * su.inv, du[6] * su.inv, du[7] * su.inv);
-      u32x2* qrow = reinterpret_cast<u32x2*>(q + (int64_t)row * 2 * cols);
-      store_stream(qrow + jc, og);
-      store_stream(qrow + chunks_per_row + jc, ou);
+#pragma unroll
+      for (int i = 0; i < 8; ++i) {
+        dg[i] = dg[i] * sg.inv;
+        du[i] = du[i] * su.inv;
+      }
+      // the row [dg | du] is one code row of 2 * chunks_per_row chunks
+      const uint32_t qc = row * 2 * chunks_per_row + jc;
+      store_chunk8<kFmt>(q, qc, dg);
+      store_chunk8<kFmt>(q, qc + chunks_per_row, du);
       if ((threadIdx.x & (kLanes - 1)) == 0) {
         float* srow = sf + (int64_t)row * 2 * groups_per_half;
         srow[jc / kLanes] = sg.sf;
@@ -122,7 +125,8 @@ hipError_t launch(const uint16_t* h, const uint16_t* dv, const float* w, int64_t
     launch_kernel((swiglu_backward_kernel<kLanes, kWeighted, kFmt, kClamp>),
                   dim3((unsigned)blocks), dim3(kThreads), 0, stream, h + r0 * 2 * cols,
                   dv + r0 * cols, kWeighted ? w + r0 : nullptr, nchunks, (uint32_t)cpr,
-                  magic, cols, floor, clamp, q + r0 * 2 * cols, sf + r0 * sf_per_row);
+                  magic, cols, floor, clamp, q + code_bytes<kFmt>(r0 * 2 * cols),
+                  sf + r0 * sf_per_row);
     const hipError_t err = hipGetLastError();
     if (err != hipSuccess) return err;
   }
@@ -172,10 +176,16 @@ hipError_t launch_swiglu_backward(const void* h, const void* dv, int64_t rows, i
   const uint16_t* hp = static_cast<const uint16_t*>(h);
   const uint16_t* dp = static_cast<const uint16_t*>(dv);
   uint8_t* qp = static_cast<uint8_t*>(q);
-  if (fmt == kE4M3)
-    return launch_c<kE4M3>(hp, dp, w, rows, cols, group, floor, swiglu_clamp, qp, sf, stream);
-  if (fmt == kE5M2)
-    return launch_c<kE5M2>(hp, dp, w, rows, cols, group, floor, swiglu_clamp, qp, sf, stream);
+  switch (fmt) {
+    case kE4M3:
+      return launch_c<kE4M3>(hp, dp, w, rows, cols, group, floor, swiglu_clamp, qp, sf, stream);
+    case kE5M2:
+      return launch_c<kE5M2>(hp, dp, w, rows, cols, group, floor, swiglu_clamp, qp, sf, stream);
+    case kE2M1:
+      return launch_c<kE2M1>(hp, dp, w, rows, cols, group, floor, swiglu_clamp, qp, sf, stream);
+    case kE5M6:
+      return launch_c<kE5M6>(hp, dp, w, rows, cols, group, floor, swiglu_clamp, qp, sf, stream);
+  }
   return hipErrorInvalidValue;
 }
 

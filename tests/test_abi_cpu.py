@@ -102,7 +102,7 @@ def test_e2m1_validation(lib):
 
 def test_swiglu_validation(lib):
     f = lib.qcast_swiglu_per_token
-    assert f(A16, 4, 256, None, E2M1, 32, 0.0, A16, A16, None) == ERR_FORMAT
+    assert f(A16, 4, 256, None, 9, 32, 0.0, A16, A16, None) == ERR_FORMAT
     assert f(A16, 4, 256, None, E4M3, 100, 0.0, A16, A16, None) == ERR_GROUP
     assert f(A16, 4, 200, None, E4M3, 128, 0.0, A16, A16, None) == ERR_SHAPE
     assert f(A16, 4, 1 << 19, None, E4M3, 128, 0.0, A16, A16, None) == ERR_SHAPE  # row too long
@@ -113,7 +113,7 @@ def test_swiglu_validation(lib):
 
 def test_per_block_validation(lib):
     f = lib.qcast_per_block
-    assert f(A16, 256, 256, E2M1, 128, 0.0, A16, A16, None) == ERR_FORMAT
+    assert f(A16, 256, 256, 9, 128, 0.0, A16, A16, None) == ERR_FORMAT
     assert f(A16, 256, 256, E4M3, 64, 0.0, A16, A16, None) == ERR_GROUP
     assert f(A16, 200, 256, E4M3, 128, 0.0, A16, A16, None) == ERR_SHAPE
     assert f(A16, 256, 200, E4M3, 128, 0.0, A16, A16, None) == ERR_SHAPE
@@ -123,7 +123,7 @@ def test_per_block_validation(lib):
 
 def test_per_channel_T_validation(lib):
     f = lib.qcast_per_channel_T
-    assert f(A16, 256, 64, E2M1, 128, 0.0, A16, A16, None) == ERR_FORMAT
+    assert f(A16, 256, 64, 0, 128, 0.0, A16, A16, None) == ERR_FORMAT
     assert f(A16, 256, 64, E4M3, 64, 0.0, A16, A16, None) == ERR_GROUP
     assert f(A16, 200, 64, E4M3, 128, 0.0, A16, A16, None) == ERR_SHAPE
     assert f(A16, 256, 60, E4M3, 128, 0.0, A16, A16, None) == ERR_SHAPE
@@ -159,13 +159,13 @@ def test_sf_layout_validation(lib):
     g = lib.qcast_swiglu_per_token_sf
     assert g(A16, 4, 512, None, E4M3, 128, 0.0, 16, A16, A16, None) == ERR_FORMAT
     assert g(A16, 4, 384, None, E4M3, 128, 0.0, 4, A16, A16, None) == ERR_SHAPE
-    assert g(A16, 4, 512, None, E2M1, 32, 0.0, 4, A16, A16, None) == ERR_FORMAT
+    assert g(A16, 4, 512, None, E2M1, 32, 0.0, 4, None, A16, None) == ERR_NULL   # E2M1 taken
 
 
 def test_swiglu_ex_validation(lib):
     f = lib.qcast_swiglu_per_token_ex
     nan = float("nan")
-    assert f(A16, 4, 256, None, E2M1, 32, 0.0, 0, 1.0, A16, A16, None, None, None) == ERR_FORMAT
+    assert f(A16, 4, 256, None, 9, 32, 0.0, 0, 1.0, A16, A16, None, None, None) == ERR_FORMAT
     assert f(A16, 4, 256, None, E4M3, 128, 0.0, 8, 1.0, A16, A16, None, None, None) == ERR_FORMAT
     assert f(A16, 4, 256, None, E4M3, 100, 0.0, 0, 1.0, A16, A16, None, None, None) == ERR_GROUP
     assert f(A16, 4, 200, None, E4M3, 128, 0.0, 0, 1.0, A16, A16, None, None, None) == ERR_SHAPE
@@ -180,7 +180,7 @@ def test_swiglu_ex_validation(lib):
 
 def test_swiglu_backward_validation(lib):
     f = lib.qcast_swiglu_backward_per_token
-    assert f(A16, A16, 4, 256, None, E2M1, 32, 0.0, 0.0, A16, A16, None) == ERR_FORMAT
+    assert f(A16, A16, 4, 256, None, 9, 32, 0.0, 0.0, A16, A16, None) == ERR_FORMAT
     assert f(A16, A16, 4, 256, None, E4M3, 16, 0.0, 0.0, A16, A16, None) == ERR_GROUP
     assert f(A16, A16, 4, 200, None, E4M3, 128, 0.0, 0.0, A16, A16, None) == ERR_SHAPE
     assert f(A16, A16, 4, 1 << 19, None, E4M3, 128, 0.0, 0.0, A16, A16, None) == ERR_SHAPE
@@ -192,7 +192,7 @@ def test_swiglu_backward_validation(lib):
 
 def test_swiglu_per_channel_T_validation(lib):
     f = lib.qcast_swiglu_per_channel_T
-    assert f(A16, 256, 64, None, E2M1, 128, 0.0, 0.0, A16, A16, None, None, None) == ERR_FORMAT
+    assert f(A16, 256, 64, None, 9, 128, 0.0, 0.0, A16, A16, None, None, None) == ERR_FORMAT
     assert f(A16, 256, 64, None, E4M3, 32, 0.0, 0.0, A16, A16, None, None, None) == ERR_GROUP
     assert f(A16, 200, 64, None, E4M3, 128, 0.0, 0.0, A16, A16, None, None, None) == ERR_SHAPE
     assert f(A16, 256, 60, None, E4M3, 128, 0.0, 0.0, A16, A16, None, None, None) == ERR_SHAPE
@@ -206,7 +206,7 @@ def test_swiglu_per_channel_T_validation(lib):
 
 def test_per_channel_validation(lib):
     f = lib.qcast_per_channel
-    assert f(A16, 256, 64, E2M1, 128, 0.0, A16, A16, None) == ERR_FORMAT
+    assert f(A16, 256, 64, 9, 128, 0.0, A16, A16, None) == ERR_FORMAT
     assert f(A16, 256, 64, E4M3, 64, 0.0, A16, A16, None) == ERR_GROUP
     assert f(A16, 200, 64, E4M3, 128, 0.0, A16, A16, None) == ERR_SHAPE
     assert f(A16, 256, 60, E4M3, 128, 0.0, A16, A16, None) == ERR_SHAPE
@@ -222,11 +222,15 @@ def test_e5m6_formats(lib):
     assert lib.qcast_per_token_sf(A16, 4, 512, E5M6, 128, 0.0, 5, None, A16, None) == ERR_NULL
     assert lib.qcast_cast_back(A16, A16, 4, 256, E5M6, 32, 1, None, None) == ERR_NULL
     assert lib.qcast_per_token(A16, 4, 256, E5M6, 16, 0.0, A16, A16, None) == ERR_GROUP
-    # refused by the casts that write 8-bit codes only
-    assert lib.qcast_swiglu_per_token(A16, 4, 256, None, E5M6, 128, 0.0, A16, A16, None) == ERR_FORMAT
-    assert lib.qcast_per_block(A16, 256, 256, E5M6, 128, 0.0, A16, A16, None) == ERR_FORMAT
-    assert lib.qcast_per_channel_T(A16, 256, 64, E5M6, 128, 0.0, A16, A16, None) == ERR_FORMAT
-    assert lib.qcast_per_channel(A16, 256, 64, E5M6, 128, 0.0, A16, A16, None) == ERR_FORMAT
+    # and by every other cast
+    assert lib.qcast_swiglu_per_token(A16, 4, 256, None, E5M6, 128, 0.0, None, A16, None) == ERR_NULL
+    assert lib.qcast_per_block(A16, 256, 256, E5M6, 128, 0.0, None, A16, None) == ERR_NULL
+    assert lib.qcast_per_channel_T(A16, 256, 64, E5M6, 128, 0.0, None, A16, None) == ERR_NULL
+    assert lib.qcast_per_channel(A16, 256, 64, E5M6, 128, 0.0, None, A16, None) == ERR_NULL
+    assert lib.qcast_swiglu_backward_per_token(A16, A16, 4, 256, None, E5M6, 128, 0.0, 0.0, None,
+                                               A16, None) == ERR_NULL
+    assert lib.qcast_swiglu_per_channel_T(A16, 256, 64, None, E5M6, 128, 0.0, 0.0, None, A16,
+                                          None, None, None) == ERR_NULL
     assert lib.qcast_e2m1(A16, 4, 256, 32, 0.0, None, A16, None) == ERR_NULL
     assert lib.qcast_bench_check_scale(E5M6, 1, 0, A16, None) == ERR_SHAPE
     assert lib.qcast_bench_check_scale(5, 1, 2, A16, None) == ERR_FORMAT
