@@ -33,7 +33,8 @@
  * Conventions shared by every entry point:
  *  - Every data pointer is a DEVICE pointer on the current HIP device, owned
  *    (allocated and freed) by the caller. The library never allocates,
- *    frees, synchronizes or keeps a pointer after returning.
+ *    frees, synchronizes or keeps a pointer after returning (its only device
+ *    memory is a static array of QCAST_NOALLOC_SCRATCH_BYTES per GPU).
  *  - Tensors are row-major and contiguous. bf16 inputs are passed as raw
  *    16-bit patterns. Inputs must not overlap outputs.
  *  - Alignment: inputs and code outputs 16 bytes, scale outputs 4 bytes,
@@ -49,8 +50,9 @@
  *    any HIP call: rows * cols / group < 2^31 scale groups for the per-token
  *    casts; for the others, the limits stated with each entry point.
  *  - Calls on one stream are ordered; concurrent calls on different streams
- *    are independent (the library holds no mutable device state; a count
- *    workspace is the caller's, and concurrent calls need different ones).
+ *    are independent (a count workspace is the caller's, and concurrent
+ *    calls need different ones). The one piece of mutable device state the
+ *    library holds is the count array of qcast_swiglu_per_token_noalloc.
  *  - Entry points may be called from several host threads at once: the
  *    library's host-side state (cached CU counts, the CU override, the
  *    measurement events of qcast_bench_time_next) is atomic or per thread.
@@ -64,10 +66,14 @@
 extern "C" {
 #endif
 
-#define QCAST_ABI_VERSION 3
+#define QCAST_ABI_VERSION 4
 
 /* Bytes of the optional clamp-count workspace (count_ws) of the SwiGLU casts. */
 #define QCAST_COUNT_WS_BYTES 8192
+
+/* Bytes of the library's own device array that qcast_swiglu_per_token_noalloc
+ * counts through (one per GPU, held until the process ends). */
+#define QCAST_NOALLOC_SCRATCH_BYTES 8192
 
 #ifndef QCAST_API
 #define QCAST_API __attribute__((visibility("default")))
@@ -212,6 +218,29 @@ QCAST_API int qcast_swiglu_per_token_ex(const void* h, int64_t rows, int64_t col
                                         float clamp_min, int sf_flags, float swiglu_clamp,
                                         void* q, void* sf, uint64_t* clamp_count,
                                         void* count_ws, void* stream);
+
+/*
+ * qcast_swiglu_per_token_ex for callers that cannot allocate device memory
+ * (code under HIP graph capture, tight serving loops, harnesses that forbid
+ * allocation): the same cast, with no count_ws argument. When it counts
+ * (clamp_count given, swiglu_clamp > 0) the count slots live in a device
+ * array of the library, QCAST_NOALLOC_SCRATCH_BYTES per GPU, that the call
+ * first clears with a small kernel on `stream`; the call itself allocates
+ * nothing. Every shape qcast_swiglu_per_token_ex takes fits that array (the
+ * slots are reused by every slab of rows, so no call needs more than
+ * QCAST_COUNT_WS_BYTES); a call that would need more returns
+ * QCAST_ERR_SHAPE. All calls on one GPU share the array: calls that may
+ * overlap on one GPU (on different streams, or from several threads without
+ * ordering) race on it and their counts are undefined; calls in order on
+ * one stream are safe. Results (codes, scales, count) equal those of
+ * qcast_swiglu_per_token_ex with a workspace. Errors as that entry point;
+ * QCAST_ERR_DEVICE if the array's device address cannot be obtained.
+ */
+QCAST_API int qcast_swiglu_per_token_noalloc(const void* h, int64_t rows, int64_t cols,
+                                             const float* row_weight, int fmt, int group,
+                                             float clamp_min, int sf_flags, float swiglu_clamp,
+                                             void* q, void* sf, uint64_t* clamp_count,
+                                             void* stream);
 
 /*
  * SwiGLU backward fused with the per-token cast of the input gradient

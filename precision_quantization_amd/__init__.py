@@ -27,7 +27,7 @@ __all__ = ["qcast_per_token", "qcast_e2m1", "qcast_swiglu_per_token", "qcast_per
            "qcast_per_channel_T", "qcast_cast_back", "qcast_per_token_sf",
            "qcast_swiglu_per_token_sf", "qcast_swiglu_per_token_ex",
            "qcast_swiglu_backward_per_token", "qcast_swiglu_per_channel_T", "qcast_per_channel",
-           "sf_layout_shape", "SF_ROUND_POW2", "SF_COL_MAJOR",
+           "qcast_swiglu_per_token_noalloc", "sf_layout_shape", "SF_ROUND_POW2", "SF_COL_MAJOR",
            "SF_PACKED_UE8M0", "qcast_abi_version", "qcast_set_num_cus", "qcast_bench_copy",
            "qcast_bench_check_scale", "qcast_bench_time_next",
            "qcast_bench_per_channel_T_traffic",
@@ -237,6 +237,29 @@ def qcast_swiglu_per_token_ex(h, row_weight=None, fmt="e4m3", group=128, clamp_m
                                                sf_flags, swiglu_clamp, out.data_ptr(),
                                                out_sf.data_ptr(), cptr, wsptr, sh),
               "qcast_swiglu_per_token_ex")
+    return out, out_sf
+
+
+def qcast_swiglu_per_token_noalloc(h, row_weight=None, fmt="e4m3", group=128, clamp_min=0.0,
+                                   sf_flags=0, swiglu_clamp=0.0, clamp_count=None, out=None,
+                                   out_sf=None, stream=None):
+    """qcast_swiglu_per_token_ex for callers that cannot allocate: the clamp
+    count goes through the library's own device array (include/qcast.h), so
+    with ``out`` and ``out_sf`` given nothing is allocated; calls that may
+    overlap on one GPU race on that array."""
+    f = fmt_id(fmt)
+    h, rows, cols = _gate_up(h)
+    wptr = _row_weight(row_weight, rows, h.device)
+    cptr = _counter(clamp_count, h.device)
+    out = _out(out, code_shape(f, rows, cols), _code_dtype(f), h.device, "out")
+    shape, dt = sf_layout_shape(rows, cols, group if group > 0 else 1, sf_flags)
+    out_sf = _out(out_sf, shape, dt, h.device, "out_sf")
+    with torch.cuda.device(h.device):
+        check(load().qcast_swiglu_per_token_noalloc(h.data_ptr(), rows, cols, wptr, f, group,
+                                                    clamp_min, sf_flags, swiglu_clamp,
+                                                    out.data_ptr(), out_sf.data_ptr(), cptr,
+                                                    _stream(h.device, stream)),
+              "qcast_swiglu_per_token_noalloc")
     return out, out_sf
 
 

@@ -6,10 +6,18 @@
 // passes its own clamp_min > 0; E5M2 and E5M6, for which the page names
 // none, take the E4M3 floor.
 #include <atomic>
+#include <mutex>
 
 #include "qcast.h"
 #include "qcast_device.h"
 #include "qcast_kernels.h"
+
+// The clamp-count slots of qcast_swiglu_per_token_noalloc: a file-scope
+// device array (one copy per GPU, held until the process ends), used in
+// place of a caller's count workspace. Host code never passes its name to a
+// kernel (on the host it is only a stand-in for the symbol); it uses the
+// device address that hipGetSymbolAddress returns for the current device.
+static __device__ __align__(256) unsigned long long scratch[QCAST_NOALLOC_SCRATCH_BYTES / 8];
 
 namespace {
 
@@ -67,6 +75,34 @@ int caps_for_current_device(qcast::LaunchCaps* caps) {
 
 int finish(hipError_t err) { return err == hipSuccess ? QCAST_OK : QCAST_ERR_LAUNCH; }
 
+// Device address of `scratch` on the current device, looked up once per
+// device (with that device current) and kept.
+std::atomic<void*> g_scratch_ptr[kMaxDevices];
+std::mutex g_scratch_mu;
+
+int scratch_for_current_device(unsigned long long** out) {
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return QCAST_ERR_DEVICE;
+  void* p = g_scratch_ptr[dev].load(std::memory_order_acquire);
+  if (!p) {
+    std::lock_guard<std::mutex> lock(g_scratch_mu);
+    p = g_scratch_ptr[dev].load(std::memory_order_relaxed);
+    if (!p) {
+      if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess || !p)
+        return QCAST_ERR_DEVICE;
+      g_scratch_ptr[dev].store(p, std::memory_order_release);
+    }
+  }
+  *out = static_cast<unsigned long long*>(p);
+  return QCAST_OK;
+}
+
+// Zeroes n 64-bit words (a fill kernel, not a memset: a caller may capture
+// the call in a graph).
+__global__ __launch_bounds__(qcast::kThreads) void zero_words(unsigned long long* p, int n) {
+  for (int i = threadIdx.x; i < n; i += qcast::kThreads) p[i] = 0ull;
+}
+
 // A clamp bound of +inf clamps nothing; so does any bound <= 0.
 float clamp_value(float c) { return (c > 0.0f && c <= 3.4028235e38f) ? c : 0.0f; }
 
@@ -88,6 +124,33 @@ bool sf_shape_ok(int64_t rows, int64_t cols, int group, int flags) {
 // Element counts beyond 2^62 would overflow the kernels' int64 offsets.
 bool too_big(int64_t rows, int64_t cols) {
   return cols > 0 && rows > (int64_t(1) << 62) / cols;
+}
+
+// Argument checks of the per-token SwiGLU casts, before any HIP call;
+// *empty when the call casts nothing (and launches nothing).
+int check_swiglu_ex(const void* h, int64_t rows, int64_t cols, const float* row_weight, int fmt,
+                    int group, float clamp_min, int sf_flags, float swiglu_clamp, const void* q,
+                    const void* sf, const uint64_t* clamp_count, const void* count_ws,
+                    bool* empty) {
+  *empty = false;
+  if (!any_fmt(fmt)) return QCAST_ERR_FORMAT;
+  if (!sf_flags_ok(sf_flags)) return QCAST_ERR_FORMAT;
+  if (!per_token_group_ok(group)) return QCAST_ERR_GROUP;
+  if (rows < 0 || cols < 0 || cols % group != 0 || cols / 8 >= (int64_t(1) << 16) ||
+      too_big(rows, 2 * cols) || !sf_shape_ok(rows, cols, group, sf_flags))
+    return QCAST_ERR_SHAPE;
+  if (swiglu_clamp != swiglu_clamp) return QCAST_ERR_VALUE;
+  if (!clamp_min_ok(clamp_min)) return QCAST_ERR_VALUE;
+  if (rows == 0 || cols == 0) {
+    *empty = true;
+    return QCAST_OK;
+  }
+  if (!h || !q || !sf) return QCAST_ERR_NULL;
+  if (!aligned(h, 16) || !aligned(q, 16) || !aligned(sf, 4) ||
+      (row_weight && !aligned(row_weight, 4)) || (clamp_count && !aligned(clamp_count, 8)) ||
+      (count_ws && !aligned(count_ws, 128)))
+    return QCAST_ERR_ALIGN;
+  return QCAST_OK;
 }
 
 }  // namespace
@@ -149,27 +212,48 @@ int qcast_swiglu_per_token_ex(const void* h, int64_t rows, int64_t cols,
                               const float* row_weight, int fmt, int group, float clamp_min,
                               int sf_flags, float swiglu_clamp, void* q, void* sf,
                               uint64_t* clamp_count, void* count_ws, void* stream) {
-  if (!any_fmt(fmt)) return QCAST_ERR_FORMAT;
-  if (!sf_flags_ok(sf_flags)) return QCAST_ERR_FORMAT;
-  if (!per_token_group_ok(group)) return QCAST_ERR_GROUP;
-  if (rows < 0 || cols < 0 || cols % group != 0 || cols / 8 >= (int64_t(1) << 16) ||
-      too_big(rows, 2 * cols) || !sf_shape_ok(rows, cols, group, sf_flags))
-    return QCAST_ERR_SHAPE;
-  if (swiglu_clamp != swiglu_clamp) return QCAST_ERR_VALUE;
-  if (!clamp_min_ok(clamp_min)) return QCAST_ERR_VALUE;
-  if (rows == 0 || cols == 0) return QCAST_OK;
-  if (!h || !q || !sf) return QCAST_ERR_NULL;
-  if (!aligned(h, 16) || !aligned(q, 16) || !aligned(sf, 4) ||
-      (row_weight && !aligned(row_weight, 4)) || (clamp_count && !aligned(clamp_count, 8)) ||
-      (count_ws && !aligned(count_ws, 128)))
-    return QCAST_ERR_ALIGN;
+  bool empty = false;
+  int rc = check_swiglu_ex(h, rows, cols, row_weight, fmt, group, clamp_min, sf_flags,
+                           swiglu_clamp, q, sf, clamp_count, count_ws, &empty);
+  if (rc != QCAST_OK || empty) return rc;
   qcast::LaunchCaps caps;
-  const int rc = caps_for_current_device(&caps);
-  if (rc != QCAST_OK) return rc;
+  if ((rc = caps_for_current_device(&caps)) != QCAST_OK) return rc;
   return finish(qcast::launch_swiglu_per_token(
       h, rows, cols, row_weight, fmt, group, floor_for(fmt, clamp_min), (uint32_t)sf_flags,
       clamp_value(swiglu_clamp), reinterpret_cast<unsigned long long*>(clamp_count),
       static_cast<unsigned long long*>(count_ws), q, sf, static_cast<hipStream_t>(stream), caps));
+}
+
+int qcast_swiglu_per_token_noalloc(const void* h, int64_t rows, int64_t cols,
+                                   const float* row_weight, int fmt, int group, float clamp_min,
+                                   int sf_flags, float swiglu_clamp, void* q, void* sf,
+                                   uint64_t* clamp_count, void* stream) {
+  static_assert(sizeof(scratch) == QCAST_NOALLOC_SCRATCH_BYTES, "scratch size");
+  bool empty = false;
+  int rc = check_swiglu_ex(h, rows, cols, row_weight, fmt, group, clamp_min, sf_flags,
+                           swiglu_clamp, q, sf, clamp_count, nullptr, &empty);
+  if (rc != QCAST_OK || empty) return rc;
+  // The count slots are reused by every slab of rows, so every shape needs
+  // QCAST_COUNT_WS_BYTES of scratch, no more; a library built with a
+  // smaller array refuses the counting call.
+  const bool counting = clamp_count && clamp_value(swiglu_clamp) > 0.0f;
+  if (counting && sizeof(scratch) < QCAST_COUNT_WS_BYTES) return QCAST_ERR_SHAPE;
+  qcast::LaunchCaps caps;
+  if ((rc = caps_for_current_device(&caps)) != QCAST_OK) return rc;
+  unsigned long long* slots = nullptr;
+  if (counting) {
+    if ((rc = scratch_for_current_device(&slots)) != QCAST_OK) return rc;
+    // The array keeps what the last call on this GPU left in it: clear the
+    // slots on the stream, ahead of the cast.
+    hipLaunchKernelGGL(zero_words, dim3(1), dim3(qcast::kThreads), 0,
+                       static_cast<hipStream_t>(stream), slots,
+                       (int)(QCAST_COUNT_WS_BYTES / sizeof(unsigned long long)));
+    if (hipGetLastError() != hipSuccess) return QCAST_ERR_LAUNCH;
+  }
+  return finish(qcast::launch_swiglu_per_token(
+      h, rows, cols, row_weight, fmt, group, floor_for(fmt, clamp_min), (uint32_t)sf_flags,
+      clamp_value(swiglu_clamp), reinterpret_cast<unsigned long long*>(clamp_count), slots, q,
+      sf, static_cast<hipStream_t>(stream), caps));
 }
 
 int qcast_swiglu_per_token_sf(const void* h, int64_t rows, int64_t cols,

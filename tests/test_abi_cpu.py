@@ -64,7 +64,7 @@ def test_binding_names_match_the_c_entry_points():
 
 
 def test_abi_version_and_status_strings(lib):
-    assert lib.qcast_abi_version() == 3
+    assert lib.qcast_abi_version() == 4
     for s in range(9):
         assert lib.qcast_status_str(s).decode()
     assert lib.qcast_status_str(99).decode() == "unknown status"
@@ -353,3 +353,29 @@ def test_binding_rejects_e5m6_codes_whose_width_is_not_a_multiple_of_3():
     q = torch.zeros(4, 100, dtype=torch.uint8)
     with pytest.raises(pq.QcastError, match="multiple of 3"):
         pq.qcast_cast_back(q, torch.zeros(4, 2), "e5m6", 32)
+
+
+def test_swiglu_noalloc_validation(lib):
+    f = lib.qcast_swiglu_per_token_noalloc
+    nan = float("nan")
+    assert f(A16, 4, 256, None, 9, 32, 0.0, 0, 1.0, A16, A16, A16, None) == ERR_FORMAT
+    assert f(A16, 4, 256, None, E4M3, 128, 0.0, 8, 1.0, A16, A16, A16, None) == ERR_FORMAT
+    assert f(A16, 4, 256, None, E4M3, 100, 0.0, 0, 1.0, A16, A16, A16, None) == ERR_GROUP
+    assert f(A16, 4, 200, None, E4M3, 128, 0.0, 0, 1.0, A16, A16, A16, None) == ERR_SHAPE
+    assert f(A16, 4, 256, None, E4M3, 128, 0.0, 0, nan, A16, A16, A16, None) == ERR_VALUE
+    assert f(A16, 4, 256, None, E4M3, 128, nan, 0, 1.0, A16, A16, A16, None) == ERR_VALUE
+    assert f(None, 4, 256, None, E4M3, 128, 0.0, 0, 1.0, A16, A16, A16, None) == ERR_NULL
+    assert f(A16, 4, 256, None, E4M3, 128, 0.0, 0, 1.0, A16, A16, A16 + 4, None) == ERR_ALIGN
+    assert f(A16, 4, 256, None, E4M3, 128, 0.0, 0, 1.0, MIS, A16, A16, None) == ERR_ALIGN
+    assert f(None, 0, 256, None, E4M3, 128, 0.0, 0, 1.0, None, None, None, None) == OK
+    if not gpu_available():
+        # valid arguments reach the device lookup, which finds no GPU here
+        assert f(A16, 4, 256, None, E4M3, 128, 0.0, 0, 1.0, A16, A16, A16, None) == ERR_DEVICE
+
+
+def test_noalloc_scratch_size_is_declared():
+    text = open(HEADERS[0]).read()
+    assert "#define QCAST_NOALLOC_SCRATCH_BYTES 8192" in text
+    src = open(os.path.join(ROOT, "precision_quantization_amd", "csrc", "qcast_abi.hip")).read()
+    assert "static __device__ __align__(256) unsigned long long scratch[" in src
+    assert "hipGetSymbolAddress" in src and "hipMalloc" not in src
