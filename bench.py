@@ -41,7 +41,9 @@ and the casts that are not among the five: cast_back of the per-token codes to b
 per-token cast with 1 x 32 groups and packed UE8M0 column-major scales, the
 per-token E5M6 cast and its cast_back,
 SwiGLU with the clamp and counter, SwiGLU + per-channel cast + transpose,
-the SwiGLU backward cast, and the per-channel cast in the input layout.
+the SwiGLU backward cast, the per-channel cast in the input layout, the
+packed formats (E2M1, E5M6) on the per-channel, per-block and SwiGLU casts,
+and the per-token cast with 1 x 32 groups and fp32 column-major scales.
 
     python bench.py [--gpus 1] [--steps 200] [--warmup 10]
 """
@@ -237,8 +239,8 @@ def extra_calls(wls, dev):
     qo = torch.empty(r, c, dtype=torch.float8_e4m3fn, device=dev)
     so = torch.empty(shape, dtype=dt, device=dev)
     calls.append(("per_token_ue8m0_g32", [r, c], 2 * r * c + r * c + shape[0] * shape[1] * 4,
-                  lambda x=x, qo=qo, so=so: pq.qcast_per_token_sf(x, "e4m3", 32, sf_flags=flags,
-                                                                  out=qo, out_sf=so)))
+                  lambda x=x, qo=qo, so=so, f=flags: pq.qcast_per_token_sf(
+                      x, "e4m3", 32, sf_flags=f, out=qo, out_sf=so)))
     # E5M6 per-token cast of the hidden-state workload, and its cast_back
     q6 = torch.empty(pq.code_shape("e5m6", r, c), dtype=torch.uint8, device=dev)
     s6 = torch.empty(r, c // 128, dtype=torch.float32, device=dev)
@@ -282,6 +284,65 @@ def extra_calls(wls, dev):
     calls.append(("per_channel", [r, c], 2 * r * c + r * c + (r // 128) * c * 4,
                   lambda a=a, qc=qc, sc=sc: pq.qcast_per_channel(a, "e4m3", 128, out=qc,
                                                                  out_sf=sc)))
+
+    def code_bytes(fmt, n):
+        return {"e2m1": n // 2, "e5m6": n // 2 * 3}.get(fmt, n)
+
+    def outputs(fmt, rows, cols, sf_shape):
+        q = torch.empty(pq.code_shape(fmt, rows, cols), dtype=torch.uint8, device=dev)
+        return q, torch.empty(sf_shape, dtype=torch.float32, device=dev)
+
+    # the packed formats on the per-channel casts (the activation workload)
+    for fmt in ("e2m1", "e5m6"):
+        qT_, sT_ = outputs(fmt, c, r, (c, r // 128))
+        calls.append((f"per_channel_T_{fmt}", [r, c],
+                      2 * r * c + c * code_bytes(fmt, r) + c * (r // 128) * 4,
+                      lambda a=a, q=qT_, s=sT_, f=fmt: pq.qcast_per_channel_T(
+                          a, f, 128, out=q, out_sf=s)))
+    qc2, sc2 = outputs("e2m1", r, c, (r // 128, c))
+    calls.append(("per_channel_e2m1", [r, c], 2 * r * c + r * c // 2 + (r // 128) * c * 4,
+                  lambda a=a, q=qc2, s=sc2: pq.qcast_per_channel(a, "e2m1", 128, out=q,
+                                                                 out_sf=s)))
+    # ... and on the per-block cast (the weight workload)
+    wb = by["per_block"].x.to(dev)
+    r, c = wb.shape
+    for fmt in ("e2m1", "e5m6"):
+        qb_, sb_ = outputs(fmt, r, c, (r // 128, c // 128))
+        calls.append((f"per_block_{fmt}", [r, c],
+                      2 * r * c + r * code_bytes(fmt, c) + (r // 128) * (c // 128) * 4,
+                      lambda x=wb, q=qb_, s=sb_, f=fmt: pq.qcast_per_block(x, f, 128, out=q,
+                                                                           out_sf=s)))
+    # SwiGLU in the packed formats: per-token (E2M1 with 1 x 32 groups, E5M6 with
+    # 1 x 128), per-channel + transpose, and the backward
+    r, n = wl.rows, wl.cols
+    sw_in = r * 2 * n * 2 + r * 4
+    for fmt, g in (("e2m1", 32), ("e5m6", 128)):
+        qs_, ss_ = outputs(fmt, r, n, (r, n // g))
+        calls.append((f"swiglu_{fmt}_g{g}", [r, 2 * n],
+                      sw_in + r * code_bytes(fmt, n) + r * (n // g) * 4,
+                      lambda h=h, w=w, q=qs_, s=ss_, f=fmt, g=g: pq.qcast_swiglu_per_token(
+                          h, w, f, g, out=q, out_sf=s)))
+    qt2, st2 = outputs("e2m1", n, r, (n, r // 128))
+    calls.append(("swiglu_per_channel_T_e2m1", [r, 2 * n],
+                  sw_in + n * r // 2 + n * (r // 128) * 4,
+                  lambda h=h, w=w, q=qt2, s=st2: pq.qcast_swiglu_per_channel_T(
+                      h, w, "e2m1", 128, out=q, out_sf=s)))
+    qb2, sb2 = outputs("e2m1", r, 2 * n, (r, 2 * n // 32))
+    calls.append(("swiglu_backward_e2m1_g32", [r, 2 * n],
+                  r * 2 * n * 2 + r * n * 2 + r * 4 + r * n + r * (2 * n // 32) * 4,
+                  lambda hg=hg, dvg=dvg, wg=wg, q=qb2, s=sb2: pq.qcast_swiglu_backward_per_token(
+                      hg, dvg, wg, "e2m1", 32, swiglu_clamp=6.0, out=q, out_sf=s)))
+    # per-token cast with 1 x 32 groups and fp32 column-major scales
+    x = by["per_token"].x.to(dev)
+    r, c = x.shape
+    cm = pq.SF_COL_MAJOR
+    shape, dt = pq.sf_layout_shape(r, c, 32, cm)
+    qo2 = torch.empty(r, c, dtype=torch.float8_e4m3fn, device=dev)
+    so2 = torch.empty(shape, dtype=dt, device=dev)
+    calls.append(("per_token_f32_colmajor_g32", [r, c], 2 * r * c + r * c + r * (c // 32) * 4,
+                  lambda x=x, qo=qo2, so=so2, f=cm: pq.qcast_per_token_sf(x, "e4m3", 32,
+                                                                         sf_flags=f, out=qo,
+                                                                         out_sf=so)))
     return calls
 
 

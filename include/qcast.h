@@ -278,7 +278,7 @@ QCAST_API int qcast_swiglu_backward_per_token(const void* h, const void* dv, int
  *   sf  [cols, rows/group] fp32, groups of `group` tokens of one channel.
  *   group must be 128; rows % group == 0; cols % 8 == 0; any format;
  *   clamp_count and count_ws as above.
- *   Limits: 256 * cols < 2^31, 64 * rows < 2^31.
+ *   Limits: 256 * cols < 2^31, 64 * rows < 2^31 (96 * rows for E5M6).
  */
 QCAST_API int qcast_swiglu_per_channel_T(const void* h, int64_t rows, int64_t cols,
                                          const float* row_weight, int fmt, int group,

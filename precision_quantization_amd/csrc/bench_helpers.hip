@@ -144,7 +144,7 @@ extern "C" int qcast_bench_copy(const void* src, void* dst, int64_t nbytes, void
 extern "C" int qcast_bench_per_channel_T_traffic(const void* x, int64_t rows, int64_t cols,
                                                  void* qT, void* stream) {
   if (rows < 0 || cols < 0 || rows % 128 != 0 || cols % 8 != 0 ||
-      !qcast::per_channel_t_fits(rows, cols, cols))
+      !qcast::per_channel_t_fits(rows, cols, cols, QCAST_FMT_E4M3))
     return QCAST_ERR_SHAPE;
   if (rows == 0 || cols == 0) return QCAST_OK;
   if (!x || !qT) return QCAST_ERR_NULL;

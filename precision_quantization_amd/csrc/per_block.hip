@@ -73,8 +73,8 @@ __global__ __launch_bounds__(kThreads) void per_block_kernel(
   // A 16-lane DPP row holds one tile's 128 columns of one row; the rows of
   // a wave that hold the same tile are kChunksPerRow lanes apart.
   uint32_t mb = __float_as_uint(lane_group_max<16>(fmaxf(bf16_lo(m16), bf16_hi(m16))));
-#pragma unroll
-  for (int o = kChunksPerRow; o < 64; o <<= 1) mb = umax(mb, (uint32_t)__shfl_xor((int)mb, o));
+  if (kChunksPerRow == 16) mb = max_xor16(mb);
+  mb = max_xor32(mb);
   if ((t & 63) < kChunksPerRow && (t & 15) == 0) wave_amax[t >> 6][ti] = __uint_as_float(mb);
   __syncthreads();
   const float m = fmaxf(fmaxf(wave_amax[0][ti], wave_amax[1][ti]),

@@ -69,7 +69,7 @@ __global__ __launch_bounds__(kThreads) void per_channel_kernel(
     m[3] = pk_umax16(m[3], raw[j].w & 0x7fff7fffu);
   }
 #pragma unroll
-  for (int w = 0; w < 4; ++w) m[w] = pk_umax16(m[w], (uint32_t)__shfl_xor((int)m[w], 32));
+  for (int w = 0; w < 4; ++w) m[w] = pk_max_xor32(m[w]);
   if ((t & 63) < kChunks) {
 #pragma unroll
     for (int w = 0; w < 4; ++w) {

@@ -1,5 +1,5 @@
 // per_channel_t.hip -- per-channel cast of bf16 activations, written
-// transposed, to E4M3 or E5M2.
+// transposed, to E4M3, E5M2, packed E2M1 or packed E5M6.
 //
 // Operation: per_channel_cast (+transpose) of the operator table on the page
 // "TileKernels 与 DeepGEMM 的分界线：DeepSeek 开源内核栈的分工", §二. The scale
@@ -22,7 +22,14 @@
 // 4 * ((channel/8) mod 8): the eight channel chunks a half-wave writes land
 // in distinct banks, and each 16-byte run of tokens stays contiguous and
 // aligned, so the read-back is one ds_read_b128 per lane and the store is a
-// full row of qT (128 * kTG bytes) per channel. (The pages' transpose pads
+// full row of qT (128 * kTG bytes) per channel. The packed formats wait in
+// LDS one code per byte (E2M1) or per 16-bit half (E5M6, rows twice as
+// long), and the read-back lane packs them (nibbles; 12-bit codes) before it
+// stores: 8 or 12 bytes per lane instead of 16. (A kernel that transposes in
+// registers instead -- each lane holding 16 tokens of 8 channels, no LDS, no
+// barrier -- was measured slower in every format: 66.0 against 63.3 us for
+// E4M3 on the 16384 x 7168 activation, 62.3 against 57.2 for E2M1, 103.5
+// against 82.5 for E5M6.) (The pages' transpose pads
 // its shared tile and rotates the column index for the same purpose; the
 // XOR form keeps 16-byte reads aligned.) Workgroups are numbered so that
 // each of the 8 XCDs walks a contiguous range of tiles, in strips of two
@@ -78,11 +85,6 @@ constexpr int kXcds = 8;
 #ifndef QCAST_PC_SW_STRIP
 #define QCAST_PC_SW_STRIP 1
 #endif
-// 1: the 8-bit formats also take the register-transpose kernel.
-#ifndef QCAST_PC_WAVE_FP8
-#define QCAST_PC_WAVE_FP8 0
-#endif
-constexpr bool kWaveFp8 = QCAST_PC_WAVE_FP8;
 constexpr uint32_t kStrip = QCAST_PC_STRIP;
 constexpr uint32_t kSwStrip = QCAST_PC_SW_STRIP;
 constexpr int kTG = QCAST_PC_TG;
@@ -102,10 +104,28 @@ constexpr int kRowVec = kRowDw / 4;                 // 16-byte vectors per row
 constexpr int kReadPasses = kChannels * kRowVec / kThreads;
 static_assert(kPassesPerGroup >= 1 && kReadPasses >= 1, "tile shape");
 
-// Dword index of token dword d of channel row c in the swizzled tile.
+// Dword index of token dword d of channel row c in the swizzled tile of
+// rows of kDw dwords (the XOR moves whole 16-byte groups and keeps d < kDw
+// for kDw a multiple of 32).
+template <int kDw = kRowDw>
 __device__ __forceinline__ int tile_index(int c, int d) {
-  return c * kRowDw + (d ^ (4 * ((c >> 3) & 7)));
+  static_assert(kDw % 32 == 0, "rows of whole 32-dword blocks");
+  return c * kDw + (d ^ (4 * ((c >> 3) & 7)));
 }
+
+// The LDS tile of a format. Codes wait in LDS one per byte (E4M3, E5M2, and
+// E2M1 with the code in the low nibble) or one per 16-bit half (E5M6), so a
+// lane's 4 tokens of a channel are one dword (two for E5M6); the read-back
+// lane packs E2M1 to nibbles and E5M6 to 12-bit codes before its store.
+template <int kFmt>
+struct TileGeo {
+  static constexpr int kCodeBytes = kFmt == kE5M6 ? 2 : 1;   // LDS bytes per code
+  static constexpr int kRowDw = kTileTokens * kCodeBytes / 4;
+  static constexpr int kRowVec = kRowDw / 4;                 // 16-byte vectors per row
+  static constexpr int kVecTokens = 16 / kCodeBytes;         // tokens per vector
+  static constexpr int kReadPasses = kChannels * kRowVec / kThreads;
+  static_assert(kReadPasses >= 1, "tile shape");
+};
 
 // Position of a tile: first channel, first token, valid channels and groups.
 // Tile counts and in-tile offsets fit in 32 bits (checked by the launcher).
@@ -114,17 +134,27 @@ struct TileCoord {
   int nc, ng;
 };
 
+// The strip walk divides by kS * ntg with a host-computed multiply and shift
+// (sdiv), and by the strip width with a shift (kS is a power of two; only a
+// last, narrower strip divides), so a workgroup issues its loads a few
+// instructions after it starts.
 template <uint32_t kS = kStrip>
 __device__ __forceinline__ TileCoord tile_coord(uint32_t tau, uint32_t ngroups, uint32_t cols,
-                                                uint32_t nct, uint32_t ntg) {
+                                                uint32_t nct, uint32_t ntg, FastDiv sdiv) {
+  static_assert((kS & (kS - 1)) == 0, "strips of a power of two");
   TileCoord tc;
   uint32_t ct;
   if (kOrder & 4) {
-    const uint32_t strip = tau / (kS * ntg);
-    const uint32_t width = nct - strip * kS < kS ? nct - strip * kS : kS;
+    const uint32_t strip = fast_div(tau, sdiv);
     const uint32_t rem = tau - strip * kS * ntg;
-    tc.gt = rem / width;
-    ct = strip * kS + (rem - tc.gt * width);
+    if (nct - strip * kS >= kS) {
+      tc.gt = rem / kS;
+      ct = strip * kS + (rem & (kS - 1));
+    } else {
+      const uint32_t width = nct - strip * kS;
+      tc.gt = rem / width;
+      ct = strip * kS + (rem - tc.gt * width);
+    }
   } else {
     ct = (kOrder & 1) ? tau % nct : tau / ntg;
     tc.gt = (kOrder & 1) ? tau / nct : tau - ct * ntg;
@@ -183,8 +213,8 @@ struct Bf16Tile {
 #pragma unroll
     for (int w = 0; w < 4; ++w) {
       if (kCC == 8) m[w] = pk_umax16(m[w], dpp<kDppRor8>(m[w]));
-      m[w] = pk_umax16(m[w], (uint32_t)__shfl_xor((int)m[w], 16));
-      m[w] = pk_umax16(m[w], (uint32_t)__shfl_xor((int)m[w], 32));
+      m[w] = pk_max_xor16(m[w]);
+      m[w] = pk_max_xor32(m[w]);
       out[2 * w] = bf16_lo(m[w]);
       out[2 * w + 1] = bf16_hi(m[w]);
     }
@@ -211,8 +241,8 @@ struct F32Tile {
           m = umax(m, __float_as_uint(v[gi * kPassesPerGroup + pp][i][j]) & 0x7fffffffu);
       }
       if (kCC == 8) m = umax(m, dpp<kDppRor8>(m));
-      m = umax(m, (uint32_t)__shfl_xor((int)m, 16));
-      m = umax(m, (uint32_t)__shfl_xor((int)m, 32));
+      m = max_xor16(m);
+      m = max_xor32(m);
       out[j] = __uint_as_float(m);
     }
   }
@@ -273,8 +303,9 @@ __device__ __forceinline__ uint32_t load_swiglu_tile(const uint16_t* __restrict_
   return nclamp;
 }
 
+template <int kFmt>
 struct Smem {
-  uint32_t tile[kChannels * kRowDw];
+  uint32_t tile[kChannels * TileGeo<kFmt>::kRowDw];
   float wave_amax[kTG][4][kChannels];
   float inv_s[kTG][kChannels];
 };
@@ -284,8 +315,9 @@ struct Smem {
 // tile) it also ends converged, with the LDS free again.
 template <int kFmt, bool kReuse, class Tile>
 __device__ __forceinline__ void process_tile(const TileCoord& tc, const Tile& tile, uint32_t rows,
-                                             uint32_t ngroups, float floor, Smem& sm,
+                                             uint32_t ngroups, float floor, Smem<kFmt>& sm,
                                              uint8_t* __restrict__ qT, float* __restrict__ sf) {
+  using TG = TileGeo<kFmt>;
   const int t = threadIdx.x;
   const int ch = t % kCC;
   const int k = t / kCC;
@@ -314,7 +346,7 @@ __device__ __forceinline__ void process_tile(const TileCoord& tc, const Tile& ti
   __syncthreads();
 
   // Codes: for each pass and each of the lane's 8 channels, the 4 tokens
-  // 4k..4k+3 of the pass as one dword of the channel's LDS row.
+  // 4k..4k+3 of the pass as one dword (two for E5M6) of the channel's LDS row.
 #pragma unroll
   for (int p = 0; p < kPasses; ++p) {
     const int gi = p / kPassesPerGroup;
@@ -324,22 +356,49 @@ __device__ __forceinline__ void process_tile(const TileCoord& tc, const Tile& ti
       float y[4];
 #pragma unroll
       for (int i = 0; i < 4; ++i) y[i] = tile.value(p, i, j) * inv;
-      sm.tile[tile_index(ch * 8 + j, p * (kPassTokens / 4) + k)] =
-          fp8x4<kFmt>(y[0], y[1], y[2], y[3]);
+      const int quad = p * (kPassTokens / 4) + k;
+      if constexpr (kFmt == kE5M6) {
+        u32x2 w;
+        w.x = e5m6_pair(y[0], y[1]);
+        w.y = e5m6_pair(y[2], y[3]);
+        *reinterpret_cast<u32x2*>(&sm.tile[tile_index<TG::kRowDw>(ch * 8 + j, 2 * quad)]) = w;
+      } else if constexpr (kFmt == kE2M1) {
+        sm.tile[tile_index<TG::kRowDw>(ch * 8 + j, quad)] = e2m1_bytes4(y[0], y[1], y[2], y[3]);
+      } else {
+        sm.tile[tile_index<TG::kRowDw>(ch * 8 + j, quad)] = fp8x4<kFmt>(y[0], y[1], y[2], y[3]);
+      }
     }
   }
   __syncthreads();
 
-  // Read back channel rows, 16 bytes per lane, and store them to qT.
-  uint8_t* out = qT + (uint64_t)tc.c0 * rows + tc.t0;
+  // Read back channel rows, 16 bytes of LDS per lane (16 codes; 8 of E5M6),
+  // and store them to qT: 16 bytes of 8-bit codes, 8 of E2M1 nibbles, 12 of
+  // E5M6 codes.
+  const uint32_t row_bytes = code_bytes<kFmt>(rows);
+  uint8_t* out = qT + (uint64_t)tc.c0 * row_bytes + code_bytes<kFmt>(tc.t0);
 #pragma unroll
-  for (int r = 0; r < kReadPasses; ++r) {
+  for (int r = 0; r < TG::kReadPasses; ++r) {
     const int idx = t + r * kThreads;
-    const int c = idx / kRowVec;
-    const int mv = idx % kRowVec;
-    if (c < tc.nc && mv * 16 < tc.ng * kGroupTokens) {
-      const u32x4 val = *reinterpret_cast<const u32x4*>(&sm.tile[tile_index(c, 4 * mv)]);
-      store_stream(reinterpret_cast<u32x4*>(out + (uint32_t)c * rows + mv * 16), val);
+    const int c = idx / TG::kRowVec;
+    const int mv = idx % TG::kRowVec;
+    if (c < tc.nc && mv * TG::kVecTokens < tc.ng * kGroupTokens) {
+      const u32x4 val =
+          *reinterpret_cast<const u32x4*>(&sm.tile[tile_index<TG::kRowDw>(c, 4 * mv)]);
+      uint8_t* dst = out + (uint32_t)c * row_bytes + code_bytes<kFmt>(mv * TG::kVecTokens);
+      if constexpr (kFmt == kE5M6) {
+        const E5M6x8 e = e5m6_pack_pairs(val.x, val.y, val.z, val.w);
+        uint32_t* d32 = reinterpret_cast<uint32_t*>(dst);
+        store_stream(d32, e.w0);
+        store_stream(d32 + 1, e.w1);
+        store_stream(d32 + 2, e.w2);
+      } else if constexpr (kFmt == kE2M1) {
+        u32x2 o;
+        o.x = e2m1_pack_bytes(val.x) | (e2m1_pack_bytes(val.y) << 16);
+        o.y = e2m1_pack_bytes(val.z) | (e2m1_pack_bytes(val.w) << 16);
+        store_stream(reinterpret_cast<u32x2*>(dst), o);
+      } else {
+        store_stream(reinterpret_cast<u32x4*>(dst), val);
+      }
     }
   }
   if (kReuse) __syncthreads();  // the LDS tile is reused by the next tile
@@ -349,13 +408,13 @@ __device__ __forceinline__ void process_tile(const TileCoord& tc, const Tile& ti
 template <int kFmt>
 __global__ __launch_bounds__(kThreads) void per_channel_t_kernel(
     const uint16_t* __restrict__ x, uint32_t rows, uint32_t cols, uint32_t ngroups,
-    uint32_t nct, uint32_t ntiles, uint32_t per_xcd, float floor, uint8_t* __restrict__ qT,
-    float* __restrict__ sf) {
-  __shared__ __attribute__((aligned(16))) Smem sm;
+    uint32_t nct, uint32_t ntg, uint32_t ntiles, uint32_t per_xcd, FastDiv sdiv, float floor,
+    uint8_t* __restrict__ qT, float* __restrict__ sf) {
+  __shared__ __attribute__((aligned(16))) Smem<kFmt> sm;
   const uint32_t b = blockIdx.x;
   const uint32_t tau = (kOrder & 2) ? b : (b % kXcds) * per_xcd + b / kXcds;
   if (tau >= ntiles) return;
-  const TileCoord tc = tile_coord(tau, ngroups, cols, nct, ntiles / nct);
+  const TileCoord tc = tile_coord(tau, ngroups, cols, nct, ntg, sdiv);
   Bf16Tile tile;
   load_tile(x, cols, tc, tile.raw);
   process_tile<kFmt, false>(tc, tile, rows, ngroups, floor, sm, qT, sf);
@@ -367,12 +426,13 @@ __global__ __launch_bounds__(kThreads) void per_channel_t_kernel(
 // exactly one store), with no scale, code or LDS work.
 __global__ __launch_bounds__(kThreads) void per_channel_t_traffic_kernel(
     const uint16_t* __restrict__ x, uint32_t rows, uint32_t cols, uint32_t ngroups,
-    uint32_t nct, uint32_t ntiles, uint32_t per_xcd, uint8_t* __restrict__ qT) {
+    uint32_t nct, uint32_t ntg, uint32_t ntiles, uint32_t per_xcd, FastDiv sdiv,
+    uint8_t* __restrict__ qT) {
   static_assert(kPasses * 4 == 2 * kReadPasses, "two loaded vectors per stored one");
   const uint32_t b = blockIdx.x;
   const uint32_t tau = (kOrder & 2) ? b : (b % kXcds) * per_xcd + b / kXcds;
   if (tau >= ntiles) return;
-  const TileCoord tc = tile_coord(tau, ngroups, cols, nct, ntiles / nct);
+  const TileCoord tc = tile_coord(tau, ngroups, cols, nct, ntg, sdiv);
   u32x4 raw[kPasses][4];
   load_tile(x, cols, tc, raw);
   const int t = threadIdx.x;
@@ -399,16 +459,16 @@ __global__ __launch_bounds__(kThreads) void per_channel_t_traffic_kernel(
 template <int kFmt, bool kWeighted, bool kClamp, int kCount>
 __global__ __launch_bounds__(kThreads) void swiglu_per_channel_t_kernel(
     const uint16_t* __restrict__ h, const float* __restrict__ w, uint32_t rows, uint32_t cols,
-    uint32_t ngroups, uint32_t nct, uint32_t ntiles, uint32_t per_xcd, uint32_t vgrid,
-    float floor, float clamp, unsigned long long* __restrict__ count,
+    uint32_t ngroups, uint32_t nct, uint32_t ntg, uint32_t ntiles, uint32_t per_xcd,
+    FastDiv sdiv, uint32_t vgrid, float floor, float clamp, unsigned long long* __restrict__ count,
     unsigned long long* __restrict__ slots, uint8_t* __restrict__ qT, float* __restrict__ sf) {
-  __shared__ __attribute__((aligned(16))) Smem sm;
+  __shared__ __attribute__((aligned(16))) Smem<kFmt> sm;
   if constexpr (kCount == kCountDirect) {
     uint32_t n = 0;
     for (uint32_t b = blockIdx.x; b < vgrid; b += gridDim.x) {
       const uint32_t tau = (kOrder & 2) ? b : (b % kXcds) * per_xcd + b / kXcds;
       if (tau >= ntiles) continue;  // uniform over the workgroup
-      const TileCoord tc = tile_coord<kSwStrip>(tau, ngroups, cols, nct, ntiles / nct);
+      const TileCoord tc = tile_coord<kSwStrip>(tau, ngroups, cols, nct, ntg, sdiv);
       F32Tile tile;
       n += load_swiglu_tile<kWeighted, kClamp, true>(h, w, cols, clamp, tc, tile);
       process_tile<kFmt, true>(tc, tile, rows, ngroups, floor, sm, qT, sf);
@@ -419,7 +479,7 @@ __global__ __launch_bounds__(kThreads) void swiglu_per_channel_t_kernel(
     const uint32_t tau = (kOrder & 2) ? b : (b % kXcds) * per_xcd + b / kXcds;
     uint32_t n = 0;
     if (tau < ntiles) {  // uniform over the workgroup
-      const TileCoord tc = tile_coord<kSwStrip>(tau, ngroups, cols, nct, ntiles / nct);
+      const TileCoord tc = tile_coord<kSwStrip>(tau, ngroups, cols, nct, ntg, sdiv);
       F32Tile tile;
       n = load_swiglu_tile<kWeighted, kClamp, kCount == kCountSlotted>(h, w, cols, clamp, tc,
                                                                         tile);
@@ -430,23 +490,29 @@ __global__ __launch_bounds__(kThreads) void swiglu_per_channel_t_kernel(
 }
 
 struct Grid {
-  uint32_t ngroups, nct, ntiles, per_xcd, grid;
+  uint32_t ngroups, nct, ntg, ntiles, per_xcd, grid;
+  FastDiv strip_div, sw_strip_div;   // by kStrip * ntg, kSwStrip * ntg
 };
 
 // Tile counts of a [rows, cols] cast; false when the kernels' 32-bit tile
-// and in-tile offsets would not hold (row_stride: elements between rows).
-bool make_grid(int64_t rows, int64_t cols, int64_t row_stride, Grid* g) {
+// and in-tile offsets would not hold (row_stride: elements between rows; a
+// tile's qT rows are kChannels code rows of `rows` codes of fmt).
+bool make_grid(int64_t rows, int64_t cols, int64_t row_stride, int fmt, Grid* g) {
   const int64_t ngroups = rows / kGroupTokens;
   const int64_t ntg = (ngroups + kTG - 1) / kTG;
   const int64_t nct = (cols + kChannels - 1) / kChannels;
   const int64_t ntiles = ntg * nct;
   const int64_t lim = int64_t(1) << 31;
   if (ntiles + 2 * kXcds >= lim || (int64_t)kTileTokens * row_stride >= lim ||
-      (int64_t)kChannels * rows >= lim || rows >= lim || row_stride >= lim)
+      (int64_t)kChannels * rows >= lim || rows >= lim || row_stride >= lim ||
+      (fmt == kE5M6 && (int64_t)kChannels * (rows / 2 * 3) >= lim))
     return false;
   const int64_t per_xcd = (ntiles + kXcds - 1) / kXcds;
   g->ngroups = (uint32_t)ngroups;
   g->nct = (uint32_t)nct;
+  g->ntg = (uint32_t)ntg;
+  g->strip_div = make_fast_div((uint32_t)(kStrip * ntg > 0 ? kStrip * ntg : 1));
+  g->sw_strip_div = make_fast_div((uint32_t)(kSwStrip * ntg > 0 ? kSwStrip * ntg : 1));
   g->ntiles = (uint32_t)ntiles;
   g->per_xcd = (uint32_t)per_xcd;
   g->grid = (uint32_t)((kOrder & 2) ? ntiles : per_xcd * kXcds);
@@ -478,7 +544,7 @@ hipError_t launch_swiglu_t(const uint16_t* h, const float* w, int64_t rows, int6
     if (ca.count && slotted) {
       launch_kernel((swiglu_per_channel_t_kernel<kFmt, kWeighted, true, kCountSlotted>),
                     dim3(g.grid), dim3(kThreads), 0, stream, h, w, (uint32_t)rows,
-                    (uint32_t)cols, g.ngroups, g.nct, g.ntiles, g.per_xcd, g.grid, floor, clamp,
+                    (uint32_t)cols, g.ngroups, g.nct, g.ntg, g.ntiles, g.per_xcd, g.sw_strip_div, g.grid, floor, clamp,
                     ca.count, ca.slots, qT, sf);
       return hipGetLastError();
     }
@@ -488,14 +554,14 @@ hipError_t launch_swiglu_t(const uint16_t* h, const float* w, int64_t rows, int6
       if (QCAST_PC_COUNT_WG_PER_CU > 0 && cap < grid) grid = (uint32_t)cap;
       launch_kernel((swiglu_per_channel_t_kernel<kFmt, kWeighted, true, kCountDirect>),
                     dim3(grid), dim3(kThreads), 0, stream, h, w, (uint32_t)rows,
-                    (uint32_t)cols, g.ngroups, g.nct, g.ntiles, g.per_xcd, g.grid, floor, clamp,
+                    (uint32_t)cols, g.ngroups, g.nct, g.ntg, g.ntiles, g.per_xcd, g.sw_strip_div, g.grid, floor, clamp,
                     ca.count, ca.slots, qT, sf);
       return hipGetLastError();
     }
   }
   launch_kernel((swiglu_per_channel_t_kernel<kFmt, kWeighted, kClamp, kCountNone>),
                 dim3(g.grid), dim3(kThreads), 0, stream, h, w, (uint32_t)rows, (uint32_t)cols,
-                g.ngroups, g.nct, g.ntiles, g.per_xcd, g.grid, floor, clamp, ca.count, ca.slots,
+                g.ngroups, g.nct, g.ntg, g.ntiles, g.per_xcd, g.sw_strip_div, g.grid, floor, clamp, ca.count, ca.slots,
                 qT, sf);
   return hipGetLastError();
 }
@@ -521,40 +587,40 @@ hipError_t launch_swiglu_t_fmt(const uint16_t* h, const float* w, int64_t rows, 
 
 }  // namespace
 
-bool per_channel_t_fits(int64_t rows, int64_t cols, int64_t row_stride) {
+bool per_channel_t_fits(int64_t rows, int64_t cols, int64_t row_stride, int fmt) {
   Grid g;
-  return make_grid(rows, cols, row_stride, &g);
+  return make_grid(rows, cols, row_stride, fmt, &g);
 }
 
 hipError_t launch_per_channel_T(const void* x, int64_t rows, int64_t cols, int fmt, float floor,
                                 void* qT, float* sf, hipStream_t stream,
                                 const LaunchCaps& caps) {
   (void)caps;
-  // E2M1 and E5M6 runs of tokens are not whole bytes per lane of this tile:
-  // the register-transpose kernel (per_channel_t_wave.hip) casts them.
-  if (fmt == kE2M1 || fmt == kE5M6 || kWaveFp8)
-    return launch_per_channel_T_wave(x, rows, cols, fmt, floor, qT, sf, stream);
   Grid g;
   // The kernels index tiles, and offsets inside a tile's rows, in 32 bits.
-  if (!make_grid(rows, cols, cols, &g)) return hipErrorInvalidValue;
+  if (!make_grid(rows, cols, cols, fmt, &g)) return hipErrorInvalidValue;
   if (g.ntiles == 0) return hipSuccess;
-  auto kernel = fmt == kE4M3 ? per_channel_t_kernel<kE4M3>
-               : fmt == kE5M2 ? per_channel_t_kernel<kE5M2> : nullptr;
+  auto kernel = fmt == kE4M3   ? per_channel_t_kernel<kE4M3>
+                : fmt == kE5M2 ? per_channel_t_kernel<kE5M2>
+                : fmt == kE2M1 ? per_channel_t_kernel<kE2M1>
+                : fmt == kE5M6 ? per_channel_t_kernel<kE5M6>
+                               : nullptr;
   if (!kernel) return hipErrorInvalidValue;
   launch_kernel(kernel, dim3(g.grid), dim3(kThreads), 0, stream,
                 static_cast<const uint16_t*>(x), (uint32_t)rows, (uint32_t)cols, g.ngroups,
-                g.nct, g.ntiles, g.per_xcd, floor, static_cast<uint8_t*>(qT), sf);
+                g.nct, g.ntg, g.ntiles, g.per_xcd, g.strip_div, floor,
+                static_cast<uint8_t*>(qT), sf);
   return hipGetLastError();
 }
 
 hipError_t launch_per_channel_T_traffic(const void* x, int64_t rows, int64_t cols, void* qT,
                                         hipStream_t stream) {
   Grid g;
-  if (!make_grid(rows, cols, cols, &g)) return hipErrorInvalidValue;
+  if (!make_grid(rows, cols, cols, kE4M3, &g)) return hipErrorInvalidValue;
   if (g.ntiles == 0) return hipSuccess;
   launch_kernel(per_channel_t_traffic_kernel, dim3(g.grid), dim3(kThreads), 0, stream,
                 static_cast<const uint16_t*>(x), (uint32_t)rows, (uint32_t)cols, g.ngroups,
-                g.nct, g.ntiles, g.per_xcd, static_cast<uint8_t*>(qT));
+                g.nct, g.ntg, g.ntiles, g.per_xcd, g.strip_div, static_cast<uint8_t*>(qT));
   return hipGetLastError();
 }
 
@@ -563,21 +629,26 @@ hipError_t launch_swiglu_per_channel_T(const void* h, int64_t rows, int64_t cols
                                        unsigned long long* clamp_count,
                                        unsigned long long* count_ws, void* qT, float* sf,
                                        hipStream_t stream, const LaunchCaps& caps) {
-  if (fmt == kE2M1 || fmt == kE5M6 || kWaveFp8)
-    return launch_swiglu_per_channel_T_wave(h, rows, cols, w, fmt, floor, swiglu_clamp,
-                                            clamp_count, count_ws, qT, sf, stream, caps);
   Grid g;
-  if (!make_grid(rows, cols, 2 * cols, &g)) return hipErrorInvalidValue;
+  if (!make_grid(rows, cols, 2 * cols, fmt, &g)) return hipErrorInvalidValue;
   if (g.ntiles == 0) return hipSuccess;
   const uint16_t* hp = static_cast<const uint16_t*>(h);
   uint8_t* qp = static_cast<uint8_t*>(qT);
   const CountArgs ca{clamp_count, count_ws};
-  if (fmt == kE4M3)
-    return launch_swiglu_t_fmt<kE4M3>(hp, w, rows, cols, g, floor, swiglu_clamp, ca, qp, sf,
-                                      stream, caps);
-  if (fmt == kE5M2)
-    return launch_swiglu_t_fmt<kE5M2>(hp, w, rows, cols, g, floor, swiglu_clamp, ca, qp, sf,
-                                      stream, caps);
+  switch (fmt) {
+    case kE4M3:
+      return launch_swiglu_t_fmt<kE4M3>(hp, w, rows, cols, g, floor, swiglu_clamp, ca, qp, sf,
+                                        stream, caps);
+    case kE5M2:
+      return launch_swiglu_t_fmt<kE5M2>(hp, w, rows, cols, g, floor, swiglu_clamp, ca, qp, sf,
+                                        stream, caps);
+    case kE2M1:
+      return launch_swiglu_t_fmt<kE2M1>(hp, w, rows, cols, g, floor, swiglu_clamp, ca, qp, sf,
+                                        stream, caps);
+    case kE5M6:
+      return launch_swiglu_t_fmt<kE5M6>(hp, w, rows, cols, g, floor, swiglu_clamp, ca, qp, sf,
+                                        stream, caps);
+  }
   return hipErrorInvalidValue;
 }
 

@@ -293,8 +293,7 @@ int qcast_swiglu_per_channel_T(const void* h, int64_t rows, int64_t cols, const 
   if (!any_fmt(fmt)) return QCAST_ERR_FORMAT;
   if (group != 128) return QCAST_ERR_GROUP;
   if (rows < 0 || cols < 0 || rows % group != 0 || cols % 8 != 0 || too_big(rows, 2 * cols) ||
-      !qcast::per_channel_t_fits(rows, cols, 2 * cols) ||
-      !qcast::per_channel_t_wave_fits(rows, cols, 2 * cols, fmt, true))
+      !qcast::per_channel_t_fits(rows, cols, 2 * cols, fmt))
     return QCAST_ERR_SHAPE;
   if (swiglu_clamp != swiglu_clamp) return QCAST_ERR_VALUE;
   if (!clamp_min_ok(clamp_min)) return QCAST_ERR_VALUE;
@@ -344,8 +343,7 @@ int qcast_per_channel_T(const void* x, int64_t rows, int64_t cols, int fmt, int 
   if (!any_fmt(fmt)) return QCAST_ERR_FORMAT;
   if (group != 128) return QCAST_ERR_GROUP;
   if (rows < 0 || cols < 0 || rows % group != 0 || cols % 8 != 0 || too_big(rows, cols) ||
-      !qcast::per_channel_t_fits(rows, cols, cols) ||
-      !qcast::per_channel_t_wave_fits(rows, cols, cols, fmt, false))
+      !qcast::per_channel_t_fits(rows, cols, cols, fmt))
     return QCAST_ERR_SHAPE;
   if (!clamp_min_ok(clamp_min)) return QCAST_ERR_VALUE;
   if (rows == 0 || cols == 0) return QCAST_OK;

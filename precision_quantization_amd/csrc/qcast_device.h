@@ -204,12 +204,52 @@ __device__ __forceinline__ float lane_group_max(float m) {
   return __uint_as_float(b);
 }
 
+// Maxima with the lane 16 (or 32) lanes away, lane i with lane i ^ 16 (i ^ 32),
+// through gfx950's v_permlane16_swap / v_permlane32_swap (no LDS round trip,
+// unlike ds_bpermute). Each swap returns the two halves it exchanged; at every
+// lane one of them is the lane's own value and the other its partner's, so
+// their maximum is the pair's maximum whichever half is which.
+__device__ __forceinline__ uint32_t max_xor16(uint32_t v) {
+  const auto r = __builtin_amdgcn_permlane16_swap(v, v, false, false);
+  return umax((uint32_t)r[0], (uint32_t)r[1]);
+}
+__device__ __forceinline__ uint32_t max_xor32(uint32_t v) {
+  const auto r = __builtin_amdgcn_permlane32_swap(v, v, false, false);
+  return umax((uint32_t)r[0], (uint32_t)r[1]);
+}
+// The same on two packed 16-bit magnitudes (v_pk_max_u16).
+__device__ __forceinline__ uint32_t pk_max_xor16(uint32_t v) {
+  const auto r = __builtin_amdgcn_permlane16_swap(v, v, false, false);
+  return pk_umax16((uint32_t)r[0], (uint32_t)r[1]);
+}
+__device__ __forceinline__ uint32_t pk_max_xor32(uint32_t v) {
+  const auto r = __builtin_amdgcn_permlane32_swap(v, v, false, false);
+  return pk_umax16((uint32_t)r[0], (uint32_t)r[1]);
+}
+
 // Max over the whole wave64 of a non-negative value; every lane gets it.
 __device__ __forceinline__ float wave_max(float m) {
   uint32_t b = __float_as_uint(lane_group_max<16>(m));
-  b = umax(b, (uint32_t)__shfl_xor((int)b, 16));
-  b = umax(b, (uint32_t)__shfl_xor((int)b, 32));
+  b = max_xor16(b);
+  b = max_xor32(b);
   return __uint_as_float(b);
+}
+
+// Quotient of n < 2^31 by a divisor d in [1, 2^31) fixed for a launch, as a
+// multiply and a shift (host-computed: s = 31 + ceil(log2 d), m =
+// ceil(2^s / d) < 2^32; then floor(n / d) = (n * m) >> s for every n < 2^31).
+struct FastDiv {
+  uint32_t m, s;
+};
+inline FastDiv make_fast_div(uint32_t d) {
+  uint32_t l = 0;
+  while ((uint64_t(1) << l) < d) ++l;   // ceil(log2 d)
+  const uint32_t s = 31 + l;
+  const uint64_t m = ((uint64_t(1) << s) + d - 1) / d;
+  return FastDiv{(uint32_t)m, s};
+}
+__device__ __forceinline__ uint32_t fast_div(uint32_t n, FastDiv f) {
+  return (uint32_t)(((uint64_t)n * f.m) >> f.s);
 }
 
 // Four fp32 -> four E4M3 bytes (v0 in the lowest byte).
@@ -229,6 +269,23 @@ template <int kFmt>
 __device__ __forceinline__ uint32_t fp8x4(float v0, float v1, float v2, float v3) {
   static_assert(kFmt == kE4M3 || kFmt == kE5M2, "8-bit formats only");
   return kFmt == kE4M3 ? e4m3x4(v0, v1, v2, v3) : e5m2x4(v0, v1, v2, v3);
+}
+
+// Four fp32 -> four E2M1 codes, one per byte (v0 in the lowest byte, the
+// high nibble of each byte zero: the code of +0).
+__device__ __forceinline__ uint32_t e2m1_bytes4(float v0, float v1, float v2, float v3) {
+  uint32_t w = 0u;
+  w = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(w, v0, 0.0f, 1.0f, 0);
+  w = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(w, v1, 0.0f, 1.0f, 1);
+  w = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(w, v2, 0.0f, 1.0f, 2);
+  w = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(w, v3, 0.0f, 1.0f, 3);
+  return w;
+}
+
+// Four one-per-byte E2M1 codes -> four nibbles in the low 16 bits (byte i's
+// code in nibble i).
+__device__ __forceinline__ uint32_t e2m1_pack_bytes(uint32_t w) {
+  return (w & 0xFu) | ((w >> 4) & 0xF0u) | ((w >> 8) & 0xF00u) | ((w >> 12) & 0xF000u);
 }
 
 // Eight fp32 -> eight E2M1 nibbles (v0 in the lowest nibble).
@@ -359,9 +416,10 @@ __device__ __forceinline__ uint32_t e5m6_pair(float y0, float y1) {
 struct E5M6x8 {
   uint32_t w0, w1, w2;
 };
-__device__ __forceinline__ E5M6x8 e5m6x8(const float y[8]) {
-  const uint32_t p0 = e5m6_pair(y[0], y[1]), p1 = e5m6_pair(y[2], y[3]);
-  const uint32_t p2 = e5m6_pair(y[4], y[5]), p3 = e5m6_pair(y[6], y[7]);
+// Eight E5M6 codes held two per dword (bits 0..11 and 16..27, as e5m6_pair
+// returns them) -> their 96-bit stream.
+__device__ __forceinline__ E5M6x8 e5m6_pack_pairs(uint32_t p0, uint32_t p1, uint32_t p2,
+                                                  uint32_t p3) {
   // p = c_even | c_odd << 16 -> c_even | c_odd << 12 (24 bits)
   const uint32_t t0 = (p0 & 0xfffu) | ((p0 >> 4) & 0xfff000u);
   const uint32_t t1 = (p1 & 0xfffu) | ((p1 >> 4) & 0xfff000u);
@@ -372,6 +430,10 @@ __device__ __forceinline__ E5M6x8 e5m6x8(const float y[8]) {
   p.w1 = (t1 >> 8) | (t2 << 16);
   p.w2 = (t2 >> 16) | (t3 << 8);
   return p;
+}
+__device__ __forceinline__ E5M6x8 e5m6x8(const float y[8]) {
+  return e5m6_pack_pairs(e5m6_pair(y[0], y[1]), e5m6_pair(y[2], y[3]), e5m6_pair(y[4], y[5]),
+                         e5m6_pair(y[6], y[7]));
 }
 
 // Streaming accesses: the data is touched once.

@@ -32,7 +32,7 @@ inline void launch_kernel(void (*kernel)(KArgs...), dim3 grid, dim3 block, uint3
 // Whether a shape fits the kernels' 32-bit tile counts and in-tile offsets
 // (checked by the C ABI before any HIP call; the launchers check again).
 bool per_block_fits(int64_t rows, int64_t cols);
-bool per_channel_t_fits(int64_t rows, int64_t cols, int64_t row_stride);
+bool per_channel_t_fits(int64_t rows, int64_t cols, int64_t row_stride, int fmt);
 bool per_channel_fits(int64_t rows, int64_t cols);
 bool cast_back_fits(int64_t rows, int64_t cols);
 
@@ -100,20 +100,6 @@ hipError_t launch_swiglu_per_channel_T(const void* h, int64_t rows, int64_t cols
                                        unsigned long long* clamp_count,
                                        unsigned long long* count_ws, void* qT, float* sf,
                                        hipStream_t stream, const LaunchCaps& caps);
-
-// The transposed per-channel casts with the transpose in registers (one wave
-// per tile), for every format: qT holds one code row of `rows` codes per
-// channel. The shape limits of their 32-bit tile counts and offsets (swiglu:
-// the SwiGLU form, whose input rows are row_stride = 2 * cols apart).
-bool per_channel_t_wave_fits(int64_t rows, int64_t cols, int64_t row_stride, int fmt,
-                             bool swiglu);
-hipError_t launch_per_channel_T_wave(const void* x, int64_t rows, int64_t cols, int fmt,
-                                     float floor, void* qT, float* sf, hipStream_t stream);
-hipError_t launch_swiglu_per_channel_T_wave(const void* h, int64_t rows, int64_t cols,
-                                            const float* w, int fmt, float floor,
-                                            float swiglu_clamp, unsigned long long* clamp_count,
-                                            unsigned long long* count_ws, void* qT, float* sf,
-                                            hipStream_t stream, const LaunchCaps& caps);
 
 // x [rows (tokens), cols (channels)] bf16 -> q [rows, cols] 8-bit codes in the
 // input layout + sf [rows/128, cols]; rows % 128 == 0, cols % 8 == 0.
