@@ -94,6 +94,75 @@ __global__ __launch_bounds__(kThreads) void per_token_kernel(
   }
 }
 
+// fp32 column-major scales with 1 x 32 groups: sf[group][row] puts a row's
+// scales 4 * rows_pad bytes apart and a workgroup of the flat walk covers
+// less than a row, so every scale would leave as a lone 4-byte store (the
+// cast 20% slower than with row-major scales). Here workgroup b casts a tile
+// of kCmRows rows x kCmSpan chunks (two chunks per lane), parks the tile's
+// scales in LDS and writes each group column's kCmRows consecutive rows as
+// one 128-byte run. Tiles walk the chunk columns fastest; the bottom and
+// right tiles may be partial, always in whole groups (cols % 32 == 0).
+constexpr int kCmSpan = 16;                          // chunks per tile row
+constexpr int kCmRows = 2 * kThreads / kCmSpan;      // 32 rows
+
+template <int kFmt>
+__global__ __launch_bounds__(kThreads) void per_token_cm32_kernel(
+    const u32x4* __restrict__ x, uint32_t rows, uint32_t cpr, uint32_t col_tiles, float floor,
+    uint8_t* __restrict__ q, float* __restrict__ sf, SfLayout lay) {
+  constexpr int kLanes = 4;                          // lanes per 32-group
+  constexpr int kGroupCols = kCmSpan / kLanes;
+  __shared__ float tile_sf[kGroupCols][kCmRows];
+  const uint32_t rt = blockIdx.x / col_tiles;
+  const uint32_t ct = blockIdx.x - rt * col_tiles;
+  const uint32_t row0 = rt * kCmRows, c0 = ct * kCmSpan;
+  const uint32_t nrows = rows - row0 < (uint32_t)kCmRows ? rows - row0 : (uint32_t)kCmRows;
+  const uint32_t nspan = cpr - c0 < (uint32_t)kCmSpan ? cpr - c0 : (uint32_t)kCmSpan;
+  u32x4 raw[2];
+#pragma unroll
+  for (int u = 0; u < 2; ++u) {
+    const uint32_t l = threadIdx.x + u * kThreads;
+    const uint32_t tr = l / kCmSpan, tc = l % kCmSpan;
+    if (tr < nrows && tc < nspan) raw[u] = load_stream(x + ((int64_t)(row0 + tr) * cpr + c0 + tc));
+  }
+#pragma unroll
+  for (int u = 0; u < 2; ++u) {
+    const uint32_t l = threadIdx.x + u * kThreads;
+    const uint32_t tr = l / kCmSpan, tc = l % kCmSpan;
+    // a group's 4 lanes share tr and are all inside or all outside
+    if (tr < nrows && tc < nspan) {
+      float v[8];
+      unpack8(raw[u], v);
+      const float amax = lane_group_max<kLanes>(absmax8(v));
+      Scale s = group_scale<kFmt>(amax, floor);
+      if (lay.flags & kSfRound) s = round_scale_pow2(s);
+#pragma unroll
+      for (int i = 0; i < 8; ++i) v[i] = v[i] * s.inv;
+      store_chunk8<kFmt>(q, (int64_t)(row0 + tr) * cpr + c0 + tc, v);
+      if ((threadIdx.x & (kLanes - 1)) == 0) tile_sf[tc / kLanes][tr] = s.sf;
+    }
+  }
+  __syncthreads();
+  // group column gc of the tile: kCmRows consecutive rows from consecutive lanes
+  const uint32_t gc = threadIdx.x / kCmRows, r = threadIdx.x % kCmRows;
+  if (gc < (uint32_t)kGroupCols && gc * kLanes < nspan && r < nrows)
+    sf[(size_t)(c0 / kLanes + gc) * lay.rows_pad + row0 + r] = tile_sf[gc][r];
+}
+
+template <int kFmt>
+hipError_t launch_cm32(const void* x, int64_t rows, int64_t cols, float floor, void* q, void* sf,
+                       const SfLayout& lay, hipStream_t stream) {
+  const int64_t cpr = cols / 8;
+  const int64_t col_tiles = (cpr + kCmSpan - 1) / kCmSpan;
+  const int64_t blocks = (rows + kCmRows - 1) / kCmRows * col_tiles;
+  if (blocks >= (int64_t(1) << 31) || rows >= (int64_t(1) << 31) || cpr >= (int64_t(1) << 31))
+    return hipErrorInvalidValue;
+  launch_kernel(per_token_cm32_kernel<kFmt>, dim3((unsigned)blocks), dim3(kThreads), 0, stream,
+                static_cast<const u32x4*>(x), (uint32_t)rows, (uint32_t)cpr,
+                (uint32_t)col_tiles, floor, static_cast<uint8_t*>(q), static_cast<float*>(sf),
+                lay);
+  return hipGetLastError();
+}
+
 template <int kLanes, int kFmt>
 hipError_t launch(const void* x, int64_t nchunks, float floor, void* q, void* sf,
                   const SfLayout& lay, hipStream_t stream, const LaunchCaps& caps) {
@@ -138,6 +207,15 @@ hipError_t launch_per_token(const void* x, int64_t rows, int64_t cols, int fmt, 
   if (nchunks == 0) return hipSuccess;
   if (rows * cols / group >= (int64_t(1) << 31)) return hipErrorInvalidValue;
   const SfLayout lay = make_sf_layout(rows, cols, group, sf_flags);
+  if (group == 32 && (lay.flags & kSfColMajor) && !(lay.flags & kSfPacked)) {
+    switch (fmt) {
+      case kE4M3: return launch_cm32<kE4M3>(x, rows, cols, floor, q, sf, lay, stream);
+      case kE2M1: return launch_cm32<kE2M1>(x, rows, cols, floor, q, sf, lay, stream);
+      case kE5M2: return launch_cm32<kE5M2>(x, rows, cols, floor, q, sf, lay, stream);
+      case kE5M6: return launch_cm32<kE5M6>(x, rows, cols, floor, q, sf, lay, stream);
+    }
+    return hipErrorInvalidValue;
+  }
   switch (fmt) {
     case kE4M3: return launch_fmt<kE4M3>(x, nchunks, group, floor, q, sf, lay, stream, caps);
     case kE2M1: return launch_fmt<kE2M1>(x, nchunks, group, floor, q, sf, lay, stream, caps);
