@@ -477,15 +477,21 @@ __global__ __launch_bounds__(kThreads) void swiglu_per_channel_t_kernel(
   } else {
     const uint32_t b = blockIdx.x;
     const uint32_t tau = (kOrder & 2) ? b : (b % kXcds) * per_xcd + b / kXcds;
+    const bool has_tile = tau < ntiles;  // uniform over the workgroup
     uint32_t n = 0;
-    if (tau < ntiles) {  // uniform over the workgroup
-      const TileCoord tc = tile_coord<kSwStrip>(tau, ngroups, cols, nct, ntg, sdiv);
-      F32Tile tile;
+    TileCoord tc{};
+    F32Tile tile;
+    if (has_tile) {
+      tc = tile_coord<kSwStrip>(tau, ngroups, cols, nct, ntg, sdiv);
       n = load_swiglu_tile<kWeighted, kClamp, kCount == kCountSlotted>(h, w, cols, clamp, tc,
                                                                         tile);
-      process_tile<kFmt, false>(tc, tile, rows, ngroups, floor, sm, qT, sf);
     }
-    if constexpr (kCount == kCountSlotted) add_wave_counts_slotted(n, slots, count);
+    // With a workspace the count goes to its slot before the tile is
+    // processed, so the slot atomic's round trip overlaps that work.
+    SlotCount<> sc;
+    if constexpr (kCount == kCountSlotted) sc.arrive(n, slots);
+    if (has_tile) process_tile<kFmt, false>(tc, tile, rows, ngroups, floor, sm, qT, sf);
+    if constexpr (kCount == kCountSlotted) sc.finish(slots, count);
   }
 }
 

@@ -87,6 +87,58 @@ __global__ __launch_bounds__(kBlock) void swiglu_kernel(
   const uint32_t n32 = (uint32_t)nchunks;
   const u32x4* h4 = reinterpret_cast<const u32x4*>(h);
   const uint32_t row_chunks = 2 * chunks_per_row;
+  if constexpr (kCount == kCountSlotted) {
+    // The grid covers the stream in one pass. The values come first, then
+    // the workgroup's count goes to its slot, and the slot atomic's round
+    // trip overlaps the codes and stores that follow.
+    const uint32_t base = blockIdx.x * kBlock * kUnroll + threadIdx.x;
+    u32x4 graw[kUnroll], uraw[kUnroll];
+    float wr[kUnroll];
+#pragma unroll
+    for (int u = 0; u < kUnroll; ++u) {
+      const uint32_t c = base + u * kBlock;
+      if (c < n32) {
+        const uint32_t row = (uint32_t)(((uint64_t)c * row_magic) >> 40);
+        const uint32_t gi = row * row_chunks + (c - row * chunks_per_row);
+        graw[u] = load_stream(h4 + gi);
+        uraw[u] = load_stream(h4 + (gi + chunks_per_row));
+        wr[u] = kWeighted ? w[row] : 1.0f;
+      }
+    }
+    float v[kUnroll][8];
+#pragma unroll
+    for (int u = 0; u < kUnroll; ++u) {
+      if (base + u * kBlock < n32) {
+        float gv[8], uv[8];
+        unpack8(graw[u], gv);
+        unpack8(uraw[u], uv);
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+          nclamp += wave_clamp_count(gv[i], uv[i], clamp);
+          clamp_gate_up(gv[i], uv[i], clamp);
+          v[u][i] = silu_times(gv[i], uv[i]);
+          if (kWeighted) v[u][i] = v[u][i] * wr[u];
+        }
+      }
+    }
+    SlotCount<kBlock> sc;
+    sc.arrive(nclamp, slots);
+#pragma unroll
+    for (int u = 0; u < kUnroll; ++u) {
+      const uint32_t c = base + u * kBlock;
+      if (c < n32) {
+        const float amax = lane_group_max<kLanes>(absmax8(v[u]));
+        Scale s = group_scale<kFmt>(amax, floor);
+        if (lay.flags & kSfRound) s = round_scale_pow2(s);
+#pragma unroll
+        for (int i = 0; i < 8; ++i) v[u][i] = v[u][i] * s.inv;
+        store_chunk8<kFmt>(q, c, v[u]);
+        store_group_scale<kLanes>(sf, group0 + c / kLanes, s, lay);
+      }
+    }
+    sc.finish(slots, count);
+    return;
+  }
   const uint32_t step = gridDim.x * kBlock * kUnroll;
   for (uint32_t base = blockIdx.x * kBlock * kUnroll + threadIdx.x; base < n32; base += step) {
     u32x4 graw[kUnroll], uraw[kUnroll];
@@ -128,7 +180,6 @@ __global__ __launch_bounds__(kBlock) void swiglu_kernel(
     }
   }
   if constexpr (kCount == kCountDirect) add_wave_counts<kBlock>(nclamp, count);
-  if constexpr (kCount == kCountSlotted) add_wave_counts_slotted<kBlock>(nclamp, slots, count);
 }
 
 struct ClampArgs {
