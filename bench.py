@@ -346,7 +346,7 @@ def extra_calls(wls, dev):
     return calls
 
 
-def time_extras(extras, dev, steps, warmup):
+def time_extras(extras, dev, steps, warmup, min_launches=10):
     import torch
     for _ in range(warmup):
         for *_, fn in extras:
@@ -355,7 +355,7 @@ def time_extras(extras, dev, steps, warmup):
     hev = HipEvents()
     # the same one-timed-launch-per-pass rotation as the step, over enough
     # passes to time every cast at least 10 times
-    passes = max(steps, 10 * len(extras))
+    passes = max(steps, min_launches * len(extras))
     ev = make_events(hev, len(extras), passes)
     timed_runs([fn for *_, fn in extras], ev)
     ms_all = collect(ev, hev)
@@ -456,7 +456,7 @@ def flushed_runs(fns, dev, runs=30):
     return [sorted(t) for t in out]
 
 
-def pattern_ceiling(dev, x):
+def pattern_ceiling(dev, x, runs=6):
     """The transposed per-channel cast against its memory traffic alone
     (include/qcast_bench.h: the same loads and qT stores, no arithmetic), on
     the cast's input x, the two alternating, each after a 1 GiB flush;
@@ -470,7 +470,7 @@ def pattern_ceiling(dev, x):
     flush = torch.empty(1 << 30, dtype=torch.uint8, device=dev)
     hev = HipEvents()
     times = ([], [])
-    for _ in range(6):
+    for _ in range(runs):
         for i in range(2):
             flush.fill_(0)
             a, b = hev.create(), hev.create()
@@ -558,6 +558,9 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-extras", action="store_true",
                     help="skip timing the casts that are not part of the step")
+    ap.add_argument("--profile-run", action="store_true",
+                    help="every kernel, each timing loop cut to a few launches: for the "
+                         "counter passes of rocprofv3, where every dispatch is slow")
     args = ap.parse_args()
     if args.steps < 1 or args.warmup < 0:
         ap.error("--steps must be at least 1 and --warmup at least 0")
@@ -596,7 +599,8 @@ def main():
     # steps in which kernel s mod n records events from its own dispatch,
     # enough of them for every kernel to be timed MIN_TIMED_LAUNCHES times
     hev = HipEvents()
-    rot_steps = max(args.steps, MIN_TIMED_LAUNCHES * len(fns))
+    min_launches = 0 if args.profile_run else MIN_TIMED_LAUNCHES
+    rot_steps = max(args.steps, min_launches * len(fns))
     log(f"bench: per-kernel timing over {rot_steps} steps")
     ev = make_events(hev, len(fns), rot_steps)
     timed_runs(fns, ev)
@@ -622,7 +626,8 @@ def main():
     # last copy of the run
     copy_nbytes = max(k["bytes"] for k in kernels.values())
     log("bench: copy ceilings (library copy and the runtime's hipMemcpyAsync)")
-    ceilings = copy_ceilings(dev, [k["bytes"] for k in kernels.values()])
+    reps = 2 if args.profile_run else None
+    ceilings = copy_ceilings(dev, [k["bytes"] for k in kernels.values()], runs=reps or 11)
     copy_gbs = ceilings[copy_nbytes]["library"]
     for k in kernels.values():
         c = ceilings[k["bytes"]]
@@ -630,7 +635,8 @@ def main():
         k["of_copy"] = round(k["GBps"] / c["library"], 4)
         k["runtime_copy_GBps"] = round(c["runtime_marker"], 1)
         k["library_copy_marker_GBps"] = round(c["library_marker"], 1)
-    for (name, wl, _), ms in zip(calls, flushed_runs([fn for _, _, fn in calls], dev)):
+    for (name, wl, _), ms in zip(calls, flushed_runs([fn for _, _, fn in calls], dev,
+                                                     runs=reps or 30)):
         k = kernels[name]
         sp = spread_us(ms)
         k["flushed"] = {"runs": len(ms), "median_us": sp["median_us"], "p10_us": sp["p10_us"],
@@ -638,7 +644,7 @@ def main():
                         "GBps": round(k["bytes"] / (sp["median_us"] * 1e-6) / 1e9, 1)}
     pt = kernels["per_channel_T"]
     pc_x = next(wl for name, wl in wls if name == "per_channel_T").x.to(dev)
-    pattern_us, flushed_us = pattern_ceiling(dev, pc_x)
+    pattern_us, flushed_us = pattern_ceiling(dev, pc_x, runs=reps or 6)
     pt["pattern_us"] = round(pattern_us, 2)
     pt["flushed_us"] = round(flushed_us, 2)
     pt["of_pattern"] = round(pattern_us / flushed_us, 4)
@@ -676,7 +682,8 @@ def main():
     if not args.no_extras:
         log("bench: timing the other casts")
         result["other_kernels"] = time_extras(extra_calls(wls, dev), dev, args.steps,
-                                              args.warmup)
+                                              args.warmup,
+                                              min_launches=0 if args.profile_run else 10)
     if not args.no_cpu_baseline:
         log("bench: CPU baseline (oracle)")
         gbs, secs = cpu_baseline(wls)

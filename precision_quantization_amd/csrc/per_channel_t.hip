@@ -385,17 +385,21 @@ __device__ __forceinline__ void process_tile(const TileCoord& tc, const Tile& ti
       const u32x4 val =
           *reinterpret_cast<const u32x4*>(&sm.tile[tile_index<TG::kRowDw>(c, 4 * mv)]);
       uint8_t* dst = out + (uint32_t)c * row_bytes + code_bytes<kFmt>(mv * TG::kVecTokens);
+      // A tile's run of packed codes per channel is 64 bytes (E2M1) or 192
+      // (E5M6), part of a 128-byte line whose other part a neighbouring tile
+      // writes: plain stores let the two meet in L2 and leave as whole lines
+      // (E2M1 on 16384 x 7168: 54.9 us against 57.3 with streaming stores).
       if constexpr (kFmt == kE5M6) {
         const E5M6x8 e = e5m6_pack_pairs(val.x, val.y, val.z, val.w);
         uint32_t* d32 = reinterpret_cast<uint32_t*>(dst);
-        store_stream(d32, e.w0);
-        store_stream(d32 + 1, e.w1);
-        store_stream(d32 + 2, e.w2);
+        d32[0] = e.w0;
+        d32[1] = e.w1;
+        d32[2] = e.w2;
       } else if constexpr (kFmt == kE2M1) {
         u32x2 o;
         o.x = e2m1_pack_bytes(val.x) | (e2m1_pack_bytes(val.y) << 16);
         o.y = e2m1_pack_bytes(val.z) | (e2m1_pack_bytes(val.w) << 16);
-        store_stream(reinterpret_cast<u32x2*>(dst), o);
+        *reinterpret_cast<u32x2*>(dst) = o;
       } else {
         store_stream(reinterpret_cast<u32x4*>(dst), val);
       }
