@@ -81,6 +81,13 @@ def _load():
                                              i32),
         "oracle_swiglu_per_channel_T": ([vp, i64, i64, vp, i32, i32, f32, f32, vp, vp], i32),
         "oracle_per_channel": ([vp, i64, i64, i32, i32, f32, vp, vp], i32),
+        "oracle_per_block_sf": ([vp, i64, i64, i32, i32, f32, i32, vp, vp], i32),
+        "oracle_per_channel_sf": ([vp, i64, i64, i32, i32, f32, i32, vp, vp], i32),
+        "oracle_per_channel_T_sf": ([vp, i64, i64, i32, i32, f32, i32, vp, vp], i32),
+        "oracle_swiglu_per_channel_T_sf": ([vp, i64, i64, vp, i32, i32, f32, i32, f32, vp, vp],
+                                           i32),
+        "oracle_swiglu_backward_per_token_sf": ([vp, vp, i64, i64, vp, i32, i32, f32, i32, f32,
+                                                 vp, vp], i32),
     }
     for name, (args, res) in sig.items():
         fn = getattr(lib, name)
@@ -405,4 +412,78 @@ def per_channel(x, fmt="e4m3", group=128, clamp_min=0.0):
     sf = np.zeros((rows // group if group > 0 else 0, cols), np.float32)
     _check(_load().oracle_per_channel(_ptr(x), rows, cols, f, group, clamp_min, _ptr(q), _ptr(sf)),
            "per_channel")
+    return q, sf
+
+
+def per_block_sf(x, fmt="e4m3", block=128, clamp_min=0.0, sf_flags=0):
+    """Per-block cast with round_sf (SF_ROUND_POW2, the one option it takes)."""
+    f = fmt_id(fmt)
+    x = _u16(x)
+    rows, cols = x.shape
+    q = np.zeros(_code_shape(f, rows, cols), np.uint8)
+    sf = np.zeros((rows // block, cols // block) if block > 0 else (0, 0), np.float32)
+    _check(_load().oracle_per_block_sf(_ptr(x), rows, cols, f, block, clamp_min, sf_flags, _ptr(q),
+                                       _ptr(sf)), "per_block_sf")
+    return q, sf
+
+
+def per_channel_sf(x, fmt="e4m3", group=128, clamp_min=0.0, sf_flags=0):
+    """Per-channel cast in the input layout with round_sf (SF_ROUND_POW2 only)."""
+    f = fmt_id(fmt)
+    x = _u16(x)
+    rows, cols = x.shape
+    q = np.zeros(_code_shape(f, rows, cols), np.uint8)
+    sf = np.zeros((rows // group if group > 0 else 0, cols), np.float32)
+    _check(_load().oracle_per_channel_sf(_ptr(x), rows, cols, f, group, clamp_min, sf_flags,
+                                         _ptr(q), _ptr(sf)), "per_channel_sf")
+    return q, sf
+
+
+def per_channel_T_sf(x, fmt="e4m3", group=128, clamp_min=0.0, sf_flags=0, sf_fill=0):
+    """Transposed per-channel cast with a scale layout: the per-token layout
+    of x^T (rows = the channels, groups = the token groups)."""
+    f = fmt_id(fmt)
+    x = _u16(x)
+    rows, cols = x.shape
+    qT = np.zeros(_code_shape(f, cols, rows), np.uint8)
+    shape, dt = sf_shape(cols, rows, group, sf_flags)
+    sf = np.full(shape, sf_fill, dt)
+    _check(_load().oracle_per_channel_T_sf(_ptr(x), rows, cols, f, group, clamp_min, sf_flags,
+                                           _ptr(qT), _ptr(sf)), "per_channel_T_sf")
+    return qT, sf
+
+
+def swiglu_per_channel_T_sf(h, w=None, fmt="e4m3", group=128, clamp_min=0.0, sf_flags=0,
+                            swiglu_clamp=0.0, sf_fill=0):
+    f = fmt_id(fmt)
+    h = _u16(h)
+    rows, two_n = h.shape
+    cols = two_n // 2
+    w = None if w is None else _f32(w)
+    qT = np.zeros(_code_shape(f, cols, rows), np.uint8)
+    shape, dt = sf_shape(cols, rows, group, sf_flags)
+    sf = np.full(shape, sf_fill, dt)
+    _check(_load().oracle_swiglu_per_channel_T_sf(_ptr(h), rows, cols, _ptr(w), f, group,
+                                                  clamp_min, sf_flags, swiglu_clamp, _ptr(qT),
+                                                  _ptr(sf)), "swiglu_per_channel_T_sf")
+    return qT, sf
+
+
+def swiglu_backward_per_token_sf(h, dv, w=None, fmt="e4m3", group=128, clamp_min=0.0,
+                                 sf_flags=0, swiglu_clamp=0.0, sf_fill=0):
+    """SwiGLU backward + per-token cast of [dg | du] with a scale layout over
+    rows of 2*cols values."""
+    f = fmt_id(fmt)
+    h = _u16(h)
+    dv = _u16(dv)
+    rows, two_n = h.shape
+    cols = two_n // 2
+    w = None if w is None else _f32(w)
+    q = np.zeros(_code_shape(f, rows, two_n), np.uint8)
+    shape, dt = sf_shape(rows, two_n, group, sf_flags)
+    sf = np.full(shape, sf_fill, dt)
+    _check(_load().oracle_swiglu_backward_per_token_sf(_ptr(h), _ptr(dv), rows, cols, _ptr(w), f,
+                                                       group, clamp_min, sf_flags, swiglu_clamp,
+                                                       _ptr(q), _ptr(sf)),
+           "swiglu_backward_per_token_sf")
     return q, sf

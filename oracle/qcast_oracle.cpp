@@ -55,7 +55,11 @@
  *    scales group-major with the row count padded to a multiple of 4 (16
  *    bytes of fp32 or of packed words); "packed UE8M0" stores each (power of
  *    two) scale as its biased exponent byte, 4 per 32-bit word along the
- *    groups of a row, lowest group in the lowest byte.
+ *    groups of a row, lowest group in the lowest byte. The transposed
+ *    per-channel casts write the layouts of the per-token cast of x^T (its
+ *    rows are the channels), the SwiGLU backward those of its rows
+ *    [dg | du]; the per-block and input-layout per-channel casts take
+ *    round_sf only (their scale arrays have no per-token row structure).
  *
  *  - the exponential in SiLU ([WALK] §3.3) is exp(-g) rounded once to the
  *    nearest fp32 value (exp_f32 below), so the SwiGLU forms are a fixed
@@ -456,9 +460,10 @@ void per_token_row_sf(const float* xr, int64_t r, int64_t rows, int64_t cols, in
 
 /* Per-channel cast of an fp32 matrix x [rows, cols]: groups of `group`
  * tokens of one channel. transposed: code of x[t][c] at q[c][t], scale at
- * sf[c][g]; otherwise at q[t][c] and sf[g][c]. */
+ * sf[c][g]; otherwise at q[t][c] and sf[g][c]. round: sf rounded up to a
+ * power of two (round_sf), codes from its inverse. */
 void per_channel_f32(const float* x, int64_t rows, int64_t cols, int fmt, int group, float floor,
-                     bool transposed, uint8_t* q, float* sf) {
+                     bool transposed, bool round, uint8_t* q, float* sf) {
   const FormatTable& t = *table_for(fmt);
   const int64_t groups = rows / group;
   for (int64_t c = 0; c < cols; ++c) {
@@ -468,7 +473,11 @@ void per_channel_f32(const float* x, int64_t rows, int64_t cols, int fmt, int gr
         const float m = std::fabs(x[tk * cols + c]);
         if (m > amax) amax = m;
       }
-      const Scale s = scale_from_amax(t, amax, floor);
+      Scale s = scale_from_amax(t, amax, floor);
+      if (round) {
+        s.sf = round_up_pow2(s.sf);
+        s.sf_inv = 1.0f / s.sf;
+      }
       for (int64_t tk = g * group; tk < (g + 1) * group; ++tk) {
         const uint16_t code = encode(t, x[tk * cols + c] * s.sf_inv);
         if (transposed) put_code(fmt, q, rows, c, tk, code);
@@ -503,6 +512,19 @@ int check_sf_flags(int flags, int64_t cols, int group) {
     return ORACLE_ERR_FORMAT;
   if ((flags & ORACLE_SF_PACKED_UE8M0) && (cols / group) % 4 != 0) return ORACLE_ERR_SHAPE;
   return ORACLE_OK;
+}
+
+/* The transposed per-channel cast with a scale layout is the per-token cast
+ * of x^T: channel c of the fp32 matrix x [rows, cols] is row c of x^T, a
+ * row of `rows` tokens, and the layout's rows are the channels. */
+void per_channel_T_sf_f32(const float* x, int64_t rows, int64_t cols, int fmt, int group,
+                          float floor, int flags, uint8_t* qT, void* sf) {
+  std::vector<float> col(static_cast<size_t>(rows));
+  const int64_t code_bytes = code_row_bytes(fmt, rows);
+  for (int64_t c = 0; c < cols; ++c) {
+    for (int64_t tk = 0; tk < rows; ++tk) col[tk] = x[tk * cols + c];
+    per_token_row_sf(col.data(), c, cols, rows, fmt, group, floor, flags, qT + c * code_bytes, sf);
+  }
 }
 
 } /* namespace */
@@ -655,8 +677,14 @@ int oracle_swiglu_per_token(const uint16_t* h, int64_t rows, int64_t cols, const
 
 int oracle_per_block(const uint16_t* x, int64_t rows, int64_t cols, int fmt, int block,
                      float clamp_min, uint8_t* q, float* sf) {
+  return oracle_per_block_sf(x, rows, cols, fmt, block, clamp_min, 0, q, sf);
+}
+
+int oracle_per_block_sf(const uint16_t* x, int64_t rows, int64_t cols, int fmt, int block,
+                        float clamp_min, int sf_flags, uint8_t* q, float* sf) {
   const int rc = check_common(x, q, sf, fmt, block);
   if (rc != ORACLE_OK) return rc;
+  if (sf_flags & ~ORACLE_SF_ROUND_POW2) return ORACLE_ERR_FORMAT;
   if (rows < 0 || cols < 0 || rows % block != 0 || cols % block != 0) return ORACLE_ERR_SHAPE;
   if (pairs(fmt) && block % 2 != 0) return ORACLE_ERR_GROUP;
   const FormatTable& t = *table_for(fmt);
@@ -670,7 +698,11 @@ int oracle_per_block(const uint16_t* x, int64_t rows, int64_t cols, int fmt, int
           const float m = std::fabs(bf16_value(x[r * cols + c]));
           if (m > amax) amax = m;
         }
-      const Scale s = scale_from_amax(t, amax, floor);
+      Scale s = scale_from_amax(t, amax, floor);
+      if (sf_flags & ORACLE_SF_ROUND_POW2) {
+        s.sf = round_up_pow2(s.sf);
+        s.sf_inv = 1.0f / s.sf;
+      }
       for (int64_t r = bi * block; r < (bi + 1) * block; ++r)
         for (int64_t c = bj * block; c < (bj + 1) * block; ++c) {
           const float y = bf16_value(x[r * cols + c]) * s.sf_inv;
@@ -691,7 +723,7 @@ int oracle_per_channel_T(const uint16_t* x, int64_t rows, int64_t cols, int fmt,
   std::vector<float> xf(static_cast<size_t>(rows * cols));
   for (int64_t i = 0; i < rows * cols; ++i) xf[i] = bf16_value(x[i]);
   per_channel_f32(xf.data(), rows, cols, fmt, group, floor_for(*table_for(fmt), clamp_min), true,
-                  qT, sf);
+                  false, qT, sf);
   return ORACLE_OK;
 }
 
@@ -704,7 +736,7 @@ int oracle_per_channel(const uint16_t* x, int64_t rows, int64_t cols, int fmt, i
   std::vector<float> xf(static_cast<size_t>(rows * cols));
   for (int64_t i = 0; i < rows * cols; ++i) xf[i] = bf16_value(x[i]);
   per_channel_f32(xf.data(), rows, cols, fmt, group, floor_for(*table_for(fmt), clamp_min), false,
-                  q, sf);
+                  false, q, sf);
   return ORACLE_OK;
 }
 
@@ -834,7 +866,70 @@ int oracle_swiglu_per_channel_T(const uint16_t* h, int64_t rows, int64_t cols, c
   std::vector<float> v(static_cast<size_t>(rows * cols));
   oracle_swiglu_values_ex(h, rows, cols, w, swiglu_clamp, v.data(), nullptr);
   per_channel_f32(v.data(), rows, cols, fmt, group, floor_for(*table_for(fmt), clamp_min), true,
-                  qT, sf);
+                  false, qT, sf);
+  return ORACLE_OK;
+}
+
+int oracle_per_channel_sf(const uint16_t* x, int64_t rows, int64_t cols, int fmt, int group,
+                          float clamp_min, int sf_flags, uint8_t* q, float* sf) {
+  const int rc = check_common(x, q, sf, fmt, group);
+  if (rc != ORACLE_OK) return rc;
+  if (sf_flags & ~ORACLE_SF_ROUND_POW2) return ORACLE_ERR_FORMAT;
+  if (rows < 0 || cols < 0 || rows % group != 0) return ORACLE_ERR_SHAPE;
+  if (pairs(fmt) && cols % 2 != 0) return ORACLE_ERR_SHAPE;
+  std::vector<float> xf(static_cast<size_t>(rows * cols));
+  for (int64_t i = 0; i < rows * cols; ++i) xf[i] = bf16_value(x[i]);
+  per_channel_f32(xf.data(), rows, cols, fmt, group, floor_for(*table_for(fmt), clamp_min), false,
+                  (sf_flags & ORACLE_SF_ROUND_POW2) != 0, q, sf);
+  return ORACLE_OK;
+}
+
+int oracle_per_channel_T_sf(const uint16_t* x, int64_t rows, int64_t cols, int fmt, int group,
+                            float clamp_min, int sf_flags, uint8_t* qT, void* sf) {
+  int rc = check_common(x, qT, sf, fmt, group);
+  if (rc != ORACLE_OK) return rc;
+  if (rows < 0 || cols < 0 || rows % group != 0) return ORACLE_ERR_SHAPE;
+  if (pairs(fmt) && group % 2 != 0) return ORACLE_ERR_GROUP;
+  if ((rc = check_sf_flags(sf_flags, rows, group)) != ORACLE_OK) return rc;
+  std::vector<float> xf(static_cast<size_t>(rows * cols));
+  for (int64_t i = 0; i < rows * cols; ++i) xf[i] = bf16_value(x[i]);
+  per_channel_T_sf_f32(xf.data(), rows, cols, fmt, group, floor_for(*table_for(fmt), clamp_min),
+                       sf_flags, qT, sf);
+  return ORACLE_OK;
+}
+
+int oracle_swiglu_per_channel_T_sf(const uint16_t* h, int64_t rows, int64_t cols, const float* w,
+                                   int fmt, int group, float clamp_min, int sf_flags,
+                                   float swiglu_clamp, uint8_t* qT, void* sf) {
+  int rc = check_common(h, qT, sf, fmt, group);
+  if (rc != ORACLE_OK) return rc;
+  if (rows < 0 || cols < 0 || rows % group != 0) return ORACLE_ERR_SHAPE;
+  if (pairs(fmt) && group % 2 != 0) return ORACLE_ERR_GROUP;
+  if ((rc = check_sf_flags(sf_flags, rows, group)) != ORACLE_OK) return rc;
+  std::vector<float> v(static_cast<size_t>(rows * cols));
+  oracle_swiglu_values_ex(h, rows, cols, w, swiglu_clamp, v.data(), nullptr);
+  per_channel_T_sf_f32(v.data(), rows, cols, fmt, group, floor_for(*table_for(fmt), clamp_min),
+                       sf_flags, qT, sf);
+  return ORACLE_OK;
+}
+
+int oracle_swiglu_backward_per_token_sf(const uint16_t* h, const uint16_t* dv, int64_t rows,
+                                        int64_t cols, const float* w, int fmt, int group,
+                                        float clamp_min, int sf_flags, float swiglu_clamp,
+                                        uint8_t* q, void* sf) {
+  int rc = check_common(h, q, sf, fmt, group);
+  if (rc != ORACLE_OK) return rc;
+  if (!dv) return ORACLE_ERR_NULL;
+  if (rows < 0 || cols < 0 || cols % group != 0) return ORACLE_ERR_SHAPE;
+  if (pairs(fmt) && group % 2 != 0) return ORACLE_ERR_GROUP;
+  if ((rc = check_sf_flags(sf_flags, 2 * cols, group)) != ORACLE_OK) return rc;
+  std::vector<float> vals(static_cast<size_t>(rows * 2 * cols));
+  oracle_swiglu_backward_values(h, dv, rows, cols, w, swiglu_clamp, vals.data());
+  const float floor = floor_for(*table_for(fmt), clamp_min);
+  const int64_t code_bytes = code_row_bytes(fmt, 2 * cols);
+  for (int64_t r = 0; r < rows; ++r)
+    per_token_row_sf(vals.data() + r * 2 * cols, r, rows, 2 * cols, fmt, group, floor, sf_flags,
+                     q + r * code_bytes, sf);
   return ORACLE_OK;
 }
 

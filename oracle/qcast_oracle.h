@@ -121,6 +121,31 @@ int oracle_swiglu_per_token_sf(const uint16_t* h, int64_t rows, int64_t cols, co
                                int fmt, int group, float clamp_min, int sf_flags, uint8_t* q,
                                void* sf);
 
+/* The other casts with scale-factor options (the same ORACLE_SF_* bits):
+ *  - per-block and per-channel (input layout): ORACLE_SF_ROUND_POW2 only;
+ *    the scales keep their fp32 [rows/block, cols/block] and
+ *    [rows/group, cols] shapes.
+ *  - per-channel + transpose (plain and SwiGLU): the per-token layouts of
+ *    x^T, whose rows are the cols channels and whose groups are the
+ *    rows/group token groups: fp32 [cols][rows/group], COL_MAJOR
+ *    [rows/group][ceil(cols/4)*4], PACKED_UE8M0 [cols][rows/group/4] or
+ *    [rows/group/4][ceil(cols/4)*4] (requires (rows/group) % 4 == 0).
+ *  - SwiGLU backward: the per-token layouts of the rows [dg | du] of
+ *    2*cols values: groups per row 2*cols/group. */
+int oracle_per_block_sf(const uint16_t* x, int64_t rows, int64_t cols, int fmt, int block,
+                        float clamp_min, int sf_flags, uint8_t* q, float* sf);
+int oracle_per_channel_sf(const uint16_t* x, int64_t rows, int64_t cols, int fmt, int group,
+                          float clamp_min, int sf_flags, uint8_t* q, float* sf);
+int oracle_per_channel_T_sf(const uint16_t* x, int64_t rows, int64_t cols, int fmt, int group,
+                            float clamp_min, int sf_flags, uint8_t* qT, void* sf);
+int oracle_swiglu_per_channel_T_sf(const uint16_t* h, int64_t rows, int64_t cols, const float* w,
+                                   int fmt, int group, float clamp_min, int sf_flags,
+                                   float swiglu_clamp, uint8_t* qT, void* sf);
+int oracle_swiglu_backward_per_token_sf(const uint16_t* h, const uint16_t* dv, int64_t rows,
+                                        int64_t cols, const float* w, int fmt, int group,
+                                        float clamp_min, int sf_flags, float swiglu_clamp,
+                                        uint8_t* q, void* sf);
+
 /* ---- SwiGLU variants and per-channel without transpose ---- */
 
 /* SwiGLU values with the optional clamp of the walk-through page §3.3:
