@@ -66,7 +66,7 @@
 extern "C" {
 #endif
 
-#define QCAST_ABI_VERSION 4
+#define QCAST_ABI_VERSION 5
 
 /* Bytes of the optional clamp-count workspace (count_ws) of the SwiGLU casts. */
 #define QCAST_COUNT_WS_BYTES 8192
@@ -132,6 +132,24 @@ typedef enum {
   QCAST_SF_COL_MAJOR = 2,
   QCAST_SF_PACKED_UE8M0 = 4
 } qcast_sf_flags;
+
+/*
+ * The other casts take the same options where their scales have a per-token
+ * row structure ([SPLIT] §四 C: the casts write the consumer's layout while
+ * they quantize or re-arrange):
+ *   - the SwiGLU backward (qcast_swiglu_backward_per_token_sf): the layouts
+ *     of its code rows [dg | du], rows = rows, groups = 2*cols/group;
+ *     packed needs (cols/group) % 4 == 0, so no word spans the two halves;
+ *   - the transposed per-channel casts (qcast_per_channel_T_sf,
+ *     qcast_swiglu_per_channel_T_sf): the layouts of the per-token cast of
+ *     x^T, whose rows are the cols channels and whose groups are the
+ *     rows/group token groups: fp32 sf[cols][rows/group], COL_MAJOR
+ *     sf[rows/group][ceil(cols/4)*4], packed uint32 [cols][rows/group/4]
+ *     or [rows/group/4][ceil(cols/4)*4]; packed needs (rows/group) % 4 == 0;
+ *   - the per-block and input-layout per-channel casts (qcast_per_block_sf,
+ *     qcast_per_channel_sf): QCAST_SF_ROUND_POW2 only (any other bit returns
+ *     QCAST_ERR_FORMAT); their fp32 scale arrays keep their shapes.
+ */
 
 /* Output type of qcast_cast_back. */
 typedef enum { QCAST_OUT_BF16 = 1, QCAST_OUT_F32 = 2 } qcast_out_dtype;
@@ -265,6 +283,15 @@ QCAST_API int qcast_swiglu_backward_per_token(const void* h, const void* dv, int
                                               int group, float clamp_min, float swiglu_clamp,
                                               void* q, float* sf, void* stream);
 
+/* qcast_swiglu_backward_per_token with a scale-factor layout (qcast_sf_flags
+ * over the rows [dg | du]: groups = 2*cols/group, packed needs
+ * (cols/group) % 4 == 0); sf is float or uint32 storage accordingly. */
+QCAST_API int qcast_swiglu_backward_per_token_sf(const void* h, const void* dv, int64_t rows,
+                                                 int64_t cols, const float* row_weight, int fmt,
+                                                 int group, float clamp_min, int sf_flags,
+                                                 float swiglu_clamp, void* q, void* sf,
+                                                 void* stream);
+
 /*
  * SwiGLU forward fused with the per-channel cast and the transpose ([NEWS]
  * item 2; the SwiGLU of [WALK] §3.3, the transposed per-channel layout of
@@ -285,6 +312,15 @@ QCAST_API int qcast_swiglu_per_channel_T(const void* h, int64_t rows, int64_t co
                                          float clamp_min, float swiglu_clamp, void* qT, float* sf,
                                          uint64_t* clamp_count, void* count_ws, void* stream);
 
+/* qcast_swiglu_per_channel_T with a scale-factor layout: the per-token
+ * layouts of v^T (rows = the cols channels, groups = the rows/group token
+ * groups; packed needs (rows/group) % 4 == 0). */
+QCAST_API int qcast_swiglu_per_channel_T_sf(const void* h, int64_t rows, int64_t cols,
+                                            const float* row_weight, int fmt, int group,
+                                            float clamp_min, int sf_flags, float swiglu_clamp,
+                                            void* qT, void* sf, uint64_t* clamp_count,
+                                            void* count_ws, void* stream);
+
 /*
  * Per-block cast of a weight ([SPLIT] §二 per_block_cast; [NEWS]
  * "刚刚！DeepSeek开源高性能GPU算子库TileKernels", item 2, per-block granularity).
@@ -298,6 +334,13 @@ QCAST_API int qcast_swiglu_per_channel_T(const void* h, int64_t rows, int64_t co
  */
 QCAST_API int qcast_per_block(const void* x, int64_t rows, int64_t cols, int fmt, int block,
                     float clamp_min, void* q, float* sf, void* stream);
+
+/* qcast_per_block with round_sf ([WALK] §3.1): sf_flags 0 or
+ * QCAST_SF_ROUND_POW2 (each tile's scale rounded up to a power of two, the
+ * codes formed with its exact inverse); sf keeps its fp32 shape. */
+QCAST_API int qcast_per_block_sf(const void* x, int64_t rows, int64_t cols, int fmt, int block,
+                                 float clamp_min, int sf_flags, void* q, float* sf,
+                                 void* stream);
 
 /*
  * Per-channel cast written transposed ([SPLIT] §二 per_channel_cast
@@ -318,6 +361,15 @@ QCAST_API int qcast_per_block(const void* x, int64_t rows, int64_t cols, int fmt
 QCAST_API int qcast_per_channel_T(const void* x, int64_t rows, int64_t cols, int fmt, int group,
                         float clamp_min, void* qT, float* sf, void* stream);
 
+/* qcast_per_channel_T with a scale-factor layout: the per-token layouts of
+ * x^T (rows = the cols channels, groups = the rows/group token groups):
+ * fp32 sf[cols][rows/group] or, COL_MAJOR, sf[rows/group][ceil(cols/4)*4];
+ * packed uint32 [cols][rows/group/4] or [rows/group/4][ceil(cols/4)*4],
+ * which needs (rows/group) % 4 == 0. */
+QCAST_API int qcast_per_channel_T_sf(const void* x, int64_t rows, int64_t cols, int fmt,
+                                     int group, float clamp_min, int sf_flags, void* qT,
+                                     void* sf, void* stream);
+
 /*
  * Per-channel cast in the input layout ([SPLIT] §二 per_channel_cast without
  * the transpose).
@@ -331,6 +383,11 @@ QCAST_API int qcast_per_channel_T(const void* x, int64_t rows, int64_t cols, int
  */
 QCAST_API int qcast_per_channel(const void* x, int64_t rows, int64_t cols, int fmt, int group,
                                 float clamp_min, void* q, float* sf, void* stream);
+
+/* qcast_per_channel with round_sf: sf_flags 0 or QCAST_SF_ROUND_POW2. */
+QCAST_API int qcast_per_channel_sf(const void* x, int64_t rows, int64_t cols, int fmt, int group,
+                                   float clamp_min, int sf_flags, void* q, float* sf,
+                                   void* stream);
 
 /*
  * cast_back: dequantize per-token codes ([SPLIT] §二 cast_back).

@@ -27,7 +27,9 @@ __all__ = ["qcast_per_token", "qcast_e2m1", "qcast_swiglu_per_token", "qcast_per
            "qcast_per_channel_T", "qcast_cast_back", "qcast_per_token_sf",
            "qcast_swiglu_per_token_sf", "qcast_swiglu_per_token_ex",
            "qcast_swiglu_backward_per_token", "qcast_swiglu_per_channel_T", "qcast_per_channel",
-           "qcast_swiglu_per_token_noalloc", "sf_layout_shape", "SF_ROUND_POW2", "SF_COL_MAJOR",
+           "qcast_swiglu_per_token_noalloc", "qcast_per_block_sf", "qcast_per_channel_sf",
+           "qcast_per_channel_T_sf", "qcast_swiglu_per_channel_T_sf",
+           "qcast_swiglu_backward_per_token_sf", "sf_layout_shape", "SF_ROUND_POW2", "SF_COL_MAJOR",
            "SF_PACKED_UE8M0", "qcast_abi_version", "qcast_set_num_cus", "qcast_bench_copy",
            "qcast_bench_check_scale", "qcast_bench_time_next",
            "qcast_bench_per_channel_T_traffic",
@@ -287,6 +289,56 @@ def qcast_swiglu_backward_per_token(h, dv, row_weight=None, fmt="e4m3", group=12
     return out, out_sf
 
 
+def qcast_swiglu_backward_per_token_sf(h, dv, row_weight=None, fmt="e4m3", group=128,
+                                       clamp_min=0.0, sf_flags=0, swiglu_clamp=0.0, out=None,
+                                       out_sf=None, stream=None):
+    """qcast_swiglu_backward_per_token with a scale-factor layout over the
+    rows ``[dgate | dup]`` of 2*cols values (``sf_layout_shape(rows, 2*cols,
+    group, sf_flags)``)."""
+    f = fmt_id(fmt)
+    h, rows, cols = _gate_up(h)
+    two_n = 2 * cols
+    dv = _bf16_input(dv, "dv")
+    if tuple(dv.shape) != (rows, cols) or dv.device != h.device:
+        raise QcastError(2, f"dv must be [{rows}, {cols}] on h's device")
+    wptr = _row_weight(row_weight, rows, h.device)
+    out = _out(out, code_shape(f, rows, two_n), _code_dtype(f), h.device, "out")
+    shape, dt = sf_layout_shape(rows, two_n, group if group > 0 else 1, sf_flags)
+    out_sf = _out(out_sf, shape, dt, h.device, "out_sf")
+    with torch.cuda.device(h.device):
+        check(load().qcast_swiglu_backward_per_token_sf(h.data_ptr(), dv.data_ptr(), rows, cols,
+                                                        wptr, f, group, clamp_min, sf_flags,
+                                                        swiglu_clamp, out.data_ptr(),
+                                                        out_sf.data_ptr(),
+                                                        _stream(h.device, stream)),
+              "qcast_swiglu_backward_per_token_sf")
+    return out, out_sf
+
+
+def qcast_swiglu_per_channel_T_sf(h, row_weight=None, fmt="e4m3", group=128, clamp_min=0.0,
+                                  sf_flags=0, swiglu_clamp=0.0, clamp_count=None, out=None,
+                                  out_sf=None, stream=None, count_workspace=None):
+    """qcast_swiglu_per_channel_T with a scale-factor layout: the per-token
+    layouts of the transposed values (``sf_layout_shape(cols, rows, group,
+    sf_flags)``: rows are the channels)."""
+    f = fmt_id(fmt)
+    h, rows, cols = _gate_up(h)
+    wptr = _row_weight(row_weight, rows, h.device)
+    cptr = _counter(clamp_count, h.device)
+    out = _out(out, code_shape(f, cols, rows), _code_dtype(f), h.device, "out")
+    shape, dt = sf_layout_shape(cols, rows, group if group > 0 else 1, sf_flags)
+    out_sf = _out(out_sf, shape, dt, h.device, "out_sf")
+    with torch.cuda.device(h.device):
+        sh = _stream(h.device, stream)
+        wsptr = _count_ws(count_workspace, clamp_count, h.device, sh)
+        check(load().qcast_swiglu_per_channel_T_sf(h.data_ptr(), rows, cols, wptr, f, group,
+                                                   clamp_min, sf_flags, swiglu_clamp,
+                                                   out.data_ptr(), out_sf.data_ptr(), cptr,
+                                                   wsptr, sh),
+              "qcast_swiglu_per_channel_T_sf")
+    return out, out_sf
+
+
 def qcast_swiglu_per_channel_T(h, row_weight=None, fmt="e4m3", group=128, clamp_min=0.0,
                                swiglu_clamp=0.0, clamp_count=None, out=None, out_sf=None,
                                stream=None, count_workspace=None):
@@ -393,6 +445,56 @@ def qcast_per_channel_T(x, fmt="e4m3", group=128, clamp_min=0.0, out=None, out_s
         check(load().qcast_per_channel_T(x.data_ptr(), rows, cols, f, group, clamp_min,
                                          out.data_ptr(), out_sf.data_ptr(),
                                          _stream(x.device, stream)), "qcast_per_channel_T")
+    return out, out_sf
+
+
+def qcast_per_block_sf(x, fmt="e4m3", block=128, clamp_min=0.0, sf_flags=0, out=None,
+                       out_sf=None, stream=None):
+    """qcast_per_block with round_sf (``sf_flags`` 0 or SF_ROUND_POW2);
+    ``out_sf [rows/block, cols/block]`` float32."""
+    f = fmt_id(fmt)
+    x = _bf16_input(x, "x")
+    rows, cols = x.shape
+    out = _out(out, code_shape(f, rows, cols), _code_dtype(f), x.device, "out")
+    out_sf = _out(out_sf, (rows // block if block > 0 else 0, cols // block if block > 0 else 0),
+                  torch.float32, x.device, "out_sf")
+    with torch.cuda.device(x.device):
+        check(load().qcast_per_block_sf(x.data_ptr(), rows, cols, f, block, clamp_min, sf_flags,
+                                        out.data_ptr(), out_sf.data_ptr(),
+                                        _stream(x.device, stream)), "qcast_per_block_sf")
+    return out, out_sf
+
+
+def qcast_per_channel_sf(x, fmt="e4m3", group=128, clamp_min=0.0, sf_flags=0, out=None,
+                         out_sf=None, stream=None):
+    """qcast_per_channel with round_sf (``sf_flags`` 0 or SF_ROUND_POW2)."""
+    f = fmt_id(fmt)
+    x = _bf16_input(x, "x")
+    rows, cols = x.shape
+    out = _out(out, code_shape(f, rows, cols), _code_dtype(f), x.device, "out")
+    out_sf = _out(out_sf, (rows // group if group > 0 else 0, cols), torch.float32, x.device,
+                  "out_sf")
+    with torch.cuda.device(x.device):
+        check(load().qcast_per_channel_sf(x.data_ptr(), rows, cols, f, group, clamp_min, sf_flags,
+                                          out.data_ptr(), out_sf.data_ptr(),
+                                          _stream(x.device, stream)), "qcast_per_channel_sf")
+    return out, out_sf
+
+
+def qcast_per_channel_T_sf(x, fmt="e4m3", group=128, clamp_min=0.0, sf_flags=0, out=None,
+                           out_sf=None, stream=None):
+    """qcast_per_channel_T with a scale-factor layout: the per-token layouts
+    of ``x^T`` (``sf_layout_shape(channels, tokens, group, sf_flags)``)."""
+    f = fmt_id(fmt)
+    x = _bf16_input(x, "x")
+    rows, cols = x.shape
+    out = _out(out, code_shape(f, cols, rows), _code_dtype(f), x.device, "out")
+    shape, dt = sf_layout_shape(cols, rows, group if group > 0 else 1, sf_flags)
+    out_sf = _out(out_sf, shape, dt, x.device, "out_sf")
+    with torch.cuda.device(x.device):
+        check(load().qcast_per_channel_T_sf(x.data_ptr(), rows, cols, f, group, clamp_min,
+                                            sf_flags, out.data_ptr(), out_sf.data_ptr(),
+                                            _stream(x.device, stream)), "qcast_per_channel_T_sf")
     return out, out_sf
 
 

@@ -70,6 +70,13 @@ def load():
         "qcast_per_channel": [vp, i64, i64, i32, i32, f32, vp, vp, vp],
         "qcast_swiglu_per_token_noalloc": [vp, i64, i64, vp, i32, i32, f32, i32, f32, vp, vp,
                                            vp, vp],
+        "qcast_per_block_sf": [vp, i64, i64, i32, i32, f32, i32, vp, vp, vp],
+        "qcast_per_channel_sf": [vp, i64, i64, i32, i32, f32, i32, vp, vp, vp],
+        "qcast_per_channel_T_sf": [vp, i64, i64, i32, i32, f32, i32, vp, vp, vp],
+        "qcast_swiglu_per_channel_T_sf": [vp, i64, i64, vp, i32, i32, f32, i32, f32, vp, vp, vp,
+                                          vp, vp],
+        "qcast_swiglu_backward_per_token_sf": [vp, vp, i64, i64, vp, i32, i32, f32, i32, f32, vp,
+                                               vp, vp],
     }
     for name, args in sig.items():
         fn = getattr(lib, name)
@@ -103,6 +110,8 @@ EXPORTS = ["qcast_per_token", "qcast_e2m1", "qcast_swiglu_per_token", "qcast_per
            "qcast_per_channel_T", "qcast_cast_back", "qcast_per_token_sf",
            "qcast_swiglu_per_token_sf", "qcast_swiglu_per_token_ex",
            "qcast_swiglu_backward_per_token", "qcast_swiglu_per_channel_T", "qcast_per_channel",
-           "qcast_swiglu_per_token_noalloc", "qcast_status_str", "qcast_abi_version", "qcast_set_num_cus",
+           "qcast_swiglu_per_token_noalloc", "qcast_per_block_sf", "qcast_per_channel_sf",
+           "qcast_per_channel_T_sf", "qcast_swiglu_per_channel_T_sf",
+           "qcast_swiglu_backward_per_token_sf", "qcast_status_str", "qcast_abi_version", "qcast_set_num_cus",
            "qcast_bench_copy", "qcast_bench_check_scale", "qcast_bench_time_next",
            "qcast_bench_per_channel_T_traffic"]

@@ -36,7 +36,7 @@ constexpr int kBlock = 128;
 template <int kFmt, int kSpan>
 __global__ __launch_bounds__(kThreads) void per_block_kernel(
     const uint16_t* __restrict__ x, uint32_t cols, uint32_t bcols, float floor,
-    uint8_t* __restrict__ q, float* __restrict__ sf) {
+    uint32_t round_sf, uint8_t* __restrict__ q, float* __restrict__ sf) {
   constexpr int kChunksPerRow = kSpan * kBlock / 8;       // lanes per row: 16 or 32
   constexpr int kRowsPerPass = kThreads / kChunksPerRow;  // 16 or 8
   constexpr int kPasses = kBlock / kRowsPerPass;          // 8 or 16
@@ -79,7 +79,8 @@ __global__ __launch_bounds__(kThreads) void per_block_kernel(
   __syncthreads();
   const float m = fmaxf(fmaxf(wave_amax[0][ti], wave_amax[1][ti]),
                         fmaxf(wave_amax[2][ti], wave_amax[3][ti]));
-  const Scale s = group_scale<kFmt>(m, floor);
+  Scale s = group_scale<kFmt>(m, floor);
+  if (round_sf) s = round_scale_pow2(s);
 #pragma unroll
   for (int p = 0; p < kPasses; ++p) {
     float v[8];
@@ -94,13 +95,14 @@ __global__ __launch_bounds__(kThreads) void per_block_kernel(
 
 template <int kFmt>
 hipError_t launch_fmt(const uint16_t* x, int64_t nblocks, int64_t cols, int64_t bcols,
-                      float floor, uint8_t* q, float* sf, hipStream_t stream) {
+                      float floor, uint32_t round_sf, uint8_t* q, float* sf,
+                      hipStream_t stream) {
   if (bcols % 2 == 0)
     launch_kernel(per_block_kernel<kFmt, 2>, dim3((unsigned)(nblocks / 2)), dim3(kThreads), 0,
-                  stream, x, (uint32_t)cols, (uint32_t)bcols, floor, q, sf);
+                  stream, x, (uint32_t)cols, (uint32_t)bcols, floor, round_sf, q, sf);
   else
     launch_kernel(per_block_kernel<kFmt, 1>, dim3((unsigned)nblocks), dim3(kThreads), 0,
-                  stream, x, (uint32_t)cols, (uint32_t)bcols, floor, q, sf);
+                  stream, x, (uint32_t)cols, (uint32_t)bcols, floor, round_sf, q, sf);
   return hipGetLastError();
 }
 
@@ -112,7 +114,8 @@ bool per_block_fits(int64_t rows, int64_t cols) {
 }
 
 hipError_t launch_per_block(const void* x, int64_t rows, int64_t cols, int fmt, float floor,
-                            void* q, float* sf, hipStream_t stream, const LaunchCaps& caps) {
+                            uint32_t sf_flags, void* q, float* sf, hipStream_t stream,
+                            const LaunchCaps& caps) {
   (void)caps;
   const int64_t bcols = cols / kBlock;
   const int64_t nblocks = (rows / kBlock) * bcols;
@@ -121,11 +124,12 @@ hipError_t launch_per_block(const void* x, int64_t rows, int64_t cols, int fmt, 
   if (!per_block_fits(rows, cols)) return hipErrorInvalidValue;
   const uint16_t* xp = static_cast<const uint16_t*>(x);
   uint8_t* qp = static_cast<uint8_t*>(q);
+  const uint32_t r = sf_flags & kSfRound;
   switch (fmt) {
-    case kE4M3: return launch_fmt<kE4M3>(xp, nblocks, cols, bcols, floor, qp, sf, stream);
-    case kE5M2: return launch_fmt<kE5M2>(xp, nblocks, cols, bcols, floor, qp, sf, stream);
-    case kE2M1: return launch_fmt<kE2M1>(xp, nblocks, cols, bcols, floor, qp, sf, stream);
-    case kE5M6: return launch_fmt<kE5M6>(xp, nblocks, cols, bcols, floor, qp, sf, stream);
+    case kE4M3: return launch_fmt<kE4M3>(xp, nblocks, cols, bcols, floor, r, qp, sf, stream);
+    case kE5M2: return launch_fmt<kE5M2>(xp, nblocks, cols, bcols, floor, r, qp, sf, stream);
+    case kE2M1: return launch_fmt<kE2M1>(xp, nblocks, cols, bcols, floor, r, qp, sf, stream);
+    case kE5M6: return launch_fmt<kE5M6>(xp, nblocks, cols, bcols, floor, r, qp, sf, stream);
   }
   return hipErrorInvalidValue;
 }

@@ -36,7 +36,7 @@ static_assert(kTileChannels == kThreads, "one scale per thread");
 
 template <int kFmt>
 __global__ __launch_bounds__(kThreads) void per_channel_kernel(
-    const uint16_t* __restrict__ x, uint32_t cols, uint32_t nct, float floor,
+    const uint16_t* __restrict__ x, uint32_t cols, uint32_t nct, float floor, uint32_t round_sf,
     uint8_t* __restrict__ q, float* __restrict__ sf) {
   __shared__ float wave_amax[kThreads / 64][kTileChannels];
   __shared__ __attribute__((aligned(16))) float inv_s[kTileChannels];
@@ -82,7 +82,8 @@ __global__ __launch_bounds__(kThreads) void per_channel_kernel(
     float a = wave_amax[0][t];
 #pragma unroll
     for (int w = 1; w < kThreads / 64; ++w) a = fmaxf(a, wave_amax[w][t]);
-    const Scale s = group_scale<kFmt>(a, floor);
+    Scale s = group_scale<kFmt>(a, floor);
+    if (round_sf) s = round_scale_pow2(s);
     inv_s[t] = s.inv;
     if (c0 + t < cols) sf[(uint64_t)g * cols + c0 + t] = s.sf;
   }
@@ -113,7 +114,8 @@ bool per_channel_fits(int64_t rows, int64_t cols) {
 }
 
 hipError_t launch_per_channel(const void* x, int64_t rows, int64_t cols, int fmt, float floor,
-                              void* q, float* sf, hipStream_t stream, const LaunchCaps& caps) {
+                              uint32_t sf_flags, void* q, float* sf, hipStream_t stream,
+                              const LaunchCaps& caps) {
   (void)caps;
   const int64_t ngroups = rows / kGroupTokens;
   const int64_t nct = (cols + kTileChannels - 1) / kTileChannels;
@@ -128,7 +130,7 @@ hipError_t launch_per_channel(const void* x, int64_t rows, int64_t cols, int fmt
   if (!kernel) return hipErrorInvalidValue;
   launch_kernel(kernel, dim3((unsigned)ntiles), dim3(kThreads), 0, stream,
                 static_cast<const uint16_t*>(x), (uint32_t)cols, (uint32_t)nct, floor,
-                static_cast<uint8_t*>(q), sf);
+                (uint32_t)(sf_flags & kSfRound), static_cast<uint8_t*>(q), sf);
   return hipGetLastError();
 }
 

@@ -48,6 +48,15 @@
 // the changed values), and the tile continues from fp32 values instead of
 // packed bf16.
 //
+// Scales: fp32 sf[channel][token group] by default; on request the layouts
+// of the per-token cast of the transposed input, whose rows are the
+// channels (round_sf, TMA-aligned column-major sf[group][channels padded to
+// 4], packed UE8M0 words: the cast config of the walk-through page, §3.1, and
+// the consumer layouts the first page's §四 C says the casts write while
+// they quantize or re-arrange). One lane forms each scale, so a packed word,
+// whose four bytes belong to four token groups of other tiles, is written
+// one byte at a time.
+//
 // A traffic-only twin of the cast (per_channel_t_traffic_kernel: the same
 // walk, loads and qT stores, no arithmetic) serves measurement only.
 #include "qcast_device.h"
@@ -315,8 +324,8 @@ struct Smem {
 // tile) it also ends converged, with the LDS free again.
 template <int kFmt, bool kReuse, class Tile>
 __device__ __forceinline__ void process_tile(const TileCoord& tc, const Tile& tile, uint32_t rows,
-                                             uint32_t ngroups, float floor, Smem<kFmt>& sm,
-                                             uint8_t* __restrict__ qT, float* __restrict__ sf) {
+                                             float floor, const SfLayout& lay, Smem<kFmt>& sm,
+                                             uint8_t* __restrict__ qT, void* __restrict__ sf) {
   using TG = TileGeo<kFmt>;
   const int t = threadIdx.x;
   const int ch = t % kCC;
@@ -338,10 +347,10 @@ __device__ __forceinline__ void process_tile(const TileCoord& tc, const Tile& ti
     const int c = t % kChannels;
     const float m = fmaxf(fmaxf(sm.wave_amax[gi][0][c], sm.wave_amax[gi][1][c]),
                           fmaxf(sm.wave_amax[gi][2][c], sm.wave_amax[gi][3][c]));
-    const Scale s = group_scale<kFmt>(m, floor);
+    Scale s = group_scale<kFmt>(m, floor);
+    if (lay.flags & kSfRound) s = round_scale_pow2(s);
     sm.inv_s[gi][c] = s.inv;
-    if (c < tc.nc && gi < tc.ng)
-      sf[(uint64_t)tc.c0 * ngroups + (uint32_t)c * ngroups + tc.gt * kTG + gi] = s.sf;
+    if (c < tc.nc && gi < tc.ng) store_lone_scale(sf, tc.c0 + c, tc.gt * kTG + gi, s, lay);
   }
   __syncthreads();
 
@@ -413,7 +422,7 @@ template <int kFmt>
 __global__ __launch_bounds__(kThreads) void per_channel_t_kernel(
     const uint16_t* __restrict__ x, uint32_t rows, uint32_t cols, uint32_t ngroups,
     uint32_t nct, uint32_t ntg, uint32_t ntiles, uint32_t per_xcd, FastDiv sdiv, float floor,
-    uint8_t* __restrict__ qT, float* __restrict__ sf) {
+    SfLayout lay, uint8_t* __restrict__ qT, void* __restrict__ sf) {
   __shared__ __attribute__((aligned(16))) Smem<kFmt> sm;
   const uint32_t b = blockIdx.x;
   const uint32_t tau = (kOrder & 2) ? b : (b % kXcds) * per_xcd + b / kXcds;
@@ -421,7 +430,7 @@ __global__ __launch_bounds__(kThreads) void per_channel_t_kernel(
   const TileCoord tc = tile_coord(tau, ngroups, cols, nct, ntg, sdiv);
   Bf16Tile tile;
   load_tile(x, cols, tc, tile.raw);
-  process_tile<kFmt, false>(tc, tile, rows, ngroups, floor, sm, qT, sf);
+  process_tile<kFmt, false>(tc, tile, rows, floor, lay, sm, qT, sf);
 }
 
 // The cast's memory traffic alone, for measurement: the same workgroup ->
@@ -464,8 +473,9 @@ template <int kFmt, bool kWeighted, bool kClamp, int kCount>
 __global__ __launch_bounds__(kThreads) void swiglu_per_channel_t_kernel(
     const uint16_t* __restrict__ h, const float* __restrict__ w, uint32_t rows, uint32_t cols,
     uint32_t ngroups, uint32_t nct, uint32_t ntg, uint32_t ntiles, uint32_t per_xcd,
-    FastDiv sdiv, uint32_t vgrid, float floor, float clamp, unsigned long long* __restrict__ count,
-    unsigned long long* __restrict__ slots, uint8_t* __restrict__ qT, float* __restrict__ sf) {
+    FastDiv sdiv, uint32_t vgrid, float floor, float clamp, SfLayout lay,
+    unsigned long long* __restrict__ count, unsigned long long* __restrict__ slots,
+    uint8_t* __restrict__ qT, void* __restrict__ sf) {
   __shared__ __attribute__((aligned(16))) Smem<kFmt> sm;
   if constexpr (kCount == kCountDirect) {
     uint32_t n = 0;
@@ -475,7 +485,7 @@ __global__ __launch_bounds__(kThreads) void swiglu_per_channel_t_kernel(
       const TileCoord tc = tile_coord<kSwStrip>(tau, ngroups, cols, nct, ntg, sdiv);
       F32Tile tile;
       n += load_swiglu_tile<kWeighted, kClamp, true>(h, w, cols, clamp, tc, tile);
-      process_tile<kFmt, true>(tc, tile, rows, ngroups, floor, sm, qT, sf);
+      process_tile<kFmt, true>(tc, tile, rows, floor, lay, sm, qT, sf);
     }
     add_wave_counts(n, count);
   } else {
@@ -494,7 +504,7 @@ __global__ __launch_bounds__(kThreads) void swiglu_per_channel_t_kernel(
     // processed, so the slot atomic's round trip overlaps that work.
     SlotCount<> sc;
     if constexpr (kCount == kCountSlotted) sc.arrive(n, slots);
-    if (has_tile) process_tile<kFmt, false>(tc, tile, rows, ngroups, floor, sm, qT, sf);
+    if (has_tile) process_tile<kFmt, false>(tc, tile, rows, floor, lay, sm, qT, sf);
     if constexpr (kCount == kCountSlotted) sc.finish(slots, count);
   }
 }
@@ -543,8 +553,9 @@ struct CountArgs {
 
 template <int kFmt, bool kWeighted, bool kClamp>
 hipError_t launch_swiglu_t(const uint16_t* h, const float* w, int64_t rows, int64_t cols,
-                           const Grid& g, float floor, float clamp, const CountArgs& ca,
-                           uint8_t* qT, float* sf, hipStream_t stream, const LaunchCaps& caps) {
+                           const Grid& g, float floor, float clamp, const SfLayout& lay,
+                           const CountArgs& ca, uint8_t* qT, void* sf, hipStream_t stream,
+                           const LaunchCaps& caps) {
   if constexpr (kClamp) {
     // The slots count the workgroups that reach them in 24 bits (and the
     // clamped values in 40: at most 2 * rows * cols, under 2^37 for any h
@@ -555,7 +566,7 @@ hipError_t launch_swiglu_t(const uint16_t* h, const float* w, int64_t rows, int6
       launch_kernel((swiglu_per_channel_t_kernel<kFmt, kWeighted, true, kCountSlotted>),
                     dim3(g.grid), dim3(kThreads), 0, stream, h, w, (uint32_t)rows,
                     (uint32_t)cols, g.ngroups, g.nct, g.ntg, g.ntiles, g.per_xcd, g.sw_strip_div, g.grid, floor, clamp,
-                    ca.count, ca.slots, qT, sf);
+                    lay, ca.count, ca.slots, qT, sf);
       return hipGetLastError();
     }
     if (ca.count) {
@@ -565,33 +576,33 @@ hipError_t launch_swiglu_t(const uint16_t* h, const float* w, int64_t rows, int6
       launch_kernel((swiglu_per_channel_t_kernel<kFmt, kWeighted, true, kCountDirect>),
                     dim3(grid), dim3(kThreads), 0, stream, h, w, (uint32_t)rows,
                     (uint32_t)cols, g.ngroups, g.nct, g.ntg, g.ntiles, g.per_xcd, g.sw_strip_div, g.grid, floor, clamp,
-                    ca.count, ca.slots, qT, sf);
+                    lay, ca.count, ca.slots, qT, sf);
       return hipGetLastError();
     }
   }
   launch_kernel((swiglu_per_channel_t_kernel<kFmt, kWeighted, kClamp, kCountNone>),
                 dim3(g.grid), dim3(kThreads), 0, stream, h, w, (uint32_t)rows, (uint32_t)cols,
-                g.ngroups, g.nct, g.ntg, g.ntiles, g.per_xcd, g.sw_strip_div, g.grid, floor, clamp, ca.count, ca.slots,
-                qT, sf);
+                g.ngroups, g.nct, g.ntg, g.ntiles, g.per_xcd, g.sw_strip_div, g.grid, floor, clamp, lay, ca.count,
+                ca.slots, qT, sf);
   return hipGetLastError();
 }
 
 template <int kFmt>
 hipError_t launch_swiglu_t_fmt(const uint16_t* h, const float* w, int64_t rows, int64_t cols,
-                               const Grid& g, float floor, float clamp, const CountArgs& ca,
-                               uint8_t* qT, float* sf, hipStream_t stream,
+                               const Grid& g, float floor, float clamp, const SfLayout& lay,
+                               const CountArgs& ca, uint8_t* qT, void* sf, hipStream_t stream,
                                const LaunchCaps& caps) {
   if (w) {
     return clamp > 0.0f
-               ? launch_swiglu_t<kFmt, true, true>(h, w, rows, cols, g, floor, clamp, ca, qT, sf,
+               ? launch_swiglu_t<kFmt, true, true>(h, w, rows, cols, g, floor, clamp, lay, ca, qT, sf,
                                                    stream, caps)
-               : launch_swiglu_t<kFmt, true, false>(h, w, rows, cols, g, floor, clamp, ca, qT,
+               : launch_swiglu_t<kFmt, true, false>(h, w, rows, cols, g, floor, clamp, lay, ca, qT,
                                                     sf, stream, caps);
   }
   return clamp > 0.0f
-             ? launch_swiglu_t<kFmt, false, true>(h, w, rows, cols, g, floor, clamp, ca, qT, sf,
+             ? launch_swiglu_t<kFmt, false, true>(h, w, rows, cols, g, floor, clamp, lay, ca, qT, sf,
                                                   stream, caps)
-             : launch_swiglu_t<kFmt, false, false>(h, w, rows, cols, g, floor, clamp, ca, qT,
+             : launch_swiglu_t<kFmt, false, false>(h, w, rows, cols, g, floor, clamp, lay, ca, qT,
                                                    sf, stream, caps);
 }
 
@@ -603,22 +614,25 @@ bool per_channel_t_fits(int64_t rows, int64_t cols, int64_t row_stride, int fmt)
 }
 
 hipError_t launch_per_channel_T(const void* x, int64_t rows, int64_t cols, int fmt, float floor,
-                                void* qT, float* sf, hipStream_t stream,
+                                uint32_t sf_flags, void* qT, void* sf, hipStream_t stream,
                                 const LaunchCaps& caps) {
   (void)caps;
   Grid g;
   // The kernels index tiles, and offsets inside a tile's rows, in 32 bits.
   if (!make_grid(rows, cols, cols, fmt, &g)) return hipErrorInvalidValue;
   if (g.ntiles == 0) return hipSuccess;
+  if ((sf_flags & kSfPacked) && g.ngroups % 4 != 0) return hipErrorInvalidValue;
   auto kernel = fmt == kE4M3   ? per_channel_t_kernel<kE4M3>
                 : fmt == kE5M2 ? per_channel_t_kernel<kE5M2>
                 : fmt == kE2M1 ? per_channel_t_kernel<kE2M1>
                 : fmt == kE5M6 ? per_channel_t_kernel<kE5M6>
                                : nullptr;
   if (!kernel) return hipErrorInvalidValue;
+  // the layout of x^T: rows are the channels, groups the token groups
+  const SfLayout lay = make_sf_layout(cols, rows, kGroupTokens, sf_flags);
   launch_kernel(kernel, dim3(g.grid), dim3(kThreads), 0, stream,
                 static_cast<const uint16_t*>(x), (uint32_t)rows, (uint32_t)cols, g.ngroups,
-                g.nct, g.ntg, g.ntiles, g.per_xcd, g.strip_div, floor,
+                g.nct, g.ntg, g.ntiles, g.per_xcd, g.strip_div, floor, lay,
                 static_cast<uint8_t*>(qT), sf);
   return hipGetLastError();
 }
@@ -635,29 +649,31 @@ hipError_t launch_per_channel_T_traffic(const void* x, int64_t rows, int64_t col
 }
 
 hipError_t launch_swiglu_per_channel_T(const void* h, int64_t rows, int64_t cols, const float* w,
-                                       int fmt, float floor, float swiglu_clamp,
-                                       unsigned long long* clamp_count,
-                                       unsigned long long* count_ws, void* qT, float* sf,
+                                       int fmt, float floor, uint32_t sf_flags,
+                                       float swiglu_clamp, unsigned long long* clamp_count,
+                                       unsigned long long* count_ws, void* qT, void* sf,
                                        hipStream_t stream, const LaunchCaps& caps) {
   Grid g;
   if (!make_grid(rows, cols, 2 * cols, fmt, &g)) return hipErrorInvalidValue;
   if (g.ntiles == 0) return hipSuccess;
+  if ((sf_flags & kSfPacked) && g.ngroups % 4 != 0) return hipErrorInvalidValue;
+  const SfLayout lay = make_sf_layout(cols, rows, kGroupTokens, sf_flags);
   const uint16_t* hp = static_cast<const uint16_t*>(h);
   uint8_t* qp = static_cast<uint8_t*>(qT);
   const CountArgs ca{clamp_count, count_ws};
   switch (fmt) {
     case kE4M3:
-      return launch_swiglu_t_fmt<kE4M3>(hp, w, rows, cols, g, floor, swiglu_clamp, ca, qp, sf,
-                                        stream, caps);
+      return launch_swiglu_t_fmt<kE4M3>(hp, w, rows, cols, g, floor, swiglu_clamp, lay, ca, qp,
+                                        sf, stream, caps);
     case kE5M2:
-      return launch_swiglu_t_fmt<kE5M2>(hp, w, rows, cols, g, floor, swiglu_clamp, ca, qp, sf,
-                                        stream, caps);
+      return launch_swiglu_t_fmt<kE5M2>(hp, w, rows, cols, g, floor, swiglu_clamp, lay, ca, qp,
+                                        sf, stream, caps);
     case kE2M1:
-      return launch_swiglu_t_fmt<kE2M1>(hp, w, rows, cols, g, floor, swiglu_clamp, ca, qp, sf,
-                                        stream, caps);
+      return launch_swiglu_t_fmt<kE2M1>(hp, w, rows, cols, g, floor, swiglu_clamp, lay, ca, qp,
+                                        sf, stream, caps);
     case kE5M6:
-      return launch_swiglu_t_fmt<kE5M6>(hp, w, rows, cols, g, floor, swiglu_clamp, ca, qp, sf,
-                                        stream, caps);
+      return launch_swiglu_t_fmt<kE5M6>(hp, w, rows, cols, g, floor, swiglu_clamp, lay, ca, qp,
+                                        sf, stream, caps);
   }
   return hipErrorInvalidValue;
 }

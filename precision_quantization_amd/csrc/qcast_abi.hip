@@ -263,13 +263,18 @@ int qcast_swiglu_per_token_sf(const void* h, int64_t rows, int64_t cols,
                                    0.0f, q, sf, nullptr, nullptr, stream);
 }
 
-int qcast_swiglu_backward_per_token(const void* h, const void* dv, int64_t rows, int64_t cols,
-                                    const float* row_weight, int fmt, int group, float clamp_min,
-                                    float swiglu_clamp, void* q, float* sf, void* stream) {
+int qcast_swiglu_backward_per_token_sf(const void* h, const void* dv, int64_t rows,
+                                       int64_t cols, const float* row_weight, int fmt, int group,
+                                       float clamp_min, int sf_flags, float swiglu_clamp, void* q,
+                                       void* sf, void* stream) {
   if (!any_fmt(fmt)) return QCAST_ERR_FORMAT;
+  if (!sf_flags_ok(sf_flags)) return QCAST_ERR_FORMAT;
   if (!per_token_group_ok(group)) return QCAST_ERR_GROUP;
+  // The scales are those of rows of 2 * cols values; a packed word never
+  // straddles the dg and du halves.
   if (rows < 0 || cols < 0 || cols % group != 0 || cols / 8 >= (int64_t(1) << 16) ||
-      too_big(rows, 2 * cols))
+      too_big(rows, 2 * cols) || !sf_shape_ok(rows, 2 * cols, group, sf_flags) ||
+      ((sf_flags & QCAST_SF_PACKED_UE8M0) && (cols / group) % 4 != 0))
     return QCAST_ERR_SHAPE;
   if (swiglu_clamp != swiglu_clamp) return QCAST_ERR_VALUE;
   if (!clamp_min_ok(clamp_min)) return QCAST_ERR_VALUE;
@@ -281,19 +286,28 @@ int qcast_swiglu_backward_per_token(const void* h, const void* dv, int64_t rows,
   qcast::LaunchCaps caps;
   const int rc = caps_for_current_device(&caps);
   if (rc != QCAST_OK) return rc;
-  return finish(qcast::launch_swiglu_backward(h, dv, rows, cols, row_weight, fmt, group,
-                                              floor_for(fmt, clamp_min), clamp_value(swiglu_clamp),
-                                              q, sf, static_cast<hipStream_t>(stream), caps));
+  return finish(qcast::launch_swiglu_backward(
+      h, dv, rows, cols, row_weight, fmt, group, floor_for(fmt, clamp_min), (uint32_t)sf_flags,
+      clamp_value(swiglu_clamp), q, sf, static_cast<hipStream_t>(stream), caps));
 }
 
-int qcast_swiglu_per_channel_T(const void* h, int64_t rows, int64_t cols, const float* row_weight,
-                               int fmt, int group, float clamp_min, float swiglu_clamp, void* qT,
-                               float* sf, uint64_t* clamp_count, void* count_ws,
-                               void* stream) {
+int qcast_swiglu_backward_per_token(const void* h, const void* dv, int64_t rows, int64_t cols,
+                                    const float* row_weight, int fmt, int group, float clamp_min,
+                                    float swiglu_clamp, void* q, float* sf, void* stream) {
+  return qcast_swiglu_backward_per_token_sf(h, dv, rows, cols, row_weight, fmt, group, clamp_min,
+                                            0, swiglu_clamp, q, sf, stream);
+}
+
+int qcast_swiglu_per_channel_T_sf(const void* h, int64_t rows, int64_t cols,
+                                  const float* row_weight, int fmt, int group, float clamp_min,
+                                  int sf_flags, float swiglu_clamp, void* qT, void* sf,
+                                  uint64_t* clamp_count, void* count_ws, void* stream) {
   if (!any_fmt(fmt)) return QCAST_ERR_FORMAT;
+  if (!sf_flags_ok(sf_flags)) return QCAST_ERR_FORMAT;
   if (group != 128) return QCAST_ERR_GROUP;
   if (rows < 0 || cols < 0 || rows % group != 0 || cols % 8 != 0 || too_big(rows, 2 * cols) ||
-      !qcast::per_channel_t_fits(rows, cols, 2 * cols, fmt))
+      !qcast::per_channel_t_fits(rows, cols, 2 * cols, fmt) ||
+      ((sf_flags & QCAST_SF_PACKED_UE8M0) && (rows / group) % 4 != 0))
     return QCAST_ERR_SHAPE;
   if (swiglu_clamp != swiglu_clamp) return QCAST_ERR_VALUE;
   if (!clamp_min_ok(clamp_min)) return QCAST_ERR_VALUE;
@@ -307,10 +321,18 @@ int qcast_swiglu_per_channel_T(const void* h, int64_t rows, int64_t cols, const 
   const int rc = caps_for_current_device(&caps);
   if (rc != QCAST_OK) return rc;
   return finish(qcast::launch_swiglu_per_channel_T(
-      h, rows, cols, row_weight, fmt, floor_for(fmt, clamp_min), clamp_value(swiglu_clamp),
-      reinterpret_cast<unsigned long long*>(clamp_count),
+      h, rows, cols, row_weight, fmt, floor_for(fmt, clamp_min), (uint32_t)sf_flags,
+      clamp_value(swiglu_clamp), reinterpret_cast<unsigned long long*>(clamp_count),
       static_cast<unsigned long long*>(count_ws), qT, sf, static_cast<hipStream_t>(stream),
       caps));
+}
+
+int qcast_swiglu_per_channel_T(const void* h, int64_t rows, int64_t cols, const float* row_weight,
+                               int fmt, int group, float clamp_min, float swiglu_clamp, void* qT,
+                               float* sf, uint64_t* clamp_count, void* count_ws,
+                               void* stream) {
+  return qcast_swiglu_per_channel_T_sf(h, rows, cols, row_weight, fmt, group, clamp_min, 0,
+                                       swiglu_clamp, qT, sf, clamp_count, count_ws, stream);
 }
 
 int qcast_swiglu_per_token(const void* h, int64_t rows, int64_t cols, const float* row_weight,
@@ -320,9 +342,10 @@ int qcast_swiglu_per_token(const void* h, int64_t rows, int64_t cols, const floa
                                    stream);
 }
 
-int qcast_per_block(const void* x, int64_t rows, int64_t cols, int fmt, int block,
-                    float clamp_min, void* q, float* sf, void* stream) {
+int qcast_per_block_sf(const void* x, int64_t rows, int64_t cols, int fmt, int block,
+                       float clamp_min, int sf_flags, void* q, float* sf, void* stream) {
   if (!any_fmt(fmt)) return QCAST_ERR_FORMAT;
+  if (sf_flags & ~QCAST_SF_ROUND_POW2) return QCAST_ERR_FORMAT;
   if (block != 128) return QCAST_ERR_GROUP;
   if (rows < 0 || cols < 0 || rows % block != 0 || cols % block != 0 || too_big(rows, cols) ||
       !qcast::per_block_fits(rows, cols))
@@ -334,16 +357,24 @@ int qcast_per_block(const void* x, int64_t rows, int64_t cols, int fmt, int bloc
   qcast::LaunchCaps caps;
   const int rc = caps_for_current_device(&caps);
   if (rc != QCAST_OK) return rc;
-  return finish(qcast::launch_per_block(x, rows, cols, fmt, floor_for(fmt, clamp_min), q, sf,
+  return finish(qcast::launch_per_block(x, rows, cols, fmt, floor_for(fmt, clamp_min),
+                                        (uint32_t)sf_flags, q, sf,
                                         static_cast<hipStream_t>(stream), caps));
 }
 
-int qcast_per_channel_T(const void* x, int64_t rows, int64_t cols, int fmt, int group,
-                        float clamp_min, void* qT, float* sf, void* stream) {
+int qcast_per_block(const void* x, int64_t rows, int64_t cols, int fmt, int block,
+                    float clamp_min, void* q, float* sf, void* stream) {
+  return qcast_per_block_sf(x, rows, cols, fmt, block, clamp_min, 0, q, sf, stream);
+}
+
+int qcast_per_channel_T_sf(const void* x, int64_t rows, int64_t cols, int fmt, int group,
+                           float clamp_min, int sf_flags, void* qT, void* sf, void* stream) {
   if (!any_fmt(fmt)) return QCAST_ERR_FORMAT;
+  if (!sf_flags_ok(sf_flags)) return QCAST_ERR_FORMAT;
   if (group != 128) return QCAST_ERR_GROUP;
   if (rows < 0 || cols < 0 || rows % group != 0 || cols % 8 != 0 || too_big(rows, cols) ||
-      !qcast::per_channel_t_fits(rows, cols, cols, fmt))
+      !qcast::per_channel_t_fits(rows, cols, cols, fmt) ||
+      ((sf_flags & QCAST_SF_PACKED_UE8M0) && (rows / group) % 4 != 0))
     return QCAST_ERR_SHAPE;
   if (!clamp_min_ok(clamp_min)) return QCAST_ERR_VALUE;
   if (rows == 0 || cols == 0) return QCAST_OK;
@@ -352,13 +383,20 @@ int qcast_per_channel_T(const void* x, int64_t rows, int64_t cols, int fmt, int 
   qcast::LaunchCaps caps;
   const int rc = caps_for_current_device(&caps);
   if (rc != QCAST_OK) return rc;
-  return finish(qcast::launch_per_channel_T(x, rows, cols, fmt, floor_for(fmt, clamp_min), qT, sf,
+  return finish(qcast::launch_per_channel_T(x, rows, cols, fmt, floor_for(fmt, clamp_min),
+                                            (uint32_t)sf_flags, qT, sf,
                                             static_cast<hipStream_t>(stream), caps));
 }
 
-int qcast_per_channel(const void* x, int64_t rows, int64_t cols, int fmt, int group,
-                      float clamp_min, void* q, float* sf, void* stream) {
+int qcast_per_channel_T(const void* x, int64_t rows, int64_t cols, int fmt, int group,
+                        float clamp_min, void* qT, float* sf, void* stream) {
+  return qcast_per_channel_T_sf(x, rows, cols, fmt, group, clamp_min, 0, qT, sf, stream);
+}
+
+int qcast_per_channel_sf(const void* x, int64_t rows, int64_t cols, int fmt, int group,
+                         float clamp_min, int sf_flags, void* q, float* sf, void* stream) {
   if (!any_fmt(fmt)) return QCAST_ERR_FORMAT;
+  if (sf_flags & ~QCAST_SF_ROUND_POW2) return QCAST_ERR_FORMAT;
   if (group != 128) return QCAST_ERR_GROUP;
   if (rows < 0 || cols < 0 || rows % group != 0 || cols % 8 != 0 || too_big(rows, cols) ||
       !qcast::per_channel_fits(rows, cols))
@@ -370,8 +408,14 @@ int qcast_per_channel(const void* x, int64_t rows, int64_t cols, int fmt, int gr
   qcast::LaunchCaps caps;
   const int rc = caps_for_current_device(&caps);
   if (rc != QCAST_OK) return rc;
-  return finish(qcast::launch_per_channel(x, rows, cols, fmt, floor_for(fmt, clamp_min), q, sf,
+  return finish(qcast::launch_per_channel(x, rows, cols, fmt, floor_for(fmt, clamp_min),
+                                          (uint32_t)sf_flags, q, sf,
                                           static_cast<hipStream_t>(stream), caps));
+}
+
+int qcast_per_channel(const void* x, int64_t rows, int64_t cols, int fmt, int group,
+                      float clamp_min, void* q, float* sf, void* stream) {
+  return qcast_per_channel_sf(x, rows, cols, fmt, group, clamp_min, 0, q, sf, stream);
 }
 
 int qcast_cast_back(const void* q, const float* sf, int64_t rows, int64_t cols, int fmt,

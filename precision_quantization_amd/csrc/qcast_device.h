@@ -115,6 +115,55 @@ __device__ __forceinline__ uint32_t row_of_group(uint32_t k, const SfLayout& lay
   return r;
 }
 
+// The packed UE8M0 word of 4 consecutive groups whose scales sit in
+// 4 * kLanes consecutive lanes (aligned), valid in the first of them: the
+// biased exponent byte of each (power-of-two) scale, lowest group lowest.
+template <int kLanes>
+__device__ __forceinline__ uint32_t gather_ue8m0_word(const Scale& s) {
+  const int lane = threadIdx.x & 63;
+  const uint32_t e = __float_as_uint(s.sf) >> 23;
+  return e | ((uint32_t)__shfl((int)e, lane + kLanes) << 8) |
+         ((uint32_t)__shfl((int)e, lane + 2 * kLanes) << 16) |
+         ((uint32_t)__shfl((int)e, lane + 3 * kLanes) << 24);
+}
+
+// Store the scale of group kr of row r held by this lane (lanes of a group
+// are kLanes consecutive lanes; every active lane calls this), in any
+// layout: fp32 sf[r][kr] or sf[kr][rows_pad]; packed words
+// [r][kr/4] or [kr/4][rows_pad] (4 groups of a word in aligned lanes).
+template <int kLanes>
+__device__ __forceinline__ void store_row_group_scale(void* sf, uint32_t r, uint32_t kr,
+                                                      const Scale& s, const SfLayout& lay) {
+  const int lane = threadIdx.x & 63;
+  const bool col = (lay.flags & kSfColMajor) != 0;
+  if (lay.flags & kSfPacked) {
+    const uint32_t w = gather_ue8m0_word<kLanes>(s);
+    if ((lane & (4 * kLanes - 1)) == 0) {
+      const uint32_t idx = col ? (kr / 4) * lay.rows_pad + r : r * (lay.gpr / 4) + kr / 4;
+      static_cast<uint32_t*>(sf)[idx] = w;
+    }
+  } else if ((lane & (kLanes - 1)) == 0) {
+    static_cast<float*>(sf)[col ? kr * lay.rows_pad + r : r * lay.gpr + kr] = s.sf;
+  }
+}
+
+// Store the scale of group g of row r formed by one lane on its own (no
+// other lane takes part): packed layouts get its exponent byte, which a
+// byte store puts in place beside the bytes other lanes or workgroups
+// write into the same word.
+__device__ __forceinline__ void store_lone_scale(void* sf, uint32_t r, uint32_t g, const Scale& s,
+                                                 const SfLayout& lay) {
+  const bool col = (lay.flags & kSfColMajor) != 0;
+  if (lay.flags & kSfPacked) {
+    const uint64_t word = col ? (uint64_t)(g >> 2) * lay.rows_pad + r
+                              : (uint64_t)r * (lay.gpr >> 2) + (g >> 2);
+    static_cast<uint8_t*>(sf)[word * 4 + (g & 3)] = (uint8_t)(__float_as_uint(s.sf) >> 23);
+  } else {
+    const uint64_t idx = col ? (uint64_t)g * lay.rows_pad + r : (uint64_t)r * lay.gpr + g;
+    static_cast<float*>(sf)[idx] = s.sf;
+  }
+}
+
 // Store the scale of flat group k held by this lane (lanes of a group are
 // kLanes consecutive lanes; every active lane calls this). Row-major fp32 is
 // sf[k]; the other layouts are chosen at run time.
@@ -125,10 +174,7 @@ __device__ __forceinline__ void store_group_scale(void* sf, uint32_t k, const Sc
   if (lay.flags & kSfPacked) {
     // 4 consecutive groups sit in 4 * kLanes consecutive lanes (aligned):
     // the first lane gathers the exponent bytes and writes one word.
-    const uint32_t e = __float_as_uint(s.sf) >> 23;
-    const uint32_t w = e | ((uint32_t)__shfl((int)e, lane + kLanes) << 8) |
-                       ((uint32_t)__shfl((int)e, lane + 2 * kLanes) << 16) |
-                       ((uint32_t)__shfl((int)e, lane + 3 * kLanes) << 24);
+    const uint32_t w = gather_ue8m0_word<kLanes>(s);
     if ((lane & (4 * kLanes - 1)) == 0) {
       uint32_t idx = k / 4;
       if (lay.flags & kSfColMajor) {

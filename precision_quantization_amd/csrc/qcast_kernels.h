@@ -71,20 +71,26 @@ hipError_t launch_swiglu_per_token(const void* h, int64_t rows, int64_t cols, co
                                    hipStream_t stream, const LaunchCaps& caps);
 
 // SwiGLU backward: h [rows, 2*cols] bf16, dv [rows, cols] bf16, w or null
-// -> q [rows, 2*cols] 8-bit codes of [dgate | dup], sf [rows, 2*cols/group].
+// -> codes of the rows [dgate | dup] (2*cols columns each) + scales in the
+// per-token layout sf_flags of those rows; (cols / group) % 4 == 0 for
+// kSfPacked.
 hipError_t launch_swiglu_backward(const void* h, const void* dv, int64_t rows, int64_t cols,
                                   const float* w, int fmt, int group, float floor,
-                                  float swiglu_clamp, void* q, float* sf, hipStream_t stream,
-                                  const LaunchCaps& caps);
+                                  uint32_t sf_flags, float swiglu_clamp, void* q, void* sf,
+                                  hipStream_t stream, const LaunchCaps& caps);
 
-// x [rows, cols] bf16 -> 8-bit codes + one scale per 128 x 128 block.
+// x [rows, cols] bf16 -> codes + one scale per 128 x 128 block (rounded up
+// to a power of two when sf_flags has kSfRound; no other option).
 hipError_t launch_per_block(const void* x, int64_t rows, int64_t cols, int fmt, float floor,
-                            void* q, float* sf, hipStream_t stream, const LaunchCaps& caps);
+                            uint32_t sf_flags, void* q, float* sf, hipStream_t stream,
+                            const LaunchCaps& caps);
 
-// x [rows (tokens), cols (channels)] bf16 -> qT [cols, rows] 8-bit codes +
-// sf [cols, rows/128]; rows % 128 == 0, cols % 8 == 0.
+// x [rows (tokens), cols (channels)] bf16 -> qT [cols, rows] codes + scales
+// in the per-token layout sf_flags of x^T (rows = the cols channels, groups
+// = the rows/128 token groups); rows % 128 == 0, cols % 8 == 0, and
+// (rows / 128) % 4 == 0 for kSfPacked.
 hipError_t launch_per_channel_T(const void* x, int64_t rows, int64_t cols, int fmt, float floor,
-                                void* qT, float* sf, hipStream_t stream,
+                                uint32_t sf_flags, void* qT, void* sf, hipStream_t stream,
                                 const LaunchCaps& caps);
 
 // The memory traffic of launch_per_channel_T alone (same grid, loads and
@@ -94,17 +100,20 @@ hipError_t launch_per_channel_T_traffic(const void* x, int64_t rows, int64_t col
 
 // SwiGLU of h [rows, 2*cols] (clamped when swiglu_clamp > 0, changed values
 // added to *clamp_count when not null, through count_ws as above), then the
-// per-channel cast written transposed: qT [cols, rows], sf [cols, rows/128].
+// per-channel cast written transposed: qT [cols, rows], scales as
+// launch_per_channel_T writes them.
 hipError_t launch_swiglu_per_channel_T(const void* h, int64_t rows, int64_t cols, const float* w,
-                                       int fmt, float floor, float swiglu_clamp,
-                                       unsigned long long* clamp_count,
-                                       unsigned long long* count_ws, void* qT, float* sf,
+                                       int fmt, float floor, uint32_t sf_flags,
+                                       float swiglu_clamp, unsigned long long* clamp_count,
+                                       unsigned long long* count_ws, void* qT, void* sf,
                                        hipStream_t stream, const LaunchCaps& caps);
 
 // x [rows (tokens), cols (channels)] bf16 -> q [rows, cols] 8-bit codes in the
-// input layout + sf [rows/128, cols]; rows % 128 == 0, cols % 8 == 0.
+// input layout + sf [rows/128, cols] (rounded up to powers of two with
+// kSfRound, the one option); rows % 128 == 0, cols % 8 == 0.
 hipError_t launch_per_channel(const void* x, int64_t rows, int64_t cols, int fmt, float floor,
-                              void* q, float* sf, hipStream_t stream, const LaunchCaps& caps);
+                              uint32_t sf_flags, void* q, float* sf, hipStream_t stream,
+                              const LaunchCaps& caps);
 
 // q per-token codes [rows, cols] (or [rows, cols/2] E2M1) + sf [rows, cols/group]
 // -> out [rows, cols] bf16 (out_bf16) or fp32: decode(q) * sf.

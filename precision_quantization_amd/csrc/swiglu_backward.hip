@@ -11,9 +11,11 @@
 // evaluated in fp32 on the clamped g, u when a clamp c > 0 is given, with a
 // zero gradient where the clamp changed the value (g > c; |u| > c). The row
 // [dg | du] (2 * cols values) is then cast per token like any other row:
-// one code row of 2 * cols columns per row, scales [rows, 2 * cols / group].
-// The same page, §四 A, pairs the SwiGLU cast's four formats with this
-// backward.
+// one code row of 2 * cols columns per row, scales [rows, 2 * cols / group]
+// or, on request, in the per-token scale layouts of those rows (round_sf,
+// TMA-aligned column-major, packed UE8M0: the cast config of the second
+// page, §3.1, and the consumer layouts of the first page, §四 C). The same
+// page, §四 A, pairs the SwiGLU cast's four formats with this backward.
 //
 // gfx950 design. A lane owns 8 consecutive columns j of one row: three
 // 16-byte loads (gate, up, dv) and two stores of 8 codes, dg at column j and
@@ -42,7 +44,8 @@ template <int kLanes, bool kWeighted, int kFmt, bool kClamp>
 __global__ __launch_bounds__(kThreads) void swiglu_backward_kernel(
     const uint16_t* __restrict__ h, const uint16_t* __restrict__ dv,
     const float* __restrict__ w, int64_t nchunks, uint32_t chunks_per_row, uint64_t row_magic,
-    int64_t cols, float floor, float clamp, uint8_t* __restrict__ q, float* __restrict__ sf) {
+    int64_t cols, float floor, float clamp, uint32_t row0, SfLayout lay, uint8_t* __restrict__ q,
+    void* __restrict__ sf) {
   const int64_t base0 = (int64_t)blockIdx.x * kThreads * kUnroll + threadIdx.x;
   const uint32_t groups_per_half = chunks_per_row / kLanes;
   u32x4 graw[kUnroll], uraw[kUnroll], draw[kUnroll];
@@ -89,8 +92,12 @@ __global__ __launch_bounds__(kThreads) void swiglu_backward_kernel(
       }
       const float amax_g = lane_group_max<kLanes>(absmax8(dg));
       const float amax_u = lane_group_max<kLanes>(absmax8(du));
-      const Scale sg = group_scale<kFmt>(amax_g, floor);
-      const Scale su = group_scale<kFmt>(amax_u, floor);
+      Scale sg = group_scale<kFmt>(amax_g, floor);
+      Scale su = group_scale<kFmt>(amax_u, floor);
+      if (lay.flags & kSfRound) {
+        sg = round_scale_pow2(sg);
+        su = round_scale_pow2(su);
+      }
 #pragma unroll
       for (int i = 0; i < 8; ++i) {
         dg[i] = dg[i] * sg.inv;
@@ -100,22 +107,20 @@ __global__ __launch_bounds__(kThreads) void swiglu_backward_kernel(
       const uint32_t qc = row * 2 * chunks_per_row + jc;
       store_chunk8<kFmt>(q, qc, dg);
       store_chunk8<kFmt>(q, qc + chunks_per_row, du);
-      if ((threadIdx.x & (kLanes - 1)) == 0) {
-        float* srow = sf + (int64_t)row * 2 * groups_per_half;
-        srow[jc / kLanes] = sg.sf;
-        srow[groups_per_half + jc / kLanes] = su.sf;
-      }
+      // dg groups first, then the du groups, of row row0 + row (a packed
+      // word's 4 groups sit in aligned lanes: groups_per_half % 4 == 0)
+      store_row_group_scale<kLanes>(sf, row0 + row, jc / kLanes, sg, lay);
+      store_row_group_scale<kLanes>(sf, row0 + row, groups_per_half + jc / kLanes, su, lay);
     }
   }
 }
 
 template <int kLanes, bool kWeighted, int kFmt, bool kClamp>
 hipError_t launch(const uint16_t* h, const uint16_t* dv, const float* w, int64_t rows,
-                  int64_t cols, float floor, float clamp, uint8_t* q, float* sf,
-                  hipStream_t stream) {
+                  int64_t cols, float floor, float clamp, const SfLayout& lay, uint8_t* q,
+                  void* sf, hipStream_t stream) {
   const int64_t cpr = cols / 8;
   const uint64_t magic = ((uint64_t(1) << 40) + (uint64_t)cpr - 1) / (uint64_t)cpr;
-  const int64_t sf_per_row = 2 * cols / (kLanes * 8);
   const int64_t slab_rows = kMaxChunksPerLaunch / cpr;
   for (int64_t r0 = 0; r0 < rows; r0 += slab_rows) {
     const int64_t nr = rows - r0 < slab_rows ? rows - r0 : slab_rows;
@@ -125,8 +130,8 @@ hipError_t launch(const uint16_t* h, const uint16_t* dv, const float* w, int64_t
     launch_kernel((swiglu_backward_kernel<kLanes, kWeighted, kFmt, kClamp>),
                   dim3((unsigned)blocks), dim3(kThreads), 0, stream, h + r0 * 2 * cols,
                   dv + r0 * cols, kWeighted ? w + r0 : nullptr, nchunks, (uint32_t)cpr,
-                  magic, cols, floor, clamp, q + code_bytes<kFmt>(r0 * 2 * cols),
-                  sf + r0 * sf_per_row);
+                  magic, cols, floor, clamp, (uint32_t)r0, lay,
+                  q + code_bytes<kFmt>(r0 * 2 * cols), sf);
     const hipError_t err = hipGetLastError();
     if (err != hipSuccess) return err;
   }
@@ -135,56 +140,68 @@ hipError_t launch(const uint16_t* h, const uint16_t* dv, const float* w, int64_t
 
 template <int kLanes, int kFmt, bool kClamp>
 hipError_t launch_w(const uint16_t* h, const uint16_t* dv, const float* w, int64_t rows,
-                    int64_t cols, float floor, float clamp, uint8_t* q, float* sf,
-                    hipStream_t stream) {
-  return w ? launch<kLanes, true, kFmt, kClamp>(h, dv, w, rows, cols, floor, clamp, q, sf, stream)
-           : launch<kLanes, false, kFmt, kClamp>(h, dv, w, rows, cols, floor, clamp, q, sf,
+                    int64_t cols, float floor, float clamp, const SfLayout& lay, uint8_t* q,
+                    void* sf, hipStream_t stream) {
+  return w ? launch<kLanes, true, kFmt, kClamp>(h, dv, w, rows, cols, floor, clamp, lay, q, sf,
+                                                stream)
+           : launch<kLanes, false, kFmt, kClamp>(h, dv, w, rows, cols, floor, clamp, lay, q, sf,
                                                  stream);
 }
 
 template <int kFmt, bool kClamp>
 hipError_t launch_g(const uint16_t* h, const uint16_t* dv, const float* w, int64_t rows,
-                    int64_t cols, int group, float floor, float clamp, uint8_t* q, float* sf,
-                    hipStream_t stream) {
+                    int64_t cols, int group, float floor, float clamp, const SfLayout& lay,
+                    uint8_t* q, void* sf, hipStream_t stream) {
   switch (group) {
-    case 32: return launch_w<4, kFmt, kClamp>(h, dv, w, rows, cols, floor, clamp, q, sf, stream);
-    case 64: return launch_w<8, kFmt, kClamp>(h, dv, w, rows, cols, floor, clamp, q, sf, stream);
+    case 32:
+      return launch_w<4, kFmt, kClamp>(h, dv, w, rows, cols, floor, clamp, lay, q, sf, stream);
+    case 64:
+      return launch_w<8, kFmt, kClamp>(h, dv, w, rows, cols, floor, clamp, lay, q, sf, stream);
     case 128:
-      return launch_w<16, kFmt, kClamp>(h, dv, w, rows, cols, floor, clamp, q, sf, stream);
+      return launch_w<16, kFmt, kClamp>(h, dv, w, rows, cols, floor, clamp, lay, q, sf, stream);
   }
   return hipErrorInvalidValue;
 }
 
 template <int kFmt>
 hipError_t launch_c(const uint16_t* h, const uint16_t* dv, const float* w, int64_t rows,
-                    int64_t cols, int group, float floor, float clamp, uint8_t* q, float* sf,
-                    hipStream_t stream) {
+                    int64_t cols, int group, float floor, float clamp, const SfLayout& lay,
+                    uint8_t* q, void* sf, hipStream_t stream) {
   return clamp > 0.0f
-             ? launch_g<kFmt, true>(h, dv, w, rows, cols, group, floor, clamp, q, sf, stream)
-             : launch_g<kFmt, false>(h, dv, w, rows, cols, group, floor, clamp, q, sf, stream);
+             ? launch_g<kFmt, true>(h, dv, w, rows, cols, group, floor, clamp, lay, q, sf, stream)
+             : launch_g<kFmt, false>(h, dv, w, rows, cols, group, floor, clamp, lay, q, sf,
+                                     stream);
 }
 
 }  // namespace
 
 hipError_t launch_swiglu_backward(const void* h, const void* dv, int64_t rows, int64_t cols,
                                   const float* w, int fmt, int group, float floor,
-                                  float swiglu_clamp, void* q, float* sf, hipStream_t stream,
-                                  const LaunchCaps& caps) {
+                                  uint32_t sf_flags, float swiglu_clamp, void* q, void* sf,
+                                  hipStream_t stream, const LaunchCaps& caps) {
   (void)caps;
   if (rows == 0 || cols == 0) return hipSuccess;
-  if (cols / 8 >= kMaxChunksPerRow) return hipErrorInvalidValue;
+  if (cols / 8 >= kMaxChunksPerRow || rows >= (int64_t(1) << 32)) return hipErrorInvalidValue;
+  // The scale layout of the rows [dg | du]; packed words of 4 groups must
+  // not straddle the two halves.
+  if ((sf_flags & kSfPacked) && (cols / group) % 4 != 0) return hipErrorInvalidValue;
+  const SfLayout lay = make_sf_layout(rows, 2 * cols, group, sf_flags);
   const uint16_t* hp = static_cast<const uint16_t*>(h);
   const uint16_t* dp = static_cast<const uint16_t*>(dv);
   uint8_t* qp = static_cast<uint8_t*>(q);
   switch (fmt) {
     case kE4M3:
-      return launch_c<kE4M3>(hp, dp, w, rows, cols, group, floor, swiglu_clamp, qp, sf, stream);
+      return launch_c<kE4M3>(hp, dp, w, rows, cols, group, floor, swiglu_clamp, lay, qp, sf,
+                             stream);
     case kE5M2:
-      return launch_c<kE5M2>(hp, dp, w, rows, cols, group, floor, swiglu_clamp, qp, sf, stream);
+      return launch_c<kE5M2>(hp, dp, w, rows, cols, group, floor, swiglu_clamp, lay, qp, sf,
+                             stream);
     case kE2M1:
-      return launch_c<kE2M1>(hp, dp, w, rows, cols, group, floor, swiglu_clamp, qp, sf, stream);
+      return launch_c<kE2M1>(hp, dp, w, rows, cols, group, floor, swiglu_clamp, lay, qp, sf,
+                             stream);
     case kE5M6:
-      return launch_c<kE5M6>(hp, dp, w, rows, cols, group, floor, swiglu_clamp, qp, sf, stream);
+      return launch_c<kE5M6>(hp, dp, w, rows, cols, group, floor, swiglu_clamp, lay, qp, sf,
+                             stream);
   }
   return hipErrorInvalidValue;
 }

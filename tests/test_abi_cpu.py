@@ -64,7 +64,7 @@ def test_binding_names_match_the_c_entry_points():
 
 
 def test_abi_version_and_status_strings(lib):
-    assert lib.qcast_abi_version() == 4
+    assert lib.qcast_abi_version() == 5
     for s in range(9):
         assert lib.qcast_status_str(s).decode()
     assert lib.qcast_status_str(99).decode() == "unknown status"
@@ -379,3 +379,39 @@ def test_noalloc_scratch_size_is_declared():
     src = open(os.path.join(ROOT, "precision_quantization_amd", "csrc", "qcast_abi.hip")).read()
     assert "static __device__ __align__(256) unsigned long long scratch[" in src
     assert "hipGetSymbolAddress" in src and "hipMalloc" not in src
+
+
+def test_layouts_of_the_other_casts_validation(lib):
+    nan = float("nan")
+    # per-block and input-layout per-channel: round_sf only
+    f = lib.qcast_per_block_sf
+    for flags in (2, 4, 6, 8):
+        assert f(A16, 256, 256, E4M3, 128, 0.0, flags, A16, A16, None) == ERR_FORMAT
+    assert f(A16, 256, 256, E4M3, 128, 0.0, 1, None, A16, None) == ERR_NULL
+    assert f(A16, 256, 256, E4M3, 128, nan, 1, A16, A16, None) == ERR_VALUE
+    g = lib.qcast_per_channel_sf
+    for flags in (2, 4, 6, 8):
+        assert g(A16, 256, 64, E4M3, 128, 0.0, flags, A16, A16, None) == ERR_FORMAT
+    assert g(A16, 256, 64, E2M1, 128, 0.0, 1, A16, None, None) == ERR_NULL
+    # transposed per-channel: every layout; packed words need 4 token groups
+    t = lib.qcast_per_channel_T_sf
+    assert t(A16, 512, 64, E4M3, 128, 0.0, 8, A16, A16, None) == ERR_FORMAT
+    assert t(A16, 384, 64, E4M3, 128, 0.0, 4, A16, A16, None) == ERR_SHAPE
+    assert t(A16, 384, 64, E4M3, 128, 0.0, 3, A16, None, None) == ERR_NULL    # col-major fine
+    assert t(A16, 512, 64, E4M3, 128, 0.0, 6, A16, None, None) == ERR_NULL
+    assert t(A16, 512, 64, E5M2, 128, 0.0, 4, A16, A16 + 2, None) == ERR_ALIGN
+    assert t(None, 0, 64, E4M3, 128, 0.0, 4, None, None, None) == OK
+    u = lib.qcast_swiglu_per_channel_T_sf
+    assert u(A16, 512, 64, None, E4M3, 128, 0.0, 8, 0.0, A16, A16, None, None, None) == ERR_FORMAT
+    assert u(A16, 384, 64, None, E4M3, 128, 0.0, 4, 0.0, A16, A16, None, None, None) == ERR_SHAPE
+    assert u(A16, 512, 64, None, E4M3, 128, 0.0, 5, nan, A16, A16, None, None, None) == ERR_VALUE
+    assert u(A16, 512, 64, None, E4M3, 128, 0.0, 4, 1.0, A16, None, None, None, None) == ERR_NULL
+    # backward: packed words must not straddle the dg and du halves
+    b = lib.qcast_swiglu_backward_per_token_sf
+    assert b(A16, A16, 4, 256, None, E4M3, 128, 0.0, 8, 0.0, A16, A16, None) == ERR_FORMAT
+    assert b(A16, A16, 4, 256, None, E4M3, 128, 0.0, 4, 0.0, A16, A16, None) == ERR_SHAPE
+    assert b(A16, A16, 4, 384, None, E4M3, 128, 0.0, 4, 0.0, A16, A16, None) == ERR_SHAPE
+    assert b(A16, A16, 4, 512, None, E4M3, 128, 0.0, 4, 0.0, A16, None, None) == ERR_NULL
+    assert b(A16, A16, 4, 256, None, E4M3, 128, 0.0, 2, 0.0, A16, None, None) == ERR_NULL
+    assert b(A16, A16, 4, 256, None, E4M3, 128, nan, 2, 0.0, A16, A16, None) == ERR_VALUE
+    assert b(None, None, 0, 256, None, E4M3, 128, 0.0, 2, 0.0, None, None, None) == OK
