@@ -332,6 +332,26 @@ def extra_calls(wls, dev):
                   r * 2 * n * 2 + r * n * 2 + r * 4 + r * n + r * (2 * n // 32) * 4,
                   lambda hg=hg, dvg=dvg, wg=wg, q=qb2, s=sb2: pq.qcast_swiglu_backward_per_token(
                       hg, dvg, wg, "e2m1", 32, swiglu_clamp=6.0, out=q, out_sf=s)))
+    # the scale layouts of the transposed and backward casts: packed UE8M0,
+    # column-major (the activation workload, and the backward's inputs)
+    pc = pq.SF_PACKED_UE8M0 | pq.SF_COL_MAJOR
+    r, c = a.shape
+    shape, dt = pq.sf_layout_shape(c, r, 128, pc)
+    qT3 = torch.empty(c, r, dtype=torch.float8_e4m3fn, device=dev)
+    sT3 = torch.empty(shape, dtype=dt, device=dev)
+    calls.append(("per_channel_T_ue8m0_colmajor", [r, c],
+                  2 * r * c + r * c + shape[0] * shape[1] * 4,
+                  lambda a=a, q=qT3, s=sT3, f=pc: pq.qcast_per_channel_T_sf(
+                      a, "e4m3", 128, sf_flags=f, out=q, out_sf=s)))
+    r, n = wl.rows, wl.cols
+    shape, dt = pq.sf_layout_shape(r, 2 * n, 128, pc)
+    qb3 = torch.empty(r, 2 * n, dtype=torch.float8_e4m3fn, device=dev)
+    sb3 = torch.empty(shape, dtype=dt, device=dev)
+    calls.append(("swiglu_backward_ue8m0_colmajor", [r, 2 * n],
+                  r * 2 * n * 2 + r * n * 2 + r * 4 + r * 2 * n + shape[0] * shape[1] * 4,
+                  lambda hg=hg, dvg=dvg, wg=wg, q=qb3, s=sb3, f=pc:
+                  pq.qcast_swiglu_backward_per_token_sf(hg, dvg, wg, "e4m3", 128, sf_flags=f,
+                                                        swiglu_clamp=6.0, out=q, out_sf=s)))
     # per-token cast with 1 x 32 groups and fp32 column-major scales
     x = by["per_token"].x.to(dev)
     r, c = x.shape

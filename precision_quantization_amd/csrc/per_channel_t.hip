@@ -322,7 +322,7 @@ struct Smem {
 // Scales, codes and stores of one tile whose values are in raw. Starts with
 // the workgroup converged; with kReuse (a workgroup that goes on to another
 // tile) it also ends converged, with the LDS free again.
-template <int kFmt, bool kReuse, class Tile>
+template <int kFmt, bool kReuse, bool kLayout, class Tile>
 __device__ __forceinline__ void process_tile(const TileCoord& tc, const Tile& tile, uint32_t rows,
                                              float floor, const SfLayout& lay, Smem<kFmt>& sm,
                                              uint8_t* __restrict__ qT, void* __restrict__ sf) {
@@ -348,9 +348,14 @@ __device__ __forceinline__ void process_tile(const TileCoord& tc, const Tile& ti
     const float m = fmaxf(fmaxf(sm.wave_amax[gi][0][c], sm.wave_amax[gi][1][c]),
                           fmaxf(sm.wave_amax[gi][2][c], sm.wave_amax[gi][3][c]));
     Scale s = group_scale<kFmt>(m, floor);
-    if (lay.flags & kSfRound) s = round_scale_pow2(s);
+    if (kLayout && (lay.flags & kSfRound)) s = round_scale_pow2(s);
     sm.inv_s[gi][c] = s.inv;
-    if (c < tc.nc && gi < tc.ng) store_lone_scale(sf, tc.c0 + c, tc.gt * kTG + gi, s, lay);
+    if (c < tc.nc && gi < tc.ng) {
+      if (kLayout)
+        store_lone_scale(sf, tc.c0 + c, tc.gt * kTG + gi, s, lay);
+      else
+        static_cast<float*>(sf)[(uint64_t)(tc.c0 + c) * lay.gpr + tc.gt * kTG + gi] = s.sf;
+    }
   }
   __syncthreads();
 
@@ -417,8 +422,8 @@ __device__ __forceinline__ void process_tile(const TileCoord& tc, const Tile& ti
   if (kReuse) __syncthreads();  // the LDS tile is reused by the next tile
 }
 
-// One workgroup per tile.
-template <int kFmt>
+// One workgroup per tile; kLayout: scale options other than plain fp32.
+template <int kFmt, bool kLayout>
 __global__ __launch_bounds__(kThreads) void per_channel_t_kernel(
     const uint16_t* __restrict__ x, uint32_t rows, uint32_t cols, uint32_t ngroups,
     uint32_t nct, uint32_t ntg, uint32_t ntiles, uint32_t per_xcd, FastDiv sdiv, float floor,
@@ -430,7 +435,7 @@ __global__ __launch_bounds__(kThreads) void per_channel_t_kernel(
   const TileCoord tc = tile_coord(tau, ngroups, cols, nct, ntg, sdiv);
   Bf16Tile tile;
   load_tile(x, cols, tc, tile.raw);
-  process_tile<kFmt, false>(tc, tile, rows, floor, lay, sm, qT, sf);
+  process_tile<kFmt, false, kLayout>(tc, tile, rows, floor, lay, sm, qT, sf);
 }
 
 // The cast's memory traffic alone, for measurement: the same workgroup ->
@@ -469,7 +474,7 @@ __global__ __launch_bounds__(kThreads) void per_channel_t_traffic_kernel(
 // workgroup ends in an atomic add on the same word, serialized where the
 // word lives, so a capped grid walks the virtual workgroup indices
 // [0, vgrid) with a stride of gridDim.x.
-template <int kFmt, bool kWeighted, bool kClamp, int kCount>
+template <int kFmt, bool kWeighted, bool kClamp, int kCount, bool kLayout>
 __global__ __launch_bounds__(kThreads) void swiglu_per_channel_t_kernel(
     const uint16_t* __restrict__ h, const float* __restrict__ w, uint32_t rows, uint32_t cols,
     uint32_t ngroups, uint32_t nct, uint32_t ntg, uint32_t ntiles, uint32_t per_xcd,
@@ -485,7 +490,7 @@ __global__ __launch_bounds__(kThreads) void swiglu_per_channel_t_kernel(
       const TileCoord tc = tile_coord<kSwStrip>(tau, ngroups, cols, nct, ntg, sdiv);
       F32Tile tile;
       n += load_swiglu_tile<kWeighted, kClamp, true>(h, w, cols, clamp, tc, tile);
-      process_tile<kFmt, true>(tc, tile, rows, floor, lay, sm, qT, sf);
+      process_tile<kFmt, true, kLayout>(tc, tile, rows, floor, lay, sm, qT, sf);
     }
     add_wave_counts(n, count);
   } else {
@@ -504,7 +509,7 @@ __global__ __launch_bounds__(kThreads) void swiglu_per_channel_t_kernel(
     // processed, so the slot atomic's round trip overlaps that work.
     SlotCount<> sc;
     if constexpr (kCount == kCountSlotted) sc.arrive(n, slots);
-    if (has_tile) process_tile<kFmt, false>(tc, tile, rows, floor, lay, sm, qT, sf);
+    if (has_tile) process_tile<kFmt, false, kLayout>(tc, tile, rows, floor, lay, sm, qT, sf);
     if constexpr (kCount == kCountSlotted) sc.finish(slots, count);
   }
 }
@@ -551,7 +556,7 @@ struct CountArgs {
   unsigned long long* slots;  // count workspace or null
 };
 
-template <int kFmt, bool kWeighted, bool kClamp>
+template <int kFmt, bool kWeighted, bool kClamp, bool kLayout>
 hipError_t launch_swiglu_t(const uint16_t* h, const float* w, int64_t rows, int64_t cols,
                            const Grid& g, float floor, float clamp, const SfLayout& lay,
                            const CountArgs& ca, uint8_t* qT, void* sf, hipStream_t stream,
@@ -563,28 +568,47 @@ hipError_t launch_swiglu_t(const uint16_t* h, const float* w, int64_t rows, int6
     const bool slotted =
         ca.slots && (int64_t)g.grid < (int64_t(kCountSlots) << (64 - kSlotArrivalShift));
     if (ca.count && slotted) {
-      launch_kernel((swiglu_per_channel_t_kernel<kFmt, kWeighted, true, kCountSlotted>),
+      launch_kernel((swiglu_per_channel_t_kernel<kFmt, kWeighted, true, kCountSlotted, kLayout>),
                     dim3(g.grid), dim3(kThreads), 0, stream, h, w, (uint32_t)rows,
-                    (uint32_t)cols, g.ngroups, g.nct, g.ntg, g.ntiles, g.per_xcd, g.sw_strip_div, g.grid, floor, clamp,
-                    lay, ca.count, ca.slots, qT, sf);
+                    (uint32_t)cols, g.ngroups, g.nct, g.ntg, g.ntiles, g.per_xcd,
+                    g.sw_strip_div, g.grid, floor, clamp, lay, ca.count, ca.slots, qT, sf);
       return hipGetLastError();
     }
     if (ca.count) {
       uint32_t grid = g.grid;
       const int64_t cap = (int64_t)caps.num_cus * QCAST_PC_COUNT_WG_PER_CU;
       if (QCAST_PC_COUNT_WG_PER_CU > 0 && cap < grid) grid = (uint32_t)cap;
-      launch_kernel((swiglu_per_channel_t_kernel<kFmt, kWeighted, true, kCountDirect>),
+      launch_kernel((swiglu_per_channel_t_kernel<kFmt, kWeighted, true, kCountDirect, kLayout>),
                     dim3(grid), dim3(kThreads), 0, stream, h, w, (uint32_t)rows,
-                    (uint32_t)cols, g.ngroups, g.nct, g.ntg, g.ntiles, g.per_xcd, g.sw_strip_div, g.grid, floor, clamp,
-                    lay, ca.count, ca.slots, qT, sf);
+                    (uint32_t)cols, g.ngroups, g.nct, g.ntg, g.ntiles, g.per_xcd,
+                    g.sw_strip_div, g.grid, floor, clamp, lay, ca.count, ca.slots, qT, sf);
       return hipGetLastError();
     }
   }
-  launch_kernel((swiglu_per_channel_t_kernel<kFmt, kWeighted, kClamp, kCountNone>),
+  launch_kernel((swiglu_per_channel_t_kernel<kFmt, kWeighted, kClamp, kCountNone, kLayout>),
                 dim3(g.grid), dim3(kThreads), 0, stream, h, w, (uint32_t)rows, (uint32_t)cols,
-                g.ngroups, g.nct, g.ntg, g.ntiles, g.per_xcd, g.sw_strip_div, g.grid, floor, clamp, lay, ca.count,
-                ca.slots, qT, sf);
+                g.ngroups, g.nct, g.ntg, g.ntiles, g.per_xcd, g.sw_strip_div, g.grid, floor,
+                clamp, lay, ca.count, ca.slots, qT, sf);
   return hipGetLastError();
+}
+
+template <int kFmt, bool kLayout>
+hipError_t launch_swiglu_t_wc(const uint16_t* h, const float* w, int64_t rows, int64_t cols,
+                              const Grid& g, float floor, float clamp, const SfLayout& lay,
+                              const CountArgs& ca, uint8_t* qT, void* sf, hipStream_t stream,
+                              const LaunchCaps& caps) {
+  if (w) {
+    return clamp > 0.0f
+               ? launch_swiglu_t<kFmt, true, true, kLayout>(h, w, rows, cols, g, floor, clamp,
+                                                            lay, ca, qT, sf, stream, caps)
+               : launch_swiglu_t<kFmt, true, false, kLayout>(h, w, rows, cols, g, floor, clamp,
+                                                             lay, ca, qT, sf, stream, caps);
+  }
+  return clamp > 0.0f
+             ? launch_swiglu_t<kFmt, false, true, kLayout>(h, w, rows, cols, g, floor, clamp,
+                                                           lay, ca, qT, sf, stream, caps)
+             : launch_swiglu_t<kFmt, false, false, kLayout>(h, w, rows, cols, g, floor, clamp,
+                                                            lay, ca, qT, sf, stream, caps);
 }
 
 template <int kFmt>
@@ -592,18 +616,16 @@ hipError_t launch_swiglu_t_fmt(const uint16_t* h, const float* w, int64_t rows, 
                                const Grid& g, float floor, float clamp, const SfLayout& lay,
                                const CountArgs& ca, uint8_t* qT, void* sf, hipStream_t stream,
                                const LaunchCaps& caps) {
-  if (w) {
-    return clamp > 0.0f
-               ? launch_swiglu_t<kFmt, true, true>(h, w, rows, cols, g, floor, clamp, lay, ca, qT, sf,
-                                                   stream, caps)
-               : launch_swiglu_t<kFmt, true, false>(h, w, rows, cols, g, floor, clamp, lay, ca, qT,
-                                                    sf, stream, caps);
-  }
-  return clamp > 0.0f
-             ? launch_swiglu_t<kFmt, false, true>(h, w, rows, cols, g, floor, clamp, lay, ca, qT, sf,
-                                                  stream, caps)
-             : launch_swiglu_t<kFmt, false, false>(h, w, rows, cols, g, floor, clamp, lay, ca, qT,
-                                                   sf, stream, caps);
+  return lay.flags ? launch_swiglu_t_wc<kFmt, true>(h, w, rows, cols, g, floor, clamp, lay, ca,
+                                                    qT, sf, stream, caps)
+                   : launch_swiglu_t_wc<kFmt, false>(h, w, rows, cols, g, floor, clamp, lay, ca,
+                                                     qT, sf, stream, caps);
+}
+
+// The transposed cast's kernel for fmt, with or without scale options.
+template <int kFmt>
+auto cast_kernel(bool layout) {
+  return layout ? per_channel_t_kernel<kFmt, true> : per_channel_t_kernel<kFmt, false>;
 }
 
 }  // namespace
@@ -622,10 +644,11 @@ hipError_t launch_per_channel_T(const void* x, int64_t rows, int64_t cols, int f
   if (!make_grid(rows, cols, cols, fmt, &g)) return hipErrorInvalidValue;
   if (g.ntiles == 0) return hipSuccess;
   if ((sf_flags & kSfPacked) && g.ngroups % 4 != 0) return hipErrorInvalidValue;
-  auto kernel = fmt == kE4M3   ? per_channel_t_kernel<kE4M3>
-                : fmt == kE5M2 ? per_channel_t_kernel<kE5M2>
-                : fmt == kE2M1 ? per_channel_t_kernel<kE2M1>
-                : fmt == kE5M6 ? per_channel_t_kernel<kE5M6>
+  const bool any = sf_flags != 0;
+  auto kernel = fmt == kE4M3   ? cast_kernel<kE4M3>(any)
+                : fmt == kE5M2 ? cast_kernel<kE5M2>(any)
+                : fmt == kE2M1 ? cast_kernel<kE2M1>(any)
+                : fmt == kE5M6 ? cast_kernel<kE5M6>(any)
                                : nullptr;
   if (!kernel) return hipErrorInvalidValue;
   // the layout of x^T: rows are the channels, groups the token groups

@@ -40,7 +40,8 @@ constexpr float kLog2e = 1.4426950408889634f;
 constexpr int64_t kMaxChunksPerLaunch = int64_t(1) << 24;
 constexpr int64_t kMaxChunksPerRow = int64_t(1) << 16;
 
-template <int kLanes, bool kWeighted, int kFmt, bool kClamp>
+// kLayout: scale options other than plain fp32 row-major.
+template <int kLanes, bool kWeighted, int kFmt, bool kClamp, bool kLayout>
 __global__ __launch_bounds__(kThreads) void swiglu_backward_kernel(
     const uint16_t* __restrict__ h, const uint16_t* __restrict__ dv,
     const float* __restrict__ w, int64_t nchunks, uint32_t chunks_per_row, uint64_t row_magic,
@@ -94,7 +95,7 @@ __global__ __launch_bounds__(kThreads) void swiglu_backward_kernel(
       const float amax_u = lane_group_max<kLanes>(absmax8(du));
       Scale sg = group_scale<kFmt>(amax_g, floor);
       Scale su = group_scale<kFmt>(amax_u, floor);
-      if (lay.flags & kSfRound) {
+      if (kLayout && (lay.flags & kSfRound)) {
         sg = round_scale_pow2(sg);
         su = round_scale_pow2(su);
       }
@@ -109,13 +110,19 @@ __global__ __launch_bounds__(kThreads) void swiglu_backward_kernel(
       store_chunk8<kFmt>(q, qc + chunks_per_row, du);
       // dg groups first, then the du groups, of row row0 + row (a packed
       // word's 4 groups sit in aligned lanes: groups_per_half % 4 == 0)
-      store_row_group_scale<kLanes>(sf, row0 + row, jc / kLanes, sg, lay);
-      store_row_group_scale<kLanes>(sf, row0 + row, groups_per_half + jc / kLanes, su, lay);
+      if (kLayout) {
+        store_row_group_scale<kLanes>(sf, row0 + row, jc / kLanes, sg, lay);
+        store_row_group_scale<kLanes>(sf, row0 + row, groups_per_half + jc / kLanes, su, lay);
+      } else if ((threadIdx.x & (kLanes - 1)) == 0) {
+        float* srow = static_cast<float*>(sf) + (uint64_t)(row0 + row) * 2 * groups_per_half;
+        srow[jc / kLanes] = sg.sf;
+        srow[groups_per_half + jc / kLanes] = su.sf;
+      }
     }
   }
 }
 
-template <int kLanes, bool kWeighted, int kFmt, bool kClamp>
+template <int kLanes, bool kWeighted, int kFmt, bool kClamp, bool kLayout>
 hipError_t launch(const uint16_t* h, const uint16_t* dv, const float* w, int64_t rows,
                   int64_t cols, float floor, float clamp, const SfLayout& lay, uint8_t* q,
                   void* sf, hipStream_t stream) {
@@ -127,7 +134,7 @@ hipError_t launch(const uint16_t* h, const uint16_t* dv, const float* w, int64_t
     const int64_t nchunks = nr * cpr;
     const int64_t per_block = (int64_t)kThreads * kUnroll;
     const int64_t blocks = (nchunks + per_block - 1) / per_block;
-    launch_kernel((swiglu_backward_kernel<kLanes, kWeighted, kFmt, kClamp>),
+    launch_kernel((swiglu_backward_kernel<kLanes, kWeighted, kFmt, kClamp, kLayout>),
                   dim3((unsigned)blocks), dim3(kThreads), 0, stream, h + r0 * 2 * cols,
                   dv + r0 * cols, kWeighted ? w + r0 : nullptr, nchunks, (uint32_t)cpr,
                   magic, cols, floor, clamp, (uint32_t)r0, lay,
@@ -142,10 +149,16 @@ template <int kLanes, int kFmt, bool kClamp>
 hipError_t launch_w(const uint16_t* h, const uint16_t* dv, const float* w, int64_t rows,
                     int64_t cols, float floor, float clamp, const SfLayout& lay, uint8_t* q,
                     void* sf, hipStream_t stream) {
-  return w ? launch<kLanes, true, kFmt, kClamp>(h, dv, w, rows, cols, floor, clamp, lay, q, sf,
-                                                stream)
-           : launch<kLanes, false, kFmt, kClamp>(h, dv, w, rows, cols, floor, clamp, lay, q, sf,
-                                                 stream);
+  if (lay.flags) {
+    return w ? launch<kLanes, true, kFmt, kClamp, true>(h, dv, w, rows, cols, floor, clamp, lay,
+                                                        q, sf, stream)
+             : launch<kLanes, false, kFmt, kClamp, true>(h, dv, w, rows, cols, floor, clamp, lay,
+                                                         q, sf, stream);
+  }
+  return w ? launch<kLanes, true, kFmt, kClamp, false>(h, dv, w, rows, cols, floor, clamp, lay, q,
+                                                       sf, stream)
+           : launch<kLanes, false, kFmt, kClamp, false>(h, dv, w, rows, cols, floor, clamp, lay,
+                                                        q, sf, stream);
 }
 
 template <int kFmt, bool kClamp>
