@@ -239,16 +239,19 @@ struct Bf16Tile {
 struct F32Tile {
   float v[kPasses][4][8];
 
+  // The lane's maximum is an fp32 max of magnitudes (one v_max_f32 with an
+  // abs modifier per value); the cross-lane steps then compare the bit
+  // patterns of those non-negative values, which order as the values do.
   __device__ __forceinline__ void group_amax(int gi, float out[8]) const {
 #pragma unroll
     for (int j = 0; j < 8; ++j) {
-      uint32_t m = 0u;
+      float mf = 0.0f;
 #pragma unroll
       for (int pp = 0; pp < kPassesPerGroup; ++pp) {
 #pragma unroll
-        for (int i = 0; i < 4; ++i)
-          m = umax(m, __float_as_uint(v[gi * kPassesPerGroup + pp][i][j]) & 0x7fffffffu);
+        for (int i = 0; i < 4; ++i) mf = fmaxf(mf, fabsf(v[gi * kPassesPerGroup + pp][i][j]));
       }
+      uint32_t m = __float_as_uint(mf);
       if (kCC == 8) m = umax(m, dpp<kDppRor8>(m));
       m = max_xor16(m);
       m = max_xor32(m);
