@@ -229,6 +229,39 @@ struct Bf16Tile {
     }
   }
 
+  // The same maxima, reduced as a butterfly over the 8 lanes (bits 3, 4, 5
+  // of the lane index) that hold the chunk, each exchange carrying two
+  // different channels: after it every lane holds one channel's maximum,
+  // channel lane_channel() of its chunk. 3 swaps and 4 packed maxima
+  // instead of 8 swaps and 12.
+  __device__ __forceinline__ float group_amax_lane(int gi) const {
+    uint32_t m[4] = {0u, 0u, 0u, 0u};
+#pragma unroll
+    for (int pp = 0; pp < kPassesPerGroup; ++pp) {
+      const int p = gi * kPassesPerGroup + pp;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        m[0] = pk_umax16(m[0], raw[p][i].x & 0x7fff7fffu);
+        m[1] = pk_umax16(m[1], raw[p][i].y & 0x7fff7fffu);
+        m[2] = pk_umax16(m[2], raw[p][i].z & 0x7fff7fffu);
+        m[3] = pk_umax16(m[3], raw[p][i].w & 0x7fff7fffu);
+      }
+    }
+    // lanes i ^ 16: words 0, 1 stay with the even rows, words 2, 3 go to the odd
+    uint32_t n[2];
+#pragma unroll
+    for (int w = 0; w < 2; ++w) {
+      const auto r = __builtin_amdgcn_permlane16_swap(m[w], m[w + 2], false, false);
+      n[w] = pk_umax16((uint32_t)r[0], (uint32_t)r[1]);
+    }
+    // lanes i ^ 32: word n[0] stays with the lower half, n[1] goes to the upper
+    const auto r = __builtin_amdgcn_permlane32_swap(n[0], n[1], false, false);
+    uint32_t q = pk_umax16((uint32_t)r[0], (uint32_t)r[1]);
+    // lanes i ^ 8 (both halves), then each lane takes its half
+    q = pk_umax16(q, dpp<kDppRor8>(q));
+    return (threadIdx.x & 8) ? bf16_hi(q) : bf16_lo(q);
+  }
+
   __device__ __forceinline__ float value(int p, int i, int j) const {
     const uint32_t word = raw[p][i][j >> 1];
     return (j & 1) ? bf16_hi(word) : bf16_lo(word);
@@ -259,8 +292,50 @@ struct F32Tile {
     }
   }
 
+  // As Bf16Tile::group_amax_lane, on fp32 values: 6 swaps and 7 maxima
+  // instead of 16 swaps and 24.
+  __device__ __forceinline__ float group_amax_lane(int gi) const {
+    uint32_t m[8];
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      float mf = 0.0f;
+#pragma unroll
+      for (int pp = 0; pp < kPassesPerGroup; ++pp) {
+#pragma unroll
+        for (int i = 0; i < 4; ++i) mf = fmaxf(mf, fabsf(v[gi * kPassesPerGroup + pp][i][j]));
+      }
+      m[j] = __float_as_uint(mf);
+    }
+    uint32_t n[4];
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const auto r = __builtin_amdgcn_permlane16_swap(m[j], m[j + 4], false, false);
+      n[j] = umax((uint32_t)r[0], (uint32_t)r[1]);
+    }
+    uint32_t q[2];
+#pragma unroll
+    for (int j = 0; j < 2; ++j) {
+      const auto r = __builtin_amdgcn_permlane32_swap(n[j], n[j + 2], false, false);
+      q[j] = umax((uint32_t)r[0], (uint32_t)r[1]);
+    }
+    const bool odd = (threadIdx.x & 8) != 0;
+    const uint32_t keep = odd ? q[1] : q[0];
+    const uint32_t send = odd ? q[0] : q[1];
+    return __uint_as_float(umax(keep, dpp<kDppRor8>(send)));
+  }
+
   __device__ __forceinline__ float value(int p, int i, int j) const { return v[p][i][j]; }
 };
+
+// The channel of its 8-channel chunk whose column maximum a lane holds after
+// group_amax_lane: v_permlane16_swap exchanges the odd rows of its first
+// operand with the even rows of its second, v_permlane32_swap the upper half
+// of the first with the lower half of the second, so lane bit 4 picks the
+// upper four channels, bit 5 the upper two of those, bit 3 the odd one.
+__device__ __forceinline__ int lane_channel() {
+  const int l = threadIdx.x & 63;
+  return ((l >> 3) & 1) | (((l >> 5) & 1) << 1) | (((l >> 4) & 1) << 2);
+}
 
 constexpr float kLog2e = 1.4426950408889634f;
 
@@ -337,11 +412,16 @@ __device__ __forceinline__ void process_tile(const TileCoord& tc, const Tile& ti
   // Column abs-maxima per token group within each wave, then across waves.
 #pragma unroll
   for (int gi = 0; gi < kTG; ++gi) {
-    float m[8];
-    tile.group_amax(gi, m);
-    if ((t & 63) < kCC) {
+    if constexpr (kCC == 8) {
+      // every lane writes one channel's maximum of the wave
+      sm.wave_amax[gi][wave][ch * 8 + lane_channel()] = tile.group_amax_lane(gi);
+    } else {
+      float m[8];
+      tile.group_amax(gi, m);
+      if ((t & 63) < kCC) {
 #pragma unroll
-      for (int j = 0; j < 8; ++j) sm.wave_amax[gi][wave][ch * 8 + j] = m[j];
+        for (int j = 0; j < 8; ++j) sm.wave_amax[gi][wave][ch * 8 + j] = m[j];
+      }
     }
   }
   __syncthreads();
