@@ -450,11 +450,12 @@ __device__ __forceinline__ uint32_t wave_clamp_count(float g, float u, float c) 
 // sum |y| + C lies in [C, 2C], where fp32 spacing is exactly that grid
 // spacing, so (|y| + C) - C is |y| rounded to the grid with ties to even
 // (C is an even multiple of the spacing) and the subtraction is exact. The
-// sign is put back afterwards (tiny negatives stay -0), and y is first
-// clamped to the largest finite magnitude (saturation).
+// sign is put back afterwards (tiny negatives stay -0). No clamp is needed:
+// the casts scale every group so that |y| <= 65024 * (1 + 2^-22) (three
+// rounded operations from amax / 65024), which rounds to 65024, far below
+// the midpoint 65280 where rounding would leave the format; non-finite
+// inputs, which the casts do not define, come out as infinity or NaN codes.
 __device__ __forceinline__ float e5m6_grid(float y) {
-  constexpr float kMax = 65024.0f;
-  y = __builtin_amdgcn_fmed3f(y, -kMax, kMax);
   const uint32_t b = __float_as_uint(y);
   const uint32_t c_bits = (b & 0x7f800000u) + (17u << 23);
   const float c = __uint_as_float(c_bits > 0x41000000u ? c_bits : 0x41000000u);  // >= 8
