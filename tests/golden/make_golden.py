@@ -39,6 +39,15 @@ CASES = {
     "swiglu_T_256x128": lambda: _op(workloads.swiglu_input(rows=256, cols=128), "swiglu_T"),
     "per_channel_256x384": lambda: _op(workloads.activation_channel(rows=256, cols=384),
                                        "per_channel"),
+    # scale options of the other casts, in the other formats
+    "per_channel_T_512x136_ue8m0_colmajor": lambda: _op(
+        workloads.activation_channel(rows=512, cols=136), "per_channel_T_ue8m0_cm"),
+    "swiglu_T_512x72_e2m1_round_colmajor": lambda: _op(
+        _fmt(workloads.swiglu_input(rows=512, cols=72), "e2m1"), "swiglu_T_round_cm"),
+    "per_block_256x512_e5m6_round": lambda: _op(
+        _fmt(workloads.weight_block(rows=256, cols=512), "e5m6"), "per_block_round"),
+    "per_channel_256x384_e2m1_round": lambda: _op(
+        _fmt(workloads.activation_channel(rows=256, cols=384), "e2m1"), "per_channel_round"),
 }
 
 # The SwiGLU backward takes two inputs; its digests cover both.
@@ -92,6 +101,17 @@ def run_case(wl):
         q, sf = oracle.swiglu_per_channel_T(x, wl.w.numpy(), wl.fmt, wl.group, swiglu_clamp=5.0)
     elif wl.op == "per_channel":
         q, sf = oracle.per_channel(x, wl.fmt, wl.group)
+    elif wl.op == "per_channel_T_ue8m0_cm":
+        q, sf = oracle.per_channel_T_sf(x, wl.fmt, wl.group,
+                                        sf_flags=oracle.SF_PACKED_UE8M0 | oracle.SF_COL_MAJOR)
+    elif wl.op == "swiglu_T_round_cm":
+        q, sf = oracle.swiglu_per_channel_T_sf(x, wl.w.numpy(), wl.fmt, 128,
+                                               sf_flags=oracle.SF_ROUND_POW2 | oracle.SF_COL_MAJOR,
+                                               swiglu_clamp=5.0)
+    elif wl.op == "per_block_round":
+        q, sf = oracle.per_block_sf(x, wl.fmt, wl.group, sf_flags=oracle.SF_ROUND_POW2)
+    elif wl.op == "per_channel_round":
+        q, sf = oracle.per_channel_sf(x, wl.fmt, 128, sf_flags=oracle.SF_ROUND_POW2)
     else:
         raise ValueError(wl.op)
     return q, sf
@@ -111,6 +131,15 @@ def compute():
     out["swiglu_backward_e5m2_r16"] = {"input": digest(workloads.bf16_bits(h),
                                                        workloads.bf16_bits(dv), w.numpy()),
                                        "codes": digest(q), "scales": digest(sf)}
+    # the backward with packed UE8M0 row-major scales (4 groups per half)
+    h, dv, w = workloads.swiglu_grad(seed=c["seed"], rows=c["rows"], cols=512)
+    q, sf = oracle.swiglu_backward_per_token_sf(workloads.bf16_bits(h), workloads.bf16_bits(dv),
+                                                w.numpy(), "e4m3", 128,
+                                                sf_flags=oracle.SF_PACKED_UE8M0,
+                                                swiglu_clamp=c["swiglu_clamp"])
+    out["swiglu_backward_e4m3_r16_ue8m0"] = {"input": digest(workloads.bf16_bits(h),
+                                                             workloads.bf16_bits(dv), w.numpy()),
+                                             "codes": digest(q), "scales": digest(sf)}
     return out
 
 
