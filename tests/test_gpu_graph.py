@@ -189,3 +189,69 @@ def test_graph_replays_of_the_other_casts(dev):
         torch.cuda.synchronize()
         for i, (t, r) in enumerate(zip(graph_outs, ref)):
             assert torch.equal(t.view(torch.uint8), r), (replay, i)
+
+
+def test_graph_replays_of_the_scale_option_casts(dev):
+    # the _sf entry points of the transposed, backward, per-block and
+    # per-channel casts under capture; the packed words of the transposed
+    # cast are written one byte per token group, by four different tiles
+    a = workloads.activation_channel(rows=1024, cols=384).x.to(dev)
+    h = workloads.swiglu_input(rows=512, cols=512).x.to(dev)
+    w = workloads.swiglu_input(rows=512, cols=512).w.to(dev)
+    hg, dv, wg = workloads.swiglu_grad(rows=256, cols=1024)
+    hg, dv, wg = hg.to(dev), dv.to(dev), wg.to(dev)
+    wt = workloads.weight_block(rows=256, cols=512).x.to(dev)
+    pc = pq.SF_PACKED_UE8M0 | pq.SF_COL_MAJOR
+    rc = pq.SF_ROUND_POW2 | pq.SF_COL_MAJOR
+    f8 = torch.float8_e4m3fn
+    s_t, d_t = pq.sf_layout_shape(384, 1024, 128, pc)
+    s_s, d_s = pq.sf_layout_shape(512, 512, 128, rc)
+    s_b, d_b = pq.sf_layout_shape(256, 2048, 128, pq.SF_PACKED_UE8M0)
+
+    def alloc():
+        return [torch.empty(384, 1024, dtype=f8, device=dev),
+                torch.empty(s_t, dtype=d_t, device=dev),
+                torch.empty(pq.code_shape("e2m1", 512, 512), dtype=torch.uint8, device=dev),
+                torch.empty(s_s, dtype=d_s, device=dev),
+                torch.empty(256, 2048, dtype=f8, device=dev),
+                torch.empty(s_b, dtype=d_b, device=dev),
+                torch.empty(pq.code_shape("e5m6", 256, 512), dtype=torch.uint8, device=dev),
+                torch.empty(2, 4, device=dev),
+                torch.empty(1024, 384, dtype=f8, device=dev),
+                torch.empty(8, 384, device=dev)]
+
+    def casts(o):
+        pq.qcast_per_channel_T_sf(a, "e4m3", 128, sf_flags=pc, out=o[0], out_sf=o[1])
+        pq.qcast_swiglu_per_channel_T_sf(h, w, "e2m1", 128, sf_flags=rc, out=o[2], out_sf=o[3])
+        pq.qcast_swiglu_backward_per_token_sf(hg, dv, wg, "e4m3", 128,
+                                              sf_flags=pq.SF_PACKED_UE8M0, swiglu_clamp=6.0,
+                                              out=o[4], out_sf=o[5])
+        pq.qcast_per_block_sf(wt, "e5m6", 128, sf_flags=pq.SF_ROUND_POW2, out=o[6], out_sf=o[7])
+        pq.qcast_per_channel_sf(a, "e4m3", 128, sf_flags=pq.SF_ROUND_POW2, out=o[8],
+                                out_sf=o[9])
+
+    eager = alloc()
+    casts(eager)
+    torch.cuda.synchronize()
+    ref = [t.view(torch.uint8).clone() for t in eager]
+    graph_outs = alloc()
+    for t in graph_outs:
+        t.view(torch.uint8).fill_(0xA5)
+    side = torch.cuda.Stream(dev)
+    side.wait_stream(torch.cuda.current_stream(dev))
+    with torch.cuda.stream(side):
+        casts(graph_outs)
+    torch.cuda.current_stream(dev).wait_stream(side)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        casts(graph_outs)
+    for replay in range(4):
+        for t in graph_outs:
+            t.view(torch.uint8).fill_(0x5A + replay)
+        torch.cuda.synchronize()
+        g.replay()
+        casts(eager)                       # eager work between the replays
+        torch.cuda.synchronize()
+        for i, (t, r) in enumerate(zip(graph_outs, ref)):
+            assert torch.equal(t.view(torch.uint8), r), (replay, i)
