@@ -39,15 +39,21 @@ constexpr float kLog2e = 1.4426950408889634f;
 // is exact for c < 2^24 and chunks per row < 2^16.
 constexpr int64_t kMaxChunksPerLaunch = int64_t(1) << 24;
 constexpr int64_t kMaxChunksPerRow = int64_t(1) << 16;
+constexpr int kXcds = 8;
 
 // kLayout: scale options other than plain fp32 row-major.
 template <int kLanes, bool kWeighted, int kFmt, bool kClamp, bool kLayout>
 __global__ __launch_bounds__(kThreads) void swiglu_backward_kernel(
     const uint16_t* __restrict__ h, const uint16_t* __restrict__ dv,
     const float* __restrict__ w, int64_t nchunks, uint32_t chunks_per_row, uint64_t row_magic,
-    int64_t cols, float floor, float clamp, uint32_t row0, SfLayout lay, uint8_t* __restrict__ q,
-    void* __restrict__ sf) {
-  const int64_t base0 = (int64_t)blockIdx.x * kThreads * kUnroll + threadIdx.x;
+    int64_t cols, float floor, float clamp, uint32_t row0, SfLayout lay, uint32_t per_xcd,
+    uint8_t* __restrict__ q, void* __restrict__ sf) {
+  // With column-major scales each XCD takes a contiguous range of rows, so
+  // the scale words of neighbouring rows meet in one L2 before they are
+  // written back (workgroups remapped past the end find no chunk).
+  uint32_t blk = blockIdx.x;
+  if (kLayout && per_xcd) blk = (blk % kXcds) * per_xcd + blk / kXcds;
+  const int64_t base0 = (int64_t)blk * kThreads * kUnroll + threadIdx.x;
   const uint32_t groups_per_half = chunks_per_row / kLanes;
   u32x4 graw[kUnroll], uraw[kUnroll], draw[kUnroll];
   float wr[kUnroll];
@@ -133,11 +139,16 @@ hipError_t launch(const uint16_t* h, const uint16_t* dv, const float* w, int64_t
     const int64_t nr = rows - r0 < slab_rows ? rows - r0 : slab_rows;
     const int64_t nchunks = nr * cpr;
     const int64_t per_block = (int64_t)kThreads * kUnroll;
-    const int64_t blocks = (nchunks + per_block - 1) / per_block;
+    int64_t blocks = (nchunks + per_block - 1) / per_block;
+    int64_t per_xcd = 0;
+    if (kLayout && (lay.flags & kSfColMajor)) {
+      per_xcd = (blocks + kXcds - 1) / kXcds;
+      blocks = per_xcd * kXcds;
+    }
     launch_kernel((swiglu_backward_kernel<kLanes, kWeighted, kFmt, kClamp, kLayout>),
                   dim3((unsigned)blocks), dim3(kThreads), 0, stream, h + r0 * 2 * cols,
                   dv + r0 * cols, kWeighted ? w + r0 : nullptr, nchunks, (uint32_t)cpr,
-                  magic, cols, floor, clamp, (uint32_t)r0, lay,
+                  magic, cols, floor, clamp, (uint32_t)r0, lay, (uint32_t)per_xcd,
                   q + code_bytes<kFmt>(r0 * 2 * cols), sf);
     const hipError_t err = hipGetLastError();
     if (err != hipSuccess) return err;
