@@ -199,9 +199,9 @@ QCAST_API int qcast_e2m1(const void* x, int64_t rows, int64_t cols, int group, f
  *   use the hardware's fast forms, so the codes may differ from an exact
  *   evaluation by one step where v lies next to a rounding midpoint.
  */
-QCAST_API int qcast_swiglu_per_token(const void* h, int64_t rows, int64_t cols, const float* row_weight,
-                           int fmt, int group, float clamp_min, void* q, float* sf,
-                           void* stream);
+QCAST_API int qcast_swiglu_per_token(const void* h, int64_t rows, int64_t cols,
+                                     const float* row_weight, int fmt, int group,
+                                     float clamp_min, void* q, float* sf, void* stream);
 
 /* qcast_swiglu_per_token with a scale-factor layout (qcast_sf_flags). */
 QCAST_API int qcast_swiglu_per_token_sf(const void* h, int64_t rows, int64_t cols,
@@ -333,7 +333,7 @@ QCAST_API int qcast_swiglu_per_channel_T_sf(const void* h, int64_t rows, int64_t
  *   Limits: (rows/128) * (cols/128) < 2^31 and 128 * cols < 2^31.
  */
 QCAST_API int qcast_per_block(const void* x, int64_t rows, int64_t cols, int fmt, int block,
-                    float clamp_min, void* q, float* sf, void* stream);
+                              float clamp_min, void* q, float* sf, void* stream);
 
 /* qcast_per_block with round_sf ([WALK] §3.1): sf_flags 0 or
  * QCAST_SF_ROUND_POW2 (each tile's scale rounded up to a power of two, the
@@ -359,7 +359,7 @@ QCAST_API int qcast_per_block_sf(const void* x, int64_t rows, int64_t cols, int 
  *   Limits: 128 * cols < 2^31, 64 * rows < 2^31 (96 * rows for E5M6).
  */
 QCAST_API int qcast_per_channel_T(const void* x, int64_t rows, int64_t cols, int fmt, int group,
-                        float clamp_min, void* qT, float* sf, void* stream);
+                                  float clamp_min, void* qT, float* sf, void* stream);
 
 /* qcast_per_channel_T with a scale-factor layout: the per-token layouts of
  * x^T (rows = the cols channels, groups = the rows/group token groups):

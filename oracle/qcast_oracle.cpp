@@ -765,7 +765,8 @@ int oracle_per_token_sf(const uint16_t* x, int64_t rows, int64_t cols, int fmt, 
   std::vector<float> row(static_cast<size_t>(cols));
   for (int64_t r = 0; r < rows; ++r) {
     for (int64_t c = 0; c < cols; ++c) row[c] = bf16_value(x[r * cols + c]);
-    per_token_row_sf(row.data(), r, rows, cols, fmt, group, floor, sf_flags, q + r * code_bytes, sf);
+    per_token_row_sf(row.data(), r, rows, cols, fmt, group, floor, sf_flags, q + r * code_bytes,
+                     sf);
   }
   return ORACLE_OK;
 }

@@ -140,7 +140,8 @@ __global__ __launch_bounds__(kThreads) void cast_back_kernel(const uint8_t* __re
 template <int kLanes, int kFmt>
 hipError_t launch(const void* q, const float* sf, int64_t nchunks, bool out_bf16, void* out,
                   hipStream_t stream) {
-  const int64_t blocks = (nchunks + (int64_t)kThreads * kUnroll - 1) / ((int64_t)kThreads * kUnroll);
+  const int64_t per_block = (int64_t)kThreads * kUnroll;
+  const int64_t blocks = (nchunks + per_block - 1) / per_block;
   if (blocks >= (int64_t(1) << 31)) return hipErrorInvalidValue;
   if (out_bf16)
     launch_kernel((cast_back_kernel<kLanes, kFmt, true>), dim3((unsigned)blocks),

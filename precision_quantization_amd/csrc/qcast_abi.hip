@@ -40,7 +40,9 @@ bool any_fmt(int fmt) {
          fmt == QCAST_FMT_E5M6;
 }
 
-float floor_for(int fmt, float clamp_min) { return clamp_min > 0.0f ? clamp_min : default_floor(fmt); }
+float floor_for(int fmt, float clamp_min) {
+  return clamp_min > 0.0f ? clamp_min : default_floor(fmt);
+}
 
 // A caller's floor must be a number below +inf: NaN would silently select the
 // default, and +inf would make every scale infinite (and, rounded to a power
