@@ -237,3 +237,59 @@ def test_per_block_round_sf_full_size(dev):
     band = np.ascontiguousarray(xb[31 * 128:32 * 128])
     q_ref, _ = oracle.per_block_sf(band, "e4m3", 128, sf_flags=pq.SF_ROUND_POW2)
     assert np.array_equal(u8(q)[31 * 128:32 * 128], q_ref)
+
+
+def test_swiglu_backward_layouts_full_size(dev):
+    # 8192 x 2048 gradient, packed UE8M0 column-major scales: 32 rows spread
+    # over the tensor held to the SwiGLU bar against the oracle on those rows
+    h, dv, w = workloads.swiglu_grad()
+    flags = pq.SF_PACKED_UE8M0 | pq.SF_COL_MAJOR
+    rows, cols = dv.shape
+    out = code_tensor("e4m3", rows, 2 * cols, dev, 0xAA)
+    sf = sf_tensor(rows, 2 * cols, 128, flags, dev, 0xAA)
+    pq.qcast_swiglu_backward_per_token_sf(h.to(dev), dv.to(dev), w.to(dev), "e4m3", 128,
+                                          sf_flags=flags, swiglu_clamp=6.0, out=out, out_sf=sf)
+    torch.cuda.synchronize()
+    q = u8(out)
+    words = u32(sf)                                       # [groups/4][rows]
+    picks = np.linspace(0, rows - 1, 32).astype(int)
+    hb, db, wn = bits(h), bits(dv), w.numpy()
+    for r in picks:
+        sl = slice(r, r + 1)
+        q_ref, sf_ref = oracle.swiglu_backward_per_token_sf(
+            np.ascontiguousarray(hb[sl]), np.ascontiguousarray(db[sl]), wn[sl], "e4m3", 128,
+            sf_flags=pq.SF_PACKED_UE8M0, swiglu_clamp=6.0)
+        v = oracle.swiglu_backward_values(np.ascontiguousarray(hb[sl]),
+                                          np.ascontiguousarray(db[sl]), wn[sl],
+                                          swiglu_clamp=6.0)
+        got_sf = np.ascontiguousarray(words[:, r:r + 1].T)  # this row's words, row-major
+        check_swiglu_bar(q[sl], got_sf, q_ref, sf_ref, v, "e4m3", 128,
+                         sf_flags=pq.SF_PACKED_UE8M0, what=f"backward full, row {r}")
+
+
+def test_swiglu_per_channel_T_layouts_full_size(dev):
+    # 8192 tokens x 2048 outputs, round_sf column-major scales, clamp 5 with a
+    # counter: 64 channels spread over the output held to the SwiGLU bar
+    # against the oracle on those channels; the clamp count is exact
+    wl = workloads.swiglu_input()
+    rows, n = wl.rows, wl.cols
+    flags = pq.SF_ROUND_POW2 | pq.SF_COL_MAJOR
+    count = torch.zeros(1, dtype=torch.int64, device=dev)
+    out = code_tensor("e4m3", n, rows, dev, 0x55)
+    sf = sf_tensor(n, rows, 128, flags, dev, 0x55)
+    pq.qcast_swiglu_per_channel_T_sf(wl.x.to(dev), wl.w.to(dev), "e4m3", 128, sf_flags=flags,
+                                     swiglu_clamp=5.0, clamp_count=count, out=out, out_sf=sf)
+    torch.cuda.synchronize()
+    hb, wn = bits(wl.x), wl.w.numpy()
+    _, n_ref = oracle.swiglu_values_ex(hb, wn, swiglu_clamp=5.0)
+    assert int(count.item()) == n_ref
+    q, sfn = u8(out), sf.cpu().numpy()
+    for c0 in np.linspace(0, n - 8, 8).astype(int) // 8 * 8:
+        sub = np.ascontiguousarray(np.concatenate([hb[:, c0:c0 + 8], hb[:, n + c0:n + c0 + 8]],
+                                                  axis=1))
+        q_ref, sf_ref = oracle.swiglu_per_channel_T_sf(sub, wn, "e4m3", 128, sf_flags=flags,
+                                                       swiglu_clamp=5.0)
+        v, _ = oracle.swiglu_values_ex(sub, wn, swiglu_clamp=5.0)
+        got_sf = np.ascontiguousarray(sfn[:, c0:c0 + 8])   # [groups][channels of the slice]
+        check_swiglu_bar(q[c0:c0 + 8], got_sf, q_ref, sf_ref, v.T, "e4m3", 128, sf_flags=flags,
+                         what=f"swiglu_T full, channels {c0}..{c0 + 7}")
