@@ -14,9 +14,11 @@
 // channels) of tokens 4k..4k+3 in each of kPasses passes, all loads issued
 // before any is used; the data stays in registers as packed bf16.
 // Column abs-maxima per token group: packed 16-bit maxima of the magnitude
-// bits (v_pk_max_u16) over the lane's tokens, the same over the lanes that
-// hold the same channel chunk (DPP / cross-lane), then a 4-wave LDS
-// exchange; one lane per (group, channel) forms the scale. Each lane packs
+// bits (v_pk_max_u16) over the lane's tokens, then a butterfly over the 8
+// lanes that hold the same channel chunk (permlane swaps that each carry two
+// channels, and a DPP step), after which every lane holds one channel's
+// maximum of the wave; a 4-wave LDS exchange, and one lane per (group,
+// channel) forms the scale. Each lane packs
 // the codes of 4 tokens of one channel into a dword and writes it to an LDS
 // tile [channel][token] whose dword index is XOR-swizzled by
 // 4 * ((channel/8) mod 8): the eight channel chunks a half-wave writes land
