@@ -4,11 +4,13 @@
  * path on the current HIP device -- per-token E4M3 (groups of 128), the
  * transposed per-channel cast, packed E2M1 (groups of 32), the 128x128
  * per-block cast, and SwiGLU + per-token E4M3 (groups of 64, no routing
- * weight) reading the same rows as [gate | up] halves of cols/2 each -- and
- * write codes and scales to files for the test to compare with the oracle.
+ * weight) reading the same rows as [gate | up] halves of cols/2 each --
+ * and the transposed cast again with round_sf column-major scales
+ * (qcast_per_channel_T_sf), and write codes and scales to files for the
+ * test to compare with the oracle.
  *
  *   abi_smoke IN ROWS COLS OUT_PREFIX
- * writes OUT_PREFIX.{q,sf,qT,sfT,q4,sf4,qb,sfb,qs,sfs}; prints "ok" and
+ * writes OUT_PREFIX.{q,sf,qT,sfT,q4,sf4,qb,sfb,qs,sfs,qTr,sfTr}; prints "ok" and
  * returns 0, or prints the failing call and its status text and returns 1.
  */
 #include <hip/hip_runtime_api.h>
@@ -58,13 +60,15 @@ int main(int argc, char** argv) {
   const size_t nb = (size_t)(rows / 128) * (size_t)(cols / 128); /* per-block scales */
   const int64_t half = cols / 2;                                   /* SwiGLU outputs per row */
   const size_t ns = (size_t)(rows * half);
-  void *x, *q, *sf, *qT, *sfT, *q4, *sf4, *qb, *sfb, *qs, *sfs;
+  const size_t ntr = (size_t)(rows / 128) * (size_t)((cols + 3) / 4 * 4); /* col-major sf */
+  void *x, *q, *sf, *qT, *sfT, *q4, *sf4, *qb, *sfb, *qs, *sfs, *qTr, *sfTr;
   if (!hip_ok(hipMalloc(&x, 2 * n), "hipMalloc") || !hip_ok(hipMalloc(&q, n), "hipMalloc") ||
       !hip_ok(hipMalloc(&sf, n / 128 * 4), "hipMalloc") || !hip_ok(hipMalloc(&qT, n), "hipMalloc") ||
       !hip_ok(hipMalloc(&sfT, n / 128 * 4), "hipMalloc") ||
       !hip_ok(hipMalloc(&q4, n / 2), "hipMalloc") || !hip_ok(hipMalloc(&sf4, n / 32 * 4), "hipMalloc") ||
       !hip_ok(hipMalloc(&qb, n), "hipMalloc") || !hip_ok(hipMalloc(&sfb, nb * 4 + 4), "hipMalloc") ||
-      !hip_ok(hipMalloc(&qs, ns + 1), "hipMalloc") || !hip_ok(hipMalloc(&sfs, ns / 64 * 4 + 4), "hipMalloc"))
+      !hip_ok(hipMalloc(&qs, ns + 1), "hipMalloc") || !hip_ok(hipMalloc(&sfs, ns / 64 * 4 + 4), "hipMalloc") ||
+      !hip_ok(hipMalloc(&qTr, n), "hipMalloc") || !hip_ok(hipMalloc(&sfTr, ntr * 4 + 4), "hipMalloc"))
     return 1;
   if (!hip_ok(hipMemcpy(x, host, 2 * n, hipMemcpyHostToDevice), "hipMemcpy H2D")) return 1;
   int rc = qcast_per_token(x, rows, cols, QCAST_FMT_E4M3, 128, 0.0f, q, (float*)sf, NULL);
@@ -77,6 +81,9 @@ int main(int argc, char** argv) {
   if (rc != QCAST_OK) return fail("qcast_per_block", rc);
   rc = qcast_swiglu_per_token(x, rows, half, NULL, QCAST_FMT_E4M3, 64, 0.0f, qs, (float*)sfs, NULL);
   if (rc != QCAST_OK) return fail("qcast_swiglu_per_token", rc);
+  rc = qcast_per_channel_T_sf(x, rows, cols, QCAST_FMT_E4M3, 128, 0.0f,
+                              QCAST_SF_ROUND_POW2 | QCAST_SF_COL_MAJOR, qTr, sfTr, NULL);
+  if (rc != QCAST_OK) return fail("qcast_per_channel_T_sf", rc);
   /* an argument error comes back before anything is launched */
   rc = qcast_per_token(x, rows, cols, QCAST_FMT_E4M3, 100, 0.0f, q, (float*)sf, NULL);
   if (rc != QCAST_ERR_GROUP) return fail("qcast_per_token with group 100", rc);
@@ -85,12 +92,13 @@ int main(int argc, char** argv) {
       !save(argv[4], "qT", qT, n) || !save(argv[4], "sfT", sfT, n / 128 * 4) ||
       !save(argv[4], "q4", q4, n / 2) || !save(argv[4], "sf4", sf4, n / 32 * 4) ||
       !save(argv[4], "qb", qb, n) || !save(argv[4], "sfb", sfb, nb * 4) ||
-      !save(argv[4], "qs", qs, ns) || !save(argv[4], "sfs", sfs, ns / 64 * 4)) {
+      !save(argv[4], "qs", qs, ns) || !save(argv[4], "sfs", sfs, ns / 64 * 4) ||
+      !save(argv[4], "qTr", qTr, n) || !save(argv[4], "sfTr", sfTr, ntr * 4)) {
     fprintf(stderr, "cannot write the outputs\n");
     return 1;
   }
   hipFree(x); hipFree(q); hipFree(sf); hipFree(qT); hipFree(sfT); hipFree(q4); hipFree(sf4);
-  hipFree(qb); hipFree(sfb); hipFree(qs); hipFree(sfs);
+  hipFree(qb); hipFree(sfb); hipFree(qs); hipFree(sfs); hipFree(qTr); hipFree(sfTr);
   free(host);
   printf("ok\n");
   return 0;

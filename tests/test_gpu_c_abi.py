@@ -2,7 +2,9 @@
 no Python or torch inside) casts a seeded bf16 input with the five casts of
 the hot path on the GPU: qcast_per_token, qcast_per_channel_T, qcast_e2m1 and
 qcast_per_block must equal the oracle bit for bit, and qcast_swiglu_per_token
-(the same rows read as [gate | up]) must meet the SwiGLU tolerance."""
+(the same rows read as [gate | up]) must meet the SwiGLU tolerance; the
+transposed cast with round_sf column-major scales (qcast_per_channel_T_sf)
+must equal the oracle too."""
 import os
 import subprocess
 
@@ -47,6 +49,12 @@ def test_c_program_matches_the_oracle(tmp_path):
     qb_ref, sfb_ref = oracle.per_block(xb, "e4m3", 128)
     assert np.array_equal(read("qb", np.uint8), qb_ref.ravel())
     assert np.array_equal(read("sfb", np.uint32), sfb_ref.view(np.uint32).ravel())
+    # the transposed cast with round_sf column-major scales (padding not compared)
+    qr_ref, sfr_ref = oracle.per_channel_T_sf(xb, "e4m3", 128,
+                                              sf_flags=oracle.SF_ROUND_POW2 | oracle.SF_COL_MAJOR)
+    assert np.array_equal(read("qTr", np.uint8), qr_ref.ravel())
+    got = read("sfTr", np.uint32).reshape(sfr_ref.shape)
+    assert np.array_equal(got[:, :cols], sfr_ref.view(np.uint32)[:, :cols])
     # SwiGLU: the bar of tests/swiglu_bar.py (the device exponential is not the
     # correctly rounded one)
     qs_ref, sfs_ref = oracle.swiglu_per_token(xb, None, "e4m3", 64)
