@@ -100,10 +100,12 @@ __global__ __launch_bounds__(kThreads) void per_token_kernel(
 // cast 20% slower than with row-major scales). Here workgroup b casts a tile
 // of kCmRows rows x kCmSpan chunks (two chunks per lane), parks the tile's
 // scales in LDS and writes each group column's kCmRows consecutive rows as
-// one 128-byte run. Tiles walk the chunk columns fastest; the bottom and
-// right tiles may be partial, always in whole groups (cols % 32 == 0).
-constexpr int kCmSpan = 16;                          // chunks per tile row
-constexpr int kCmRows = 2 * kThreads / kCmSpan;      // 32 rows
+// one 64-byte run. A tile 256 columns wide and 16 rows tall ran 3% faster
+// than one 128 wide and 32 tall; taller tiles, with longer scale runs, ran
+// slower. Tiles walk the chunk columns fastest; the bottom and right tiles
+// may be partial, always in whole groups (cols % 32 == 0).
+constexpr int kCmSpan = 32;                          // chunks per tile row
+constexpr int kCmRows = 2 * kThreads / kCmSpan;      // 16 rows
 
 template <int kFmt>
 __global__ __launch_bounds__(kThreads) void per_token_cm32_kernel(
@@ -111,6 +113,7 @@ __global__ __launch_bounds__(kThreads) void per_token_cm32_kernel(
     uint8_t* __restrict__ q, float* __restrict__ sf, SfLayout lay) {
   constexpr int kLanes = 4;                          // lanes per 32-group
   constexpr int kGroupCols = kCmSpan / kLanes;
+  static_assert(kGroupCols * kCmRows <= kThreads, "one scale store per lane at most");
   __shared__ float tile_sf[kGroupCols][kCmRows];
   const uint32_t rt = blockIdx.x / col_tiles;
   const uint32_t ct = blockIdx.x - rt * col_tiles;
