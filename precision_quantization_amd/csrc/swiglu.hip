@@ -33,8 +33,15 @@ namespace {
 
 // Launch shape (compile-time; defaults chosen by measurement): output
 // chunks in flight per lane, and the cap on workgroups per CU (0: no cap).
+// The E5M6 form, whose encode takes about three times the arithmetic per
+// value, keeps 2 chunks per lane in flight (17.1 against 17.9 us at 1 and
+// 18.2 at 4 on the 8192 x 2048 output, interleaved); the other formats are
+// fastest at 1 (E4M3 15.0 against 15.3 at 2; E2M1 13.9 at 1 and 2).
 #ifndef QCAST_SW_UNROLL
 #define QCAST_SW_UNROLL 1
+#endif
+#ifndef QCAST_SW_UNROLL_E5M6
+#define QCAST_SW_UNROLL_E5M6 2
 #endif
 #ifndef QCAST_SW_WG_PER_CU
 #define QCAST_SW_WG_PER_CU 0
@@ -61,7 +68,8 @@ namespace {
 constexpr int kSlotUnroll = QCAST_SW_SLOT_UNROLL;
 constexpr int kCountBlock = QCAST_SW_COUNT_BLOCK;
 constexpr int kCountUnroll = QCAST_SW_COUNT_UNROLL;
-constexpr int kStreamUnroll = QCAST_SW_UNROLL;
+template <int kFmt>
+constexpr int kStreamUnroll = kFmt == kE5M6 ? QCAST_SW_UNROLL_E5M6 : QCAST_SW_UNROLL;
 constexpr int kWgPerCu = QCAST_SW_WG_PER_CU;
 constexpr int kCountWgPerCu = QCAST_SW_COUNT_WG_PER_CU;
 constexpr float kLog2e = 1.4426950408889634f;
@@ -213,7 +221,7 @@ hipError_t launch(const uint16_t* h, const float* w, int64_t rows, int64_t cols,
     // clamped values per slab, within the slots' 24 and 40 bits.
     const bool slotted = counting && ca.slots;
     const int block = counting && !slotted ? kCountBlock : kThreads;
-    const int unroll = slotted ? kSlotUnroll : counting ? kCountUnroll : kStreamUnroll;
+    const int unroll = slotted ? kSlotUnroll : counting ? kCountUnroll : kStreamUnroll<kFmt>;
     const int64_t per_block_iter = (int64_t)block * unroll;
     const int64_t iters = (nchunks + per_block_iter - 1) / per_block_iter;
     const int wg_per_cu = slotted ? 0 : counting ? kCountWgPerCu : kWgPerCu;
@@ -224,7 +232,7 @@ hipError_t launch(const uint16_t* h, const float* w, int64_t rows, int64_t cols,
                         q + code_bytes<kFmt>(r0 * cols), (uint32_t)(r0 * groups_per_row)};
     auto plain = [&] {
       launch_kernel((swiglu_kernel<kLanes, kWeighted, kFmt, kClamp, kCountNone, kThreads,
-                                   kStreamUnroll>),
+                                   kStreamUnroll<kFmt>>),
                     dim3((unsigned)blocks), dim3(kThreads), 0, stream, args.h, args.w, nchunks,
                     (uint32_t)cpr, magic, floor, args.q, sf, lay, args.group0, ca.c,
                     ca.count, ca.slots);
