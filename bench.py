@@ -39,7 +39,7 @@ is the oracle (single thread) on every workload in full, on this host (about
 per-token workload X[128, 512] next to the launch floor (a 16-byte copy),
 and the casts that are not among the five: cast_back of the per-token codes to bf16, the
 per-token cast with 1 x 32 groups and packed UE8M0 column-major scales, the
-per-token E5M6 cast and its cast_back,
+per-token E5M6 cast and its cast_back, the cast_back of E2M1 codes,
 SwiGLU with the clamp and counter, SwiGLU + per-channel cast + transpose,
 the SwiGLU backward cast, the per-channel cast in the input layout, the
 packed formats (E2M1, E5M6) on the per-channel, per-block and SwiGLU casts,
@@ -251,6 +251,11 @@ def extra_calls(wls, dev):
     o6 = torch.empty(r, c, dtype=torch.bfloat16, device=dev)
     calls.append(("cast_back_e5m6", [r, c], e5m6_bytes,
                   lambda q6=q6, s6=s6, o6=o6: pq.qcast_cast_back(q6, s6, "e5m6", 128, out=o6)))
+    # cast_back of the same workload's E2M1 codes (1 x 32 groups)
+    q2, s2 = pq.qcast_per_token(x, "e2m1", 32)
+    o2 = torch.empty(r, c, dtype=torch.bfloat16, device=dev)
+    calls.append(("cast_back_e2m1", [r, c], r * c // 2 + r * (c // 32) * 4 + r * c * 2,
+                  lambda q2=q2, s2=s2, o2=o2: pq.qcast_cast_back(q2, s2, "e2m1", 32, out=o2)))
     # SwiGLU with clamp and counter
     wl = by["swiglu"]
     h, w = wl.x.to(dev), wl.w.to(dev)

@@ -15,20 +15,28 @@
 // table), multiplied by the group's scale (the lanes of a group read the
 // same scale word), and written as 8 bf16 (one 16-byte store, converted with
 // v_cvt_pk_bf16_f32) or 8 fp32 (two 16-byte stores). One workgroup per
-// 256 * kUnroll chunks.
+// 256 * kUnroll chunks (kUnroll by format, below).
 #include "qcast_device.h"
 #include "qcast_kernels.h"
 
 namespace qcast {
 namespace {
 
-// Chunks per lane (1 measured about 8% faster than 2 or 4 on 4096 x 7168:
-// the kernel writes twice what it reads, and more workgroups spread those
-// writes better).
+// Chunks per lane. The 8-, 12-byte code loads of E4M3, E5M2 and E5M6 run
+// best at 1 (about 8% faster than 2 or 4 on 4096 x 7168: the kernel writes
+// twice what it reads, and more workgroups spread those writes better).
+// E2M1's 4-byte code loads want more in flight: 14.6 us at 4 chunks per
+// lane against 14.8 at 2 and 16.2 at 1 (interleaved, 100 rounds).
 #ifndef QCAST_CB_UNROLL
 #define QCAST_CB_UNROLL 1
 #endif
-constexpr int kUnroll = QCAST_CB_UNROLL;
+#ifndef QCAST_CB_UNROLL_E2M1
+#define QCAST_CB_UNROLL_E2M1 4
+#endif
+template <int kFmt>
+constexpr int kUnroll = kFmt == kE2M1 ? QCAST_CB_UNROLL_E2M1 : QCAST_CB_UNROLL;
+constexpr int kMinUnroll =
+    QCAST_CB_UNROLL < QCAST_CB_UNROLL_E2M1 ? QCAST_CB_UNROLL : QCAST_CB_UNROLL_E2M1;
 
 typedef float f32x2 __attribute__((ext_vector_type(2)));
 
@@ -90,11 +98,12 @@ __global__ __launch_bounds__(kThreads) void cast_back_kernel(const uint8_t* __re
                                                              const float* __restrict__ sf,
                                                              int64_t nchunks,
                                                              void* __restrict__ out) {
-  const int64_t base = (int64_t)blockIdx.x * kThreads * kUnroll + threadIdx.x;
-  u32x4 codes[kUnroll];
-  float s[kUnroll];
+  constexpr int kU = kUnroll<kFmt>;
+  const int64_t base = (int64_t)blockIdx.x * kThreads * kU + threadIdx.x;
+  u32x4 codes[kU];
+  float s[kU];
 #pragma unroll
-  for (int u = 0; u < kUnroll; ++u) {
+  for (int u = 0; u < kU; ++u) {
     const int64_t c = base + (int64_t)u * kThreads;
     if (c < nchunks) {
       codes[u] = u32x4{0u, 0u, 0u, 0u};
@@ -114,7 +123,7 @@ __global__ __launch_bounds__(kThreads) void cast_back_kernel(const uint8_t* __re
     }
   }
 #pragma unroll
-  for (int u = 0; u < kUnroll; ++u) {
+  for (int u = 0; u < kU; ++u) {
     const int64_t c = base + (int64_t)u * kThreads;
     if (c < nchunks) {
       float v[8];
@@ -140,7 +149,7 @@ __global__ __launch_bounds__(kThreads) void cast_back_kernel(const uint8_t* __re
 template <int kLanes, int kFmt>
 hipError_t launch(const void* q, const float* sf, int64_t nchunks, bool out_bf16, void* out,
                   hipStream_t stream) {
-  const int64_t per_block = (int64_t)kThreads * kUnroll;
+  const int64_t per_block = (int64_t)kThreads * kUnroll<kFmt>;
   const int64_t blocks = (nchunks + per_block - 1) / per_block;
   if (blocks >= (int64_t(1) << 31)) return hipErrorInvalidValue;
   if (out_bf16)
@@ -166,7 +175,7 @@ hipError_t launch_fmt(const void* q, const float* sf, int64_t nchunks, int group
 }  // namespace
 
 bool cast_back_fits(int64_t rows, int64_t cols) {
-  const int64_t per_block = (int64_t)kThreads * kUnroll;
+  const int64_t per_block = (int64_t)kThreads * kMinUnroll;  // the largest grid of any format
   return (rows * cols / 8 + per_block - 1) / per_block < (int64_t(1) << 31);
 }
 

@@ -509,15 +509,16 @@ def test_cast_back_every_code(dev, fmt):
         assert np.array_equal(out.cpu().numpy().view(np.uint32), ref.view(np.uint32))
 
 
-def test_cast_back_round_trip_full_size(dev):
+@pytest.mark.parametrize("fmt,group", [("e4m3", 128), ("e2m1", 32)])
+def test_cast_back_round_trip_full_size(dev, fmt, group):
     # the GPU's own codes of the hidden-size workload, dequantized on the GPU
-    # and by the oracle
+    # and by the oracle (the shapes and launches bench.py times)
     wl = workloads.per_token_hidden()
     x = wl.x.to(dev)
-    q, sf = pq.qcast_per_token(x)
-    out = pq.qcast_cast_back(q, sf)
+    q, sf = pq.qcast_per_token(x, fmt, group)
+    out = pq.qcast_cast_back(q, sf, fmt, group)
     torch.cuda.synchronize()
-    ref = oracle.cast_back(codes_np(q), sf.cpu().numpy(), 7168, "e4m3", 128, "bf16")
+    ref = oracle.cast_back(codes_np(q), sf.cpu().numpy(), 7168, fmt, group, "bf16")
     assert np.array_equal(out.cpu().view(torch.int16).numpy().view(np.uint16), ref)
 
 
