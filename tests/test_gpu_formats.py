@@ -168,7 +168,7 @@ def gpu_swiglu_ex(wl, dev, fmt, group, clamp=0.0, flags=0, count=None, ws=None):
 @pytest.mark.parametrize("fmt,group", [("e2m1", 32), ("e2m1", 64), ("e2m1", 128),
                                        ("e5m6", 128), ("e5m6", 32)])
 @pytest.mark.parametrize("rows,cols,weighted", [(1, 128, True), (5, 384, False),
-                                                (130, 2048, True)])
+                                                (130, 2048, True), (67, 1920, False)])
 def test_swiglu_per_token_shapes(dev, fmt, group, rows, cols, weighted):
     wl = workloads.swiglu_input(seed=rows + cols + group, rows=rows, cols=cols,
                                 with_weight=weighted)
