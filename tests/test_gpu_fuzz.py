@@ -101,20 +101,21 @@ def test_per_token_random(dev, fmt, group, flags, rows, cols, floor, seed):
 
 def block_cases():
     rng = np.random.default_rng(20261203)
-    return [(str(rng.choice(["e4m3", "e5m2"])), 128 * int(rng.integers(1, 7)),
-             128 * int(rng.integers(1, 10)), float(rng.choice(FLOORS)), 2000 + i)
+    return [(FORMATS[i % 4], 128 * int(rng.integers(1, 7)), 128 * int(rng.integers(1, 10)),
+             float(rng.choice(FLOORS)), pq.SF_ROUND_POW2 if i % 8 >= 4 else 0, 2000 + i)
             for i in range(16)]
 
 
-@pytest.mark.parametrize("fmt,rows,cols,floor,seed", block_cases())
-def test_per_block_random(dev, fmt, rows, cols, floor, seed):
+@pytest.mark.parametrize("fmt,rows,cols,floor,flags,seed", block_cases())
+def test_per_block_random(dev, fmt, rows, cols, floor, flags, seed):
     rng = np.random.default_rng(seed)
     # a magnitude per 128 x 128 block as well
     block = np.exp(rng.standard_normal((rows // 128, 1, cols // 128, 1)) * 3).astype(np.float32)
     block = np.broadcast_to(block, (rows // 128, 128, cols // 128, 128)).reshape(rows, cols)
     x = random_input(rng, rows, cols, 128, scale=block)
-    q_ref, sf_ref = oracle.per_block(workloads.bf16_bits(x), fmt, 128, clamp_min=floor)
-    q, sf = pq.qcast_per_block(x.to(dev), fmt, 128, clamp_min=floor)
+    q_ref, sf_ref = oracle.per_block_sf(workloads.bf16_bits(x), fmt, 128, clamp_min=floor,
+                                        sf_flags=flags)
+    q, sf = pq.qcast_per_block_sf(x.to(dev), fmt, 128, clamp_min=floor, sf_flags=flags)
     torch.cuda.synchronize()
     assert np.array_equal(q.view(torch.uint8).cpu().numpy(), q_ref)
     assert np.array_equal(sf.cpu().numpy().view(np.uint32), sf_ref.view(np.uint32))
@@ -122,23 +123,38 @@ def test_per_block_random(dev, fmt, rows, cols, floor, seed):
 
 def channel_cases():
     rng = np.random.default_rng(20261204)
-    return [(str(rng.choice(["e4m3", "e5m2"])), 128 * int(rng.integers(1, 7)),
-             8 * int(rng.integers(1, 100)), float(rng.choice(FLOORS)), 3000 + i)
-            for i in range(16)]
+    cases = []
+    for i in range(16):
+        rows = 128 * int(rng.integers(1, 7))
+        # the transposed cast's layouts: packed words hold 4 token groups
+        options = SF_FLAG_SETS if (rows // 128) % 4 == 0 else [
+            f for f in SF_FLAG_SETS if not f & pq.SF_PACKED_UE8M0]
+        flags = options[int(rng.integers(len(options)))]
+        cases.append((FORMATS[i % 4], rows, 8 * int(rng.integers(1, 100)),
+                      float(rng.choice(FLOORS)), flags, 3000 + i))
+    return cases
 
 
-@pytest.mark.parametrize("fmt,rows,cols,floor,seed", channel_cases())
-def test_per_channel_random(dev, fmt, rows, cols, floor, seed):
+@pytest.mark.parametrize("fmt,rows,cols,floor,flags,seed", channel_cases())
+def test_per_channel_random(dev, fmt, rows, cols, floor, flags, seed):
     # groups run along the tokens: plant the special groups in the transpose
     x = random_input(np.random.default_rng(seed), cols, rows, 128).t().contiguous()
     xb = workloads.bf16_bits(x)
-    qT_ref, sfT_ref = oracle.per_channel_T(xb, fmt, 128, clamp_min=floor)
-    qT, sfT = pq.qcast_per_channel_T(x.to(dev), fmt, 128, clamp_min=floor)
-    q, sf = pq.qcast_per_channel(x.to(dev), fmt, 128, clamp_min=floor)
+    # the transposed cast with a scale layout (padding entries keep the fill)
+    fill = 0x5A5A5A5A
+    qT_ref, sfT_ref = oracle.per_channel_T_sf(xb, fmt, 128, clamp_min=floor, sf_flags=flags,
+                                              sf_fill=fill)
+    shape, dt = pq.sf_layout_shape(cols, rows, 128, flags)
+    sfT = torch.full(shape, fill, dtype=dt, device=dev)
+    qT, _ = pq.qcast_per_channel_T_sf(x.to(dev), fmt, 128, clamp_min=floor, sf_flags=flags,
+                                      out_sf=sfT)
+    # the input-layout cast, with round_sf when the layout asks for it
+    round_only = flags & pq.SF_ROUND_POW2
+    q, sf = pq.qcast_per_channel_sf(x.to(dev), fmt, 128, clamp_min=floor, sf_flags=round_only)
     torch.cuda.synchronize()
     assert np.array_equal(qT.view(torch.uint8).cpu().numpy(), qT_ref)
     assert np.array_equal(sfT.cpu().numpy().view(np.uint32), sfT_ref.view(np.uint32))
-    q_ref, sf_ref = oracle.per_channel(xb, fmt, 128, clamp_min=floor)
+    q_ref, sf_ref = oracle.per_channel_sf(xb, fmt, 128, clamp_min=floor, sf_flags=round_only)
     assert np.array_equal(q.view(torch.uint8).cpu().numpy(), q_ref)
     assert np.array_equal(sf.cpu().numpy().view(np.uint32), sf_ref.view(np.uint32))
 
