@@ -50,9 +50,12 @@ __global__ __launch_bounds__(kThreads) void swiglu_backward_kernel(
     uint8_t* __restrict__ q, void* __restrict__ sf) {
   // With column-major scales each XCD takes a contiguous range of rows, so
   // the scale words of neighbouring rows meet in one L2 before they are
-  // written back (workgroups remapped past the end find no chunk).
+  // written back (workgroups remapped past the end find no chunk). E2M1
+  // takes that order in every layout (20.1 against 20.8 us on the 8192 x
+  // 2048 gradient, interleaved, 100 rounds; E4M3 22.8 against 22.5 and
+  // E5M6 25.9 against 25.6 keep the natural order).
   uint32_t blk = blockIdx.x;
-  if (kLayout && per_xcd) blk = (blk % kXcds) * per_xcd + blk / kXcds;
+  if ((kLayout || kFmt == kE2M1) && per_xcd) blk = (blk % kXcds) * per_xcd + blk / kXcds;
   const int64_t base0 = (int64_t)blk * kThreads * kUnroll + threadIdx.x;
   const uint32_t groups_per_half = chunks_per_row / kLanes;
   u32x4 graw[kUnroll], uraw[kUnroll], draw[kUnroll];
@@ -141,7 +144,7 @@ hipError_t launch(const uint16_t* h, const uint16_t* dv, const float* w, int64_t
     const int64_t per_block = (int64_t)kThreads * kUnroll;
     int64_t blocks = (nchunks + per_block - 1) / per_block;
     int64_t per_xcd = 0;
-    if (kLayout && (lay.flags & kSfColMajor)) {
+    if (kFmt == kE2M1 || (kLayout && (lay.flags & kSfColMajor))) {
       per_xcd = (blocks + kXcds - 1) / kXcds;
       blocks = per_xcd * kXcds;
     }
