@@ -75,6 +75,11 @@ def test_per_token_and_swiglu_stay_inside(dev, fmt, group, flags, rows):
     pq.qcast_swiglu_per_token_ex(h, w, fmt, group, sf_flags=flags, swiglu_clamp=2.0,
                                  clamp_count=count, out=qs, out_sf=ss)
     g.check(f"swiglu {fmt} g{group} flags {flags} rows {rows}")
+    # without a counter: the launch whose grid is padded to whole XCD ranges
+    qp = g.make(pq.code_shape(fmt, rows, cols), code_dtype(fmt))
+    sp = g.make(shape, dt)
+    pq.qcast_swiglu_per_token_sf(h, w, fmt, group, sf_flags=flags, out=qp, out_sf=sp)
+    g.check(f"swiglu, no counter, {fmt} g{group} flags {flags} rows {rows}")
 
 
 @pytest.mark.parametrize("fmt", ["e4m3", "e2m1", "e5m6"])
