@@ -95,6 +95,17 @@ def test_per_block_e2m1_full_size(dev):
     assert_exact(q, sf, *oracle.per_block(bits(wl.x), "e2m1", 128), "per_block e2m1 full")
 
 
+def test_per_block_e5m6_full_size_sampled(dev):
+    # every 7th row of 128 x 128 blocks, and the last, of the full weight
+    wl = workloads.weight_block()
+    rows = wl.x.shape[0]
+    q, sf = gpu_per_block(wl.x, dev, "e5m6")
+    brows = np.unique(np.r_[np.arange(0, rows // 128, 7), rows // 128 - 1])
+    sel = (brows[:, None] * 128 + np.arange(128)[None, :]).ravel()
+    q_ref, sf_ref = oracle.per_block(bits(wl.x[sel]), "e5m6", 128)
+    assert_exact(q[sel], sf[brows], q_ref, sf_ref, "per_block e5m6 full, sampled")
+
+
 # ---------------------------------------------------------- per-channel (T)
 
 def gpu_per_channel_T(x, dev, fmt, byte=0xA5):
@@ -141,6 +152,12 @@ def test_per_channel_T_e5m6_full_size_sampled(dev):
     chans = np.unique(np.r_[np.arange(0, cols, 61), cols - 1])
     q_ref, sf_ref = oracle.per_channel_T(bits(wl.x[:, chans]), "e5m6", 128)
     assert_exact(q[chans], sf[chans], q_ref, sf_ref, "per_channel_T e5m6 full, sampled")
+
+
+def test_per_channel_e2m1_full_size(dev):
+    wl = workloads.activation_channel()      # A [16384, 7168], codes in the input layout
+    q, sf = gpu_per_channel(wl.x, dev, "e2m1")
+    assert_exact(q, sf, *oracle.per_channel(bits(wl.x), "e2m1", 128), "per_channel e2m1 full")
 
 
 @pytest.mark.parametrize("fmt", PACKED)
@@ -260,3 +277,20 @@ def test_swiglu_backward_shapes(dev, fmt, group, clamp, rows, cols):
     v = oracle.swiglu_backward_values(bits(h), bits(dv), w.numpy(), swiglu_clamp=clamp)
     check_swiglu_bar(codes_np(q), sf.cpu().numpy(), q_ref, sf_ref, v, fmt, group,
                      what=f"backward {fmt} g{group} c{clamp}")
+
+
+def test_swiglu_backward_e2m1_full_size(dev):
+    # the 8192 x 2048 gradient in E2M1 with 1 x 32 groups and clamp 6
+    h, dv, w = workloads.swiglu_grad()
+    rows, cols = dv.shape
+    q = poisoned(pq.code_shape("e2m1", rows, 2 * cols), torch.uint8, dev)
+    sf = poisoned((rows, 2 * cols // 32), torch.float32, dev)
+    pq.qcast_swiglu_backward_per_token(h.to(dev), dv.to(dev), w.to(dev), "e2m1", 32,
+                                       swiglu_clamp=6.0, out=q, out_sf=sf)
+    torch.cuda.synchronize()
+    q_ref, sf_ref = oracle.swiglu_backward_per_token(bits(h), bits(dv), w.numpy(), "e2m1", 32,
+                                                     swiglu_clamp=6.0)
+    v = oracle.swiglu_backward_values(bits(h), bits(dv), w.numpy(), swiglu_clamp=6.0)
+    frac = check_swiglu_bar(codes_np(q), sf.cpu().numpy(), q_ref, sf_ref, v, "e2m1", 32,
+                            what="backward e2m1 g32 full")
+    print(f"swiglu backward e2m1 full: {frac:.5%} of codes differ from the oracle")
