@@ -94,20 +94,24 @@ __global__ __launch_bounds__(kThreads) void per_token_kernel(
   }
 }
 
-// fp32 column-major scales with 1 x 32 groups: sf[group][row] puts a row's
-// scales 4 * rows_pad bytes apart and a workgroup of the flat walk covers
-// less than a row, so every scale would leave as a lone 4-byte store (the
-// cast 20% slower than with row-major scales). Here workgroup b casts a tile
+// Column-major scales with 1 x 32 groups, fp32 or packed UE8M0:
+// sf[group][row] puts a row's scales 4 * rows_pad bytes apart and a
+// workgroup of the flat walk covers less than a row, so every scale (or
+// packed word) would leave as a lone 4-byte store (fp32 scales: the cast 20%
+// slower than with row-major scales). Here workgroup b casts a tile
 // of kCmRows rows x kCmSpan chunks (two chunks per lane), parks the tile's
 // scales in LDS and writes each group column's kCmRows consecutive rows as
-// one 64-byte run. A tile 256 columns wide and 16 rows tall ran 3% faster
-// than one 128 wide and 32 tall; taller tiles, with longer scale runs, ran
-// slower. Tiles walk the chunk columns fastest; the bottom and right tiles
-// may be partial, always in whole groups (cols % 32 == 0).
+// one 64-byte run (packed: each word column's, the word formed from the
+// parked scales with no cross-lane gather). A tile 256 columns wide and 16
+// rows tall ran 3% faster than one 128 wide and 32 tall; taller tiles, with
+// longer scale runs, ran slower. Packed scales take 16.5 us here against
+// 16.8 for the flat walk (4096 x 7168, interleaved, 150 rounds). Tiles walk
+// the chunk columns fastest; the bottom and right tiles may be partial,
+// always in whole groups (cols % 32 == 0).
 constexpr int kCmSpan = 32;                          // chunks per tile row
 constexpr int kCmRows = 2 * kThreads / kCmSpan;      // 16 rows
 
-template <int kFmt>
+template <int kFmt, bool kPacked>
 __global__ __launch_bounds__(kThreads) void per_token_cm32_kernel(
     const u32x4* __restrict__ x, uint32_t rows, uint32_t cpr, uint32_t col_tiles, float floor,
     uint8_t* __restrict__ q, float* __restrict__ sf, SfLayout lay) {
@@ -145,10 +149,26 @@ __global__ __launch_bounds__(kThreads) void per_token_cm32_kernel(
     }
   }
   __syncthreads();
-  // group column gc of the tile: kCmRows consecutive rows from consecutive lanes
-  const uint32_t gc = threadIdx.x / kCmRows, r = threadIdx.x % kCmRows;
-  if (gc < (uint32_t)kGroupCols && gc * kLanes < nspan && r < nrows)
-    sf[(size_t)(c0 / kLanes + gc) * lay.rows_pad + row0 + r] = tile_sf[gc][r];
+  if constexpr (kPacked) {
+    // word column wc of the tile: the exponent bytes of its groups 4wc..4wc+3
+    // (power-of-two scales), for kCmRows consecutive rows from consecutive
+    // lanes. Packed rows hold whole words (cols % 128 == 0), so a partial
+    // tile holds whole words too.
+    constexpr int kWordCols = kGroupCols / 4;
+    const uint32_t wc = threadIdx.x / kCmRows, r = threadIdx.x % kCmRows;
+    if (wc < (uint32_t)kWordCols && (wc + 1) * 4 * kLanes <= nspan && r < nrows) {
+      uint32_t w = 0u;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) w |= (__float_as_uint(tile_sf[4 * wc + i][r]) >> 23) << (8 * i);
+      reinterpret_cast<uint32_t*>(sf)[(size_t)(c0 / (4 * kLanes) + wc) * lay.rows_pad + row0 + r] =
+          w;
+    }
+  } else {
+    // group column gc of the tile: kCmRows consecutive rows from consecutive lanes
+    const uint32_t gc = threadIdx.x / kCmRows, r = threadIdx.x % kCmRows;
+    if (gc < (uint32_t)kGroupCols && gc * kLanes < nspan && r < nrows)
+      sf[(size_t)(c0 / kLanes + gc) * lay.rows_pad + row0 + r] = tile_sf[gc][r];
+  }
 }
 
 template <int kFmt>
@@ -159,7 +179,9 @@ hipError_t launch_cm32(const void* x, int64_t rows, int64_t cols, float floor, v
   const int64_t blocks = (rows + kCmRows - 1) / kCmRows * col_tiles;
   if (blocks >= (int64_t(1) << 31) || rows >= (int64_t(1) << 31) || cpr >= (int64_t(1) << 31))
     return hipErrorInvalidValue;
-  launch_kernel(per_token_cm32_kernel<kFmt>, dim3((unsigned)blocks), dim3(kThreads), 0, stream,
+  auto kernel = (lay.flags & kSfPacked) ? per_token_cm32_kernel<kFmt, true>
+                                        : per_token_cm32_kernel<kFmt, false>;
+  launch_kernel(kernel, dim3((unsigned)blocks), dim3(kThreads), 0, stream,
                 static_cast<const u32x4*>(x), (uint32_t)rows, (uint32_t)cpr,
                 (uint32_t)col_tiles, floor, static_cast<uint8_t*>(q), static_cast<float*>(sf),
                 lay);
@@ -210,7 +232,7 @@ hipError_t launch_per_token(const void* x, int64_t rows, int64_t cols, int fmt, 
   if (nchunks == 0) return hipSuccess;
   if (rows * cols / group >= (int64_t(1) << 31)) return hipErrorInvalidValue;
   const SfLayout lay = make_sf_layout(rows, cols, group, sf_flags);
-  if (group == 32 && (lay.flags & kSfColMajor) && !(lay.flags & kSfPacked)) {
+  if (group == 32 && (lay.flags & kSfColMajor)) {
     switch (fmt) {
       case kE4M3: return launch_cm32<kE4M3>(x, rows, cols, floor, q, sf, lay, stream);
       case kE2M1: return launch_cm32<kE2M1>(x, rows, cols, floor, q, sf, lay, stream);
